@@ -1,0 +1,117 @@
+/*
+ * mimo_bwd_fwd.h -- C ABI of the MI355X (gfx950) implementation of the first
+ * stage of the Mamba-3 MIMO combined backward, "mamba_mimo_bwd_fwd".
+ *
+ * Operation (Triton-Ascend mamba_mimo_bwd_fwd pull request page: operator
+ * document, "inputs and outputs" tables and constraints; BF16-boundary
+ * PyTorch reference, whole listing). For every batch b and value head h
+ * (q/k group g = h / (H/G)) the call re-runs the chunked MIMO scan over the
+ * sequence in chunks of C tokens and writes
+ *   states [B,H,nc,N,P] bf16  -- the fp32 recurrent state *entering* chunk c,
+ *                                rounded to bf16 (nc = ceil(S/C));
+ *   qk_dot [B,H,S,R,R]  bf16  -- the same-token dot of the biased, unrotated
+ *                                q (rank r_out) and k (rank r_in);
+ *   dmimo_o [B,H,R,P]   fp32  -- (reduced dout only) output-projection gradient;
+ *   dz      [B,S,H,P]   bf16  -- (z given) gradient of the gate input;
+ *   dmimo_z [B,H,R,P]   fp32  -- (z given) gate-projection gradient.
+ * dmimo_o and dmimo_z are per batch (not summed over B). Intermediate values
+ * are rounded to bf16 at the same points as the pages' BF16-boundary
+ * reference; dots, the state and the gradient sums accumulate in fp32.
+ *
+ * Layouts: every tensor is dense, row-major (C order), in the pages' shapes:
+ *   dout   [B,S,H,P] when mimo_o != NULL ("reduced"), else [B,S,R,H,P]   bf16
+ *   q, k   [B,S,R,G,N] bf16        v, z [B,S,H,P] bf16
+ *   q_bias, k_bias [H,R,N] fp32    mimo_v, mimo_o, mimo_z [H,R,P] fp32
+ *   angles [B,S,H,N/rotary_dim_divisor] fp32
+ *   da_cs, da_cs_rev, dt [B,H,S] fp32     trap [B,H,S] bf16
+ *   d [H] fp32                     segsum [B,H,nc,C,C] fp32
+ * bf16 values are passed as their 16-bit patterns (uint16_t).
+ *
+ * Branches follow the pages: mimo_o != NULL selects the reduced dout layout
+ * and enables dmimo_o; z != NULL enables dz and dmimo_z (mimo_z is then
+ * required, and must be NULL otherwise); d != NULL adds the skip term.
+ *
+ * Ownership: the caller owns every buffer (inputs, outputs and the
+ * workspace) and keeps them alive until the work queued on the stream has
+ * finished. All pointers are device pointers of the current HIP device.
+ * The library never allocates, frees or synchronises; it keeps no state
+ * between calls except a per-device cache of the device architecture.
+ *
+ * Errors: every entry point returns a mimo_status. On error nothing has been
+ * queued, and mimo_last_error() returns a message (thread-local storage).
+ */
+#ifndef MIMO_BWD_FWD_H
+#define MIMO_BWD_FWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MIMO_ABI_VERSION 1
+
+typedef enum {
+    MIMO_OK = 0,
+    MIMO_ERR_VALUE = 1,        /* bad shape, size, pointer or branch combination (ValueError) */
+    MIMO_ERR_TYPE = 2,         /* reserved for dtype errors raised by bindings (TypeError)     */
+    MIMO_ERR_UNSUPPORTED = 3,  /* valid on the pages but not supported here (NotImplementedError) */
+    MIMO_ERR_HIP = 4           /* a HIP runtime call failed (RuntimeError)                     */
+} mimo_status;
+
+typedef struct mimo_bwd_fwd_args {
+    /* sizes: batch, sequence, value heads, q/k groups, MIMO rank, state dim, value dim */
+    int64_t B, S, H, G, R, N, P;
+    int32_t chunk_size;          /* C >= 1, C*R <= 128                               */
+    int32_t rotary_dim_divisor;  /* 2 or 4; N must be even and divisible by it       */
+    /* inputs (device pointers; the optional ones may be NULL) */
+    const uint16_t *dout, *q, *k, *v;
+    const float *q_bias, *k_bias, *mimo_v;
+    const float *mimo_o;         /* optional: selects reduced dout                    */
+    const uint16_t *z;           /* optional                                          */
+    const float *mimo_z;         /* required iff z != NULL                            */
+    const float *angles, *da_cs, *da_cs_rev, *dt;
+    const uint16_t *trap;
+    const float *d;              /* optional                                          */
+    const float *segsum;
+    /* outputs (device pointers): dmimo_o must be non-NULL iff mimo_o is given,
+     * dz and dmimo_z iff z is given; states and qk_dot always. */
+    float *dmimo_o;
+    uint16_t *states;
+    uint16_t *dz;
+    float *dmimo_z;
+    uint16_t *qk_dot;
+    /* scratch: device memory of at least mimo_bwd_fwd_workspace_size() bytes,
+     * 256-byte aligned; its contents on entry do not matter. May be NULL when
+     * the required size is 0. */
+    void *workspace;
+    size_t workspace_bytes;
+} mimo_bwd_fwd_args;
+
+/* Size in bytes of the workspace a call with these sizes and branches needs
+ * (reads only the size fields, chunk_size and which optional pointers are
+ * NULL). Returns MIMO_ERR_VALUE / MIMO_ERR_UNSUPPORTED for shapes the call
+ * would reject. */
+mimo_status mimo_bwd_fwd_workspace_size(const mimo_bwd_fwd_args *args, size_t *bytes);
+
+/* Validate the arguments and queue the whole computation on `stream`
+ * (a hipStream_t; NULL = the default stream of the current device).
+ * Asynchronous: returns once the kernels are queued. Supported beyond the
+ * pages' constraints: N and P multiples of 16, N, P <= 128, C <= 64, and each
+ * rank's rows padded to a multiple of 16 tokens must fit 128 rows
+ * (R * 16*ceil(C/16) <= 128), else MIMO_ERR_UNSUPPORTED. Requires a gfx950
+ * device, else MIMO_ERR_UNSUPPORTED. */
+mimo_status mimo_bwd_fwd(const mimo_bwd_fwd_args *args, void *stream);
+
+/* Message describing the last error of the calling thread ("" if none). */
+const char *mimo_last_error(void);
+
+/* MIMO_ABI_VERSION of the library. */
+int mimo_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIMO_BWD_FWD_H */

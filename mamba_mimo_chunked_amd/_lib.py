@@ -1,0 +1,79 @@
+"""ctypes view of the C ABI in include/mimo_bwd_fwd.h.
+
+Only argument marshalling lives here. The shared library is the in-tree
+build (``mamba_mimo_chunked_amd/_build/libmimo_bwd_fwd.so``); when it is
+missing the import of this module's ``lib()`` raises, there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().parent / "_build" / "libmimo_bwd_fwd.so"
+
+MIMO_OK, MIMO_ERR_VALUE, MIMO_ERR_TYPE, MIMO_ERR_UNSUPPORTED, MIMO_ERR_HIP = range(5)
+ABI_VERSION = 1
+
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+
+
+class MimoBwdFwdArgs(ctypes.Structure):
+    """Mirror of ``mimo_bwd_fwd_args`` (field order and types must match)."""
+
+    _fields_ = [
+        ("B", ctypes.c_int64), ("S", ctypes.c_int64), ("H", ctypes.c_int64), ("G", ctypes.c_int64),
+        ("R", ctypes.c_int64), ("N", ctypes.c_int64), ("P", ctypes.c_int64),
+        ("chunk_size", ctypes.c_int32), ("rotary_dim_divisor", ctypes.c_int32),
+        ("dout", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("q_bias", ctypes.c_void_p), ("k_bias", ctypes.c_void_p), ("mimo_v", ctypes.c_void_p),
+        ("mimo_o", ctypes.c_void_p),
+        ("z", ctypes.c_void_p),
+        ("mimo_z", ctypes.c_void_p),
+        ("angles", ctypes.c_void_p), ("da_cs", ctypes.c_void_p), ("da_cs_rev", ctypes.c_void_p),
+        ("dt", ctypes.c_void_p),
+        ("trap", ctypes.c_void_p),
+        ("d", ctypes.c_void_p),
+        ("segsum", ctypes.c_void_p),
+        ("dmimo_o", ctypes.c_void_p),
+        ("states", ctypes.c_void_p),
+        ("dz", ctypes.c_void_p),
+        ("dmimo_z", ctypes.c_void_p),
+        ("qk_dot", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+EXPORTED = ("mimo_bwd_fwd", "mimo_bwd_fwd_workspace_size", "mimo_last_error", "mimo_abi_version")
+
+_lib = None
+
+
+def lib():
+    """Load the HIP library (once). Raises ImportError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m mamba_mimo_chunked_amd.build` "
+                "(or __graft_entry__.build()); there is no fallback implementation")
+        L = ctypes.CDLL(str(LIB_PATH))
+        argp = ctypes.POINTER(MimoBwdFwdArgs)
+        L.mimo_bwd_fwd.argtypes = [argp, ctypes.c_void_p]
+        L.mimo_bwd_fwd.restype = ctypes.c_int
+        L.mimo_bwd_fwd_workspace_size.argtypes = [argp, ctypes.POINTER(ctypes.c_size_t)]
+        L.mimo_bwd_fwd_workspace_size.restype = ctypes.c_int
+        L.mimo_last_error.argtypes = []
+        L.mimo_last_error.restype = ctypes.c_char_p
+        L.mimo_abi_version.argtypes = []
+        L.mimo_abi_version.restype = ctypes.c_int
+        if L.mimo_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH}: ABI version {L.mimo_abi_version()} != {ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().mimo_last_error().decode(errors="replace")

@@ -1,0 +1,208 @@
+"""Public Python entry point: ``mamba_mimo_bwd_fwd``.
+
+Signature, defaults, output order, validation order and error types follow
+the Triton-Ascend mamba_mimo_bwd_fwd page (public API module: the
+``MambaMimoBwdFwdOutputs`` named tuple, ``_check_tensor`` and
+``_validate_inputs``). PyTorch supplies device memory (outputs and the
+workspace) and the current stream; every step of the computation runs in the
+HIP library behind ``include/mimo_bwd_fwd.h``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from functools import lru_cache
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _lib
+
+__all__ = ["MambaMimoBwdFwdOutputs", "mamba_mimo_bwd_fwd", "workspace_size"]
+
+Tensor = torch.Tensor
+
+
+class MambaMimoBwdFwdOutputs(NamedTuple):
+    """Outputs of the first Mamba-3 MIMO backward stage, in the pages' order."""
+
+    dmimo_o: Optional[Tensor]
+    states: Tensor
+    dz: Optional[Tensor]
+    dmimo_z: Optional[Tensor]
+    qk_dot: Tensor
+
+
+@lru_cache
+def _is_gfx950(index: int) -> bool:
+    name = getattr(torch.cuda.get_device_properties(index), "gcnArchName", "")
+    return name.startswith("gfx950")
+
+
+def _check_tensor(name, tensor, shape, dtype, device):
+    if tuple(tensor.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(tensor.shape)}")
+    if tensor.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {tensor.dtype}")
+    if tensor.device != device:
+        raise ValueError(f"{name} must be on {device}, got {tensor.device}")
+
+
+def _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
+                     da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor):
+    if q.dim() != 5:
+        raise ValueError("q must have shape [B, S, R, G, N]")
+    batch, seqlen, rank, groups, state_dim = q.shape
+    if batch < 1 or seqlen < 1 or rank < 1 or groups < 1:
+        raise ValueError("B, S, R and G must be positive")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q, k, v, dout and trap must use torch.bfloat16")
+    if q.device.type != "cuda":
+        raise ValueError("mamba_mimo_bwd_fwd requires GPU (HIP) tensors")
+    if not _is_gfx950(q.device.index if q.device.index is not None else torch.cuda.current_device()):
+        raise NotImplementedError("mamba_mimo_bwd_fwd supports gfx950 (MI355X) devices only")
+    if chunk_size < 1 or chunk_size * rank > 128:
+        raise ValueError("chunk_size * R must be in [1, 128]")
+    if rotary_dim_divisor not in (2, 4):
+        raise ValueError("rotary_dim_divisor must be 2 or 4")
+    if state_dim % rotary_dim_divisor or state_dim % 2:
+        raise ValueError("N must be even and divisible by rotary_dim_divisor")
+    if state_dim > 128:
+        raise ValueError("N greater than 128 is not supported")
+    if k.shape != q.shape:
+        raise ValueError("k must have the same shape as q")
+    if v.dim() != 4 or tuple(v.shape[:2]) != (batch, seqlen):
+        raise ValueError("v must have shape [B, S, H, P]")
+    heads, value_dim = v.shape[2:]
+    if heads % groups:
+        raise ValueError("H must be divisible by G")
+    if value_dim > 128:
+        raise ValueError("P greater than 128 is not supported")
+
+    device = q.device
+    _check_tensor("k", k, tuple(q.shape), torch.bfloat16, device)
+    _check_tensor("v", v, (batch, seqlen, heads, value_dim), torch.bfloat16, device)
+    _check_tensor("q_bias", q_bias, (heads, rank, state_dim), torch.float32, device)
+    _check_tensor("k_bias", k_bias, (heads, rank, state_dim), torch.float32, device)
+    _check_tensor("mimo_v", mimo_v, (heads, rank, value_dim), torch.float32, device)
+    _check_tensor("angles", angles, (batch, seqlen, heads, state_dim // rotary_dim_divisor),
+                  torch.float32, device)
+    for name, tensor in (("da_cs", da_cs), ("da_cs_rev", da_cs_rev), ("dt", dt)):
+        _check_tensor(name, tensor, (batch, heads, seqlen), torch.float32, device)
+    _check_tensor("trap", trap, (batch, heads, seqlen), torch.bfloat16, device)
+    nchunks = (seqlen + chunk_size - 1) // chunk_size
+    _check_tensor("segsum", segsum, (batch, heads, nchunks, chunk_size, chunk_size), torch.float32, device)
+    if d is not None:
+        _check_tensor("d", d, (heads,), torch.float32, device)
+    if mimo_o is not None:
+        _check_tensor("mimo_o", mimo_o, (heads, rank, value_dim), torch.float32, device)
+        _check_tensor("dout", dout, (batch, seqlen, heads, value_dim), torch.bfloat16, device)
+    else:
+        _check_tensor("dout", dout, (batch, seqlen, rank, heads, value_dim), torch.bfloat16, device)
+    if z is None:
+        if mimo_z is not None:
+            raise ValueError("mimo_z must be None when z is None")
+    else:
+        _check_tensor("z", z, (batch, seqlen, heads, value_dim), torch.bfloat16, device)
+        if mimo_z is None:
+            raise ValueError("mimo_z is required when z is present")
+        _check_tensor("mimo_z", mimo_z, (heads, rank, value_dim), torch.float32, device)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _raise(status: int):
+    msg = _lib.last_error()
+    if status == _lib.MIMO_ERR_VALUE:
+        raise ValueError(msg)
+    if status == _lib.MIMO_ERR_TYPE:
+        raise TypeError(msg)
+    if status == _lib.MIMO_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(f"mimo_bwd_fwd failed: {msg}")
+
+
+def _make_args(B, S, H, G, R, N, P, C, rd, t: dict, outs: dict, workspace=None, ws_bytes=0):
+    a = _lib.MimoBwdFwdArgs()
+    a.B, a.S, a.H, a.G, a.R, a.N, a.P = B, S, H, G, R, N, P
+    a.chunk_size, a.rotary_dim_divisor = C, rd
+    for name in ("dout", "q", "k", "v", "q_bias", "k_bias", "mimo_v", "mimo_o", "z", "mimo_z",
+                 "angles", "da_cs", "da_cs_rev", "dt", "trap", "d", "segsum"):
+        x = t.get(name)
+        setattr(a, name, None if x is None else x.data_ptr())
+    for name in ("dmimo_o", "states", "dz", "dmimo_z", "qk_dot"):
+        x = outs.get(name)
+        setattr(a, name, None if x is None else x.data_ptr())
+    a.workspace = None if workspace is None else workspace.data_ptr()
+    a.workspace_bytes = ws_bytes
+    return a
+
+
+def workspace_size(B, S, H, G, R, N, P, chunk_size, rotary_dim_divisor=4, *, reduce_o=True,
+                   has_z=True) -> int:
+    """Workspace bytes the library needs for these sizes and branches."""
+    a = _lib.MimoBwdFwdArgs()
+    a.B, a.S, a.H, a.G, a.R, a.N, a.P = B, S, H, G, R, N, P
+    a.chunk_size, a.rotary_dim_divisor = chunk_size, rotary_dim_divisor
+    # only NULL-ness of the optional pointers matters here
+    a.mimo_o = 1 if reduce_o else None
+    a.z = a.mimo_z = 1 if has_z else None
+    n = ctypes.c_size_t(0)
+    st = _lib.lib().mimo_bwd_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if st != _lib.MIMO_OK:
+        _raise(st)
+    return int(n.value)
+
+
+def mamba_mimo_bwd_fwd(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
+                       da_cs_rev, dt, trap, d, segsum, chunk_size: int = 16,
+                       rotary_dim_divisor: int = 4, *, out: Optional[dict] = None,
+                       workspace: Optional[Tensor] = None) -> MambaMimoBwdFwdOutputs:
+    """Run the Mamba-3 MIMO backward first stage on the current HIP stream.
+
+    Passing ``mimo_o`` selects reduced dout; passing ``z`` enables ``dz`` and
+    ``dmimo_z``; passing ``d`` enables the skip term. Optional ``out`` holds
+    preallocated output tensors (keys dmimo_o, states, dz, dmimo_z, qk_dot) and
+    ``workspace`` a preallocated uint8 scratch tensor (see ``workspace_size``).
+    The call is asynchronous with respect to the host.
+    """
+    _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
+                     da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor)
+    L = _lib.lib()
+    B, S, R, G, N = q.shape
+    H, P = v.shape[2:]
+    C = int(chunk_size)
+    nc = (S + C - 1) // C
+    dev = q.device
+    t = {name: (None if x is None else x.contiguous()) for name, x in (
+        ("dout", dout), ("q", q), ("k", k), ("v", v), ("q_bias", q_bias), ("k_bias", k_bias),
+        ("mimo_v", mimo_v), ("mimo_o", mimo_o), ("z", z), ("mimo_z", mimo_z), ("angles", angles),
+        ("da_cs", da_cs), ("da_cs_rev", da_cs_rev), ("dt", dt), ("trap", trap), ("d", d),
+        ("segsum", segsum))}
+    reduce_o, has_z = mimo_o is not None, z is not None
+    if out is None:
+        out = {
+            "dmimo_o": torch.empty((B, H, R, P), dtype=torch.float32, device=dev) if reduce_o else None,
+            "states": torch.empty((B, H, nc, N, P), dtype=torch.bfloat16, device=dev),
+            "dz": torch.empty((B, S, H, P), dtype=torch.bfloat16, device=dev) if has_z else None,
+            "dmimo_z": torch.empty((B, H, R, P), dtype=torch.float32, device=dev) if has_z else None,
+            "qk_dot": torch.empty((B, H, S, R, R), dtype=torch.bfloat16, device=dev),
+        }
+    args = _make_args(B, S, H, G, R, N, P, C, int(rotary_dim_divisor), t, out)
+    need = ctypes.c_size_t(0)
+    st = L.mimo_bwd_fwd_workspace_size(ctypes.byref(args), ctypes.byref(need))
+    if st != _lib.MIMO_OK:
+        _raise(st)
+    if need.value > 0:
+        if workspace is None or workspace.numel() < need.value:
+            workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.mimo_bwd_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != _lib.MIMO_OK:
+        _raise(st)
+    return MambaMimoBwdFwdOutputs(out["dmimo_o"], out["states"], out["dz"], out["dmimo_z"], out["qk_dot"])

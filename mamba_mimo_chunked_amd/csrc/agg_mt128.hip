@@ -1,0 +1,11 @@
+// Segment-aggregate kernel instantiations for chunk tiles of 128 rows.
+#include "mimo_kernels.hpp"
+
+namespace mimo {
+const kfn* agg_table_mt128() {
+#define MIMO_AGG(NT, PT) agg_for<128, NT, PT>()
+    static const kfn table[9] = {MIMO_NP_TABLE(MIMO_AGG)};
+#undef MIMO_AGG
+    return table;
+}
+}  // namespace mimo

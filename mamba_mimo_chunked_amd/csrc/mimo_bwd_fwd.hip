@@ -1,0 +1,343 @@
+// MI355X (gfx950) implementation of the first stage of the Mamba-3 MIMO
+// combined backward ("mamba_mimo_bwd_fwd"), behind the C ABI declared in
+// include/mimo_bwd_fwd.h.
+//
+// What is computed follows the Triton-Ascend mamba_mimo_bwd_fwd pull request
+// page: its operator document (inputs/outputs, constraints, bf16 rounding
+// boundaries) and its BF16-boundary PyTorch reference (bias and qk_dot,
+// rotation, PsiV, trapezoidal discretisation, the chunk loop, the gating
+// branches). The kernel split below is this library's own.
+//
+// Work decomposition. Chunks of one (batch, head) form a serial fp32 state
+// recurrence S_{c+1} = S_c * exp(da_cs[last(c)]) + kappa_c^T Psi_c, which is
+// elementwise-linear in the [N,P] state. The chunks are grouped into
+// segments of L consecutive chunks:
+//   k_agg   (segment-parallel)  the state each segment adds from a zero start,
+//                               and its decay product;
+//   k_scan  ((n,p)-parallel)    the state entering every segment;
+//   k_main  (segment-parallel)  walks its L chunks from the entry state: bf16
+//                               entry states, qk_dot, the chunk-local causal
+//                               block, y, and the gating gradients, with
+//                               per-segment partial sums of dmimo_o/dmimo_z;
+//   k_finish                    sums the partials over segments in order.
+// With one segment only k_main runs. The bf16 rounding of the carried state
+// (states[c] = bf16(S_c)) is applied to the fp32 state, so splitting the
+// recurrence this way changes nothing but fp32 summation order.
+//
+// Chunk tile. Rows of a chunk are rank-major: row i = r*Cp + t for rank r and
+// token t of the chunk, Cp = C rounded up to 16, so a 16-row MFMA tile holds
+// 16 tokens of one rank, and the lane that holds token t of rank r in one
+// tile holds token t of every rank in the rank's other tiles. That keeps the
+// rank-ordered diagonal and dz chains, and the per-rank projection-gradient
+// sums, inside one lane. The strictly causal mask works on token index.
+// Padded rows and columns are zero in every operand.
+//
+// MFMA: v_mfma_f32_16x16x32_bf16, fp32 accumulate. Operand fragments are
+// read from LDS as 8 consecutive bf16 along the contraction index, so each
+// operand is stored contraction-contiguous:
+//   A^T = K~ Q^T       sK [i][n], sQ [i][n]      (contract over n)
+//   inter = Q bf16(S)  sQ [i][n], sSbT [p][n]
+//   intra = A Psi      sA [i][j], sPsiT [p][j]  (contract over j)
+//   S' = kappa^T Psi   sKapT [n][i], sPsiT [p][i]
+#include "mimo_kernels.hpp"
+
+namespace mimo {
+
+// ---------------------------------------------------------------- segment scan
+// In place: agg[s] <- E_{s+1} = E_s * decay_s + U_s, E_0 = 0. Each thread owns
+// four consecutive state elements. Loads run ahead of the serial chain.
+__global__ __launch_bounds__(256) void k_scan(Params p) {
+    const int bh = blockIdx.y;
+    const int NP = p.N * p.P;
+    const int e4 = blockIdx.x * 256 + threadIdx.x;
+    if (4 * e4 >= NP) return;
+    const int ns = p.nseg - 1;
+    float* base = p.agg + (long)bh * ns * NP + 4 * e4;
+    const float* dec = p.decay + (long)bh * p.nseg;
+    float4 E = make_float4(0.f, 0.f, 0.f, 0.f);
+    constexpr int AHEAD = 8;
+    for (int s0 = 0; s0 < ns; s0 += AHEAD) {
+        float4 U[AHEAD];
+        float D[AHEAD];
+#pragma unroll
+        for (int j = 0; j < AHEAD; ++j) {
+            if (s0 + j < ns) {
+                U[j] = *reinterpret_cast<const float4*>(base + (long)(s0 + j) * NP);
+                D[j] = dec[s0 + j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < AHEAD; ++j) {
+            if (s0 + j < ns) {
+                E.x = E.x * D[j] + U[j].x;
+                E.y = E.y * D[j] + U[j].y;
+                E.z = E.z * D[j] + U[j].z;
+                E.w = E.w * D[j] + U[j].w;
+                *reinterpret_cast<float4*>(base + (long)(s0 + j) * NP) = E;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_finish(Params p) {
+    const long RP = (long)p.R * p.P;
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (long)p.B * p.H * RP) return;
+    const long bh = e / RP, rp = e - bh * RP;
+    if (p.reduce_o) {
+        float s = 0.f;
+        for (int sg = 0; sg < p.nseg; ++sg) s += p.part_o[(bh * p.nseg + sg) * RP + rp];
+        p.dmimo_o[e] = s;
+    }
+    if (p.has_z) {
+        float s = 0.f;
+        for (int sg = 0; sg < p.nseg; ++sg) s += p.part_z[(bh * p.nseg + sg) * RP + rp];
+        p.dmimo_z[e] = s;
+    }
+}
+
+}  // namespace mimo
+
+namespace {
+
+using namespace mimo;
+
+// ---------------------------------------------------------------- host side
+thread_local std::string g_err;
+
+mimo_status fail(mimo_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+struct Plan {
+    int RP, CT, MTm, NWm, MTa, NWa, NT, PT, Cp, W, nc, L, nseg;
+    size_t off_agg, off_decay, off_po, off_pz, ws_bytes;
+    int lds_agg, lds_main;
+};
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+int tile_size(int x) { return x <= 32 ? 32 : (x <= 64 ? 64 : 128); }
+int next_pow2(int x) {
+    int y = 1;
+    while (y < x) y *= 2;
+    return y;
+}
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
+    if (a == nullptr) return fail(MIMO_ERR_VALUE, "args must not be NULL");
+    const int64_t B = a->B, S = a->S, H = a->H, G = a->G, R = a->R, N = a->N, P = a->P;
+    const int64_t C = a->chunk_size, rd = a->rotary_dim_divisor;
+    if (B < 1 || S < 1 || R < 1 || G < 1) return fail(MIMO_ERR_VALUE, "B, S, R and G must be positive");
+    if (H < 1 || N < 1 || P < 1) return fail(MIMO_ERR_VALUE, "H, N and P must be positive");
+    if (C < 1 || C * R > 128) return fail(MIMO_ERR_VALUE, "chunk_size * R must be in [1, 128]");
+    if (rd != 2 && rd != 4) return fail(MIMO_ERR_VALUE, "rotary_dim_divisor must be 2 or 4");
+    if (N % rd || N % 2) return fail(MIMO_ERR_VALUE, "N must be even and divisible by rotary_dim_divisor");
+    if (N > 128) return fail(MIMO_ERR_VALUE, "N greater than 128 is not supported");
+    if (H % G) return fail(MIMO_ERR_VALUE, "H must be divisible by G");
+    if (P > 128) return fail(MIMO_ERR_VALUE, "P greater than 128 is not supported");
+    if ((a->z == nullptr) != (a->mimo_z == nullptr))
+        return fail(MIMO_ERR_VALUE, "z and mimo_z must either both be present or both be NULL");
+    if (N % 16) return fail(MIMO_ERR_UNSUPPORTED, "N must be a multiple of 16 (got %lld)", (long long)N);
+    if (P % 16) return fail(MIMO_ERR_UNSUPPORTED, "P must be a multiple of 16 (got %lld)", (long long)P);
+    if (C > 64) return fail(MIMO_ERR_UNSUPPORTED, "chunk_size above 64 is not supported");
+    if (R > 8) return fail(MIMO_ERR_UNSUPPORTED, "R above 8 is not supported (got %lld)", (long long)R);
+    // rows of a chunk tile: ranks padded to a power of two, tokens to 16, 32 or 64
+    const int CT = next_pow2((int)((C + 15) / 16));
+    const int RP = next_pow2((int)R);
+    if (RP * CT > 8)
+        return fail(MIMO_ERR_UNSUPPORTED,
+                    "R=%lld with chunk_size=%lld needs %d tile rows (limit 128)", (long long)R, (long long)C,
+                    16 * RP * CT);
+    if (B * H > 65535) return fail(MIMO_ERR_UNSUPPORTED, "B * H above 65535 is not supported");
+    if (S > (int64_t)1 << 30) return fail(MIMO_ERR_UNSUPPORTED, "S above 2^30 is not supported");
+    pl->RP = RP;
+    pl->CT = CT;
+    pl->Cp = 16 * CT;
+    pl->W = (int)(N / rd);
+    pl->NT = tile_size((int)N);
+    pl->PT = tile_size((int)P);
+    pl->MTm = 16 * RP * CT < 32 ? 32 : 16 * RP * CT;
+    pl->NWm = (pl->MTm == 128 && pl->PT >= 64) ? 8 : 4;
+    pl->MTa = tile_size((int)R * pl->Cp);
+    pl->NWa = (pl->MTa == 128 && pl->PT >= 64) ? 8 : 4;
+    pl->nc = (int)((S + C - 1) / C);
+    // segments: aim at >= 4 workgroups per compute unit
+    const int64_t target = 1024;
+    int64_t L = (pl->nc * B * H + target - 1) / target;
+    if (L < 1) L = 1;
+    if (L > pl->nc) L = pl->nc;
+    pl->L = (int)L;
+    pl->nseg = (int)((pl->nc + L - 1) / L);
+    if (pl->nseg > 65535) return fail(MIMO_ERR_UNSUPPORTED, "too many segments");
+    const bool reduce_o = a->mimo_o != nullptr, has_z = a->z != nullptr;
+    size_t off = 0;
+    pl->off_agg = off;
+    if (pl->nseg > 1) off = align256(off + (size_t)B * H * (pl->nseg - 1) * N * P * 4);
+    pl->off_decay = off;
+    if (pl->nseg > 1) off = align256(off + (size_t)B * H * pl->nseg * 4);
+    pl->off_po = off;
+    if (pl->nseg > 1 && reduce_o) off = align256(off + (size_t)B * H * pl->nseg * R * P * 4);
+    pl->off_pz = off;
+    if (pl->nseg > 1 && has_z) off = align256(off + (size_t)B * H * pl->nseg * R * P * 4);
+    pl->ws_bytes = off;
+    Lds lm = lds_layout(pl->MTm, pl->NT, pl->PT, (int)C, (int)R, pl->W, true);
+    Lds la = lds_layout(pl->MTa, pl->NT, pl->PT, (int)C, (int)R, pl->W, false);
+    pl->lds_main = lm.total;
+    pl->lds_agg = la.total;
+    // the token-tile reduction of the dmimo partials reuses LDS from offset 0
+    if (CT > 1) {
+        const int red = 2 * CT * RP * pl->PT * 4;
+        if (red > pl->lds_main) pl->lds_main = red;
+    }
+    if (pl->lds_main > 160 * 1024)
+        return fail(MIMO_ERR_UNSUPPORTED, "shape needs %d bytes of LDS per workgroup (limit 163840)", pl->lds_main);
+    return MIMO_OK;
+}
+
+int tidx(int x) { return x == 32 ? 0 : (x == 64 ? 1 : 2); }
+
+kfn agg_kernel(int MT, int NT, int PT) {
+    const kfn* t = MT == 32 ? agg_table_mt32() : (MT == 64 ? agg_table_mt64() : agg_table_mt128());
+    return t[tidx(NT) * 3 + tidx(PT)];
+}
+
+kfn main_kernel(int RP, int CT, int NT, int PT) {
+    const kfn* t = nullptr;
+    switch (RP * 10 + CT) {
+        case 11: t = main_table_rp1_ct1(); break;
+        case 12: t = main_table_rp1_ct2(); break;
+        case 14: t = main_table_rp1_ct4(); break;
+        case 21: t = main_table_rp2_ct1(); break;
+        case 22: t = main_table_rp2_ct2(); break;
+        case 24: t = main_table_rp2_ct4(); break;
+        case 41: t = main_table_rp4_ct1(); break;
+        case 42: t = main_table_rp4_ct2(); break;
+        case 81: t = main_table_rp8_ct1(); break;
+        default: return nullptr;
+    }
+    return t[tidx(NT) * 3 + tidx(PT)];
+}
+
+std::mutex g_mu;
+int g_arch_ok[64];  // 0 unknown, 1 gfx950, 2 other
+
+mimo_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MIMO_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= 64) return fail(MIMO_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_arch_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(MIMO_ERR_HIP, "hipGetDeviceProperties failed");
+        g_arch_ok[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    if (g_arch_ok[dev] != 1) return fail(MIMO_ERR_UNSUPPORTED, "mamba_mimo_bwd_fwd requires a gfx950 (MI355X) device");
+    return MIMO_OK;
+}
+
+mimo_status set_lds(kfn f, int bytes) {
+    if (bytes <= 64 * 1024) return MIMO_OK;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(f), hipFuncAttributeMaxDynamicSharedMemorySize, bytes) !=
+        hipSuccess)
+        return fail(MIMO_ERR_HIP, "hipFuncSetAttribute(MaxDynamicSharedMemorySize=%d) failed", bytes);
+    return MIMO_OK;
+}
+
+mimo_status launch(kfn f, dim3 grid, dim3 block, int lds, hipStream_t st, Params& p) {
+    void* args[] = {&p};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(f), grid, block, args, (size_t)lds, st);
+    if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return MIMO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mimo_abi_version(void) { return MIMO_ABI_VERSION; }
+
+const char* mimo_last_error(void) { return g_err.c_str(); }
+
+mimo_status mimo_bwd_fwd_workspace_size(const mimo_bwd_fwd_args* args, size_t* bytes) {
+    Plan pl;
+    const mimo_status s = make_plan(args, &pl);
+    if (s != MIMO_OK) return s;
+    if (bytes == nullptr) return fail(MIMO_ERR_VALUE, "bytes must not be NULL");
+    *bytes = pl.ws_bytes;
+    return MIMO_OK;
+}
+
+mimo_status mimo_bwd_fwd(const mimo_bwd_fwd_args* a, void* stream) {
+    g_err.clear();
+    Plan pl;
+    mimo_status s = make_plan(a, &pl);
+    if (s != MIMO_OK) return s;
+    const bool reduce_o = a->mimo_o != nullptr, has_z = a->z != nullptr;
+    if (!a->dout && (reduce_o || has_z)) return fail(MIMO_ERR_VALUE, "dout must not be NULL");
+    if (!a->q || !a->k || !a->v || !a->q_bias || !a->k_bias || !a->mimo_v || !a->angles || !a->da_cs ||
+        !a->da_cs_rev || !a->dt || !a->trap || !a->segsum)
+        return fail(MIMO_ERR_VALUE, "a required input pointer is NULL");
+    if (!a->states || !a->qk_dot) return fail(MIMO_ERR_VALUE, "states and qk_dot must not be NULL");
+    if ((a->dmimo_o != nullptr) != reduce_o)
+        return fail(MIMO_ERR_VALUE, "dmimo_o must be given exactly when mimo_o is given");
+    if ((a->dz != nullptr) != has_z || (a->dmimo_z != nullptr) != has_z)
+        return fail(MIMO_ERR_VALUE, "dz and dmimo_z must be given exactly when z is given");
+    if (a->workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && a->workspace == nullptr))
+        return fail(MIMO_ERR_VALUE, "workspace too small: need %zu bytes, got %zu", pl.ws_bytes, a->workspace_bytes);
+    if (pl.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(a->workspace) & 255))
+        return fail(MIMO_ERR_VALUE, "workspace must be 256-byte aligned");
+    s = check_device();
+    if (s != MIMO_OK) return s;
+
+    Params p;
+    p.B = (int)a->B; p.S = (int)a->S; p.H = (int)a->H; p.G = (int)a->G;
+    p.R = (int)a->R; p.N = (int)a->N; p.P = (int)a->P; p.C = a->chunk_size;
+    p.Cp = pl.Cp; p.W = pl.W; p.nc = pl.nc; p.L = pl.L; p.nseg = pl.nseg; p.rd = a->rotary_dim_divisor;
+    p.reduce_o = reduce_o; p.has_z = has_z; p.has_d = a->d != nullptr; p.need_y = reduce_o || has_z;
+    p.dout = a->dout; p.q = a->q; p.k = a->k; p.v = a->v; p.z = a->z; p.trap = a->trap;
+    p.q_bias = a->q_bias; p.k_bias = a->k_bias; p.mimo_v = a->mimo_v; p.mimo_o = a->mimo_o;
+    p.mimo_z = a->mimo_z; p.angles = a->angles; p.da_cs = a->da_cs; p.da_cs_rev = a->da_cs_rev;
+    p.dt = a->dt; p.d = a->d; p.segsum = a->segsum;
+    p.dmimo_o = a->dmimo_o; p.dmimo_z = a->dmimo_z; p.states = a->states; p.dz = a->dz; p.qk_dot = a->qk_dot;
+    unsigned char* ws = static_cast<unsigned char*>(a->workspace);
+    p.agg = pl.nseg > 1 ? reinterpret_cast<float*>(ws + pl.off_agg) : nullptr;
+    p.decay = pl.nseg > 1 ? reinterpret_cast<float*>(ws + pl.off_decay) : nullptr;
+    if (pl.nseg > 1) {
+        p.part_o = reduce_o ? reinterpret_cast<float*>(ws + pl.off_po) : nullptr;
+        p.part_z = has_z ? reinterpret_cast<float*>(ws + pl.off_pz) : nullptr;
+    } else {
+        p.part_o = a->dmimo_o;
+        p.part_z = a->dmimo_z;
+    }
+
+    const kfn kmain = main_kernel(pl.RP, pl.CT, pl.NT, pl.PT);
+    const kfn kagg = agg_kernel(pl.MTa, pl.NT, pl.PT);
+    if (kmain == nullptr || kagg == nullptr) return fail(MIMO_ERR_UNSUPPORTED, "no kernel for this tile shape");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int BH = p.B * p.H;
+    if ((s = set_lds(kmain, pl.lds_main)) != MIMO_OK) return s;
+    if (pl.nseg > 1) {
+        if ((s = set_lds(kagg, pl.lds_agg)) != MIMO_OK) return s;
+        if ((s = launch(kagg, dim3(pl.nseg - 1, BH), dim3(pl.NWa * 64), pl.lds_agg, st, p)) != MIMO_OK) return s;
+        const int NP = p.N * p.P;
+        if ((s = launch(k_scan, dim3((NP / 4 + 255) / 256, BH), dim3(256), 0, st, p)) != MIMO_OK) return s;
+    }
+    if ((s = launch(kmain, dim3(pl.nseg, BH), dim3(pl.NWm * 64), pl.lds_main, st, p)) != MIMO_OK) return s;
+    if (pl.nseg > 1 && p.need_y) {
+        const long tot = (long)BH * p.R * p.P;
+        if ((s = launch(k_finish, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, p)) != MIMO_OK) return s;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return MIMO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+"""Host-side checks of the boundary (no GPU needed).
+
+* the C library loads and exports every entry point include/mimo_bwd_fwd.h declares;
+* the ctypes mirror of ``mimo_bwd_fwd_args`` has the C layout (gcc reports it);
+* the workspace-size query validates shapes like the call does;
+* the Python entry point raises the pages' errors, in the pages' order, before
+  touching a device (the pages' three invalid-input tests use CPU tensors).
+"""
+
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+import torch
+
+from mamba_mimo_chunked_amd import _lib, mamba_mimo_bwd_fwd, workspace_size
+from synth.inputs import Case, api_args, make_inputs
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "mimo_bwd_fwd.h"
+
+
+def test_library_exports_every_declared_symbol():
+    decl = set(re.findall(r"^\w[\w\s\*]*?\b(mimo_\w+)\s*\(", HEADER.read_text(), re.M))
+    assert decl == set(_lib.EXPORTED)
+    L = _lib.lib()
+    for name in decl:
+        assert hasattr(L, name), name
+    assert L.mimo_abi_version() == _lib.ABI_VERSION
+    out = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)], capture_output=True,
+                         text=True, check=True).stdout
+    for name in decl:
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def test_struct_layout_matches_c(tmp_path):
+    fields = [f[0] for f in _lib.MimoBwdFwdArgs._fields_]
+    prog = ["#include <stddef.h>", "#include <stdio.h>", '#include "mimo_bwd_fwd.h"', "int main(void){",
+            'printf("%zu\\n", sizeof(mimo_bwd_fwd_args));']
+    prog += [f'printf("%zu\\n", offsetof(mimo_bwd_fwd_args, {f}));' for f in fields]
+    prog += ["return 0;}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(prog))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", f"-I{ROOT / 'include'}", str(src), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(_lib.MimoBwdFwdArgs)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(_lib.MimoBwdFwdArgs, f).offset == off, f
+
+
+def test_workspace_size_query():
+    assert workspace_size(1, 16, 2, 1, 2, 16, 16, 16) == 0          # one chunk: no scratch
+    assert workspace_size(1, 64, 2, 1, 2, 16, 16, 16) > 0
+    big = workspace_size(1, 8192, 16, 1, 4, 64, 64, 16)
+    assert big > 0 and big % 256 == 0
+    with pytest.raises(ValueError, match="chunk_size"):
+        workspace_size(1, 64, 2, 1, 16, 16, 16, 16)                   # C*R = 256
+    with pytest.raises(ValueError, match="rotary"):
+        workspace_size(1, 64, 2, 1, 2, 16, 16, 16, 3)
+    with pytest.raises(ValueError, match="divisible by G"):
+        workspace_size(1, 64, 3, 2, 2, 16, 16, 16)
+    with pytest.raises(NotImplementedError, match="multiple of 16"):
+        workspace_size(1, 64, 2, 1, 2, 24, 16, 16)
+    with pytest.raises(NotImplementedError, match="chunk_size above 64"):
+        workspace_size(1, 256, 1, 1, 1, 16, 16, 128)
+
+
+def test_c_call_rejects_bad_arguments_without_a_device():
+    """Argument errors are reported before the library looks at the device."""
+    L = _lib.lib()
+    a = _lib.MimoBwdFwdArgs()
+    a.B, a.S, a.H, a.G, a.R, a.N, a.P = 1, 64, 2, 1, 2, 16, 16
+    a.chunk_size, a.rotary_dim_divisor = 16, 4
+    assert L.mimo_bwd_fwd(ctypes.byref(a), None) == _lib.MIMO_ERR_VALUE   # NULL inputs
+    assert "NULL" in _lib.last_error()
+    assert L.mimo_bwd_fwd(None, None) == _lib.MIMO_ERR_VALUE
+
+
+# -------------------------------------------------------------- the pages' invalid-input tests
+def _args(**kw):
+    inp = make_inputs(Case(1, 16, 1, 1, 64, 64, 4, 16, recipe="ut", has_z=False, has_d=False, **kw))
+    return list(api_args(inp))
+
+
+def test_invalid_q_shape():
+    args = _args()
+    args[1] = torch.randn((1, 16, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="q must have shape"):
+        mamba_mimo_bwd_fwd(*args)
+
+
+def test_invalid_empty_batch():
+    args = list(api_args(make_inputs(Case(0, 16, 1, 1, 64, 64, 4, 16, recipe="ut", has_z=False,
+                                          has_d=False))))
+    with pytest.raises(ValueError, match="B, S, R and G must be positive"):
+        mamba_mimo_bwd_fwd(*args)
+
+
+def test_invalid_q_dtype():
+    args = _args()
+    args[1] = args[1].to(torch.float16)
+    with pytest.raises(TypeError, match="torch.bfloat16"):
+        mamba_mimo_bwd_fwd(*args)
+
+
+def test_cpu_tensors_are_rejected():
+    with pytest.raises(ValueError, match="GPU"):
+        mamba_mimo_bwd_fwd(*_args())

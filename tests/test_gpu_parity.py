@@ -1,0 +1,193 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle O1.
+
+Every output must satisfy RMS(gpu - oracle) / RMS(oracle) < 1e-3 on the same
+seeded inputs, with the right dtype and None-ness. Cases:
+* the small workload shape and every unit-test shape of the pages (their own
+  input formulas: independent random controls) and the ATK shapes;
+* extra shapes that span several tiles, segments and ragged tails;
+* the larger workload shapes, on all heads where the oracle is quick enough
+  and on sampled (batch, head) pairs otherwise (heads are independent).
+Invariants that must hold bit for bit on the GPU too: power-of-two scaling,
+reduced == non-reduced with the projected dout, unused segsum entries
+ignored, every output element written, run-to-run determinism.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import o1
+from synth.inputs import ATK_CASES, CONFIGS, UT_CASES, Case, make_inputs
+
+from ._parity import NAMES, compare, log, oracle, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+EXTRA = [
+    Case(1, 300, 3, 1, 64, 64, 4, 16, name="segments_tail"),
+    Case(2, 777, 4, 2, 32, 64, 2, 16, name="gqa_tail_r2"),
+    Case(1, 1000, 2, 1, 128, 64, 2, 64, name="c64_n128"),
+    Case(1, 500, 2, 1, 128, 128, 8, 16, name="r8_n128_p128"),
+    Case(1, 333, 2, 2, 64, 32, 4, 16, reduce_o=False, has_z=True, has_d=True, name="nonreduced_z"),
+    Case(2, 257, 4, 4, 64, 64, 4, 16, reduce_o=False, has_z=False, has_d=False, name="nonreduced_noz"),
+    Case(1, 200, 2, 1, 64, 64, 4, 16, reduce_o=True, has_z=False, has_d=True, name="reduced_noz"),
+    Case(1, 130, 2, 1, 16, 16, 8, 8, name="r8_c8_small"),
+    Case(1, 95, 1, 1, 32, 48, 3, 6, rd=2, name="r3_c6_rd2_p48"),
+    Case(1, 64, 1, 1, 64, 64, 1, 64, name="r1_c64"),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from mamba_mimo_chunked_amd import _lib
+    _lib.lib()
+
+
+def _check(case, **kw):
+    log(f"[parity] {case.name or case} B={case.B} S={case.S} H={case.H} G={case.G} N={case.N} "
+        f"P={case.P} R={case.R} C={case.C}")
+    inp = make_inputs(case)
+    ref = oracle(inp)
+    got = run_gpu(to_device(inp), **kw)
+    errs = compare(got, ref, label=f"{case.name}: ")
+    log("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    return inp, ref, got
+
+
+def test_tiny_config():
+    _check(CONFIGS["tiny"])
+
+
+@pytest.mark.parametrize("case", UT_CASES, ids=lambda c: c.name)
+def test_pages_unit_test_grid(case):
+    _check(case)
+
+
+@pytest.mark.parametrize("case", [c.with_(recipe="configs") for c in UT_CASES], ids=lambda c: c.name)
+def test_unit_test_shapes_workload_inputs(case):
+    _check(case)
+
+
+@pytest.mark.parametrize("case", ATK_CASES, ids=lambda c: c.name)
+def test_atk_shapes(case):
+    _check(case)
+
+
+@pytest.mark.parametrize("case", EXTRA, ids=lambda c: c.name)
+def test_extra_shapes(case):
+    _check(case)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 42])
+def test_tiny_and_tail_seeds(seed):
+    _check(CONFIGS["tiny"].with_(seed=seed, name=f"tiny_seed{seed}"))
+
+
+def _sampled(name, heads, seed=123):
+    case = CONFIGS[name].with_(seed=seed)
+    log(f"[parity-full] {name} seed={seed}: generating inputs")
+    inp = make_inputs(case)
+    got = run_gpu(to_device(inp))
+    log(f"[parity-full] {name}: GPU done, oracle on {len(heads) if heads else 'all'} heads")
+    if heads is None:
+        ref = oracle(inp)
+        errs = compare(got, ref, label=f"{name}: ")
+        log("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        return
+    for b, h in heads:
+        ref = o1.run_inputs(o1.slice_heads(inp, b, h))
+        sl = (
+            None if got.dmimo_o is None else got.dmimo_o[b:b + 1, h:h + 1],
+            got.states[b:b + 1, h:h + 1],
+            None if got.dz is None else got.dz[b:b + 1, :, h:h + 1],
+            None if got.dmimo_z is None else got.dmimo_z[b:b + 1, h:h + 1],
+            got.qk_dot[b:b + 1, h:h + 1],
+        )
+        errs = compare(sl, ref, label=f"{name} b={b} h={h}: ")
+        log(f"    b={b} h={h} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+def test_full_perf_shape_all_heads():
+    _sampled("perf_s8192", None)
+
+
+def test_full_gqa_tail_nonreduced_all_heads():
+    _sampled("gqa_tail_nonreduced", None)
+
+
+def test_full_wide_chunk_sampled_heads():
+    _sampled("wide_chunk_n128", [(0, 0), (1, 9), (3, 31)])
+
+
+def test_full_max_rank_tile_sampled_heads():
+    _sampled("max_rank_tile", [(0, 0), (1, 15)])
+
+
+# ---------------------------------------------------------------- bitwise invariants on the GPU
+def _gpu_np(res):
+    return [None if x is None else x.float().cpu().numpy() for x in res]
+
+
+def _same(a, b):
+    if a is None or b is None:
+        return a is None and b is None
+    return np.array_equal(a, b, equal_nan=True)
+
+
+def test_determinism_and_every_element_written():
+    case = Case(1, 300, 3, 1, 64, 64, 4, 16)
+    d = to_device(make_inputs(case))
+    a = _gpu_np(run_gpu(d))
+    B, S, H, G, R, N, P = 1, 300, 3, 1, 4, 64, 64
+    nc = (S + 15) // 16
+    nan = float("nan")
+    out = {
+        "dmimo_o": torch.full((B, H, R, P), nan, device="cuda"),
+        "states": torch.full((B, H, nc, N, P), nan, device="cuda", dtype=torch.bfloat16),
+        "dz": torch.full((B, S, H, P), nan, device="cuda", dtype=torch.bfloat16),
+        "dmimo_z": torch.full((B, H, R, P), nan, device="cuda"),
+        "qk_dot": torch.full((B, H, S, R, R), nan, device="cuda", dtype=torch.bfloat16),
+    }
+    b = _gpu_np(run_gpu(d, out=out))
+    for i, n in enumerate(NAMES):
+        assert _same(a[i], b[i]), n
+        assert np.isfinite(b[i]).all(), n
+
+
+def test_power_of_two_scaling_bitwise():
+    case = Case(1, 200, 2, 1, 64, 64, 4, 16)
+    inp = make_inputs(case)
+    a = _gpu_np(run_gpu(to_device(inp)))
+    b = _gpu_np(run_gpu(to_device(dict(inp, v=inp["v"] * 2))))
+    for i in (0, 1, 2, 3):
+        assert _same(b[i], 2 * a[i]), NAMES[i]
+    assert _same(b[4], a[4])
+
+
+def test_reduced_equals_nonreduced_bitwise():
+    case = Case(1, 150, 2, 1, 64, 64, 4, 16)
+    inp = make_inputs(case)
+    a = _gpu_np(run_gpu(to_device(inp)))
+    mo = inp["mimo_o"].to(torch.bfloat16).float()
+    dnr = (inp["dout"].float()[:, :, None] * mo.permute(1, 0, 2)[None, None]).to(torch.bfloat16)
+    b = _gpu_np(run_gpu(to_device(dict(inp, dout=dnr, mimo_o=None))))
+    assert b[0] is None
+    for i in (1, 2, 3, 4):
+        assert _same(a[i], b[i]), NAMES[i]
+
+
+def test_unused_segsum_entries_ignored():
+    case = Case(1, 75, 2, 1, 64, 64, 4, 16)
+    inp = make_inputs(case)
+    a = _gpu_np(run_gpu(to_device(inp)))
+    seg = inp["segsum"].clone()
+    C = case.C
+    seg[..., torch.ones(C, C, dtype=torch.bool).triu()] = float("nan")
+    last = case.S - (case.nchunks - 1) * C
+    seg[:, :, -1, last:, :] = float("nan")
+    seg[:, :, -1, :, last:] = float("nan")
+    b = _gpu_np(run_gpu(to_device(dict(inp, segsum=seg))))
+    for i in range(5):
+        assert _same(a[i], b[i]), NAMES[i]
