@@ -97,12 +97,24 @@ mimo_status mimo_bwd_fwd_workspace_size(const mimo_bwd_fwd_args *args, size_t *b
 
 /* Validate the arguments and queue the whole computation on `stream`
  * (a hipStream_t; NULL = the default stream of the current device).
- * Asynchronous: returns once the kernels are queued. Supported beyond the
- * pages' constraints: N and P multiples of 16, N, P <= 128, C <= 64, and each
- * rank's rows padded to a multiple of 16 tokens must fit 128 rows
- * (R * 16*ceil(C/16) <= 128), else MIMO_ERR_UNSUPPORTED. Requires a gfx950
- * device, else MIMO_ERR_UNSUPPORTED. */
+ * Asynchronous: returns once the kernels are queued. Within the pages'
+ * constraints (C*R <= 128, N, P <= 128, N even and divisible by the rotary
+ * divisor, H % G == 0) this library further requires N and P to be
+ * multiples of 16, C <= 64, R <= 8 and RP * CP <= 128, where RP is R rounded
+ * up to a power of two and CP is C rounded up to 16, 32 or 64; other shapes
+ * return MIMO_ERR_UNSUPPORTED. Requires a gfx950 device, else
+ * MIMO_ERR_UNSUPPORTED. */
 mimo_status mimo_bwd_fwd(const mimo_bwd_fwd_args *args, void *stream);
+
+/* mimo_bwd_fwd with per-kernel timing, for measurement. `events` points to
+ * MIMO_TIMED_EVENTS hipEvent_t handles the caller created (hipEventCreate) on
+ * the current device. They are recorded on `stream` before the
+ * segment-aggregate kernel, before the segment scan, before the chunk
+ * kernel, after the chunk kernel and after the final reduction; a kernel
+ * that does not run for this shape leaves its two events back to back.
+ * Same operation, arguments, ownership and errors as mimo_bwd_fwd. */
+#define MIMO_TIMED_EVENTS 5
+mimo_status mimo_bwd_fwd_timed(const mimo_bwd_fwd_args *args, void *stream, void *const *events);
 
 /* Message describing the last error of the calling thread ("" if none). */
 const char *mimo_last_error(void);

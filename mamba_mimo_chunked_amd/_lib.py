@@ -46,7 +46,9 @@ class MimoBwdFwdArgs(ctypes.Structure):
     ]
 
 
-EXPORTED = ("mimo_bwd_fwd", "mimo_bwd_fwd_workspace_size", "mimo_last_error", "mimo_abi_version")
+EXPORTED = ("mimo_bwd_fwd", "mimo_bwd_fwd_timed", "mimo_bwd_fwd_workspace_size", "mimo_last_error",
+            "mimo_abi_version")
+TIMED_EVENTS = 5
 
 _lib = None
 
@@ -63,6 +65,8 @@ def lib():
         argp = ctypes.POINTER(MimoBwdFwdArgs)
         L.mimo_bwd_fwd.argtypes = [argp, ctypes.c_void_p]
         L.mimo_bwd_fwd.restype = ctypes.c_int
+        L.mimo_bwd_fwd_timed.argtypes = [argp, ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+        L.mimo_bwd_fwd_timed.restype = ctypes.c_int
         L.mimo_bwd_fwd_workspace_size.argtypes = [argp, ctypes.POINTER(ctypes.c_size_t)]
         L.mimo_bwd_fwd_workspace_size.restype = ctypes.c_int
         L.mimo_last_error.argtypes = []

@@ -39,6 +39,12 @@
 //   inter = Q bf16(S)  sQ [i][n], sSbT [p][n]
 //   intra = A Psi      sA [i][j], sPsiT [p][j]  (contract over j)
 //   S' = kappa^T Psi   sKapT [n][i], sPsiT [p][i]
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
 #include "mimo_kernels.hpp"
 
 namespace mimo {
@@ -79,21 +85,29 @@ __global__ __launch_bounds__(256) void k_scan(Params p) {
     }
 }
 
+// dmimo = sum over segments of the partials, in segment order. Loads run
+// eight segments ahead of the additions.
+__device__ __forceinline__ float sum_segments(const float* part, long stride, int nseg) {
+    float s = 0.f;
+    int sg = 0;
+    for (; sg + 8 <= nseg; sg += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = part[(long)(sg + j) * stride];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += v[j];
+    }
+    for (; sg < nseg; ++sg) s += part[(long)sg * stride];
+    return s;
+}
+
 __global__ __launch_bounds__(256) void k_finish(Params p) {
     const long RP = (long)p.R * p.P;
     const long e = (long)blockIdx.x * 256 + threadIdx.x;
     if (e >= (long)p.B * p.H * RP) return;
     const long bh = e / RP, rp = e - bh * RP;
-    if (p.reduce_o) {
-        float s = 0.f;
-        for (int sg = 0; sg < p.nseg; ++sg) s += p.part_o[(bh * p.nseg + sg) * RP + rp];
-        p.dmimo_o[e] = s;
-    }
-    if (p.has_z) {
-        float s = 0.f;
-        for (int sg = 0; sg < p.nseg; ++sg) s += p.part_z[(bh * p.nseg + sg) * RP + rp];
-        p.dmimo_z[e] = s;
-    }
+    if (p.reduce_o) p.dmimo_o[e] = sum_segments(p.part_o + bh * p.nseg * RP + rp, RP, p.nseg);
+    if (p.has_z) p.dmimo_z[e] = sum_segments(p.part_z + bh * p.nseg * RP + rp, RP, p.nseg);
 }
 
 }  // namespace mimo
@@ -116,7 +130,7 @@ mimo_status fail(mimo_status s, const char* fmt, ...) {
 }
 
 struct Plan {
-    int RP, CT, MTm, NWm, MTa, NWa, NT, PT, Cp, W, nc, L, nseg;
+    int RP, CT, MT, NW, NT, PT, Cp, W, nc, L, nseg;
     size_t off_agg, off_decay, off_po, off_pz, ws_bytes;
     int lds_agg, lds_main;
 };
@@ -163,13 +177,13 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
     pl->W = (int)(N / rd);
     pl->NT = tile_size((int)N);
     pl->PT = tile_size((int)P);
-    pl->MTm = 16 * RP * CT < 32 ? 32 : 16 * RP * CT;
-    pl->NWm = (pl->MTm == 128 && pl->PT >= 64) ? 8 : 4;
-    pl->MTa = tile_size((int)R * pl->Cp);
-    pl->NWa = (pl->MTa == 128 && pl->PT >= 64) ? 8 : 4;
+    // must match Tile<RP, CT, NT, PT> in mimo_kernels.hpp
+    pl->MT = 16 * RP * CT < 32 ? 32 : 16 * RP * CT;
+    pl->NW = (pl->MT == 128 && pl->PT >= 64) ? 8 : 4;
     pl->nc = (int)((S + C - 1) / C);
-    // segments: aim at >= 4 workgroups per compute unit
-    const int64_t target = 1024;
+    // segments: about two workgroups per compute unit, so that every
+    // workgroup of the chunk kernel is resident at once
+    const int64_t target = 512;
     int64_t L = (pl->nc * B * H + target - 1) / target;
     if (L < 1) L = 1;
     if (L > pl->nc) L = pl->nc;
@@ -187,8 +201,8 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
     pl->off_pz = off;
     if (pl->nseg > 1 && has_z) off = align256(off + (size_t)B * H * pl->nseg * R * P * 4);
     pl->ws_bytes = off;
-    Lds lm = lds_layout(pl->MTm, pl->NT, pl->PT, (int)C, (int)R, pl->W, true);
-    Lds la = lds_layout(pl->MTa, pl->NT, pl->PT, (int)C, (int)R, pl->W, false);
+    Lds lm = lds_layout(pl->MT, pl->NT, pl->PT, (int)C, (int)R, (int)N, (int)P, pl->W, true);
+    Lds la = lds_layout(pl->MT, pl->NT, pl->PT, (int)C, (int)R, (int)N, (int)P, pl->W, false);
     pl->lds_main = lm.total;
     pl->lds_agg = la.total;
     // the token-tile reduction of the dmimo partials reuses LDS from offset 0
@@ -203,26 +217,19 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
 
 int tidx(int x) { return x == 32 ? 0 : (x == 64 ? 1 : 2); }
 
-kfn agg_kernel(int MT, int NT, int PT) {
-    const kfn* t = MT == 32 ? agg_table_mt32() : (MT == 64 ? agg_table_mt64() : agg_table_mt128());
-    return t[tidx(NT) * 3 + tidx(PT)];
-}
-
-kfn main_kernel(int RP, int CT, int NT, int PT) {
-    const kfn* t = nullptr;
+const Family* family(int RP, int CT) {
     switch (RP * 10 + CT) {
-        case 11: t = main_table_rp1_ct1(); break;
-        case 12: t = main_table_rp1_ct2(); break;
-        case 14: t = main_table_rp1_ct4(); break;
-        case 21: t = main_table_rp2_ct1(); break;
-        case 22: t = main_table_rp2_ct2(); break;
-        case 24: t = main_table_rp2_ct4(); break;
-        case 41: t = main_table_rp4_ct1(); break;
-        case 42: t = main_table_rp4_ct2(); break;
-        case 81: t = main_table_rp8_ct1(); break;
+        case 11: return family_rp1_ct1();
+        case 12: return family_rp1_ct2();
+        case 14: return family_rp1_ct4();
+        case 21: return family_rp2_ct1();
+        case 22: return family_rp2_ct2();
+        case 24: return family_rp2_ct4();
+        case 41: return family_rp4_ct1();
+        case 42: return family_rp4_ct2();
+        case 81: return family_rp8_ct1();
         default: return nullptr;
     }
-    return t[tidx(NT) * 3 + tidx(PT)];
 }
 
 std::mutex g_mu;
@@ -275,7 +282,7 @@ mimo_status mimo_bwd_fwd_workspace_size(const mimo_bwd_fwd_args* args, size_t* b
     return MIMO_OK;
 }
 
-mimo_status mimo_bwd_fwd(const mimo_bwd_fwd_args* a, void* stream) {
+static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* events) {
     g_err.clear();
     Plan pl;
     mimo_status s = make_plan(a, &pl);
@@ -300,7 +307,7 @@ mimo_status mimo_bwd_fwd(const mimo_bwd_fwd_args* a, void* stream) {
     Params p;
     p.B = (int)a->B; p.S = (int)a->S; p.H = (int)a->H; p.G = (int)a->G;
     p.R = (int)a->R; p.N = (int)a->N; p.P = (int)a->P; p.C = a->chunk_size;
-    p.Cp = pl.Cp; p.W = pl.W; p.nc = pl.nc; p.L = pl.L; p.nseg = pl.nseg; p.rd = a->rotary_dim_divisor;
+    p.W = pl.W; p.nc = pl.nc; p.L = pl.L; p.nseg = pl.nseg; p.rd = a->rotary_dim_divisor;
     p.reduce_o = reduce_o; p.has_z = has_z; p.has_d = a->d != nullptr; p.need_y = reduce_o || has_z;
     p.dout = a->dout; p.q = a->q; p.k = a->k; p.v = a->v; p.z = a->z; p.trap = a->trap;
     p.q_bias = a->q_bias; p.k_bias = a->k_bias; p.mimo_v = a->mimo_v; p.mimo_o = a->mimo_o;
@@ -318,26 +325,50 @@ mimo_status mimo_bwd_fwd(const mimo_bwd_fwd_args* a, void* stream) {
         p.part_z = a->dmimo_z;
     }
 
-    const kfn kmain = main_kernel(pl.RP, pl.CT, pl.NT, pl.PT);
-    const kfn kagg = agg_kernel(pl.MTa, pl.NT, pl.PT);
-    if (kmain == nullptr || kagg == nullptr) return fail(MIMO_ERR_UNSUPPORTED, "no kernel for this tile shape");
+    const Family* fam = family(pl.RP, pl.CT);
+    if (fam == nullptr) return fail(MIMO_ERR_UNSUPPORTED, "no kernel for this tile shape");
+    const kfn kmain = fam->main[tidx(pl.NT) * 3 + tidx(pl.PT)];
+    const kfn kagg = fam->agg[tidx(pl.NT) * 3 + tidx(pl.PT)];
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int BH = p.B * p.H;
+    auto mark = [&](int i) -> mimo_status {
+        if (events == nullptr) return MIMO_OK;
+        if (hipEventRecord(static_cast<hipEvent_t>(events[i]), st) != hipSuccess)
+            return fail(MIMO_ERR_HIP, "hipEventRecord failed");
+        return MIMO_OK;
+    };
+    if (events != nullptr)
+        for (int i = 0; i < MIMO_TIMED_EVENTS; ++i)
+            if (events[i] == nullptr) return fail(MIMO_ERR_VALUE, "timing event %d is NULL", i);
     if ((s = set_lds(kmain, pl.lds_main)) != MIMO_OK) return s;
+    if ((s = mark(0)) != MIMO_OK) return s;
     if (pl.nseg > 1) {
         if ((s = set_lds(kagg, pl.lds_agg)) != MIMO_OK) return s;
-        if ((s = launch(kagg, dim3(pl.nseg - 1, BH), dim3(pl.NWa * 64), pl.lds_agg, st, p)) != MIMO_OK) return s;
+        if ((s = launch(kagg, dim3(pl.nseg - 1, BH), dim3(pl.NW * 64), pl.lds_agg, st, p)) != MIMO_OK) return s;
+        if ((s = mark(1)) != MIMO_OK) return s;
         const int NP = p.N * p.P;
         if ((s = launch(k_scan, dim3((NP / 4 + 255) / 256, BH), dim3(256), 0, st, p)) != MIMO_OK) return s;
+    } else if ((s = mark(1)) != MIMO_OK) {
+        return s;
     }
-    if ((s = launch(kmain, dim3(pl.nseg, BH), dim3(pl.NWm * 64), pl.lds_main, st, p)) != MIMO_OK) return s;
+    if ((s = mark(2)) != MIMO_OK) return s;
+    if ((s = launch(kmain, dim3(pl.nseg, BH), dim3(pl.NW * 64), pl.lds_main, st, p)) != MIMO_OK) return s;
+    if ((s = mark(3)) != MIMO_OK) return s;
     if (pl.nseg > 1 && p.need_y) {
         const long tot = (long)BH * p.R * p.P;
         if ((s = launch(k_finish, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, p)) != MIMO_OK) return s;
     }
+    if ((s = mark(4)) != MIMO_OK) return s;
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return MIMO_OK;
+}
+
+mimo_status mimo_bwd_fwd(const mimo_bwd_fwd_args* a, void* stream) { return run(a, stream, nullptr); }
+
+mimo_status mimo_bwd_fwd_timed(const mimo_bwd_fwd_args* a, void* stream, void* const* events) {
+    if (events == nullptr) return fail(MIMO_ERR_VALUE, "events must not be NULL");
+    return run(a, stream, events);
 }
 
 }  // extern "C"

@@ -1,382 +1,550 @@
 // Device code of the mamba_mimo_bwd_fwd HIP library: parameters, LDS layout,
-// preparation stages and the two chunk kernels (templates over tile sizes).
-// Instantiated per tile height in inst_mt*.hip; the host side lives in
-// mimo_bwd_fwd.hip.
+// the per-chunk preparation stages and the two chunk kernels (templates over
+// the tile shape). Instantiated per tile family in tiles_rp*_ct*.hip; the
+// host side lives in mimo_bwd_fwd.hip.
+//
+// The arithmetic follows the Triton-Ascend mamba_mimo_bwd_fwd page's
+// BF16-boundary PyTorch reference: bf16 (round to nearest even) at the same
+// points, fp32 everywhere else. Two roundings are done by one
+// v_cvt_pk_bf16_f32 whenever two independent values are ready together.
 #pragma once
 #include <hip/hip_runtime.h>
 
-#include <atomic>
-#include <cstdarg>
 #include <cstdint>
-#include <cstdio>
-#include <cstring>
-#include <mutex>
-#include <string>
 
 #include "mimo_bwd_fwd.h"
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
-
 namespace mimo {
 
-constexpr int kMaxRows = 128;  // C*R rows of a chunk tile (padded)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// ---------------------------------------------------------------- scalar helpers
-// bf16 round-to-nearest-even of an fp32 value, returned as fp32.
-__device__ __forceinline__ float bfr(float x) { return static_cast<float>(static_cast<__bf16>(x)); }
+constexpr int kTok = 64;  // tokens per chunk tile (Cp) at most
+
+// ---------------------------------------------------------------- bf16 helpers
+// bf16(a) in the low and bf16(b) in the high half, round to nearest even.
+__device__ __forceinline__ unsigned pk2(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ float lo16(unsigned u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi16(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
+// round two fp32 values to bf16 in place
+__device__ __forceinline__ void rnd2(float& a, float& b) {
+    const unsigned u = pk2(a, b);
+    a = lo16(u);
+    b = hi16(u);
+}
+__device__ __forceinline__ float rnd1(float a) { return lo16(pk2(a, 0.f)); }
 __device__ __forceinline__ float bf2f(unsigned short u) { return __uint_as_float(static_cast<unsigned>(u) << 16); }
-__device__ __forceinline__ unsigned short f2bf(float x) {
-    return __builtin_bit_cast(unsigned short, static_cast<__bf16>(x));
-}
-__device__ __forceinline__ float bfv(const __bf16 x) { return static_cast<float>(x); }
-// precise logistic function for per-token scalars
-__device__ __forceinline__ float sigmoid_precise(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ unsigned short f2bf(float x) { return static_cast<unsigned short>(pk2(x, 0.f)); }
 
-__device__ __forceinline__ f32x4 mfma(const bf16x8 a, const bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
 }
+// a.lo*b.lo + a.hi*b.hi + c (bf16 pairs, fp32 accumulate)
+__device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+// logistic function: precise for the per-token controls, fast for the gate
+__device__ __forceinline__ float sigmoid_precise(float x) { return 1.0f / (1.0f + expf(-x)); }
+__device__ __forceinline__ float sigmoid_fast(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_ld(const void* p) { return *reinterpret_cast<const T*>(p); }
+template <typename T>
+__device__ __forceinline__ void lds_st(void* p, T v) { *reinterpret_cast<T*>(p) = v; }
 
 // ---------------------------------------------------------------- parameters
 struct Params {
-    int B, S, H, G, R, N, P, C, Cp, W, nc, L, nseg, rd;
+    int B, S, H, G, R, N, P, C, W, nc, L, nseg, rd;
     int reduce_o, has_z, has_d, need_y;
     const unsigned short *dout, *q, *k, *v, *z, *trap;
-    const float *q_bias, *k_bias, *mimo_v, *mimo_o, *mimo_z, *angles, *da_cs, *da_cs_rev, *dt, *d,
-        *segsum;
+    const float *q_bias, *k_bias, *mimo_v, *mimo_o, *mimo_z, *angles, *da_cs, *da_cs_rev, *dt, *d, *segsum;
     float *dmimo_o, *dmimo_z;
     unsigned short *states, *dz, *qk_dot;
-    float *agg;     // [B*H][nseg-1][N*P]: segment state increments, then segment entry states
-    float *decay;   // [B*H][nseg]: product of the chunk decays of each segment
-    float *part_o;  // [B*H][nseg][R*P] partial dmimo_o (== dmimo_o when nseg == 1)
-    float *part_z;  // [B*H][nseg][R*P] partial dmimo_z
+    float* agg;     // [B*H][nseg-1][N*P]: segment state increments, then segment entry states
+    float* decay;   // [B*H][nseg]: product of the chunk decays of each segment
+    float* part_o;  // [B*H][nseg][R*P] partial dmimo_o (== dmimo_o when nseg == 1)
+    float* part_z;  // [B*H][nseg][R*P] partial dmimo_z
 };
 
-// LDS carve-up shared by host and device. Element pitches keep rows 16-byte
-// aligned and add 8 bf16 of padding per row.
+// ---------------------------------------------------------------- tile family
+// RP: rank count rounded up to a power of two (ranks >= R are zero rows);
+// CT: 16-token tiles per rank (Cp = 16*CT >= C); NT / PT: state and value
+// dimensions rounded up to 32, 64 or 128. Rows of a chunk tile are
+// rank-major, row = r*Cp + t.
+template <int RP, int CT, int NT, int PT>
+struct Tile {
+    static constexpr int Cp = 16 * CT;
+    static constexpr int MT = (RP * Cp < 32) ? 32 : RP * Cp;   // rows (MFMA K-steps of 32)
+    static constexpr int NW = (MT == 128 && PT >= 64) ? 8 : 4;  // waves per workgroup
+    static constexpr int NTHR = NW * 64;
+    static constexpr int LDQ = NT + 8;                          // pitch of [*][NT] bf16 rows
+    static constexpr int LDA = MT + 8;                          // pitch of [*][MT] bf16 rows
+    static constexpr int PTT = PT / 16;
+    static constexpr int QK_IT = (MT * (NT / 16) + NTHR - 1) / NTHR;      // q/k items per thread
+    static constexpr int PSI_IT = (Cp * (PT / 8) + NTHR - 1) / NTHR;      // v items per thread
+    static constexpr int ANG_IT = (Cp * (NT / 2) + NTHR - 1) / NTHR;      // angle items per thread
+    static constexpr int SEG_IT = (Cp * Cp + NTHR - 1) / NTHR;            // segsum items per thread
+    static constexpr int ST = (NT / 16) * PTT;                             // state tiles
+    static constexpr int STW = (ST + NW - 1) / NW;
+    static constexpr int MTT = MT / 16;
+    static constexpr int AT = MTT * MTT;                                   // causal-block tiles
+    static constexpr int ATW = (AT + NW - 1) / NW;
+    static constexpr int NPAIRS = CT * PTT;                                // (token tile, value tile)
+    static constexpr int PW = (NPAIRS + NW - 1) / NW;                      // pairs per wave
+};
+
+// LDS carve-up (byte offsets), shared by host and device.
 struct Lds {
-    int ldq;  // pitch of [*][NT] rows (sQ, sK, sSbT)
-    int lda;  // pitch of [*][MT] rows (sA, sKapT, sPsiT)
-    int r1, r2, r3, r4, sm1, sqk, sc, total;  // byte offsets / size
+    int r1;   // bf16 [MT][LDQ] q (main) | [MT][LDA] causal block | [NT][LDA] kappa^T
+    int r2;   // bf16 [MT][LDQ] k (main only)
+    int r3;   // bf16 [PT][LDA] Psi^T
+    int r4;   // bf16 [PT][LDQ] bf16(state)^T (main only)
+    int cs;   // fp32 [2][C][W] cos, sin
+    int se;   // fp32 [C][C] exp(segsum) (main only)
+    int qk;   // fp32 [C][R*R+1] qk_dot, one pad word per token (main only)
+    int sc;   // fp32 [5][kTok] token scalars + chunk decay
+    int tb;   // bf16 tables: q_bias [R][N], k_bias [R][N], mimo_v [R][P]
+    int total;
 };
 
 __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
 
-__host__ __device__ inline Lds lds_layout(int MT, int NT, int PT, int C, int R, int W, bool main) {
+__host__ __device__ inline Lds lds_layout(int MT, int NT, int PT, int C, int R, int N, int P, int W, bool main) {
+    const int ldq = NT + 8, lda = MT + 8;
+    int r1 = NT * lda;
+    if (main && MT * ldq > r1) r1 = MT * ldq;
+    if (main && MT * lda > r1) r1 = MT * lda;
     Lds s;
-    s.ldq = NT + 8;
-    s.lda = MT + 8;
-    int r1 = MT * s.ldq;
-    if (MT * s.lda > r1) r1 = MT * s.lda;
-    if (NT * s.lda > r1) r1 = NT * s.lda;
     int off = 0;
-    s.r1 = off;
-    off += align16(r1 * 2);
-    s.r2 = off;
-    if (main) off += align16(MT * s.ldq * 2);
-    s.r3 = off;
-    off += align16(PT * s.lda * 2);
-    s.r4 = off;
-    if (main) off += align16(PT * s.ldq * 2);
-    int sm1 = 2 * C * W;
-    if (main && C * C > sm1) sm1 = C * C;
-    s.sm1 = off;
-    off += align16(sm1 * 4);
-    s.sqk = off;
-    if (main) off += align16(C * R * R * 4);
-    s.sc = off;
-    off += align16((5 * kMaxRows + 8) * 4);
+    s.r1 = off; off += align16(r1 * 2);
+    s.r2 = off; if (main) off += align16(MT * ldq * 2);
+    s.r3 = off; off += align16(PT * lda * 2);
+    s.r4 = off; if (main) off += align16(PT * ldq * 2);
+    s.cs = off; off += align16(2 * C * W * 4);
+    s.se = off; if (main) off += align16(C * C * 4);
+    s.qk = off; if (main) off += align16(C * (R * R + 1) * 4);
+    s.sc = off; off += align16((5 * kTok + 4) * 4);
+    s.tb = off; off += align16((2 * R * N + R * P) * 2);
     s.total = off;
     return s;
 }
 
-// Per-token scalars of one chunk (tokens t < Cp; zero beyond the chunk's
-// real tokens) and the cos/sin table of the rotation, [C][W] each.
-// gamma_t = bf16(dt_t) * sigmoid(trap_t)                        (fp32)
+// ---------------------------------------------------------------- per-chunk inputs
+// Everything one chunk reads from global memory, loaded in one go at the top
+// of the chunk so that a single memory latency is paid per chunk.
+template <int RP, int CT, int NT, int PT, bool MAIN>
+struct ChunkIn {
+    using T = Tile<RP, CT, NT, PT>;
+    u32x4 q0[T::QK_IT], q1[T::QK_IT], k0[T::QK_IT], k1[T::QK_IT];   // columns col0.., N/2+col0..
+    u32x4 v[T::PSI_IT];
+    float dt0, dt1, tr0, tr1, cs, rev, dlast;
+    float ang[T::ANG_IT];
+    float seg[MAIN ? T::SEG_IT : 1];
+};
+
+// Per-thread item coordinates, fixed for the whole kernel.
+template <int RP, int CT, int NT, int PT>
+struct Items {
+    using T = Tile<RP, CT, NT, PT>;
+    int qk_row[T::QK_IT];   // tile row (-1: no item)
+    int qk_col[T::QK_IT];   // first column of the 8-column group in the first half
+    int qk_off[T::QK_IT];   // element offset of (t, r, g, col) inside a chunk's q/k block
+    int ang_t[T::ANG_IT], ang_off[T::ANG_IT];   // token, element offset inside a chunk (-1: none)
+};
+
+// ROWS_FAST: consecutive threads take consecutive tile rows (the chunk-aggregate
+// kernel writes kappa^T transposed straight from registers); otherwise the
+// 8-column groups of one row are adjacent.
+template <int RP, int CT, int NT, int PT, bool ROWS_FAST = false>
+__device__ __forceinline__ void make_items(const Params& p, int g, Items<RP, CT, NT, PT>& it) {
+    using T = Tile<RP, CT, NT, PT>;
+    const int tid = threadIdx.x;
+    const int ng = p.N / 16;
+#pragma unroll
+    for (int j = 0; j < T::QK_IT; ++j) {
+        const int e = tid + j * T::NTHR;
+        it.qk_row[j] = -1;
+        it.qk_col[j] = 0;
+        it.qk_off[j] = 0;
+        if (e < T::MT * ng) {
+            const int i = ROWS_FAST ? e % T::MT : e / ng;
+            const int gg = ROWS_FAST ? e / T::MT : e - i * ng;
+            const int r = i / T::Cp, t = i % T::Cp;
+            it.qk_row[j] = i;
+            it.qk_col[j] = 8 * gg;
+            it.qk_off[j] = ((t * p.R + r) * p.G + g) * p.N + 8 * gg;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < T::ANG_IT; ++j) {
+        const int e = tid + j * T::NTHR;
+        it.ang_t[j] = -1;
+        it.ang_off[j] = 0;
+        if (e < p.C * p.W) {
+            const int t = e / p.W, n = e - t * p.W;
+            it.ang_t[j] = t;
+            it.ang_off[j] = t * p.H * p.W + n;
+        }
+    }
+}
+
+// Global loads of chunk c (c0 = first token, cl = real tokens).
+template <int RP, int CT, int NT, int PT, bool MAIN>
+__device__ __forceinline__ void load_chunk(const Params& p, const Items<RP, CT, NT, PT>& it, int b, int h, int bh,
+                                           int c, int c0, int cl, ChunkIn<RP, CT, NT, PT, MAIN>& in) {
+    using T = Tile<RP, CT, NT, PT>;
+    const int tid = threadIdx.x;
+    const int R = p.R;
+    const unsigned short* qb = p.q + (long)(b * p.S + c0) * R * p.G * p.N;
+    const unsigned short* kb = p.k + (long)(b * p.S + c0) * R * p.G * p.N;
+#pragma unroll
+    for (int j = 0; j < T::QK_IT; ++j) {
+        const int i = it.qk_row[j];
+        const int r = i / T::Cp, t = i % T::Cp;
+        if (i >= 0 && r < R && t < cl) {
+            const int o = it.qk_off[j];
+            if (MAIN) {
+                in.q0[j] = *reinterpret_cast<const u32x4*>(qb + o);
+                in.q1[j] = *reinterpret_cast<const u32x4*>(qb + o + p.N / 2);
+            }
+            in.k0[j] = *reinterpret_cast<const u32x4*>(kb + o);
+            in.k1[j] = *reinterpret_cast<const u32x4*>(kb + o + p.N / 2);
+        }
+    }
+    const unsigned short* vb = p.v + ((long)(b * p.S + c0) * p.H + h) * p.P;
+#pragma unroll
+    for (int j = 0; j < T::PSI_IT; ++j) {
+        const int e = tid + j * T::NTHR;
+        const int t = e % T::Cp, pc = (e / T::Cp) * 8;
+        if (e < T::Cp * (PT / 8) && t < cl && pc < p.P)
+            in.v[j] = *reinterpret_cast<const u32x4*>(vb + (long)t * p.H * p.P + pc);
+    }
+    const long tok = (long)bh * p.S + c0;
+    if (tid < cl) {
+        in.dt0 = p.dt[tok + tid];
+        in.tr0 = bf2f(p.trap[tok + tid]);
+        in.rev = p.da_cs_rev[tok + tid];
+        if (MAIN) in.cs = p.da_cs[tok + tid];
+        if (c0 + tid + 1 < p.S) {
+            in.dt1 = p.dt[tok + tid + 1];
+            in.tr1 = bf2f(p.trap[tok + tid + 1]);
+        }
+    }
+    if (tid == 0) in.dlast = p.da_cs[tok + cl - 1];
+    const float* ab = p.angles + ((long)(b * p.S + c0) * p.H + h) * p.W;
+#pragma unroll
+    for (int j = 0; j < T::ANG_IT; ++j)
+        if (it.ang_t[j] >= 0 && it.ang_t[j] < cl) in.ang[j] = ab[it.ang_off[j]];
+    if (MAIN && p.need_y) {
+        const float* sb = p.segsum + ((long)bh * p.nc + c) * p.C * p.C;
+#pragma unroll
+        for (int j = 0; j < T::SEG_IT; ++j) {
+            const int e = tid + j * T::NTHR;
+            if (e < p.C * p.C) in.seg[j] = sb[e];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- LDS staging of chunk inputs
+// For tile families whose LDS leaves room for two workgroups per compute unit,
+// the inputs of chunk c+1 are fetched straight into a staging area of LDS
+// (global_load_lds: lane l of a wave writes its 4 or 16 bytes at base + 4l or
+// base + 16l; a 2-byte load fills the low half of the lane's 4-byte slot)
+// while chunk c computes. Each thread later reads back exactly the slots it
+// fetched, so only its own outstanding loads have to be waited for.
+template <int RP, int CT, int NT, int PT, bool MAIN>
+struct Stage {
+    using T = Tile<RP, CT, NT, PT>;
+    static constexpr int NQ = MAIN ? 4 : 2;   // q0, q1, k0, k1 (or k0, k1)
+    static constexpr int QK = 0;
+    static constexpr int V = QK + T::QK_IT * NQ * T::NTHR * 16;
+    static constexpr int ANG = V + T::PSI_IT * T::NTHR * 16;
+    static constexpr int SEG = ANG + T::ANG_IT * T::NTHR * 4;
+    static constexpr int SCAL = SEG + (MAIN ? T::SEG_IT * T::NTHR * 4 : 0);   // [7][64] dwords, wave 0
+    static constexpr int BYTES = SCAL + 7 * 64 * 4;
+    // dynamic LDS of the family at its largest chunk (C = Cp, R = RP, N = NT, P = PT)
+    static constexpr int ldq = NT + 8, lda = T::MT + 8;
+    static constexpr int r1 = (MAIN ? ((T::MT * ldq > NT * lda ? T::MT * ldq : NT * lda) > T::MT * lda
+                                           ? (T::MT * ldq > NT * lda ? T::MT * ldq : NT * lda)
+                                           : T::MT * lda)
+                                     : NT * lda);
+    static constexpr int DYN = 2 * r1 + (MAIN ? 2 * T::MT * ldq : 0) + 2 * PT * lda + (MAIN ? 2 * PT * ldq : 0) +
+                               8 * T::Cp * (NT / 2) + (MAIN ? 4 * T::Cp * T::Cp + 4 * T::Cp * (RP * RP + 1) : 0) +
+                               4 * (5 * kTok + 4) + 2 * (2 * RP * NT + RP * PT) + 256;
+    static constexpr bool ON = DYN + BYTES <= 80 * 1024;
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void* src, unsigned char* dst_wave) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, unsigned char* dst_wave) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 4, 0, 0);
+}
+__device__ __forceinline__ void dma2(const void* src, unsigned char* dst_wave) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 2, 0, 0);
+}
+
+// Issue the staging loads of chunk c (first token c0, cl real tokens).
+template <int RP, int CT, int NT, int PT, bool MAIN>
+__device__ __forceinline__ void prefetch_chunk(const Params& p, const Items<RP, CT, NT, PT>& it, int b, int h, int bh,
+                                               int c, int c0, int cl, unsigned char* stg) {
+    using T = Tile<RP, CT, NT, PT>;
+    using SG = Stage<RP, CT, NT, PT, MAIN>;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int R = p.R;
+    const unsigned short* qb = p.q + (long)(b * p.S + c0) * R * p.G * p.N;
+    const unsigned short* kb = p.k + (long)(b * p.S + c0) * R * p.G * p.N;
+#pragma unroll
+    for (int j = 0; j < T::QK_IT; ++j) {
+        const int i = it.qk_row[j];
+        const int r = i / T::Cp, t = i % T::Cp;
+        unsigned char* d = stg + SG::QK + (j * SG::NQ) * T::NTHR * 16 + wave * 1024;
+        if (i >= 0 && r < R && t < cl) {
+            const int o = it.qk_off[j];
+            if (MAIN) {
+                dma16(qb + o, d);
+                dma16(qb + o + p.N / 2, d + T::NTHR * 16);
+                dma16(kb + o, d + 2 * T::NTHR * 16);
+                dma16(kb + o + p.N / 2, d + 3 * T::NTHR * 16);
+            } else {
+                dma16(kb + o, d);
+                dma16(kb + o + p.N / 2, d + T::NTHR * 16);
+            }
+        }
+    }
+    const unsigned short* vb = p.v + ((long)(b * p.S + c0) * p.H + h) * p.P;
+#pragma unroll
+    for (int j = 0; j < T::PSI_IT; ++j) {
+        const int e = tid + j * T::NTHR;
+        const int t = e % T::Cp, pc = (e / T::Cp) * 8;
+        if (e < T::Cp * (PT / 8) && t < cl && pc < p.P)
+            dma16(vb + (long)t * p.H * p.P + pc, stg + SG::V + j * T::NTHR * 16 + wave * 1024);
+    }
+    const float* ab = p.angles + ((long)(b * p.S + c0) * p.H + h) * p.W;
+#pragma unroll
+    for (int j = 0; j < T::ANG_IT; ++j)
+        if (it.ang_t[j] >= 0 && it.ang_t[j] < cl) dma4(ab + it.ang_off[j], stg + SG::ANG + j * T::NTHR * 4 + wave * 256);
+    if (MAIN && p.need_y) {
+        const float* sb = p.segsum + ((long)bh * p.nc + c) * p.C * p.C;
+#pragma unroll
+        for (int j = 0; j < T::SEG_IT; ++j) {
+            const int e = tid + j * T::NTHR;
+            if (e < p.C * p.C) dma4(sb + e, stg + SG::SEG + j * T::NTHR * 4 + wave * 256);
+        }
+    }
+    if (wave == 0) {
+        const long tok = (long)bh * p.S + c0;
+        unsigned char* sc = stg + SG::SCAL;
+        if (tid < cl) {
+            dma4(p.dt + tok + tid, sc);
+            dma2(p.trap + tok + tid, sc + 2 * 256);
+            dma4(p.da_cs_rev + tok + tid, sc + 5 * 256);
+            if (MAIN) dma4(p.da_cs + tok + tid, sc + 4 * 256);
+            if (c0 + tid + 1 < p.S) {
+                dma4(p.dt + tok + tid + 1, sc + 1 * 256);
+                dma2(p.trap + tok + tid + 1, sc + 3 * 256);
+            }
+        }
+        if (tid == 0) dma4(p.da_cs + tok + cl - 1, sc + 6 * 256);
+    }
+}
+
+// Copy this thread's staged slots of the current chunk into registers.
+template <int RP, int CT, int NT, int PT, bool MAIN>
+__device__ __forceinline__ void read_stage(const unsigned char* stg, ChunkIn<RP, CT, NT, PT, MAIN>& in) {
+    using T = Tile<RP, CT, NT, PT>;
+    using SG = Stage<RP, CT, NT, PT, MAIN>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < T::QK_IT; ++j) {
+        const unsigned char* d = stg + SG::QK + (j * SG::NQ) * T::NTHR * 16 + tid * 16;
+        if (MAIN) {
+            in.q0[j] = lds_ld<u32x4>(d);
+            in.q1[j] = lds_ld<u32x4>(d + T::NTHR * 16);
+            in.k0[j] = lds_ld<u32x4>(d + 2 * T::NTHR * 16);
+            in.k1[j] = lds_ld<u32x4>(d + 3 * T::NTHR * 16);
+        } else {
+            in.k0[j] = lds_ld<u32x4>(d);
+            in.k1[j] = lds_ld<u32x4>(d + T::NTHR * 16);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < T::PSI_IT; ++j) in.v[j] = lds_ld<u32x4>(stg + SG::V + j * T::NTHR * 16 + tid * 16);
+#pragma unroll
+    for (int j = 0; j < T::ANG_IT; ++j) in.ang[j] = lds_ld<float>(stg + SG::ANG + j * T::NTHR * 4 + tid * 4);
+    if (MAIN) {
+#pragma unroll
+        for (int j = 0; j < (MAIN ? T::SEG_IT : 0); ++j)
+            in.seg[j] = lds_ld<float>(stg + SG::SEG + j * T::NTHR * 4 + tid * 4);
+    }
+    if (tid < 64) {
+        const unsigned char* sc = stg + SG::SCAL + tid * 4;
+        in.dt0 = lds_ld<float>(sc);
+        in.dt1 = lds_ld<float>(sc + 256);
+        in.tr0 = bf2f(static_cast<unsigned short>(lds_ld<unsigned>(sc + 2 * 256)));
+        in.tr1 = bf2f(static_cast<unsigned short>(lds_ld<unsigned>(sc + 3 * 256)));
+        if (MAIN) in.cs = lds_ld<float>(sc + 4 * 256);
+        in.rev = lds_ld<float>(sc + 5 * 256);
+        in.dlast = lds_ld<float>(stg + SG::SCAL + 6 * 256);
+    }
+}
+
+// Phase 0: token scalars, cos/sin, exp(segsum) into LDS.
+// gamma_t = bf16(dt_t) * sigmoid(trap_t)                      (fp32)
 // beta_t  = bf16(bf16(dt_{t+1}) * sigmoid(-trap_{t+1})), 0 at the last token
 // factor_t = bf16(gamma_t + beta_t)
-template <int NTHR>
-__device__ __forceinline__ void prep_scalars(const Params& p, int bh, int b, int h, int c0, int cl,
-                                             float* sc, float* scs, bool main) {
+template <int RP, int CT, int NT, int PT, bool MAIN>
+__device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, PT>& it, int c0, int cl,
+                                       const ChunkIn<RP, CT, NT, PT, MAIN>& in, unsigned char* smem, const Lds& L) {
+    using T = Tile<RP, CT, NT, PT>;
     const int tid = threadIdx.x;
-    float* s_ecs = sc;
-    float* s_gam = sc + kMaxRows;
-    float* s_erev = sc + 2 * kMaxRows;
-    float* s_fac = sc + 3 * kMaxRows;
-    for (int t = tid; t < p.Cp; t += NTHR) {
+    float* sc = reinterpret_cast<float*>(smem + L.sc);
+    if (tid < T::Cp) {
         float gam = 0.f, fac = 0.f, ecs = 0.f, erev = 0.f;
-        if (t < cl) {
-            const long idx = (long)bh * p.S + c0 + t;
-            const float dtb = bfr(p.dt[idx]);
-            gam = dtb * sigmoid_precise(bf2f(p.trap[idx]));
+        if (tid < cl) {
+            gam = rnd1(in.dt0) * sigmoid_precise(in.tr0);
             float beta = 0.f;
-            if (c0 + t + 1 < p.S) beta = bfr(bfr(p.dt[idx + 1]) * sigmoid_precise(-bf2f(p.trap[idx + 1])));
-            fac = bfr(gam + beta);
-            erev = expf(p.da_cs_rev[idx]);
-            if (main) ecs = expf(p.da_cs[idx]);
+            if (c0 + tid + 1 < p.S) beta = rnd1(rnd1(in.dt1) * sigmoid_precise(-in.tr1));
+            fac = rnd1(gam + beta);
+            erev = expf(in.rev);
+            if (MAIN) ecs = expf(in.cs);
         }
-        s_ecs[t] = ecs;
-        s_gam[t] = gam;
-        s_erev[t] = erev;
-        s_fac[t] = fac;
+        sc[tid] = ecs;
+        sc[kTok + tid] = gam;
+        sc[2 * kTok + tid] = erev;
+        sc[3 * kTok + tid] = fac;
     }
-    if (tid == 0) sc[4 * kMaxRows] = expf(p.da_cs[(long)bh * p.S + c0 + cl - 1]);
+    if (tid == 0) sc[4 * kTok] = expf(in.dlast);
+    float* scs = reinterpret_cast<float*>(smem + L.cs);
     const int CW = p.C * p.W;
-    for (int e = tid; e < CW; e += NTHR) {
-        const int t = e / p.W, n = e - t * p.W;
-        float cs = 0.f, sn = 0.f;
-        if (t < cl) {
-            const float th = p.angles[((long)(b * p.S + c0 + t) * p.H + h) * p.W + n];
-            sincosf(th, &sn, &cs);
+#pragma unroll
+    for (int j = 0; j < T::ANG_IT; ++j) {
+        const int e = tid + j * T::NTHR;
+        if (e < CW) {
+            float s = 0.f, co = 0.f;
+            if (it.ang_t[j] < cl) sincosf(in.ang[j], &s, &co);
+            scs[e] = co;
+            scs[CW + e] = s;
         }
-        scs[e] = cs;
-        scs[CW + e] = sn;
+    }
+    if (MAIN && p.need_y) {
+        float* se = reinterpret_cast<float*>(smem + L.se);
+#pragma unroll
+        for (int j = 0; j < T::SEG_IT; ++j) {
+            const int e = tid + j * T::NTHR;
+            if (e < p.C * p.C) se[e] = expf(in.seg[j]);
+        }
     }
 }
 
-// Load 8 consecutive bf16 (16 bytes) from global memory.
-__device__ __forceinline__ u16x8 ld8(const unsigned short* ptr) { return *reinterpret_cast<const u16x8*>(ptr); }
-
-// Biased, bf16-rounded values of one 8-column group: bf16(x + bf16(bias)).
-__device__ __forceinline__ void bias8(const u16x8 x, const float* bias, float out[8]) {
-    const float4 b0 = *reinterpret_cast<const float4*>(bias);
-    const float4 b1 = *reinterpret_cast<const float4*>(bias + 4);
-    const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+// bias + round of one 8-column group: bf16(x + bf16(bias)), packed
+__device__ __forceinline__ u32x4 add_bias(u32x4 x, u32x4 bias) {
+    u32x4 o;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = bfr(bf2f(x[e]) + bfr(bb[e]));
+    for (int d = 0; d < 4; ++d) o[d] = pk2(lo16(x[d]) + lo16(bias[d]), hi16(x[d]) + hi16(bias[d]));
+    return o;
 }
 
-__device__ __forceinline__ void st8(__bf16* dst, const float v[8]) {
-    bf16x8 o;
+// Rotate the column pairs (col0 + e, N/2 + col0 + e) of one group: a is the
+// first-half group, e the second; both packed bf16, rounded after rotation.
+__device__ __forceinline__ void rotate_group(u32x4& a, u32x4& e, int col0, int W, const float* cs, const float* sn) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(v[e]);
-    *reinterpret_cast<bf16x8*>(dst) = o;
-}
-
-__device__ __forceinline__ void st8_zero(__bf16* dst) {
-    *reinterpret_cast<u16x8*>(dst) = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-}
-
-// Rotation of one column pair group: columns n (first half) and N/2 + n.
-__device__ __forceinline__ void rotate8(float a[8], float e[8], int col0, int W, const float* cs,
-                                        const float* sn) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int n = col0 + j;
+    for (int d = 0; d < 4; ++d) {
+        const int n = col0 + 2 * d;
         if (n < W) {
-            const float c = cs[n], s = sn[n];
-            const float x = a[j], y = e[j];
-            a[j] = bfr(__fmul_rn(c, x) - __fmul_rn(s, y));
-            e[j] = bfr(__fmul_rn(s, x) + __fmul_rn(c, y));
+            const float x0 = lo16(a[d]), x1 = hi16(a[d]);
+            const float y0 = lo16(e[d]), y1 = hi16(e[d]);
+            const float c0 = cs[n], c1 = cs[n + 1], s0 = sn[n], s1 = sn[n + 1];
+            a[d] = pk2(__fmul_rn(c0, x0) - __fmul_rn(s0, y0), __fmul_rn(c1, x1) - __fmul_rn(s1, y1));
+            e[d] = pk2(__fmul_rn(s0, x0) + __fmul_rn(c0, y0), __fmul_rn(s1, x1) + __fmul_rn(c1, y1));
         }
     }
 }
 
-// ---------------------------------------------------------------- Psi^T fill
-// sPsiT[p][r*Cp + t] = bf16(v[t,p] * bf16(mimo_v[r,p])), zero for padded
-// tokens, ranks, rows and value columns.
-template <int MT, int PT, int NTHR>
-__device__ __forceinline__ void fill_psi(const Params& p, int b, int h, int c0, int cl, __bf16* sPsiT,
-                                         int lda) {
+__device__ __forceinline__ u32x4 scale_group(u32x4 a, float f) {
+    u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] = pk2(lo16(a[d]) * f, hi16(a[d]) * f);
+    return o;
+}
+
+// Psi^T: sPsiT[p][r*Cp + t] = bf16(v[t,p] * bf16(mimo_v[r,p])), zero for padded tokens and columns.
+template <int RP, int CT, int NT, int PT, bool MAIN>
+__device__ __forceinline__ void fill_psi(const Params& p, int cl, const ChunkIn<RP, CT, NT, PT, MAIN>& in,
+                                         unsigned char* smem, const Lds& L) {
+    using T = Tile<RP, CT, NT, PT>;
     const int tid = threadIdx.x;
-    constexpr int P8 = PT / 8;
-    const int nit = p.Cp * P8;
-    for (int it = tid; it < nit; it += NTHR) {
-        const int t = it / P8, pc = (it - t * P8) * 8;
+    unsigned short* sPsiT = reinterpret_cast<unsigned short*>(smem + L.r3);
+    const unsigned short* smv = reinterpret_cast<const unsigned short*>(smem + L.tb) + 2 * p.R * p.N;
+#pragma unroll
+    for (int j = 0; j < T::PSI_IT; ++j) {
+        const int e = tid + j * T::NTHR;
+        if (e >= T::Cp * (PT / 8)) continue;
+        const int t = e % T::Cp, pc = (e / T::Cp) * 8;   // consecutive threads: consecutive tokens
         const bool real = t < cl && pc < p.P;
-        float vv[8];
-        if (real) {
-            const u16x8 x = ld8(p.v + ((long)(b * p.S + c0 + t) * p.H + h) * p.P + pc);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vv[e] = bf2f(x[e]);
-        }
         for (int r = 0; r < p.R; ++r) {
-            float mv[8];
+            unsigned short* dst = sPsiT + pc * T::LDA + r * T::Cp + t;
             if (real) {
-                const float* src = p.mimo_v + ((long)h * p.R + r) * p.P + pc;
-                const float4 m0 = *reinterpret_cast<const float4*>(src);
-                const float4 m1 = *reinterpret_cast<const float4*>(src + 4);
-                mv[0] = m0.x; mv[1] = m0.y; mv[2] = m0.z; mv[3] = m0.w;
-                mv[4] = m1.x; mv[5] = m1.y; mv[6] = m1.z; mv[7] = m1.w;
-            }
-            const int col = r * p.Cp + t;
+                const u32x4 mv = lds_ld<u32x4>(smv + r * p.P + pc);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sPsiT[(pc + e) * lda + col] = static_cast<__bf16>(real ? bfr(vv[e] * bfr(mv[e])) : 0.f);
+                for (int d = 0; d < 4; ++d) {
+                    const unsigned u = pk2(lo16(in.v[j][d]) * lo16(mv[d]), hi16(in.v[j][d]) * hi16(mv[d]));
+                    dst[(2 * d) * T::LDA] = static_cast<unsigned short>(u);
+                    dst[(2 * d + 1) * T::LDA] = static_cast<unsigned short>(u >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int d = 0; d < 8; ++d) dst[d * T::LDA] = 0;
+            }
         }
     }
-    // rows of the tile beyond R*Cp
-    const int used = p.R * p.Cp;
-    const int pad = MT - used;
-    if (pad > 0) {
-        for (int it = tid; it < PT * pad; it += NTHR) {
-            const int pp = it / pad, i = used + (it - pp * pad);
-            sPsiT[pp * lda + i] = static_cast<__bf16>(0.f);
-        }
+}
+
+// Tables filled once per workgroup: bf16(q_bias), bf16(k_bias), bf16(mimo_v) for head h,
+// and the zero padding of Psi^T that no chunk overwrites.
+template <int RP, int CT, int NT, int PT>
+__device__ __forceinline__ void fill_tables(const Params& p, int h, unsigned char* smem, const Lds& L) {
+    using T = Tile<RP, CT, NT, PT>;
+    const int tid = threadIdx.x;
+    unsigned short* tb = reinterpret_cast<unsigned short*>(smem + L.tb);
+    const int RN = p.R * p.N, RPn = p.R * p.P;
+    for (int e = tid; e < RN; e += T::NTHR) {
+        tb[e] = f2bf(p.q_bias[(long)h * RN + e]);
+        tb[RN + e] = f2bf(p.k_bias[(long)h * RN + e]);
+    }
+    for (int e = tid; e < RPn; e += T::NTHR) tb[2 * RN + e] = f2bf(p.mimo_v[(long)h * RPn + e]);
+    unsigned short* sPsiT = reinterpret_cast<unsigned short*>(smem + L.r3);
+    const int used = p.R * T::Cp, pad = T::MT - used;
+    for (int e = tid; e < PT * pad; e += T::NTHR) {
+        const int pp = e / pad, i = used + e % pad;
+        sPsiT[pp * T::LDA + i] = 0;
     }
 }
 
 // ---------------------------------------------------------------- segment aggregate
 // U_s = state added by segment s from a zero start: U <- U*exp(da_cs[last]) + kappa^T Psi
-// per chunk. Also the product of the chunk decays.
-template <int MT, int NT, int PT, int NW>
-__global__ __launch_bounds__(NW * 64) void k_agg(Params p) {
-    constexpr int NTHR = NW * 64;
-    constexpr int NG_MAX = NT / 16;
-    constexpr int QK_IT = (MT * NG_MAX + NTHR - 1) / NTHR;
-    constexpr int ST = (NT / 16) * (PT / 16);
-    constexpr int STW = (ST + NW - 1) / NW;
-    extern __shared__ __align__(16) unsigned char smem[];
-    const Lds L = lds_layout(MT, NT, PT, p.C, p.R, p.W, false);
-    __bf16* sKapT = reinterpret_cast<__bf16*>(smem + L.r1);
-    __bf16* sPsiT = reinterpret_cast<__bf16*>(smem + L.r3);
-    float* scs = reinterpret_cast<float*>(smem + L.sm1);
-    float* sc = reinterpret_cast<float*>(smem + L.sc);
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int seg = blockIdx.x, bh = blockIdx.y;
-    const int b = bh / p.H, h = bh - b * p.H;
-    const int g = h / (p.H / p.G);
-    const int c_begin = seg * p.L;
-    const int c_end = min(c_begin + p.L, p.nc);
-    const int lda = L.lda;
-    const int l16 = lane & 15, q4 = lane >> 4;
-
-    f32x4 U[STW];
-#pragma unroll
-    for (int w = 0; w < STW; ++w) U[w] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float dprod = 1.f;
-
-    for (int c = c_begin; c < c_end; ++c) {
-        const int c0 = c * p.C;
-        const int cl = min(p.C, p.S - c0);
-        prep_scalars<NTHR>(p, bh, b, h, c0, cl, sc, scs, false);
-        __syncthreads();
-        const float* s_erev = sc + 2 * kMaxRows;
-        const float* s_fac = sc + 3 * kMaxRows;
-        const float dl = sc[4 * kMaxRows];
-        // kappa^T: rotated k, times factor (bf16), times exp(da_cs_rev) (bf16), transposed.
-        const int ng = p.N / 16;
-        const int nit = MT * ng;
-#pragma unroll
-        for (int j = 0; j < QK_IT; ++j) {
-            const int it = tid + j * NTHR;
-            if (it < nit) {
-                const int i = it / ng, gg = it - i * ng;
-                const int r = i / p.Cp, t = i - r * p.Cp;
-                const int col0 = gg * 8, col1 = p.N / 2 + gg * 8;
-                float ka[8], kb[8];
-                if (r < p.R && t < cl) {
-                    const long row = (((long)(b * p.S + c0 + t) * p.R + r) * p.G + g) * p.N;
-                    const float* kbias = p.k_bias + ((long)h * p.R + r) * p.N;
-                    bias8(ld8(p.k + row + col0), kbias + col0, ka);
-                    bias8(ld8(p.k + row + col1), kbias + col1, kb);
-                    rotate8(ka, kb, col0, p.W, scs + t * p.W, scs + p.C * p.W + t * p.W);
-                    const float f = s_fac[t], er = s_erev[t];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        ka[e] = bfr(bfr(ka[e] * f) * er);
-                        kb[e] = bfr(bfr(kb[e] * f) * er);
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) ka[e] = kb[e] = 0.f;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sKapT[(col0 + e) * lda + i] = static_cast<__bf16>(ka[e]);
-                    sKapT[(col1 + e) * lda + i] = static_cast<__bf16>(kb[e]);
-                }
-            }
-        }
-        // state columns beyond N
-        for (int it = tid; it < (NT - p.N) * MT; it += NTHR) {
-            const int n = p.N + it / MT, i = it % MT;
-            sKapT[n * lda + i] = static_cast<__bf16>(0.f);
-        }
-        fill_psi<MT, PT, NTHR>(p, b, h, c0, cl, sPsiT, lda);
-        __syncthreads();
-#pragma unroll
-        for (int w = 0; w < STW; ++w) {
-            const int u = wave + w * NW;
-            if (u < ST) {
-                const int nt = u / (PT / 16), pt = u - nt * (PT / 16);
-                f32x4 acc = U[w] * dl;
-#pragma unroll
-                for (int ks = 0; ks < MT / 32; ++ks) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sKapT + (16 * nt + l16) * lda + 32 * ks + 8 * q4);
-                    const bf16x8 bb = *reinterpret_cast<const bf16x8*>(sPsiT + (16 * pt + l16) * lda + 32 * ks + 8 * q4);
-                    acc = mfma(a, bb, acc);
-                }
-                U[w] = acc;
-            }
-        }
-        dprod *= dl;
-        __syncthreads();
-    }
-    float* out = p.agg + ((long)bh * (p.nseg - 1) + seg) * p.N * p.P;
-#pragma unroll
-    for (int w = 0; w < STW; ++w) {
-        const int u = wave + w * NW;
-        if (u < ST) {
-            const int nt = u / (PT / 16), pt = u - nt * (PT / 16);
-            const int pc = 16 * pt + l16;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int n = 16 * nt + 4 * q4 + v;
-                if (n < p.N && pc < p.P) out[(long)n * p.P + pc] = U[w][v];
-            }
-        }
-    }
-    if (tid == 0) p.decay[(long)bh * p.nseg + seg] = dprod;
-}
-
-// ---------------------------------------------------------------- main chunk pass
-// Template: RP = rank count rounded up to a power of two (ranks >= R are zero
-// rows), CT = 16-token tiles per rank (Cp = 16*CT >= C), NT / PT = state and
-// value dimensions rounded up to 32 / 64 / 128.
+// per chunk; also the product of the chunk decays.
 template <int RP, int CT, int NT, int PT>
-struct MainCfg {
-    static constexpr int MT = (RP * CT * 16 < 32) ? 32 : RP * CT * 16;
-    static constexpr int NW = (MT == 128 && PT >= 64) ? 8 : 4;
-};
-
-template <int RP, int CT, int NT, int PT>
-__global__ __launch_bounds__((MainCfg<RP, CT, NT, PT>::NW * 64), 2) void k_main(Params p) {
-    constexpr int MT = MainCfg<RP, CT, NT, PT>::MT;
-    constexpr int NW = MainCfg<RP, CT, NT, PT>::NW;
-    constexpr int NTHR = NW * 64;
-    constexpr int Cp = CT * 16;
-    constexpr int QK_IT = (MT * (NT / 16) + NTHR - 1) / NTHR;  // q/k prep items per thread (bound)
-    constexpr int PTT = PT / 16;
-    constexpr int ST = (NT / 16) * PTT;                         // state tiles
-    constexpr int STW = (ST + NW - 1) / NW;
-    constexpr int MTT = MT / 16;
-    constexpr int AT = MTT * MTT;                               // causal-block tiles
-    constexpr int ATW = (AT + NW - 1) / NW;
-    constexpr int NPAIRS = CT * PTT;                            // (token tile, value tile) pairs
-    constexpr int PW = (NPAIRS + NW - 1) / NW;                  // pairs per wave
-
+__global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params p) {
+    using T = Tile<RP, CT, NT, PT>;
     extern __shared__ __align__(16) unsigned char smem[];
-    const Lds L = lds_layout(MT, NT, PT, p.C, p.R, p.W, true);
-    __bf16* sQ = reinterpret_cast<__bf16*>(smem + L.r1);     // also sA, sKapT
-    __bf16* sA = sQ;
-    __bf16* sKapT = sQ;
-    __bf16* sK = reinterpret_cast<__bf16*>(smem + L.r2);
-    __bf16* sPsiT = reinterpret_cast<__bf16*>(smem + L.r3);
-    __bf16* sSbT = reinterpret_cast<__bf16*>(smem + L.r4);
-    float* scs = reinterpret_cast<float*>(smem + L.sm1);     // cos/sin, then exp(segsum)
-    float* sE = scs;
-    float* sQK = reinterpret_cast<float*>(smem + L.sqk);
-    float* sc = reinterpret_cast<float*>(smem + L.sc);
-    const float* s_ecs = sc;
-    const float* s_gam = sc + kMaxRows;
-    const float* s_erev = sc + 2 * kMaxRows;
-    const float* s_fac = sc + 3 * kMaxRows;
-    constexpr int ldq = NT + 8, lda = MT + 8;
+    const Lds L = lds_layout(T::MT, NT, PT, p.C, p.R, p.N, p.P, p.W, false);
+    unsigned short* sKapT = reinterpret_cast<unsigned short*>(smem + L.r1);
+    const unsigned short* sPsiT = reinterpret_cast<const unsigned short*>(smem + L.r3);
+    const float* sc = reinterpret_cast<const float*>(smem + L.sc);
+    const float* scs = reinterpret_cast<const float*>(smem + L.cs);
+    const unsigned short* tbk = reinterpret_cast<const unsigned short*>(smem + L.tb) + p.R * p.N;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -387,259 +555,408 @@ __global__ __launch_bounds__((MainCfg<RP, CT, NT, PT>::NW * 64), 2) void k_main(
     const int c_end = min(c_begin + p.L, p.nc);
     const int R = p.R;
 
+    Items<RP, CT, NT, PT> it;
+    make_items<RP, CT, NT, PT, true>(p, g, it);
+    fill_tables<RP, CT, NT, PT>(p, h, smem, L);
+    // kappa^T columns beyond the real rows, and rows n >= N, stay zero
+    for (int e = tid; e < NT * T::MT; e += T::NTHR) sKapT[e / T::MT * T::LDA + e % T::MT] = 0;
+
+    using SG = Stage<RP, CT, NT, PT, false>;
+    __shared__ __align__(16) unsigned char stg[SG::ON ? SG::BYTES : 16];
+    if constexpr (SG::ON) prefetch_chunk<RP, CT, NT, PT, false>(p, it, b, h, bh, c_begin, c_begin * p.C, min(p.C, p.S - c_begin * p.C), stg);
+
+    f32x4 U[T::STW];
+#pragma unroll
+    for (int w = 0; w < T::STW; ++w) U[w] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dprod = 1.f;
+
+    for (int c = c_begin; c < c_end; ++c) {
+        const int c0 = c * p.C;
+        const int cl = min(p.C, p.S - c0);
+        ChunkIn<RP, CT, NT, PT, false> in = {};
+        if constexpr (SG::ON) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's staging loads
+            read_stage(stg, in);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (c + 1 < c_end) prefetch_chunk<RP, CT, NT, PT, false>(p, it, b, h, bh, c + 1, c0 + p.C, min(p.C, p.S - c0 - p.C), stg);
+        } else {
+            load_chunk(p, it, b, h, bh, c, c0, cl, in);
+        }
+        __syncthreads();   // previous chunk done with LDS (and tables written)
+        phase0(p, it, c0, cl, in, smem, L);
+        __syncthreads();
+        // kappa^T = bf16(bf16(rot(bf16(k + bf16(k_bias))) * factor) * exp(da_cs_rev)), transposed
+#pragma unroll
+        for (int j = 0; j < T::QK_IT; ++j) {
+            const int i = it.qk_row[j];
+            if (i < 0) continue;
+            const int r = i / T::Cp, t = i % T::Cp;
+            if (r >= R || t >= cl) continue;   // stays zero from the initial fill / last chunk
+            const int col0 = it.qk_col[j], col1 = p.N / 2 + col0;
+            u32x4 a = add_bias(in.k0[j], lds_ld<u32x4>(tbk + r * p.N + col0));
+            u32x4 e = add_bias(in.k1[j], lds_ld<u32x4>(tbk + r * p.N + col1));
+            rotate_group(a, e, col0, p.W, scs + t * p.W, scs + p.C * p.W + t * p.W);
+            const float f = sc[3 * kTok + t], er = sc[2 * kTok + t];
+            a = scale_group(scale_group(a, f), er);
+            e = scale_group(scale_group(e, f), er);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                sKapT[(col0 + 2 * d) * T::LDA + i] = static_cast<unsigned short>(a[d]);
+                sKapT[(col0 + 2 * d + 1) * T::LDA + i] = static_cast<unsigned short>(a[d] >> 16);
+                sKapT[(col1 + 2 * d) * T::LDA + i] = static_cast<unsigned short>(e[d]);
+                sKapT[(col1 + 2 * d + 1) * T::LDA + i] = static_cast<unsigned short>(e[d] >> 16);
+            }
+        }
+        if (cl < p.C) {
+            // tail chunk: rows of tokens beyond the sequence are zero
+            for (int e = tid; e < NT * T::MT; e += T::NTHR) {
+                const int i = e % T::MT;
+                if (i % T::Cp >= cl) sKapT[e / T::MT * T::LDA + i] = 0;
+            }
+        }
+        fill_psi(p, cl, in, smem, L);
+        __syncthreads();
+        const float dl = sc[4 * kTok];
+#pragma unroll
+        for (int w = 0; w < T::STW; ++w) {
+            const int u = wave + w * T::NW;
+            if (u < T::ST) {
+                const int nt = u / T::PTT, pt = u % T::PTT;
+                f32x4 acc = U[w] * dl;
+#pragma unroll
+                for (int ks = 0; ks < T::MT / 32; ++ks) {
+                    const u32x4 a = lds_ld<u32x4>(sKapT + (16 * nt + l16) * T::LDA + 32 * ks + 8 * q4);
+                    const u32x4 bb = lds_ld<u32x4>(sPsiT + (16 * pt + l16) * T::LDA + 32 * ks + 8 * q4);
+                    acc = mfma(a, bb, acc);
+                }
+                U[w] = acc;
+            }
+        }
+        dprod *= dl;
+    }
+    float* out = p.agg + ((long)bh * (p.nseg - 1) + seg) * p.N * p.P;
+#pragma unroll
+    for (int w = 0; w < T::STW; ++w) {
+        const int u = wave + w * T::NW;
+        if (u < T::ST) {
+            const int nt = u / T::PTT, pt = u % T::PTT;
+            const int pc = 16 * pt + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int n = 16 * nt + 4 * q4 + v;
+                if (n < p.N && pc < p.P) out[n * p.P + pc] = U[w][v];
+            }
+        }
+    }
+    if (tid == 0) p.decay[(long)bh * p.nseg + seg] = dprod;
+}
+
+// ---------------------------------------------------------------- main chunk pass
+template <int RP, int CT, int NT, int PT>
+__global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params p) {
+    using T = Tile<RP, CT, NT, PT>;
+    constexpr int MT = T::MT, NW = T::NW, NTHR = T::NTHR, Cp = T::Cp;
+    constexpr int LDQ = T::LDQ, LDA = T::LDA, PTT = T::PTT, MTT = T::MTT;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const Lds L = lds_layout(MT, NT, PT, p.C, p.R, p.N, p.P, p.W, true);
+    unsigned short* sQ = reinterpret_cast<unsigned short*>(smem + L.r1);   // also sA, sKapT
+    unsigned short* sA = sQ;
+    unsigned short* sKapT = sQ;
+    unsigned short* sK = reinterpret_cast<unsigned short*>(smem + L.r2);
+    unsigned short* sPsiT = reinterpret_cast<unsigned short*>(smem + L.r3);
+    unsigned short* sSbT = reinterpret_cast<unsigned short*>(smem + L.r4);
+    const float* scs = reinterpret_cast<const float*>(smem + L.cs);
+    const float* sE = reinterpret_cast<const float*>(smem + L.se);
+    float* sQK = reinterpret_cast<float*>(smem + L.qk);
+    const float* sc = reinterpret_cast<const float*>(smem + L.sc);
+    const unsigned short* tbq = reinterpret_cast<const unsigned short*>(smem + L.tb);
+    const unsigned short* tbk = tbq + p.R * p.N;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int seg = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int g = h / (p.H / p.G);
+    const int c_begin = seg * p.L;
+    const int c_end = min(c_begin + p.L, p.nc);
+    const int R = p.R;
+    const bool need_y = p.need_y;
+
+    Items<RP, CT, NT, PT> it;
+    make_items(p, g, it);
+    fill_tables<RP, CT, NT, PT>(p, h, smem, L);
+
     // ---- state entering the segment (fp32, MFMA accumulator layout: rows n, columns p)
-    f32x4 Sacc[STW];
+    f32x4 Sacc[T::STW];
     {
         const float* E = (seg > 0) ? p.agg + ((long)bh * (p.nseg - 1) + seg - 1) * p.N * p.P : nullptr;
 #pragma unroll
-        for (int w = 0; w < STW; ++w) {
+        for (int w = 0; w < T::STW; ++w) {
             const int u = wave + w * NW;
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if (E != nullptr && u < ST) {
+            if (E != nullptr && u < T::ST) {
                 const int nt = u / PTT, pt = u % PTT;
                 const int pc = 16 * pt + l16;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int n = 16 * nt + 4 * q4 + v;
-                    if (n < p.N && pc < p.P) s[v] = E[(long)n * p.P + pc];
+                    if (n < p.N && pc < p.P) s[v] = E[n * p.P + pc];
                 }
             }
             Sacc[w] = s;
         }
     }
-    // bf16(S) into sSbT (operand of the next inter term) and into states[c]
-    auto emit_state = [&](int c) {
-        unsigned short* dst = p.states + ((long)bh * p.nc + c) * p.N * p.P;
+    // bf16(S) into sSbT, the operand of the inter term; states[c] is copied out of
+    // sSbT at the top of chunk c
+    auto emit_state = [&]() {
 #pragma unroll
-        for (int w = 0; w < STW; ++w) {
+        for (int w = 0; w < T::STW; ++w) {
             const int u = wave + w * NW;
-            if (u < ST) {
+            if (u < T::ST) {
                 const int nt = u / PTT, pt = u % PTT;
                 const int pc = 16 * pt + l16;
-                bf16x4 o;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) o[v] = static_cast<__bf16>(Sacc[w][v]);
-                *reinterpret_cast<bf16x4*>(sSbT + pc * ldq + 16 * nt + 4 * q4) = o;
-                if (pc < p.P) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int n = 16 * nt + 4 * q4 + v;
-                        if (n < p.N) dst[(long)n * p.P + pc] = f2bf(Sacc[w][v]);
-                    }
-                }
+                const u32x2 o = {pk2(Sacc[w][0], Sacc[w][1]), pk2(Sacc[w][2], Sacc[w][3])};
+                lds_st<u32x2>(sSbT + pc * LDQ + 16 * nt + 4 * q4, o);
             }
         }
     };
-    emit_state(c_begin);
+    emit_state();
 
-    // ---- per-lane constants of this wave's output tiles: slot (ps, r) is
-    // value tile pt of pair wave + ps*NW, rank r; lane column pc = 16*pt + l16.
-    float cz[PW][RP], co[PW][RP], dmo[PW][RP], dmz[PW][RP];
+    // ---- per-lane constants of this wave's output tiles: slot (ps, r) is the
+    // value tile of pair wave + ps*NW and rank r; lane column pc = 16*pt + l16.
+    float cz[T::PW][RP], co[T::PW][RP], dmo[T::PW][RP], dmz[T::PW][RP];
 #pragma unroll
-    for (int ps = 0; ps < PW; ++ps) {
+    for (int ps = 0; ps < T::PW; ++ps) {
         const int pair = wave + ps * NW;
         const int pc = 16 * (pair % PTT) + l16;
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
             cz[ps][r] = co[ps][r] = dmo[ps][r] = dmz[ps][r] = 0.f;
-            if (pair < NPAIRS && r < R && pc < p.P) {
+            if (pair < T::NPAIRS && r < R && pc < p.P) {
                 if (p.has_z) cz[ps][r] = p.mimo_z[((long)h * R + r) * p.P + pc];
-                if (p.reduce_o) co[ps][r] = bfr(p.mimo_o[((long)h * R + r) * p.P + pc]);
+                if (p.reduce_o) co[ps][r] = rnd1(p.mimo_o[((long)h * R + r) * p.P + pc]);
             }
         }
     }
     const float dval = p.has_d ? p.d[h] : 0.f;
+    using SG = Stage<RP, CT, NT, PT, true>;
+    __shared__ __align__(16) unsigned char stg[SG::ON ? SG::BYTES : 16];
+    if constexpr (SG::ON) prefetch_chunk<RP, CT, NT, PT, true>(p, it, b, h, bh, c_begin, c_begin * p.C, min(p.C, p.S - c_begin * p.C), stg);
 
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * p.C;
         const int cl = min(p.C, p.S - c0);
 
-        // ---- phase 0: per-token scalars, cos/sin
-        prep_scalars<NTHR>(p, bh, b, h, c0, cl, sc, scs, true);
+        ChunkIn<RP, CT, NT, PT, true> in = {};
+        if constexpr (SG::ON) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's staging loads
+            read_stage(stg, in);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (c + 1 < c_end) prefetch_chunk<RP, CT, NT, PT, true>(p, it, b, h, bh, c + 1, c0 + p.C, min(p.C, p.S - c0 - p.C), stg);
+        } else {
+            load_chunk(p, it, b, h, bh, c, c0, cl, in);
+        }
+        // gate inputs of this lane's tokens (read in the epilogue)
+        float zr[T::PW][4], dr[T::PW][4];
+        {
+            const long base = ((long)(b * p.S + c0)) * p.H * p.P + (long)h * p.P;
+#pragma unroll
+            for (int ps = 0; ps < T::PW; ++ps) {
+                const int pair = wave + ps * NW;
+                const int tt = pair / PTT, pc = 16 * (pair % PTT) + l16;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int t = 16 * tt + 4 * q4 + v;
+                    zr[ps][v] = dr[ps][v] = 0.f;
+                    if (need_y && pair < T::NPAIRS && t < cl && pc < p.P) {
+                        const int o = t * p.H * p.P + pc;
+                        if (p.has_z) zr[ps][v] = bf2f(p.z[base + o]);
+                        if (p.reduce_o) dr[ps][v] = bf2f(p.dout[base + o]);
+                    }
+                }
+            }
+        }
+        __syncthreads();   // previous chunk (and the tables) done
+
+        // ---- states[c] = bf16(S entering chunk c), from sSbT ([p][n]) to [n][p], 16 bytes a thread
+        {
+            unsigned short* dst = p.states + ((long)bh * p.nc + c) * p.N * p.P;
+            const int P8 = p.P / 8;
+            for (int e = tid; e < p.N * P8; e += NTHR) {
+                const int pc = (e / p.N) * 8, n = e % p.N;   // consecutive threads: consecutive n
+                const unsigned short* src = sSbT + pc * LDQ + n;
+                u32x4 o;
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    o[d] = static_cast<unsigned>(src[(2 * d) * LDQ]) | (static_cast<unsigned>(src[(2 * d + 1) * LDQ]) << 16);
+                *reinterpret_cast<u32x4*>(dst + n * p.P + pc) = o;
+            }
+        }
+
+        // ---- phase 0: token scalars, cos/sin, exp(segsum)
+        phase0(p, it, c0, cl, in, smem, L);
         __syncthreads();
 
         // ---- phase A: biased q/k (unrotated into LDS, rotated kept in registers), Psi^T
-        const int ng = p.N / 16;
-        const int nit = MT * ng;
-        bf16x8 rq0[QK_IT], rq1[QK_IT], rk0[QK_IT], rk1[QK_IT];
+        u32x4 rq0[T::QK_IT], rq1[T::QK_IT], rk0[T::QK_IT], rk1[T::QK_IT];
 #pragma unroll
-        for (int j = 0; j < QK_IT; ++j) {
-            const int it = tid + j * NTHR;
-            if (it < nit) {
-                const int i = it / ng, gg = it - i * ng;
-                const int r = i / Cp, t = i % Cp;
-                const int col0 = gg * 8, col1 = p.N / 2 + gg * 8;
-                float qa[8], qb[8], ka[8], kb[8];
-                if (r < R && t < cl) {
-                    const long row = (((long)(b * p.S + c0 + t) * R + r) * p.G + g) * p.N;
-                    const float* qbias = p.q_bias + ((long)h * R + r) * p.N;
-                    const float* kbias = p.k_bias + ((long)h * R + r) * p.N;
-                    bias8(ld8(p.q + row + col0), qbias + col0, qa);
-                    bias8(ld8(p.q + row + col1), qbias + col1, qb);
-                    bias8(ld8(p.k + row + col0), kbias + col0, ka);
-                    bias8(ld8(p.k + row + col1), kbias + col1, kb);
-                    st8(sQ + i * ldq + col0, qa);
-                    st8(sQ + i * ldq + col1, qb);
-                    st8(sK + i * ldq + col0, ka);
-                    st8(sK + i * ldq + col1, kb);
-                    const float* cs = scs + t * p.W;
-                    const float* sn = scs + p.C * p.W + t * p.W;
-                    rotate8(qa, qb, col0, p.W, cs, sn);
-                    rotate8(ka, kb, col0, p.W, cs, sn);
-                    const float f = s_fac[t];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        ka[e] = bfr(ka[e] * f);
-                        kb[e] = bfr(kb[e] * f);
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) qa[e] = qb[e] = ka[e] = kb[e] = 0.f;
-                    st8_zero(sQ + i * ldq + col0);
-                    st8_zero(sQ + i * ldq + col1);
-                    st8_zero(sK + i * ldq + col0);
-                    st8_zero(sK + i * ldq + col1);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    rq0[j][e] = static_cast<__bf16>(qa[e]);
-                    rq1[j][e] = static_cast<__bf16>(qb[e]);
-                    rk0[j][e] = static_cast<__bf16>(ka[e]);
-                    rk1[j][e] = static_cast<__bf16>(kb[e]);
-                }
+        for (int j = 0; j < T::QK_IT; ++j) {
+            const int i = it.qk_row[j];
+            if (i < 0) continue;
+            const int r = i / Cp, t = i % Cp;
+            const int col0 = it.qk_col[j], col1 = p.N / 2 + col0;
+            u32x4 qa = {0u, 0u, 0u, 0u}, qb = qa, ka = qa, kb = qa;
+            if (r < R && t < cl) {
+                qa = add_bias(in.q0[j], lds_ld<u32x4>(tbq + r * p.N + col0));
+                qb = add_bias(in.q1[j], lds_ld<u32x4>(tbq + r * p.N + col1));
+                ka = add_bias(in.k0[j], lds_ld<u32x4>(tbk + r * p.N + col0));
+                kb = add_bias(in.k1[j], lds_ld<u32x4>(tbk + r * p.N + col1));
             }
+            lds_st<u32x4>(sQ + i * LDQ + col0, qa);
+            lds_st<u32x4>(sQ + i * LDQ + col1, qb);
+            lds_st<u32x4>(sK + i * LDQ + col0, ka);
+            lds_st<u32x4>(sK + i * LDQ + col1, kb);
+            if (r < R && t < cl) {
+                const float* cs = scs + t * p.W;
+                const float* sn = scs + p.C * p.W + t * p.W;
+                rotate_group(qa, qb, col0, p.W, cs, sn);
+                rotate_group(ka, kb, col0, p.W, cs, sn);
+                const float f = sc[3 * kTok + t];
+                ka = scale_group(ka, f);
+                kb = scale_group(kb, f);
+            }
+            rq0[j] = qa;
+            rq1[j] = qb;
+            rk0[j] = ka;
+            rk1[j] = kb;
         }
-        // state columns beyond N are zero in both operands of the n-contractions
         if (p.N < NT) {
+            // state columns beyond N are zero in both operands of the n-contractions
             const int zc = (NT - p.N) / 8;
-            for (int it = tid; it < MT * zc; it += NTHR) {
-                const int i = it / zc, col = p.N + 8 * (it - i * zc);
-                st8_zero(sQ + i * ldq + col);
-                st8_zero(sK + i * ldq + col);
+            for (int e = tid; e < MT * zc; e += NTHR) {
+                const int i = e / zc, col = p.N + 8 * (e % zc);
+                lds_st<u32x4>(sQ + i * LDQ + col, u32x4{0u, 0u, 0u, 0u});
+                lds_st<u32x4>(sK + i * LDQ + col, u32x4{0u, 0u, 0u, 0u});
             }
         }
-        fill_psi<MT, PT, NTHR>(p, b, h, c0, cl, sPsiT, lda);
+        fill_psi(p, cl, in, smem, L);
         __syncthreads();
 
-        // ---- phase B: qk_dot (same token, unrotated) and exp(segsum)
+        // ---- phase B: qk_dot of the same token (biased, unrotated), fp32 accumulate
         {
             const int RR = R * R;
-            const int nq = cl * RR;
-            for (int it = tid; it < nq; it += NTHR) {
-                const int t = it / RR, rr = it - t * RR;
+            unsigned short* qko = p.qk_dot + ((long)bh * p.S + c0) * RR;
+            for (int e = tid; e < cl * RR; e += NTHR) {
+                const int rr = e / cl, t = e - rr * cl;   // consecutive threads: consecutive tokens
                 const int r = rr / R, r2 = rr - r * R;
-                const __bf16* xq = sQ + (r * Cp + t) * ldq;
-                const __bf16* xk = sK + (r2 * Cp + t) * ldq;
+                const unsigned short* xq = sQ + (r * Cp + t) * LDQ;
+                const unsigned short* xk = sK + (r2 * Cp + t) * LDQ;
                 float sum = 0.f;
                 for (int n = 0; n < p.N; n += 8) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(xq + n);
-                    const bf16x8 bb = *reinterpret_cast<const bf16x8*>(xk + n);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) sum += bfv(a[e]) * bfv(bb[e]);
+                    const u32x4 a = lds_ld<u32x4>(xq + n), bb = lds_ld<u32x4>(xk + n);
+                    sum = dot2(a[0], bb[0], sum);
+                    sum = dot2(a[1], bb[1], sum);
+                    sum = dot2(a[2], bb[2], sum);
+                    sum = dot2(a[3], bb[3], sum);
                 }
-                const float vq = bfr(sum);
-                sQK[it] = vq;
-                p.qk_dot[(((long)bh * p.S + c0 + t) * R + r) * R + r2] = f2bf(vq);
-            }
-            if (p.need_y) {
-                const float* sg = p.segsum + ((long)bh * p.nc + c) * p.C * p.C;
-                for (int e = tid; e < p.C * p.C; e += NTHR) sE[e] = expf(sg[e]);
+                const unsigned u = pk2(sum, 0.f);
+                sQK[t * (RR + 1) + rr] = lo16(u);
+                qko[t * RR + rr] = static_cast<unsigned short>(u);
             }
         }
         __syncthreads();
 
         // ---- phase C: rotated q and factor-scaled k into LDS
 #pragma unroll
-        for (int j = 0; j < QK_IT; ++j) {
-            const int it = tid + j * NTHR;
-            if (it < nit) {
-                const int i = it / ng, gg = it - i * ng;
-                const int col0 = gg * 8, col1 = p.N / 2 + gg * 8;
-                if (p.need_y) {
-                    *reinterpret_cast<bf16x8*>(sQ + i * ldq + col0) = rq0[j];
-                    *reinterpret_cast<bf16x8*>(sQ + i * ldq + col1) = rq1[j];
-                }
-                *reinterpret_cast<bf16x8*>(sK + i * ldq + col0) = rk0[j];
-                *reinterpret_cast<bf16x8*>(sK + i * ldq + col1) = rk1[j];
+        for (int j = 0; j < T::QK_IT; ++j) {
+            const int i = it.qk_row[j];
+            if (i < 0) continue;
+            const int col0 = it.qk_col[j], col1 = p.N / 2 + col0;
+            if (need_y) {
+                lds_st<u32x4>(sQ + i * LDQ + col0, rq0[j]);
+                lds_st<u32x4>(sQ + i * LDQ + col1, rq1[j]);
             }
+            lds_st<u32x4>(sK + i * LDQ + col0, rk0[j]);
+            lds_st<u32x4>(sK + i * LDQ + col1, rk1[j]);
         }
         __syncthreads();
 
-        f32x4 acc[PW][RP];
-        if (p.need_y) {
+        f32x4 acc[T::PW][RP];
+        if (need_y) {
             // ---- inter = Q bf16(S), scaled by exp(da_cs[t]) per row
 #pragma unroll
-            for (int ps = 0; ps < PW; ++ps) {
+            for (int ps = 0; ps < T::PW; ++ps) {
                 const int pair = wave + ps * NW;
                 const int tt = pair / PTT, pt = pair % PTT;
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
                     f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-                    if (pair < NPAIRS && r < R) {
-                        const int it16 = r * CT + tt;
+                    if (pair < T::NPAIRS && r < R) {
+                        const int i16 = r * CT + tt;
 #pragma unroll
                         for (int ks = 0; ks < NT / 32; ++ks) {
-                            const bf16x8 a = *reinterpret_cast<const bf16x8*>(sQ + (16 * it16 + l16) * ldq + 32 * ks + 8 * q4);
-                            const bf16x8 bb = *reinterpret_cast<const bf16x8*>(sSbT + (16 * pt + l16) * ldq + 32 * ks + 8 * q4);
+                            const u32x4 a = lds_ld<u32x4>(sQ + (16 * i16 + l16) * LDQ + 32 * ks + 8 * q4);
+                            const u32x4 bb = lds_ld<u32x4>(sSbT + (16 * pt + l16) * LDQ + 32 * ks + 8 * q4);
                             a4 = mfma(a, bb, a4);
                         }
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) a4[v] *= s_ecs[16 * tt + 4 * q4 + v];
+                        const f32x4 e4 = lds_ld<f32x4>(sc + 16 * tt + 4 * q4);
+                        a4 *= e4;
                     }
                     acc[ps][r] = a4;
                 }
             }
             // ---- causal block A^T = K~ Q^T, masked on token index, times exp(segsum), bf16
-            bf16x4 at[ATW];
+            u32x2 at[T::ATW];
 #pragma unroll
-            for (int w = 0; w < ATW; ++w) {
+            for (int w = 0; w < T::ATW; ++w) {
                 const int u = wave + w * NW;
-                at[w] = bf16x4{};
-                const int jt = u / MTT, it16 = u % MTT;
-                const int ri = it16 / CT, rj = jt / CT;
-                const int tti = it16 % CT, ttj = jt % CT;
-                if (u < AT && ri < R && rj < R && ttj <= tti) {
+                at[w] = u32x2{0u, 0u};
+                const int jt = u / MTT, i16 = u % MTT;
+                const int ri = i16 / CT, rj = jt / CT;
+                const int tti = i16 % CT, ttj = jt % CT;
+                if (u < T::AT && ri < R && rj < R && ttj <= tti) {
                     f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < NT / 32; ++ks) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + (16 * jt + l16) * ldq + 32 * ks + 8 * q4);
-                        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(sQ + (16 * it16 + l16) * ldq + 32 * ks + 8 * q4);
+                        const u32x4 a = lds_ld<u32x4>(sK + (16 * jt + l16) * LDQ + 32 * ks + 8 * q4);
+                        const u32x4 bb = lds_ld<u32x4>(sQ + (16 * i16 + l16) * LDQ + 32 * ks + 8 * q4);
                         a4 = mfma(a, bb, a4);
                     }
                     const int ti = 16 * tti + l16;
+                    float m[4];
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int tj = 16 * ttj + 4 * q4 + v;
                         const bool keep = ti < cl && ti > tj;
-                        const float e = keep ? sE[ti * p.C + tj] : 0.f;
-                        at[w][v] = static_cast<__bf16>(keep ? a4[v] * e : 0.f);
+                        m[v] = keep ? a4[v] * sE[ti * p.C + tj] : 0.f;
                     }
+                    at[w] = u32x2{pk2(m[0], m[1]), pk2(m[2], m[3])};
                 }
             }
             __syncthreads();   // every wave is done reading sQ
 #pragma unroll
-            for (int w = 0; w < ATW; ++w) {
+            for (int w = 0; w < T::ATW; ++w) {
                 const int u = wave + w * NW;
-                if (u < AT) {
-                    const int jt = u / MTT, it16 = u % MTT;
-                    *reinterpret_cast<bf16x4*>(sA + (16 * it16 + l16) * lda + 16 * jt + 4 * q4) = at[w];
+                if (u < T::AT) {
+                    const int jt = u / MTT, i16 = u % MTT;
+                    lds_st<u32x2>(sA + (16 * i16 + l16) * LDA + 16 * jt + 4 * q4, at[w]);
                 }
             }
             __syncthreads();
             // ---- intra = A Psi, accumulated onto the scaled inter term
 #pragma unroll
-            for (int ps = 0; ps < PW; ++ps) {
+            for (int ps = 0; ps < T::PW; ++ps) {
                 const int pair = wave + ps * NW;
                 const int tt = pair / PTT, pt = pair % PTT;
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
-                    if (pair < NPAIRS && r < R) {
-                        const int it16 = r * CT + tt;
+                    if (pair < T::NPAIRS && r < R) {
+                        const int i16 = r * CT + tt;
                         f32x4 a4 = acc[ps][r];
 #pragma unroll
                         for (int ks = 0; ks < MT / 32; ++ks) {
-                            const bf16x8 a = *reinterpret_cast<const bf16x8*>(sA + (16 * it16 + l16) * lda + 32 * ks + 8 * q4);
-                            const bf16x8 bb = *reinterpret_cast<const bf16x8*>(sPsiT + (16 * pt + l16) * lda + 32 * ks + 8 * q4);
+                            const u32x4 a = lds_ld<u32x4>(sA + (16 * i16 + l16) * LDA + 32 * ks + 8 * q4);
+                            const u32x4 bb = lds_ld<u32x4>(sPsiT + (16 * pt + l16) * LDA + 32 * ks + 8 * q4);
                             a4 = mfma(a, bb, a4);
                         }
                         acc[ps][r] = a4;
@@ -652,128 +969,149 @@ __global__ __launch_bounds__((MainCfg<RP, CT, NT, PT>::NW * 64), 2) void k_main(
         // ---- kappa^T = bf16(K~ * exp(da_cs_rev)), transposed, into R1
         {
             constexpr int n8 = NT / 8;
-            for (int it = tid; it < MT * n8; it += NTHR) {
-                const int i = it / n8, nn = (it % n8) * 8;
+            for (int e = tid; e < MT * n8; e += NTHR) {
+                const int i = e % MT, nn = (e / MT) * 8;   // consecutive threads: consecutive rows
                 const int r = i / Cp, t = i % Cp;
-                const bf16x8 x = *reinterpret_cast<const bf16x8*>(sK + i * ldq + nn);
-                const float er = (r < R && t < cl) ? s_erev[t] : 0.f;
+                const u32x4 x = lds_ld<u32x4>(sK + i * LDQ + nn);
+                const float er = (r < R && t < cl) ? sc[2 * kTok + t] : 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sKapT[(nn + e) * lda + i] = static_cast<__bf16>(bfv(x[e]) * er);
+                for (int d = 0; d < 4; ++d) {
+                    const unsigned u = pk2(lo16(x[d]) * er, hi16(x[d]) * er);
+                    sKapT[(nn + 2 * d) * LDA + i] = static_cast<unsigned short>(u);
+                    sKapT[(nn + 2 * d + 1) * LDA + i] = static_cast<unsigned short>(u >> 16);
+                }
             }
         }
         __syncthreads();
 
         // ---- state update S <- S * exp(da_cs[last]) + kappa^T Psi; bf16 copy for the next chunk
         {
-            const float dl = sc[4 * kMaxRows];
+            const float dl = sc[4 * kTok];
 #pragma unroll
-            for (int w = 0; w < STW; ++w) {
+            for (int w = 0; w < T::STW; ++w) {
                 const int u = wave + w * NW;
-                if (u < ST) {
+                if (u < T::ST) {
                     const int nt = u / PTT, pt = u % PTT;
                     f32x4 a4 = Sacc[w] * dl;
 #pragma unroll
                     for (int ks = 0; ks < MT / 32; ++ks) {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sKapT + (16 * nt + l16) * lda + 32 * ks + 8 * q4);
-                        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(sPsiT + (16 * pt + l16) * lda + 32 * ks + 8 * q4);
+                        const u32x4 a = lds_ld<u32x4>(sKapT + (16 * nt + l16) * LDA + 32 * ks + 8 * q4);
+                        const u32x4 bb = lds_ld<u32x4>(sPsiT + (16 * pt + l16) * LDA + 32 * ks + 8 * q4);
                         a4 = mfma(a, bb, a4);
                     }
                     Sacc[w] = a4;
                 }
             }
-            if (c + 1 < c_end) emit_state(c + 1);
+            emit_state();
         }
 
         // ---- y = bf16(inter + intra + diag + d*Psi) and the gating gradients
-        if (p.need_y) {
+        if (need_y) {
+            const long base = ((long)(b * p.S + c0)) * p.H * p.P + (long)h * p.P;
 #pragma unroll
-            for (int ps = 0; ps < PW; ++ps) {
+            for (int ps = 0; ps < T::PW; ++ps) {
                 const int pair = wave + ps * NW;
-                if (pair >= NPAIRS) continue;
+                if (pair >= T::NPAIRS) continue;
                 const int tt = pair / PTT, pt = pair % PTT;
                 const int pc = 16 * pt + l16;
                 const int tb = 16 * tt + 4 * q4;   // first of this lane's 4 tokens
                 float psi[RP][4];
 #pragma unroll
                 for (int r2 = 0; r2 < RP; ++r2) {
-                    if (r2 < R) {
-                        const bf16x4 x = *reinterpret_cast<const bf16x4*>(sPsiT + pc * lda + r2 * Cp + tb);
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) psi[r2][v] = bfv(x[v]);
-                    } else {
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) psi[r2][v] = 0.f;
-                    }
+                    const u32x2 x = (r2 < R) ? lds_ld<u32x2>(sPsiT + pc * LDA + r2 * Cp + tb) : u32x2{0u, 0u};
+                    psi[r2][0] = lo16(x[0]);
+                    psi[r2][1] = hi16(x[0]);
+                    psi[r2][2] = lo16(x[1]);
+                    psi[r2][3] = hi16(x[1]);
                 }
-                float zv[4], dov[4], dzc[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    dzc[v] = zv[v] = dov[v] = 0.f;
-                    const int t = tb + v;
-                    if (t < cl && pc < p.P) {
-                        const long ivp = ((long)(b * p.S + c0 + t) * p.H + h) * p.P + pc;
-                        if (p.has_z) zv[v] = bf2f(p.z[ivp]);
-                        if (p.reduce_o) dov[v] = bf2f(p.dout[ivp]);
-                    }
-                }
+                const f32x4 gam4 = lds_ld<f32x4>(sc + kTok + tb);
+                float dzc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
                     if (r >= R) continue;
+                    // diagonal of two tokens at a time: rank-ordered bf16 products and sums
+                    float y[4];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int t = tb + v;
-                        const bool real = t < cl && pc < p.P;
-                        // diagonal: rank-ordered bf16 products and sums, times gamma
-                        const float* qkrow = sQK + (t * R + r) * R;
-                        float dg = 0.f;
+                    for (int vp = 0; vp < 2; ++vp) {
+                        const int va = 2 * vp, vb = va + 1;
+                        const float* qa = sQK + (tb + va) * (R * R + 1) + r * R;
+                        const float* qb = sQK + (tb + vb) * (R * R + 1) + r * R;
+                        float da = 0.f, db = 0.f;
 #pragma unroll
                         for (int r2 = 0; r2 < RP; ++r2) {
                             if (r2 < R) {
-                                const float qk = real ? qkrow[r2] : 0.f;
-                                dg = bfr(dg + bfr(qk * psi[r2][v]));
+                                float pa = qa[r2] * psi[r2][va], pb = qb[r2] * psi[r2][vb];
+                                rnd2(pa, pb);
+                                da += pa;
+                                db += pb;
+                                rnd2(da, db);
                             }
                         }
-                        dg = bfr(dg * s_gam[t]);
-                        float o = acc[ps][r][v] + dg;
-                        if (p.has_d) o += dval * psi[r][v];
-                        const float y = bfr(o);
-                        if (!real) continue;
-                        if (p.has_z) {
-                            const float pz = zv[v] * cz[ps][r];
-                            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-pz));
-                            float G;
-                            if (p.reduce_o) {
-                                dmo[ps][r] += (y * (pz * sg)) * dov[v];
-                                G = bfr(bfr(dov[v] * co[ps][r]) * y);
-                            } else {
-                                const long inr = (((long)(b * p.S + c0 + t) * R + r) * p.H + h) * p.P + pc;
-                                G = bfr(bf2f(p.dout[inr]) * y);
-                            }
-                            const float gz = (G * sg) * (1.0f + pz * (1.0f - sg));
-                            dzc[v] = bfr(dzc[v] + __fmul_rn(gz, cz[ps][r]));
-                            dmz[ps][r] += gz * zv[v];
-                        } else if (p.reduce_o) {
-                            dmo[ps][r] += y * dov[v];
+                        da *= gam4[va];
+                        db *= gam4[vb];
+                        rnd2(da, db);
+                        float oa = acc[ps][r][va] + da, ob = acc[ps][r][vb] + db;
+                        oa += dval * psi[r][va];
+                        ob += dval * psi[r][vb];
+                        rnd2(oa, ob);
+                        // tokens past the chunk's end contribute nothing
+                        y[va] = (tb + va < cl) ? oa : 0.f;
+                        y[vb] = (tb + vb < cl) ? ob : 0.f;
+                    }
+                    if (p.has_z) {
+                        float sg[4], pz[4], G[4], gz[4];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            pz[v] = zr[ps][v] * cz[ps][r];
+                            sg[v] = sigmoid_fast(pz[v]);
                         }
+                        if (p.reduce_o) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                dmo[ps][r] += (y[v] * (pz[v] * sg[v])) * dr[ps][v];
+                                G[v] = dr[ps][v] * co[ps][r];
+                            }
+                            rnd2(G[0], G[1]);
+                            rnd2(G[2], G[3]);
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) G[v] *= y[v];
+                        } else {
+                            const long nb = ((long)(b * p.S + c0) * R + r) * p.H * p.P + (long)h * p.P;
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const int t = tb + v;
+                                const float dn = (t < cl && pc < p.P) ? bf2f(p.dout[nb + (long)t * R * p.H * p.P + pc]) : 0.f;
+                                G[v] = dn * y[v];
+                            }
+                        }
+                        rnd2(G[0], G[1]);
+                        rnd2(G[2], G[3]);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            gz[v] = (G[v] * sg[v]) * (1.0f + pz[v] * (1.0f - sg[v]));
+                            dzc[v] += __fmul_rn(gz[v], cz[ps][r]);
+                            dmz[ps][r] += gz[v] * zr[ps][v];
+                        }
+                        rnd2(dzc[0], dzc[1]);
+                        rnd2(dzc[2], dzc[3]);
+                    } else if (p.reduce_o) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) dmo[ps][r] += y[v] * dr[ps][v];
                     }
                 }
-                if (p.has_z) {
+                if (p.has_z && pc < p.P) {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int t = tb + v;
-                        if (t < cl && pc < p.P)
-                            p.dz[((long)(b * p.S + c0 + t) * p.H + h) * p.P + pc] = f2bf(dzc[v]);
-                    }
+                    for (int v = 0; v < 4; ++v)
+                        if (tb + v < cl) p.dz[base + (long)(tb + v) * p.H * p.P + pc] = f2bf(dzc[v]);
                 }
             }
         }
-        __syncthreads();
     }
 
     // ---- per-segment partial sums of dmimo_o / dmimo_z: reduce over the 4 lane groups
-    if (p.need_y) {
+    if (need_y) {
 #pragma unroll
-        for (int ps = 0; ps < PW; ++ps) {
+        for (int ps = 0; ps < T::PW; ++ps) {
 #pragma unroll
             for (int r = 0; r < RP; ++r) {
                 float so = dmo[ps][r], sz = dmz[ps][r];
@@ -787,12 +1125,12 @@ __global__ __launch_bounds__((MainCfg<RP, CT, NT, PT>::NW * 64), 2) void k_main(
         }
         if constexpr (CT == 1) {
 #pragma unroll
-            for (int ps = 0; ps < PW; ++ps) {
+            for (int ps = 0; ps < T::PW; ++ps) {
                 const int pair = wave + ps * NW;
                 const int pc = 16 * (pair % PTT) + l16;
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
-                    if (pair < NPAIRS && r < R && q4 == 0 && pc < p.P) {
+                    if (pair < T::NPAIRS && r < R && q4 == 0 && pc < p.P) {
                         const long o = ((long)bh * p.nseg + seg) * R * p.P + (long)r * p.P + pc;
                         if (p.reduce_o) p.part_o[o] = dmo[ps][r];
                         if (p.has_z) p.part_z[o] = dmz[ps][r];
@@ -802,15 +1140,16 @@ __global__ __launch_bounds__((MainCfg<RP, CT, NT, PT>::NW * 64), 2) void k_main(
         } else {
             // the token tiles of one (rank, value tile) belong to different waves;
             // add them in token-tile order through LDS
+            __syncthreads();
             float* red = reinterpret_cast<float*>(smem);   // [2][CT][RP][PT]
             constexpr int per = RP * PT;
 #pragma unroll
-            for (int ps = 0; ps < PW; ++ps) {
+            for (int ps = 0; ps < T::PW; ++ps) {
                 const int pair = wave + ps * NW;
                 const int tt = pair / PTT, pc = 16 * (pair % PTT) + l16;
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
-                    if (pair < NPAIRS && q4 == 0) {
+                    if (pair < T::NPAIRS && q4 == 0) {
                         red[tt * per + r * PT + pc] = dmo[ps][r];
                         red[CT * per + tt * per + r * PT + pc] = dmz[ps][r];
                     }
@@ -837,28 +1176,26 @@ __global__ __launch_bounds__((MainCfg<RP, CT, NT, PT>::NW * 64), 2) void k_main(
 
 typedef void (*kfn)(Params);
 
-// k_agg: indexed by (MT, NT, PT); k_main: indexed by (RP, CT, NT, PT).
-template <int MT, int NT, int PT>
-kfn agg_for() {
-    constexpr int NW = (MT == 128 && PT >= 64) ? 8 : 4;
-    return k_agg<MT, NT, PT, NW>;
-}
-
-template <int RP, int CT, int NT, int PT>
-kfn main_for() {
-    return k_main<RP, CT, NT, PT>;
-}
-
-// Each returns the 9 kernels of one tile family, indexed 3 * idx(NT) + idx(PT)
+// The 9 (NT, PT) combinations of one (RP, CT) family, indexed 3 * idx(NT) + idx(PT)
 // with idx(32, 64, 128) = 0, 1, 2.
-#define MIMO_NP_TABLE(F) \
-    F(32, 32), F(32, 64), F(32, 128), F(64, 32), F(64, 64), F(64, 128), F(128, 32), F(128, 64), F(128, 128)
-const kfn* agg_table_mt32();
-const kfn* agg_table_mt64();
-const kfn* agg_table_mt128();
-#define MIMO_DECL_MAIN(RP, CT) const kfn* main_table_rp##RP##_ct##CT();
-MIMO_DECL_MAIN(1, 1) MIMO_DECL_MAIN(1, 2) MIMO_DECL_MAIN(1, 4)
-MIMO_DECL_MAIN(2, 1) MIMO_DECL_MAIN(2, 2) MIMO_DECL_MAIN(2, 4)
-MIMO_DECL_MAIN(4, 1) MIMO_DECL_MAIN(4, 2) MIMO_DECL_MAIN(8, 1)
+struct Family {
+    kfn agg[9];
+    kfn main[9];
+};
+
+#define MIMO_NP_LIST(F, RP, CT)                                                                             \
+    F(RP, CT, 32, 32), F(RP, CT, 32, 64), F(RP, CT, 32, 128), F(RP, CT, 64, 32), F(RP, CT, 64, 64),         \
+        F(RP, CT, 64, 128), F(RP, CT, 128, 32), F(RP, CT, 128, 64), F(RP, CT, 128, 128)
+#define MIMO_AGG_FN(RP, CT, NT, PT) k_agg<RP, CT, NT, PT>
+#define MIMO_MAIN_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT>
+#define MIMO_FAMILY(RP, CT)                                                                               \
+    const Family* family_rp##RP##_ct##CT() {                                                              \
+        static const Family f = {{MIMO_NP_LIST(MIMO_AGG_FN, RP, CT)}, {MIMO_NP_LIST(MIMO_MAIN_FN, RP, CT)}}; \
+        return &f;                                                                                        \
+    }
+#define MIMO_DECL_FAMILY(RP, CT) const Family* family_rp##RP##_ct##CT();
+MIMO_DECL_FAMILY(1, 1) MIMO_DECL_FAMILY(1, 2) MIMO_DECL_FAMILY(1, 4)
+MIMO_DECL_FAMILY(2, 1) MIMO_DECL_FAMILY(2, 2) MIMO_DECL_FAMILY(2, 4)
+MIMO_DECL_FAMILY(4, 1) MIMO_DECL_FAMILY(4, 2) MIMO_DECL_FAMILY(8, 1)
 
 }  // namespace mimo

@@ -1,0 +1,6 @@
+// Kernel instantiations of the tile family with ranks padded to 1 and 2 token tile(s) per rank.
+#include "mimo_kernels.hpp"
+
+namespace mimo {
+MIMO_FAMILY(1, 2)
+}  // namespace mimo

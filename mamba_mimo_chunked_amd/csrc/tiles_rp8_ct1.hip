@@ -1,0 +1,6 @@
+// Kernel instantiations of the tile family with ranks padded to 8 and 1 token tile(s) per rank.
+#include "mimo_kernels.hpp"
+
+namespace mimo {
+MIMO_FAMILY(8, 1)
+}  // namespace mimo
