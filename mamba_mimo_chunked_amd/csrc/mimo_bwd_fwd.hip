@@ -169,7 +169,8 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
         return fail(MIMO_ERR_UNSUPPORTED,
                     "R=%lld with chunk_size=%lld needs %d tile rows (limit 128)", (long long)R, (long long)C,
                     16 * RP * CT);
-    if (B * H > 65535) return fail(MIMO_ERR_UNSUPPORTED, "B * H above 65535 is not supported");
+    if (B * H * ((S + C - 1) / C + 8) > (int64_t)1 << 31)
+        return fail(MIMO_ERR_UNSUPPORTED, "B * H * nchunks is too large");
     if (S > (int64_t)1 << 30) return fail(MIMO_ERR_UNSUPPORTED, "S above 2^30 is not supported");
     pl->RP = RP;
     pl->CT = CT;
@@ -258,6 +259,12 @@ mimo_status set_lds(kfn f, int bytes) {
     return MIMO_OK;
 }
 
+// 1-D grid of the chunk kernels (see map_block): 8 XCDs x H/G heads x units per XCD.
+unsigned grid_blocks(const Params& p, int nseg_k) {
+    const long units = (long)p.B * p.G * nseg_k;
+    return (unsigned)(8L * (p.H / p.G) * ((units + 7) / 8));
+}
+
 mimo_status launch(kfn f, dim3 grid, dim3 block, int lds, hipStream_t st, Params& p) {
     void* args[] = {&p};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(f), grid, block, args, (size_t)lds, st);
@@ -344,7 +351,7 @@ static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* ev
     if ((s = mark(0)) != MIMO_OK) return s;
     if (pl.nseg > 1) {
         if ((s = set_lds(kagg, pl.lds_agg)) != MIMO_OK) return s;
-        if ((s = launch(kagg, dim3(pl.nseg - 1, BH), dim3(pl.NW * 64), pl.lds_agg, st, p)) != MIMO_OK) return s;
+        if ((s = launch(kagg, dim3(grid_blocks(p, pl.nseg - 1)), dim3(pl.NW * 64), pl.lds_agg, st, p)) != MIMO_OK) return s;
         if ((s = mark(1)) != MIMO_OK) return s;
         const int NP = p.N * p.P;
         if ((s = launch(k_scan, dim3((NP / 4 + 255) / 256, BH), dim3(256), 0, st, p)) != MIMO_OK) return s;
@@ -352,7 +359,7 @@ static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* ev
         return s;
     }
     if ((s = mark(2)) != MIMO_OK) return s;
-    if ((s = launch(kmain, dim3(pl.nseg, BH), dim3(pl.NW * 64), pl.lds_main, st, p)) != MIMO_OK) return s;
+    if ((s = launch(kmain, dim3(grid_blocks(p, pl.nseg)), dim3(pl.NW * 64), pl.lds_main, st, p)) != MIMO_OK) return s;
     if ((s = mark(3)) != MIMO_OK) return s;
     if (pl.nseg > 1 && p.need_y) {
         const long tot = (long)BH * p.R * p.P;

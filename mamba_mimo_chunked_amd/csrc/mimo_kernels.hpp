@@ -532,6 +532,26 @@ __device__ __forceinline__ void fill_tables(const Params& p, int h, unsigned cha
     }
 }
 
+// ---------------------------------------------------------------- XCD-aware work mapping
+// Workgroups are dealt to the 8 XCDs round-robin by block index, and each XCD
+// has its own L2. The H/G heads that share a q/k group read the same q/k
+// chunk, so they are mapped to the same XCD and to consecutive blocks of it.
+// A work unit is (batch, group, segment); block k of XCD x takes head k % HPG
+// of unit x + 8*(k / HPG). Returns false for the padding blocks of the grid.
+__device__ __forceinline__ bool map_block(const Params& p, int nseg_k, int& seg, int& bh) {
+    const int hpg = p.H / p.G;
+    const int id = blockIdx.x;
+    const int xcd = id & 7, k = id >> 3;
+    const int unit = xcd + 8 * (k / hpg);
+    if (unit >= p.B * p.G * nseg_k) return false;
+    const int hh = k % hpg;
+    seg = unit % nseg_k;
+    const int bg = unit / nseg_k;          // b * G + g
+    const int b = bg / p.G, g = bg % p.G;
+    bh = b * p.H + g * hpg + hh;
+    return true;
+}
+
 // ---------------------------------------------------------------- segment aggregate
 // U_s = state added by segment s from a zero start: U <- U*exp(da_cs[last]) + kappa^T Psi
 // per chunk; also the product of the chunk decays.
@@ -548,7 +568,8 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
-    const int seg = blockIdx.x, bh = blockIdx.y;
+    int seg, bh;
+    if (!map_block(p, p.nseg - 1, seg, bh)) return;
     const int b = bh / p.H, h = bh - b * p.H;
     const int g = h / (p.H / p.G);
     const int c_begin = seg * p.L;
@@ -674,7 +695,8 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
-    const int seg = blockIdx.x, bh = blockIdx.y;
+    int seg, bh;
+    if (!map_block(p, p.nseg, seg, bh)) return;
     const int b = bh / p.H, h = bh - b * p.H;
     const int g = h / (p.H / p.G);
     const int c_begin = seg * p.L;
