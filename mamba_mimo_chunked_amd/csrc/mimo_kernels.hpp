@@ -56,6 +56,13 @@ __device__ __forceinline__ float sigmoid_fast(float x) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
 }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS accesses, not
+// for its global memory traffic. __syncthreads() also waits for outstanding global
+// loads into LDS (the staging prefetch below), which would serialise the prefetch
+// with the chunk it is meant to overlap. The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <typename T>
 __device__ __forceinline__ T lds_ld(const void* p) { return *reinterpret_cast<const T*>(p); }
 template <typename T>
@@ -110,7 +117,8 @@ struct Lds {
     int r4;   // bf16 [PT][LDQ] bf16(state)^T (main only)
     int cs;   // fp32 [2][C][W] cos, sin
     int se;   // fp32 [C][C] exp(segsum) (main only)
-    int qk;   // fp32 [C][R*R+1] qk_dot, one pad word per token (main only)
+    int qk;   // fp32 [Cp][RP*RP+1] qk_dot, zero for padded ranks, one pad word per token (main only)
+    int dz;   // bf16 [C][P+8] dz of the chunk, written out at the top of the next one (main only)
     int sc;   // fp32 [5][kTok] token scalars + chunk decay
     int tb;   // bf16 tables: q_bias [R][N], k_bias [R][N], mimo_v [R][P]
     int total;
@@ -120,6 +128,8 @@ __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
 
 __host__ __device__ inline Lds lds_layout(int MT, int NT, int PT, int C, int R, int N, int P, int W, bool main) {
     const int ldq = NT + 8, lda = MT + 8;
+    const int rp = R <= 1 ? 1 : (R <= 2 ? 2 : (R <= 4 ? 4 : 8));
+    const int cp = C <= 16 ? 16 : (C <= 32 ? 32 : 64);
     int r1 = NT * lda;
     if (main && MT * ldq > r1) r1 = MT * ldq;
     if (main && MT * lda > r1) r1 = MT * lda;
@@ -131,7 +141,8 @@ __host__ __device__ inline Lds lds_layout(int MT, int NT, int PT, int C, int R, 
     s.r4 = off; if (main) off += align16(PT * ldq * 2);
     s.cs = off; off += align16(2 * C * W * 4);
     s.se = off; if (main) off += align16(C * C * 4);
-    s.qk = off; if (main) off += align16(C * (R * R + 1) * 4);
+    s.qk = off; if (main) off += align16(cp * (rp * rp + 1) * 4);
+    s.dz = off; if (main) off += align16(C * (P + 8) * 2);
     s.sc = off; off += align16((5 * kTok + 4) * 4);
     s.tb = off; off += align16((2 * R * N + R * P) * 2);
     s.total = off;
@@ -151,14 +162,19 @@ struct ChunkIn {
     float seg[MAIN ? T::SEG_IT : 1];
 };
 
-// Per-thread item coordinates, fixed for the whole kernel.
+// Per-thread item coordinates, fixed for the whole kernel. Global reads of a chunk
+// are addressed as (chunk base, the same for every lane) + (byte offset of the
+// lane's item inside the chunk, the same for every chunk), so that the offsets
+// stay in registers for the whole kernel and the bases are scalar.
 template <int RP, int CT, int NT, int PT>
 struct Items {
     using T = Tile<RP, CT, NT, PT>;
-    int qk_row[T::QK_IT];   // tile row (-1: no item)
-    int qk_col[T::QK_IT];   // first column of the 8-column group in the first half
-    int qk_off[T::QK_IT];   // element offset of (t, r, g, col) inside a chunk's q/k block
-    int ang_t[T::ANG_IT], ang_off[T::ANG_IT];   // token, element offset inside a chunk (-1: none)
+    int qk_row[T::QK_IT];         // tile row (-1: no item)
+    int qk_col[T::QK_IT];         // first column of the 8-column group in the first half
+    unsigned qk_off[T::QK_IT];    // byte offset of (t, r, g, col) inside a chunk's q/k block
+    int ang_t[T::ANG_IT];         // token of the angle item (-1: none)
+    unsigned ang_off[T::ANG_IT];  // byte offset inside a chunk's angle block
+    unsigned v_off[T::PSI_IT];    // byte offset of the 8-column v group inside a chunk's v block
 };
 
 // ROWS_FAST: consecutive threads take consecutive tile rows (the chunk-aggregate
@@ -181,7 +197,7 @@ __device__ __forceinline__ void make_items(const Params& p, int g, Items<RP, CT,
             const int r = i / T::Cp, t = i % T::Cp;
             it.qk_row[j] = i;
             it.qk_col[j] = 8 * gg;
-            it.qk_off[j] = ((t * p.R + r) * p.G + g) * p.N + 8 * gg;
+            it.qk_off[j] = 2u * (unsigned)(((t * p.R + r) * p.G + g) * p.N + 8 * gg);
         }
     }
 #pragma unroll
@@ -192,9 +208,21 @@ __device__ __forceinline__ void make_items(const Params& p, int g, Items<RP, CT,
         if (e < p.C * p.W) {
             const int t = e / p.W, n = e - t * p.W;
             it.ang_t[j] = t;
-            it.ang_off[j] = t * p.H * p.W + n;
+            it.ang_off[j] = 4u * (unsigned)(t * p.H * p.W + n);
         }
     }
+#pragma unroll
+    for (int j = 0; j < T::PSI_IT; ++j) {
+        const int e = tid + j * T::NTHR;
+        const int t = e % T::Cp, pc = (e / T::Cp) * 8;
+        it.v_off[j] = 2u * (unsigned)(t * p.H * p.P + pc);
+    }
+}
+
+
+template <typename T>
+__device__ __forceinline__ const T* at(const void* base, unsigned byte_off) {
+    return reinterpret_cast<const T*>(static_cast<const unsigned char*>(base) + byte_off);
 }
 
 // Global loads of chunk c (c0 = first token, cl = real tokens).
@@ -206,18 +234,20 @@ __device__ __forceinline__ void load_chunk(const Params& p, const Items<RP, CT, 
     const int R = p.R;
     const unsigned short* qb = p.q + (long)(b * p.S + c0) * R * p.G * p.N;
     const unsigned short* kb = p.k + (long)(b * p.S + c0) * R * p.G * p.N;
+    const unsigned short* qb2 = qb + p.N / 2;
+    const unsigned short* kb2 = kb + p.N / 2;
 #pragma unroll
     for (int j = 0; j < T::QK_IT; ++j) {
         const int i = it.qk_row[j];
         const int r = i / T::Cp, t = i % T::Cp;
         if (i >= 0 && r < R && t < cl) {
-            const int o = it.qk_off[j];
+            const unsigned o = it.qk_off[j];
             if (MAIN) {
-                in.q0[j] = *reinterpret_cast<const u32x4*>(qb + o);
-                in.q1[j] = *reinterpret_cast<const u32x4*>(qb + o + p.N / 2);
+                in.q0[j] = *at<u32x4>(qb, o);
+                in.q1[j] = *at<u32x4>(qb2, o);
             }
-            in.k0[j] = *reinterpret_cast<const u32x4*>(kb + o);
-            in.k1[j] = *reinterpret_cast<const u32x4*>(kb + o + p.N / 2);
+            in.k0[j] = *at<u32x4>(kb, o);
+            in.k1[j] = *at<u32x4>(kb2, o);
         }
     }
     const unsigned short* vb = p.v + ((long)(b * p.S + c0) * p.H + h) * p.P;
@@ -225,8 +255,7 @@ __device__ __forceinline__ void load_chunk(const Params& p, const Items<RP, CT, 
     for (int j = 0; j < T::PSI_IT; ++j) {
         const int e = tid + j * T::NTHR;
         const int t = e % T::Cp, pc = (e / T::Cp) * 8;
-        if (e < T::Cp * (PT / 8) && t < cl && pc < p.P)
-            in.v[j] = *reinterpret_cast<const u32x4*>(vb + (long)t * p.H * p.P + pc);
+        if (e < T::Cp * (PT / 8) && t < cl && pc < p.P) in.v[j] = *at<u32x4>(vb, it.v_off[j]);
     }
     const long tok = (long)bh * p.S + c0;
     if (tid < cl) {
@@ -243,7 +272,7 @@ __device__ __forceinline__ void load_chunk(const Params& p, const Items<RP, CT, 
     const float* ab = p.angles + ((long)(b * p.S + c0) * p.H + h) * p.W;
 #pragma unroll
     for (int j = 0; j < T::ANG_IT; ++j)
-        if (it.ang_t[j] >= 0 && it.ang_t[j] < cl) in.ang[j] = ab[it.ang_off[j]];
+        if (it.ang_t[j] >= 0 && it.ang_t[j] < cl) in.ang[j] = *at<float>(ab, it.ang_off[j]);
     if (MAIN && p.need_y) {
         const float* sb = p.segsum + ((long)bh * p.nc + c) * p.C * p.C;
 #pragma unroll
@@ -278,24 +307,58 @@ struct Stage {
                                            : T::MT * lda)
                                      : NT * lda);
     static constexpr int DYN = 2 * r1 + (MAIN ? 2 * T::MT * ldq : 0) + 2 * PT * lda + (MAIN ? 2 * PT * ldq : 0) +
-                               8 * T::Cp * (NT / 2) + (MAIN ? 4 * T::Cp * T::Cp + 4 * T::Cp * (RP * RP + 1) : 0) +
+                               8 * T::Cp * (NT / 2) +
+                               (MAIN ? 4 * T::Cp * T::Cp + 4 * T::Cp * (RP * RP + 1) + 2 * T::Cp * (PT + 8) : 0) +
                                4 * (5 * kTok + 4) + 2 * (2 * RP * NT + RP * PT) + 256;
     static constexpr bool ON = DYN + BYTES <= 80 * 1024;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void dma16(const void* src, unsigned char* dst_wave) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 16, 0, 0);
+// One global_load_lds per lane: 16, 4 or 2 bytes from base + off (base the same
+// for every lane, off a 32-bit byte offset) into the wave's LDS block at dst_wave
+// (M0 holds its LDS address). Written as inline assembly so that the compiler's
+// wait-count tracking does not treat the address registers as pending until the
+// load completes (it would then wait for the whole prefetch as soon as such a
+// register is reused). The waits are explicit instead: s_waitcnt vmcnt(0) before
+// a thread reads its staged slots, and lgkmcnt(0) after the reads, before the
+// next prefetch overwrites them. M0 is saved and restored around the load; an
+// SALU write of M0 needs one wait state before an LDS DMA.
+// A wave-uniform pointer, pinned to scalar registers (a no-op when it already is).
+// readfirstlane returns int: each half goes through unsigned so that it is
+// zero-extended, never sign-extended, into the 64-bit address.
+__device__ __forceinline__ unsigned rfl(unsigned x) { return static_cast<unsigned>(__builtin_amdgcn_readfirstlane(x)); }
+__device__ __forceinline__ const void* sgpr_ptr(const void* p) {
+    const uint64_t x = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = rfl(static_cast<unsigned>(x));
+    const uint64_t hi = rfl(static_cast<unsigned>(x >> 32));
+    return reinterpret_cast<const void*>((hi << 32) | lo);
 }
-__device__ __forceinline__ void dma4(const void* src, unsigned char* dst_wave) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 4, 0, 0);
+// Raw buffer resource over [base, base + bytes) of a wave-uniform base: loads at
+// or beyond `bytes` return zero (word 3 is the gfx9 untyped-buffer format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(sgpr_ptr(base)), (short)0, (int)rfl(bytes), 0x00020000);
 }
-__device__ __forceinline__ void dma2(const void* src, unsigned char* dst_wave) {
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst_wave, 2, 0, 0);
-}
+constexpr unsigned kOut = 0x80000000u;   // buffer offset that is always out of range
+#define MIMO_DMA(NAME, INSN)                                                                          \
+    __device__ __forceinline__ void NAME(const void* base, unsigned off, unsigned char* dst_wave) { \
+        const void* sb = sgpr_ptr(base);                                                            \
+        const unsigned m = rfl(static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)dst_wave))); \
+        unsigned saved;                                                                             \
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t" INSN                       \
+                     " %1, %2\n\ts_mov_b32 m0, %0"                                                  \
+                     : "=&s"(saved)                                                                 \
+                     : "v"(off), "s"(sb), "s"(m)                                                    \
+                     : "memory");                                                                   \
+    }
+MIMO_DMA(dma16, "global_load_lds_dwordx4")
+MIMO_DMA(dma4, "global_load_lds_dword")
+MIMO_DMA(dma2, "global_load_lds_ushort")
+#undef MIMO_DMA
 
-// Issue the staging loads of chunk c (first token c0, cl real tokens).
+// Issue the staging loads of chunk c (first token c0, cl real tokens). Every
+// address is a scalar chunk base plus a per-lane offset that does not change
+// from chunk to chunk.
 template <int RP, int CT, int NT, int PT, bool MAIN>
 __device__ __forceinline__ void prefetch_chunk(const Params& p, const Items<RP, CT, NT, PT>& it, int b, int h, int bh,
                                                int c, int c0, int cl, unsigned char* stg) {
@@ -311,15 +374,15 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const Items<RP, 
         const int r = i / T::Cp, t = i % T::Cp;
         unsigned char* d = stg + SG::QK + (j * SG::NQ) * T::NTHR * 16 + wave * 1024;
         if (i >= 0 && r < R && t < cl) {
-            const int o = it.qk_off[j];
+            const unsigned o = it.qk_off[j], o2 = o + p.N;   // second half: N/2 bf16 further
             if (MAIN) {
-                dma16(qb + o, d);
-                dma16(qb + o + p.N / 2, d + T::NTHR * 16);
-                dma16(kb + o, d + 2 * T::NTHR * 16);
-                dma16(kb + o + p.N / 2, d + 3 * T::NTHR * 16);
+                dma16(qb, o, d);
+                dma16(qb, o2, d + T::NTHR * 16);
+                dma16(kb, o, d + 2 * T::NTHR * 16);
+                dma16(kb, o2, d + 3 * T::NTHR * 16);
             } else {
-                dma16(kb + o, d);
-                dma16(kb + o + p.N / 2, d + T::NTHR * 16);
+                dma16(kb, o, d);
+                dma16(kb, o2, d + T::NTHR * 16);
             }
         }
     }
@@ -329,34 +392,35 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const Items<RP, 
         const int e = tid + j * T::NTHR;
         const int t = e % T::Cp, pc = (e / T::Cp) * 8;
         if (e < T::Cp * (PT / 8) && t < cl && pc < p.P)
-            dma16(vb + (long)t * p.H * p.P + pc, stg + SG::V + j * T::NTHR * 16 + wave * 1024);
+            dma16(vb, it.v_off[j], stg + SG::V + j * T::NTHR * 16 + wave * 1024);
     }
     const float* ab = p.angles + ((long)(b * p.S + c0) * p.H + h) * p.W;
 #pragma unroll
     for (int j = 0; j < T::ANG_IT; ++j)
-        if (it.ang_t[j] >= 0 && it.ang_t[j] < cl) dma4(ab + it.ang_off[j], stg + SG::ANG + j * T::NTHR * 4 + wave * 256);
+        if (it.ang_t[j] >= 0 && it.ang_t[j] < cl) dma4(ab, it.ang_off[j], stg + SG::ANG + j * T::NTHR * 4 + wave * 256);
     if (MAIN && p.need_y) {
         const float* sb = p.segsum + ((long)bh * p.nc + c) * p.C * p.C;
 #pragma unroll
         for (int j = 0; j < T::SEG_IT; ++j) {
             const int e = tid + j * T::NTHR;
-            if (e < p.C * p.C) dma4(sb + e, stg + SG::SEG + j * T::NTHR * 4 + wave * 256);
+            if (e < p.C * p.C) dma4(sb, 4u * e, stg + SG::SEG + j * T::NTHR * 4 + wave * 256);
         }
     }
     if (wave == 0) {
         const long tok = (long)bh * p.S + c0;
         unsigned char* sc = stg + SG::SCAL;
+        const unsigned o4 = 4u * tid, o2 = 2u * tid;
         if (tid < cl) {
-            dma4(p.dt + tok + tid, sc);
-            dma2(p.trap + tok + tid, sc + 2 * 256);
-            dma4(p.da_cs_rev + tok + tid, sc + 5 * 256);
-            if (MAIN) dma4(p.da_cs + tok + tid, sc + 4 * 256);
+            dma4(p.dt + tok, o4, sc);
+            dma2(p.trap + tok, o2, sc + 2 * 256);
+            dma4(p.da_cs_rev + tok, o4, sc + 5 * 256);
+            if (MAIN) dma4(p.da_cs + tok, o4, sc + 4 * 256);
             if (c0 + tid + 1 < p.S) {
-                dma4(p.dt + tok + tid + 1, sc + 1 * 256);
-                dma2(p.trap + tok + tid + 1, sc + 3 * 256);
+                dma4(p.dt + tok + 1, o4, sc + 1 * 256);
+                dma2(p.trap + tok + 1, o2, sc + 3 * 256);
             }
         }
-        if (tid == 0) dma4(p.da_cs + tok + cl - 1, sc + 6 * 256);
+        if (tid == 0) dma4(p.da_cs + tok + cl - 1, 0u, sc + 6 * 256);
     }
 }
 
@@ -603,9 +667,9 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
         } else {
             load_chunk(p, it, b, h, bh, c, c0, cl, in);
         }
-        __syncthreads();   // previous chunk done with LDS (and tables written)
+        bar();   // previous chunk done with LDS (and tables written)
         phase0(p, it, c0, cl, in, smem, L);
-        __syncthreads();
+        bar();
         // kappa^T = bf16(bf16(rot(bf16(k + bf16(k_bias))) * factor) * exp(da_cs_rev)), transposed
 #pragma unroll
         for (int j = 0; j < T::QK_IT; ++j) {
@@ -636,7 +700,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
             }
         }
         fill_psi(p, cl, in, smem, L);
-        __syncthreads();
+        bar();
         const float dl = sc[4 * kTok];
 #pragma unroll
         for (int w = 0; w < T::STW; ++w) {
@@ -673,6 +737,18 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
 }
 
 // ---------------------------------------------------------------- main chunk pass
+// dz rows of one chunk (first token c0, cl tokens) from LDS ([t][P + 8] bf16) to
+// global, 16 bytes a thread.
+template <int NTHR>
+__device__ __forceinline__ void flush_dz(const Params& p, const unsigned short* sDz, int b, int h, int c0, int cl) {
+    const int P8 = p.P / 8;
+    unsigned short* dst = p.dz + ((long)(b * p.S + c0) * p.H + h) * p.P;
+    for (int e = threadIdx.x; e < cl * P8; e += NTHR) {
+        const int t = e / P8, pc = (e - t * P8) * 8;
+        *reinterpret_cast<u32x4*>(dst + (long)t * p.H * p.P + pc) = lds_ld<u32x4>(sDz + t * (p.P + 8) + pc);
+    }
+}
+
 template <int RP, int CT, int NT, int PT>
 __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params p) {
     using T = Tile<RP, CT, NT, PT>;
@@ -689,6 +765,8 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
     const float* scs = reinterpret_cast<const float*>(smem + L.cs);
     const float* sE = reinterpret_cast<const float*>(smem + L.se);
     float* sQK = reinterpret_cast<float*>(smem + L.qk);
+    unsigned short* sDz = reinterpret_cast<unsigned short*>(smem + L.dz);
+    constexpr int QKS = RP * RP + 1;   // sQK pitch per token
     const float* sc = reinterpret_cast<const float*>(smem + L.sc);
     const unsigned short* tbq = reinterpret_cast<const unsigned short*>(smem + L.tb);
     const unsigned short* tbk = tbq + p.R * p.N;
@@ -761,6 +839,18 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         }
     }
     const float dval = p.has_d ? p.d[h] : 0.f;
+    // byte offsets of this lane's gate inputs inside a chunk's [C, H, P] rows
+    unsigned gate_off[T::PW][4];
+#pragma unroll
+    for (int ps = 0; ps < T::PW; ++ps) {
+        const int pair = wave + ps * NW;
+        const int tt = pair / PTT, pc = 16 * (pair % PTT) + l16;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int t = 16 * tt + 4 * q4 + v;
+            gate_off[ps][v] = (pair < T::NPAIRS && pc < p.P) ? 2u * (unsigned)(t * p.H * p.P + pc) : kOut;
+        }
+    }
     using SG = Stage<RP, CT, NT, PT, true>;
     __shared__ __align__(16) unsigned char stg[SG::ON ? SG::BYTES : 16];
     if constexpr (SG::ON) prefetch_chunk<RP, CT, NT, PT, true>(p, it, b, h, bh, c_begin, c_begin * p.C, min(p.C, p.S - c_begin * p.C), stg);
@@ -778,27 +868,29 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         } else {
             load_chunk(p, it, b, h, bh, c, c0, cl, in);
         }
-        // gate inputs of this lane's tokens (read in the epilogue)
-        float zr[T::PW][4], dr[T::PW][4];
+        // gate inputs of this lane's tokens, raw bf16, consumed in the epilogue. The
+        // loads are issued unconditionally (lanes without a token read the chunk's
+        // first element) so that nothing waits for them before the epilogue.
+        // Buffer loads over the chunk's rows of z and dout: lanes past the chunk's
+        // end fall outside the buffer and read zero. Without gating the loads still
+        // run (from v) so that every iteration loads and consumes the same
+        // registers (see the end of the loop).
+        unsigned short zraw[T::PW][4], draw[T::PW][4];
         {
             const long base = ((long)(b * p.S + c0)) * p.H * p.P + (long)h * p.P;
+            const unsigned bytes = 2u * (unsigned)((cl - 1) * p.H * p.P + p.P);
+            const auto zb = buffer((p.has_z ? p.z : (need_y ? p.dout : p.v)) + base, bytes);
+            const auto db = p.reduce_o ? buffer(p.dout + base, bytes) : zb;
 #pragma unroll
             for (int ps = 0; ps < T::PW; ++ps) {
-                const int pair = wave + ps * NW;
-                const int tt = pair / PTT, pc = 16 * (pair % PTT) + l16;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int t = 16 * tt + 4 * q4 + v;
-                    zr[ps][v] = dr[ps][v] = 0.f;
-                    if (need_y && pair < T::NPAIRS && t < cl && pc < p.P) {
-                        const int o = t * p.H * p.P + pc;
-                        if (p.has_z) zr[ps][v] = bf2f(p.z[base + o]);
-                        if (p.reduce_o) dr[ps][v] = bf2f(p.dout[base + o]);
-                    }
+                    zraw[ps][v] = __builtin_amdgcn_raw_buffer_load_b16(zb, gate_off[ps][v], 0, 0);
+                    draw[ps][v] = __builtin_amdgcn_raw_buffer_load_b16(db, gate_off[ps][v], 0, 0);
                 }
             }
         }
-        __syncthreads();   // previous chunk (and the tables) done
+        bar();   // previous chunk (and the tables) done
 
         // ---- states[c] = bf16(S entering chunk c), from sSbT ([p][n]) to [n][p], 16 bytes a thread
         {
@@ -814,10 +906,12 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                 *reinterpret_cast<u32x4*>(dst + n * p.P + pc) = o;
             }
         }
+        // ---- dz of the previous chunk (always a full one), staged in LDS by its epilogue
+        if (p.has_z && c > c_begin) flush_dz<NTHR>(p, sDz, b, h, c0 - p.C, p.C);
 
         // ---- phase 0: token scalars, cos/sin, exp(segsum)
         phase0(p, it, c0, cl, in, smem, L);
-        __syncthreads();
+        bar();
 
         // ---- phase A: biased q/k (unrotated into LDS, rotated kept in registers), Psi^T
         u32x4 rq0[T::QK_IT], rq1[T::QK_IT], rk0[T::QK_IT], rk1[T::QK_IT];
@@ -862,31 +956,35 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             }
         }
         fill_psi(p, cl, in, smem, L);
-        __syncthreads();
+        bar();
 
-        // ---- phase B: qk_dot of the same token (biased, unrotated), fp32 accumulate
+        // ---- phase B: qk_dot of the same token (biased, unrotated), fp32 accumulate;
+        // padded rank pairs get zero
         {
             const int RR = R * R;
             unsigned short* qko = p.qk_dot + ((long)bh * p.S + c0) * RR;
-            for (int e = tid; e < cl * RR; e += NTHR) {
+            for (int e = tid; e < cl * RP * RP; e += NTHR) {
                 const int rr = e / cl, t = e - rr * cl;   // consecutive threads: consecutive tokens
-                const int r = rr / R, r2 = rr - r * R;
-                const unsigned short* xq = sQ + (r * Cp + t) * LDQ;
-                const unsigned short* xk = sK + (r2 * Cp + t) * LDQ;
+                const int r = rr / RP, r2 = rr % RP;
                 float sum = 0.f;
-                for (int n = 0; n < p.N; n += 8) {
-                    const u32x4 a = lds_ld<u32x4>(xq + n), bb = lds_ld<u32x4>(xk + n);
-                    sum = dot2(a[0], bb[0], sum);
-                    sum = dot2(a[1], bb[1], sum);
-                    sum = dot2(a[2], bb[2], sum);
-                    sum = dot2(a[3], bb[3], sum);
+                if (r < R && r2 < R) {
+                    const unsigned short* xq = sQ + (r * Cp + t) * LDQ;
+                    const unsigned short* xk = sK + (r2 * Cp + t) * LDQ;
+                    for (int n = 0; n < p.N; n += 8) {
+                        const u32x4 a = lds_ld<u32x4>(xq + n), bb = lds_ld<u32x4>(xk + n);
+                        sum = dot2(a[0], bb[0], sum);
+                        sum = dot2(a[1], bb[1], sum);
+                        sum = dot2(a[2], bb[2], sum);
+                        sum = dot2(a[3], bb[3], sum);
+                    }
+                    const unsigned u = pk2(sum, 0.f);
+                    sum = lo16(u);
+                    qko[t * RR + r * R + r2] = static_cast<unsigned short>(u);
                 }
-                const unsigned u = pk2(sum, 0.f);
-                sQK[t * (RR + 1) + rr] = lo16(u);
-                qko[t * RR + rr] = static_cast<unsigned short>(u);
+                sQK[t * QKS + rr] = sum;
             }
         }
-        __syncthreads();
+        bar();
 
         // ---- phase C: rotated q and factor-scaled k into LDS
 #pragma unroll
@@ -901,7 +999,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             lds_st<u32x4>(sK + i * LDQ + col0, rk0[j]);
             lds_st<u32x4>(sK + i * LDQ + col1, rk1[j]);
         }
-        __syncthreads();
+        bar();
 
         f32x4 acc[T::PW][RP];
         if (need_y) {
@@ -955,7 +1053,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                     at[w] = u32x2{pk2(m[0], m[1]), pk2(m[2], m[3])};
                 }
             }
-            __syncthreads();   // every wave is done reading sQ
+            bar();   // every wave is done reading sQ
 #pragma unroll
             for (int w = 0; w < T::ATW; ++w) {
                 const int u = wave + w * NW;
@@ -964,7 +1062,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                     lds_st<u32x2>(sA + (16 * i16 + l16) * LDA + 16 * jt + 4 * q4, at[w]);
                 }
             }
-            __syncthreads();
+            bar();
             // ---- intra = A Psi, accumulated onto the scaled inter term
 #pragma unroll
             for (int ps = 0; ps < T::PW; ++ps) {
@@ -985,7 +1083,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                     }
                 }
             }
-            __syncthreads();   // every wave is done reading sA
+            bar();   // every wave is done reading sA
         }
 
         // ---- kappa^T = bf16(K~ * exp(da_cs_rev)), transposed, into R1
@@ -1004,7 +1102,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                 }
             }
         }
-        __syncthreads();
+        bar();
 
         // ---- state update S <- S * exp(da_cs[last]) + kappa^T Psi; bf16 copy for the next chunk
         {
@@ -1027,9 +1125,10 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             emit_state();
         }
 
-        // ---- y = bf16(inter + intra + diag + d*Psi) and the gating gradients
+        // ---- y = bf16(inter + intra + diag + d*Psi) and the gating gradients. Ranks
+        // r >= R run on zero data (zero Psi rows, qk pairs and projections) and add
+        // nothing, so the rank loops need no bounds.
         if (need_y) {
-            const long base = ((long)(b * p.S + c0)) * p.H * p.P + (long)h * p.P;
 #pragma unroll
             for (int ps = 0; ps < T::PW; ++ps) {
                 const int pair = wave + ps * NW;
@@ -1037,10 +1136,18 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                 const int tt = pair / PTT, pt = pair % PTT;
                 const int pc = 16 * pt + l16;
                 const int tb = 16 * tt + 4 * q4;   // first of this lane's 4 tokens
+                bool ok[4];
+                float zr[4], dr[4];   // zero outside the chunk (buffer range)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    ok[v] = tb + v < cl && pc < p.P;
+                    zr[v] = bf2f(zraw[ps][v]);
+                    dr[v] = bf2f(draw[ps][v]);
+                }
                 float psi[RP][4];
 #pragma unroll
                 for (int r2 = 0; r2 < RP; ++r2) {
-                    const u32x2 x = (r2 < R) ? lds_ld<u32x2>(sPsiT + pc * LDA + r2 * Cp + tb) : u32x2{0u, 0u};
+                    const u32x2 x = lds_ld<u32x2>(sPsiT + pc * LDA + r2 * Cp + tb);
                     psi[r2][0] = lo16(x[0]);
                     psi[r2][1] = hi16(x[0]);
                     psi[r2][2] = lo16(x[1]);
@@ -1050,24 +1157,22 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                 float dzc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
-                    if (r >= R) continue;
                     // diagonal of two tokens at a time: rank-ordered bf16 products and sums
                     float y[4];
 #pragma unroll
                     for (int vp = 0; vp < 2; ++vp) {
                         const int va = 2 * vp, vb = va + 1;
-                        const float* qa = sQK + (tb + va) * (R * R + 1) + r * R;
-                        const float* qb = sQK + (tb + vb) * (R * R + 1) + r * R;
-                        float da = 0.f, db = 0.f;
+                        const float* qa = sQK + (tb + va) * QKS + r * RP;
+                        const float* qb = sQK + (tb + vb) * QKS + r * RP;
+                        float da = qa[0] * psi[0][va], db = qb[0] * psi[0][vb];
+                        rnd2(da, db);
 #pragma unroll
-                        for (int r2 = 0; r2 < RP; ++r2) {
-                            if (r2 < R) {
-                                float pa = qa[r2] * psi[r2][va], pb = qb[r2] * psi[r2][vb];
-                                rnd2(pa, pb);
-                                da += pa;
-                                db += pb;
-                                rnd2(da, db);
-                            }
+                        for (int r2 = 1; r2 < RP; ++r2) {
+                            float pa = qa[r2] * psi[r2][va], pb = qb[r2] * psi[r2][vb];
+                            rnd2(pa, pb);
+                            da += pa;
+                            db += pb;
+                            rnd2(da, db);
                         }
                         da *= gam4[va];
                         db *= gam4[vb];
@@ -1084,26 +1189,27 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                         float sg[4], pz[4], G[4], gz[4];
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
-                            pz[v] = zr[ps][v] * cz[ps][r];
+                            pz[v] = zr[v] * cz[ps][r];
                             sg[v] = sigmoid_fast(pz[v]);
                         }
                         if (p.reduce_o) {
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
-                                dmo[ps][r] += (y[v] * (pz[v] * sg[v])) * dr[ps][v];
-                                G[v] = dr[ps][v] * co[ps][r];
+                                dmo[ps][r] += (y[v] * (pz[v] * sg[v])) * dr[v];
+                                G[v] = dr[v] * co[ps][r];
                             }
                             rnd2(G[0], G[1]);
                             rnd2(G[2], G[3]);
 #pragma unroll
                             for (int v = 0; v < 4; ++v) G[v] *= y[v];
                         } else {
+                            // per-rank dout [B,S,R,H,P]; lanes without a token read element 0
                             const long nb = ((long)(b * p.S + c0) * R + r) * p.H * p.P + (long)h * p.P;
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
-                                const int t = tb + v;
-                                const float dn = (t < cl && pc < p.P) ? bf2f(p.dout[nb + (long)t * R * p.H * p.P + pc]) : 0.f;
-                                G[v] = dn * y[v];
+                                const bool okr = ok[v] && r < R;
+                                const unsigned short raw = p.dout[okr ? nb + (long)(tb + v) * R * p.H * p.P + pc : 0];
+                                G[v] = (okr ? bf2f(raw) : 0.f) * y[v];
                             }
                         }
                         rnd2(G[0], G[1]);
@@ -1112,22 +1218,36 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                         for (int v = 0; v < 4; ++v) {
                             gz[v] = (G[v] * sg[v]) * (1.0f + pz[v] * (1.0f - sg[v]));
                             dzc[v] += __fmul_rn(gz[v], cz[ps][r]);
-                            dmz[ps][r] += gz[v] * zr[ps][v];
+                            dmz[ps][r] += gz[v] * zr[v];
                         }
                         rnd2(dzc[0], dzc[1]);
                         rnd2(dzc[2], dzc[3]);
                     } else if (p.reduce_o) {
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) dmo[ps][r] += y[v] * dr[ps][v];
+                        for (int v = 0; v < 4; ++v) dmo[ps][r] += y[v] * dr[v];
                     }
                 }
-                if (p.has_z && pc < p.P) {
+                if (p.has_z) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        if (tb + v < cl) p.dz[base + (long)(tb + v) * p.H * p.P + pc] = f2bf(dzc[v]);
+                        if (ok[v]) sDz[(tb + v) * (p.P + 8) + pc] = f2bf(dzc[v]);
                 }
             }
         }
+        // The gate inputs are consumed on every path, so that no load of them is
+        // still pending when the next iteration reuses their registers (a pending
+        // one would make that reuse wait for every load issued since, including
+        // the prefetch).
+#pragma unroll
+        for (int ps = 0; ps < T::PW; ++ps)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) asm volatile("" ::"v"(zraw[ps][v]), "v"(draw[ps][v]));
+    }
+    if (p.has_z) {
+        // dz of the segment's last chunk
+        bar();
+        const int cl_last = min(p.C, p.S - (c_end - 1) * p.C);
+        flush_dz<NTHR>(p, sDz, b, h, (c_end - 1) * p.C, cl_last);
     }
 
     // ---- per-segment partial sums of dmimo_o / dmimo_z: reduce over the 4 lane groups
@@ -1162,7 +1282,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         } else {
             // the token tiles of one (rank, value tile) belong to different waves;
             // add them in token-tile order through LDS
-            __syncthreads();
+            bar();
             float* red = reinterpret_cast<float*>(smem);   // [2][CT][RP][PT]
             constexpr int per = RP * PT;
 #pragma unroll
@@ -1177,7 +1297,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                     }
                 }
             }
-            __syncthreads();
+            bar();
             for (int e = tid; e < R * PT; e += NTHR) {
                 const int r = e / PT, pc = e % PT;
                 if (pc < p.P) {
