@@ -41,6 +41,7 @@
 //   S' = kappa^T Psi   sKapT [n][i], sPsiT [p][i]
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -202,8 +203,8 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
     pl->off_pz = off;
     if (pl->nseg > 1 && has_z) off = align256(off + (size_t)B * H * pl->nseg * R * P * 4);
     pl->ws_bytes = off;
-    Lds lm = lds_layout(pl->MT, pl->NT, pl->PT, (int)C, (int)R, (int)N, (int)P, pl->W, true);
-    Lds la = lds_layout(pl->MT, pl->NT, pl->PT, (int)C, (int)R, (int)N, (int)P, pl->W, false);
+    Lds lm = lds_layout(RP, CT, pl->NT, pl->PT, (int)C, pl->W, true);
+    Lds la = lds_layout(RP, CT, pl->NT, pl->PT, (int)C, pl->W, false);
     pl->lds_main = lm.total;
     pl->lds_agg = la.total;
     // the token-tile reduction of the dmimo partials reuses LDS from offset 0
@@ -217,6 +218,13 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
 }
 
 int tidx(int x) { return x == 32 ? 0 : (x == 64 ? 1 : 2); }
+
+// MIMO_FORCE_GENERIC=1 in the environment disables the shape-exact kernel
+// instances (used by the tests to compare both paths on the same inputs).
+bool force_generic() {
+    const char* e = getenv("MIMO_FORCE_GENERIC");
+    return e != nullptr && e[0] == '1';
+}
 
 const Family* family(int RP, int CT) {
     switch (RP * 10 + CT) {
@@ -334,8 +342,13 @@ static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* ev
 
     const Family* fam = family(pl.RP, pl.CT);
     if (fam == nullptr) return fail(MIMO_ERR_UNSUPPORTED, "no kernel for this tile shape");
-    const kfn kmain = fam->main[tidx(pl.NT) * 3 + tidx(pl.PT)];
-    const kfn kagg = fam->agg[tidx(pl.NT) * 3 + tidx(pl.PT)];
+    // shape-exact instances when the call's shape equals the tile (see specialise())
+    const int ti = tidx(pl.NT) * 3 + tidx(pl.PT);
+    const bool ex = !force_generic() && p.R == pl.RP && p.N == pl.NT && p.P == pl.PT && p.C == pl.Cp && p.rd == 4;
+    kfn kmain = fam->main[ti];
+    if (ex && !p.need_y) kmain = fam->main_ex_noy[ti];
+    if (ex && p.reduce_o && p.has_z) kmain = fam->main_ex_rz[ti];
+    const kfn kagg = ex ? fam->agg_ex[ti] : fam->agg[ti];
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int BH = p.B * p.H;
     auto mark = [&](int i) -> mimo_status {

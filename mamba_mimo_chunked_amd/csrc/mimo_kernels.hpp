@@ -109,27 +109,30 @@ struct Tile {
     static constexpr int PW = (NPAIRS + NW - 1) / NW;                      // pairs per wave
 };
 
-// LDS carve-up (byte offsets), shared by host and device.
+// LDS carve-up (byte offsets), shared by host and device. Every region but the
+// last two depends only on the tile family (RP, CT, NT, PT), so inside a kernel
+// their offsets and pitches are compile-time constants and one per-lane address
+// register serves many accesses (the rest goes into the instructions' offset
+// field). cos/sin and exp(segsum) are sized by the runtime C and W and come last.
 struct Lds {
     int r1;   // bf16 [MT][LDQ] q (main) | [MT][LDA] causal block | [NT][LDA] kappa^T
     int r2;   // bf16 [MT][LDQ] k (main only)
     int r3;   // bf16 [PT][LDA] Psi^T
     int r4;   // bf16 [PT][LDQ] bf16(state)^T (main only)
+    int qk;   // fp32 [Cp][RP*RP+1] qk_dot, zero for padded ranks, one pad word per token (main only)
+    int dz;   // bf16 [Cp][PT+8] dz of the chunk, written out at the top of the next one (main only)
+    int sc;   // fp32 [5][kTok] token scalars + chunk decay
+    int tb;   // bf16 tables: q_bias [RP][NT], k_bias [RP][NT], mimo_v [RP][PT]
     int cs;   // fp32 [2][C][W] cos, sin
     int se;   // fp32 [C][C] exp(segsum) (main only)
-    int qk;   // fp32 [Cp][RP*RP+1] qk_dot, zero for padded ranks, one pad word per token (main only)
-    int dz;   // bf16 [C][P+8] dz of the chunk, written out at the top of the next one (main only)
-    int sc;   // fp32 [5][kTok] token scalars + chunk decay
-    int tb;   // bf16 tables: q_bias [R][N], k_bias [R][N], mimo_v [R][P]
     int total;
 };
 
 __host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
 
-__host__ __device__ inline Lds lds_layout(int MT, int NT, int PT, int C, int R, int N, int P, int W, bool main) {
+__host__ __device__ inline Lds lds_layout(int RP, int CT, int NT, int PT, int C, int W, bool main) {
+    const int Cp = 16 * CT, MT = RP * Cp < 32 ? 32 : RP * Cp;
     const int ldq = NT + 8, lda = MT + 8;
-    const int rp = R <= 1 ? 1 : (R <= 2 ? 2 : (R <= 4 ? 4 : 8));
-    const int cp = C <= 16 ? 16 : (C <= 32 ? 32 : 64);
     int r1 = NT * lda;
     if (main && MT * ldq > r1) r1 = MT * ldq;
     if (main && MT * lda > r1) r1 = MT * lda;
@@ -139,12 +142,12 @@ __host__ __device__ inline Lds lds_layout(int MT, int NT, int PT, int C, int R, 
     s.r2 = off; if (main) off += align16(MT * ldq * 2);
     s.r3 = off; off += align16(PT * lda * 2);
     s.r4 = off; if (main) off += align16(PT * ldq * 2);
+    s.qk = off; if (main) off += align16(Cp * (RP * RP + 1) * 4);
+    s.dz = off; if (main) off += align16(Cp * (PT + 8) * 2);
+    s.sc = off; off += align16((5 * kTok + 4) * 4);
+    s.tb = off; off += align16((2 * RP * NT + RP * PT) * 2);
     s.cs = off; off += align16(2 * C * W * 4);
     s.se = off; if (main) off += align16(C * C * 4);
-    s.qk = off; if (main) off += align16(cp * (rp * rp + 1) * 4);
-    s.dz = off; if (main) off += align16(C * (P + 8) * 2);
-    s.sc = off; off += align16((5 * kTok + 4) * 4);
-    s.tb = off; off += align16((2 * R * N + R * P) * 2);
     s.total = off;
     return s;
 }
@@ -313,11 +316,11 @@ struct Stage {
     static constexpr bool ON = DYN + BYTES <= 80 * 1024;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // One global_load_lds per lane: 16, 4 or 2 bytes from base + off (base the same
 // for every lane, off a 32-bit byte offset) into the wave's LDS block at dst_wave
-// (M0 holds its LDS address). Written as inline assembly so that the compiler's
+// (M0 holds its LDS address: the low 32 bits of a generic pointer into LDS are
+// the LDS byte address, the high half being the shared aperture). Written as inline assembly so that the compiler's
 // wait-count tracking does not treat the address registers as pending until the
 // load completes (it would then wait for the whole prefetch as soon as such a
 // register is reused). The waits are explicit instead: s_waitcnt vmcnt(0) before
@@ -343,7 +346,7 @@ constexpr unsigned kOut = 0x80000000u;   // buffer offset that is always out of 
 #define MIMO_DMA(NAME, INSN)                                                                          \
     __device__ __forceinline__ void NAME(const void* base, unsigned off, unsigned char* dst_wave) { \
         const void* sb = sgpr_ptr(base);                                                            \
-        const unsigned m = rfl(static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)dst_wave))); \
+        const unsigned m = rfl(static_cast<unsigned>(reinterpret_cast<uintptr_t>(dst_wave)));      \
         unsigned saved;                                                                             \
         asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t" INSN                       \
                      " %1, %2\n\ts_mov_b32 m0, %0"                                                  \
@@ -550,7 +553,7 @@ __device__ __forceinline__ void fill_psi(const Params& p, int cl, const ChunkIn<
     using T = Tile<RP, CT, NT, PT>;
     const int tid = threadIdx.x;
     unsigned short* sPsiT = reinterpret_cast<unsigned short*>(smem + L.r3);
-    const unsigned short* smv = reinterpret_cast<const unsigned short*>(smem + L.tb) + 2 * p.R * p.N;
+    const unsigned short* smv = reinterpret_cast<const unsigned short*>(smem + L.tb) + 2 * RP * NT;
 #pragma unroll
     for (int j = 0; j < T::PSI_IT; ++j) {
         const int e = tid + j * T::NTHR;
@@ -560,7 +563,7 @@ __device__ __forceinline__ void fill_psi(const Params& p, int cl, const ChunkIn<
         for (int r = 0; r < p.R; ++r) {
             unsigned short* dst = sPsiT + pc * T::LDA + r * T::Cp + t;
             if (real) {
-                const u32x4 mv = lds_ld<u32x4>(smv + r * p.P + pc);
+                const u32x4 mv = lds_ld<u32x4>(smv + r * PT + pc);
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
                     const unsigned u = pk2(lo16(in.v[j][d]) * lo16(mv[d]), hi16(in.v[j][d]) * hi16(mv[d]));
@@ -581,13 +584,17 @@ template <int RP, int CT, int NT, int PT>
 __device__ __forceinline__ void fill_tables(const Params& p, int h, unsigned char* smem, const Lds& L) {
     using T = Tile<RP, CT, NT, PT>;
     const int tid = threadIdx.x;
-    unsigned short* tb = reinterpret_cast<unsigned short*>(smem + L.tb);
+    unsigned short* tb = reinterpret_cast<unsigned short*>(smem + L.tb);   // [RP][NT] x2, [RP][PT]
     const int RN = p.R * p.N, RPn = p.R * p.P;
     for (int e = tid; e < RN; e += T::NTHR) {
-        tb[e] = f2bf(p.q_bias[(long)h * RN + e]);
-        tb[RN + e] = f2bf(p.k_bias[(long)h * RN + e]);
+        const int r = e / p.N, n = e - r * p.N;
+        tb[r * NT + n] = f2bf(p.q_bias[(long)h * RN + e]);
+        tb[RP * NT + r * NT + n] = f2bf(p.k_bias[(long)h * RN + e]);
     }
-    for (int e = tid; e < RPn; e += T::NTHR) tb[2 * RN + e] = f2bf(p.mimo_v[(long)h * RPn + e]);
+    for (int e = tid; e < RPn; e += T::NTHR) {
+        const int r = e / p.P, pc = e - r * p.P;
+        tb[2 * RP * NT + r * PT + pc] = f2bf(p.mimo_v[(long)h * RPn + e]);
+    }
     unsigned short* sPsiT = reinterpret_cast<unsigned short*>(smem + L.r3);
     const int used = p.R * T::Cp, pad = T::MT - used;
     for (int e = tid; e < PT * pad; e += T::NTHR) {
@@ -616,19 +623,49 @@ __device__ __forceinline__ bool map_block(const Params& p, int nseg_k, int& seg,
     return true;
 }
 
+// ---------------------------------------------------------------- kernel specialisation
+// EX: the call's shape equals the tile (R = RP, N = NT, P = PT, C = Cp) with rotary
+// divisor 4, so sizes, pitches and bounds fold to constants. MODE: -1 reads the
+// branch flags at run time; 0 = no y (neither reduced dout nor z); 1 = reduced
+// dout with z. Returns the parameters with those fields replaced by constants.
+template <int RP, int CT, int NT, int PT, bool EX, int MODE>
+__device__ __forceinline__ Params specialise(const Params& pin) {
+    Params p = pin;
+    if constexpr (EX) {
+        p.R = RP;
+        p.N = NT;
+        p.P = PT;
+        p.C = 16 * CT;
+        p.rd = 4;
+        p.W = NT / 4;
+    }
+    if constexpr (MODE == 0) {
+        p.need_y = 0;
+        p.reduce_o = 0;
+        p.has_z = 0;
+    }
+    if constexpr (MODE == 1) {
+        p.need_y = 1;
+        p.reduce_o = 1;
+        p.has_z = 1;
+    }
+    return p;
+}
+
 // ---------------------------------------------------------------- segment aggregate
 // U_s = state added by segment s from a zero start: U <- U*exp(da_cs[last]) + kappa^T Psi
 // per chunk; also the product of the chunk decays.
-template <int RP, int CT, int NT, int PT>
-__global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params p) {
+template <int RP, int CT, int NT, int PT, bool EX>
+__global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params pin) {
+    const Params p = specialise<RP, CT, NT, PT, EX, -1>(pin);
     using T = Tile<RP, CT, NT, PT>;
     extern __shared__ __align__(16) unsigned char smem[];
-    const Lds L = lds_layout(T::MT, NT, PT, p.C, p.R, p.N, p.P, p.W, false);
+    const Lds L = lds_layout(RP, CT, NT, PT, p.C, p.W, false);
     unsigned short* sKapT = reinterpret_cast<unsigned short*>(smem + L.r1);
     const unsigned short* sPsiT = reinterpret_cast<const unsigned short*>(smem + L.r3);
     const float* sc = reinterpret_cast<const float*>(smem + L.sc);
     const float* scs = reinterpret_cast<const float*>(smem + L.cs);
-    const unsigned short* tbk = reinterpret_cast<const unsigned short*>(smem + L.tb) + p.R * p.N;
+    const unsigned short* tbk = reinterpret_cast<const unsigned short*>(smem + L.tb) + RP * NT;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -678,8 +715,8 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
             const int r = i / T::Cp, t = i % T::Cp;
             if (r >= R || t >= cl) continue;   // stays zero from the initial fill / last chunk
             const int col0 = it.qk_col[j], col1 = p.N / 2 + col0;
-            u32x4 a = add_bias(in.k0[j], lds_ld<u32x4>(tbk + r * p.N + col0));
-            u32x4 e = add_bias(in.k1[j], lds_ld<u32x4>(tbk + r * p.N + col1));
+            u32x4 a = add_bias(in.k0[j], lds_ld<u32x4>(tbk + r * NT + col0));
+            u32x4 e = add_bias(in.k1[j], lds_ld<u32x4>(tbk + r * NT + col1));
             rotate_group(a, e, col0, p.W, scs + t * p.W, scs + p.C * p.W + t * p.W);
             const float f = sc[3 * kTok + t], er = sc[2 * kTok + t];
             a = scale_group(scale_group(a, f), er);
@@ -737,25 +774,26 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
 }
 
 // ---------------------------------------------------------------- main chunk pass
-// dz rows of one chunk (first token c0, cl tokens) from LDS ([t][P + 8] bf16) to
+// dz rows of one chunk (first token c0, cl tokens) from LDS ([t][PT + 8] bf16) to
 // global, 16 bytes a thread.
-template <int NTHR>
+template <int NTHR, int PT>
 __device__ __forceinline__ void flush_dz(const Params& p, const unsigned short* sDz, int b, int h, int c0, int cl) {
     const int P8 = p.P / 8;
     unsigned short* dst = p.dz + ((long)(b * p.S + c0) * p.H + h) * p.P;
     for (int e = threadIdx.x; e < cl * P8; e += NTHR) {
         const int t = e / P8, pc = (e - t * P8) * 8;
-        *reinterpret_cast<u32x4*>(dst + (long)t * p.H * p.P + pc) = lds_ld<u32x4>(sDz + t * (p.P + 8) + pc);
+        *reinterpret_cast<u32x4*>(dst + (long)t * p.H * p.P + pc) = lds_ld<u32x4>(sDz + t * (PT + 8) + pc);
     }
 }
 
-template <int RP, int CT, int NT, int PT>
-__global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params p) {
+template <int RP, int CT, int NT, int PT, bool EX, int MODE>
+__global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params pin) {
+    const Params p = specialise<RP, CT, NT, PT, EX, MODE>(pin);
     using T = Tile<RP, CT, NT, PT>;
     constexpr int MT = T::MT, NW = T::NW, NTHR = T::NTHR, Cp = T::Cp;
     constexpr int LDQ = T::LDQ, LDA = T::LDA, PTT = T::PTT, MTT = T::MTT;
     extern __shared__ __align__(16) unsigned char smem[];
-    const Lds L = lds_layout(MT, NT, PT, p.C, p.R, p.N, p.P, p.W, true);
+    const Lds L = lds_layout(RP, CT, NT, PT, p.C, p.W, true);
     unsigned short* sQ = reinterpret_cast<unsigned short*>(smem + L.r1);   // also sA, sKapT
     unsigned short* sA = sQ;
     unsigned short* sKapT = sQ;
@@ -769,7 +807,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
     constexpr int QKS = RP * RP + 1;   // sQK pitch per token
     const float* sc = reinterpret_cast<const float*>(smem + L.sc);
     const unsigned short* tbq = reinterpret_cast<const unsigned short*>(smem + L.tb);
-    const unsigned short* tbk = tbq + p.R * p.N;
+    const unsigned short* tbk = tbq + RP * NT;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -907,7 +945,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             }
         }
         // ---- dz of the previous chunk (always a full one), staged in LDS by its epilogue
-        if (p.has_z && c > c_begin) flush_dz<NTHR>(p, sDz, b, h, c0 - p.C, p.C);
+        if (p.has_z && c > c_begin) flush_dz<NTHR, PT>(p, sDz, b, h, c0 - p.C, p.C);
 
         // ---- phase 0: token scalars, cos/sin, exp(segsum)
         phase0(p, it, c0, cl, in, smem, L);
@@ -923,10 +961,10 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             const int col0 = it.qk_col[j], col1 = p.N / 2 + col0;
             u32x4 qa = {0u, 0u, 0u, 0u}, qb = qa, ka = qa, kb = qa;
             if (r < R && t < cl) {
-                qa = add_bias(in.q0[j], lds_ld<u32x4>(tbq + r * p.N + col0));
-                qb = add_bias(in.q1[j], lds_ld<u32x4>(tbq + r * p.N + col1));
-                ka = add_bias(in.k0[j], lds_ld<u32x4>(tbk + r * p.N + col0));
-                kb = add_bias(in.k1[j], lds_ld<u32x4>(tbk + r * p.N + col1));
+                qa = add_bias(in.q0[j], lds_ld<u32x4>(tbq + r * NT + col0));
+                qb = add_bias(in.q1[j], lds_ld<u32x4>(tbq + r * NT + col1));
+                ka = add_bias(in.k0[j], lds_ld<u32x4>(tbk + r * NT + col0));
+                kb = add_bias(in.k1[j], lds_ld<u32x4>(tbk + r * NT + col1));
             }
             lds_st<u32x4>(sQ + i * LDQ + col0, qa);
             lds_st<u32x4>(sQ + i * LDQ + col1, qb);
@@ -1230,7 +1268,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                 if (p.has_z) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        if (ok[v]) sDz[(tb + v) * (p.P + 8) + pc] = f2bf(dzc[v]);
+                        if (ok[v]) sDz[(tb + v) * (PT + 8) + pc] = f2bf(dzc[v]);
                 }
             }
         }
@@ -1247,7 +1285,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         // dz of the segment's last chunk
         bar();
         const int cl_last = min(p.C, p.S - (c_end - 1) * p.C);
-        flush_dz<NTHR>(p, sDz, b, h, (c_end - 1) * p.C, cl_last);
+        flush_dz<NTHR, PT>(p, sDz, b, h, (c_end - 1) * p.C, cl_last);
     }
 
     // ---- per-segment partial sums of dmimo_o / dmimo_z: reduce over the 4 lane groups
@@ -1319,20 +1357,25 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
 typedef void (*kfn)(Params);
 
 // The 9 (NT, PT) combinations of one (RP, CT) family, indexed 3 * idx(NT) + idx(PT)
-// with idx(32, 64, 128) = 0, 1, 2.
+// with idx(32, 64, 128) = 0, 1, 2: the generic instances and the shape-exact ones.
 struct Family {
-    kfn agg[9];
-    kfn main[9];
+    kfn agg[9], agg_ex[9];
+    kfn main[9], main_ex_noy[9], main_ex_rz[9];
 };
 
 #define MIMO_NP_LIST(F, RP, CT)                                                                             \
     F(RP, CT, 32, 32), F(RP, CT, 32, 64), F(RP, CT, 32, 128), F(RP, CT, 64, 32), F(RP, CT, 64, 64),         \
         F(RP, CT, 64, 128), F(RP, CT, 128, 32), F(RP, CT, 128, 64), F(RP, CT, 128, 128)
-#define MIMO_AGG_FN(RP, CT, NT, PT) k_agg<RP, CT, NT, PT>
-#define MIMO_MAIN_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT>
+#define MIMO_AGG_FN(RP, CT, NT, PT) k_agg<RP, CT, NT, PT, false>
+#define MIMO_AGG_EX_FN(RP, CT, NT, PT) k_agg<RP, CT, NT, PT, true>
+#define MIMO_MAIN_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT, false, -1>
+#define MIMO_MAIN_EX0_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT, true, 0>
+#define MIMO_MAIN_EX1_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT, true, 1>
 #define MIMO_FAMILY(RP, CT)                                                                               \
     const Family* family_rp##RP##_ct##CT() {                                                              \
-        static const Family f = {{MIMO_NP_LIST(MIMO_AGG_FN, RP, CT)}, {MIMO_NP_LIST(MIMO_MAIN_FN, RP, CT)}}; \
+        static const Family f = {{MIMO_NP_LIST(MIMO_AGG_FN, RP, CT)},     {MIMO_NP_LIST(MIMO_AGG_EX_FN, RP, CT)}, \
+                                 {MIMO_NP_LIST(MIMO_MAIN_FN, RP, CT)},    {MIMO_NP_LIST(MIMO_MAIN_EX0_FN, RP, CT)}, \
+                                 {MIMO_NP_LIST(MIMO_MAIN_EX1_FN, RP, CT)}};                               \
         return &f;                                                                                        \
     }
 #define MIMO_DECL_FAMILY(RP, CT) const Family* family_rp##RP##_ct##CT();

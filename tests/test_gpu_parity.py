@@ -191,3 +191,25 @@ def test_unused_segsum_entries_ignored():
     b = _gpu_np(run_gpu(to_device(dict(inp, segsum=seg))))
     for i in range(5):
         assert _same(a[i], b[i]), NAMES[i]
+
+
+@pytest.mark.parametrize("case", [
+    Case(1, 1000, 4, 1, 64, 64, 4, 16, name="exact_reduced_z"),
+    Case(2, 777, 4, 2, 64, 64, 4, 16, reduce_o=False, has_z=False, name="exact_no_y"),
+    Case(1, 500, 2, 1, 128, 64, 2, 64, name="exact_c64_n128"),
+], ids=lambda c: c.name)
+def test_shape_exact_and_generic_kernels_agree(case, monkeypatch):
+    """Shapes equal to their tile run shape-specialised kernel instances; the
+    generic instances (forced through MIMO_FORCE_GENERIC) must give the same
+    outputs on the same inputs, and both must meet the oracle bar."""
+    log(f"[exact-vs-generic] {case}")
+    d = to_device(make_inputs(case))
+    ex = run_gpu(d)
+    monkeypatch.setenv("MIMO_FORCE_GENERIC", "1")
+    gen = run_gpu(d)
+    monkeypatch.delenv("MIMO_FORCE_GENERIC")
+    ref = oracle(make_inputs(case))
+    compare(ex, ref, label="exact ")
+    compare(gen, ref, label="generic ")
+    for name, a, b in zip(NAMES, _gpu_np(ex), _gpu_np(gen)):
+        assert _same(a, b), f"{name}: shape-exact and generic instances differ"
