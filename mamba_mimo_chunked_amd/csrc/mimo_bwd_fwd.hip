@@ -11,9 +11,10 @@
 // Work decomposition. Chunks of one (batch, head) form a serial fp32 state
 // recurrence S_{c+1} = S_c * exp(da_cs[last(c)]) + kappa_c^T Psi_c, which is
 // elementwise-linear in the [N,P] state. The chunks are grouped into
-// segments of L consecutive chunks:
-//   k_agg   (segment-parallel)  the state each segment adds from a zero start,
-//                               and its decay product;
+// segments of L consecutive chunks, and each segment but the last into F
+// sub-segments of L/F chunks:
+//   k_agg   (sub-segment-parallel) the state each sub-segment adds from a zero
+//                               start, and its decay product;
 //   k_scan  ((n,p)-parallel)    the state entering every segment;
 //   k_main  (segment-parallel)  walks its L chunks from the entry state: bf16
 //                               entry states, qk_dot, the chunk-local causal
@@ -51,54 +52,53 @@
 namespace mimo {
 
 // ---------------------------------------------------------------- segment scan
-// In place: agg[s] <- E_{s+1} = E_s * decay_s + U_s, E_0 = 0. Each thread owns
-// four consecutive state elements. Loads run ahead of the serial chain.
+// Over the sub-segments j of one (batch, head): E_{j+1} = E_j * decay_j + U_j with
+// E_0 = 0, written in place to agg[j] where the chunk kernel reads it, i.e. at the
+// end of each segment ((j + 1) % F == 0). One thread per state element (the
+// chain is latency-bound, so more waves keep more loads in flight); loads run
+// up to 32 sub-segments ahead of the serial chain.
 __global__ __launch_bounds__(256) void k_scan(Params p) {
     const int bh = blockIdx.y;
     const int NP = p.N * p.P;
-    const int e4 = blockIdx.x * 256 + threadIdx.x;
-    if (4 * e4 >= NP) return;
-    const int ns = p.nseg - 1;
-    float* base = p.agg + (long)bh * ns * NP + 4 * e4;
-    const float* dec = p.decay + (long)bh * p.nseg;
-    float4 E = make_float4(0.f, 0.f, 0.f, 0.f);
-    constexpr int AHEAD = 8;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= NP) return;
+    const int ns = p.nsub;
+    float* base = p.agg + (long)bh * ns * NP + e;
+    const float* dec = p.decay + (long)bh * ns;
+    float E = 0.f;
+    constexpr int AHEAD = 32;
     for (int s0 = 0; s0 < ns; s0 += AHEAD) {
-        float4 U[AHEAD];
-        float D[AHEAD];
+        float U[AHEAD], D[AHEAD];
 #pragma unroll
         for (int j = 0; j < AHEAD; ++j) {
             if (s0 + j < ns) {
-                U[j] = *reinterpret_cast<const float4*>(base + (long)(s0 + j) * NP);
+                U[j] = base[(long)(s0 + j) * NP];
                 D[j] = dec[s0 + j];
             }
         }
 #pragma unroll
         for (int j = 0; j < AHEAD; ++j) {
             if (s0 + j < ns) {
-                E.x = E.x * D[j] + U[j].x;
-                E.y = E.y * D[j] + U[j].y;
-                E.z = E.z * D[j] + U[j].z;
-                E.w = E.w * D[j] + U[j].w;
-                *reinterpret_cast<float4*>(base + (long)(s0 + j) * NP) = E;
+                E = E * D[j] + U[j];
+                if ((s0 + j + 1) % p.F == 0) base[(long)(s0 + j) * NP] = E;
             }
         }
     }
 }
 
-// dmimo = sum over segments of the partials, in segment order. Loads run
-// eight segments ahead of the additions.
+// dmimo = sum over segments of the partials, in segment order. Loads run up to
+// 32 segments ahead of the additions.
 __device__ __forceinline__ float sum_segments(const float* part, long stride, int nseg) {
+    constexpr int AHEAD = 32;
     float s = 0.f;
-    int sg = 0;
-    for (; sg + 8 <= nseg; sg += 8) {
-        float v[8];
+    for (int s0 = 0; s0 < nseg; s0 += AHEAD) {
+        float v[AHEAD];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = part[(long)(sg + j) * stride];
+        for (int j = 0; j < AHEAD; ++j) v[j] = (s0 + j < nseg) ? part[(long)(s0 + j) * stride] : 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s += v[j];
+        for (int j = 0; j < AHEAD; ++j)
+            if (s0 + j < nseg) s += v[j];
     }
-    for (; sg < nseg; ++sg) s += part[(long)sg * stride];
     return s;
 }
 
@@ -131,7 +131,7 @@ mimo_status fail(mimo_status s, const char* fmt, ...) {
 }
 
 struct Plan {
-    int RP, CT, MT, NW, NT, PT, Cp, W, nc, L, nseg;
+    int RP, CT, MT, NW, NT, PT, Cp, W, nc, L, nseg, F, nsub;
     size_t off_agg, off_decay, off_po, off_pz, ws_bytes;
     int lds_agg, lds_main;
 };
@@ -192,12 +192,18 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
     pl->L = (int)L;
     pl->nseg = (int)((pl->nc + L - 1) / L);
     if (pl->nseg > 65535) return fail(MIMO_ERR_UNSUPPORTED, "too many segments");
+    // the aggregate kernel splits each full segment into F = 2 sub-segments: it
+    // fits more workgroups per compute unit than the chunk kernel (no y path), so
+    // twice the workgroups run at once; a larger F costs more than it saves in
+    // the scan, which reads every sub-segment's [N,P] increment
+    pl->F = (L % 2 == 0 && L >= 4) ? 2 : 1;
+    pl->nsub = (pl->nseg - 1) * pl->F;
     const bool reduce_o = a->mimo_o != nullptr, has_z = a->z != nullptr;
     size_t off = 0;
     pl->off_agg = off;
-    if (pl->nseg > 1) off = align256(off + (size_t)B * H * (pl->nseg - 1) * N * P * 4);
+    if (pl->nseg > 1) off = align256(off + (size_t)B * H * pl->nsub * N * P * 4);
     pl->off_decay = off;
-    if (pl->nseg > 1) off = align256(off + (size_t)B * H * pl->nseg * 4);
+    if (pl->nseg > 1) off = align256(off + (size_t)B * H * pl->nsub * 4);
     pl->off_po = off;
     if (pl->nseg > 1 && reduce_o) off = align256(off + (size_t)B * H * pl->nseg * R * P * 4);
     pl->off_pz = off;
@@ -323,6 +329,7 @@ static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* ev
     p.B = (int)a->B; p.S = (int)a->S; p.H = (int)a->H; p.G = (int)a->G;
     p.R = (int)a->R; p.N = (int)a->N; p.P = (int)a->P; p.C = a->chunk_size;
     p.W = pl.W; p.nc = pl.nc; p.L = pl.L; p.nseg = pl.nseg; p.rd = a->rotary_dim_divisor;
+    p.F = pl.F; p.nsub = pl.nsub;
     p.reduce_o = reduce_o; p.has_z = has_z; p.has_d = a->d != nullptr; p.need_y = reduce_o || has_z;
     p.dout = a->dout; p.q = a->q; p.k = a->k; p.v = a->v; p.z = a->z; p.trap = a->trap;
     p.q_bias = a->q_bias; p.k_bias = a->k_bias; p.mimo_v = a->mimo_v; p.mimo_o = a->mimo_o;
@@ -364,10 +371,10 @@ static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* ev
     if ((s = mark(0)) != MIMO_OK) return s;
     if (pl.nseg > 1) {
         if ((s = set_lds(kagg, pl.lds_agg)) != MIMO_OK) return s;
-        if ((s = launch(kagg, dim3(grid_blocks(p, pl.nseg - 1)), dim3(pl.NW * 64), pl.lds_agg, st, p)) != MIMO_OK) return s;
+        if ((s = launch(kagg, dim3(grid_blocks(p, pl.nsub)), dim3(pl.NW * 64), pl.lds_agg, st, p)) != MIMO_OK) return s;
         if ((s = mark(1)) != MIMO_OK) return s;
         const int NP = p.N * p.P;
-        if ((s = launch(k_scan, dim3((NP / 4 + 255) / 256, BH), dim3(256), 0, st, p)) != MIMO_OK) return s;
+        if ((s = launch(k_scan, dim3((NP + 255) / 256, BH), dim3(256), 0, st, p)) != MIMO_OK) return s;
     } else if ((s = mark(1)) != MIMO_OK) {
         return s;
     }

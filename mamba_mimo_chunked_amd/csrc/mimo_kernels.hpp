@@ -71,13 +71,14 @@ __device__ __forceinline__ void lds_st(void* p, T v) { *reinterpret_cast<T*>(p) 
 // ---------------------------------------------------------------- parameters
 struct Params {
     int B, S, H, G, R, N, P, C, W, nc, L, nseg, rd;
+    int F, nsub;    // the aggregate splits each segment but the last into F sub-segments of L/F chunks
     int reduce_o, has_z, has_d, need_y;
     const unsigned short *dout, *q, *k, *v, *z, *trap;
     const float *q_bias, *k_bias, *mimo_v, *mimo_o, *mimo_z, *angles, *da_cs, *da_cs_rev, *dt, *d, *segsum;
     float *dmimo_o, *dmimo_z;
     unsigned short *states, *dz, *qk_dot;
-    float* agg;     // [B*H][nseg-1][N*P]: segment state increments, then segment entry states
-    float* decay;   // [B*H][nseg]: product of the chunk decays of each segment
+    float* agg;     // [B*H][nsub][N*P]: sub-segment state increments, then the states after each
+    float* decay;   // [B*H][nsub]: product of the chunk decays of each sub-segment
     float* part_o;  // [B*H][nseg][R*P] partial dmimo_o (== dmimo_o when nseg == 1)
     float* part_z;  // [B*H][nseg][R*P] partial dmimo_z
 };
@@ -670,11 +671,12 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
     int seg, bh;
-    if (!map_block(p, p.nseg - 1, seg, bh)) return;
+    if (!map_block(p, p.nsub, seg, bh)) return;
     const int b = bh / p.H, h = bh - b * p.H;
     const int g = h / (p.H / p.G);
-    const int c_begin = seg * p.L;
-    const int c_end = min(c_begin + p.L, p.nc);
+    const int La = p.L / p.F;   // chunks per sub-segment (all full)
+    const int c_begin = seg * La;
+    const int c_end = c_begin + La;
     const int R = p.R;
 
     Items<RP, CT, NT, PT> it;
@@ -756,7 +758,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
         }
         dprod *= dl;
     }
-    float* out = p.agg + ((long)bh * (p.nseg - 1) + seg) * p.N * p.P;
+    float* out = p.agg + ((long)bh * p.nsub + seg) * p.N * p.P;
 #pragma unroll
     for (int w = 0; w < T::STW; ++w) {
         const int u = wave + w * T::NW;
@@ -770,7 +772,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
             }
         }
     }
-    if (tid == 0) p.decay[(long)bh * p.nseg + seg] = dprod;
+    if (tid == 0) p.decay[(long)bh * p.nsub + seg] = dprod;
 }
 
 // ---------------------------------------------------------------- main chunk pass
@@ -827,7 +829,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
     // ---- state entering the segment (fp32, MFMA accumulator layout: rows n, columns p)
     f32x4 Sacc[T::STW];
     {
-        const float* E = (seg > 0) ? p.agg + ((long)bh * (p.nseg - 1) + seg - 1) * p.N * p.P : nullptr;
+        const float* E = (seg > 0) ? p.agg + ((long)bh * p.nsub + seg * p.F - 1) * p.N * p.P : nullptr;
 #pragma unroll
         for (int w = 0; w < T::STW; ++w) {
             const int u = wave + w * NW;
