@@ -108,6 +108,11 @@ struct Tile {
     static constexpr int ATW = (AT + NW - 1) / NW;
     static constexpr int NPAIRS = CT * PTT;                                // (token tile, value tile)
     static constexpr int PW = (NPAIRS + NW - 1) / NW;                      // pairs per wave
+    // work items that divide evenly over the waves need no bound check (the
+    // compiler cannot see that wave < NW)
+    static constexpr bool ST_FULL = ST % NW == 0;
+    static constexpr bool AT_FULL = AT % NW == 0;
+    static constexpr bool PAIRS_FULL = NPAIRS % NW == 0;
 };
 
 // LDS carve-up (byte offsets), shared by host and device. Every region but the
@@ -744,7 +749,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
 #pragma unroll
         for (int w = 0; w < T::STW; ++w) {
             const int u = wave + w * T::NW;
-            if (u < T::ST) {
+            if (T::ST_FULL || u < T::ST) {
                 const int nt = u / T::PTT, pt = u % T::PTT;
                 f32x4 acc = U[w] * dl;
 #pragma unroll
@@ -762,7 +767,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
 #pragma unroll
     for (int w = 0; w < T::STW; ++w) {
         const int u = wave + w * T::NW;
-        if (u < T::ST) {
+        if (T::ST_FULL || u < T::ST) {
             const int nt = u / T::PTT, pt = u % T::PTT;
             const int pc = 16 * pt + l16;
 #pragma unroll
@@ -834,7 +839,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         for (int w = 0; w < T::STW; ++w) {
             const int u = wave + w * NW;
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if (E != nullptr && u < T::ST) {
+            if (E != nullptr && (T::ST_FULL || u < T::ST)) {
                 const int nt = u / PTT, pt = u % PTT;
                 const int pc = 16 * pt + l16;
 #pragma unroll
@@ -852,7 +857,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
 #pragma unroll
         for (int w = 0; w < T::STW; ++w) {
             const int u = wave + w * NW;
-            if (u < T::ST) {
+            if (T::ST_FULL || u < T::ST) {
                 const int nt = u / PTT, pt = u % PTT;
                 const int pc = 16 * pt + l16;
                 const u32x2 o = {pk2(Sacc[w][0], Sacc[w][1]), pk2(Sacc[w][2], Sacc[w][3])};
@@ -1043,29 +1048,33 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
 
         f32x4 acc[T::PW][RP];
         if (need_y) {
-            // ---- inter = Q bf16(S), scaled by exp(da_cs[t]) per row
+            // ---- inter = Q bf16(S), scaled by exp(da_cs[t]) per row; the bf16(S)
+            // fragments of the wave's value tile serve every rank
 #pragma unroll
             for (int ps = 0; ps < T::PW; ++ps) {
                 const int pair = wave + ps * NW;
                 const int tt = pair / PTT, pt = pair % PTT;
+                const bool pok = T::PAIRS_FULL || pair < T::NPAIRS;
+                u32x4 bS[NT / 32];
+#pragma unroll
+                for (int ks = 0; ks < NT / 32; ++ks)
+                    bS[ks] = lds_ld<u32x4>(sSbT + (16 * pt + l16) * LDQ + 32 * ks + 8 * q4);
+                const f32x4 e4 = lds_ld<f32x4>(sc + 16 * tt + 4 * q4);
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
                     f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-                    if (pair < T::NPAIRS && r < R) {
+                    if (pok && r < R) {
                         const int i16 = r * CT + tt;
 #pragma unroll
-                        for (int ks = 0; ks < NT / 32; ++ks) {
-                            const u32x4 a = lds_ld<u32x4>(sQ + (16 * i16 + l16) * LDQ + 32 * ks + 8 * q4);
-                            const u32x4 bb = lds_ld<u32x4>(sSbT + (16 * pt + l16) * LDQ + 32 * ks + 8 * q4);
-                            a4 = mfma(a, bb, a4);
-                        }
-                        const f32x4 e4 = lds_ld<f32x4>(sc + 16 * tt + 4 * q4);
+                        for (int ks = 0; ks < NT / 32; ++ks)
+                            a4 = mfma(lds_ld<u32x4>(sQ + (16 * i16 + l16) * LDQ + 32 * ks + 8 * q4), bS[ks], a4);
                         a4 *= e4;
                     }
                     acc[ps][r] = a4;
                 }
             }
-            // ---- causal block A^T = K~ Q^T, masked on token index, times exp(segsum), bf16
+            // ---- causal block A^T = K~ Q^T, masked on token index, times exp(segsum), bf16.
+            // The mask is applied with selects on values read unconditionally.
             u32x2 at[T::ATW];
 #pragma unroll
             for (int w = 0; w < T::ATW; ++w) {
@@ -1074,7 +1083,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                 const int jt = u / MTT, i16 = u % MTT;
                 const int ri = i16 / CT, rj = jt / CT;
                 const int tti = i16 % CT, ttj = jt % CT;
-                if (u < T::AT && ri < R && rj < R && ttj <= tti) {
+                if ((T::AT_FULL || u < T::AT) && ri < R && rj < R && ttj <= tti) {
                     f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < NT / 32; ++ks) {
@@ -1082,13 +1091,20 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                         const u32x4 bb = lds_ld<u32x4>(sQ + (16 * i16 + l16) * LDQ + 32 * ks + 8 * q4);
                         a4 = mfma(a, bb, a4);
                     }
-                    const int ti = 16 * tti + l16;
+                    const int ti = 16 * tti + l16, tj0 = 16 * ttj + 4 * q4;
+                    f32x4 e;
+                    if constexpr (EX) {
+                        e = lds_ld<f32x4>(sE + ti * Cp + tj0);   // C == Cp: always inside the block
+                    } else {
+                        const int tic = min(ti, p.C - 1);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) e[v] = sE[tic * p.C + min(tj0 + v, p.C - 1)];
+                    }
                     float m[4];
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const int tj = 16 * ttj + 4 * q4 + v;
-                        const bool keep = ti < cl && ti > tj;
-                        m[v] = keep ? a4[v] * sE[ti * p.C + tj] : 0.f;
+                        const bool keep = ti < cl && ti > tj0 + v;
+                        m[v] = keep ? a4[v] * e[v] : 0.f;
                     }
                     at[w] = u32x2{pk2(m[0], m[1]), pk2(m[2], m[3])};
                 }
@@ -1097,28 +1113,31 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
 #pragma unroll
             for (int w = 0; w < T::ATW; ++w) {
                 const int u = wave + w * NW;
-                if (u < T::AT) {
+                if (T::AT_FULL || u < T::AT) {
                     const int jt = u / MTT, i16 = u % MTT;
                     lds_st<u32x2>(sA + (16 * i16 + l16) * LDA + 16 * jt + 4 * q4, at[w]);
                 }
             }
             bar();
-            // ---- intra = A Psi, accumulated onto the scaled inter term
+            // ---- intra = A Psi, accumulated onto the scaled inter term; the Psi
+            // fragments of the wave's value tile serve every rank
 #pragma unroll
             for (int ps = 0; ps < T::PW; ++ps) {
                 const int pair = wave + ps * NW;
                 const int tt = pair / PTT, pt = pair % PTT;
+                const bool pok = T::PAIRS_FULL || pair < T::NPAIRS;
+                u32x4 bP[MT / 32];
+#pragma unroll
+                for (int ks = 0; ks < MT / 32; ++ks)
+                    bP[ks] = lds_ld<u32x4>(sPsiT + (16 * pt + l16) * LDA + 32 * ks + 8 * q4);
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
-                    if (pair < T::NPAIRS && r < R) {
+                    if (pok && r < R) {
                         const int i16 = r * CT + tt;
                         f32x4 a4 = acc[ps][r];
 #pragma unroll
-                        for (int ks = 0; ks < MT / 32; ++ks) {
-                            const u32x4 a = lds_ld<u32x4>(sA + (16 * i16 + l16) * LDA + 32 * ks + 8 * q4);
-                            const u32x4 bb = lds_ld<u32x4>(sPsiT + (16 * pt + l16) * LDA + 32 * ks + 8 * q4);
-                            a4 = mfma(a, bb, a4);
-                        }
+                        for (int ks = 0; ks < MT / 32; ++ks)
+                            a4 = mfma(lds_ld<u32x4>(sA + (16 * i16 + l16) * LDA + 32 * ks + 8 * q4), bP[ks], a4);
                         acc[ps][r] = a4;
                     }
                 }
@@ -1150,7 +1169,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
 #pragma unroll
             for (int w = 0; w < T::STW; ++w) {
                 const int u = wave + w * NW;
-                if (u < T::ST) {
+                if (T::ST_FULL || u < T::ST) {
                     const int nt = u / PTT, pt = u % PTT;
                     f32x4 a4 = Sacc[w] * dl;
 #pragma unroll
@@ -1172,7 +1191,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
 #pragma unroll
             for (int ps = 0; ps < T::PW; ++ps) {
                 const int pair = wave + ps * NW;
-                if (pair >= T::NPAIRS) continue;
+                if (!T::PAIRS_FULL && pair >= T::NPAIRS) continue;
                 const int tt = pair / PTT, pt = pair % PTT;
                 const int pc = 16 * pt + l16;
                 const int tb = 16 * tt + 4 * q4;   // first of this lane's 4 tokens
