@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void k_scan(Params p) {
 #pragma unroll
         for (int j = 0; j < AHEAD; ++j) {
             if (s0 + j < ns) {
-                E = E * D[j] + U[j];
+                E = __fmaf_rn(E, D[j], U[j]);
                 if ((s0 + j + 1) % p.F == 0) base[(long)(s0 + j) * NP] = E;
             }
         }

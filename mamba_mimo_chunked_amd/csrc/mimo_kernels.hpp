@@ -5,14 +5,22 @@
 //
 // The arithmetic follows the Triton-Ascend mamba_mimo_bwd_fwd page's
 // BF16-boundary PyTorch reference: bf16 (round to nearest even) at the same
-// points, fp32 everywhere else. Two roundings are done by one
-// v_cvt_pk_bf16_f32 whenever two independent values are ready together.
+// points, fp32 everywhere else. A bf16 rounding of an fp32 value is one
+// v_cvt_pk_bf16_f32 with a zero low half: the result, read as fp32, is the
+// rounded value. Two values that go to memory together are rounded and
+// packed by one v_cvt_pk_bf16_f32.
 #pragma once
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "mimo_bwd_fwd.h"
+
+// No implicit fusion of a multiply and an add into an FMA anywhere below: the
+// contract rounds some products on their own (rotation, diagonal, dz chain),
+// and every instance of a kernel must compute the same fp32 operations. FMAs
+// are written out (__builtin_fmaf / __fmaf_rn) where the rounding allows them.
+#pragma clang fp contract(off)
 
 namespace mimo {
 
@@ -32,28 +40,53 @@ __device__ __forceinline__ unsigned pk2(float a, float b) {
 }
 __device__ __forceinline__ float lo16(unsigned u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi16(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
-// round two fp32 values to bf16 in place
-__device__ __forceinline__ void rnd2(float& a, float& b) {
-    const unsigned u = pk2(a, b);
-    a = lo16(u);
-    b = hi16(u);
-}
-__device__ __forceinline__ float rnd1(float a) { return lo16(pk2(a, 0.f)); }
+// bf16(x) as an fp32 value (one instruction: the rounded value lands in the high half)
+__device__ __forceinline__ float rnd(float x) { return __uint_as_float(pk2(0.f, x)); }
 __device__ __forceinline__ float bf2f(unsigned short u) { return __uint_as_float(static_cast<unsigned>(u) << 16); }
 __device__ __forceinline__ unsigned short f2bf(float x) { return static_cast<unsigned short>(pk2(x, 0.f)); }
+// the bf16 bits of a value that is already bf16-exact
+__device__ __forceinline__ unsigned short bits16(float x) { return static_cast<unsigned short>(__float_as_uint(x) >> 16); }
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
 }
-// a.lo*b.lo + a.hi*b.hi + c (bf16 pairs, fp32 accumulate)
-__device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-// logistic function: precise for the per-token controls, fast for the gate
-__device__ __forceinline__ float sigmoid_precise(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// ---------------------------------------------------------------- fp32 math
+// logistic function 1 / (1 + e^-x): hardware exp2 and reciprocal (about 2 ulp)
 __device__ __forceinline__ float sigmoid_fast(float x) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+
+// sin and cos of x in radians. For |x| <= 8192: Cody-Waite reduction by pi/2
+// (pi/2 split into three fp32 parts, fused multiply-adds), then the Taylor
+// polynomials of sin (to x^9) and cos (to x^10) on [-pi/4, pi/4], whose
+// truncation errors there are below 3e-9 and 2e-10; about 1 ulp overall.
+// Larger arguments take the library's sincosf.
+__device__ __forceinline__ void sin_cos(float x, float& s, float& c) {
+    if (__builtin_fabsf(x) <= 8192.f) {
+        const float k = __builtin_rintf(x * 0.636619772367581343f);
+        float r = __builtin_fmaf(-k, 1.57079637050628662109375f, x);
+        r = __builtin_fmaf(-k, -4.37113882867379300e-08f, r);
+        r = __builtin_fmaf(-k, -1.71512451000588190e-15f, r);
+        const float z = r * r;
+        float ps = __builtin_fmaf(z, 2.75573192239858907e-06f, -1.98412698412698413e-04f);
+        ps = __builtin_fmaf(z, ps, 8.33333333333333333e-03f);
+        ps = __builtin_fmaf(z, ps, -1.66666666666666667e-01f);
+        const float sr = __builtin_fmaf(r * z, ps, r);
+        float pc = __builtin_fmaf(z, -2.75573192239858907e-07f, 2.48015873015873016e-05f);
+        pc = __builtin_fmaf(z, pc, -1.38888888888888889e-03f);
+        pc = __builtin_fmaf(z, pc, 4.16666666666666667e-02f);
+        pc = __builtin_fmaf(z, pc, -0.5f);
+        const float cr = __builtin_fmaf(z, pc, 1.0f);
+        // quadrant q = k mod 4: (sin, cos) = (s, c), (c, -s), (-s, -c), (-c, s)
+        const int q = static_cast<int>(k);
+        const float a = (q & 1) ? cr : sr, b = (q & 1) ? sr : cr;
+        s = __uint_as_float(__float_as_uint(a) ^ ((static_cast<unsigned>(q) & 2u) << 30));
+        c = __uint_as_float(__float_as_uint(b) ^ ((static_cast<unsigned>(q + 1) & 2u) << 30));
+    } else {
+        sincosf(x, &s, &c);
+    }
 }
 
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS accesses, not
@@ -108,11 +141,20 @@ struct Tile {
     static constexpr int ATW = (AT + NW - 1) / NW;
     static constexpr int NPAIRS = CT * PTT;                                // (token tile, value tile)
     static constexpr int PW = (NPAIRS + NW - 1) / NW;                      // pairs per wave
+    static constexpr int PSI_ITEMS = (Cp / 2) * RP * (PT / 8);             // (token pair, rank, 8 values)
+    static constexpr int KAP_ITEMS = (MT / 2) * (NT / 8);                  // (row pair, 8 state columns)
+    static constexpr int QKT = RP * RP * CT;                               // same-token (qk_dot) tiles
     // work items that divide evenly over the waves need no bound check (the
     // compiler cannot see that wave < NW)
     static constexpr bool ST_FULL = ST % NW == 0;
     static constexpr bool AT_FULL = AT % NW == 0;
     static constexpr bool PAIRS_FULL = NPAIRS % NW == 0;
+    static constexpr bool QKT_FULL = QKT % NW == 0;
+    // Rotation split (rotary divisor 4, N = NT): the rotated 8-column groups
+    // (first N/32 of each half) go to the first half of the threads, the others
+    // to the second half, so that no wave runs the rotation with half its lanes
+    // idle; the second half fills Psi^T meanwhile.
+    static constexpr bool RSPLIT_OK = NT >= 32 && (MT * NT / 32) % (NTHR / 2) == 0;
 };
 
 // LDS carve-up (byte offsets), shared by host and device. Every region but the
@@ -134,15 +176,15 @@ struct Lds {
     int total;
 };
 
-__host__ __device__ inline int align16(int x) { return (x + 15) & ~15; }
+__host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
 
-__host__ __device__ inline Lds lds_layout(int RP, int CT, int NT, int PT, int C, int W, bool main) {
+__host__ __device__ constexpr Lds lds_layout(int RP, int CT, int NT, int PT, int C, int W, bool main) {
     const int Cp = 16 * CT, MT = RP * Cp < 32 ? 32 : RP * Cp;
     const int ldq = NT + 8, lda = MT + 8;
     int r1 = NT * lda;
     if (main && MT * ldq > r1) r1 = MT * ldq;
     if (main && MT * lda > r1) r1 = MT * lda;
-    Lds s;
+    Lds s{};
     int off = 0;
     s.r1 = off; off += align16(r1 * 2);
     s.r2 = off; if (main) off += align16(MT * ldq * 2);
@@ -154,21 +196,60 @@ __host__ __device__ inline Lds lds_layout(int RP, int CT, int NT, int PT, int C,
     s.tb = off; off += align16((2 * RP * NT + RP * PT) * 2);
     s.cs = off; off += align16(2 * C * W * 4);
     s.se = off; if (main) off += align16(C * C * 4);
-    s.total = off;
+    s.total = off + 16;   // slack: 8-wide cos/sin reads of a partial last group stay inside
     return s;
 }
 
-// ---------------------------------------------------------------- per-chunk inputs
-// Everything one chunk reads from global memory, loaded in one go at the top
-// of the chunk so that a single memory latency is paid per chunk.
+// ---------------------------------------------------------------- staging of chunk inputs
+// LITE tile families (their LDS leaves room for two workgroups per compute unit
+// with the staging below) fetch the inputs of chunk c+1 straight into LDS
+// (global_load_lds: lane l of a wave writes its 4 or 16 bytes at base + 4l or
+// base + 16l; a 2-byte load fills the low half of the lane's 4-byte slot) while
+// chunk c computes.
+//   Small inputs (v, angles, segsum, token scalars): two buffers, chunk c in
+//   buffer c & 1. Slot e holds input item e, so after the workgroup barrier
+//   that follows each thread's wait for its own loads, any thread may read any
+//   slot of the current buffer.
+//   q and k (QKON, when that fits as well): one buffer. Each thread reads back
+//   exactly the slots it fetched, into registers, before it issues the next
+//   prefetch.
+// The other families load their inputs into registers at the top of the chunk.
 template <int RP, int CT, int NT, int PT, bool MAIN>
-struct ChunkIn {
+struct Stage {
+    using T = Tile<RP, CT, NT, PT>;
+    static constexpr int NQ = MAIN ? 4 : 2;                        // q0, q1, k0, k1 (or k0, k1)
+    static constexpr int V = 0;                                    // slot t + Cp*pg: v[t][8pg .. 8pg+7]
+    static constexpr int ANG = V + T::Cp * PT * 2;                 // slot e = t*W + n: angle
+    static constexpr int SEG = ANG + T::ANG_IT * T::NTHR * 4;      // slot e = ti*C + tj: segsum
+    static constexpr int SCAL = SEG + (MAIN ? T::SEG_IT * T::NTHR * 4 : 0);   // [7][64] dwords
+    static constexpr int SMB = SCAL + 7 * 64 * 4;                  // one small-input buffer
+    static constexpr int QKB = T::QK_IT * NQ * T::NTHR * 16;       // q/k of one chunk
+    // dynamic LDS of the family at its largest chunk (C = Cp, W = NT/2)
+    static constexpr int DYN = lds_layout(RP, CT, NT, PT, T::Cp, NT / 2, MAIN).total + 256;
+    static constexpr bool LITE = DYN + 2 * SMB <= 80 * 1024;
+    static constexpr bool QKON = LITE && DYN + 2 * SMB + QKB <= 80 * 1024;
+    static constexpr int QK = 2 * SMB;
+    static constexpr int BYTES = LITE ? 2 * SMB + (QKON ? QKB : 0) : 16;
+    // scalar rows inside SCAL
+    static constexpr int DT0 = 0, DT1 = 256, TR0 = 512, TR1 = 768, CS = 1024, REV = 1280, DLAST = 1536;
+};
+
+// q/k of one chunk in registers
+template <int RP, int CT, int NT, int PT, bool MAIN>
+struct ChunkQK {
     using T = Tile<RP, CT, NT, PT>;
     u32x4 q0[T::QK_IT], q1[T::QK_IT], k0[T::QK_IT], k1[T::QK_IT];   // columns col0.., N/2+col0..
+};
+
+// Small inputs of one chunk in registers (families that are not LITE): the
+// thread's v, angle and segsum items, and in wave 0 the scalars of token `lane`.
+template <int RP, int CT, int NT, int PT, bool MAIN>
+struct SmallRegs {
+    using T = Tile<RP, CT, NT, PT>;
     u32x4 v[T::PSI_IT];
-    float dt0, dt1, tr0, tr1, cs, rev, dlast;
     float ang[T::ANG_IT];
     float seg[MAIN ? T::SEG_IT : 1];
+    float dt0, dt1, tr0, tr1, cs, rev, dlast;
 };
 
 // Per-thread item coordinates, fixed for the whole kernel. Global reads of a chunk
@@ -186,26 +267,35 @@ struct Items {
     unsigned v_off[T::PSI_IT];    // byte offset of the 8-column v group inside a chunk's v block
 };
 
-// ROWS_FAST: consecutive threads take consecutive tile rows (the chunk-aggregate
-// kernel writes kappa^T transposed straight from registers); otherwise the
+// q/k items. ROWS_FAST: consecutive threads take consecutive tile rows (the
+// chunk-aggregate kernel writes kappa^T transposed straight from registers).
+// RSPLIT: the rotation split described at Tile::RSPLIT_OK. Otherwise the
 // 8-column groups of one row are adjacent.
-template <int RP, int CT, int NT, int PT, bool ROWS_FAST = false>
+template <int RP, int CT, int NT, int PT, bool ROWS_FAST, bool RSPLIT>
 __device__ __forceinline__ void make_items(const Params& p, int g, Items<RP, CT, NT, PT>& it) {
     using T = Tile<RP, CT, NT, PT>;
     const int tid = threadIdx.x;
     const int ng = p.N / 16;
 #pragma unroll
     for (int j = 0; j < T::QK_IT; ++j) {
-        const int e = tid + j * T::NTHR;
-        it.qk_row[j] = -1;
-        it.qk_col[j] = 0;
+        int i = -1, gg = 0;
+        if constexpr (RSPLIT) {
+            constexpr int GR = NT / 32, HALF = T::NTHR / 2;
+            const int half = tid / HALF, e = tid % HALF + j * HALF;
+            i = e / GR;
+            gg = e % GR + half * GR;
+        } else {
+            const int e = tid + j * T::NTHR;
+            if (e < T::MT * ng) {
+                i = ROWS_FAST ? e % T::MT : e / ng;
+                gg = ROWS_FAST ? e / T::MT : e - i * ng;
+            }
+        }
+        it.qk_row[j] = i;
+        it.qk_col[j] = 8 * gg;
         it.qk_off[j] = 0;
-        if (e < T::MT * ng) {
-            const int i = ROWS_FAST ? e % T::MT : e / ng;
-            const int gg = ROWS_FAST ? e / T::MT : e - i * ng;
+        if (i >= 0) {
             const int r = i / T::Cp, t = i % T::Cp;
-            it.qk_row[j] = i;
-            it.qk_col[j] = 8 * gg;
             it.qk_off[j] = 2u * (unsigned)(((t * p.R + r) * p.G + g) * p.N + 8 * gg);
         }
     }
@@ -228,18 +318,16 @@ __device__ __forceinline__ void make_items(const Params& p, int g, Items<RP, CT,
     }
 }
 
-
 template <typename T>
 __device__ __forceinline__ const T* at(const void* base, unsigned byte_off) {
     return reinterpret_cast<const T*>(static_cast<const unsigned char*>(base) + byte_off);
 }
 
-// Global loads of chunk c (c0 = first token, cl = real tokens).
+// Register loads of chunk c's q/k (c0 = first token, cl = real tokens).
 template <int RP, int CT, int NT, int PT, bool MAIN>
-__device__ __forceinline__ void load_chunk(const Params& p, const Items<RP, CT, NT, PT>& it, int b, int h, int bh,
-                                           int c, int c0, int cl, ChunkIn<RP, CT, NT, PT, MAIN>& in) {
+__device__ __forceinline__ void load_qk(const Params& p, const Items<RP, CT, NT, PT>& it, int b, int c0, int cl,
+                                        ChunkQK<RP, CT, NT, PT, MAIN>& in) {
     using T = Tile<RP, CT, NT, PT>;
-    const int tid = threadIdx.x;
     const int R = p.R;
     const unsigned short* qb = p.q + (long)(b * p.S + c0) * R * p.G * p.N;
     const unsigned short* kb = p.k + (long)(b * p.S + c0) * R * p.G * p.N;
@@ -259,6 +347,14 @@ __device__ __forceinline__ void load_chunk(const Params& p, const Items<RP, CT, 
             in.k1[j] = *at<u32x4>(kb2, o);
         }
     }
+}
+
+// Register loads of chunk c's small inputs (the items a LITE family stages).
+template <int RP, int CT, int NT, int PT, bool MAIN>
+__device__ __forceinline__ void load_small(const Params& p, const Items<RP, CT, NT, PT>& it, int b, int h, int bh,
+                                           int c, int c0, int cl, SmallRegs<RP, CT, NT, PT, MAIN>& in) {
+    using T = Tile<RP, CT, NT, PT>;
+    const int tid = threadIdx.x;
     const unsigned short* vb = p.v + ((long)(b * p.S + c0) * p.H + h) * p.P;
 #pragma unroll
     for (int j = 0; j < T::PSI_IT; ++j) {
@@ -292,37 +388,6 @@ __device__ __forceinline__ void load_chunk(const Params& p, const Items<RP, CT, 
     }
 }
 
-// ---------------------------------------------------------------- LDS staging of chunk inputs
-// For tile families whose LDS leaves room for two workgroups per compute unit,
-// the inputs of chunk c+1 are fetched straight into a staging area of LDS
-// (global_load_lds: lane l of a wave writes its 4 or 16 bytes at base + 4l or
-// base + 16l; a 2-byte load fills the low half of the lane's 4-byte slot)
-// while chunk c computes. Each thread later reads back exactly the slots it
-// fetched, so only its own outstanding loads have to be waited for.
-template <int RP, int CT, int NT, int PT, bool MAIN>
-struct Stage {
-    using T = Tile<RP, CT, NT, PT>;
-    static constexpr int NQ = MAIN ? 4 : 2;   // q0, q1, k0, k1 (or k0, k1)
-    static constexpr int QK = 0;
-    static constexpr int V = QK + T::QK_IT * NQ * T::NTHR * 16;
-    static constexpr int ANG = V + T::PSI_IT * T::NTHR * 16;
-    static constexpr int SEG = ANG + T::ANG_IT * T::NTHR * 4;
-    static constexpr int SCAL = SEG + (MAIN ? T::SEG_IT * T::NTHR * 4 : 0);   // [7][64] dwords, wave 0
-    static constexpr int BYTES = SCAL + 7 * 64 * 4;
-    // dynamic LDS of the family at its largest chunk (C = Cp, R = RP, N = NT, P = PT)
-    static constexpr int ldq = NT + 8, lda = T::MT + 8;
-    static constexpr int r1 = (MAIN ? ((T::MT * ldq > NT * lda ? T::MT * ldq : NT * lda) > T::MT * lda
-                                           ? (T::MT * ldq > NT * lda ? T::MT * ldq : NT * lda)
-                                           : T::MT * lda)
-                                     : NT * lda);
-    static constexpr int DYN = 2 * r1 + (MAIN ? 2 * T::MT * ldq : 0) + 2 * PT * lda + (MAIN ? 2 * PT * ldq : 0) +
-                               8 * T::Cp * (NT / 2) +
-                               (MAIN ? 4 * T::Cp * T::Cp + 4 * T::Cp * (RP * RP + 1) + 2 * T::Cp * (PT + 8) : 0) +
-                               4 * (5 * kTok + 4) + 2 * (2 * RP * NT + RP * PT) + 256;
-    static constexpr bool ON = DYN + BYTES <= 80 * 1024;
-};
-
-
 // One global_load_lds per lane: 16, 4 or 2 bytes from base + off (base the same
 // for every lane, off a 32-bit byte offset) into the wave's LDS block at dst_wave
 // (M0 holds its LDS address: the low 32 bits of a generic pointer into LDS are
@@ -330,9 +395,9 @@ struct Stage {
 // wait-count tracking does not treat the address registers as pending until the
 // load completes (it would then wait for the whole prefetch as soon as such a
 // register is reused). The waits are explicit instead: s_waitcnt vmcnt(0) before
-// a thread reads its staged slots, and lgkmcnt(0) after the reads, before the
-// next prefetch overwrites them. M0 is saved and restored around the load; an
-// SALU write of M0 needs one wait state before an LDS DMA.
+// the staged data is read, and lgkmcnt(0) after the reads, before the next
+// prefetch overwrites them. M0 is saved and restored around the load; an SALU
+// write of M0 needs one wait state before an LDS DMA.
 // A wave-uniform pointer, pinned to scalar registers (a no-op when it already is).
 // readfirstlane returns int: each half goes through unsigned so that it is
 // zero-extended, never sign-extended, into the 64-bit address.
@@ -365,33 +430,35 @@ MIMO_DMA(dma4, "global_load_lds_dword")
 MIMO_DMA(dma2, "global_load_lds_ushort")
 #undef MIMO_DMA
 
-// Issue the staging loads of chunk c (first token c0, cl real tokens). Every
-// address is a scalar chunk base plus a per-lane offset that does not change
-// from chunk to chunk.
-template <int RP, int CT, int NT, int PT, bool MAIN>
+// Issue the staging loads of chunk c (first token c0, cl real tokens): q/k into
+// qkst (when QKON), the small inputs into the buffer smb. Every address is a
+// scalar chunk base plus a per-lane offset that does not change from chunk to chunk.
+template <int RP, int CT, int NT, int PT, bool MAIN, bool QKON>
 __device__ __forceinline__ void prefetch_chunk(const Params& p, const Items<RP, CT, NT, PT>& it, int b, int h, int bh,
-                                               int c, int c0, int cl, unsigned char* stg) {
+                                               int c, int c0, int cl, unsigned char* qkst, unsigned char* smb) {
     using T = Tile<RP, CT, NT, PT>;
     using SG = Stage<RP, CT, NT, PT, MAIN>;
     const int tid = threadIdx.x, wave = tid >> 6;
     const int R = p.R;
-    const unsigned short* qb = p.q + (long)(b * p.S + c0) * R * p.G * p.N;
-    const unsigned short* kb = p.k + (long)(b * p.S + c0) * R * p.G * p.N;
+    if constexpr (QKON) {
+        const unsigned short* qb = p.q + (long)(b * p.S + c0) * R * p.G * p.N;
+        const unsigned short* kb = p.k + (long)(b * p.S + c0) * R * p.G * p.N;
 #pragma unroll
-    for (int j = 0; j < T::QK_IT; ++j) {
-        const int i = it.qk_row[j];
-        const int r = i / T::Cp, t = i % T::Cp;
-        unsigned char* d = stg + SG::QK + (j * SG::NQ) * T::NTHR * 16 + wave * 1024;
-        if (i >= 0 && r < R && t < cl) {
-            const unsigned o = it.qk_off[j], o2 = o + p.N;   // second half: N/2 bf16 further
-            if (MAIN) {
-                dma16(qb, o, d);
-                dma16(qb, o2, d + T::NTHR * 16);
-                dma16(kb, o, d + 2 * T::NTHR * 16);
-                dma16(kb, o2, d + 3 * T::NTHR * 16);
-            } else {
-                dma16(kb, o, d);
-                dma16(kb, o2, d + T::NTHR * 16);
+        for (int j = 0; j < T::QK_IT; ++j) {
+            const int i = it.qk_row[j];
+            const int r = i / T::Cp, t = i % T::Cp;
+            unsigned char* d = qkst + (j * SG::NQ) * T::NTHR * 16 + wave * 1024;
+            if (i >= 0 && r < R && t < cl) {
+                const unsigned o = it.qk_off[j], o2 = o + p.N;   // second half: N/2 bf16 further
+                if (MAIN) {
+                    dma16(qb, o, d);
+                    dma16(qb, o2, d + T::NTHR * 16);
+                    dma16(kb, o, d + 2 * T::NTHR * 16);
+                    dma16(kb, o2, d + 3 * T::NTHR * 16);
+                } else {
+                    dma16(kb, o, d);
+                    dma16(kb, o2, d + T::NTHR * 16);
+                }
             }
         }
     }
@@ -401,47 +468,47 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const Items<RP, 
         const int e = tid + j * T::NTHR;
         const int t = e % T::Cp, pc = (e / T::Cp) * 8;
         if (e < T::Cp * (PT / 8) && t < cl && pc < p.P)
-            dma16(vb, it.v_off[j], stg + SG::V + j * T::NTHR * 16 + wave * 1024);
+            dma16(vb, it.v_off[j], smb + SG::V + (j * T::NTHR + wave * 64) * 16);
     }
     const float* ab = p.angles + ((long)(b * p.S + c0) * p.H + h) * p.W;
 #pragma unroll
     for (int j = 0; j < T::ANG_IT; ++j)
-        if (it.ang_t[j] >= 0 && it.ang_t[j] < cl) dma4(ab, it.ang_off[j], stg + SG::ANG + j * T::NTHR * 4 + wave * 256);
+        if (it.ang_t[j] >= 0 && it.ang_t[j] < cl) dma4(ab, it.ang_off[j], smb + SG::ANG + (j * T::NTHR + wave * 64) * 4);
     if (MAIN && p.need_y) {
         const float* sb = p.segsum + ((long)bh * p.nc + c) * p.C * p.C;
 #pragma unroll
         for (int j = 0; j < T::SEG_IT; ++j) {
             const int e = tid + j * T::NTHR;
-            if (e < p.C * p.C) dma4(sb, 4u * e, stg + SG::SEG + j * T::NTHR * 4 + wave * 256);
+            if (e < p.C * p.C) dma4(sb, 4u * e, smb + SG::SEG + (j * T::NTHR + wave * 64) * 4);
         }
     }
     if (wave == 0) {
         const long tok = (long)bh * p.S + c0;
-        unsigned char* sc = stg + SG::SCAL;
+        unsigned char* sc = smb + SG::SCAL;
         const unsigned o4 = 4u * tid, o2 = 2u * tid;
         if (tid < cl) {
-            dma4(p.dt + tok, o4, sc);
-            dma2(p.trap + tok, o2, sc + 2 * 256);
-            dma4(p.da_cs_rev + tok, o4, sc + 5 * 256);
-            if (MAIN) dma4(p.da_cs + tok, o4, sc + 4 * 256);
+            dma4(p.dt + tok, o4, sc + SG::DT0);
+            dma2(p.trap + tok, o2, sc + SG::TR0);
+            dma4(p.da_cs_rev + tok, o4, sc + SG::REV);
+            if (MAIN) dma4(p.da_cs + tok, o4, sc + SG::CS);
             if (c0 + tid + 1 < p.S) {
-                dma4(p.dt + tok + 1, o4, sc + 1 * 256);
-                dma2(p.trap + tok + 1, o2, sc + 3 * 256);
+                dma4(p.dt + tok + 1, o4, sc + SG::DT1);
+                dma2(p.trap + tok + 1, o2, sc + SG::TR1);
             }
         }
-        if (tid == 0) dma4(p.da_cs + tok + cl - 1, 0u, sc + 6 * 256);
+        if (tid == 0) dma4(p.da_cs + tok + cl - 1, 0u, sc + SG::DLAST);
     }
 }
 
-// Copy this thread's staged slots of the current chunk into registers.
+// Copy this thread's staged q/k slots into registers.
 template <int RP, int CT, int NT, int PT, bool MAIN>
-__device__ __forceinline__ void read_stage(const unsigned char* stg, ChunkIn<RP, CT, NT, PT, MAIN>& in) {
+__device__ __forceinline__ void read_stage(const unsigned char* qkst, ChunkQK<RP, CT, NT, PT, MAIN>& in) {
     using T = Tile<RP, CT, NT, PT>;
     using SG = Stage<RP, CT, NT, PT, MAIN>;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < T::QK_IT; ++j) {
-        const unsigned char* d = stg + SG::QK + (j * SG::NQ) * T::NTHR * 16 + tid * 16;
+        const unsigned char* d = qkst + (j * SG::NQ) * T::NTHR * 16 + tid * 16;
         if (MAIN) {
             in.q0[j] = lds_ld<u32x4>(d);
             in.q1[j] = lds_ld<u32x4>(d + T::NTHR * 16);
@@ -452,53 +519,54 @@ __device__ __forceinline__ void read_stage(const unsigned char* stg, ChunkIn<RP,
             in.k1[j] = lds_ld<u32x4>(d + T::NTHR * 16);
         }
     }
-#pragma unroll
-    for (int j = 0; j < T::PSI_IT; ++j) in.v[j] = lds_ld<u32x4>(stg + SG::V + j * T::NTHR * 16 + tid * 16);
-#pragma unroll
-    for (int j = 0; j < T::ANG_IT; ++j) in.ang[j] = lds_ld<float>(stg + SG::ANG + j * T::NTHR * 4 + tid * 4);
-    if (MAIN) {
-#pragma unroll
-        for (int j = 0; j < (MAIN ? T::SEG_IT : 0); ++j)
-            in.seg[j] = lds_ld<float>(stg + SG::SEG + j * T::NTHR * 4 + tid * 4);
-    }
-    if (tid < 64) {
-        const unsigned char* sc = stg + SG::SCAL + tid * 4;
-        in.dt0 = lds_ld<float>(sc);
-        in.dt1 = lds_ld<float>(sc + 256);
-        in.tr0 = bf2f(static_cast<unsigned short>(lds_ld<unsigned>(sc + 2 * 256)));
-        in.tr1 = bf2f(static_cast<unsigned short>(lds_ld<unsigned>(sc + 3 * 256)));
-        if (MAIN) in.cs = lds_ld<float>(sc + 4 * 256);
-        in.rev = lds_ld<float>(sc + 5 * 256);
-        in.dlast = lds_ld<float>(stg + SG::SCAL + 6 * 256);
-    }
 }
 
-// Phase 0: token scalars, cos/sin, exp(segsum) into LDS.
-// gamma_t = bf16(dt_t) * sigmoid(trap_t)                      (fp32)
-// beta_t  = bf16(bf16(dt_{t+1}) * sigmoid(-trap_{t+1})), 0 at the last token
-// factor_t = bf16(gamma_t + beta_t)
+// Phase 0: token scalars, cos/sin, exp(segsum) into LDS. LITE families read the
+// small-input buffer of the chunk and spread the token scalars over three waves;
+// the others read their registers, token scalars in wave 0:
+//   gamma_t = bf16(dt_t) * sigmoid(trap_t)                                    (fp32)
+//   beta_t  = bf16(bf16(dt_{t+1}) * sigmoid(-trap_{t+1})), 0 at the last token
+//   factor_t = bf16(gamma_t + beta_t)
+//   exp(da_cs_t) (main only), exp(da_cs_rev_t)             (LITE: wave 1)
+//   exp(da_cs) of the chunk's last token, the chunk decay  (LITE: wave 2)
+// Tokens past the chunk's end get zero.
 template <int RP, int CT, int NT, int PT, bool MAIN>
 __device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, PT>& it, int c0, int cl,
-                                       const ChunkIn<RP, CT, NT, PT, MAIN>& in, unsigned char* smem, const Lds& L) {
+                                       const unsigned char* smb, const SmallRegs<RP, CT, NT, PT, MAIN>& sr,
+                                       unsigned char* smem, const Lds& L) {
     using T = Tile<RP, CT, NT, PT>;
-    const int tid = threadIdx.x;
+    using SG = Stage<RP, CT, NT, PT, MAIN>;
+    constexpr bool LITE = SG::LITE;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     float* sc = reinterpret_cast<float*>(smem + L.sc);
-    if (tid < T::Cp) {
-        float gam = 0.f, fac = 0.f, ecs = 0.f, erev = 0.f;
-        if (tid < cl) {
-            gam = rnd1(in.dt0) * sigmoid_precise(in.tr0);
+    const unsigned char* ss = smb + SG::SCAL + 4 * lane;
+    if (wave == 0 && lane < T::Cp) {
+        float gam = 0.f, fac = 0.f;
+        if (lane < cl) {
+            const float dt0 = LITE ? lds_ld<float>(ss + SG::DT0) : sr.dt0;
+            const float tr0 = LITE ? bf2f(lds_ld<unsigned short>(ss + SG::TR0)) : sr.tr0;
+            gam = __fmul_rn(rnd(dt0), sigmoid_fast(tr0));
             float beta = 0.f;
-            if (c0 + tid + 1 < p.S) beta = rnd1(rnd1(in.dt1) * sigmoid_precise(-in.tr1));
-            fac = rnd1(gam + beta);
-            erev = expf(in.rev);
-            if (MAIN) ecs = expf(in.cs);
+            if (c0 + lane + 1 < p.S) {
+                const float dt1 = LITE ? lds_ld<float>(ss + SG::DT1) : sr.dt1;
+                const float tr1 = LITE ? bf2f(lds_ld<unsigned short>(ss + SG::TR1)) : sr.tr1;
+                beta = rnd(__fmul_rn(rnd(dt1), sigmoid_fast(-tr1)));
+            }
+            fac = rnd(__fadd_rn(gam, beta));
         }
-        sc[tid] = ecs;
-        sc[kTok + tid] = gam;
-        sc[2 * kTok + tid] = erev;
-        sc[3 * kTok + tid] = fac;
+        sc[kTok + lane] = gam;
+        sc[3 * kTok + lane] = fac;
     }
-    if (tid == 0) sc[4 * kTok] = expf(in.dlast);
+    if (wave == (LITE ? 1 : 0) && lane < T::Cp) {
+        float ecs = 0.f, erev = 0.f;
+        if (lane < cl) {
+            erev = expf(LITE ? lds_ld<float>(ss + SG::REV) : sr.rev);
+            if (MAIN) ecs = expf(LITE ? lds_ld<float>(ss + SG::CS) : sr.cs);
+        }
+        sc[lane] = ecs;
+        sc[2 * kTok + lane] = erev;
+    }
+    if (tid == (LITE ? 128 : 0)) sc[4 * kTok] = expf(LITE ? lds_ld<float>(smb + SG::SCAL + SG::DLAST) : sr.dlast);
     float* scs = reinterpret_cast<float*>(smem + L.cs);
     const int CW = p.C * p.W;
 #pragma unroll
@@ -506,7 +574,7 @@ __device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, 
         const int e = tid + j * T::NTHR;
         if (e < CW) {
             float s = 0.f, co = 0.f;
-            if (it.ang_t[j] < cl) sincosf(in.ang[j], &s, &co);
+            if (it.ang_t[j] < cl) sin_cos(LITE ? lds_ld<float>(smb + SG::ANG + 4 * e) : sr.ang[j], s, co);
             scs[e] = co;
             scs[CW + e] = s;
         }
@@ -516,46 +584,47 @@ __device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, 
 #pragma unroll
         for (int j = 0; j < T::SEG_IT; ++j) {
             const int e = tid + j * T::NTHR;
-            if (e < p.C * p.C) se[e] = expf(in.seg[j]);
+            if (e < p.C * p.C) se[e] = expf(LITE ? lds_ld<float>(smb + SG::SEG + 4 * e) : sr.seg[(MAIN ? j : 0)]);
         }
     }
 }
 
-// bias + round of one 8-column group: bf16(x + bf16(bias)), packed
-__device__ __forceinline__ u32x4 add_bias(u32x4 x, u32x4 bias) {
-    u32x4 o;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o[d] = pk2(lo16(x[d]) + lo16(bias[d]), hi16(x[d]) + hi16(bias[d]));
-    return o;
-}
-
-// Rotate the column pairs (col0 + e, N/2 + col0 + e) of one group: a is the
-// first-half group, e the second; both packed bf16, rounded after rotation.
-__device__ __forceinline__ void rotate_group(u32x4& a, u32x4& e, int col0, int W, const float* cs, const float* sn) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const int n = col0 + 2 * d;
-        if (n < W) {
-            const float x0 = lo16(a[d]), x1 = hi16(a[d]);
-            const float y0 = lo16(e[d]), y1 = hi16(e[d]);
-            const float c0 = cs[n], c1 = cs[n + 1], s0 = sn[n], s1 = sn[n + 1];
-            a[d] = pk2(__fmul_rn(c0, x0) - __fmul_rn(s0, y0), __fmul_rn(c1, x1) - __fmul_rn(s1, y1));
-            e[d] = pk2(__fmul_rn(s0, x0) + __fmul_rn(c0, y0), __fmul_rn(s1, x1) + __fmul_rn(c1, y1));
-        }
-    }
-}
-
-__device__ __forceinline__ u32x4 scale_group(u32x4 a, float f) {
-    u32x4 o;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o[d] = pk2(lo16(a[d]) * f, hi16(a[d]) * f);
-    return o;
-}
-
-// Psi^T: sPsiT[p][r*Cp + t] = bf16(v[t,p] * bf16(mimo_v[r,p])), zero for padded tokens and columns.
+// Psi^T: sPsiT[p][r*Cp + t] = bf16(v[t,p] * bf16(mimo_v[r,p])), zero for padded
+// tokens, ranks and columns.
+// LITE families: items (token pair, rank, 8 value columns) from the small-input
+// buffer, handled by threads [t0, t0 + nth); the two tokens of a column go out as
+// one 4-byte write. Consecutive lanes take consecutive token pairs, then ranks,
+// so that the 32 lanes of a write hit 32 different banks.
 template <int RP, int CT, int NT, int PT, bool MAIN>
-__device__ __forceinline__ void fill_psi(const Params& p, int cl, const ChunkIn<RP, CT, NT, PT, MAIN>& in,
-                                         unsigned char* smem, const Lds& L) {
+__device__ __forceinline__ void fill_psi(const Params& p, int cl, const unsigned char* smb, unsigned char* smem,
+                                         const Lds& L, int t0, int nth) {
+    using T = Tile<RP, CT, NT, PT>;
+    using SG = Stage<RP, CT, NT, PT, MAIN>;
+    constexpr int TPN = T::Cp / 2;
+    unsigned short* sPsiT = reinterpret_cast<unsigned short*>(smem + L.r3);
+    const unsigned short* smv = reinterpret_cast<const unsigned short*>(smem + L.tb) + 2 * RP * NT;
+    for (int e = threadIdx.x - t0; e < T::PSI_ITEMS; e += nth) {
+        const int tp = e % TPN, r = (e / TPN) % RP, pg = e / (TPN * RP);
+        const int t = 2 * tp;
+        u32x4 va = lds_ld<u32x4>(smb + SG::V + (t + T::Cp * pg) * 16);
+        u32x4 vb = lds_ld<u32x4>(smb + SG::V + (t + 1 + T::Cp * pg) * 16);
+        const bool col_ok = 8 * pg < p.P;
+        if (!(col_ok && t < cl)) va = u32x4{0u, 0u, 0u, 0u};       // slots of absent tokens are stale
+        if (!(col_ok && t + 1 < cl)) vb = u32x4{0u, 0u, 0u, 0u};
+        const u32x4 m = lds_ld<u32x4>(smv + r * PT + 8 * pg);
+        unsigned short* dst = sPsiT + (8 * pg) * T::LDA + r * T::Cp + t;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const float m0 = lo16(m[d]), m1 = hi16(m[d]);
+            lds_st<unsigned>(dst + (2 * d) * T::LDA, pk2(lo16(va[d]) * m0, lo16(vb[d]) * m0));
+            lds_st<unsigned>(dst + (2 * d + 1) * T::LDA, pk2(hi16(va[d]) * m1, hi16(vb[d]) * m1));
+        }
+    }
+}
+// Other families: each thread's register v items (token t, 8 columns), every rank.
+template <int RP, int CT, int NT, int PT, bool MAIN>
+__device__ __forceinline__ void fill_psi_regs(const Params& p, int cl, const SmallRegs<RP, CT, NT, PT, MAIN>& in,
+                                              unsigned char* smem, const Lds& L) {
     using T = Tile<RP, CT, NT, PT>;
     const int tid = threadIdx.x;
     unsigned short* sPsiT = reinterpret_cast<unsigned short*>(smem + L.r3);
@@ -566,46 +635,78 @@ __device__ __forceinline__ void fill_psi(const Params& p, int cl, const ChunkIn<
         if (e >= T::Cp * (PT / 8)) continue;
         const int t = e % T::Cp, pc = (e / T::Cp) * 8;   // consecutive threads: consecutive tokens
         const bool real = t < cl && pc < p.P;
-        for (int r = 0; r < p.R; ++r) {
+        for (int r = 0; r < RP; ++r) {
             unsigned short* dst = sPsiT + pc * T::LDA + r * T::Cp + t;
-            if (real) {
-                const u32x4 mv = lds_ld<u32x4>(smv + r * PT + pc);
+            const u32x4 mv = lds_ld<u32x4>(smv + r * PT + pc);
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const unsigned u = pk2(lo16(in.v[j][d]) * lo16(mv[d]), hi16(in.v[j][d]) * hi16(mv[d]));
-                    dst[(2 * d) * T::LDA] = static_cast<unsigned short>(u);
-                    dst[(2 * d + 1) * T::LDA] = static_cast<unsigned short>(u >> 16);
-                }
-            } else {
-#pragma unroll
-                for (int d = 0; d < 8; ++d) dst[d * T::LDA] = 0;
+            for (int d = 0; d < 4; ++d) {
+                unsigned u = pk2(lo16(in.v[j][d]) * lo16(mv[d]), hi16(in.v[j][d]) * hi16(mv[d]));
+                if (!real) u = 0u;
+                dst[(2 * d) * T::LDA] = static_cast<unsigned short>(u);
+                dst[(2 * d + 1) * T::LDA] = static_cast<unsigned short>(u >> 16);
             }
         }
     }
 }
 
-// Tables filled once per workgroup: bf16(q_bias), bf16(k_bias), bf16(mimo_v) for head h,
-// and the zero padding of Psi^T that no chunk overwrites.
+// Tables filled once per workgroup: bf16(q_bias), bf16(k_bias), bf16(mimo_v) of
+// head h, zero for padded ranks and columns; and the rows of Psi^T beyond every
+// rank, which no chunk writes.
 template <int RP, int CT, int NT, int PT>
 __device__ __forceinline__ void fill_tables(const Params& p, int h, unsigned char* smem, const Lds& L) {
     using T = Tile<RP, CT, NT, PT>;
     const int tid = threadIdx.x;
     unsigned short* tb = reinterpret_cast<unsigned short*>(smem + L.tb);   // [RP][NT] x2, [RP][PT]
-    const int RN = p.R * p.N, RPn = p.R * p.P;
-    for (int e = tid; e < RN; e += T::NTHR) {
-        const int r = e / p.N, n = e - r * p.N;
-        tb[r * NT + n] = f2bf(p.q_bias[(long)h * RN + e]);
-        tb[RP * NT + r * NT + n] = f2bf(p.k_bias[(long)h * RN + e]);
+    for (int e = tid; e < RP * NT; e += T::NTHR) {
+        const int r = e / NT, n = e % NT;
+        const bool ok = r < p.R && n < p.N;
+        const long src = ((long)h * p.R + r) * p.N + n;
+        tb[e] = ok ? f2bf(p.q_bias[src]) : 0;
+        tb[RP * NT + e] = ok ? f2bf(p.k_bias[src]) : 0;
     }
-    for (int e = tid; e < RPn; e += T::NTHR) {
-        const int r = e / p.P, pc = e - r * p.P;
-        tb[2 * RP * NT + r * PT + pc] = f2bf(p.mimo_v[(long)h * RPn + e]);
+    for (int e = tid; e < RP * PT; e += T::NTHR) {
+        const int r = e / PT, pc = e % PT;
+        const bool ok = r < p.R && pc < p.P;
+        tb[2 * RP * NT + e] = ok ? f2bf(p.mimo_v[((long)h * p.R + r) * p.P + pc]) : 0;
     }
     unsigned short* sPsiT = reinterpret_cast<unsigned short*>(smem + L.r3);
-    const int used = p.R * T::Cp, pad = T::MT - used;
-    for (int e = tid; e < PT * pad; e += T::NTHR) {
-        const int pp = e / pad, i = used + e % pad;
-        sPsiT[pp * T::LDA + i] = 0;
+    constexpr int used = RP * T::Cp, pad = T::MT - used;
+    if constexpr (pad > 0) {
+        for (int e = tid; e < PT * pad; e += T::NTHR) {
+            const int pp = e / pad, i = used + e % pad;
+            sPsiT[pp * T::LDA + i] = 0;
+        }
+    }
+}
+
+// Biased, bf16-rounded values of one 8-column group of one row: x[d] = bf16(x + bias)
+__device__ __forceinline__ void bias_group(u32x4 x, const unsigned short* bias, float out[8]) {
+    const u32x4 b = lds_ld<u32x4>(bias);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        out[2 * d] = rnd(lo16(x[d]) + lo16(b[d]));
+        out[2 * d + 1] = rnd(hi16(x[d]) + hi16(b[d]));
+    }
+}
+__device__ __forceinline__ u32x4 pack8(const float x[8]) {
+    return u32x4{pk2(x[0], x[1]), pk2(x[2], x[3]), pk2(x[4], x[5]), pk2(x[6], x[7])};
+}
+// Rotation of the column pairs (col0 + d, N/2 + col0 + d) with d < lim (every d
+// when LIM >= 8): a holds the first-half values, e the second-half ones; the
+// products are rounded separately, the sums are left unrounded (the caller rounds).
+template <int LIM>
+__device__ __forceinline__ void rotate8(float a[8], float e[8], int lim, const float* cs, const float* sn) {
+    const f32x4 c0 = lds_ld<f32x4>(cs), c1 = lds_ld<f32x4>(cs + 4);
+    const f32x4 s0 = lds_ld<f32x4>(sn), s1 = lds_ld<f32x4>(sn + 4);
+    const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    const float s[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+        if (LIM >= 8 || d < lim) {
+            const float x = a[d], y = e[d];
+            a[d] = __fmul_rn(c[d], x) - __fmul_rn(s[d], y);
+            e[d] = __fmul_rn(s[d], x) + __fmul_rn(c[d], y);
+        }
     }
 }
 
@@ -665,6 +766,7 @@ template <int RP, int CT, int NT, int PT, bool EX>
 __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params pin) {
     const Params p = specialise<RP, CT, NT, PT, EX, -1>(pin);
     using T = Tile<RP, CT, NT, PT>;
+    using SG = Stage<RP, CT, NT, PT, false>;
     extern __shared__ __align__(16) unsigned char smem[];
     const Lds L = lds_layout(RP, CT, NT, PT, p.C, p.W, false);
     unsigned short* sKapT = reinterpret_cast<unsigned short*>(smem + L.r1);
@@ -683,16 +785,22 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
     const int c_begin = seg * La;
     const int c_end = c_begin + La;
     const int R = p.R;
+    // With one 8-column group per thread and rotary divisor 4, the threads of the
+    // first half hold exactly the rotated groups; the second half fills Psi^T.
+    constexpr bool SPLIT = SG::LITE && EX && T::QK_IT == 1 && T::MT * (NT / 32) == T::NTHR / 2;
+    const int psi_t0 = SPLIT ? T::NTHR / 2 : 0, psi_n = SPLIT ? T::NTHR / 2 : T::NTHR;
 
     Items<RP, CT, NT, PT> it;
-    make_items<RP, CT, NT, PT, true>(p, g, it);
+    make_items<RP, CT, NT, PT, true, false>(p, g, it);
     fill_tables<RP, CT, NT, PT>(p, h, smem, L);
     // kappa^T columns beyond the real rows, and rows n >= N, stay zero
     for (int e = tid; e < NT * T::MT; e += T::NTHR) sKapT[e / T::MT * T::LDA + e % T::MT] = 0;
 
-    using SG = Stage<RP, CT, NT, PT, false>;
-    __shared__ __align__(16) unsigned char stg[SG::ON ? SG::BYTES : 16];
-    if constexpr (SG::ON) prefetch_chunk<RP, CT, NT, PT, false>(p, it, b, h, bh, c_begin, c_begin * p.C, min(p.C, p.S - c_begin * p.C), stg);
+    __shared__ __align__(16) unsigned char stg[SG::BYTES];
+    unsigned char* qkst = stg + SG::QK;
+    if constexpr (SG::LITE)
+        prefetch_chunk<RP, CT, NT, PT, false, SG::QKON>(p, it, b, h, bh, c_begin, c_begin * p.C,
+                                                        min(p.C, p.S - c_begin * p.C), qkst, stg + (c_begin & 1) * SG::SMB);
 
     f32x4 U[T::STW];
 #pragma unroll
@@ -702,17 +810,24 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * p.C;
         const int cl = min(p.C, p.S - c0);
-        ChunkIn<RP, CT, NT, PT, false> in = {};
-        if constexpr (SG::ON) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's staging loads
-            read_stage(stg, in);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (c + 1 < c_end) prefetch_chunk<RP, CT, NT, PT, false>(p, it, b, h, bh, c + 1, c0 + p.C, min(p.C, p.S - c0 - p.C), stg);
+        const unsigned char* smb = stg + (c & 1) * SG::SMB;
+        ChunkQK<RP, CT, NT, PT, false> in = {};
+        SmallRegs<RP, CT, NT, PT, false> sr = {};
+        if constexpr (SG::LITE) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's staging loads of chunk c
+            if constexpr (SG::QKON) {
+                read_stage(qkst, in);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+            if (c + 1 < c_end)
+                prefetch_chunk<RP, CT, NT, PT, false, SG::QKON>(p, it, b, h, bh, c + 1, c0 + p.C,
+                                                                min(p.C, p.S - c0 - p.C), qkst, stg + ((c + 1) & 1) * SG::SMB);
         } else {
-            load_chunk(p, it, b, h, bh, c, c0, cl, in);
+            load_small(p, it, b, h, bh, c, c0, cl, sr);
         }
-        bar();   // previous chunk done with LDS (and tables written)
-        phase0(p, it, c0, cl, in, smem, L);
+        if constexpr (!SG::QKON) load_qk(p, it, b, c0, cl, in);
+        bar();   // chunk c's staging loads of every thread have landed; previous chunk done with LDS
+        phase0<RP, CT, NT, PT, false>(p, it, c0, cl, smb, sr, smem, L);
         bar();
         // kappa^T = bf16(bf16(rot(bf16(k + bf16(k_bias))) * factor) * exp(da_cs_rev)), transposed
 #pragma unroll
@@ -722,18 +837,22 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
             const int r = i / T::Cp, t = i % T::Cp;
             if (r >= R || t >= cl) continue;   // stays zero from the initial fill / last chunk
             const int col0 = it.qk_col[j], col1 = p.N / 2 + col0;
-            u32x4 a = add_bias(in.k0[j], lds_ld<u32x4>(tbk + r * NT + col0));
-            u32x4 e = add_bias(in.k1[j], lds_ld<u32x4>(tbk + r * NT + col1));
-            rotate_group(a, e, col0, p.W, scs + t * p.W, scs + p.C * p.W + t * p.W);
-            const float f = sc[3 * kTok + t], er = sc[2 * kTok + t];
-            a = scale_group(scale_group(a, f), er);
-            e = scale_group(scale_group(e, f), er);
+            float a[8], e[8];
+            bias_group(in.k0[j], tbk + r * NT + col0, a);
+            bias_group(in.k1[j], tbk + r * NT + col1, e);
+            if (col0 < p.W) {
+                rotate8<(EX ? 8 : 0)>(a, e, p.W - col0, scs + t * p.W + col0, scs + p.C * p.W + t * p.W + col0);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                sKapT[(col0 + 2 * d) * T::LDA + i] = static_cast<unsigned short>(a[d]);
-                sKapT[(col0 + 2 * d + 1) * T::LDA + i] = static_cast<unsigned short>(a[d] >> 16);
-                sKapT[(col1 + 2 * d) * T::LDA + i] = static_cast<unsigned short>(e[d]);
-                sKapT[(col1 + 2 * d + 1) * T::LDA + i] = static_cast<unsigned short>(e[d] >> 16);
+                for (int d = 0; d < 8; ++d) {
+                    a[d] = rnd(a[d]);
+                    e[d] = rnd(e[d]);
+                }
+            }
+            const float f = sc[3 * kTok + t], er = sc[2 * kTok + t];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                sKapT[(col0 + d) * T::LDA + i] = f2bf(rnd(a[d] * f) * er);
+                sKapT[(col1 + d) * T::LDA + i] = f2bf(rnd(e[d] * f) * er);
             }
         }
         if (cl < p.C) {
@@ -743,7 +862,11 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
                 if (i % T::Cp >= cl) sKapT[e / T::MT * T::LDA + i] = 0;
             }
         }
-        fill_psi(p, cl, in, smem, L);
+        if constexpr (SG::LITE) {
+            if (tid >= psi_t0) fill_psi<RP, CT, NT, PT, false>(p, cl, smb, smem, L, psi_t0, psi_n);
+        } else {
+            fill_psi_regs(p, cl, sr, smem, L);
+        }
         bar();
         const float dl = sc[4 * kTok];
 #pragma unroll
@@ -797,8 +920,11 @@ template <int RP, int CT, int NT, int PT, bool EX, int MODE>
 __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params pin) {
     const Params p = specialise<RP, CT, NT, PT, EX, MODE>(pin);
     using T = Tile<RP, CT, NT, PT>;
+    using SG = Stage<RP, CT, NT, PT, true>;
     constexpr int MT = T::MT, NW = T::NW, NTHR = T::NTHR, Cp = T::Cp;
     constexpr int LDQ = T::LDQ, LDA = T::LDA, PTT = T::PTT, MTT = T::MTT;
+    constexpr bool RSPLIT = EX && T::RSPLIT_OK;
+    constexpr bool PSPLIT = RSPLIT && SG::LITE;   // the second half fills Psi^T
     extern __shared__ __align__(16) unsigned char smem[];
     const Lds L = lds_layout(RP, CT, NT, PT, p.C, p.W, true);
     unsigned short* sQ = reinterpret_cast<unsigned short*>(smem + L.r1);   // also sA, sKapT
@@ -826,9 +952,12 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
     const int c_end = min(c_begin + p.L, p.nc);
     const int R = p.R;
     const bool need_y = p.need_y;
+    // which threads fill Psi^T (LITE families): the second half under the rotation split, else all
+    const int psi_t0 = PSPLIT ? NTHR / 2 : 0, psi_n = PSPLIT ? NTHR / 2 : NTHR;
+    const bool rot_half = !RSPLIT || tid < NTHR / 2;   // threads whose q/k groups may be rotated
 
     Items<RP, CT, NT, PT> it;
-    make_items(p, g, it);
+    make_items<RP, CT, NT, PT, false, RSPLIT>(p, g, it);
     fill_tables<RP, CT, NT, PT>(p, h, smem, L);
 
     // ---- state entering the segment (fp32, MFMA accumulator layout: rows n, columns p)
@@ -879,7 +1008,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             cz[ps][r] = co[ps][r] = dmo[ps][r] = dmz[ps][r] = 0.f;
             if (pair < T::NPAIRS && r < R && pc < p.P) {
                 if (p.has_z) cz[ps][r] = p.mimo_z[((long)h * R + r) * p.P + pc];
-                if (p.reduce_o) co[ps][r] = rnd1(p.mimo_o[((long)h * R + r) * p.P + pc]);
+                if (p.reduce_o) co[ps][r] = rnd(p.mimo_o[((long)h * R + r) * p.P + pc]);
             }
         }
     }
@@ -896,23 +1025,32 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             gate_off[ps][v] = (pair < T::NPAIRS && pc < p.P) ? 2u * (unsigned)(t * p.H * p.P + pc) : kOut;
         }
     }
-    using SG = Stage<RP, CT, NT, PT, true>;
-    __shared__ __align__(16) unsigned char stg[SG::ON ? SG::BYTES : 16];
-    if constexpr (SG::ON) prefetch_chunk<RP, CT, NT, PT, true>(p, it, b, h, bh, c_begin, c_begin * p.C, min(p.C, p.S - c_begin * p.C), stg);
+    __shared__ __align__(16) unsigned char stg[SG::BYTES];
+    unsigned char* qkst = stg + SG::QK;
+    if constexpr (SG::LITE)
+        prefetch_chunk<RP, CT, NT, PT, true, SG::QKON>(p, it, b, h, bh, c_begin, c_begin * p.C,
+                                                       min(p.C, p.S - c_begin * p.C), qkst, stg + (c_begin & 1) * SG::SMB);
 
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * p.C;
         const int cl = min(p.C, p.S - c0);
+        const unsigned char* smb = stg + (c & 1) * SG::SMB;
 
-        ChunkIn<RP, CT, NT, PT, true> in = {};
-        if constexpr (SG::ON) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's staging loads
-            read_stage(stg, in);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (c + 1 < c_end) prefetch_chunk<RP, CT, NT, PT, true>(p, it, b, h, bh, c + 1, c0 + p.C, min(p.C, p.S - c0 - p.C), stg);
+        ChunkQK<RP, CT, NT, PT, true> in = {};
+        SmallRegs<RP, CT, NT, PT, true> sr = {};
+        if constexpr (SG::LITE) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's staging loads of chunk c
+            if constexpr (SG::QKON) {
+                read_stage(qkst, in);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+            if (c + 1 < c_end)
+                prefetch_chunk<RP, CT, NT, PT, true, SG::QKON>(p, it, b, h, bh, c + 1, c0 + p.C,
+                                                               min(p.C, p.S - c0 - p.C), qkst, stg + ((c + 1) & 1) * SG::SMB);
         } else {
-            load_chunk(p, it, b, h, bh, c, c0, cl, in);
+            load_small(p, it, b, h, bh, c, c0, cl, sr);
         }
+        if constexpr (!SG::QKON) load_qk(p, it, b, c0, cl, in);
         // gate inputs of this lane's tokens, raw bf16, consumed in the epilogue. The
         // loads are issued unconditionally (lanes without a token read the chunk's
         // first element) so that nothing waits for them before the epilogue.
@@ -935,7 +1073,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                 }
             }
         }
-        bar();   // previous chunk (and the tables) done
+        bar();   // chunk c's staging loads of every thread have landed; previous chunk (and the tables) done
 
         // ---- states[c] = bf16(S entering chunk c), from sSbT ([p][n]) to [n][p], 16 bytes a thread
         {
@@ -955,10 +1093,11 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         if (p.has_z && c > c_begin) flush_dz<NTHR, PT>(p, sDz, b, h, c0 - p.C, p.C);
 
         // ---- phase 0: token scalars, cos/sin, exp(segsum)
-        phase0(p, it, c0, cl, in, smem, L);
+        phase0<RP, CT, NT, PT, true>(p, it, c0, cl, smb, sr, smem, L);
         bar();
 
-        // ---- phase A: biased q/k (unrotated into LDS, rotated kept in registers), Psi^T
+        // ---- phase A: biased q/k (unrotated into LDS, rotated and factor-scaled kept
+        // in registers), Psi^T
         u32x4 rq0[T::QK_IT], rq1[T::QK_IT], rk0[T::QK_IT], rk1[T::QK_IT];
 #pragma unroll
         for (int j = 0; j < T::QK_IT; ++j) {
@@ -966,30 +1105,44 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             if (i < 0) continue;
             const int r = i / Cp, t = i % Cp;
             const int col0 = it.qk_col[j], col1 = p.N / 2 + col0;
-            u32x4 qa = {0u, 0u, 0u, 0u}, qb = qa, ka = qa, kb = qa;
+            float qa[8], qe[8], ka[8], ke[8];
             if (r < R && t < cl) {
-                qa = add_bias(in.q0[j], lds_ld<u32x4>(tbq + r * NT + col0));
-                qb = add_bias(in.q1[j], lds_ld<u32x4>(tbq + r * NT + col1));
-                ka = add_bias(in.k0[j], lds_ld<u32x4>(tbk + r * NT + col0));
-                kb = add_bias(in.k1[j], lds_ld<u32x4>(tbk + r * NT + col1));
+                bias_group(in.q0[j], tbq + r * NT + col0, qa);
+                bias_group(in.q1[j], tbq + r * NT + col1, qe);
+                bias_group(in.k0[j], tbk + r * NT + col0, ka);
+                bias_group(in.k1[j], tbk + r * NT + col1, ke);
+            } else {
+#pragma unroll
+                for (int d = 0; d < 8; ++d) qa[d] = qe[d] = ka[d] = ke[d] = 0.f;
             }
-            lds_st<u32x4>(sQ + i * LDQ + col0, qa);
-            lds_st<u32x4>(sQ + i * LDQ + col1, qb);
-            lds_st<u32x4>(sK + i * LDQ + col0, ka);
-            lds_st<u32x4>(sK + i * LDQ + col1, kb);
-            if (r < R && t < cl) {
-                const float* cs = scs + t * p.W;
-                const float* sn = scs + p.C * p.W + t * p.W;
-                rotate_group(qa, qb, col0, p.W, cs, sn);
-                rotate_group(ka, kb, col0, p.W, cs, sn);
-                const float f = sc[3 * kTok + t];
-                ka = scale_group(ka, f);
-                kb = scale_group(kb, f);
+            const u32x4 uqa = pack8(qa), uqe = pack8(qe);
+            lds_st<u32x4>(sQ + i * LDQ + col0, uqa);
+            lds_st<u32x4>(sQ + i * LDQ + col1, uqe);
+            lds_st<u32x4>(sK + i * LDQ + col0, pack8(ka));
+            lds_st<u32x4>(sK + i * LDQ + col1, pack8(ke));
+            rq0[j] = uqa;
+            rq1[j] = uqe;
+            if (rot_half && col0 < p.W && r < R && t < cl) {
+                const float* cs = scs + t * p.W + col0;
+                const float* sn = scs + p.C * p.W + t * p.W + col0;
+                rotate8<(RSPLIT ? 8 : 0)>(qa, qe, p.W - col0, cs, sn);
+                rotate8<(RSPLIT ? 8 : 0)>(ka, ke, p.W - col0, cs, sn);
+                rq0[j] = pack8(qa);
+                rq1[j] = pack8(qe);
+#pragma unroll
+                for (int d = 0; d < 8; ++d) {
+                    ka[d] = rnd(ka[d]);
+                    ke[d] = rnd(ke[d]);
+                }
             }
-            rq0[j] = qa;
-            rq1[j] = qb;
-            rk0[j] = ka;
-            rk1[j] = kb;
+            const float f = sc[3 * kTok + t];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                ka[d] *= f;
+                ke[d] *= f;
+            }
+            rk0[j] = pack8(ka);
+            rk1[j] = pack8(ke);
         }
         if (p.N < NT) {
             // state columns beyond N are zero in both operands of the n-contractions
@@ -1000,49 +1153,73 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                 lds_st<u32x4>(sK + i * LDQ + col, u32x4{0u, 0u, 0u, 0u});
             }
         }
-        fill_psi(p, cl, in, smem, L);
+        if constexpr (SG::LITE) {
+            if (tid >= psi_t0) fill_psi<RP, CT, NT, PT, true>(p, cl, smb, smem, L, psi_t0, psi_n);
+        } else {
+            fill_psi_regs(p, cl, sr, smem, L);
+        }
         bar();
 
-        // ---- phase B: qk_dot of the same token (biased, unrotated), fp32 accumulate;
-        // padded rank pairs get zero
-        {
-            const int RR = R * R;
-            unsigned short* qko = p.qk_dot + ((long)bh * p.S + c0) * RR;
-            for (int e = tid; e < cl * RP * RP; e += NTHR) {
-                const int rr = e / cl, t = e - rr * cl;   // consecutive threads: consecutive tokens
-                const int r = rr / RP, r2 = rr % RP;
-                float sum = 0.f;
-                if (r < R && r2 < R) {
-                    const unsigned short* xq = sQ + (r * Cp + t) * LDQ;
-                    const unsigned short* xk = sK + (r2 * Cp + t) * LDQ;
-                    for (int n = 0; n < p.N; n += 8) {
-                        const u32x4 a = lds_ld<u32x4>(xq + n), bb = lds_ld<u32x4>(xk + n);
-                        sum = dot2(a[0], bb[0], sum);
-                        sum = dot2(a[1], bb[1], sum);
-                        sum = dot2(a[2], bb[2], sum);
-                        sum = dot2(a[3], bb[3], sum);
+        // ---- phase B: qk_dot of the same token (biased, unrotated) by MFMA: tile
+        // (ri, rj, tt) is Q0 rows of rank ri times K0 rows of rank rj over one token
+        // tile; its diagonal holds the same-token dots. Lane (l16, q4) holds rows
+        // 4*q4 .. 4*q4+3 of column l16, so the lanes with q4 == l16/4 hold one
+        // diagonal element each (token 16*tt + l16). Padded rank pairs get zero.
+#pragma unroll
+        for (int w = 0; w < (T::QKT + NW - 1) / NW; ++w) {
+            const int u = wave + w * NW;
+            if (T::QKT_FULL || u < T::QKT) {
+                const int rj = u % RP, ri = (u / RP) % RP, tt = u / (RP * RP);
+                float val = 0.f;
+                if (ri < R && rj < R) {
+                    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < NT / 32; ++ks) {
+                        const u32x4 a = lds_ld<u32x4>(sQ + (16 * (ri * CT + tt) + l16) * LDQ + 32 * ks + 8 * q4);
+                        const u32x4 bb = lds_ld<u32x4>(sK + (16 * (rj * CT + tt) + l16) * LDQ + 32 * ks + 8 * q4);
+                        a4 = mfma(a, bb, a4);
                     }
-                    const unsigned u = pk2(sum, 0.f);
-                    sum = lo16(u);
-                    qko[t * RR + r * R + r2] = static_cast<unsigned short>(u);
+                    const int v = l16 & 3;
+                    const float x01 = (v & 1) ? a4[1] : a4[0], x23 = (v & 1) ? a4[3] : a4[2];
+                    val = rnd((v & 2) ? x23 : x01);
                 }
-                sQK[t * QKS + rr] = sum;
+                if (q4 == (l16 >> 2)) sQK[(16 * tt + l16) * QKS + ri * RP + rj] = val;
             }
         }
         bar();
 
-        // ---- phase C: rotated q and factor-scaled k into LDS
+        // ---- phase C: rotated q and factor-scaled k into LDS; qk_dot of the chunk out
 #pragma unroll
         for (int j = 0; j < T::QK_IT; ++j) {
             const int i = it.qk_row[j];
             if (i < 0) continue;
             const int col0 = it.qk_col[j], col1 = p.N / 2 + col0;
-            if (need_y) {
+            if (need_y && rot_half) {
                 lds_st<u32x4>(sQ + i * LDQ + col0, rq0[j]);
                 lds_st<u32x4>(sQ + i * LDQ + col1, rq1[j]);
             }
             lds_st<u32x4>(sK + i * LDQ + col0, rk0[j]);
             lds_st<u32x4>(sK + i * LDQ + col1, rk1[j]);
+        }
+        {
+            const int RR = R * R;
+            unsigned short* qko = p.qk_dot + ((long)bh * p.S + c0) * RR;
+            if constexpr (EX && (RP * RP) % 8 == 0) {
+                // R = RP: a token's R*R values are contiguous in sQK; 8 per thread
+                constexpr int G8 = RP * RP / 8;
+                for (int e = tid; e < cl * G8; e += NTHR) {
+                    const int t = e / G8, k8 = (e % G8) * 8;
+                    const float* s = sQK + t * QKS + k8;
+                    const u32x4 o = {pk2(s[0], s[1]), pk2(s[2], s[3]), pk2(s[4], s[5]), pk2(s[6], s[7])};
+                    *reinterpret_cast<u32x4*>(qko + t * RR + k8) = o;
+                }
+            } else {
+                for (int e = tid; e < cl * RR; e += NTHR) {
+                    const int t = e / RR, rr = e % RR;
+                    const int r = rr / R, r2 = rr % R;
+                    qko[e] = bits16(sQK[t * QKS + r * RP + r2]);
+                }
+            }
         }
         bar();
 
@@ -1145,20 +1322,21 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             bar();   // every wave is done reading sA
         }
 
-        // ---- kappa^T = bf16(K~ * exp(da_cs_rev)), transposed, into R1
-        {
-            constexpr int n8 = NT / 8;
-            for (int e = tid; e < MT * n8; e += NTHR) {
-                const int i = e % MT, nn = (e / MT) * 8;   // consecutive threads: consecutive rows
-                const int r = i / Cp, t = i % Cp;
-                const u32x4 x = lds_ld<u32x4>(sK + i * LDQ + nn);
-                const float er = (r < R && t < cl) ? sc[2 * kTok + t] : 0.f;
+        // ---- kappa^T = bf16(K~ * exp(da_cs_rev)), transposed, into R1: items (row
+        // pair, 8 columns); the two rows of a column go out as one 4-byte write, and
+        // consecutive lanes take consecutive row pairs (32 banks per 32 lanes)
+        for (int e = tid; e < T::KAP_ITEMS; e += NTHR) {
+            const int ip = e % (MT / 2), nn = (e / (MT / 2)) * 8;
+            const int i = 2 * ip, r = i / Cp, t = i % Cp;
+            const u32x4 xa = lds_ld<u32x4>(sK + i * LDQ + nn), xb = lds_ld<u32x4>(sK + (i + 1) * LDQ + nn);
+            const bool rok = r < R;
+            const float ea = (rok && t < cl) ? sc[2 * kTok + t] : 0.f;
+            const float eb = (rok && t + 1 < cl) ? sc[2 * kTok + t + 1] : 0.f;
+            unsigned short* dst = sKapT + nn * LDA + i;
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const unsigned u = pk2(lo16(x[d]) * er, hi16(x[d]) * er);
-                    sKapT[(nn + 2 * d) * LDA + i] = static_cast<unsigned short>(u);
-                    sKapT[(nn + 2 * d + 1) * LDA + i] = static_cast<unsigned short>(u >> 16);
-                }
+            for (int d = 0; d < 4; ++d) {
+                lds_st<unsigned>(dst + (2 * d) * LDA, pk2(lo16(xa[d]) * ea, lo16(xb[d]) * eb));
+                lds_st<unsigned>(dst + (2 * d + 1) * LDA, pk2(hi16(xa[d]) * ea, hi16(xb[d]) * eb));
             }
         }
         bar();
@@ -1185,8 +1363,9 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         }
 
         // ---- y = bf16(inter + intra + diag + d*Psi) and the gating gradients. Ranks
-        // r >= R run on zero data (zero Psi rows, qk pairs and projections) and add
-        // nothing, so the rank loops need no bounds.
+        // r >= R, tokens past the chunk's end and columns p >= P run on zero data
+        // (zero Psi, qk pairs, projections, gate inputs and scales) and come out
+        // as zero, so nothing here needs a bound.
         if (need_y) {
 #pragma unroll
             for (int ps = 0; ps < T::PW; ++ps) {
@@ -1195,11 +1374,9 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                 const int tt = pair / PTT, pt = pair % PTT;
                 const int pc = 16 * pt + l16;
                 const int tb = 16 * tt + 4 * q4;   // first of this lane's 4 tokens
-                bool ok[4];
                 float zr[4], dr[4];   // zero outside the chunk (buffer range)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    ok[v] = tb + v < cl && pc < p.P;
                     zr[v] = bf2f(zraw[ps][v]);
                     dr[v] = bf2f(draw[ps][v]);
                 }
@@ -1216,80 +1393,45 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                 float dzc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
-                    // diagonal of two tokens at a time: rank-ordered bf16 products and sums
+                    // diagonal: rank-ordered chain of bf16 products and bf16 sums, times gamma
                     float y[4];
 #pragma unroll
-                    for (int vp = 0; vp < 2; ++vp) {
-                        const int va = 2 * vp, vb = va + 1;
-                        const float* qa = sQK + (tb + va) * QKS + r * RP;
-                        const float* qb = sQK + (tb + vb) * QKS + r * RP;
-                        float da = qa[0] * psi[0][va], db = qb[0] * psi[0][vb];
-                        rnd2(da, db);
+                    for (int v = 0; v < 4; ++v) {
+                        const float* qk = sQK + (tb + v) * QKS + r * RP;
+                        float dg = rnd(qk[0] * psi[0][v]);
 #pragma unroll
-                        for (int r2 = 1; r2 < RP; ++r2) {
-                            float pa = qa[r2] * psi[r2][va], pb = qb[r2] * psi[r2][vb];
-                            rnd2(pa, pb);
-                            da += pa;
-                            db += pb;
-                            rnd2(da, db);
-                        }
-                        da *= gam4[va];
-                        db *= gam4[vb];
-                        rnd2(da, db);
-                        float oa = acc[ps][r][va] + da, ob = acc[ps][r][vb] + db;
-                        oa += dval * psi[r][va];
-                        ob += dval * psi[r][vb];
-                        rnd2(oa, ob);
-                        // tokens past the chunk's end contribute nothing
-                        y[va] = (tb + va < cl) ? oa : 0.f;
-                        y[vb] = (tb + vb < cl) ? ob : 0.f;
+                        for (int r2 = 1; r2 < RP; ++r2) dg = rnd(dg + rnd(qk[r2] * psi[r2][v]));
+                        dg = rnd(dg * gam4[v]);
+                        y[v] = rnd(__fmaf_rn(dval, psi[r][v], __fadd_rn(acc[ps][r][v], dg)));
                     }
                     if (p.has_z) {
-                        float sg[4], pz[4], G[4], gz[4];
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
-                            pz[v] = zr[v] * cz[ps][r];
-                            sg[v] = sigmoid_fast(pz[v]);
-                        }
-                        if (p.reduce_o) {
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                dmo[ps][r] += (y[v] * (pz[v] * sg[v])) * dr[v];
-                                G[v] = dr[v] * co[ps][r];
-                            }
-                            rnd2(G[0], G[1]);
-                            rnd2(G[2], G[3]);
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) G[v] *= y[v];
-                        } else {
-                            // per-rank dout [B,S,R,H,P]; lanes without a token read element 0
-                            const long nb = ((long)(b * p.S + c0) * R + r) * p.H * p.P + (long)h * p.P;
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                const bool okr = ok[v] && r < R;
+                            const float pz = zr[v] * cz[ps][r];
+                            const float sg = sigmoid_fast(pz);
+                            float G;
+                            if (p.reduce_o) {
+                                dmo[ps][r] = __fmaf_rn(__fmul_rn(y[v], __fmul_rn(pz, sg)), dr[v], dmo[ps][r]);
+                                G = rnd(rnd(dr[v] * co[ps][r]) * y[v]);
+                            } else {
+                                // per-rank dout [B,S,R,H,P]; lanes without a token read element 0
+                                const bool okr = tb + v < cl && pc < p.P && r < R;
+                                const long nb = ((long)(b * p.S + c0) * R + r) * p.H * p.P + (long)h * p.P;
                                 const unsigned short raw = p.dout[okr ? nb + (long)(tb + v) * R * p.H * p.P + pc : 0];
-                                G[v] = (okr ? bf2f(raw) : 0.f) * y[v];
+                                G = rnd((okr ? bf2f(raw) : 0.f) * y[v]);
                             }
+                            const float gz = __fmul_rn(__fmul_rn(G, sg), __fmaf_rn(pz, 1.0f - sg, 1.0f));
+                            dzc[v] = rnd(dzc[v] + __fmul_rn(gz, cz[ps][r]));
+                            dmz[ps][r] = __fmaf_rn(gz, zr[v], dmz[ps][r]);
                         }
-                        rnd2(G[0], G[1]);
-                        rnd2(G[2], G[3]);
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            gz[v] = (G[v] * sg[v]) * (1.0f + pz[v] * (1.0f - sg[v]));
-                            dzc[v] += __fmul_rn(gz[v], cz[ps][r]);
-                            dmz[ps][r] += gz[v] * zr[v];
-                        }
-                        rnd2(dzc[0], dzc[1]);
-                        rnd2(dzc[2], dzc[3]);
                     } else if (p.reduce_o) {
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) dmo[ps][r] += y[v] * dr[v];
+                        for (int v = 0; v < 4; ++v) dmo[ps][r] = __fmaf_rn(y[v], dr[v], dmo[ps][r]);
                     }
                 }
                 if (p.has_z) {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (ok[v]) sDz[(tb + v) * (PT + 8) + pc] = f2bf(dzc[v]);
+                    for (int v = 0; v < 4; ++v) sDz[(tb + v) * (PT + 8) + pc] = bits16(dzc[v]);
                 }
             }
         }
