@@ -56,7 +56,8 @@ namespace mimo {
 // E_0 = 0, written in place to agg[j] where the chunk kernel reads it, i.e. at the
 // end of each segment ((j + 1) % F == 0). One thread per state element (the
 // chain is latency-bound, so more waves keep more loads in flight); loads run
-// up to 32 sub-segments ahead of the serial chain.
+// up to 64 sub-segments ahead of the serial chain, so that the usual segment
+// counts need a single round trip to memory.
 __global__ __launch_bounds__(256) void k_scan(Params p) {
     const int bh = blockIdx.y;
     const int NP = p.N * p.P;
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256) void k_scan(Params p) {
     float* base = p.agg + (long)bh * ns * NP + e;
     const float* dec = p.decay + (long)bh * ns;
     float E = 0.f;
-    constexpr int AHEAD = 32;
+    constexpr int AHEAD = 64;
     for (int s0 = 0; s0 < ns; s0 += AHEAD) {
         float U[AHEAD], D[AHEAD];
 #pragma unroll

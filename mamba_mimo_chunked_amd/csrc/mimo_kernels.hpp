@@ -214,24 +214,27 @@ __host__ __device__ constexpr Lds lds_layout(int RP, int CT, int NT, int PT, int
 //   exactly the slots it fetched, into registers, before it issues the next
 //   prefetch.
 // The other families load their inputs into registers at the top of the chunk.
-template <int RP, int CT, int NT, int PT, bool MAIN>
+template <int RP, int CT, int NT, int PT, bool MAIN, bool EX>
 struct Stage {
     using T = Tile<RP, CT, NT, PT>;
     static constexpr int NQ = MAIN ? 4 : 2;                        // q0, q1, k0, k1 (or k0, k1)
+    // slot regions sized to the items a chunk can have (W <= NT/4 in the shape-exact
+    // instances, NT/2 otherwise); lanes past the last item write nothing
     static constexpr int V = 0;                                    // slot t + Cp*pg: v[t][8pg .. 8pg+7]
     static constexpr int ANG = V + T::Cp * PT * 2;                 // slot e = t*W + n: angle
-    static constexpr int SEG = ANG + T::ANG_IT * T::NTHR * 4;      // slot e = ti*C + tj: segsum
-    static constexpr int SCAL = SEG + (MAIN ? T::SEG_IT * T::NTHR * 4 : 0);   // [7][64] dwords
-    static constexpr int SMB = SCAL + 7 * 64 * 4;                  // one small-input buffer
+    static constexpr int SEG = ANG + T::Cp * (EX ? NT / 4 : NT / 2) * 4;   // slot e = ti*C + tj: segsum
+    static constexpr int SCAL = SEG + (MAIN ? T::Cp * T::Cp * 4 : 0);      // 7 rows of Cp dwords
+    static constexpr int SMB = align16(SCAL + (6 * T::Cp + 1) * 4);       // one small-input buffer
     static constexpr int QKB = T::QK_IT * NQ * T::NTHR * 16;       // q/k of one chunk
     // dynamic LDS of the family at its largest chunk (C = Cp, W = NT/2)
-    static constexpr int DYN = lds_layout(RP, CT, NT, PT, T::Cp, NT / 2, MAIN).total + 256;
+    static constexpr int DYN = lds_layout(RP, CT, NT, PT, T::Cp, EX ? NT / 4 : NT / 2, MAIN).total + 256;
     static constexpr bool LITE = DYN + 2 * SMB <= 80 * 1024;
     static constexpr bool QKON = LITE && DYN + 2 * SMB + QKB <= 80 * 1024;
     static constexpr int QK = 2 * SMB;
     static constexpr int BYTES = LITE ? 2 * SMB + (QKON ? QKB : 0) : 16;
     // scalar rows inside SCAL
-    static constexpr int DT0 = 0, DT1 = 256, TR0 = 512, TR1 = 768, CS = 1024, REV = 1280, DLAST = 1536;
+    static constexpr int DT0 = 0, DT1 = 4 * T::Cp, TR0 = 8 * T::Cp, TR1 = 12 * T::Cp, CS = 16 * T::Cp,
+                         REV = 20 * T::Cp, DLAST = 24 * T::Cp;
 };
 
 // q/k of one chunk in registers
@@ -433,11 +436,11 @@ MIMO_DMA(dma2, "global_load_lds_ushort")
 // Issue the staging loads of chunk c (first token c0, cl real tokens): q/k into
 // qkst (when QKON), the small inputs into the buffer smb. Every address is a
 // scalar chunk base plus a per-lane offset that does not change from chunk to chunk.
-template <int RP, int CT, int NT, int PT, bool MAIN, bool QKON>
+template <int RP, int CT, int NT, int PT, bool MAIN, bool QKON, bool EX>
 __device__ __forceinline__ void prefetch_chunk(const Params& p, const Items<RP, CT, NT, PT>& it, int b, int h, int bh,
                                                int c, int c0, int cl, unsigned char* qkst, unsigned char* smb) {
     using T = Tile<RP, CT, NT, PT>;
-    using SG = Stage<RP, CT, NT, PT, MAIN>;
+    using SG = Stage<RP, CT, NT, PT, MAIN, EX>;
     const int tid = threadIdx.x, wave = tid >> 6;
     const int R = p.R;
     if constexpr (QKON) {
@@ -501,10 +504,10 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const Items<RP, 
 }
 
 // Copy this thread's staged q/k slots into registers.
-template <int RP, int CT, int NT, int PT, bool MAIN>
+template <int RP, int CT, int NT, int PT, bool MAIN, bool EX>
 __device__ __forceinline__ void read_stage(const unsigned char* qkst, ChunkQK<RP, CT, NT, PT, MAIN>& in) {
     using T = Tile<RP, CT, NT, PT>;
-    using SG = Stage<RP, CT, NT, PT, MAIN>;
+    using SG = Stage<RP, CT, NT, PT, MAIN, EX>;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < T::QK_IT; ++j) {
@@ -530,12 +533,12 @@ __device__ __forceinline__ void read_stage(const unsigned char* qkst, ChunkQK<RP
 //   exp(da_cs_t) (main only), exp(da_cs_rev_t)             (LITE: wave 1)
 //   exp(da_cs) of the chunk's last token, the chunk decay  (LITE: wave 2)
 // Tokens past the chunk's end get zero.
-template <int RP, int CT, int NT, int PT, bool MAIN>
+template <int RP, int CT, int NT, int PT, bool MAIN, bool EX>
 __device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, PT>& it, int c0, int cl,
                                        const unsigned char* smb, const SmallRegs<RP, CT, NT, PT, MAIN>& sr,
                                        unsigned char* smem, const Lds& L) {
     using T = Tile<RP, CT, NT, PT>;
-    using SG = Stage<RP, CT, NT, PT, MAIN>;
+    using SG = Stage<RP, CT, NT, PT, MAIN, EX>;
     constexpr bool LITE = SG::LITE;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     float* sc = reinterpret_cast<float*>(smem + L.sc);
@@ -595,11 +598,11 @@ __device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, 
 // buffer, handled by threads [t0, t0 + nth); the two tokens of a column go out as
 // one 4-byte write. Consecutive lanes take consecutive token pairs, then ranks,
 // so that the 32 lanes of a write hit 32 different banks.
-template <int RP, int CT, int NT, int PT, bool MAIN>
+template <int RP, int CT, int NT, int PT, bool MAIN, bool EX>
 __device__ __forceinline__ void fill_psi(const Params& p, int cl, const unsigned char* smb, unsigned char* smem,
                                          const Lds& L, int t0, int nth) {
     using T = Tile<RP, CT, NT, PT>;
-    using SG = Stage<RP, CT, NT, PT, MAIN>;
+    using SG = Stage<RP, CT, NT, PT, MAIN, EX>;
     constexpr int TPN = T::Cp / 2;
     unsigned short* sPsiT = reinterpret_cast<unsigned short*>(smem + L.r3);
     const unsigned short* smv = reinterpret_cast<const unsigned short*>(smem + L.tb) + 2 * RP * NT;
@@ -766,7 +769,7 @@ template <int RP, int CT, int NT, int PT, bool EX>
 __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params pin) {
     const Params p = specialise<RP, CT, NT, PT, EX, -1>(pin);
     using T = Tile<RP, CT, NT, PT>;
-    using SG = Stage<RP, CT, NT, PT, false>;
+    using SG = Stage<RP, CT, NT, PT, false, EX>;
     extern __shared__ __align__(16) unsigned char smem[];
     const Lds L = lds_layout(RP, CT, NT, PT, p.C, p.W, false);
     unsigned short* sKapT = reinterpret_cast<unsigned short*>(smem + L.r1);
@@ -799,7 +802,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
     __shared__ __align__(16) unsigned char stg[SG::BYTES];
     unsigned char* qkst = stg + SG::QK;
     if constexpr (SG::LITE)
-        prefetch_chunk<RP, CT, NT, PT, false, SG::QKON>(p, it, b, h, bh, c_begin, c_begin * p.C,
+        prefetch_chunk<RP, CT, NT, PT, false, SG::QKON, EX>(p, it, b, h, bh, c_begin, c_begin * p.C,
                                                         min(p.C, p.S - c_begin * p.C), qkst, stg + (c_begin & 1) * SG::SMB);
 
     f32x4 U[T::STW];
@@ -816,18 +819,18 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
         if constexpr (SG::LITE) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's staging loads of chunk c
             if constexpr (SG::QKON) {
-                read_stage(qkst, in);
+                read_stage<RP, CT, NT, PT, false, EX>(qkst, in);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             }
             if (c + 1 < c_end)
-                prefetch_chunk<RP, CT, NT, PT, false, SG::QKON>(p, it, b, h, bh, c + 1, c0 + p.C,
+                prefetch_chunk<RP, CT, NT, PT, false, SG::QKON, EX>(p, it, b, h, bh, c + 1, c0 + p.C,
                                                                 min(p.C, p.S - c0 - p.C), qkst, stg + ((c + 1) & 1) * SG::SMB);
         } else {
             load_small(p, it, b, h, bh, c, c0, cl, sr);
         }
         if constexpr (!SG::QKON) load_qk(p, it, b, c0, cl, in);
         bar();   // chunk c's staging loads of every thread have landed; previous chunk done with LDS
-        phase0<RP, CT, NT, PT, false>(p, it, c0, cl, smb, sr, smem, L);
+        phase0<RP, CT, NT, PT, false, EX>(p, it, c0, cl, smb, sr, smem, L);
         bar();
         // kappa^T = bf16(bf16(rot(bf16(k + bf16(k_bias))) * factor) * exp(da_cs_rev)), transposed
 #pragma unroll
@@ -863,7 +866,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
             }
         }
         if constexpr (SG::LITE) {
-            if (tid >= psi_t0) fill_psi<RP, CT, NT, PT, false>(p, cl, smb, smem, L, psi_t0, psi_n);
+            if (tid >= psi_t0) fill_psi<RP, CT, NT, PT, false, EX>(p, cl, smb, smem, L, psi_t0, psi_n);
         } else {
             fill_psi_regs(p, cl, sr, smem, L);
         }
@@ -920,7 +923,7 @@ template <int RP, int CT, int NT, int PT, bool EX, int MODE>
 __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params pin) {
     const Params p = specialise<RP, CT, NT, PT, EX, MODE>(pin);
     using T = Tile<RP, CT, NT, PT>;
-    using SG = Stage<RP, CT, NT, PT, true>;
+    using SG = Stage<RP, CT, NT, PT, true, EX>;
     constexpr int MT = T::MT, NW = T::NW, NTHR = T::NTHR, Cp = T::Cp;
     constexpr int LDQ = T::LDQ, LDA = T::LDA, PTT = T::PTT, MTT = T::MTT;
     constexpr bool RSPLIT = EX && T::RSPLIT_OK;
@@ -1028,7 +1031,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
     __shared__ __align__(16) unsigned char stg[SG::BYTES];
     unsigned char* qkst = stg + SG::QK;
     if constexpr (SG::LITE)
-        prefetch_chunk<RP, CT, NT, PT, true, SG::QKON>(p, it, b, h, bh, c_begin, c_begin * p.C,
+        prefetch_chunk<RP, CT, NT, PT, true, SG::QKON, EX>(p, it, b, h, bh, c_begin, c_begin * p.C,
                                                        min(p.C, p.S - c_begin * p.C), qkst, stg + (c_begin & 1) * SG::SMB);
 
     for (int c = c_begin; c < c_end; ++c) {
@@ -1041,11 +1044,11 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         if constexpr (SG::LITE) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's staging loads of chunk c
             if constexpr (SG::QKON) {
-                read_stage(qkst, in);
+                read_stage<RP, CT, NT, PT, true, EX>(qkst, in);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             }
             if (c + 1 < c_end)
-                prefetch_chunk<RP, CT, NT, PT, true, SG::QKON>(p, it, b, h, bh, c + 1, c0 + p.C,
+                prefetch_chunk<RP, CT, NT, PT, true, SG::QKON, EX>(p, it, b, h, bh, c + 1, c0 + p.C,
                                                                min(p.C, p.S - c0 - p.C), qkst, stg + ((c + 1) & 1) * SG::SMB);
         } else {
             load_small(p, it, b, h, bh, c, c0, cl, sr);
@@ -1093,7 +1096,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         if (p.has_z && c > c_begin) flush_dz<NTHR, PT>(p, sDz, b, h, c0 - p.C, p.C);
 
         // ---- phase 0: token scalars, cos/sin, exp(segsum)
-        phase0<RP, CT, NT, PT, true>(p, it, c0, cl, smb, sr, smem, L);
+        phase0<RP, CT, NT, PT, true, EX>(p, it, c0, cl, smb, sr, smem, L);
         bar();
 
         // ---- phase A: biased q/k (unrotated into LDS, rotated and factor-scaled kept
@@ -1154,7 +1157,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             }
         }
         if constexpr (SG::LITE) {
-            if (tid >= psi_t0) fill_psi<RP, CT, NT, PT, true>(p, cl, smb, smem, L, psi_t0, psi_n);
+            if (tid >= psi_t0) fill_psi<RP, CT, NT, PT, true, EX>(p, cl, smb, smem, L, psi_t0, psi_n);
         } else {
             fill_psi_regs(p, cl, sr, smem, L);
         }
