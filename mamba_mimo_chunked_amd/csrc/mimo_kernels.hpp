@@ -167,12 +167,12 @@ struct Lds {
     int r2;   // bf16 [MT][LDQ] k (main only)
     int r3;   // bf16 [PT][LDA] Psi^T
     int r4;   // bf16 [PT][LDQ] bf16(state)^T (main only)
-    int qk;   // fp32 [Cp][RP*RP+1] qk_dot, zero for padded ranks, one pad word per token (main only)
+    int qk;   // fp32 [Cp][RP*RP+RP] qk_dot, zero for padded ranks, RP pad words per token (main only)
     int dz;   // bf16 [Cp][PT+8] dz of the chunk, written out at the top of the next one (main only)
     int sc;   // fp32 [5][kTok] token scalars + chunk decay
     int tb;   // bf16 tables: q_bias [RP][NT], k_bias [RP][NT], mimo_v [RP][PT]
-    int cs;   // fp32 [2][C][W] cos, sin
-    int se;   // fp32 [C][C] exp(segsum) (main only)
+    int cs;   // fp32 [2][C][W + 4] cos, sin (rows padded: 8 consecutive tokens hit distinct banks)
+    int se;   // fp32 [C][C + 4] exp(segsum) (main only; rows padded likewise)
     int total;
 };
 
@@ -190,12 +190,12 @@ __host__ __device__ constexpr Lds lds_layout(int RP, int CT, int NT, int PT, int
     s.r2 = off; if (main) off += align16(MT * ldq * 2);
     s.r3 = off; off += align16(PT * lda * 2);
     s.r4 = off; if (main) off += align16(PT * ldq * 2);
-    s.qk = off; if (main) off += align16(Cp * (RP * RP + 1) * 4);
+    s.qk = off; if (main) off += align16(Cp * (RP * RP + RP) * 4);
     s.dz = off; if (main) off += align16(Cp * (PT + 8) * 2);
     s.sc = off; off += align16((5 * kTok + 4) * 4);
     s.tb = off; off += align16((2 * RP * NT + RP * PT) * 2);
-    s.cs = off; off += align16(2 * C * W * 4);
-    s.se = off; if (main) off += align16(C * C * 4);
+    s.cs = off; off += align16(2 * C * (W + 4) * 4);
+    s.se = off; if (main) off += align16(C * (C + 4) * 4);
     s.total = off + 16;   // slack: 8-wide cos/sin reads of a partial last group stay inside
     return s;
 }
@@ -272,8 +272,8 @@ struct Items {
 
 // q/k items. ROWS_FAST: consecutive threads take consecutive tile rows (the
 // chunk-aggregate kernel writes kappa^T transposed straight from registers).
-// RSPLIT: the rotation split described at Tile::RSPLIT_OK. Otherwise the
-// 8-column groups of one row are adjacent.
+// RSPLIT: the rotation split described at Tile::RSPLIT_OK (rows fastest within
+// each half). Otherwise the 8-column groups of one row are adjacent.
 template <int RP, int CT, int NT, int PT, bool ROWS_FAST, bool RSPLIT>
 __device__ __forceinline__ void make_items(const Params& p, int g, Items<RP, CT, NT, PT>& it) {
     using T = Tile<RP, CT, NT, PT>;
@@ -283,10 +283,12 @@ __device__ __forceinline__ void make_items(const Params& p, int g, Items<RP, CT,
     for (int j = 0; j < T::QK_IT; ++j) {
         int i = -1, gg = 0;
         if constexpr (RSPLIT) {
+            // rows fastest: 8 consecutive lanes write 8 rows of one column group,
+            // which the padded row pitch spreads over all banks
             constexpr int GR = NT / 32, HALF = T::NTHR / 2;
             const int half = tid / HALF, e = tid % HALF + j * HALF;
-            i = e / GR;
-            gg = e % GR + half * GR;
+            i = e % T::MT;
+            gg = e / T::MT + half * GR;
         } else {
             const int e = tid + j * T::NTHR;
             if (e < T::MT * ng) {
@@ -571,15 +573,16 @@ __device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, 
     }
     if (tid == (LITE ? 128 : 0)) sc[4 * kTok] = expf(LITE ? lds_ld<float>(smb + SG::SCAL + SG::DLAST) : sr.dlast);
     float* scs = reinterpret_cast<float*>(smem + L.cs);
-    const int CW = p.C * p.W;
+    const int CW = p.C * p.W, WP = p.W + 4;
 #pragma unroll
     for (int j = 0; j < T::ANG_IT; ++j) {
         const int e = tid + j * T::NTHR;
         if (e < CW) {
+            const int t = it.ang_t[j], n = e - t * p.W;
             float s = 0.f, co = 0.f;
-            if (it.ang_t[j] < cl) sin_cos(LITE ? lds_ld<float>(smb + SG::ANG + 4 * e) : sr.ang[j], s, co);
-            scs[e] = co;
-            scs[CW + e] = s;
+            if (t < cl) sin_cos(LITE ? lds_ld<float>(smb + SG::ANG + 4 * e) : sr.ang[j], s, co);
+            scs[t * WP + n] = co;
+            scs[(p.C + t) * WP + n] = s;
         }
     }
     if (MAIN && p.need_y) {
@@ -587,7 +590,10 @@ __device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, 
 #pragma unroll
         for (int j = 0; j < T::SEG_IT; ++j) {
             const int e = tid + j * T::NTHR;
-            if (e < p.C * p.C) se[e] = expf(LITE ? lds_ld<float>(smb + SG::SEG + 4 * e) : sr.seg[(MAIN ? j : 0)]);
+            if (e < p.C * p.C) {
+                const int ti = e / p.C, tj = e - ti * p.C;
+                se[ti * (p.C + 4) + tj] = expf(LITE ? lds_ld<float>(smb + SG::SEG + 4 * e) : sr.seg[(MAIN ? j : 0)]);
+            }
         }
     }
 }
@@ -596,8 +602,9 @@ __device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, 
 // tokens, ranks and columns.
 // LITE families: items (token pair, rank, 8 value columns) from the small-input
 // buffer, handled by threads [t0, t0 + nth); the two tokens of a column go out as
-// one 4-byte write. Consecutive lanes take consecutive token pairs, then ranks,
-// so that the 32 lanes of a write hit 32 different banks.
+// one 4-byte write. Consecutive lanes take consecutive ranks, then token pairs:
+// the 32 lanes of a write hit 32 different banks, and each group of 8 lanes
+// reads two v slots in different banks.
 template <int RP, int CT, int NT, int PT, bool MAIN, bool EX>
 __device__ __forceinline__ void fill_psi(const Params& p, int cl, const unsigned char* smb, unsigned char* smem,
                                          const Lds& L, int t0, int nth) {
@@ -607,7 +614,7 @@ __device__ __forceinline__ void fill_psi(const Params& p, int cl, const unsigned
     unsigned short* sPsiT = reinterpret_cast<unsigned short*>(smem + L.r3);
     const unsigned short* smv = reinterpret_cast<const unsigned short*>(smem + L.tb) + 2 * RP * NT;
     for (int e = threadIdx.x - t0; e < T::PSI_ITEMS; e += nth) {
-        const int tp = e % TPN, r = (e / TPN) % RP, pg = e / (TPN * RP);
+        const int r = e % RP, tp = (e / RP) % TPN, pg = e / (TPN * RP);
         const int t = 2 * tp;
         u32x4 va = lds_ld<u32x4>(smb + SG::V + (t + T::Cp * pg) * 16);
         u32x4 vb = lds_ld<u32x4>(smb + SG::V + (t + 1 + T::Cp * pg) * 16);
@@ -844,7 +851,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
             bias_group(in.k0[j], tbk + r * NT + col0, a);
             bias_group(in.k1[j], tbk + r * NT + col1, e);
             if (col0 < p.W) {
-                rotate8<(EX ? 8 : 0)>(a, e, p.W - col0, scs + t * p.W + col0, scs + p.C * p.W + t * p.W + col0);
+                rotate8<(EX ? 8 : 0)>(a, e, p.W - col0, scs + t * (p.W + 4) + col0, scs + (p.C + t) * (p.W + 4) + col0);
 #pragma unroll
                 for (int d = 0; d < 8; ++d) {
                     a[d] = rnd(a[d]);
@@ -940,7 +947,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
     const float* sE = reinterpret_cast<const float*>(smem + L.se);
     float* sQK = reinterpret_cast<float*>(smem + L.qk);
     unsigned short* sDz = reinterpret_cast<unsigned short*>(smem + L.dz);
-    constexpr int QKS = RP * RP + 1;   // sQK pitch per token
+    constexpr int QKS = RP * RP + RP;   // sQK pitch per token: a rank's RP values are 4*RP-byte aligned
     const float* sc = reinterpret_cast<const float*>(smem + L.sc);
     const unsigned short* tbq = reinterpret_cast<const unsigned short*>(smem + L.tb);
     const unsigned short* tbk = tbq + RP * NT;
@@ -1126,8 +1133,8 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             rq0[j] = uqa;
             rq1[j] = uqe;
             if (rot_half && col0 < p.W && r < R && t < cl) {
-                const float* cs = scs + t * p.W + col0;
-                const float* sn = scs + p.C * p.W + t * p.W + col0;
+                const float* cs = scs + t * (p.W + 4) + col0;
+                const float* sn = scs + (p.C + t) * (p.W + 4) + col0;
                 rotate8<(RSPLIT ? 8 : 0)>(qa, qe, p.W - col0, cs, sn);
                 rotate8<(RSPLIT ? 8 : 0)>(ka, ke, p.W - col0, cs, sn);
                 rq0[j] = pack8(qa);
@@ -1274,11 +1281,11 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                     const int ti = 16 * tti + l16, tj0 = 16 * ttj + 4 * q4;
                     f32x4 e;
                     if constexpr (EX) {
-                        e = lds_ld<f32x4>(sE + ti * Cp + tj0);   // C == Cp: always inside the block
+                        e = lds_ld<f32x4>(sE + ti * (Cp + 4) + tj0);   // C == Cp: always inside the block
                     } else {
                         const int tic = min(ti, p.C - 1);
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) e[v] = sE[tic * p.C + min(tj0 + v, p.C - 1)];
+                        for (int v = 0; v < 4; ++v) e[v] = sE[tic * (p.C + 4) + min(tj0 + v, p.C - 1)];
                     }
                     float m[4];
 #pragma unroll
