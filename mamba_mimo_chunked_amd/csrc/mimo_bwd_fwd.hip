@@ -133,6 +133,7 @@ mimo_status fail(mimo_status s, const char* fmt, ...) {
 
 struct Plan {
     int RP, CT, MT, NW, NT, PT, Cp, W, nc, L, nseg, F, nsub;
+    bool ex;   // the shape-exact kernel instances apply
     size_t off_agg, off_decay, off_po, off_pz, ws_bytes;
     int lds_agg, lds_main;
 };
@@ -145,6 +146,30 @@ int next_pow2(int x) {
     return y;
 }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int tidx(int x) { return x == 32 ? 0 : (x == 64 ? 1 : 2); }
+
+// MIMO_FORCE_GENERIC=1 in the environment disables the shape-exact kernel
+// instances (used by the tests to compare both paths on the same inputs).
+bool force_generic() {
+    const char* e = getenv("MIMO_FORCE_GENERIC");
+    return e != nullptr && e[0] == '1';
+}
+
+const Family* family(int RP, int CT) {
+    switch (RP * 10 + CT) {
+        case 11: return family_rp1_ct1();
+        case 12: return family_rp1_ct2();
+        case 14: return family_rp1_ct4();
+        case 21: return family_rp2_ct1();
+        case 22: return family_rp2_ct2();
+        case 24: return family_rp2_ct4();
+        case 41: return family_rp4_ct1();
+        case 42: return family_rp4_ct2();
+        case 81: return family_rp8_ct1();
+        default: return nullptr;
+    }
+}
 
 mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
     if (a == nullptr) return fail(MIMO_ERR_VALUE, "args must not be NULL");
@@ -186,6 +211,7 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
     pl->nc = (int)((S + C - 1) / C);
     // segments: about two workgroups per compute unit, so that every
     // workgroup of the chunk kernel is resident at once
+    pl->ex = !force_generic() && R == RP && N == pl->NT && P == pl->PT && C == pl->Cp && rd == 4;
     const int64_t target = 512;
     int64_t L = (pl->nc * B * H + target - 1) / target;
     if (L < 1) L = 1;
@@ -222,30 +248,6 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
     if (pl->lds_main > 160 * 1024)
         return fail(MIMO_ERR_UNSUPPORTED, "shape needs %d bytes of LDS per workgroup (limit 163840)", pl->lds_main);
     return MIMO_OK;
-}
-
-int tidx(int x) { return x == 32 ? 0 : (x == 64 ? 1 : 2); }
-
-// MIMO_FORCE_GENERIC=1 in the environment disables the shape-exact kernel
-// instances (used by the tests to compare both paths on the same inputs).
-bool force_generic() {
-    const char* e = getenv("MIMO_FORCE_GENERIC");
-    return e != nullptr && e[0] == '1';
-}
-
-const Family* family(int RP, int CT) {
-    switch (RP * 10 + CT) {
-        case 11: return family_rp1_ct1();
-        case 12: return family_rp1_ct2();
-        case 14: return family_rp1_ct4();
-        case 21: return family_rp2_ct1();
-        case 22: return family_rp2_ct2();
-        case 24: return family_rp2_ct4();
-        case 41: return family_rp4_ct1();
-        case 42: return family_rp4_ct2();
-        case 81: return family_rp8_ct1();
-        default: return nullptr;
-    }
 }
 
 std::mutex g_mu;
@@ -352,7 +354,7 @@ static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* ev
     if (fam == nullptr) return fail(MIMO_ERR_UNSUPPORTED, "no kernel for this tile shape");
     // shape-exact instances when the call's shape equals the tile (see specialise())
     const int ti = tidx(pl.NT) * 3 + tidx(pl.PT);
-    const bool ex = !force_generic() && p.R == pl.RP && p.N == pl.NT && p.P == pl.PT && p.C == pl.Cp && p.rd == 4;
+    const bool ex = pl.ex;
     kfn kmain = fam->main[ti];
     if (ex && !p.need_y) kmain = fam->main_ex_noy[ti];
     if (ex && p.reduce_o && p.has_z) kmain = fam->main_ex_rz[ti];

@@ -31,7 +31,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTok = 64;  // tokens per chunk tile (Cp) at most
 
 // ---------------------------------------------------------------- bf16 helpers
 // bf16(a) in the low and bf16(b) in the high half, round to nearest even.
@@ -50,6 +49,23 @@ __device__ __forceinline__ unsigned short bits16(float x) { return static_cast<u
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// One MFMA operand fragment of a row-major bf16 tile T[k][n] (pitch ld): lane
+// (l16, q4) gets T[k0 + 8*q4 + 0..7][n0 + l16], the 8 consecutive contraction
+// indices of column n0 + l16, from two transpose reads (ds_read_b64_tr_b16). In
+// each 16-lane group, lane j of a read receives element j % 4 of the 4-element
+// pieces supplied by lanes j/4, j/4 + 4, j/4 + 8 and j/4 + 12; so lane s points
+// at row R0 + s/4, columns n0 + 4*(s%4) .. +3, and lane j gets rows R0 .. R0+3
+// of column n0 + j.
+__device__ __forceinline__ u32x4 frag_tr(const unsigned short* tile, int ld, int k0, int n0, int l16, int q4) {
+    const unsigned short* a = tile + (k0 + 8 * q4 + (l16 >> 2)) * ld + n0 + 4 * (l16 & 3);
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 4 * ld));
+    const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
+    return u32x4{ux[0], ux[1], uy[0], uy[1]};
 }
 
 // ---------------------------------------------------------------- fp32 math
@@ -129,6 +145,10 @@ struct Tile {
     static constexpr int NTHR = NW * 64;
     static constexpr int LDQ = NT + 8;                          // pitch of [*][NT] bf16 rows
     static constexpr int LDA = MT + 8;                          // pitch of [*][MT] bf16 rows
+    // pitches of row-major tiles read through transpose reads (frag_tr): 16 extra
+    // bf16 put the 4 rows of one read in 4 different 8-bank groups
+    static constexpr int KPN = NT + 16;                         // [MT][KPN] kappa (aggregate kernel)
+    static constexpr int PPN = PT + 16;                         // [MT][PPN] Psi (aggregate kernel)
     static constexpr int PTT = PT / 16;
     static constexpr int QK_IT = (MT * (NT / 16) + NTHR - 1) / NTHR;      // q/k items per thread
     static constexpr int PSI_IT = (Cp * (PT / 8) + NTHR - 1) / NTHR;      // v items per thread
@@ -163,13 +183,14 @@ struct Tile {
 // register serves many accesses (the rest goes into the instructions' offset
 // field). cos/sin and exp(segsum) are sized by the runtime C and W and come last.
 struct Lds {
-    int r1;   // bf16 [MT][LDQ] q (main) | [MT][LDA] causal block | [NT][LDA] kappa^T
+    int r1;   // bf16 main: [MT][LDQ] q | [MT][LDA] causal block | [NT][LDA] kappa^T; aggregate: [MT][NT+16] kappa
     int r2;   // bf16 [MT][LDQ] k (main only)
-    int r3;   // bf16 [PT][LDA] Psi^T
+    int r3;   // bf16 main: [PT][LDA] Psi^T; aggregate: [MT][PT+16] Psi
     int r4;   // bf16 [PT][LDQ] bf16(state)^T (main only)
     int qk;   // fp32 [Cp][RP*RP+RP] qk_dot, zero for padded ranks, RP pad words per token (main only)
-    int dz;   // bf16 [Cp][PT+8] dz of the chunk, written out at the top of the next one (main only)
-    int sc;   // fp32 [5][kTok] token scalars + chunk decay
+    int dz;   // bf16 [Cp][PT+8] dz of the chunk, written out at the top of the next one (main only;
+              // inside r2 when it fits there: k is dead from the kappa^T pass to the next chunk's phase A)
+    int sc;   // fp32 [5][Cp] token scalars (exp(da_cs), gamma, exp(da_cs_rev), factor) + chunk decay
     int tb;   // bf16 tables: q_bias [RP][NT], k_bias [RP][NT], mimo_v [RP][PT]
     int cs;   // fp32 [2][C][W + 4] cos, sin (rows padded: 8 consecutive tokens hit distinct banks)
     int se;   // fp32 [C][C + 4] exp(segsum) (main only; rows padded likewise)
@@ -181,22 +202,24 @@ __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
 __host__ __device__ constexpr Lds lds_layout(int RP, int CT, int NT, int PT, int C, int W, bool main) {
     const int Cp = 16 * CT, MT = RP * Cp < 32 ? 32 : RP * Cp;
     const int ldq = NT + 8, lda = MT + 8;
-    int r1 = NT * lda;
+    int r1 = main ? NT * lda : MT * (NT + 16);
     if (main && MT * ldq > r1) r1 = MT * ldq;
     if (main && MT * lda > r1) r1 = MT * lda;
     Lds s{};
     int off = 0;
     s.r1 = off; off += align16(r1 * 2);
     s.r2 = off; if (main) off += align16(MT * ldq * 2);
-    s.r3 = off; off += align16(PT * lda * 2);
+    s.r3 = off; off += align16((main ? PT * lda : MT * (PT + 16)) * 2);
     s.r4 = off; if (main) off += align16(PT * ldq * 2);
     s.qk = off; if (main) off += align16(Cp * (RP * RP + RP) * 4);
-    s.dz = off; if (main) off += align16(Cp * (PT + 8) * 2);
-    s.sc = off; off += align16((5 * kTok + 4) * 4);
+    s.dz = off;
+    if (main && Cp * (PT + 8) <= MT * ldq) s.dz = s.r2;
+    else if (main) off += align16(Cp * (PT + 8) * 2);
+    s.sc = off; off += align16((4 * Cp + 4) * 4);
     s.tb = off; off += align16((2 * RP * NT + RP * PT) * 2);
     s.cs = off; off += align16(2 * C * (W + 4) * 4);
     s.se = off; if (main) off += align16(C * (C + 4) * 4);
-    s.total = off + 16;   // slack: 8-wide cos/sin reads of a partial last group stay inside
+    s.total = off;
     return s;
 }
 
@@ -407,6 +430,7 @@ __device__ __forceinline__ void load_small(const Params& p, const Items<RP, CT, 
 // readfirstlane returns int: each half goes through unsigned so that it is
 // zero-extended, never sign-extended, into the 64-bit address.
 __device__ __forceinline__ unsigned rfl(unsigned x) { return static_cast<unsigned>(__builtin_amdgcn_readfirstlane(x)); }
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ const void* sgpr_ptr(const void* p) {
     const uint64_t x = reinterpret_cast<uint64_t>(p);
     const uint64_t lo = rfl(static_cast<unsigned>(x));
@@ -443,7 +467,7 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const Items<RP, 
                                                int c, int c0, int cl, unsigned char* qkst, unsigned char* smb) {
     using T = Tile<RP, CT, NT, PT>;
     using SG = Stage<RP, CT, NT, PT, MAIN, EX>;
-    const int tid = threadIdx.x, wave = tid >> 6;
+    const int tid = threadIdx.x, wave = uni(tid >> 6);
     const int R = p.R;
     if constexpr (QKON) {
         const unsigned short* qb = p.q + (long)(b * p.S + c0) * R * p.G * p.N;
@@ -542,7 +566,7 @@ __device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, 
     using T = Tile<RP, CT, NT, PT>;
     using SG = Stage<RP, CT, NT, PT, MAIN, EX>;
     constexpr bool LITE = SG::LITE;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63;
     float* sc = reinterpret_cast<float*>(smem + L.sc);
     const unsigned char* ss = smb + SG::SCAL + 4 * lane;
     if (wave == 0 && lane < T::Cp) {
@@ -559,8 +583,8 @@ __device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, 
             }
             fac = rnd(__fadd_rn(gam, beta));
         }
-        sc[kTok + lane] = gam;
-        sc[3 * kTok + lane] = fac;
+        sc[T::Cp + lane] = gam;
+        sc[3 * T::Cp + lane] = fac;
     }
     if (wave == (LITE ? 1 : 0) && lane < T::Cp) {
         float ecs = 0.f, erev = 0.f;
@@ -569,9 +593,9 @@ __device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, 
             if (MAIN) ecs = expf(LITE ? lds_ld<float>(ss + SG::CS) : sr.cs);
         }
         sc[lane] = ecs;
-        sc[2 * kTok + lane] = erev;
+        sc[2 * T::Cp + lane] = erev;
     }
-    if (tid == (LITE ? 128 : 0)) sc[4 * kTok] = expf(LITE ? lds_ld<float>(smb + SG::SCAL + SG::DLAST) : sr.dlast);
+    if (tid == (LITE ? 128 : 0)) sc[4 * T::Cp] = expf(LITE ? lds_ld<float>(smb + SG::SCAL + SG::DLAST) : sr.dlast);
     float* scs = reinterpret_cast<float*>(smem + L.cs);
     const int CW = p.C * p.W, WP = p.W + 4;
 #pragma unroll
@@ -659,10 +683,54 @@ __device__ __forceinline__ void fill_psi_regs(const Params& p, int cl, const Sma
     }
 }
 
+// Psi in row-major form, dst[r*Cp + t][p] (pitch PPN) = bf16(v[t,p] * bf16(mimo_v[r,p])),
+// zero for padded tokens and columns (and ranks, whose table rows are zero). Items
+// (token, 8 value columns) write that piece of the token's row in every rank.
+// LITE families take v from the small-input buffer (threads [t0, t0 + nth),
+// columns fastest: the 8 lanes of a write cover all banks); the others from
+// their register items.
+template <int RP, int CT, int NT, int PT, bool MAIN, bool EX>
+__device__ __forceinline__ void fill_psi_nat(const Params& p, int cl, const unsigned char* smb,
+                                             const SmallRegs<RP, CT, NT, PT, MAIN>& sr, unsigned short* dst,
+                                             const unsigned short* smv, int t0, int nth) {
+    using T = Tile<RP, CT, NT, PT>;
+    using SG = Stage<RP, CT, NT, PT, MAIN, EX>;
+    constexpr int PG = PT / 8;
+    auto item = [&](int t, int pg, u32x4 v) {
+        if (!(t < cl && 8 * pg < p.P)) v = u32x4{0u, 0u, 0u, 0u};   // absent tokens' data is stale
+        float x[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            x[2 * d] = lo16(v[d]);
+            x[2 * d + 1] = hi16(v[d]);
+        }
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            const u32x4 m = lds_ld<u32x4>(smv + r * PT + 8 * pg);
+            u32x4 o;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) o[d] = pk2(x[2 * d] * lo16(m[d]), x[2 * d + 1] * hi16(m[d]));
+            lds_st<u32x4>(dst + (r * T::Cp + t) * T::PPN + 8 * pg, o);
+        }
+    };
+    if constexpr (SG::LITE) {
+        for (int e = threadIdx.x - t0; e < T::Cp * PG; e += nth) {
+            const int pg = e % PG, t = e / PG;
+            item(t, pg, lds_ld<u32x4>(smb + SG::V + (t + T::Cp * pg) * 16));
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < T::PSI_IT; ++j) {
+            const int e = threadIdx.x + j * T::NTHR;
+            if (e < T::Cp * PG) item(e % T::Cp, e / T::Cp, sr.v[j]);
+        }
+    }
+}
+
 // Tables filled once per workgroup: bf16(q_bias), bf16(k_bias), bf16(mimo_v) of
-// head h, zero for padded ranks and columns; and the rows of Psi^T beyond every
-// rank, which no chunk writes.
-template <int RP, int CT, int NT, int PT>
+// head h, zero for padded ranks and columns; and the rows of Psi (Psi^T in the
+// chunk kernel) beyond every rank, which no chunk writes.
+template <int RP, int CT, int NT, int PT, bool NAT = false>
 __device__ __forceinline__ void fill_tables(const Params& p, int h, unsigned char* smem, const Lds& L) {
     using T = Tile<RP, CT, NT, PT>;
     const int tid = threadIdx.x;
@@ -684,7 +752,8 @@ __device__ __forceinline__ void fill_tables(const Params& p, int h, unsigned cha
     if constexpr (pad > 0) {
         for (int e = tid; e < PT * pad; e += T::NTHR) {
             const int pp = e / pad, i = used + e % pad;
-            sPsiT[pp * T::LDA + i] = 0;
+            if constexpr (NAT) sPsiT[i * T::PPN + pp] = 0;
+            else sPsiT[pp * T::LDA + i] = 0;
         }
     }
 }
@@ -779,32 +848,38 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
     using SG = Stage<RP, CT, NT, PT, false, EX>;
     extern __shared__ __align__(16) unsigned char smem[];
     const Lds L = lds_layout(RP, CT, NT, PT, p.C, p.W, false);
-    unsigned short* sKapT = reinterpret_cast<unsigned short*>(smem + L.r1);
-    const unsigned short* sPsiT = reinterpret_cast<const unsigned short*>(smem + L.r3);
+    unsigned short* sKap = reinterpret_cast<unsigned short*>(smem + L.r1);   // [MT][KPN] kappa
+    unsigned short* sPsi = reinterpret_cast<unsigned short*>(smem + L.r3);   // [MT][PPN] Psi
     const float* sc = reinterpret_cast<const float*>(smem + L.sc);
     const float* scs = reinterpret_cast<const float*>(smem + L.cs);
     const unsigned short* tbk = reinterpret_cast<const unsigned short*>(smem + L.tb) + RP * NT;
+    const unsigned short* smv = reinterpret_cast<const unsigned short*>(smem + L.tb) + 2 * RP * NT;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
     int seg, bh;
     if (!map_block(p, p.nsub, seg, bh)) return;
-    const int b = bh / p.H, h = bh - b * p.H;
-    const int g = h / (p.H / p.G);
+    // block-uniform indices, pinned to scalar registers (the divisions by run-time
+    // sizes leave them in vector registers, and every address derived from them
+    // would follow)
+    seg = uni(seg);
+    bh = uni(bh);
+    const int b = uni(bh / p.H), h = uni(bh - b * p.H);
+    const int g = uni(h / (p.H / p.G));
     const int La = p.L / p.F;   // chunks per sub-segment (all full)
     const int c_begin = seg * La;
     const int c_end = c_begin + La;
     const int R = p.R;
     // With one 8-column group per thread and rotary divisor 4, the threads of the
-    // first half hold exactly the rotated groups; the second half fills Psi^T.
+    // first half hold exactly the rotated groups; the second half fills Psi.
     constexpr bool SPLIT = SG::LITE && EX && T::QK_IT == 1 && T::MT * (NT / 32) == T::NTHR / 2;
     const int psi_t0 = SPLIT ? T::NTHR / 2 : 0, psi_n = SPLIT ? T::NTHR / 2 : T::NTHR;
 
     Items<RP, CT, NT, PT> it;
     make_items<RP, CT, NT, PT, true, false>(p, g, it);
-    fill_tables<RP, CT, NT, PT>(p, h, smem, L);
-    // kappa^T columns beyond the real rows, and rows n >= N, stay zero
-    for (int e = tid; e < NT * T::MT; e += T::NTHR) sKapT[e / T::MT * T::LDA + e % T::MT] = 0;
+    fill_tables<RP, CT, NT, PT, true>(p, h, smem, L);
+    // kappa columns n >= N stay zero (every chunk writes each row's first N)
+    for (int e = tid; e < T::MT * NT; e += T::NTHR) sKap[(e / NT) * T::KPN + e % NT] = 0;
 
     __shared__ __align__(16) unsigned char stg[SG::BYTES];
     unsigned char* qkst = stg + SG::QK;
@@ -839,46 +914,46 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
         bar();   // chunk c's staging loads of every thread have landed; previous chunk done with LDS
         phase0<RP, CT, NT, PT, false, EX>(p, it, c0, cl, smb, sr, smem, L);
         bar();
-        // kappa^T = bf16(bf16(rot(bf16(k + bf16(k_bias))) * factor) * exp(da_cs_rev)), transposed
+        // kappa = bf16(bf16(rot(bf16(k + bf16(k_bias))) * factor) * exp(da_cs_rev)), row-major;
+        // rows of absent tokens and padded ranks are written as zero
 #pragma unroll
         for (int j = 0; j < T::QK_IT; ++j) {
             const int i = it.qk_row[j];
             if (i < 0) continue;
             const int r = i / T::Cp, t = i % T::Cp;
-            if (r >= R || t >= cl) continue;   // stays zero from the initial fill / last chunk
             const int col0 = it.qk_col[j], col1 = p.N / 2 + col0;
-            float a[8], e[8];
-            bias_group(in.k0[j], tbk + r * NT + col0, a);
-            bias_group(in.k1[j], tbk + r * NT + col1, e);
-            if (col0 < p.W) {
-                rotate8<(EX ? 8 : 0)>(a, e, p.W - col0, scs + t * (p.W + 4) + col0, scs + (p.C + t) * (p.W + 4) + col0);
+            u32x4 oa = {0u, 0u, 0u, 0u}, oe = oa;
+            if (r < R && t < cl) {
+                float a[8], e[8];
+                bias_group(in.k0[j], tbk + r * NT + col0, a);
+                bias_group(in.k1[j], tbk + r * NT + col1, e);
+                if (col0 < p.W) {
+                    rotate8<(EX ? 8 : 0)>(a, e, p.W - col0, scs + t * (p.W + 4) + col0, scs + (p.C + t) * (p.W + 4) + col0);
+#pragma unroll
+                    for (int d = 0; d < 8; ++d) {
+                        a[d] = rnd(a[d]);
+                        e[d] = rnd(e[d]);
+                    }
+                }
+                const float f = sc[3 * T::Cp + t], er = sc[2 * T::Cp + t];
 #pragma unroll
                 for (int d = 0; d < 8; ++d) {
-                    a[d] = rnd(a[d]);
-                    e[d] = rnd(e[d]);
+                    a[d] = rnd(a[d] * f) * er;
+                    e[d] = rnd(e[d] * f) * er;
                 }
+                oa = pack8(a);
+                oe = pack8(e);
             }
-            const float f = sc[3 * kTok + t], er = sc[2 * kTok + t];
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                sKapT[(col0 + d) * T::LDA + i] = f2bf(rnd(a[d] * f) * er);
-                sKapT[(col1 + d) * T::LDA + i] = f2bf(rnd(e[d] * f) * er);
-            }
-        }
-        if (cl < p.C) {
-            // tail chunk: rows of tokens beyond the sequence are zero
-            for (int e = tid; e < NT * T::MT; e += T::NTHR) {
-                const int i = e % T::MT;
-                if (i % T::Cp >= cl) sKapT[e / T::MT * T::LDA + i] = 0;
-            }
+            lds_st<u32x4>(sKap + i * T::KPN + col0, oa);
+            lds_st<u32x4>(sKap + i * T::KPN + col1, oe);
         }
         if constexpr (SG::LITE) {
-            if (tid >= psi_t0) fill_psi<RP, CT, NT, PT, false, EX>(p, cl, smb, smem, L, psi_t0, psi_n);
+            if (tid >= psi_t0) fill_psi_nat<RP, CT, NT, PT, false, EX>(p, cl, smb, sr, sPsi, smv, psi_t0, psi_n);
         } else {
-            fill_psi_regs(p, cl, sr, smem, L);
+            fill_psi_nat<RP, CT, NT, PT, false, EX>(p, cl, smb, sr, sPsi, smv, 0, T::NTHR);
         }
         bar();
-        const float dl = sc[4 * kTok];
+        const float dl = sc[4 * T::Cp];
 #pragma unroll
         for (int w = 0; w < T::STW; ++w) {
             const int u = wave + w * T::NW;
@@ -886,11 +961,9 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
                 const int nt = u / T::PTT, pt = u % T::PTT;
                 f32x4 acc = U[w] * dl;
 #pragma unroll
-                for (int ks = 0; ks < T::MT / 32; ++ks) {
-                    const u32x4 a = lds_ld<u32x4>(sKapT + (16 * nt + l16) * T::LDA + 32 * ks + 8 * q4);
-                    const u32x4 bb = lds_ld<u32x4>(sPsiT + (16 * pt + l16) * T::LDA + 32 * ks + 8 * q4);
-                    acc = mfma(a, bb, acc);
-                }
+                for (int ks = 0; ks < T::MT / 32; ++ks)
+                    acc = mfma(frag_tr(sKap, T::KPN, 32 * ks, 16 * nt, l16, q4),
+                               frag_tr(sPsi, T::PPN, 32 * ks, 16 * pt, l16, q4), acc);
                 U[w] = acc;
             }
         }
@@ -952,12 +1025,15 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
     const unsigned short* tbq = reinterpret_cast<const unsigned short*>(smem + L.tb);
     const unsigned short* tbk = tbq + RP * NT;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
     int seg, bh;
     if (!map_block(p, p.nseg, seg, bh)) return;
-    const int b = bh / p.H, h = bh - b * p.H;
-    const int g = h / (p.H / p.G);
+    // block-uniform indices, pinned to scalar registers (see k_agg)
+    seg = uni(seg);
+    bh = uni(bh);
+    const int b = uni(bh / p.H), h = uni(bh - b * p.H);
+    const int g = uni(h / (p.H / p.G));
     const int c_begin = seg * p.L;
     const int c_end = min(c_begin + p.L, p.nc);
     const int R = p.R;
@@ -1145,7 +1221,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                     ke[d] = rnd(ke[d]);
                 }
             }
-            const float f = sc[3 * kTok + t];
+            const float f = sc[3 * Cp + t];
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
                 ka[d] *= f;
@@ -1340,8 +1416,8 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             const int i = 2 * ip, r = i / Cp, t = i % Cp;
             const u32x4 xa = lds_ld<u32x4>(sK + i * LDQ + nn), xb = lds_ld<u32x4>(sK + (i + 1) * LDQ + nn);
             const bool rok = r < R;
-            const float ea = (rok && t < cl) ? sc[2 * kTok + t] : 0.f;
-            const float eb = (rok && t + 1 < cl) ? sc[2 * kTok + t + 1] : 0.f;
+            const float ea = (rok && t < cl) ? sc[2 * Cp + t] : 0.f;
+            const float eb = (rok && t + 1 < cl) ? sc[2 * Cp + t + 1] : 0.f;
             unsigned short* dst = sKapT + nn * LDA + i;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
@@ -1353,7 +1429,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
 
         // ---- state update S <- S * exp(da_cs[last]) + kappa^T Psi; bf16 copy for the next chunk
         {
-            const float dl = sc[4 * kTok];
+            const float dl = sc[4 * Cp];
 #pragma unroll
             for (int w = 0; w < T::STW; ++w) {
                 const int u = wave + w * NW;
@@ -1399,7 +1475,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                     psi[r2][2] = lo16(x[1]);
                     psi[r2][3] = hi16(x[1]);
                 }
-                const f32x4 gam4 = lds_ld<f32x4>(sc + kTok + tb);
+                const f32x4 gam4 = lds_ld<f32x4>(sc + Cp + tb);
                 float dzc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
