@@ -511,21 +511,25 @@ __device__ __forceinline__ void prefetch_chunk(const Params& p, const Items<RP, 
             if (e < p.C * p.C) dma4(sb, 4u * e, smb + SG::SEG + (j * T::NTHR + wave * 64) * 4);
         }
     }
-    if (wave == 0) {
-        const long tok = (long)bh * p.S + c0;
-        unsigned char* sc = smb + SG::SCAL;
-        const unsigned o4 = 4u * tid, o2 = 2u * tid;
-        if (tid < cl) {
-            dma4(p.dt + tok, o4, sc + SG::DT0);
-            dma2(p.trap + tok, o2, sc + SG::TR0);
+    // token scalars: dt and trap from wave 0, the cumulative log decays from wave 1
+    const int lane = tid & 63;
+    const long tok = (long)bh * p.S + c0;
+    unsigned char* sc = smb + SG::SCAL;
+    const unsigned o4 = 4u * lane, o2 = 2u * lane;
+    if (wave == 0 && lane < cl) {
+        dma4(p.dt + tok, o4, sc + SG::DT0);
+        dma2(p.trap + tok, o2, sc + SG::TR0);
+        if (c0 + lane + 1 < p.S) {
+            dma4(p.dt + tok + 1, o4, sc + SG::DT1);
+            dma2(p.trap + tok + 1, o2, sc + SG::TR1);
+        }
+    }
+    if (wave == 1) {
+        if (lane < cl) {
             dma4(p.da_cs_rev + tok, o4, sc + SG::REV);
             if (MAIN) dma4(p.da_cs + tok, o4, sc + SG::CS);
-            if (c0 + tid + 1 < p.S) {
-                dma4(p.dt + tok + 1, o4, sc + SG::DT1);
-                dma2(p.trap + tok + 1, o2, sc + SG::TR1);
-            }
         }
-        if (tid == 0) dma4(p.da_cs + tok + cl - 1, 0u, sc + SG::DLAST);
+        if (lane == 0) dma4(p.da_cs + tok + cl - 1, 0u, sc + SG::DLAST);
     }
 }
 
