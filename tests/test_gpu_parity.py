@@ -213,3 +213,20 @@ def test_shape_exact_and_generic_kernels_agree(case, monkeypatch):
     compare(gen, ref, label="generic ")
     for name, a, b in zip(NAMES, _gpu_np(ex), _gpu_np(gen)):
         assert _same(a, b), f"{name}: shape-exact and generic instances differ"
+
+
+@pytest.mark.parametrize("scale,offset", [(40.0, 0.0), (1.0, 6000.0), (1.0, 100000.0)],
+                         ids=["angles_x40", "angles_plus6000", "angles_plus100000"])
+def test_large_angles(scale, offset):
+    """Angles far outside [-pi, pi]. x40 (|x| up to ~126) and +6000 exercise the
+    reduction by 2*pi ahead of the hardware sine and cosine; +100000 puts every
+    angle beyond 8192, where the library sincosf takes over. Shape-exact 64x64
+    instance."""
+    case = Case(1, 200, 2, 1, 64, 64, 4, 16, name=f"angles_x{scale:g}_plus{offset:g}")
+    log(f"[parity] {case.name}")
+    inp = make_inputs(case)
+    inp = dict(inp, angles=inp["angles"] * scale + offset)
+    ref = oracle(inp)
+    got = run_gpu(to_device(inp))
+    errs = compare(got, ref, label=f"{case.name}: ")
+    log("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
