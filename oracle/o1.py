@@ -47,6 +47,8 @@ def _load():
         i64, dp = ctypes.c_int64, ctypes.POINTER(ctypes.c_double)
         lib.o1_bwd_fwd.restype = ctypes.c_int
         lib.o1_bwd_fwd.argtypes = [i64] * 9 + [ctypes.c_int] * 4 + [dp] * 22
+        lib.o1_fwd.restype = ctypes.c_int
+        lib.o1_fwd.argtypes = [i64] * 9 + [ctypes.c_int] * 4 + [dp] * 18
         lib.o1_round_bf16.restype = None
         lib.o1_round_bf16.argtypes = [ctypes.POINTER(ctypes.c_float)] * 2 + [i64]
         _lib = lib
@@ -104,6 +106,37 @@ def run(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
     if rc != 0:
         raise ValueError("o1_bwd_fwd rejected the shape")
     return dmimo_o, states, dz, dmimo_z, qk_dot
+
+
+def run_fwd(q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, da_cs_rev,
+            dt, trap, d, segsum, chunk_size, rotary_dim_divisor=4, *, exact=False):
+    """Layer output of the same chunk walk (no dout): float64 ``o`` of shape
+    [B,S,H,P] when ``mimo_o`` is given, else [B,S,R,H,P] (see ``o1_contract.c``)."""
+    q = _dbl(q)
+    B, S, R, G, N = q.shape
+    v = _dbl(v)
+    H, P = v.shape[2], v.shape[3]
+    reduce_o = mimo_o is not None
+    arrs = [_dbl(x) for x in (q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles,
+                              da_cs, da_cs_rev, dt, trap, d, segsum)]
+    o = np.zeros((B, S, H, P)) if reduce_o else np.zeros((B, S, R, H, P))
+    rc = _load().o1_fwd(B, S, H, G, R, N, P, int(chunk_size), int(rotary_dim_divisor),
+                        int(bool(exact)), int(reduce_o), int(z is not None), int(d is not None),
+                        *[_ptr(a) for a in arrs], _ptr(o), None)
+    if rc != 0:
+        raise ValueError("o1_fwd rejected the shape")
+    return o
+
+
+def run_fwd_inputs(inp: dict, *, exact=False, exact_controls=False):
+    """``run_fwd`` on a ``synth.inputs.make_inputs`` dict (dout is not used)."""
+    cs, rev, seg = inp["da_cs"], inp["da_cs_rev"], inp["segsum"]
+    if exact_controls:
+        cs, rev, seg = inp["da_cs64"], inp["da_cs_rev64"], inp["segsum64"]
+    return run_fwd(inp["q"], inp["k"], inp["v"], inp["q_bias"], inp["k_bias"], inp["mimo_v"],
+                   inp["mimo_o"], inp["z"], inp["mimo_z"], inp["angles"], cs, rev, inp["dt"],
+                   inp["trap"], inp["d"], seg, inp["chunk_size"], inp["rotary_dim_divisor"],
+                   exact=exact)
 
 
 def run_inputs(inp: dict, *, exact=False, exact_controls=False):

@@ -27,6 +27,15 @@
  * outputs
  *   dmimo_o, dmimo_z [B,H,R,P]   states [B,H,nc,N,P]
  *   dz [B,S,H,P]                 qk_dot [B,H,S,R,R]
+ *
+ * o1_fwd runs the same chunk walk without dout and returns the layer output
+ * the backward differentiates (inferred from the gating branches of the
+ * BF16-boundary reference: dmimo_o, dz and dmimo_z are the gradients of
+ * sum(o * dout) with respect to mimo_o, z and mimo_z):
+ *   reduced (mimo_o given)  o[b,t,h,p]   = bf16( sum_r (y * bf16(mimo_o)) * silu(pz) )
+ *   not reduced             o[b,t,r,h,p] = bf16( y * silu(pz) )
+ * with silu(pz) = pz * sigmoid(pz), pz = z * mimo_z, and the silu factor left
+ * out without z. The rank sum runs in rank order in fp32.
  * Every array is double; in contract mode the caller passes values that are
  * exactly representable in the pages' dtypes (bf16 or fp32) and gets back
  * values representable in the output dtypes.
@@ -73,6 +82,8 @@ typedef struct {
     const double *dout, *q, *k, *v, *q_bias, *k_bias, *mimo_v, *mimo_o, *z, *mimo_z;
     const double *angles, *da_cs, *da_cs_rev, *dt, *trap, *d, *segsum;
     double *dmimo_o, *states, *dz, *dmimo_z, *qk_dot;
+    int fwd;     /* layer output instead of the gradients */
+    double *o;   /* [B,S,H,P] reduced, [B,S,R,H,P] otherwise */
 } o1_args;
 
 /* One (batch, head) pair: the whole sequence, chunk by chunk. */
@@ -103,8 +114,10 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
 
         /* entry state of chunk c */
         for (int64_t i = 0; i < N * P; ++i) Sb[i] = RB(St[i]);
-        double *st_out = a->states + (((b * H + h) * nc + c) * N) * P;
-        for (int64_t i = 0; i < N * P; ++i) st_out[i] = Sb[i];
+        if (a->states) {
+            double *st_out = a->states + (((b * H + h) * nc + c) * N) * P;
+            for (int64_t i = 0; i < N * P; ++i) st_out[i] = Sb[i];
+        }
 
         /* per-token preparation */
         for (int64_t t = 0; t < cl; ++t) {
@@ -128,7 +141,7 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                     for (int64_t n = 0; n < N; ++n) sum += x[n] * w[n];
                     const double v = RB(RF(sum));
                     qk[(t * R + r) * R + s2] = v;
-                    a->qk_dot[(((b * H + h) * S + T) * R + r) * R + s2] = v;
+                    if (a->qk_dot) a->qk_dot[(((b * H + h) * S + T) * R + r) * R + s2] = v;
                 }
             /* partial rotate-half: columns [0,W) pair with [M, M+W) */
             const double *th = a->angles + ((b * S + T) * H + h) * W;
@@ -223,6 +236,31 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
             }
         }
 
+        /* layer output */
+        if (a->fwd) {
+            for (int64_t t = 0; t < cl; ++t) {
+                const int64_t T = c0 + t;
+                for (int64_t p = 0; p < P; ++p) {
+                    const int64_t ivp = ((b * S + T) * H + h) * P + p;
+                    double oacc = 0.0;
+                    for (int64_t r = 0; r < R; ++r) {
+                        double val = y[(t * R + r) * P + p];
+                        if (a->reduce_o) val = RF(val * RB(a->mimo_o[(h * R + r) * P + p]));
+                        if (a->has_z) {
+                            const double pz = RF(a->z[ivp] * a->mimo_z[(h * R + r) * P + p]);
+                            val = RF(val * RF(pz * SIG(pz)));
+                        }
+                        if (a->reduce_o)
+                            oacc = RF(oacc + val);
+                        else
+                            a->o[(((b * S + T) * R + r) * H + h) * P + p] = RB(val);
+                    }
+                    if (a->reduce_o) a->o[ivp] = RB(oacc);
+                }
+            }
+            continue;
+        }
+
         /* gating branches */
         for (int64_t t = 0; t < cl; ++t) {
             const int64_t T = c0 + t;
@@ -259,7 +297,7 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
             }
         }
     }
-    for (int64_t i = 0; i < R * P; ++i) {
+    for (int64_t i = 0; i < R * P && !a->fwd; ++i) {
         if (a->reduce_o) a->dmimo_o[(b * H + h) * R * P + i] = RF(dmo[i]);
         if (a->has_z) a->dmimo_z[(b * H + h) * R * P + i] = RF(dmz[i]);
     }
@@ -282,7 +320,7 @@ int o1_bwd_fwd(int64_t B, int64_t S, int64_t H, int64_t G, int64_t R, int64_t N,
     o1_args a = {B, S, H, G, R, N, P, C, rd, reduce_o, has_z, has_d,
                  dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z,
                  angles, da_cs, da_cs_rev, dt, trap, d, segsum,
-                 dmimo_o, states, dz, dmimo_z, qk_dot};
+                 dmimo_o, states, dz, dmimo_z, qk_dot, 0, NULL};
     int64_t nbh = B * H;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < nbh; ++i) o1_head(&a, i / H, i % H);
@@ -295,4 +333,27 @@ void o1_round_bf16(const float *x, float *y, int64_t n) {
     g_exact = 0;
     for (int64_t i = 0; i < n; ++i) y[i] = (float)RB((double)x[i]);
     g_exact = save;
+}
+
+/* Layer output (see the header comment): the chunk walk of o1_bwd_fwd without
+ * dout. states may be NULL. Returns 0, or -1 for an invalid shape. */
+int o1_fwd(int64_t B, int64_t S, int64_t H, int64_t G, int64_t R, int64_t N, int64_t P,
+           int64_t C, int64_t rd, int exact, int reduce_o, int has_z, int has_d,
+           const double *q, const double *k, const double *v,
+           const double *q_bias, const double *k_bias, const double *mimo_v,
+           const double *mimo_o, const double *z, const double *mimo_z,
+           const double *angles, const double *da_cs, const double *da_cs_rev,
+           const double *dt, const double *trap, const double *d, const double *segsum,
+           double *o, double *states) {
+    if (B < 1 || S < 1 || H < 1 || G < 1 || R < 1 || N < 2 || P < 1 || C < 1) return -1;
+    if (H % G || N % 2 || (rd != 2 && rd != 4) || N % rd) return -1;
+    g_exact = exact;
+    o1_args a = {B, S, H, G, R, N, P, C, rd, reduce_o, has_z, has_d,
+                 NULL, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z,
+                 angles, da_cs, da_cs_rev, dt, trap, d, segsum,
+                 NULL, states, NULL, NULL, NULL, 1, o};
+    int64_t nbh = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nbh; ++i) o1_head(&a, i / H, i % H);
+    return 0;
 }

@@ -121,6 +121,20 @@ def run(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da, dt
     return dmimo_o, states, dz, dmimo_z, qk_dot, y
 
 
+def forward(y, mimo_o, z, mimo_z):
+    """Layer output from O2's y [B,H,S,R,P]: sum over ranks of mimo_o * y * silu(z * mimo_z)
+    as [B,S,H,P] when mimo_o is given, else the per-rank y * silu(...) as [B,S,R,H,P];
+    the silu factor is 1 without z."""
+    y = _np(y)
+    g = np.ones_like(y)
+    if z is not None:
+        pz = _np(z).transpose(0, 2, 1, 3)[:, :, :, None, :] * _np(mimo_z)[None, :, None]
+        g = pz * _sig(pz)
+    if mimo_o is not None:
+        return (y * g * _np(mimo_o)[None, :, None]).sum(axis=3).transpose(0, 2, 1, 3)
+    return (y * g).transpose(0, 2, 3, 1, 4)
+
+
 def run_inputs(inp: dict):
     """Run O2 on a ``synth.inputs.make_inputs`` dict ("configs" recipe: needs da)."""
     return run(inp["dout"], inp["q"], inp["k"], inp["v"], inp["q_bias"], inp["k_bias"],
