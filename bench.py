@@ -10,6 +10,9 @@ Several input/output buffer sets are used in turn so that the data of one
 call is not still sitting in the 256 MB Infinity Cache from the previous
 call: the figures are device-memory (HBM) figures.
 
+``--op fwd`` times the layer output ``mamba_mimo_fwd`` (the forward whose
+gradients the backward stage computes) on the same workload instead.
+
 Prints progress on stderr and ONE JSON line on stdout.
 """
 
@@ -29,6 +32,7 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 METRIC = "mimo_bwd_fwd ms/call + HBM GB/s at B1 S8192 H16 G1 N=P=64 R4 C16"
+FWD_METRIC = "mimo_fwd (layer output) ms/call + HBM GB/s at B1 S8192 H16 G1 N=P=64 R4 C16"
 PAGES_MS = 53.849475          # the pages' Ascend910_9382 median at this exact workload (context)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -40,18 +44,30 @@ ALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
 ALU_NONPACKED_TOPS = ALU_PEAK_TOPS / 2
 
 KERNEL_SOURCES = [ROOT / "mamba_mimo_chunked_amd" / "csrc" / n for n in ("mimo_kernels.hpp", "mimo_bwd_fwd.hip")]
-TRAFFIC_FILE = ROOT / "profiles" / "k_main_perf_s8192_traffic.json"
+TRAFFIC_FILES = {"bwd_fwd": ROOT / "profiles" / "k_main_perf_s8192_traffic.json",
+                 "fwd": ROOT / "profiles" / "k_main_fwd_perf_s8192_traffic.json"}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(c) -> int:
+def algorithmic_bytes(c, fwd=False) -> int:
     """Bytes the operation must move at least once: every tensor its branches
-    need, read or written once (q/k once although several heads share them)."""
+    need, read or written once (q/k once although several heads share them).
+    fwd: the layer output (no dout; o instead of states, qk_dot and gradients)."""
     B, S, H, G, R, N, P, C = c.B, c.S, c.H, c.G, c.R, c.N, c.P, c.C
     nc = (S + C - 1) // C
+    if fwd:
+        b = 2 * B * S * R * G * N * 2 + B * S * H * P * 2   # q, k, v
+        if c.has_z:
+            b += B * S * H * P * 2                          # z
+        b += B * S * H * (N // c.rd) * 4                    # angles
+        b += 3 * B * H * S * 4 + B * H * S * 2              # da_cs, da_cs_rev, dt, trap
+        b += B * H * nc * C * C * 4                         # segsum
+        b += 2 * H * R * N * 4 + (1 + c.reduce_o + c.has_z) * H * R * P * 4 + (H * 4 if c.has_d else 0)
+        b += B * S * H * P * 2 * (1 if c.reduce_o else R)  # o
+        return b
     need_y = c.reduce_o or c.has_z
     b = 2 * B * S * R * G * N * 2                       # q, k
     b += B * S * H * P * 2                              # v
@@ -73,19 +89,19 @@ def algorithmic_bytes(c) -> int:
     return b
 
 
-def algorithmic_flops(c) -> int:
+def algorithmic_flops(c, fwd=False) -> int:
     """Multiply-adds (x2) the method needs: qk_dot, the state increment, and when
     y is needed the strictly causal pairs, the inter term and the diagonal."""
     B, S, H, R, N, P, C = c.B, c.S, c.H, c.R, c.N, c.P, c.C
     nc = (S + C - 1) // C
     f = 2 * S * R * R * N + 2 * S * R * N * P
-    if c.reduce_o or c.has_z:
+    if fwd or c.reduce_o or c.has_z:
         pairs = nc * C * (C - 1) // 2
         f += pairs * R * R * 2 * (N + P) + 2 * S * R * N * P + 2 * S * R * R * P
     return B * H * f
 
 
-def algorithmic_alu_ops(c) -> int:
+def algorithmic_alu_ops(c, fwd=False) -> int:
     """Elementwise fp32 operations the bf16 contract prescribes (one per add,
     multiply, bf16 rounding, exponential, logistic or sin/cos of one element),
     excluding the contractions counted in algorithmic_flops. Per real token
@@ -96,18 +112,23 @@ def algorithmic_alu_ops(c) -> int:
       causal block scale + round   2 per strictly causal (token, rank) pair
       inter scale                  RP       y assembly and rounding        5RP
       rank-ordered diagonal        (4R + 2)RP
-      gating (sigmoid, SiLU, projections, dz chain, dmimo sums)   24RP (Z) or 2RP (no Z)."""
+      gating (sigmoid, SiLU, projections, dz chain, dmimo sums)   24RP (Z) or 2RP (no Z);
+    for the layer output (fwd) y is always needed and the gating is
+      projection, pz, sigmoid, SiLU, gate product, rank sum  6RP (Z) or 2RP (no Z), plus P
+      for the output rounding (reduced)."""
     B, S, H, R, N, P, C = c.B, c.S, c.H, c.R, c.N, c.P, c.C
     W = N // c.rd
     per_tok = 8 * R * N + 16 * R * W + 2 * W + 2 * R * P
     ops = S * per_tok
-    if c.reduce_o or c.has_z:
-        nc = (S + C - 1) // C
+    if fwd or c.reduce_o or c.has_z:
         full, tail = S // C, S - (S // C) * C
         pairs = full * C * (C - 1) // 2 + tail * (tail - 1) // 2
         ops += 2 * pairs * R * R
-        gate = 24 if c.has_z else 2
-        ops += S * (R * P + 5 * R * P + (4 * R + 2) * R * P + gate * R * P)
+        if fwd:
+            gate = (6 if c.has_z else 2) * R * P + (P if c.reduce_o else 0)
+        else:
+            gate = (24 if c.has_z else 2) * R * P
+        ops += S * (R * P + 5 * R * P + (4 * R + 2) * R * P + gate)
     return B * H * ops
 
 
@@ -158,6 +179,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--mode", choices=("op", "copy"), default="op",
                     help="copy: a plain device copy of known size, for counter calibration")
+    ap.add_argument("--op", choices=("bwd_fwd", "fwd"), default="bwd_fwd",
+                    help="fwd: time the layer output mamba_mimo_fwd instead of the backward stage")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this build has no "
@@ -166,7 +189,7 @@ def main():
 
     import torch
     from mamba_mimo_chunked_amd import _lib, mamba_mimo_bwd_fwd
-    from mamba_mimo_chunked_amd.api import _make_args
+    from mamba_mimo_chunked_amd.api import _make_args, _make_fwd_args
     from synth.inputs import API_ORDER, CONFIGS, make_inputs
 
     if not torch.cuda.is_available():
@@ -196,14 +219,19 @@ def main():
     t = time.perf_counter()
     inp = make_inputs(case)
     log(f"inputs generated in {time.perf_counter() - t:.1f}s")
-    alg_bytes = algorithmic_bytes(case)
-    alg_flops = algorithmic_flops(case)
+    fwd = a.op == "fwd"
+    alg_bytes = algorithmic_bytes(case, fwd)
+    alg_flops = algorithmic_flops(case, fwd)
     nsets = a.sets or max(2, math.ceil(512e6 / alg_bytes))
     B, S, H, G, R, N, P, C = case.B, case.S, case.H, case.G, case.R, case.N, case.P, case.C
     nc = case.nchunks
     sets = []
     for _ in range(nsets):
-        d = {n: (None if inp[n] is None else inp[n].to(dev)) for n in API_ORDER}
+        d = {n: (None if inp[n] is None or (fwd and n == "dout") else inp[n].to(dev)) for n in API_ORDER}
+        if fwd:
+            oshape = (B, S, H, P) if case.reduce_o else (B, S, R, H, P)
+            sets.append((d, torch.empty(oshape, device=dev, dtype=torch.bfloat16)))
+            continue
         out = {
             "dmimo_o": torch.empty((B, H, R, P), device=dev) if case.reduce_o else None,
             "states": torch.empty((B, H, nc, N, P), device=dev, dtype=torch.bfloat16),
@@ -212,15 +240,19 @@ def main():
             "qk_dot": torch.empty((B, H, S, R, R), device=dev, dtype=torch.bfloat16),
         }
         sets.append((d, out))
-    from mamba_mimo_chunked_amd import workspace_size
-    ws_bytes = workspace_size(B, S, H, G, R, N, P, C, case.rd, reduce_o=case.reduce_o, has_z=case.has_z)
+    from mamba_mimo_chunked_amd import fwd_workspace_size, workspace_size
+    wsf = fwd_workspace_size if fwd else workspace_size
+    ws_bytes = wsf(B, S, H, G, R, N, P, C, case.rd, reduce_o=case.reduce_o, has_z=case.has_z)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     L = _lib.lib()
-    cargs = [_make_args(B, S, H, G, R, N, P, C, case.rd, d, out, ws, ws_bytes) for d, out in sets]
+    mk = _make_fwd_args if fwd else _make_args
+    cargs = [mk(B, S, H, G, R, N, P, C, case.rd, d, out, ws, ws_bytes) for d, out in sets]
+    run_call = L.mimo_fwd if fwd else L.mimo_bwd_fwd
+    run_timed = L.mimo_fwd_timed if fwd else L.mimo_bwd_fwd_timed
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def call(i):
-        st = L.mimo_bwd_fwd(ctypes.byref(cargs[i % nsets]), ctypes.c_void_p(stream))
+        st = run_call(ctypes.byref(cargs[i % nsets]), ctypes.c_void_p(stream))
         if st != 0:
             raise RuntimeError(_lib.last_error())
 
@@ -240,7 +272,7 @@ def main():
     evs = [hip.create(_lib.TIMED_EVENTS) for _ in range(a.steps)]
     for i in range(a.steps):
         arr = (ctypes.c_void_p * _lib.TIMED_EVENTS)(*[e.value for e in evs[i]])
-        st = L.mimo_bwd_fwd_timed(ctypes.byref(cargs[i % nsets]), ctypes.c_void_p(stream), arr)
+        st = run_timed(ctypes.byref(cargs[i % nsets]), ctypes.c_void_p(stream), arr)
         if st != 0:
             raise RuntimeError(_lib.last_error())
     torch.cuda.synchronize()
@@ -253,12 +285,13 @@ def main():
     log("per-kernel ms: " + ", ".join(f"{n}={v:.4f}" for n, v in per.items()))
 
     main_ms = per["k_main"]
-    alu_ops = algorithmic_alu_ops(case)
+    alu_ops = algorithmic_alu_ops(case, fwd)
     hbm_gbps_main = alg_bytes / (main_ms * 1e-3) / 1e9
     alu_tops = alu_ops / (main_ms * 1e-3) / 1e12
     traffic = None
-    if TRAFFIC_FILE.exists():
-        rec = json.loads(TRAFFIC_FILE.read_text())
+    tfile = TRAFFIC_FILES[a.op]
+    if tfile.exists():
+        rec = json.loads(tfile.read_text())
         if rec.get("source_sha256") == source_hash() and rec.get("workload") == a.config:
             traffic = rec.get("bytes_per_launch")
     # The binding roof is the one whose ideal time is longest: elementwise ALU
@@ -284,7 +317,7 @@ def main():
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
         log(f"oracle CPU baseline on the whole workload ({threads} OpenMP threads)")
         t = time.perf_counter()
-        o1.run_inputs(inp)
+        (o1.run_fwd_inputs if fwd else o1.run_inputs)(inp)
         cpu_ms = (time.perf_counter() - t) * 1e3
         cpu = {"value": round(cpu_ms, 3), "unit": "ms/call", "cores": min(threads, B * H), "kind": "oracle",
                "sample": f"the whole {a.config} workload once (OpenMP over the {B * H} (batch, head) pairs)"}
@@ -292,7 +325,7 @@ def main():
 
     gbps = alg_bytes / (ms * 1e-3) / 1e9
     line = {
-        "metric": METRIC,
+        "metric": FWD_METRIC if fwd else METRIC,
         "value": round(ms, 5),
         "unit": "ms/call",
         "n_gpus": 1,
@@ -301,13 +334,13 @@ def main():
         "ms_per_step": round(ms, 5),
         "higher_is_better": False,
         "scaling": "weak",
-        "vs_baseline": round(ms / PAGES_MS, 6) if a.config == "perf_s8192" else None,
+        "vs_baseline": round(ms / PAGES_MS, 6) if a.config == "perf_s8192" and not fwd else None,
         "dtype": "bf16",
         "data": "synthetic",
         "hbm_gbps": round(gbps, 2),
         "hbm_frac": round(gbps / HBM_PEAK_GBS, 4),
         "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
-        "config": {"workload": a.config, "B": B, "S": S, "H": H, "G": G, "N": N, "P": P, "R": R,
+        "config": {"workload": a.config, "op": a.op, "B": B, "S": S, "H": H, "G": G, "N": N, "P": P, "R": R,
                    "chunk_size": C, "rotary_dim_divisor": case.rd, "reduce_o": case.reduce_o,
                    "has_z": case.has_z, "has_d": case.has_d, "buffer_sets": nsets,
                    "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops},

@@ -116,6 +116,49 @@ mimo_status mimo_bwd_fwd(const mimo_bwd_fwd_args *args, void *stream);
 #define MIMO_TIMED_EVENTS 5
 mimo_status mimo_bwd_fwd_timed(const mimo_bwd_fwd_args *args, void *stream, void *const *events);
 
+/*
+ * Layer output of the same chunked MIMO scan: the forward whose gradients the
+ * backward's gating branches compute (Triton-Ascend mamba_mimo_bwd_fwd pull
+ * request page, BF16-boundary PyTorch reference: dmimo_o, dz and dmimo_z are
+ * the derivatives of sum(o * dout) with respect to mimo_o, z and mimo_z; the
+ * pages give the backward only, so this is an inferred definition). With y the
+ * backward's bf16 per-rank output and silu(pz) = pz * sigmoid(pz),
+ * pz = z * mimo_z (the factor is 1 without z):
+ *   mimo_o given:  o [B,S,H,P]   bf16 = bf16( sum_r (y * bf16(mimo_o)) * silu(pz) ),
+ *                                        rank sum in rank order in fp32;
+ *   mimo_o NULL:   o [B,S,R,H,P] bf16 = bf16( y * silu(pz) ).
+ * Inputs, layouts, branch rules (except dout, which is absent), ownership,
+ * shape limits and errors as for mimo_bwd_fwd_args / mimo_bwd_fwd; the call
+ * writes o only.
+ */
+typedef struct mimo_fwd_args {
+    int64_t B, S, H, G, R, N, P;
+    int32_t chunk_size;
+    int32_t rotary_dim_divisor;
+    const uint16_t *q, *k, *v;
+    const float *q_bias, *k_bias, *mimo_v;
+    const float *mimo_o;         /* optional: selects the rank-reduced output          */
+    const uint16_t *z;           /* optional                                           */
+    const float *mimo_z;         /* required iff z != NULL                             */
+    const float *angles, *da_cs, *da_cs_rev, *dt;
+    const uint16_t *trap;
+    const float *d;              /* optional                                           */
+    const float *segsum;
+    uint16_t *o;                 /* output (device pointer), never NULL                */
+    void *workspace;             /* at least mimo_fwd_workspace_size() bytes, 256-byte aligned */
+    size_t workspace_bytes;
+} mimo_fwd_args;
+
+/* Workspace bytes a mimo_fwd call with these sizes and branches needs. */
+mimo_status mimo_fwd_workspace_size(const mimo_fwd_args *args, size_t *bytes);
+
+/* Validate and queue the layer output on `stream` (asynchronous). */
+mimo_status mimo_fwd(const mimo_fwd_args *args, void *stream);
+
+/* mimo_fwd with the same MIMO_TIMED_EVENTS events as mimo_bwd_fwd_timed (the
+ * final-reduction kernel does not run: its two events are back to back). */
+mimo_status mimo_fwd_timed(const mimo_fwd_args *args, void *stream, void *const *events);
+
 /* Message describing the last error of the calling thread ("" if none). */
 const char *mimo_last_error(void);
 

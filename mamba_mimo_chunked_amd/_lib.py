@@ -46,8 +46,31 @@ class MimoBwdFwdArgs(ctypes.Structure):
     ]
 
 
-EXPORTED = ("mimo_bwd_fwd", "mimo_bwd_fwd_timed", "mimo_bwd_fwd_workspace_size", "mimo_last_error",
-            "mimo_abi_version")
+class MimoFwdArgs(ctypes.Structure):
+    """Mirror of ``mimo_fwd_args`` (field order and types must match)."""
+
+    _fields_ = [
+        ("B", ctypes.c_int64), ("S", ctypes.c_int64), ("H", ctypes.c_int64), ("G", ctypes.c_int64),
+        ("R", ctypes.c_int64), ("N", ctypes.c_int64), ("P", ctypes.c_int64),
+        ("chunk_size", ctypes.c_int32), ("rotary_dim_divisor", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("q_bias", ctypes.c_void_p), ("k_bias", ctypes.c_void_p), ("mimo_v", ctypes.c_void_p),
+        ("mimo_o", ctypes.c_void_p),
+        ("z", ctypes.c_void_p),
+        ("mimo_z", ctypes.c_void_p),
+        ("angles", ctypes.c_void_p), ("da_cs", ctypes.c_void_p), ("da_cs_rev", ctypes.c_void_p),
+        ("dt", ctypes.c_void_p),
+        ("trap", ctypes.c_void_p),
+        ("d", ctypes.c_void_p),
+        ("segsum", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+EXPORTED = ("mimo_bwd_fwd", "mimo_bwd_fwd_timed", "mimo_bwd_fwd_workspace_size", "mimo_fwd",
+            "mimo_fwd_timed", "mimo_fwd_workspace_size", "mimo_last_error", "mimo_abi_version")
 TIMED_EVENTS = 5
 
 _lib = None
@@ -69,6 +92,13 @@ def lib():
         L.mimo_bwd_fwd_timed.restype = ctypes.c_int
         L.mimo_bwd_fwd_workspace_size.argtypes = [argp, ctypes.POINTER(ctypes.c_size_t)]
         L.mimo_bwd_fwd_workspace_size.restype = ctypes.c_int
+        fargp = ctypes.POINTER(MimoFwdArgs)
+        L.mimo_fwd.argtypes = [fargp, ctypes.c_void_p]
+        L.mimo_fwd.restype = ctypes.c_int
+        L.mimo_fwd_timed.argtypes = [fargp, ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+        L.mimo_fwd_timed.restype = ctypes.c_int
+        L.mimo_fwd_workspace_size.argtypes = [fargp, ctypes.POINTER(ctypes.c_size_t)]
+        L.mimo_fwd_workspace_size.restype = ctypes.c_int
         L.mimo_last_error.argtypes = []
         L.mimo_last_error.restype = ctypes.c_char_p
         L.mimo_abi_version.argtypes = []

@@ -1,4 +1,4 @@
-"""Public Python entry point: ``mamba_mimo_bwd_fwd``.
+"""Public Python entry points: ``mamba_mimo_bwd_fwd`` and the layer output ``mamba_mimo_fwd``.
 
 Signature, defaults, output order, validation order and error types follow
 the Triton-Ascend mamba_mimo_bwd_fwd page (public API module: the
@@ -18,7 +18,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["MambaMimoBwdFwdOutputs", "mamba_mimo_bwd_fwd", "workspace_size"]
+__all__ = ["MambaMimoBwdFwdOutputs", "mamba_mimo_bwd_fwd", "mamba_mimo_fwd", "workspace_size",
+           "fwd_workspace_size"]
 
 Tensor = torch.Tensor
 
@@ -49,7 +50,7 @@ def _check_tensor(name, tensor, shape, dtype, device):
 
 
 def _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
-                     da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor):
+                     da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, *, fwd=False):
     if q.dim() != 5:
         raise ValueError("q must have shape [B, S, R, G, N]")
     batch, seqlen, rank, groups, state_dim = q.shape
@@ -96,9 +97,11 @@ def _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, a
         _check_tensor("d", d, (heads,), torch.float32, device)
     if mimo_o is not None:
         _check_tensor("mimo_o", mimo_o, (heads, rank, value_dim), torch.float32, device)
-        _check_tensor("dout", dout, (batch, seqlen, heads, value_dim), torch.bfloat16, device)
-    else:
-        _check_tensor("dout", dout, (batch, seqlen, rank, heads, value_dim), torch.bfloat16, device)
+    if not fwd:
+        if mimo_o is not None:
+            _check_tensor("dout", dout, (batch, seqlen, heads, value_dim), torch.bfloat16, device)
+        else:
+            _check_tensor("dout", dout, (batch, seqlen, rank, heads, value_dim), torch.bfloat16, device)
     if z is None:
         if mimo_z is not None:
             raise ValueError("mimo_z must be None when z is None")
@@ -206,3 +209,79 @@ def mamba_mimo_bwd_fwd(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z,
     if st != _lib.MIMO_OK:
         _raise(st)
     return MambaMimoBwdFwdOutputs(out["dmimo_o"], out["states"], out["dz"], out["dmimo_z"], out["qk_dot"])
+
+
+_FWD_INPUTS = ("q", "k", "v", "q_bias", "k_bias", "mimo_v", "mimo_o", "z", "mimo_z", "angles", "da_cs",
+               "da_cs_rev", "dt", "trap", "d", "segsum")
+
+
+def _make_fwd_args(B, S, H, G, R, N, P, C, rd, t: dict, o, workspace=None, ws_bytes=0):
+    a = _lib.MimoFwdArgs()
+    a.B, a.S, a.H, a.G, a.R, a.N, a.P = B, S, H, G, R, N, P
+    a.chunk_size, a.rotary_dim_divisor = C, rd
+    for name in _FWD_INPUTS:
+        x = t.get(name)
+        setattr(a, name, None if x is None else x.data_ptr())
+    a.o = None if o is None else o.data_ptr()
+    a.workspace = None if workspace is None else workspace.data_ptr()
+    a.workspace_bytes = ws_bytes
+    return a
+
+
+def fwd_workspace_size(B, S, H, G, R, N, P, chunk_size, rotary_dim_divisor=4, *, reduce_o=True,
+                       has_z=True) -> int:
+    """Workspace bytes ``mamba_mimo_fwd`` needs for these sizes and branches."""
+    a = _lib.MimoFwdArgs()
+    a.B, a.S, a.H, a.G, a.R, a.N, a.P = B, S, H, G, R, N, P
+    a.chunk_size, a.rotary_dim_divisor = chunk_size, rotary_dim_divisor
+    a.mimo_o = 1 if reduce_o else None
+    a.z = a.mimo_z = 1 if has_z else None
+    n = ctypes.c_size_t(0)
+    st = _lib.lib().mimo_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if st != _lib.MIMO_OK:
+        _raise(st)
+    return int(n.value)
+
+
+def mamba_mimo_fwd(q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, da_cs_rev, dt,
+                   trap, d, segsum, chunk_size: int = 16, rotary_dim_divisor: int = 4, *,
+                   out: Optional[Tensor] = None, workspace: Optional[Tensor] = None) -> Tensor:
+    """Layer output of the chunked MIMO scan whose gradients ``mamba_mimo_bwd_fwd``
+    computes: ``o`` [B,S,H,P] bf16 = sum over ranks of (y * bf16(mimo_o)) * silu(z * mimo_z)
+    when ``mimo_o`` is given, else the per-rank ``y * silu(z * mimo_z)`` as [B,S,R,H,P]
+    (the gate is left out without ``z``). Same inputs as the backward stage minus dout;
+    asynchronous on the current HIP stream.
+    """
+    _validate_inputs(None, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
+                     da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, fwd=True)
+    L = _lib.lib()
+    B, S, R, G, N = q.shape
+    H, P = v.shape[2:]
+    C = int(chunk_size)
+    dev = q.device
+    vals = (q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, da_cs_rev, dt, trap, d,
+            segsum)
+    t = {name: (None if x is None else x.contiguous()) for name, x in zip(_FWD_INPUTS, vals)}
+    shape = (B, S, H, P) if mimo_o is not None else (B, S, R, H, P)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    else:
+        _check_tensor("out", out, shape, torch.bfloat16, dev)
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+    args = _make_fwd_args(B, S, H, G, R, N, P, C, int(rotary_dim_divisor), t, out)
+    need = ctypes.c_size_t(0)
+    st = L.mimo_fwd_workspace_size(ctypes.byref(args), ctypes.byref(need))
+    if st != _lib.MIMO_OK:
+        _raise(st)
+    if need.value > 0:
+        if workspace is None or workspace.numel() < need.value:
+            workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.mimo_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != _lib.MIMO_OK:
+        _raise(st)
+    return out

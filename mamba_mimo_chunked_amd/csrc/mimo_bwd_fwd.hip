@@ -171,7 +171,8 @@ const Family* family(int RP, int CT) {
     }
 }
 
-mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
+// fwd: the layer output (mimo_fwd), which needs no partial dmimo sums.
+mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl, bool fwd = false) {
     if (a == nullptr) return fail(MIMO_ERR_VALUE, "args must not be NULL");
     const int64_t B = a->B, S = a->S, H = a->H, G = a->G, R = a->R, N = a->N, P = a->P;
     const int64_t C = a->chunk_size, rd = a->rotary_dim_divisor;
@@ -232,9 +233,9 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl) {
     pl->off_decay = off;
     if (pl->nseg > 1) off = align256(off + (size_t)B * H * pl->nsub * 4);
     pl->off_po = off;
-    if (pl->nseg > 1 && reduce_o) off = align256(off + (size_t)B * H * pl->nseg * R * P * 4);
+    if (pl->nseg > 1 && reduce_o && !fwd) off = align256(off + (size_t)B * H * pl->nseg * R * P * 4);
     pl->off_pz = off;
-    if (pl->nseg > 1 && has_z) off = align256(off + (size_t)B * H * pl->nseg * R * P * 4);
+    if (pl->nseg > 1 && has_z && !fwd) off = align256(off + (size_t)B * H * pl->nseg * R * P * 4);
     pl->ws_bytes = off;
     Lds lm = lds_layout(RP, CT, pl->NT, pl->PT, (int)C, pl->W, true);
     Lds la = lds_layout(RP, CT, pl->NT, pl->PT, (int)C, pl->W, false);
@@ -289,6 +290,23 @@ mimo_status launch(kfn f, dim3 grid, dim3 block, int lds, hipStream_t st, Params
     return MIMO_OK;
 }
 
+// The forward's arguments as those of the backward first stage (no dout, no
+// backward outputs): both run the same plan and kernels.
+mimo_bwd_fwd_args as_bwd_args(const mimo_fwd_args* f) {
+    mimo_bwd_fwd_args a;
+    memset(&a, 0, sizeof(a));
+    a.B = f->B; a.S = f->S; a.H = f->H; a.G = f->G; a.R = f->R; a.N = f->N; a.P = f->P;
+    a.chunk_size = f->chunk_size;
+    a.rotary_dim_divisor = f->rotary_dim_divisor;
+    a.q = f->q; a.k = f->k; a.v = f->v;
+    a.q_bias = f->q_bias; a.k_bias = f->k_bias; a.mimo_v = f->mimo_v; a.mimo_o = f->mimo_o;
+    a.z = f->z; a.mimo_z = f->mimo_z; a.angles = f->angles; a.da_cs = f->da_cs;
+    a.da_cs_rev = f->da_cs_rev; a.dt = f->dt; a.trap = f->trap; a.d = f->d; a.segsum = f->segsum;
+    a.workspace = f->workspace;
+    a.workspace_bytes = f->workspace_bytes;
+    return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -306,21 +324,26 @@ mimo_status mimo_bwd_fwd_workspace_size(const mimo_bwd_fwd_args* args, size_t* b
     return MIMO_OK;
 }
 
-static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* events) {
+// The backward first stage (out == nullptr) or the layer output o (out != nullptr,
+// `a` built by as_bwd_args).
+static mimo_status run(const mimo_bwd_fwd_args* a, uint16_t* out, void* stream, void* const* events) {
     g_err.clear();
+    const bool fwd = out != nullptr;
     Plan pl;
-    mimo_status s = make_plan(a, &pl);
+    mimo_status s = make_plan(a, &pl, fwd);
     if (s != MIMO_OK) return s;
     const bool reduce_o = a->mimo_o != nullptr, has_z = a->z != nullptr;
-    if (!a->dout && (reduce_o || has_z)) return fail(MIMO_ERR_VALUE, "dout must not be NULL");
+    if (!fwd && !a->dout && (reduce_o || has_z)) return fail(MIMO_ERR_VALUE, "dout must not be NULL");
     if (!a->q || !a->k || !a->v || !a->q_bias || !a->k_bias || !a->mimo_v || !a->angles || !a->da_cs ||
         !a->da_cs_rev || !a->dt || !a->trap || !a->segsum)
         return fail(MIMO_ERR_VALUE, "a required input pointer is NULL");
-    if (!a->states || !a->qk_dot) return fail(MIMO_ERR_VALUE, "states and qk_dot must not be NULL");
-    if ((a->dmimo_o != nullptr) != reduce_o)
-        return fail(MIMO_ERR_VALUE, "dmimo_o must be given exactly when mimo_o is given");
-    if ((a->dz != nullptr) != has_z || (a->dmimo_z != nullptr) != has_z)
-        return fail(MIMO_ERR_VALUE, "dz and dmimo_z must be given exactly when z is given");
+    if (!fwd) {
+        if (!a->states || !a->qk_dot) return fail(MIMO_ERR_VALUE, "states and qk_dot must not be NULL");
+        if ((a->dmimo_o != nullptr) != reduce_o)
+            return fail(MIMO_ERR_VALUE, "dmimo_o must be given exactly when mimo_o is given");
+        if ((a->dz != nullptr) != has_z || (a->dmimo_z != nullptr) != has_z)
+            return fail(MIMO_ERR_VALUE, "dz and dmimo_z must be given exactly when z is given");
+    }
     if (a->workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && a->workspace == nullptr))
         return fail(MIMO_ERR_VALUE, "workspace too small: need %zu bytes, got %zu", pl.ws_bytes, a->workspace_bytes);
     if (pl.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(a->workspace) & 255))
@@ -333,7 +356,8 @@ static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* ev
     p.R = (int)a->R; p.N = (int)a->N; p.P = (int)a->P; p.C = a->chunk_size;
     p.W = pl.W; p.nc = pl.nc; p.L = pl.L; p.nseg = pl.nseg; p.rd = a->rotary_dim_divisor;
     p.F = pl.F; p.nsub = pl.nsub;
-    p.reduce_o = reduce_o; p.has_z = has_z; p.has_d = a->d != nullptr; p.need_y = reduce_o || has_z;
+    p.reduce_o = reduce_o; p.has_z = has_z; p.has_d = a->d != nullptr; p.need_y = fwd || reduce_o || has_z;
+    p.fwd = fwd; p.o = out;
     p.dout = a->dout; p.q = a->q; p.k = a->k; p.v = a->v; p.z = a->z; p.trap = a->trap;
     p.q_bias = a->q_bias; p.k_bias = a->k_bias; p.mimo_v = a->mimo_v; p.mimo_o = a->mimo_o;
     p.mimo_z = a->mimo_z; p.angles = a->angles; p.da_cs = a->da_cs; p.da_cs_rev = a->da_cs_rev;
@@ -342,7 +366,9 @@ static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* ev
     unsigned char* ws = static_cast<unsigned char*>(a->workspace);
     p.agg = pl.nseg > 1 ? reinterpret_cast<float*>(ws + pl.off_agg) : nullptr;
     p.decay = pl.nseg > 1 ? reinterpret_cast<float*>(ws + pl.off_decay) : nullptr;
-    if (pl.nseg > 1) {
+    if (fwd) {
+        p.part_o = p.part_z = nullptr;
+    } else if (pl.nseg > 1) {
         p.part_o = reduce_o ? reinterpret_cast<float*>(ws + pl.off_po) : nullptr;
         p.part_z = has_z ? reinterpret_cast<float*>(ws + pl.off_pz) : nullptr;
     } else {
@@ -356,8 +382,12 @@ static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* ev
     const int ti = tidx(pl.NT) * 3 + tidx(pl.PT);
     const bool ex = pl.ex;
     kfn kmain = fam->main[ti];
-    if (ex && !p.need_y) kmain = fam->main_ex_noy[ti];
-    if (ex && p.reduce_o && p.has_z) kmain = fam->main_ex_rz[ti];
+    if (fwd) {
+        if (ex && p.reduce_o && p.has_z) kmain = fam->main_ex_fwd[ti];
+    } else {
+        if (ex && !p.need_y) kmain = fam->main_ex_noy[ti];
+        if (ex && p.reduce_o && p.has_z) kmain = fam->main_ex_rz[ti];
+    }
     const kfn kagg = ex ? fam->agg_ex[ti] : fam->agg[ti];
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int BH = p.B * p.H;
@@ -384,7 +414,7 @@ static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* ev
     if ((s = mark(2)) != MIMO_OK) return s;
     if ((s = launch(kmain, dim3(grid_blocks(p, pl.nseg)), dim3(pl.NW * 64), pl.lds_main, st, p)) != MIMO_OK) return s;
     if ((s = mark(3)) != MIMO_OK) return s;
-    if (pl.nseg > 1 && p.need_y) {
+    if (pl.nseg > 1 && p.need_y && !fwd) {
         const long tot = (long)BH * p.R * p.P;
         if ((s = launch(k_finish, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, p)) != MIMO_OK) return s;
     }
@@ -394,11 +424,37 @@ static mimo_status run(const mimo_bwd_fwd_args* a, void* stream, void* const* ev
     return MIMO_OK;
 }
 
-mimo_status mimo_bwd_fwd(const mimo_bwd_fwd_args* a, void* stream) { return run(a, stream, nullptr); }
+mimo_status mimo_bwd_fwd(const mimo_bwd_fwd_args* a, void* stream) { return run(a, nullptr, stream, nullptr); }
 
 mimo_status mimo_bwd_fwd_timed(const mimo_bwd_fwd_args* a, void* stream, void* const* events) {
     if (events == nullptr) return fail(MIMO_ERR_VALUE, "events must not be NULL");
-    return run(a, stream, events);
+    return run(a, nullptr, stream, events);
+}
+
+mimo_status mimo_fwd_workspace_size(const mimo_fwd_args* args, size_t* bytes) {
+    if (args == nullptr) return fail(MIMO_ERR_VALUE, "args must not be NULL");
+    const mimo_bwd_fwd_args a = as_bwd_args(args);
+    Plan pl;
+    const mimo_status s = make_plan(&a, &pl, true);
+    if (s != MIMO_OK) return s;
+    if (bytes == nullptr) return fail(MIMO_ERR_VALUE, "bytes must not be NULL");
+    *bytes = pl.ws_bytes;
+    return MIMO_OK;
+}
+
+static mimo_status run_fwd(const mimo_fwd_args* f, void* stream, void* const* events) {
+    g_err.clear();
+    if (f == nullptr) return fail(MIMO_ERR_VALUE, "args must not be NULL");
+    if (f->o == nullptr) return fail(MIMO_ERR_VALUE, "o must not be NULL");
+    const mimo_bwd_fwd_args a = as_bwd_args(f);
+    return run(&a, f->o, stream, events);
+}
+
+mimo_status mimo_fwd(const mimo_fwd_args* a, void* stream) { return run_fwd(a, stream, nullptr); }
+
+mimo_status mimo_fwd_timed(const mimo_fwd_args* a, void* stream, void* const* events) {
+    if (events == nullptr) return fail(MIMO_ERR_VALUE, "events must not be NULL");
+    return run_fwd(a, stream, events);
 }
 
 }  // extern "C"

@@ -24,6 +24,12 @@
 
 namespace mimo {
 
+// fp32 multiply and add, each rounded on its own. The HIP headers' __fmul_rn and
+// __fadd_rn are plain operators compiled above this pragma, so a product of one
+// feeding a sum of the other may still be fused; these may not.
+__device__ __forceinline__ float fmul(float x, float y) { return x * y; }
+__device__ __forceinline__ float fadd(float x, float y) { return x + y; }
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -108,10 +114,12 @@ struct Params {
     int B, S, H, G, R, N, P, C, W, nc, L, nseg, rd;
     int F, nsub;    // the aggregate splits each segment but the last into F sub-segments of L/F chunks
     int reduce_o, has_z, has_d, need_y;
+    int fwd;        // layer output o instead of the backward's outputs (no dout, states, qk_dot)
     const unsigned short *dout, *q, *k, *v, *z, *trap;
     const float *q_bias, *k_bias, *mimo_v, *mimo_o, *mimo_z, *angles, *da_cs, *da_cs_rev, *dt, *d, *segsum;
     float *dmimo_o, *dmimo_z;
     unsigned short *states, *dz, *qk_dot;
+    unsigned short* o;   // layer output: [B,S,H,P] when reduce_o, else [B,S,R,H,P]
     float* agg;     // [B*H][nsub][N*P]: sub-segment state increments, then the states after each
     float* decay;   // [B*H][nsub]: product of the chunk decays of each sub-segment
     float* part_o;  // [B*H][nseg][R*P] partial dmimo_o (== dmimo_o when nseg == 1)
@@ -564,14 +572,14 @@ __device__ __forceinline__ void phase0(const Params& p, const Items<RP, CT, NT, 
         if (lane < cl) {
             const float dt0 = LITE ? lds_ld<float>(ss + SG::DT0) : sr.dt0;
             const float tr0 = LITE ? bf2f(lds_ld<unsigned short>(ss + SG::TR0)) : sr.tr0;
-            gam = __fmul_rn(rnd(dt0), sigmoid_fast(tr0));
+            gam = fmul(rnd(dt0), sigmoid_fast(tr0));
             float beta = 0.f;
             if (c0 + lane + 1 < p.S) {
                 const float dt1 = LITE ? lds_ld<float>(ss + SG::DT1) : sr.dt1;
                 const float tr1 = LITE ? bf2f(lds_ld<unsigned short>(ss + SG::TR1)) : sr.tr1;
-                beta = rnd(__fmul_rn(rnd(dt1), sigmoid_fast(-tr1)));
+                beta = rnd(fmul(rnd(dt1), sigmoid_fast(-tr1)));
             }
-            fac = rnd(__fadd_rn(gam, beta));
+            fac = rnd(fadd(gam, beta));
         }
         sc[T::Cp + lane] = gam;
         sc[3 * T::Cp + lane] = fac;
@@ -773,8 +781,8 @@ __device__ __forceinline__ void rotate8(float a[8], float e[8], int lim, const f
     for (int d = 0; d < 8; ++d) {
         if (LIM >= 8 || d < lim) {
             const float x = a[d], y = e[d];
-            a[d] = __fmul_rn(c[d], x) - __fmul_rn(s[d], y);
-            e[d] = __fmul_rn(s[d], x) + __fmul_rn(c[d], y);
+            a[d] = fmul(c[d], x) - fmul(s[d], y);
+            e[d] = fmul(s[d], x) + fmul(c[d], y);
         }
     }
 }
@@ -803,7 +811,8 @@ __device__ __forceinline__ bool map_block(const Params& p, int nseg_k, int& seg,
 // EX: the call's shape equals the tile (R = RP, N = NT, P = PT, C = Cp) with rotary
 // divisor 4, so sizes, pitches and bounds fold to constants. MODE: -1 reads the
 // branch flags at run time; 0 = no y (neither reduced dout nor z); 1 = reduced
-// dout with z. Returns the parameters with those fields replaced by constants.
+// dout with z; 2 = the layer output, reduced with z. Returns the parameters with
+// those fields replaced by constants.
 template <int RP, int CT, int NT, int PT, bool EX, int MODE>
 __device__ __forceinline__ Params specialise(const Params& pin) {
     Params p = pin;
@@ -819,11 +828,13 @@ __device__ __forceinline__ Params specialise(const Params& pin) {
         p.need_y = 0;
         p.reduce_o = 0;
         p.has_z = 0;
+        p.fwd = 0;
     }
-    if constexpr (MODE == 1) {
+    if constexpr (MODE == 1 || MODE == 2) {
         p.need_y = 1;
         p.reduce_o = 1;
         p.has_z = 1;
+        p.fwd = MODE == 2;
     }
     return p;
 }
@@ -979,10 +990,13 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
 // ---------------------------------------------------------------- main chunk pass
 // dz rows of one chunk (first token c0, cl tokens) from LDS ([t][PT + 8] bf16) to
 // global, 16 bytes a thread.
+// Rows of a [B,S,H,P] bf16 output (dz, or the reduced layer output) staged in LDS
+// by the epilogue, written out 16 bytes a thread.
 template <int NTHR, int PT>
-__device__ __forceinline__ void flush_dz(const Params& p, const unsigned short* sDz, int b, int h, int c0, int cl) {
+__device__ __forceinline__ void flush_dz(const Params& p, unsigned short* out, const unsigned short* sDz, int b, int h,
+                                         int c0, int cl) {
     const int P8 = p.P / 8;
-    unsigned short* dst = p.dz + ((long)(b * p.S + c0) * p.H + h) * p.P;
+    unsigned short* dst = out + ((long)(b * p.S + c0) * p.H + h) * p.P;
     for (int e = threadIdx.x; e < cl * P8; e += NTHR) {
         const int t = e / P8, pc = (e - t * P8) * 8;
         *reinterpret_cast<u32x4*>(dst + (long)t * p.H * p.P + pc) = lds_ld<u32x4>(sDz + t * (PT + 8) + pc);
@@ -1028,6 +1042,9 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
     const int c_end = min(c_begin + p.L, p.nc);
     const int R = p.R;
     const bool need_y = p.need_y;
+    // the epilogue stages one [C,P] bf16 output per chunk in LDS: dz, or the reduced layer output
+    const bool stage_out = p.fwd ? p.reduce_o : p.has_z;
+    unsigned short* const out16 = p.fwd ? p.o : p.dz;
     // which threads fill Psi^T (LITE families): the second half under the rotation split, else all
     const int psi_t0 = PSPLIT ? NTHR / 2 : 0, psi_n = PSPLIT ? NTHR / 2 : NTHR;
     const bool rot_half = !RSPLIT || tid < NTHR / 2;   // threads whose q/k groups may be rotated
@@ -1138,8 +1155,8 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         {
             const long base = ((long)(b * p.S + c0)) * p.H * p.P + (long)h * p.P;
             const unsigned bytes = 2u * (unsigned)((cl - 1) * p.H * p.P + p.P);
-            const auto zb = buffer((p.has_z ? p.z : (need_y ? p.dout : p.v)) + base, bytes);
-            const auto db = p.reduce_o ? buffer(p.dout + base, bytes) : zb;
+            const auto zb = buffer((p.has_z ? p.z : (need_y && !p.fwd ? p.dout : p.v)) + base, bytes);
+            const auto db = (p.reduce_o && !p.fwd) ? buffer(p.dout + base, bytes) : zb;
 #pragma unroll
             for (int ps = 0; ps < T::PW; ++ps) {
 #pragma unroll
@@ -1152,7 +1169,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         bar();   // chunk c's staging loads of every thread have landed; previous chunk (and the tables) done
 
         // ---- states[c] = bf16(S entering chunk c), from sSbT ([p][n]) to [n][p], 16 bytes a thread
-        {
+        if (!p.fwd) {
             unsigned short* dst = p.states + ((long)bh * p.nc + c) * p.N * p.P;
             const int P8 = p.P / 8;
             for (int e = tid; e < p.N * P8; e += NTHR) {
@@ -1166,7 +1183,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             }
         }
         // ---- dz of the previous chunk (always a full one), staged in LDS by its epilogue
-        if (p.has_z && c > c_begin) flush_dz<NTHR, PT>(p, sDz, b, h, c0 - p.C, p.C);
+        if (stage_out && c > c_begin) flush_dz<NTHR, PT>(p, out16, sDz, b, h, c0 - p.C, p.C);
 
         // ---- phase 0: token scalars, cos/sin, exp(segsum)
         phase0<RP, CT, NT, PT, true, EX>(p, it, c0, cl, smb, sr, smem, L);
@@ -1277,7 +1294,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             lds_st<u32x4>(sK + i * LDQ + col0, rk0[j]);
             lds_st<u32x4>(sK + i * LDQ + col1, rk1[j]);
         }
-        {
+        if (!p.fwd) {
             const int RR = R * R;
             unsigned short* qko = p.qk_dot + ((long)bh * p.S + c0) * RR;
             if constexpr (EX && (RP * RP) % 8 == 0) {
@@ -1466,7 +1483,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                     psi[r2][3] = hi16(x[1]);
                 }
                 const f32x4 gam4 = lds_ld<f32x4>(sc + Cp + tb);
-                float dzc[4] = {0.f, 0.f, 0.f, 0.f};
+                float dzc[4] = {0.f, 0.f, 0.f, 0.f};   // dz chain, or the layer output's rank sum
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
                     // diagonal: rank-ordered chain of bf16 products and bf16 sums, times gamma
@@ -1478,16 +1495,34 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
 #pragma unroll
                         for (int r2 = 1; r2 < RP; ++r2) dg = rnd(dg + rnd(qk[r2] * psi[r2][v]));
                         dg = rnd(dg * gam4[v]);
-                        y[v] = rnd(__fmaf_rn(dval, psi[r][v], __fadd_rn(acc[ps][r][v], dg)));
+                        y[v] = rnd(__fmaf_rn(dval, psi[r][v], fadd(acc[ps][r][v], dg)));
                     }
-                    if (p.has_z) {
+                    if (p.fwd) {
+                        // layer output: (y * bf16(mimo_o)) * silu(pz), summed over ranks in
+                        // rank order (reduced) or stored per rank
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            float val = y[v];
+                            if (p.reduce_o) val = fmul(val, co[ps][r]);
+                            if (p.has_z) {
+                                const float pz = zr[v] * cz[ps][r];
+                                val = fmul(val, fmul(pz, sigmoid_fast(pz)));
+                            }
+                            if (p.reduce_o) {
+                                dzc[v] = fadd(dzc[v], val);
+                            } else if (tb + v < cl && pc < p.P && r < R) {
+                                const long oi = ((long)(b * p.S + c0 + tb + v) * R + r) * p.H * p.P + (long)h * p.P + pc;
+                                p.o[oi] = bits16(rnd(val));
+                            }
+                        }
+                    } else if (p.has_z) {
 #pragma unroll
                         for (int v = 0; v < 4; ++v) {
                             const float pz = zr[v] * cz[ps][r];
                             const float sg = sigmoid_fast(pz);
                             float G;
                             if (p.reduce_o) {
-                                dmo[ps][r] = __fmaf_rn(__fmul_rn(y[v], __fmul_rn(pz, sg)), dr[v], dmo[ps][r]);
+                                dmo[ps][r] = __fmaf_rn(fmul(y[v], fmul(pz, sg)), dr[v], dmo[ps][r]);
                                 G = rnd(rnd(dr[v] * co[ps][r]) * y[v]);
                             } else {
                                 // per-rank dout [B,S,R,H,P]; lanes without a token read element 0
@@ -1496,8 +1531,8 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                                 const unsigned short raw = p.dout[okr ? nb + (long)(tb + v) * R * p.H * p.P + pc : 0];
                                 G = rnd((okr ? bf2f(raw) : 0.f) * y[v]);
                             }
-                            const float gz = __fmul_rn(__fmul_rn(G, sg), __fmaf_rn(pz, 1.0f - sg, 1.0f));
-                            dzc[v] = rnd(dzc[v] + __fmul_rn(gz, cz[ps][r]));
+                            const float gz = fmul(fmul(G, sg), __fmaf_rn(pz, 1.0f - sg, 1.0f));
+                            dzc[v] = rnd(dzc[v] + fmul(gz, cz[ps][r]));
                             dmz[ps][r] = __fmaf_rn(gz, zr[v], dmz[ps][r]);
                         }
                     } else if (p.reduce_o) {
@@ -1505,9 +1540,9 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                         for (int v = 0; v < 4; ++v) dmo[ps][r] = __fmaf_rn(y[v], dr[v], dmo[ps][r]);
                     }
                 }
-                if (p.has_z) {
+                if (stage_out) {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) sDz[(tb + v) * (PT + 8) + pc] = bits16(dzc[v]);
+                    for (int v = 0; v < 4; ++v) sDz[(tb + v) * (PT + 8) + pc] = bits16(p.fwd ? rnd(dzc[v]) : dzc[v]);
                 }
             }
         }
@@ -1520,15 +1555,15 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
 #pragma unroll
             for (int v = 0; v < 4; ++v) asm volatile("" ::"v"(zraw[ps][v]), "v"(draw[ps][v]));
     }
-    if (p.has_z) {
-        // dz of the segment's last chunk
+    if (stage_out) {
+        // dz (or the layer output) of the segment's last chunk
         bar();
         const int cl_last = min(p.C, p.S - (c_end - 1) * p.C);
-        flush_dz<NTHR, PT>(p, sDz, b, h, (c_end - 1) * p.C, cl_last);
+        flush_dz<NTHR, PT>(p, out16, sDz, b, h, (c_end - 1) * p.C, cl_last);
     }
 
     // ---- per-segment partial sums of dmimo_o / dmimo_z: reduce over the 4 lane groups
-    if (need_y) {
+    if (need_y && !p.fwd) {
 #pragma unroll
         for (int ps = 0; ps < T::PW; ++ps) {
 #pragma unroll
@@ -1599,7 +1634,7 @@ typedef void (*kfn)(Params);
 // with idx(32, 64, 128) = 0, 1, 2: the generic instances and the shape-exact ones.
 struct Family {
     kfn agg[9], agg_ex[9];
-    kfn main[9], main_ex_noy[9], main_ex_rz[9];
+    kfn main[9], main_ex_noy[9], main_ex_rz[9], main_ex_fwd[9];
 };
 
 #define MIMO_NP_LIST(F, RP, CT)                                                                             \
@@ -1610,11 +1645,12 @@ struct Family {
 #define MIMO_MAIN_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT, false, -1>
 #define MIMO_MAIN_EX0_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT, true, 0>
 #define MIMO_MAIN_EX1_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT, true, 1>
+#define MIMO_MAIN_EX2_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT, true, 2>
 #define MIMO_FAMILY(RP, CT)                                                                               \
     const Family* family_rp##RP##_ct##CT() {                                                              \
         static const Family f = {{MIMO_NP_LIST(MIMO_AGG_FN, RP, CT)},     {MIMO_NP_LIST(MIMO_AGG_EX_FN, RP, CT)}, \
                                  {MIMO_NP_LIST(MIMO_MAIN_FN, RP, CT)},    {MIMO_NP_LIST(MIMO_MAIN_EX0_FN, RP, CT)}, \
-                                 {MIMO_NP_LIST(MIMO_MAIN_EX1_FN, RP, CT)}};                               \
+                                 {MIMO_NP_LIST(MIMO_MAIN_EX1_FN, RP, CT)}, {MIMO_NP_LIST(MIMO_MAIN_EX2_FN, RP, CT)}}; \
         return &f;                                                                                        \
     }
 #define MIMO_DECL_FAMILY(RP, CT) const Family* family_rp##RP##_ct##CT();
