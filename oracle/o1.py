@@ -78,11 +78,27 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return y
 
 
+def _mode(exact, fp32):
+    if exact and fp32:
+        raise ValueError("exact and fp32 are exclusive")
+    return 1 if exact else (2 if fp32 else 0)
+
+
+def _width(angles, N, rotary_dim_divisor):
+    """Rotated column pairs: the angles' last axis (N / rotary_dim_divisor when given)."""
+    W = int(angles.shape[-1])
+    if rotary_dim_divisor is not None and W != N // rotary_dim_divisor:
+        raise ValueError(f"angles width {W} != N / rotary_dim_divisor")
+    return W
+
+
 def run(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, da_cs_rev,
-        dt, trap, d, segsum, chunk_size, rotary_dim_divisor=4, *, exact=False):
+        dt, trap, d, segsum, chunk_size, rotary_dim_divisor=4, *, exact=False, fp32=False):
     """Run O1. Inputs are tensors or arrays in the operator's shapes (any dtype;
     converted to float64 exactly). Returns float64 numpy arrays
-    (dmimo_o, states, dz, dmimo_z, qk_dot); inactive outputs are None."""
+    (dmimo_o, states, dz, dmimo_z, qk_dot); inactive outputs are None.
+    ``exact``: no rounding at all; ``fp32``: fp32 intermediates (the pages' FP32
+    reference), outputs rounded to their dtypes."""
     q = _dbl(q)
     B, S, R, G, N = q.shape
     v = _dbl(v)
@@ -99,7 +115,8 @@ def run(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
     states = np.zeros((B, H, nc, N, P))
     dz = np.zeros((B, S, H, P)) if has_z else None
     qk_dot = np.zeros((B, H, S, R, R))
-    rc = _load().o1_bwd_fwd(B, S, H, G, R, N, P, C, int(rotary_dim_divisor), int(bool(exact)),
+    W = _width(arrs[10], N, rotary_dim_divisor)
+    rc = _load().o1_bwd_fwd(B, S, H, G, R, N, P, C, W, _mode(exact, fp32),
                             int(reduce_o), int(has_z), int(has_d),
                             *[_ptr(a) for a in arrs],
                             _ptr(dmimo_o), _ptr(states), _ptr(dz), _ptr(dmimo_z), _ptr(qk_dot))
@@ -109,7 +126,7 @@ def run(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
 
 
 def run_fwd(q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, da_cs_rev,
-            dt, trap, d, segsum, chunk_size, rotary_dim_divisor=4, *, exact=False):
+            dt, trap, d, segsum, chunk_size, rotary_dim_divisor=4, *, exact=False, fp32=False):
     """Layer output of the same chunk walk (no dout): float64 ``o`` of shape
     [B,S,H,P] when ``mimo_o`` is given, else [B,S,R,H,P] (see ``o1_contract.c``)."""
     q = _dbl(q)
@@ -120,15 +137,16 @@ def run_fwd(q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, d
     arrs = [_dbl(x) for x in (q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles,
                               da_cs, da_cs_rev, dt, trap, d, segsum)]
     o = np.zeros((B, S, H, P)) if reduce_o else np.zeros((B, S, R, H, P))
-    rc = _load().o1_fwd(B, S, H, G, R, N, P, int(chunk_size), int(rotary_dim_divisor),
-                        int(bool(exact)), int(reduce_o), int(z is not None), int(d is not None),
+    W = _width(arrs[9], N, rotary_dim_divisor)
+    rc = _load().o1_fwd(B, S, H, G, R, N, P, int(chunk_size), W, _mode(exact, fp32),
+                        int(reduce_o), int(z is not None), int(d is not None),
                         *[_ptr(a) for a in arrs], _ptr(o), None)
     if rc != 0:
         raise ValueError("o1_fwd rejected the shape")
     return o
 
 
-def run_fwd_inputs(inp: dict, *, exact=False, exact_controls=False):
+def run_fwd_inputs(inp: dict, *, exact=False, exact_controls=False, fp32=False):
     """``run_fwd`` on a ``synth.inputs.make_inputs`` dict (dout is not used)."""
     cs, rev, seg = inp["da_cs"], inp["da_cs_rev"], inp["segsum"]
     if exact_controls:
@@ -136,10 +154,10 @@ def run_fwd_inputs(inp: dict, *, exact=False, exact_controls=False):
     return run_fwd(inp["q"], inp["k"], inp["v"], inp["q_bias"], inp["k_bias"], inp["mimo_v"],
                    inp["mimo_o"], inp["z"], inp["mimo_z"], inp["angles"], cs, rev, inp["dt"],
                    inp["trap"], inp["d"], seg, inp["chunk_size"], inp["rotary_dim_divisor"],
-                   exact=exact)
+                   exact=exact, fp32=fp32)
 
 
-def run_inputs(inp: dict, *, exact=False, exact_controls=False):
+def run_inputs(inp: dict, *, exact=False, exact_controls=False, fp32=False):
     """Run O1 on a ``synth.inputs.make_inputs`` dict. With ``exact_controls`` the
     float64 controls built from da are used instead of their float32 copies."""
     cs, rev, seg = inp["da_cs"], inp["da_cs_rev"], inp["segsum"]
@@ -148,7 +166,7 @@ def run_inputs(inp: dict, *, exact=False, exact_controls=False):
     return run(inp["dout"], inp["q"], inp["k"], inp["v"], inp["q_bias"], inp["k_bias"],
                inp["mimo_v"], inp["mimo_o"], inp["z"], inp["mimo_z"], inp["angles"], cs, rev,
                inp["dt"], inp["trap"], inp["d"], seg, inp["chunk_size"],
-               inp["rotary_dim_divisor"], exact=exact)
+               inp["rotary_dim_divisor"], exact=exact, fp32=fp32)
 
 
 def slice_heads(inp: dict, b: int, h: int) -> dict:

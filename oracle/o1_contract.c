@@ -13,16 +13,25 @@
  * fp32 tensor is rounded to fp32 (RF) and every place the pages round to
  * bf16 is rounded to bf16 round-to-nearest-even (RB). Dot products and sums
  * accumulate in double and are rounded once at the end, which is at least as
- * accurate as any fp32 summation order. With exact != 0 both roundings are
- * the identity and every quantity is carried in double: that is the
- * chunked algorithm in exact arithmetic, used to check the algebra against
- * an unchunked recurrence.
+ * accurate as any fp32 summation order. Three modes:
+ *   0  the bf16 contract above;
+ *   1  exact: both roundings are the identity and every quantity is carried
+ *      in double -- the chunked algorithm in exact arithmetic, used to check
+ *      the algebra against an unchunked recurrence;
+ *   2  fp32 intermediates: the same page's FP32 reference -- every
+ *      intermediate stays fp32 (no bf16 rounding of q, k, PsiV, the
+ *      projections, dt, the causal block, the state, y, the diagonal chain or
+ *      the dz chain) and only the outputs are cast to their dtypes (states,
+ *      qk_dot and dz to bf16). That reference writes the look-ahead weight as
+ *      dt[t+1] * (1 - sigmoid(trap[t+1])), followed here.
  *
  * All tensors are dense row-major in the operator's own layouts:
  *   dout   [B,S,H,P] (reduce_o) or [B,S,R,H,P] (non-reduced)
  *   q, k   [B,S,R,G,N]      v, z [B,S,H,P]
  *   q_bias, k_bias [H,R,N]   mimo_v, mimo_o, mimo_z [H,R,P]
- *   angles [B,S,H,N/rd]      da_cs, da_cs_rev, dt, trap [B,H,S]
+ *   angles [B,S,H,W]         da_cs, da_cs_rev, dt, trap [B,H,S]
+ * (W = N / rotary_dim_divisor rotated column pairs: columns [0,W) pair with
+ * [N/2, N/2+W))
  *   d [H]                    segsum [B,H,nc,C,C]
  * outputs
  *   dmimo_o, dmimo_z [B,H,R,P]   states [B,H,nc,N,P]
@@ -50,16 +59,16 @@
 #include <stdlib.h>
 #include <string.h>
 
-static int g_exact = 0;
+static int g_mode = 0;   /* 0 contract, 1 exact, 2 fp32 intermediates */
 
 /* fp32 rounding of a double (identity in exact mode). */
-static inline double RF(double x) { return g_exact ? x : (double)(float)x; }
+static inline double RF(double x) { return g_mode == 1 ? x : (double)(float)x; }
 
 /* bf16 round-to-nearest-even of an fp32 value, from the IEEE-754 binary
  * encoding: keep the upper 16 bits, rounding on the lower 16 with ties to
  * the even upper half. NaN stays NaN. */
 static inline double RB(double xd) {
-    if (g_exact) return xd;
+    if (g_mode == 1) return xd;
     float f = (float)xd;
     uint32_t u;
     memcpy(&u, &f, 4);
@@ -73,11 +82,15 @@ static inline double RB(double xd) {
     return (double)f;
 }
 
+/* A bf16 rounding of an intermediate value: the contract's RB, fp32 in mode 2.
+ * RB itself is kept for the outputs, which are bf16 in every mode but exact. */
+static inline double RBI(double x) { return g_mode == 2 ? RF(x) : RB(x); }
+
 static inline double EXP(double x) { return RF(exp(x)); }
 static inline double SIG(double x) { return RF(1.0 / (1.0 + exp(-x))); }
 
 typedef struct {
-    int64_t B, S, H, G, R, N, P, C, rd;
+    int64_t B, S, H, G, R, N, P, C, W;
     int reduce_o, has_z, has_d;
     const double *dout, *q, *k, *v, *q_bias, *k_bias, *mimo_v, *mimo_o, *z, *mimo_z;
     const double *angles, *da_cs, *da_cs_rev, *dt, *trap, *d, *segsum;
@@ -89,7 +102,7 @@ typedef struct {
 /* One (batch, head) pair: the whole sequence, chunk by chunk. */
 static void o1_head(const o1_args *a, int64_t b, int64_t h) {
     const int64_t S = a->S, H = a->H, G = a->G, R = a->R, N = a->N, P = a->P, C = a->C;
-    const int64_t W = N / a->rd, M = N / 2, nc = (S + C - 1) / C;
+    const int64_t W = a->W, M = N / 2, nc = (S + C - 1) / C;
     const int64_t g = h / (H / G);
 
     double *q0 = malloc(sizeof(double) * C * R * N);   /* biased q, before rotation  */
@@ -113,10 +126,10 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
         const int64_t cl = (S - c0 < C) ? (S - c0) : C;   /* real tokens in chunk */
 
         /* entry state of chunk c */
-        for (int64_t i = 0; i < N * P; ++i) Sb[i] = RB(St[i]);
+        for (int64_t i = 0; i < N * P; ++i) Sb[i] = RBI(St[i]);
         if (a->states) {
             double *st_out = a->states + (((b * H + h) * nc + c) * N) * P;
-            for (int64_t i = 0; i < N * P; ++i) st_out[i] = Sb[i];
+            for (int64_t i = 0; i < N * P; ++i) st_out[i] = RB(St[i]);
         }
 
         /* per-token preparation */
@@ -129,8 +142,8 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                 const double *kb = a->k_bias + (h * R + r) * N;
                 double *q0r = q0 + (t * R + r) * N, *k0r = k0 + (t * R + r) * N;
                 for (int64_t n = 0; n < N; ++n) {
-                    q0r[n] = RB(RF(qs[n] + RB(qb[n])));
-                    k0r[n] = RB(RF(ks[n] + RB(kb[n])));
+                    q0r[n] = RBI(RF(qs[n] + RBI(qb[n])));
+                    k0r[n] = RBI(RF(ks[n] + RBI(kb[n])));
                 }
             }
             /* same-token rank-by-rank dot of the biased, unrotated q and k */
@@ -139,9 +152,8 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                     double sum = 0.0;
                     const double *x = q0 + (t * R + r) * N, *w = k0 + (t * R + s2) * N;
                     for (int64_t n = 0; n < N; ++n) sum += x[n] * w[n];
-                    const double v = RB(RF(sum));
-                    qk[(t * R + r) * R + s2] = v;
-                    if (a->qk_dot) a->qk_dot[(((b * H + h) * S + T) * R + r) * R + s2] = v;
+                    qk[(t * R + r) * R + s2] = RBI(RF(sum));
+                    if (a->qk_dot) a->qk_dot[(((b * H + h) * S + T) * R + r) * R + s2] = RB(RF(sum));
                 }
             /* partial rotate-half: columns [0,W) pair with [M, M+W) */
             const double *th = a->angles + ((b * S + T) * H + h) * W;
@@ -151,30 +163,33 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                 for (int64_t n = 0; n < N; ++n) { qrr[n] = q0r[n]; ktr[n] = k0r[n]; }
                 for (int64_t n = 0; n < W; ++n) {
                     const double cs = RF(cos(th[n])), sn = RF(sin(th[n]));
-                    qrr[n] = RB(RF(RF(cs * q0r[n]) - RF(sn * q0r[M + n])));
-                    qrr[M + n] = RB(RF(RF(sn * q0r[n]) + RF(cs * q0r[M + n])));
-                    ktr[n] = RB(RF(RF(cs * k0r[n]) - RF(sn * k0r[M + n])));
-                    ktr[M + n] = RB(RF(RF(sn * k0r[n]) + RF(cs * k0r[M + n])));
+                    qrr[n] = RBI(RF(RF(cs * q0r[n]) - RF(sn * q0r[M + n])));
+                    qrr[M + n] = RBI(RF(RF(sn * q0r[n]) + RF(cs * q0r[M + n])));
+                    ktr[n] = RBI(RF(RF(cs * k0r[n]) - RF(sn * k0r[M + n])));
+                    ktr[M + n] = RBI(RF(RF(sn * k0r[n]) + RF(cs * k0r[M + n])));
                 }
             }
             /* PsiV = v * bf16(mimo_v) */
             for (int64_t r = 0; r < R; ++r)
                 for (int64_t p = 0; p < P; ++p)
                     psi[(t * R + r) * P + p] =
-                        RB(RF(a->v[((b * S + T) * H + h) * P + p] * RB(a->mimo_v[(h * R + r) * P + p])));
+                        RBI(RF(a->v[((b * S + T) * H + h) * P + p] * RBI(a->mimo_v[(h * R + r) * P + p])));
             /* trapezoidal discretisation: gamma (fp32), beta from the next token, factor (bf16) */
             const int64_t ih = (b * H + h) * S;
-            const double gamma = RF(RB(a->dt[ih + T]) * SIG(a->trap[ih + T]));
+            const double gamma = RF(RBI(a->dt[ih + T]) * SIG(a->trap[ih + T]));
             double beta = 0.0;
-            if (T + 1 < S) beta = RB(RF(RB(a->dt[ih + T + 1]) * SIG(-a->trap[ih + T + 1])));
-            const double factor = RB(RF(gamma + beta));
+            if (T + 1 < S) {
+                const double w = g_mode == 2 ? RF(1.0 - SIG(a->trap[ih + T + 1])) : SIG(-a->trap[ih + T + 1]);
+                beta = RBI(RF(RBI(a->dt[ih + T + 1]) * w));
+            }
+            const double factor = RBI(RF(gamma + beta));
             gam[t] = gamma;
             const double erev = EXP(a->da_cs_rev[ih + T]);
             for (int64_t r = 0; r < R; ++r)
                 for (int64_t n = 0; n < N; ++n) {
                     double *ktr = kt + (t * R + r) * N;
-                    ktr[n] = RB(RF(ktr[n] * factor));
-                    kap[(t * R + r) * N + n] = RB(RF(ktr[n] * erev));
+                    ktr[n] = RBI(RF(ktr[n] * factor));
+                    kap[(t * R + r) * N + n] = RBI(RF(ktr[n] * erev));
                 }
         }
 
@@ -192,7 +207,7 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                         double sum = 0.0;
                         const double *krow = kt + (j * R + s2) * N;
                         for (int64_t n = 0; n < N; ++n) sum += qrow[n] * krow[n];
-                        A[j * R + s2] = RB(RF(RF(sum) * es));
+                        A[j * R + s2] = RBI(RF(RF(sum) * es));
                     }
                 }
                 for (int64_t p = 0; p < P; ++p) acc[p] = 0.0;
@@ -210,13 +225,13 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                     /* diagonal: rank-ordered bf16 products and sums, then times gamma */
                     double dg = 0.0;
                     for (int64_t s2 = 0; s2 < R; ++s2) {
-                        const double prod = RB(RF(qk[(t * R + r) * R + s2] * psi[(t * R + s2) * P + p]));
-                        dg = RB(RF(dg + prod));
+                        const double prod = RBI(RF(qk[(t * R + r) * R + s2] * psi[(t * R + s2) * P + p]));
+                        dg = RBI(RF(dg + prod));
                     }
-                    dg = RB(RF(dg * gam[t]));
+                    dg = RBI(RF(dg * gam[t]));
                     double o = RF(RF(inter + intra) + dg);
                     if (a->has_d) o = RF(o + RF(a->d[h] * psi[(t * R + r) * P + p]));
-                    y[(t * R + r) * P + p] = RB(o);
+                    y[(t * R + r) * P + p] = RBI(o);
                 }
             }
         }
@@ -245,7 +260,7 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                     double oacc = 0.0;
                     for (int64_t r = 0; r < R; ++r) {
                         double val = y[(t * R + r) * P + p];
-                        if (a->reduce_o) val = RF(val * RB(a->mimo_o[(h * R + r) * P + p]));
+                        if (a->reduce_o) val = RF(val * RBI(a->mimo_o[(h * R + r) * P + p]));
                         if (a->has_z) {
                             const double pz = RF(a->z[ivp] * a->mimo_z[(h * R + r) * P + p]);
                             val = RF(val * RF(pz * SIG(pz)));
@@ -279,21 +294,21 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                         const double dv = a->dout[ivp];
                         if (a->has_z) {
                             dmo[r * P + p] += RF(RF(yv * silu) * dv);
-                            G = RB(RF(RB(RF(dv * RB(a->mimo_o[(h * R + r) * P + p]))) * yv));
+                            G = RBI(RF(RBI(RF(dv * RBI(a->mimo_o[(h * R + r) * P + p]))) * yv));
                         } else {
                             dmo[r * P + p] += RF(yv * dv);
                         }
                     } else if (a->has_z) {
                         const double dv = a->dout[(((b * S + T) * R + r) * H + h) * P + p];
-                        G = RB(RF(dv * yv));
+                        G = RBI(RF(dv * yv));
                     }
                     if (a->has_z) {
                         const double gz = RF(RF(G * sg) * RF(1.0 + RF(pz * SIG(-pz))));
-                        dzacc = RB(RF(dzacc + RF(gz * a->mimo_z[(h * R + r) * P + p])));
+                        dzacc = RBI(RF(dzacc + RF(gz * a->mimo_z[(h * R + r) * P + p])));
                         dmz[r * P + p] += RF(gz * a->z[ivp]);
                     }
                 }
-                if (a->has_z) a->dz[ivp] = dzacc;
+                if (a->has_z) a->dz[ivp] = RB(dzacc);
             }
         }
     }
@@ -307,7 +322,7 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
 
 /* Entry point. Returns 0, or -1 for an invalid shape. */
 int o1_bwd_fwd(int64_t B, int64_t S, int64_t H, int64_t G, int64_t R, int64_t N, int64_t P,
-               int64_t C, int64_t rd, int exact, int reduce_o, int has_z, int has_d,
+               int64_t C, int64_t W, int mode, int reduce_o, int has_z, int has_d,
                const double *dout, const double *q, const double *k, const double *v,
                const double *q_bias, const double *k_bias, const double *mimo_v,
                const double *mimo_o, const double *z, const double *mimo_z,
@@ -315,9 +330,9 @@ int o1_bwd_fwd(int64_t B, int64_t S, int64_t H, int64_t G, int64_t R, int64_t N,
                const double *dt, const double *trap, const double *d, const double *segsum,
                double *dmimo_o, double *states, double *dz, double *dmimo_z, double *qk_dot) {
     if (B < 1 || S < 1 || H < 1 || G < 1 || R < 1 || N < 2 || P < 1 || C < 1) return -1;
-    if (H % G || N % 2 || (rd != 2 && rd != 4) || N % rd) return -1;
-    g_exact = exact;
-    o1_args a = {B, S, H, G, R, N, P, C, rd, reduce_o, has_z, has_d,
+    if (H % G || N % 2 || W < 0 || 2 * W > N || mode < 0 || mode > 2) return -1;
+    g_mode = mode;
+    o1_args a = {B, S, H, G, R, N, P, C, W, reduce_o, has_z, has_d,
                  dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z,
                  angles, da_cs, da_cs_rev, dt, trap, d, segsum,
                  dmimo_o, states, dz, dmimo_z, qk_dot, 0, NULL};
@@ -329,16 +344,16 @@ int o1_bwd_fwd(int64_t B, int64_t S, int64_t H, int64_t G, int64_t R, int64_t N,
 
 /* bf16 rounding exposed for the oracle's own unit tests. */
 void o1_round_bf16(const float *x, float *y, int64_t n) {
-    int save = g_exact;
-    g_exact = 0;
+    int save = g_mode;
+    g_mode = 0;
     for (int64_t i = 0; i < n; ++i) y[i] = (float)RB((double)x[i]);
-    g_exact = save;
+    g_mode = save;
 }
 
 /* Layer output (see the header comment): the chunk walk of o1_bwd_fwd without
  * dout. states may be NULL. Returns 0, or -1 for an invalid shape. */
 int o1_fwd(int64_t B, int64_t S, int64_t H, int64_t G, int64_t R, int64_t N, int64_t P,
-           int64_t C, int64_t rd, int exact, int reduce_o, int has_z, int has_d,
+           int64_t C, int64_t W, int mode, int reduce_o, int has_z, int has_d,
            const double *q, const double *k, const double *v,
            const double *q_bias, const double *k_bias, const double *mimo_v,
            const double *mimo_o, const double *z, const double *mimo_z,
@@ -346,9 +361,9 @@ int o1_fwd(int64_t B, int64_t S, int64_t H, int64_t G, int64_t R, int64_t N, int
            const double *dt, const double *trap, const double *d, const double *segsum,
            double *o, double *states) {
     if (B < 1 || S < 1 || H < 1 || G < 1 || R < 1 || N < 2 || P < 1 || C < 1) return -1;
-    if (H % G || N % 2 || (rd != 2 && rd != 4) || N % rd) return -1;
-    g_exact = exact;
-    o1_args a = {B, S, H, G, R, N, P, C, rd, reduce_o, has_z, has_d,
+    if (H % G || N % 2 || W < 0 || 2 * W > N || mode < 0 || mode > 2) return -1;
+    g_mode = mode;
+    o1_args a = {B, S, H, G, R, N, P, C, W, reduce_o, has_z, has_d,
                  NULL, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z,
                  angles, da_cs, da_cs_rev, dt, trap, d, segsum,
                  NULL, states, NULL, NULL, NULL, 1, o};

@@ -46,10 +46,11 @@ def _sig(x):
     return 1.0 / (1.0 + np.exp(-x))
 
 
-def _rot(x, th, rd):
-    """Partial rotate-half of the last axis: columns [0,W) pair with [N/2, N/2+W)."""
+def _rot(x, th):
+    """Partial rotate-half of the last axis: columns [0,W) pair with [N/2, N/2+W),
+    W = the angles' last axis."""
     N = x.shape[-1]
-    W, M = N // rd, N // 2
+    W, M = th.shape[-1], N // 2
     c, s = np.cos(th), np.sin(th)       # [..., W]
     out = x.copy()
     a, e = x[..., :W], x[..., M:M + W]
@@ -84,8 +85,8 @@ def run(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da, dt
         qk = np.einsum("bhrn,bhsn->bhrs", q0, k0)
         qk_dot[:, :, t] = qk
         th = ang[:, t][:, :, None, :]                                       # [B,H,1,W]
-        qh = _rot(q0, th, rotary_dim_divisor)
-        kh = _rot(k0, th, rotary_dim_divisor)
+        qh = _rot(q0, th)
+        kh = _rot(k0, th)
         psi = v[:, t][:, :, None, :] * mv[None]                            # [B,H,R,P]
         gamma = dt[:, :, t] * _sig(trap[:, :, t])                           # [B,H]
         beta = dt[:, :, t + 1] * _sig(-trap[:, :, t + 1]) if t + 1 < S else np.zeros_like(gamma)

@@ -37,7 +37,7 @@ def run(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da, dt
     assert S <= 512, "brute force is for tiny inputs"
     C = int(chunk_size)
     nc = (S + C - 1) // C
-    W, M = N // rotary_dim_divisor, N // 2
+    W, M = _np(angles).shape[-1], N // 2
     grp = np.arange(H) // (H // G)
     ang, da, dt, trap = _np(angles), _np(da), _np(dt), _np(trap)
 

@@ -35,7 +35,8 @@ from dataclasses import dataclass, field, replace
 
 import torch
 
-__all__ = ["Case", "make_inputs", "API_ORDER", "CONFIGS", "UT_CASES", "ATK_CASES"]
+__all__ = ["Case", "make_inputs", "API_ORDER", "CONFIGS", "UT_CASES", "ATK_CASES", "SisoCase",
+           "make_siso_inputs", "SISO_ORDER", "SISO_CONFIGS"]
 
 # Positional order of the tensor arguments of mamba_mimo_bwd_fwd.
 API_ORDER = (
@@ -216,3 +217,69 @@ def make_inputs(case: Case, *, want_exact: bool = False):
 def api_args(inputs: dict):
     """Positional argument tuple of mamba_mimo_bwd_fwd for an inputs dict."""
     return tuple(inputs[n] for n in API_ORDER) + (inputs["chunk_size"], inputs["rotary_dim_divisor"])
+
+
+# ---------------------------------------------------------------- SISO forward
+# Positional order of the tensor arguments of the SISO forward (mamba3_siso_fwd_kernel).
+SISO_ORDER = ("q", "k", "v", "adt", "dt", "trap", "q_bias", "k_bias", "angles", "d", "z")
+
+
+@dataclass(frozen=True)
+class SisoCase:
+    """SISO forward shape: q/k [B,S,Hq,K], v/z [B,S,H,V], angles [B,S,H,A]."""
+    B: int
+    S: int
+    Hq: int
+    H: int
+    K: int
+    V: int
+    C: int = 64
+    A: int = 0                 # rotated pairs; 0 = K // 2
+    dtype: str = "bf16"        # "bf16" or "fp16" for q, k, v, z
+    has_z: bool = True
+    has_d: bool = True
+    seed: int = 123
+    name: str = field(default="", compare=False)
+
+    @property
+    def width(self) -> int:
+        return self.A or self.K // 2
+
+    def with_(self, **kw) -> "SisoCase":
+        return replace(self, **kw)
+
+
+# The page's usage example (fp16, Hq=2, H=4, K=64, V=96, chunk 64) and a long
+# sequence in each dtype at the K=128 state size the page singles out.
+SISO_CONFIGS = {
+    "siso_example": SisoCase(1, 128, 2, 4, 64, 96, 64, dtype="fp16", name="siso_example"),
+    "siso_s8192_k128": SisoCase(1, 8192, 16, 16, 128, 64, 64, name="siso_s8192_k128"),
+    "siso_s8192_k128_fp16": SisoCase(1, 8192, 16, 16, 128, 64, 64, dtype="fp16",
+                                     name="siso_s8192_k128_fp16"),
+}
+
+
+def make_siso_inputs(case: SisoCase):
+    """Draw the SISO forward's inputs on the CPU with the distributions of the page's
+    usage example: q, k, v, z ~ N(0,1) in the case's dtype; adt = -0.08 U(0,1);
+    dt = 0.05 N(0,1); trap ~ N(0,1); q_bias, k_bias = 0.05 N(0,1); angles =
+    0.25 U(0,1); d = 0.2 U(0,1) (numeric parameters float32). Returns a dict with
+    the ``SISO_ORDER`` tensors (absent optional ones None) and ``chunk_size``."""
+    B, S, Hq, H, K, V, A = case.B, case.S, case.Hq, case.H, case.K, case.V, case.width
+    g = torch.Generator().manual_seed(case.seed)
+    dt_ = torch.float16 if case.dtype == "fp16" else torch.bfloat16
+    out = {
+        "q": torch.randn((B, S, Hq, K), generator=g).to(dt_),
+        "k": torch.randn((B, S, Hq, K), generator=g).to(dt_),
+        "v": torch.randn((B, S, H, V), generator=g).to(dt_),
+        "adt": -torch.rand((B, H, S), generator=g) * 0.08,
+        "dt": torch.randn((B, H, S), generator=g) * 0.05,
+        "trap": torch.randn((B, H, S), generator=g),
+        "q_bias": torch.randn((H, K), generator=g) * 0.05,
+        "k_bias": torch.randn((H, K), generator=g) * 0.05,
+        "angles": torch.rand((B, S, H, A), generator=g) * 0.25,
+        "d": torch.rand((H,), generator=g) * 0.2 if case.has_d else None,
+        "z": torch.randn((B, S, H, V), generator=g).to(dt_) if case.has_z else None,
+    }
+    out["chunk_size"] = case.C
+    return out
