@@ -159,6 +159,69 @@ mimo_status mimo_fwd(const mimo_fwd_args *args, void *stream);
  * final-reduction kernel does not run: its two events are back to back). */
 mimo_status mimo_fwd_timed(const mimo_fwd_args *args, void *stream, void *const *events);
 
+/*
+ * FP32-intermediate variant (Triton-Ascend mamba_mimo_bwd_fwd pull request
+ * page, FP32 PyTorch reference): the same operation with no bf16 rounding of
+ * any intermediate value -- biased q/k, rotation, PsiV with unrounded mimo_v,
+ * dt and the trapezoid weights (look-ahead weight dt[t+1]*(1 - sigmoid(trap
+ * [t+1]))), kappa, the causal block, the fp32 state in the inter term, y, the
+ * diagonal, dPhiO with unrounded mimo_o, and the dz sum all stay fp32, with
+ * fp32 contractions. Outputs keep their dtypes (states, qk_dot, dz bf16 by
+ * round-to-nearest-even; dmimo fp32). Arguments, layouts, ownership and errors
+ * as for mimo_bwd_fwd, with these limits instead of its tile limits: N and P
+ * multiples of 16 up to 128, chunk_size <= 64, R <= 8, R * (chunk_size rounded
+ * up to 16) <= 128, and the fp32 tiles must fit one compute unit's LDS (not the
+ * case for R * chunk_size > 64 with N or P = 128): MIMO_ERR_UNSUPPORTED otherwise.
+ */
+mimo_status mimo_bwd_fwd_f32_workspace_size(const mimo_bwd_fwd_args *args, size_t *bytes);
+mimo_status mimo_bwd_fwd_f32(const mimo_bwd_fwd_args *args, void *stream);
+mimo_status mimo_bwd_fwd_f32_timed(const mimo_bwd_fwd_args *args, void *stream, void *const *events);
+
+/* The layer output (mimo_fwd) with fp32 intermediates: o = sum_r mimo_o * y * silu(pz)
+ * (or per rank) with y, the projections and the gate in fp32 and only o rounded
+ * to bf16. Limits as for mimo_bwd_fwd_f32. */
+mimo_status mimo_fwd_f32_workspace_size(const mimo_fwd_args *args, size_t *bytes);
+mimo_status mimo_fwd_f32(const mimo_fwd_args *args, void *stream);
+
+/*
+ * SISO forward (mamba3_siso_fwd_kernel migration page: interface, inputs and
+ * "implementation principle"). For batch b, head h (q/k head h / (H/Hq)):
+ * q, k get their bias and a partial rotate-half by `angles` (pairs [0,A) with
+ * [K/2, K/2+A)); gamma_t = dt_t * sigmoid(trap_t) and the look-ahead weight
+ * dt_{t+1} * (1 - sigmoid(trap_{t+1})) scale k; inside each chunk the strictly
+ * causal score q^_t . k~_s is weighted by exp(sum of adt over (s, t]), the
+ * previous chunks enter through the carried state, the same-token term is
+ * gamma_t (q^_t . k^_t) v_t, d[h] v_t is added, and with z the result is gated
+ * by silu(z). Intermediates are fp32; the output takes the input dtype.
+ * Layouts (dense, row-major): q, k [B,S,Hq,K]; v, z, out [B,S,H,V];
+ * adt, dt, trap [B,H,S] fp32; q_bias, k_bias [H,K] fp32; angles [B,S,H,A]
+ * fp32 (may be NULL when A = 0); d [H] fp32. chunk_size 32 or 64; H % Hq == 0; A even and <= K/2
+ * (MIMO_ERR_VALUE otherwise). K and V must be multiples of 16 up to 128 and
+ * the fp32 tiles must fit the LDS (MIMO_ERR_UNSUPPORTED otherwise).
+ * Ownership, asynchrony and errors as for mimo_bwd_fwd.
+ */
+#define MIMO_DTYPE_BF16 0
+#define MIMO_DTYPE_FP16 1
+typedef struct mimo_siso_fwd_args {
+    int64_t B, S, Hq, H, K, V;
+    int32_t chunk_size;          /* 32 or 64                                           */
+    int32_t A;                   /* rotated pairs: the last axis of angles             */
+    int32_t dtype;               /* MIMO_DTYPE_BF16 or MIMO_DTYPE_FP16 for q, k, v, z, out */
+    const uint16_t *q, *k, *v;
+    const float *adt, *dt, *trap;
+    const float *q_bias, *k_bias, *angles;
+    const float *d;              /* optional                                           */
+    const uint16_t *z;           /* optional                                           */
+    uint16_t *out;
+    void *workspace;             /* at least mimo_siso_fwd_workspace_size() bytes, 256-byte aligned */
+    size_t workspace_bytes;
+} mimo_siso_fwd_args;
+
+mimo_status mimo_siso_fwd_workspace_size(const mimo_siso_fwd_args *args, size_t *bytes);
+mimo_status mimo_siso_fwd(const mimo_siso_fwd_args *args, void *stream);
+/* mimo_siso_fwd with the MIMO_TIMED_EVENTS events of mimo_bwd_fwd_timed. */
+mimo_status mimo_siso_fwd_timed(const mimo_siso_fwd_args *args, void *stream, void *const *events);
+
 /* Message describing the last error of the calling thread ("" if none). */
 const char *mimo_last_error(void);
 

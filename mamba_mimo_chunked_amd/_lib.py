@@ -69,8 +69,31 @@ class MimoFwdArgs(ctypes.Structure):
     ]
 
 
+class MimoSisoFwdArgs(ctypes.Structure):
+    """Mirror of ``mimo_siso_fwd_args`` (field order and types must match)."""
+
+    _fields_ = [
+        ("B", ctypes.c_int64), ("S", ctypes.c_int64), ("Hq", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("K", ctypes.c_int64), ("V", ctypes.c_int64),
+        ("chunk_size", ctypes.c_int32), ("A", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("adt", ctypes.c_void_p), ("dt", ctypes.c_void_p), ("trap", ctypes.c_void_p),
+        ("q_bias", ctypes.c_void_p), ("k_bias", ctypes.c_void_p), ("angles", ctypes.c_void_p),
+        ("d", ctypes.c_void_p),
+        ("z", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+DTYPE_BF16, DTYPE_FP16 = 0, 1
+
 EXPORTED = ("mimo_bwd_fwd", "mimo_bwd_fwd_timed", "mimo_bwd_fwd_workspace_size", "mimo_fwd",
-            "mimo_fwd_timed", "mimo_fwd_workspace_size", "mimo_last_error", "mimo_abi_version")
+            "mimo_fwd_timed", "mimo_fwd_workspace_size", "mimo_bwd_fwd_f32", "mimo_bwd_fwd_f32_timed",
+            "mimo_bwd_fwd_f32_workspace_size", "mimo_fwd_f32", "mimo_fwd_f32_workspace_size",
+            "mimo_siso_fwd", "mimo_siso_fwd_timed", "mimo_siso_fwd_workspace_size", "mimo_last_error",
+            "mimo_abi_version")
 TIMED_EVENTS = 5
 
 _lib = None
@@ -99,6 +122,22 @@ def lib():
         L.mimo_fwd_timed.restype = ctypes.c_int
         L.mimo_fwd_workspace_size.argtypes = [fargp, ctypes.POINTER(ctypes.c_size_t)]
         L.mimo_fwd_workspace_size.restype = ctypes.c_int
+        evp = ctypes.POINTER(ctypes.c_void_p)
+        szp = ctypes.POINTER(ctypes.c_size_t)
+        for name, ap in (("mimo_bwd_fwd_f32", argp), ("mimo_fwd_f32", fargp)):
+            getattr(L, name).argtypes = [ap, ctypes.c_void_p]
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name + "_workspace_size").argtypes = [ap, szp]
+            getattr(L, name + "_workspace_size").restype = ctypes.c_int
+        L.mimo_bwd_fwd_f32_timed.argtypes = [argp, ctypes.c_void_p, evp]
+        L.mimo_bwd_fwd_f32_timed.restype = ctypes.c_int
+        sargp = ctypes.POINTER(MimoSisoFwdArgs)
+        L.mimo_siso_fwd.argtypes = [sargp, ctypes.c_void_p]
+        L.mimo_siso_fwd.restype = ctypes.c_int
+        L.mimo_siso_fwd_timed.argtypes = [sargp, ctypes.c_void_p, evp]
+        L.mimo_siso_fwd_timed.restype = ctypes.c_int
+        L.mimo_siso_fwd_workspace_size.argtypes = [sargp, szp]
+        L.mimo_siso_fwd_workspace_size.restype = ctypes.c_int
         L.mimo_last_error.argtypes = []
         L.mimo_last_error.restype = ctypes.c_char_p
         L.mimo_abi_version.argtypes = []

@@ -1,4 +1,5 @@
-"""Public Python entry points: ``mamba_mimo_bwd_fwd`` and the layer output ``mamba_mimo_fwd``.
+"""Public Python entry points: ``mamba_mimo_bwd_fwd``, the layer output ``mamba_mimo_fwd``,
+their fp32-intermediate variants, and the SISO forward ``mamba3_siso_fwd``.
 
 Signature, defaults, output order, validation order and error types follow
 the Triton-Ascend mamba_mimo_bwd_fwd page (public API module: the
@@ -18,8 +19,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["MambaMimoBwdFwdOutputs", "mamba_mimo_bwd_fwd", "mamba_mimo_fwd", "workspace_size",
-           "fwd_workspace_size"]
+__all__ = ["MambaMimoBwdFwdOutputs", "mamba_mimo_bwd_fwd", "mamba_mimo_fwd", "mamba_mimo_bwd_fwd_fp32",
+           "mamba_mimo_fwd_fp32", "mamba3_siso_fwd", "workspace_size", "fwd_workspace_size"]
 
 Tensor = torch.Tensor
 
@@ -171,6 +172,23 @@ def mamba_mimo_bwd_fwd(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z,
     ``workspace`` a preallocated uint8 scratch tensor (see ``workspace_size``).
     The call is asynchronous with respect to the host.
     """
+    return _bwd_fwd("mimo_bwd_fwd", dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles,
+                    da_cs, da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, out, workspace)
+
+
+def mamba_mimo_bwd_fwd_fp32(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
+                            da_cs_rev, dt, trap, d, segsum, chunk_size: int = 16,
+                            rotary_dim_divisor: int = 4, *, out: Optional[dict] = None,
+                            workspace: Optional[Tensor] = None) -> MambaMimoBwdFwdOutputs:
+    """``mamba_mimo_bwd_fwd`` with fp32 intermediates (no intermediate bf16 rounding;
+    outputs in their dtypes): the pages' FP32 reference semantics."""
+    return _bwd_fwd("mimo_bwd_fwd_f32", dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z,
+                    angles, da_cs, da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, out,
+                    workspace)
+
+
+def _bwd_fwd(fn, dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, da_cs_rev,
+             dt, trap, d, segsum, chunk_size, rotary_dim_divisor, out, workspace):
     _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
                      da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor)
     L = _lib.lib()
@@ -195,7 +213,7 @@ def mamba_mimo_bwd_fwd(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z,
         }
     args = _make_args(B, S, H, G, R, N, P, C, int(rotary_dim_divisor), t, out)
     need = ctypes.c_size_t(0)
-    st = L.mimo_bwd_fwd_workspace_size(ctypes.byref(args), ctypes.byref(need))
+    st = getattr(L, fn + "_workspace_size")(ctypes.byref(args), ctypes.byref(need))
     if st != _lib.MIMO_OK:
         _raise(st)
     if need.value > 0:
@@ -205,7 +223,7 @@ def mamba_mimo_bwd_fwd(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z,
         args.workspace_bytes = workspace.numel()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        st = L.mimo_bwd_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+        st = getattr(L, fn)(ctypes.byref(args), ctypes.c_void_p(stream))
     if st != _lib.MIMO_OK:
         _raise(st)
     return MambaMimoBwdFwdOutputs(out["dmimo_o"], out["states"], out["dz"], out["dmimo_z"], out["qk_dot"])
@@ -252,6 +270,20 @@ def mamba_mimo_fwd(q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, d
     (the gate is left out without ``z``). Same inputs as the backward stage minus dout;
     asynchronous on the current HIP stream.
     """
+    return _fwd("mimo_fwd", q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
+                da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, out, workspace)
+
+
+def mamba_mimo_fwd_fp32(q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, da_cs_rev,
+                        dt, trap, d, segsum, chunk_size: int = 16, rotary_dim_divisor: int = 4, *,
+                        out: Optional[Tensor] = None, workspace: Optional[Tensor] = None) -> Tensor:
+    """``mamba_mimo_fwd`` with fp32 intermediates (only o is rounded to bf16)."""
+    return _fwd("mimo_fwd_f32", q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
+                da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, out, workspace)
+
+
+def _fwd(fn, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, da_cs_rev, dt, trap, d,
+         segsum, chunk_size, rotary_dim_divisor, out, workspace):
     _validate_inputs(None, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
                      da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, fwd=True)
     L = _lib.lib()
@@ -271,7 +303,7 @@ def mamba_mimo_fwd(q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, d
             raise ValueError("out must be contiguous")
     args = _make_fwd_args(B, S, H, G, R, N, P, C, int(rotary_dim_divisor), t, out)
     need = ctypes.c_size_t(0)
-    st = L.mimo_fwd_workspace_size(ctypes.byref(args), ctypes.byref(need))
+    st = getattr(L, fn + "_workspace_size")(ctypes.byref(args), ctypes.byref(need))
     if st != _lib.MIMO_OK:
         _raise(st)
     if need.value > 0:
@@ -281,7 +313,102 @@ def mamba_mimo_fwd(q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, d
         args.workspace_bytes = workspace.numel()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        st = L.mimo_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+        st = getattr(L, fn)(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != _lib.MIMO_OK:
+        _raise(st)
+    return out
+
+
+# ---------------------------------------------------------------- SISO forward
+_SISO_INPUTS = ("q", "k", "v", "adt", "dt", "trap", "q_bias", "k_bias", "angles", "d", "z")
+
+
+def _validate_siso(q, k, v, adt, dt, trap, q_bias, k_bias, angles, d, z, chunk_size):
+    if isinstance(chunk_size, bool) or not isinstance(chunk_size, int) or chunk_size not in (32, 64):
+        raise ValueError("chunk_size must be 32 or 64")
+    if q.dim() != 4 or k.shape != q.shape:
+        raise ValueError("q and k must have shape [B, S, Hq, K]")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q, k, v and z must be torch.float16 or torch.bfloat16")
+    if q.device.type != "cuda":
+        raise ValueError("mamba3_siso_fwd requires GPU (HIP) tensors")
+    if not _is_gfx950(q.device.index if q.device.index is not None else torch.cuda.current_device()):
+        raise NotImplementedError("mamba3_siso_fwd supports gfx950 (MI355X) devices only")
+    B, S, Hq, K = q.shape
+    if v.dim() != 4 or tuple(v.shape[:2]) != (B, S):
+        raise ValueError("v must have shape [B, S, H, V]")
+    H, V = v.shape[2:]
+    if H % Hq:
+        raise ValueError("H must be divisible by Hq")
+    if angles.dim() != 4 or tuple(angles.shape[:3]) != (B, S, H):
+        raise ValueError("angles must have shape [B, S, H, A]")
+    A = angles.shape[3]
+    if A % 2 or 2 * A > K:
+        raise ValueError("the angle width A must be even and at most K / 2")
+    dev = q.device
+    _check_tensor("k", k, (B, S, Hq, K), q.dtype, dev)
+    _check_tensor("v", v, (B, S, H, V), q.dtype, dev)
+    for name, x in (("adt", adt), ("dt", dt), ("trap", trap)):
+        _check_tensor(name, x, (B, H, S), torch.float32, dev)
+    _check_tensor("q_bias", q_bias, (H, K), torch.float32, dev)
+    _check_tensor("k_bias", k_bias, (H, K), torch.float32, dev)
+    _check_tensor("angles", angles, (B, S, H, A), torch.float32, dev)
+    if d is not None:
+        _check_tensor("d", d, (H,), torch.float32, dev)
+    if z is not None:
+        _check_tensor("z", z, (B, S, H, V), q.dtype, dev)
+    return B, S, Hq, H, K, V, A
+
+
+def _make_siso_args(dims, dtype, t: dict, out, workspace=None, ws_bytes=0):
+    B, S, Hq, H, K, V, A, C = dims
+    a = _lib.MimoSisoFwdArgs()
+    a.B, a.S, a.Hq, a.H, a.K, a.V = B, S, Hq, H, K, V
+    a.chunk_size, a.A = C, A
+    a.dtype = _lib.DTYPE_FP16 if dtype == torch.float16 else _lib.DTYPE_BF16
+    for name in _SISO_INPUTS:
+        x = t.get(name)
+        setattr(a, name, None if x is None else x.data_ptr())
+    a.out = None if out is None else out.data_ptr()
+    a.workspace = None if workspace is None else workspace.data_ptr()
+    a.workspace_bytes = ws_bytes
+    return a
+
+
+def mamba3_siso_fwd(q, k, v, adt, dt, trap, q_bias, k_bias, angles, d=None, z=None,
+                    chunk_size: int = 64, *, out: Optional[Tensor] = None,
+                    workspace: Optional[Tensor] = None) -> Tensor:
+    """Dense SISO forward output [B,S,H,V] in q's dtype: bias and rotary on q/k, the
+    trapezoid weights from dt and sigmoid(trap), the adt decay inside and across chunks,
+    the same-token skip term, the optional D skip and SiLU(z) gate. q, k [B,S,Hq,K] and
+    v, z [B,S,H,V] in float16 or bfloat16; adt, dt, trap [B,H,S], q_bias, k_bias [H,K],
+    angles [B,S,H,A] (A even, <= K/2) and d [H] in float32; chunk_size 32 or 64.
+    Intermediates are fp32. Asynchronous on the current HIP stream."""
+    dims = _validate_siso(q, k, v, adt, dt, trap, q_bias, k_bias, angles, d, z, chunk_size)
+    B, S, Hq, H, K, V, A = dims
+    L = _lib.lib()
+    dev = q.device
+    vals = (q, k, v, adt, dt, trap, q_bias, k_bias, angles, d, z)
+    t = {n: (None if x is None else x.contiguous()) for n, x in zip(_SISO_INPUTS, vals)}
+    if out is None:
+        out = torch.empty((B, S, H, V), dtype=q.dtype, device=dev)
+    else:
+        _check_tensor("out", out, (B, S, H, V), q.dtype, dev)
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+    args = _make_siso_args(dims + (int(chunk_size),), q.dtype, t, out)
+    need = ctypes.c_size_t(0)
+    st = L.mimo_siso_fwd_workspace_size(ctypes.byref(args), ctypes.byref(need))
+    if st != _lib.MIMO_OK:
+        _raise(st)
+    if need.value > 0:
+        if workspace is None or workspace.numel() < need.value:
+            workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.mimo_siso_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
     if st != _lib.MIMO_OK:
         _raise(st)
     return out

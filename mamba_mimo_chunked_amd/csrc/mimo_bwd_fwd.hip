@@ -47,7 +47,7 @@
 #include <mutex>
 #include <string>
 
-#include "mimo_kernels.hpp"
+#include "mimo_f32.hpp"
 
 namespace mimo {
 
@@ -307,6 +307,223 @@ mimo_bwd_fwd_args as_bwd_args(const mimo_fwd_args* f) {
     return a;
 }
 
+// ---------------------------------------------------------------- fp32-intermediate path
+// Problem of the fp32 kernels, in the MIMO operator's terms (the SISO forward maps
+// onto it with R = 1, G = Hq, N = K, P = V and unit projections).
+struct Prob32 {
+    int64_t B, S, H, G, R, N, P;
+    int C, W;
+    bool reduce_o, has_z, has_d, fwd, f16;
+};
+
+struct Plan32 {
+    int MT, NT, PT, nc, L, nseg, F, nsub, ti, lds_main, lds_agg;
+    size_t off_agg, off_decay, off_po, off_pz, ws_bytes;
+};
+
+int tidx3(int x) { return x == 32 ? 0 : (x == 64 ? 1 : 2); }
+
+mimo_status make_plan32(const Prob32& q, Plan32* pl) {
+    if (q.B < 1 || q.S < 1 || q.R < 1 || q.G < 1 || q.H < 1 || q.N < 1 || q.P < 1)
+        return fail(MIMO_ERR_VALUE, "B, S, H, G, R, N and P must be positive");
+    if (q.C < 1) return fail(MIMO_ERR_VALUE, "chunk_size must be positive");
+    if (q.H % q.G) return fail(MIMO_ERR_VALUE, "H must be divisible by the number of q/k heads");
+    if (q.N % 2 || q.W < 0 || 2 * q.W > q.N) return fail(MIMO_ERR_VALUE, "the rotated width must be in [0, N/2]");
+    if (q.N % 16 || q.N > 128) return fail(MIMO_ERR_UNSUPPORTED, "N must be a multiple of 16 up to 128 (got %lld)", (long long)q.N);
+    if (q.P % 16 || q.P > 128) return fail(MIMO_ERR_UNSUPPORTED, "P must be a multiple of 16 up to 128 (got %lld)", (long long)q.P);
+    if (q.C > 64) return fail(MIMO_ERR_UNSUPPORTED, "chunk_size above 64 is not supported");
+    if (q.R > 8) return fail(MIMO_ERR_UNSUPPORTED, "R above 8 is not supported");
+    const int Cp = (q.C + 15) / 16 * 16;
+    const int rows = (int)q.R * Cp;
+    if (rows > 128) return fail(MIMO_ERR_UNSUPPORTED, "R * chunk_size (rounded up to 16) above 128 is not supported");
+    if (q.S > (int64_t)1 << 30 || q.B * q.H * ((q.S + q.C - 1) / q.C + 8) > (int64_t)1 << 31)
+        return fail(MIMO_ERR_UNSUPPORTED, "problem too large");
+    pl->MT = rows <= 32 ? 32 : (rows <= 64 ? 64 : 128);
+    pl->NT = tile_size((int)q.N);
+    pl->PT = tile_size((int)q.P);
+    pl->ti = 9 * tidx3(pl->MT) + 3 * tidx3(pl->NT) + tidx3(pl->PT);
+    pl->lds_main = f32::lds32(pl->MT, pl->NT, pl->PT, true).total;
+    pl->lds_agg = f32::lds32(pl->MT, pl->NT, pl->PT, false).total;
+    if (pl->lds_main > 160 * 1024)
+        return fail(MIMO_ERR_UNSUPPORTED,
+                    "the fp32-intermediate kernels need %d bytes of LDS for R*C=%d, N=%lld, P=%lld (limit 163840)",
+                    pl->lds_main, rows, (long long)q.N, (long long)q.P);
+    pl->nc = (int)((q.S + q.C - 1) / q.C);
+    int64_t L = (pl->nc * q.B * q.H + 511) / 512;
+    if (L < 1) L = 1;
+    if (L > pl->nc) L = pl->nc;
+    pl->L = (int)L;
+    pl->nseg = (int)((pl->nc + L - 1) / L);
+    if (pl->nseg > 65535) return fail(MIMO_ERR_UNSUPPORTED, "too many segments");
+    pl->F = (L % 2 == 0 && L >= 4) ? 2 : 1;
+    pl->nsub = (pl->nseg - 1) * pl->F;
+    const bool part = !q.fwd && pl->nseg > 1;
+    size_t off = 0;
+    pl->off_agg = off;
+    if (pl->nseg > 1) off = align256(off + (size_t)q.B * q.H * pl->nsub * q.N * q.P * 4);
+    pl->off_decay = off;
+    if (pl->nseg > 1) off = align256(off + (size_t)q.B * q.H * pl->nsub * 4);
+    pl->off_po = off;
+    if (part && q.reduce_o) off = align256(off + (size_t)q.B * q.H * pl->nseg * q.R * q.P * 4);
+    pl->off_pz = off;
+    if (part && q.has_z) off = align256(off + (size_t)q.B * q.H * pl->nseg * q.R * q.P * 4);
+    pl->ws_bytes = off;
+    return MIMO_OK;
+}
+
+// Queue the fp32 kernels for a filled-in Params (pointers and flags set by the caller).
+mimo_status run32(const Prob32& q, Params& p, void* workspace, size_t workspace_bytes, void* stream,
+                  void* const* events) {
+    Plan32 pl;
+    mimo_status s = make_plan32(q, &pl);
+    if (s != MIMO_OK) return s;
+    if (workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && workspace == nullptr))
+        return fail(MIMO_ERR_VALUE, "workspace too small: need %zu bytes, got %zu", pl.ws_bytes, workspace_bytes);
+    if (pl.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255))
+        return fail(MIMO_ERR_VALUE, "workspace must be 256-byte aligned");
+    if (events != nullptr)
+        for (int i = 0; i < MIMO_TIMED_EVENTS; ++i)
+            if (events[i] == nullptr) return fail(MIMO_ERR_VALUE, "timing event %d is NULL", i);
+    if ((s = check_device()) != MIMO_OK) return s;
+    const f32::F32Set* set = f32::f32_set();
+    const kfn kmain = set->main[q.f16][pl.ti], kagg = set->agg[q.f16][pl.ti];
+    if (kmain == nullptr || kagg == nullptr) return fail(MIMO_ERR_UNSUPPORTED, "no fp32 kernel for this tile shape");
+    p.B = (int)q.B; p.S = (int)q.S; p.H = (int)q.H; p.G = (int)q.G; p.R = (int)q.R; p.N = (int)q.N; p.P = (int)q.P;
+    p.C = q.C; p.W = q.W; p.nc = pl.nc; p.L = pl.L; p.nseg = pl.nseg; p.F = pl.F; p.nsub = pl.nsub;
+    p.reduce_o = q.reduce_o; p.has_z = q.has_z; p.has_d = q.has_d; p.fwd = q.fwd; p.need_y = 1;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    p.agg = pl.nseg > 1 ? reinterpret_cast<float*>(ws + pl.off_agg) : nullptr;
+    p.decay = pl.nseg > 1 ? reinterpret_cast<float*>(ws + pl.off_decay) : nullptr;
+    if (q.fwd) {
+        p.part_o = p.part_z = nullptr;
+    } else if (pl.nseg > 1) {
+        p.part_o = q.reduce_o ? reinterpret_cast<float*>(ws + pl.off_po) : nullptr;
+        p.part_z = q.has_z ? reinterpret_cast<float*>(ws + pl.off_pz) : nullptr;
+    } else {
+        p.part_o = p.dmimo_o;
+        p.part_z = p.dmimo_z;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) -> mimo_status {
+        if (events == nullptr) return MIMO_OK;
+        if (hipEventRecord(static_cast<hipEvent_t>(events[i]), st) != hipSuccess)
+            return fail(MIMO_ERR_HIP, "hipEventRecord failed");
+        return MIMO_OK;
+    };
+    if ((s = set_lds(kmain, pl.lds_main)) != MIMO_OK) return s;
+    if ((s = mark(0)) != MIMO_OK) return s;
+    if (pl.nseg > 1) {
+        if ((s = set_lds(kagg, pl.lds_agg)) != MIMO_OK) return s;
+        if ((s = launch(kagg, dim3(grid_blocks(p, pl.nsub)), dim3(256), pl.lds_agg, st, p)) != MIMO_OK) return s;
+        if ((s = mark(1)) != MIMO_OK) return s;
+        const int NP = p.N * p.P;
+        if ((s = launch(k_scan, dim3((NP + 255) / 256, p.B * p.H), dim3(256), 0, st, p)) != MIMO_OK) return s;
+    } else if ((s = mark(1)) != MIMO_OK) {
+        return s;
+    }
+    if ((s = mark(2)) != MIMO_OK) return s;
+    if ((s = launch(kmain, dim3(grid_blocks(p, pl.nseg)), dim3(256), pl.lds_main, st, p)) != MIMO_OK) return s;
+    if ((s = mark(3)) != MIMO_OK) return s;
+    if (pl.nseg > 1 && !q.fwd && (q.reduce_o || q.has_z)) {
+        const long tot = (long)p.B * p.H * p.R * p.P;
+        if ((s = launch(k_finish, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, p)) != MIMO_OK) return s;
+    }
+    if ((s = mark(4)) != MIMO_OK) return s;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return MIMO_OK;
+}
+
+// The MIMO operator's arguments as an fp32-path problem (bf16 inputs, fp32 controls).
+mimo_status prob_from_mimo(const mimo_bwd_fwd_args* a, bool fwd, Prob32* q) {
+    if (a == nullptr) return fail(MIMO_ERR_VALUE, "args must not be NULL");
+    const int64_t rd = a->rotary_dim_divisor;
+    if (rd != 2 && rd != 4) return fail(MIMO_ERR_VALUE, "rotary_dim_divisor must be 2 or 4");
+    if (a->N < 1 || a->N % rd || a->N % 2) return fail(MIMO_ERR_VALUE, "N must be even and divisible by rotary_dim_divisor");
+    if (a->chunk_size < 1 || (int64_t)a->chunk_size * a->R > 128) return fail(MIMO_ERR_VALUE, "chunk_size * R must be in [1, 128]");
+    if ((a->z == nullptr) != (a->mimo_z == nullptr))
+        return fail(MIMO_ERR_VALUE, "z and mimo_z must either both be present or both be NULL");
+    *q = Prob32{a->B, a->S, a->H, a->G, a->R, a->N, a->P, a->chunk_size, (int)(a->N / rd),
+                a->mimo_o != nullptr, a->z != nullptr, a->d != nullptr, fwd, false};
+    return MIMO_OK;
+}
+
+Params params_from_mimo(const mimo_bwd_fwd_args* a) {
+    Params p = {};
+    p.dout = a->dout; p.q = a->q; p.k = a->k; p.v = a->v; p.z = a->z; p.trap = a->trap;
+    p.q_bias = a->q_bias; p.k_bias = a->k_bias; p.mimo_v = a->mimo_v; p.mimo_o = a->mimo_o;
+    p.mimo_z = a->mimo_z; p.angles = a->angles; p.da_cs = a->da_cs; p.da_cs_rev = a->da_cs_rev;
+    p.dt = a->dt; p.d = a->d; p.segsum = a->segsum;
+    p.dmimo_o = a->dmimo_o; p.dmimo_z = a->dmimo_z; p.states = a->states; p.dz = a->dz; p.qk_dot = a->qk_dot;
+    return p;
+}
+
+mimo_status check_mimo_inputs(const mimo_bwd_fwd_args* a) {
+    if (!a->q || !a->k || !a->v || !a->q_bias || !a->k_bias || !a->mimo_v || !a->angles || !a->da_cs ||
+        !a->da_cs_rev || !a->dt || !a->trap || !a->segsum)
+        return fail(MIMO_ERR_VALUE, "a required input pointer is NULL");
+    return MIMO_OK;
+}
+
+mimo_status run_bwd32(const mimo_bwd_fwd_args* a, void* stream, void* const* events) {
+    g_err.clear();
+    Prob32 q;
+    mimo_status s = prob_from_mimo(a, false, &q);
+    if (s != MIMO_OK) return s;
+    if ((s = check_mimo_inputs(a)) != MIMO_OK) return s;
+    if (!a->dout && (q.reduce_o || q.has_z)) return fail(MIMO_ERR_VALUE, "dout must not be NULL");
+    if (!a->states || !a->qk_dot) return fail(MIMO_ERR_VALUE, "states and qk_dot must not be NULL");
+    if ((a->dmimo_o != nullptr) != q.reduce_o)
+        return fail(MIMO_ERR_VALUE, "dmimo_o must be given exactly when mimo_o is given");
+    if ((a->dz != nullptr) != q.has_z || (a->dmimo_z != nullptr) != q.has_z)
+        return fail(MIMO_ERR_VALUE, "dz and dmimo_z must be given exactly when z is given");
+    Params p = params_from_mimo(a);
+    return run32(q, p, a->workspace, a->workspace_bytes, stream, events);
+}
+
+mimo_status run_fwd32(const mimo_fwd_args* f, void* stream, void* const* events) {
+    g_err.clear();
+    if (f == nullptr) return fail(MIMO_ERR_VALUE, "args must not be NULL");
+    if (f->o == nullptr) return fail(MIMO_ERR_VALUE, "o must not be NULL");
+    const mimo_bwd_fwd_args a = as_bwd_args(f);
+    Prob32 q;
+    mimo_status s = prob_from_mimo(&a, true, &q);
+    if (s != MIMO_OK) return s;
+    if ((s = check_mimo_inputs(&a)) != MIMO_OK) return s;
+    Params p = params_from_mimo(&a);
+    p.o = f->o;
+    return run32(q, p, f->workspace, f->workspace_bytes, stream, events);
+}
+
+mimo_status prob_from_siso(const mimo_siso_fwd_args* a, Prob32* q) {
+    if (a == nullptr) return fail(MIMO_ERR_VALUE, "args must not be NULL");
+    if (a->chunk_size != 32 && a->chunk_size != 64) return fail(MIMO_ERR_VALUE, "chunk_size must be 32 or 64");
+    if (a->Hq < 1 || a->H < 1 || a->H % a->Hq) return fail(MIMO_ERR_VALUE, "H must be divisible by Hq");
+    if (a->A < 0 || a->A % 2 || 2 * a->A > a->K) return fail(MIMO_ERR_VALUE, "the angle width must be even and at most K/2");
+    if (a->dtype != MIMO_DTYPE_BF16 && a->dtype != MIMO_DTYPE_FP16)
+        return fail(MIMO_ERR_TYPE, "q, k, v and z must be bf16 or fp16");
+    *q = Prob32{a->B, a->S, a->H, a->Hq, 1, a->K, a->V, a->chunk_size, (int)a->A,
+                false, a->z != nullptr, a->d != nullptr, true, a->dtype == MIMO_DTYPE_FP16};
+    return MIMO_OK;
+}
+
+mimo_status run_siso(const mimo_siso_fwd_args* a, void* stream, void* const* events) {
+    g_err.clear();
+    Prob32 q;
+    mimo_status s = prob_from_siso(a, &q);
+    if (s != MIMO_OK) return s;
+    if (!a->q || !a->k || !a->v || !a->adt || !a->dt || !a->trap || !a->q_bias || !a->k_bias ||
+        (!a->angles && a->A > 0))
+        return fail(MIMO_ERR_VALUE, "a required input pointer is NULL");
+    if (a->out == nullptr) return fail(MIMO_ERR_VALUE, "out must not be NULL");
+    Params p = {};
+    p.q = a->q; p.k = a->k; p.v = a->v; p.z = a->z;
+    p.q_bias = a->q_bias; p.k_bias = a->k_bias; p.angles = a->angles; p.dt = a->dt; p.d = a->d;
+    p.adt = a->adt; p.trapf = a->trap;
+    p.o = a->out;
+    return run32(q, p, a->workspace, a->workspace_bytes, stream, events);
+}
+
 }  // namespace
 
 extern "C" {
@@ -351,7 +568,7 @@ static mimo_status run(const mimo_bwd_fwd_args* a, uint16_t* out, void* stream, 
     s = check_device();
     if (s != MIMO_OK) return s;
 
-    Params p;
+    Params p = {};
     p.B = (int)a->B; p.S = (int)a->S; p.H = (int)a->H; p.G = (int)a->G;
     p.R = (int)a->R; p.N = (int)a->N; p.P = (int)a->P; p.C = a->chunk_size;
     p.W = pl.W; p.nc = pl.nc; p.L = pl.L; p.nseg = pl.nseg; p.rd = a->rotary_dim_divisor;
@@ -455,6 +672,57 @@ mimo_status mimo_fwd(const mimo_fwd_args* a, void* stream) { return run_fwd(a, s
 mimo_status mimo_fwd_timed(const mimo_fwd_args* a, void* stream, void* const* events) {
     if (events == nullptr) return fail(MIMO_ERR_VALUE, "events must not be NULL");
     return run_fwd(a, stream, events);
+}
+
+mimo_status mimo_bwd_fwd_f32_workspace_size(const mimo_bwd_fwd_args* args, size_t* bytes) {
+    Prob32 q;
+    mimo_status s = prob_from_mimo(args, false, &q);
+    if (s != MIMO_OK) return s;
+    Plan32 pl;
+    if ((s = make_plan32(q, &pl)) != MIMO_OK) return s;
+    if (bytes == nullptr) return fail(MIMO_ERR_VALUE, "bytes must not be NULL");
+    *bytes = pl.ws_bytes;
+    return MIMO_OK;
+}
+
+mimo_status mimo_bwd_fwd_f32(const mimo_bwd_fwd_args* a, void* stream) { return run_bwd32(a, stream, nullptr); }
+
+mimo_status mimo_bwd_fwd_f32_timed(const mimo_bwd_fwd_args* a, void* stream, void* const* events) {
+    if (events == nullptr) return fail(MIMO_ERR_VALUE, "events must not be NULL");
+    return run_bwd32(a, stream, events);
+}
+
+mimo_status mimo_fwd_f32_workspace_size(const mimo_fwd_args* args, size_t* bytes) {
+    if (args == nullptr) return fail(MIMO_ERR_VALUE, "args must not be NULL");
+    const mimo_bwd_fwd_args a = as_bwd_args(args);
+    Prob32 q;
+    mimo_status s = prob_from_mimo(&a, true, &q);
+    if (s != MIMO_OK) return s;
+    Plan32 pl;
+    if ((s = make_plan32(q, &pl)) != MIMO_OK) return s;
+    if (bytes == nullptr) return fail(MIMO_ERR_VALUE, "bytes must not be NULL");
+    *bytes = pl.ws_bytes;
+    return MIMO_OK;
+}
+
+mimo_status mimo_fwd_f32(const mimo_fwd_args* a, void* stream) { return run_fwd32(a, stream, nullptr); }
+
+mimo_status mimo_siso_fwd_workspace_size(const mimo_siso_fwd_args* args, size_t* bytes) {
+    Prob32 q;
+    mimo_status s = prob_from_siso(args, &q);
+    if (s != MIMO_OK) return s;
+    Plan32 pl;
+    if ((s = make_plan32(q, &pl)) != MIMO_OK) return s;
+    if (bytes == nullptr) return fail(MIMO_ERR_VALUE, "bytes must not be NULL");
+    *bytes = pl.ws_bytes;
+    return MIMO_OK;
+}
+
+mimo_status mimo_siso_fwd(const mimo_siso_fwd_args* a, void* stream) { return run_siso(a, stream, nullptr); }
+
+mimo_status mimo_siso_fwd_timed(const mimo_siso_fwd_args* a, void* stream, void* const* events) {
+    if (events == nullptr) return fail(MIMO_ERR_VALUE, "events must not be NULL");
+    return run_siso(a, stream, events);
 }
 
 }  // extern "C"

@@ -1,0 +1,577 @@
+// fp32-intermediate chunk kernels: the same chunked MIMO scan as mimo_kernels.hpp
+// with every intermediate kept in fp32 and the contractions on fp32 MFMA
+// (v_mfma_f32_16x16x4_f32). They serve
+//   * the FP32 variant of the backward first stage (Triton-Ascend
+//     mamba_mimo_bwd_fwd pull request page, FP32 PyTorch reference: no bf16
+//     rounding of any intermediate; outputs cast to their dtypes);
+//   * the SISO forward (mamba3_siso_fwd_kernel migration page, "implementation
+//     principle"): rank 1, unit value and gate projections, controls derived
+//     from the per-token log decay adt, fp16 or bf16 inputs.
+// Inputs q, k, v, z, dout are 16-bit (bf16, or fp16 when in_f16); outputs take
+// the same 16-bit type (round to nearest even).
+//
+// Work split as in the bf16 path: k_chunk32<..., false> computes the state each
+// sub-segment adds from a zero start (k_scan then chains them), k_chunk32<...,
+// true> walks a segment's chunks from its entry state. Rows of a chunk tile are
+// rank-major (i = r*Cp + t). MFMA operands come from LDS with the contraction
+// index split as k = 16*kt + 4*q4 + v over the four accumulator steps v, so a
+// lane reads four consecutive floats of a contraction-contiguous row:
+//   inter = Q^ S       A: sQ[i][n]            B: the state tile in registers
+//   A     = Q^ K~^T    A: sQ[i][n]            B: sK[j][n]
+//   intra = A Psi      A: sA[i][j]            B: sPsi[j][p] (one float per step)
+//   S'    = kappa^T Psi A: sK[i][n]*erev[t]   B: sPsi[i][p] (one float per step)
+// Wave w owns the value tiles pt = w, w+4 (all state rows and all chunk rows of
+// them), so the state a wave reads for the inter term is in its own registers
+// and every rank of a (token, column) meets in one lane for the gating sums.
+#pragma once
+
+#include "mimo_kernels.hpp"
+
+namespace mimo {
+namespace f32 {
+
+template <int MT, int NT, int PT>
+struct Tile32 {
+    static constexpr int NTHR = 256, NW = 4;
+    static constexpr int MTT = MT / 16, NTT = NT / 16, PTT = PT / 16;
+    static constexpr int PW = PTT >= NW ? PTT / NW : 1;   // value tiles per wave
+    static constexpr int CX = MT < 64 ? MT : 64;          // chunk length bound (C <= MT, C <= 64)
+    static constexpr int LQ = NT + 4;                     // row pitch (floats) of sQ, sK
+    static constexpr int LA = MT + 4;                     // row pitch of the causal block
+    static constexpr int LP = PT + 4;                     // row pitch of sPsi
+    static constexpr int AT = (MTT * MTT + NW - 1) / NW;  // causal-block tiles per wave
+};
+
+// LDS layout in bytes (main: with the q tile, the causal block and the tables).
+struct Lds32 {
+    int q, k, psi, se, qk, sc, total;
+};
+__host__ __device__ constexpr Lds32 lds32(int MT, int NT, int PT, bool main) {
+    const int CX = MT < 64 ? MT : 64;
+    // q^, then the causal block, then y's partial sums: the widest of the three rows
+    const int wq = NT > MT ? (NT > PT ? NT : PT) : (MT > PT ? MT : PT);
+    const int qa = main ? 4 * MT * (wq + 4) : 0;
+    Lds32 l{0, 0, 0, 0, 0, 0, 0};
+    int off = 0;
+    l.q = off;
+    off += qa;
+    l.k = off;
+    off += 4 * MT * (NT + 4);
+    l.psi = off;
+    off += 4 * MT * (PT + 4);
+    l.se = off;
+    if (main) off += 4 * CX * (CX + 1);
+    l.qk = off;
+    if (main) off += 4 * MT * 8;
+    l.sc = off;
+    off += 4 * (6 * CX + 4);
+    l.total = off;
+    return l;
+}
+
+template <bool F16>
+__device__ __forceinline__ float ld16(const unsigned short* p, long i) {
+    const unsigned short x = p[i];
+    if constexpr (F16) return static_cast<float>(__builtin_bit_cast(_Float16, x));
+    return __uint_as_float(static_cast<unsigned>(x) << 16);
+}
+template <bool F16>
+__device__ __forceinline__ void ld16x4(const unsigned short* p, long i, float* out) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p + i);
+    const unsigned short h[4] = {static_cast<unsigned short>(w[0]), static_cast<unsigned short>(w[0] >> 16),
+                                 static_cast<unsigned short>(w[1]), static_cast<unsigned short>(w[1] >> 16)};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        if constexpr (F16)
+            out[d] = static_cast<float>(__builtin_bit_cast(_Float16, h[d]));
+        else
+            out[d] = __uint_as_float(static_cast<unsigned>(h[d]) << 16);
+    }
+}
+// fp32 -> 16-bit output, round to nearest even
+template <bool F16>
+__device__ __forceinline__ unsigned short st16(float x) {
+    if constexpr (F16) return __builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
+    return static_cast<unsigned short>(pk2(0.f, x) >> 16);
+}
+
+__device__ __forceinline__ float sig32(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+__device__ __forceinline__ f32x4 mfma32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// MAIN = false: segment aggregate (state increment of a sub-segment from zero and
+// its decay product). MAIN = true: the chunk pass (states, qk_dot, y and the
+// backward's gating outputs, or the layer output when p.fwd).
+template <int MT, int NT, int PT, bool MAIN, bool F16>
+__global__ __launch_bounds__(256, 1) void k_chunk32(Params p) {
+    using T = Tile32<MT, NT, PT>;
+    constexpr int NW = T::NW, NTHR = T::NTHR, LQ = T::LQ, LA = T::LA, LP = T::LP, CX = T::CX;
+    constexpr int MTT = T::MTT, NTT = T::NTT, PTT = T::PTT, PW = T::PW;
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr Lds32 L = lds32(MT, NT, PT, MAIN);
+    float* sQ = reinterpret_cast<float*>(smem + L.q);   // q^ [MT][LQ], then the causal block [MT][LA],
+    float* sA = sQ;                                       // then y's partial sums [MT][LP]
+    float* sY = sQ;
+    float* sK = reinterpret_cast<float*>(smem + L.k);     // k0, then K~ [MT][LQ]
+    float* sPsi = reinterpret_cast<float*>(smem + L.psi); // Psi [MT][LP]
+    float* sE = reinterpret_cast<float*>(smem + L.se);    // exp(segsum) [CX][CX+1]
+    float* sQK = reinterpret_cast<float*>(smem + L.qk);   // same-token dots [C][R][R]
+    float* sc = reinterpret_cast<float*>(smem + L.sc);    // gamma, factor, ecs, erev, cs [CX] each; dl
+    float* sGam = sc;
+    float* sFac = sc + CX;
+    float* sEcs = sc + 2 * CX;
+    float* sRev = sc + 3 * CX;
+    float* sCs = sc + 4 * CX;
+    float* sDl = sc + 6 * CX;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+    const int l16 = lane & 15, q4 = lane >> 4;
+    int seg, bh;
+    if (!map_block(p, MAIN ? p.nseg : p.nsub, seg, bh)) return;
+    seg = uni(seg);
+    bh = uni(bh);
+    const int b = uni(bh / p.H), h = uni(bh - b * p.H);
+    const int g = uni(h / (p.H / p.G));
+    const int R = p.R, N = p.N, P = p.P, C = p.C, W = p.W, M = p.N / 2;
+    const int Cp = (C + 15) / 16 * 16, CT = Cp / 16;
+    int c_begin, c_end;
+    if constexpr (MAIN) {
+        c_begin = seg * p.L;
+        c_end = min(c_begin + p.L, p.nc);
+    } else {
+        const int La = p.L / p.F;
+        c_begin = seg * La;
+        c_end = c_begin + La;
+    }
+    const long tokb = (long)bh * p.S;   // [B,H,S] row of this (batch, head)
+
+    // ---- state entering the segment: wave w holds S[16nt + 4q4 + v][16pt + l16]
+    // for its value tiles pt = w + NW*j (all nt)
+    f32x4 S[PW][NTT];
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+        const int pt = wave + NW * j;
+#pragma unroll
+        for (int nt = 0; nt < NTT; ++nt) {
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+            if (MAIN && seg > 0 && pt < PTT) {
+                const float* E = p.agg + ((long)bh * p.nsub + seg * p.F - 1) * N * P;
+                const int pc = 16 * pt + l16;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int n = 16 * nt + 4 * q4 + v;
+                    if (n < N && pc < P) s[v] = E[n * P + pc];
+                }
+            }
+            S[j][nt] = s;
+        }
+    }
+    // per-lane projections of this wave's columns, per rank
+    float cz[PW][8], co[PW][8], dmo[PW][8], dmz[PW][8];
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+        const int pc = 16 * (wave + NW * j) + l16;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            cz[j][r] = co[j][r] = dmo[j][r] = dmz[j][r] = 0.f;
+            if (MAIN && r < R && pc < P && wave + NW * j < PTT) {
+                if (p.has_z) cz[j][r] = p.mimo_z ? p.mimo_z[((long)h * R + r) * P + pc] : 1.0f;
+                if (p.reduce_o) co[j][r] = p.mimo_o[((long)h * R + r) * P + pc];
+            }
+        }
+    }
+    const float dval = (MAIN && p.has_d) ? p.d[h] : 0.f;
+    float dprod = 1.f;
+
+    for (int c = c_begin; c < c_end; ++c) {
+        const int c0 = c * C;
+        const int cl = min(C, p.S - c0);
+
+        // ---- states[c] = S entering chunk c, in the output type
+        if constexpr (MAIN) {
+            if (!p.fwd) {
+                unsigned short* dst = p.states + ((long)bh * p.nc + c) * N * P;
+#pragma unroll
+                for (int j = 0; j < PW; ++j) {
+                    const int pc = 16 * (wave + NW * j) + l16;
+                    if (wave + NW * j < PTT && pc < P) {
+#pragma unroll
+                        for (int nt = 0; nt < NTT; ++nt)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const int n = 16 * nt + 4 * q4 + v;
+                                if (n < N) dst[n * P + pc] = st16<F16>(S[j][nt][v]);
+                            }
+                    }
+                }
+            }
+        }
+
+        // ---- token scalars of the chunk (wave 0, lane t = token)
+        if (wave == 0) {
+            const int t = lane;
+            float cs = 0.f, rev = 0.f;
+            if (p.adt != nullptr) {
+                // chunk-local inclusive cumulative sum of the log decay
+                float a = (t < cl) ? p.adt[tokb + c0 + t] : 0.f;
+#pragma unroll
+                for (int o = 1; o < 64; o *= 2) {
+                    const float u = __shfl_up(a, o);
+                    if (lane >= o) a += u;
+                }
+                const float last = __shfl(a, cl - 1);
+                cs = a;
+                rev = last - a;
+            } else if (t < cl) {
+                cs = p.da_cs[tokb + c0 + t];
+                rev = p.da_cs_rev[tokb + c0 + t];
+            }
+            if (t < CX) {
+                float gam = 0.f, fac = 0.f;
+                if (t < cl) {
+                    const long T0 = tokb + c0 + t;
+                    const float tr0 = p.trapf ? p.trapf[T0] : bf2f(p.trap[T0]);
+                    gam = p.dt[T0] * sig32(tr0);
+                    float beta = 0.f;
+                    if (c0 + t + 1 < p.S) {
+                        const float tr1 = p.trapf ? p.trapf[T0 + 1] : bf2f(p.trap[T0 + 1]);
+                        beta = p.dt[T0 + 1] * (1.0f - sig32(tr1));
+                    }
+                    fac = gam + beta;
+                }
+                sGam[t] = gam;
+                sFac[t] = fac;
+                sEcs[t] = (t < cl) ? expf(cs) : 0.f;
+                sRev[t] = (t < cl) ? expf(rev) : 0.f;
+                sCs[t] = cs;
+                if (t == cl - 1) sDl[0] = expf(cs);
+            }
+        }
+
+        // ---- q0, k0 (biased, unrotated) and Psi into LDS; zero outside the problem
+        constexpr int N4 = NT / 4, P4 = PT / 4;
+        for (int e = tid; e < MT * N4; e += NTHR) {
+            const int i = e / N4, n = 4 * (e % N4);
+            const int r = i / Cp, t = i % Cp;
+            float qv[4] = {0.f, 0.f, 0.f, 0.f}, kv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (r < R && t < cl && n < N) {
+                const long src = (((long)(b * p.S + c0 + t) * R + r) * p.G + g) * N + n;
+                ld16x4<F16>(p.k, src, kv);
+                const float* kb = p.k_bias + ((long)h * R + r) * N + n;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) kv[d] += kb[d];
+                if (MAIN) {
+                    ld16x4<F16>(p.q, src, qv);
+                    const float* qb = p.q_bias + ((long)h * R + r) * N + n;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) qv[d] += qb[d];
+                }
+            }
+            *reinterpret_cast<f32x4*>(sK + i * LQ + n) = f32x4{kv[0], kv[1], kv[2], kv[3]};
+            if (MAIN) *reinterpret_cast<f32x4*>(sQ + i * LQ + n) = f32x4{qv[0], qv[1], qv[2], qv[3]};
+        }
+        for (int e = tid; e < MT * P4; e += NTHR) {
+            const int i = e / P4, pc = 4 * (e % P4);
+            const int r = i / Cp, t = i % Cp;
+            float x[4] = {0.f, 0.f, 0.f, 0.f};
+            if (r < R && t < cl && pc < P) {
+                ld16x4<F16>(p.v, ((long)(b * p.S + c0 + t) * p.H + h) * P + pc, x);
+                if (p.mimo_v) {
+                    const float* mv = p.mimo_v + ((long)h * R + r) * P + pc;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) x[d] *= mv[d];
+                }
+            }
+            *reinterpret_cast<f32x4*>(sPsi + i * LP + pc) = f32x4{x[0], x[1], x[2], x[3]};
+        }
+        __syncthreads();
+
+        // ---- same-token dots of the unrotated q, k (qk_dot) and exp(segsum)
+        if constexpr (MAIN) {
+            const int RR = R * R;
+            for (int e = tid; e < cl * RR; e += NTHR) {
+                const int t = e / RR, r = (e % RR) / R, r2 = e % R;
+                const float* x = sQ + (r * Cp + t) * LQ;
+                const float* y = sK + (r2 * Cp + t) * LQ;
+                float s = 0.f;
+                for (int n = 0; n < N; n += 4) {
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(x + n);
+                    const f32x4 bb = *reinterpret_cast<const f32x4*>(y + n);
+                    s = __fmaf_rn(a[0], bb[0], s);
+                    s = __fmaf_rn(a[1], bb[1], s);
+                    s = __fmaf_rn(a[2], bb[2], s);
+                    s = __fmaf_rn(a[3], bb[3], s);
+                }
+                sQK[e] = s;
+                if (!p.fwd) p.qk_dot[((long)bh * p.S + c0 + t) * RR + r * R + r2] = st16<F16>(s);
+            }
+            for (int e = tid; e < cl * cl; e += NTHR) {
+                const int t = e / cl, s2 = e % cl;
+                if (s2 < t) {
+                    float sg;
+                    if (p.adt != nullptr)
+                        sg = sCs[t] - sCs[s2];
+                    else
+                        sg = p.segsum[(((long)bh * p.nc + c) * C + t) * C + s2];
+                    sE[t * (CX + 1) + s2] = expf(sg);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- rotation of q and k (pairs n, N/2 + n for n < W) and K~ = k * factor
+        for (int e = tid; e < Cp * (NT / 2); e += NTHR) {
+            const int t = e / (NT / 2), n = e % (NT / 2);
+            if (t >= cl || n >= M) continue;
+            const float f = sFac[t];
+            float cn = 1.f, sn = 0.f;
+            if (n < W) sin_cos(p.angles[((long)(b * p.S + c0 + t) * p.H + h) * W + n], sn, cn);
+            for (int r = 0; r < R; ++r) {
+                float* kr = sK + (r * Cp + t) * LQ;
+                const float ka = kr[n], ke = kr[M + n];
+                kr[n] = (cn * ka - sn * ke) * f;
+                kr[M + n] = (sn * ka + cn * ke) * f;
+                if (MAIN) {
+                    float* qr = sQ + (r * Cp + t) * LQ;
+                    const float qa = qr[n], qe = qr[M + n];
+                    qr[n] = cn * qa - sn * qe;
+                    qr[M + n] = sn * qa + cn * qe;
+                }
+            }
+        }
+        __syncthreads();
+
+        f32x4 acc[PW][MTT];
+        if constexpr (MAIN) {
+            // ---- inter = Q^ S, rows scaled by exp(da_cs[t])
+#pragma unroll
+            for (int j = 0; j < PW; ++j) {
+                const bool own = wave + NW * j < PTT;
+#pragma unroll
+                for (int it = 0; it < MTT; ++it) {
+                    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+                    if (own && (it / CT) < R) {
+#pragma unroll
+                        for (int nt = 0; nt < NTT; ++nt) {
+                            const f32x4 qa = *reinterpret_cast<const f32x4*>(sQ + (16 * it + l16) * LQ + 16 * nt + 4 * q4);
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) a4 = mfma32(qa[v], S[j][nt][v], a4);
+                        }
+                        const int tb = 16 * (it % CT) + 4 * q4;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) a4[v] *= (tb + v < CX) ? sEcs[tb + v] : 0.f;
+                    }
+                    acc[j][it] = a4;
+                }
+            }
+            // ---- causal block A[i][j] = exp(segsum) * (Q^ K~^T)[i][j] for token(j) < token(i)
+            f32x4 at[T::AT];
+#pragma unroll
+            for (int w = 0; w < T::AT; ++w) {
+                const int u = wave + NW * w;
+                const int it = u / MTT, jt = u % MTT;
+                f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+                if (u < MTT * MTT && it / CT < R && jt / CT < R && (jt % CT) <= (it % CT)) {
+#pragma unroll
+                    for (int nt = 0; nt < NTT; ++nt) {
+                        const f32x4 qa = *reinterpret_cast<const f32x4*>(sQ + (16 * it + l16) * LQ + 16 * nt + 4 * q4);
+                        const f32x4 kb = *reinterpret_cast<const f32x4*>(sK + (16 * jt + l16) * LQ + 16 * nt + 4 * q4);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) a4 = mfma32(qa[v], kb[v], a4);
+                    }
+                    // lane holds rows 4q4+v of tile it, column l16 of tile jt
+                    const int tj = 16 * (jt % CT) + l16;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int ti = 16 * (it % CT) + 4 * q4 + v;
+                        a4[v] = (ti < cl && tj < ti) ? a4[v] * sE[ti * (CX + 1) + tj] : 0.f;
+                    }
+                }
+                at[w] = a4;
+            }
+            __syncthreads();   // every wave is done reading sQ
+#pragma unroll
+            for (int w = 0; w < T::AT; ++w) {
+                const int u = wave + NW * w;
+                if (u < MTT * MTT) {
+                    const int it = u / MTT, jt = u % MTT;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) sA[(16 * it + 4 * q4 + v) * LA + 16 * jt + l16] = at[w][v];
+                }
+            }
+            __syncthreads();
+            // ---- intra = A Psi onto the scaled inter term
+#pragma unroll
+            for (int j = 0; j < PW; ++j) {
+                const int pt = wave + NW * j;
+                if (pt >= PTT) continue;
+#pragma unroll
+                for (int it = 0; it < MTT; ++it) {
+                    if (it / CT >= R) continue;
+                    f32x4 a4 = acc[j][it];
+                    for (int jt = 0; jt < MTT; ++jt) {
+                        if (jt / CT >= R || (jt % CT) > (it % CT)) continue;
+                        const f32x4 aa = *reinterpret_cast<const f32x4*>(sA + (16 * it + l16) * LA + 16 * jt + 4 * q4);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            a4 = mfma32(aa[v], sPsi[(16 * jt + 4 * q4 + v) * LP + 16 * pt + l16], a4);
+                    }
+                    acc[j][it] = a4;
+                }
+            }
+        }
+
+        // ---- state update S <- S * exp(da_cs[last]) + kappa^T Psi, kappa = K~ * exp(da_cs_rev)
+        {
+            const float dl = sDl[0];
+#pragma unroll
+            for (int j = 0; j < PW; ++j) {
+                const int pt = wave + NW * j;
+                if (pt >= PTT) continue;
+#pragma unroll
+                for (int nt = 0; nt < NTT; ++nt) {
+                    f32x4 a4 = S[j][nt] * dl;
+                    for (int it = 0; it < MTT; ++it) {
+                        if (it / CT >= R) continue;
+                        const int tb = 16 * (it % CT) + 4 * q4;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int row = 16 * it + 4 * q4 + v;
+                            const float er = (tb + v < CX) ? sRev[tb + v] : 0.f;
+                            a4 = mfma32(sK[row * LQ + 16 * nt + l16] * er, sPsi[row * LP + 16 * pt + l16], a4);
+                        }
+                    }
+                    S[j][nt] = a4;
+                }
+            }
+            dprod *= dl;
+        }
+
+        if constexpr (MAIN) {
+            // ---- y's partial sums (inter + intra) through LDS, so that the epilogue
+            // can address them by run-time rank and token
+            __syncthreads();   // every wave is done reading the causal block
+#pragma unroll
+            for (int j = 0; j < PW; ++j) {
+                const int pt = wave + NW * j;
+                if (pt >= PTT) continue;
+#pragma unroll
+                for (int it = 0; it < MTT; ++it) {
+                    if (it / CT >= R) continue;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) sY[(16 * it + 4 * q4 + v) * LP + 16 * pt + l16] = acc[j][it][v];
+                }
+            }
+            // ---- y = inter + intra + gamma * sum_r2 qk[r][r2] Psi[r2] + d * Psi, then the
+            // gating outputs (backward) or the layer output (forward). A lane reads back
+            // only what it wrote itself.
+            const int RR = R * R;
+#pragma unroll
+            for (int j = 0; j < PW; ++j) {
+                const int pt = wave + NW * j;
+                const int pc = 16 * pt + l16;
+                if (pt >= PTT || pc >= P) continue;
+                for (int tt = 0; tt < CT; ++tt) {
+                    for (int v = 0; v < 4; ++v) {
+                        const int t = 16 * tt + 4 * q4 + v;
+                        if (t >= cl) continue;
+                        const long ivp = ((long)(b * p.S + c0 + t) * p.H + h) * P + pc;
+                        const float gam = sGam[t];
+                        float zr = 0.f, dv = 0.f;
+                        if (p.has_z) zr = ld16<F16>(p.z, ivp);
+                        if (!p.fwd && p.reduce_o) dv = ld16<F16>(p.dout, ivp);
+                        float dzs = 0.f, osum = 0.f;
+#pragma unroll
+                        for (int r = 0; r < 8; ++r) {
+                            if (r >= R) break;
+                            float dg = 0.f;
+                            for (int r2 = 0; r2 < R; ++r2)
+                                dg = __fmaf_rn(sQK[t * RR + r * R + r2], sPsi[(r2 * Cp + t) * LP + pc], dg);
+                            const int row = r * Cp + t;
+                            const float y = sY[row * LP + pc] + gam * dg + dval * sPsi[row * LP + pc];
+                            float pz = 0.f, sg = 0.f, silu = 1.f;
+                            if (p.has_z) {
+                                pz = zr * cz[j][r];
+                                sg = sig32(pz);
+                                silu = pz * sg;
+                            }
+                            if (p.fwd) {
+                                if (p.reduce_o) {
+                                    osum += co[j][r] * y * silu;
+                                } else {
+                                    const long oi = ((long)(b * p.S + c0 + t) * R + r) * p.H * P + (long)h * P + pc;
+                                    p.o[oi] = st16<F16>(y * silu);
+                                }
+                                continue;
+                            }
+                            float G = 0.f;
+                            if (p.reduce_o) {
+                                dmo[j][r] += y * silu * dv;
+                                G = dv * co[j][r] * y;
+                            } else if (p.has_z) {
+                                const long di = ((long)(b * p.S + c0 + t) * R + r) * p.H * P + (long)h * P + pc;
+                                G = ld16<F16>(p.dout, di) * y;
+                            }
+                            if (p.has_z) {
+                                const float gz = G * sg * (1.0f + pz * (1.0f - sg));
+                                dzs += gz * cz[j][r];
+                                dmz[j][r] += gz * zr;
+                            }
+                        }
+                        if (p.fwd && p.reduce_o) p.o[ivp] = st16<F16>(osum);
+                        if (!p.fwd && p.has_z) p.dz[ivp] = st16<F16>(dzs);
+                    }
+                }
+            }
+        }
+        __syncthreads();   // the next chunk overwrites the tiles and tables
+    }
+
+    if constexpr (!MAIN) {
+        float* out = p.agg + ((long)bh * p.nsub + seg) * N * P;
+#pragma unroll
+        for (int j = 0; j < PW; ++j) {
+            const int pc = 16 * (wave + NW * j) + l16;
+            if (wave + NW * j >= PTT || pc >= P) continue;
+#pragma unroll
+            for (int nt = 0; nt < NTT; ++nt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int n = 16 * nt + 4 * q4 + v;
+                    if (n < N) out[n * P + pc] = S[j][nt][v];
+                }
+        }
+        if (tid == 0) p.decay[(long)bh * p.nsub + seg] = dprod;
+    } else if (!p.fwd && (p.reduce_o || p.has_z)) {
+        // per-segment partial sums of dmimo_o / dmimo_z over this lane group's tokens
+#pragma unroll
+        for (int j = 0; j < PW; ++j) {
+            const int pc = 16 * (wave + NW * j) + l16;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                float so = dmo[j][r], sz = dmz[j][r];
+                so += __shfl_xor(so, 16);
+                so += __shfl_xor(so, 32);
+                sz += __shfl_xor(sz, 16);
+                sz += __shfl_xor(sz, 32);
+                if (q4 == 0 && r < R && wave + NW * j < PTT && pc < P) {
+                    const long o = ((long)bh * p.nseg + seg) * R * P + (long)r * P + pc;
+                    if (p.reduce_o) p.part_o[o] = so;
+                    if (p.has_z) p.part_z[o] = sz;
+                }
+            }
+        }
+    }
+}
+
+// Kernel table: [bf16 = 0 / fp16 = 1][9 * idx(MT) + 3 * idx(NT) + idx(PT)] with
+// idx(32, 64, 128) = 0, 1, 2; nullptr where the tile's LDS does not fit.
+struct F32Set {
+    kfn agg[2][27], main[2][27];
+};
+const F32Set* f32_set();
+
+}  // namespace f32
+}  // namespace mimo

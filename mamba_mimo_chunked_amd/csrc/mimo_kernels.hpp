@@ -120,6 +120,10 @@ struct Params {
     float *dmimo_o, *dmimo_z;
     unsigned short *states, *dz, *qk_dot;
     unsigned short* o;   // layer output: [B,S,H,P] when reduce_o, else [B,S,R,H,P]
+    // fp32-intermediate kernels only: per-token log decay [B,H,S] from which the
+    // chunk controls are derived (nullptr: da_cs, da_cs_rev, segsum are given), and
+    // an fp32 trap [B,H,S] used instead of the bf16 one when not nullptr
+    const float *adt, *trapf;
     float* agg;     // [B*H][nsub][N*P]: sub-segment state increments, then the states after each
     float* decay;   // [B*H][nsub]: product of the chunk decays of each sub-segment
     float* part_o;  // [B*H][nseg][R*P] partial dmimo_o (== dmimo_o when nseg == 1)

@@ -234,7 +234,7 @@ class SisoCase:
     K: int
     V: int
     C: int = 64
-    A: int = 0                 # rotated pairs; 0 = K // 2
+    A: int = -1                # rotated pairs; -1 = K // 2
     dtype: str = "bf16"        # "bf16" or "fp16" for q, k, v, z
     has_z: bool = True
     has_d: bool = True
@@ -243,7 +243,7 @@ class SisoCase:
 
     @property
     def width(self) -> int:
-        return self.A or self.K // 2
+        return self.K // 2 if self.A < 0 else self.A
 
     def with_(self, **kw) -> "SisoCase":
         return replace(self, **kw)
