@@ -10,8 +10,12 @@ Several input/output buffer sets are used in turn so that the data of one
 call is not still sitting in the 256 MB Infinity Cache from the previous
 call: the figures are device-memory (HBM) figures.
 
-``--op fwd`` times the layer output ``mamba_mimo_fwd`` (the forward whose
-gradients the backward stage computes) on the same workload instead.
+Other operations (``--op``), each on its own workload line:
+  fwd           the layer output mamba_mimo_fwd (the forward whose gradients the
+                backward stage computes), same workload;
+  bwd_fwd_fp32  the backward stage with fp32 intermediates, same workload;
+  siso          the SISO forward mamba3_siso_fwd, B=1, S=8192, H=Hq=16, K=128,
+                V=64, chunk 64, bf16 (--config siso_s8192_k128_fp16 for fp16).
 
 Prints progress on stderr and ONE JSON line on stdout.
 """
@@ -33,6 +37,9 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "mimo_bwd_fwd ms/call + HBM GB/s at B1 S8192 H16 G1 N=P=64 R4 C16"
 FWD_METRIC = "mimo_fwd (layer output) ms/call + HBM GB/s at B1 S8192 H16 G1 N=P=64 R4 C16"
+FP32_METRIC = "mimo_bwd_fwd_fp32 (fp32 intermediates) ms/call + HBM GB/s at B1 S8192 H16 G1 N=P=64 R4 C16"
+SISO_METRIC = "mamba3_siso_fwd ms/call + HBM GB/s at B1 S8192 H=Hq=16 K128 V64 C64"
+MFMA_FP32_PEAK_TFLOPS = 157.3
 PAGES_MS = 53.849475          # the pages' Ascend910_9382 median at this exact workload (context)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -44,8 +51,11 @@ ALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
 ALU_NONPACKED_TOPS = ALU_PEAK_TOPS / 2
 
 KERNEL_SOURCES = [ROOT / "mamba_mimo_chunked_amd" / "csrc" / n for n in ("mimo_kernels.hpp", "mimo_bwd_fwd.hip")]
+KERNEL_SOURCES += [ROOT / "mamba_mimo_chunked_amd" / "csrc" / "mimo_f32.hpp"]
 TRAFFIC_FILES = {"bwd_fwd": ROOT / "profiles" / "k_main_perf_s8192_traffic.json",
-                 "fwd": ROOT / "profiles" / "k_main_fwd_perf_s8192_traffic.json"}
+                 "fwd": ROOT / "profiles" / "k_main_fwd_perf_s8192_traffic.json",
+                 "bwd_fwd_fp32": ROOT / "profiles" / "k_chunk32_perf_s8192_traffic.json",
+                 "siso": ROOT / "profiles" / "k_chunk32_siso_s8192_k128_traffic.json"}
 
 
 def log(msg):
@@ -169,28 +179,60 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
+def siso_bytes(c) -> int:
+    """Algorithmic bytes of the SISO forward: every input once, the output once."""
+    B, S, Hq, H, K, V, A = c.B, c.S, c.Hq, c.H, c.K, c.V, c.width
+    b = 2 * B * S * Hq * K * 2 + B * S * H * V * 2 * (2 if c.has_z else 1)   # q, k, v, z
+    b += 3 * B * H * S * 4 + 2 * H * K * 4 + B * S * H * A * 4 + (H * 4 if c.has_d else 0)
+    return b + B * S * H * V * 2                                                # out
+
+
+def siso_flops(c) -> int:
+    """Multiply-adds (x2) of the SISO forward (the rank-1 case of algorithmic_flops)."""
+    B, S, H, K, V, C = c.B, c.S, c.H, c.K, c.V, c.C
+    full, tail = S // C, S - (S // C) * C
+    pairs = full * C * (C - 1) // 2 + tail * (tail - 1) // 2
+    f = 2 * S * K + 2 * S * K * V + pairs * 2 * (K + V) + 2 * S * K * V + 2 * S * V
+    return B * H * f
+
+
+def siso_alu_ops(c) -> int:
+    """Elementwise fp32 operations of the SISO forward per token and head: bias of q, k
+    (2K), rotation (8A + 2A sin/cos), factor scale of k (K), the decay weights of the
+    strictly causal pairs (2 per pair), the inter scale (V), y assembly (4V), and with z
+    the gate (sigmoid, SiLU, product: 4V)."""
+    B, S, H, K, V, C, A = c.B, c.S, c.H, c.K, c.V, c.C, c.width
+    full, tail = S // C, S - (S // C) * C
+    pairs = full * C * (C - 1) // 2 + tail * (tail - 1) // 2
+    per_tok = 2 * K + 10 * A + K + V + 4 * V + (4 * V if c.has_z else 0)
+    return B * H * (S * per_tok + 2 * pairs)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="perf_s8192", help="workload name from synth.inputs.CONFIGS")
+    ap.add_argument("--config", default=None,
+                    help="workload name (synth.inputs.CONFIGS; SISO_CONFIGS for --op siso)")
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: enough for > 512 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--mode", choices=("op", "copy"), default="op",
                     help="copy: a plain device copy of known size, for counter calibration")
-    ap.add_argument("--op", choices=("bwd_fwd", "fwd"), default="bwd_fwd",
-                    help="fwd: time the layer output mamba_mimo_fwd instead of the backward stage")
+    ap.add_argument("--op", choices=("bwd_fwd", "fwd", "bwd_fwd_fp32", "siso"), default="bwd_fwd",
+                    help="operation to time (default: the backward first stage)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    if a.config is None:
+        a.config = "siso_s8192_k128" if a.op == "siso" else "perf_s8192"
 
     import torch
-    from mamba_mimo_chunked_amd import _lib, mamba_mimo_bwd_fwd
-    from mamba_mimo_chunked_amd.api import _make_args, _make_fwd_args
-    from synth.inputs import API_ORDER, CONFIGS, make_inputs
+    from mamba_mimo_chunked_amd import _lib
+    from mamba_mimo_chunked_amd.api import _make_args, _make_fwd_args, _make_siso_args
+    from synth.inputs import API_ORDER, CONFIGS, SISO_CONFIGS, SISO_ORDER, make_inputs, make_siso_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -214,41 +256,72 @@ def main():
                           "GBps": 8 * n / ms / 1e6}))
         return
 
-    case = CONFIGS[a.config]
-    log(f"workload {a.config}: {case}")
+    op = a.op
+    siso_op = op == "siso"
+    case = SISO_CONFIGS[a.config] if siso_op else CONFIGS[a.config]
+    log(f"op {op}, workload {a.config}: {case}")
     t = time.perf_counter()
-    inp = make_inputs(case)
+    inp = make_siso_inputs(case) if siso_op else make_inputs(case)
     log(f"inputs generated in {time.perf_counter() - t:.1f}s")
-    fwd = a.op == "fwd"
-    alg_bytes = algorithmic_bytes(case, fwd)
-    alg_flops = algorithmic_flops(case, fwd)
-    nsets = a.sets or max(2, math.ceil(512e6 / alg_bytes))
-    B, S, H, G, R, N, P, C = case.B, case.S, case.H, case.G, case.R, case.N, case.P, case.C
-    nc = case.nchunks
-    sets = []
-    for _ in range(nsets):
-        d = {n: (None if inp[n] is None or (fwd and n == "dout") else inp[n].to(dev)) for n in API_ORDER}
-        if fwd:
-            oshape = (B, S, H, P) if case.reduce_o else (B, S, R, H, P)
-            sets.append((d, torch.empty(oshape, device=dev, dtype=torch.bfloat16)))
-            continue
-        out = {
-            "dmimo_o": torch.empty((B, H, R, P), device=dev) if case.reduce_o else None,
-            "states": torch.empty((B, H, nc, N, P), device=dev, dtype=torch.bfloat16),
-            "dz": torch.empty((B, S, H, P), device=dev, dtype=torch.bfloat16) if case.has_z else None,
-            "dmimo_z": torch.empty((B, H, R, P), device=dev) if case.has_z else None,
-            "qk_dot": torch.empty((B, H, S, R, R), device=dev, dtype=torch.bfloat16),
-        }
-        sets.append((d, out))
-    from mamba_mimo_chunked_amd import fwd_workspace_size, workspace_size
-    wsf = fwd_workspace_size if fwd else workspace_size
-    ws_bytes = wsf(B, S, H, G, R, N, P, C, case.rd, reduce_o=case.reduce_o, has_z=case.has_z)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     L = _lib.lib()
-    mk = _make_fwd_args if fwd else _make_args
-    cargs = [mk(B, S, H, G, R, N, P, C, case.rd, d, out, ws, ws_bytes) for d, out in sets]
-    run_call = L.mimo_fwd if fwd else L.mimo_bwd_fwd
-    run_timed = L.mimo_fwd_timed if fwd else L.mimo_bwd_fwd_timed
+    if siso_op:
+        alg_bytes, alg_flops, alu_ops = siso_bytes(case), siso_flops(case), siso_alu_ops(case)
+        mfma_peak, mfma_unit_dtype = MFMA_FP32_PEAK_TFLOPS, "fp32"
+    else:
+        fwd = op == "fwd"
+        alg_bytes, alg_flops = algorithmic_bytes(case, fwd), algorithmic_flops(case, fwd)
+        alu_ops = algorithmic_alu_ops(case, fwd)
+        fp32 = op == "bwd_fwd_fp32"
+        mfma_peak = MFMA_FP32_PEAK_TFLOPS if fp32 else MFMA_BF16_PEAK_TFLOPS
+        mfma_unit_dtype = "fp32" if fp32 else "bf16"
+    nsets = a.sets or max(2, math.ceil(512e6 / alg_bytes))
+
+    # ---- buffer sets and argument structs
+    sets = []
+    if siso_op:
+        B, S, H, V = case.B, case.S, case.H, case.V
+        dims = (case.B, case.S, case.Hq, case.H, case.K, case.V, case.width, case.C)
+        odt = torch.float16 if case.dtype == "fp16" else torch.bfloat16
+        for _ in range(nsets):
+            d = {n: (None if inp[n] is None else inp[n].to(dev)) for n in SISO_ORDER}
+            sets.append((d, torch.empty((B, S, H, V), device=dev, dtype=odt)))
+        probe = _make_siso_args(dims, odt, sets[0][0], sets[0][1])
+        nbytes = ctypes.c_size_t(0)
+        st = L.mimo_siso_fwd_workspace_size(ctypes.byref(probe), ctypes.byref(nbytes))
+        if st != 0:
+            raise RuntimeError(_lib.last_error())
+        ws_bytes = int(nbytes.value)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        cargs = [_make_siso_args(dims, odt, d, o, ws, ws_bytes) for d, o in sets]
+        run_call, run_timed = L.mimo_siso_fwd, L.mimo_siso_fwd_timed
+    else:
+        B, S, H, G, R, N, P, C = case.B, case.S, case.H, case.G, case.R, case.N, case.P, case.C
+        nc = case.nchunks
+        for _ in range(nsets):
+            d = {n: (None if inp[n] is None or (fwd and n == "dout") else inp[n].to(dev)) for n in API_ORDER}
+            if fwd:
+                oshape = (B, S, H, P) if case.reduce_o else (B, S, R, H, P)
+                sets.append((d, torch.empty(oshape, device=dev, dtype=torch.bfloat16)))
+                continue
+            out = {
+                "dmimo_o": torch.empty((B, H, R, P), device=dev) if case.reduce_o else None,
+                "states": torch.empty((B, H, nc, N, P), device=dev, dtype=torch.bfloat16),
+                "dz": torch.empty((B, S, H, P), device=dev, dtype=torch.bfloat16) if case.has_z else None,
+                "dmimo_z": torch.empty((B, H, R, P), device=dev) if case.has_z else None,
+                "qk_dot": torch.empty((B, H, S, R, R), device=dev, dtype=torch.bfloat16),
+            }
+            sets.append((d, out))
+        fn = {"bwd_fwd": "mimo_bwd_fwd", "fwd": "mimo_fwd", "bwd_fwd_fp32": "mimo_bwd_fwd_f32"}[op]
+        mk = _make_fwd_args if fwd else _make_args
+        probe = mk(B, S, H, G, R, N, P, C, case.rd, sets[0][0], sets[0][1])
+        nbytes = ctypes.c_size_t(0)
+        st = getattr(L, fn + "_workspace_size")(ctypes.byref(probe), ctypes.byref(nbytes))
+        if st != 0:
+            raise RuntimeError(_lib.last_error())
+        ws_bytes = int(nbytes.value)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        cargs = [mk(B, S, H, G, R, N, P, C, case.rd, d, out, ws, ws_bytes) for d, out in sets]
+        run_call, run_timed = getattr(L, fn), getattr(L, fn + "_timed")
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def call(i):
@@ -276,7 +349,10 @@ def main():
         if st != 0:
             raise RuntimeError(_lib.last_error())
     torch.cuda.synchronize()
+    f32_names = op in ("bwd_fwd_fp32", "siso")
     names = ("k_agg", "k_scan", "k_main", "k_finish")
+    if f32_names:
+        names = ("k_chunk32_agg", "k_scan", "k_chunk32_main", "k_finish")
     per = {n: 0.0 for n in names}
     for e in evs:
         for j, n in enumerate(names):
@@ -284,48 +360,72 @@ def main():
         hip.destroy(e)
     log("per-kernel ms: " + ", ".join(f"{n}={v:.4f}" for n, v in per.items()))
 
-    main_ms = per["k_main"]
-    alu_ops = algorithmic_alu_ops(case, fwd)
+    main_name = names[2]
+    main_ms = per[main_name]
     hbm_gbps_main = alg_bytes / (main_ms * 1e-3) / 1e9
     alu_tops = alu_ops / (main_ms * 1e-3) / 1e12
+    mfma_tflops = alg_flops / (main_ms * 1e-3) / 1e12
     traffic = None
-    tfile = TRAFFIC_FILES[a.op]
+    tfile = TRAFFIC_FILES[op]
     if tfile.exists():
         rec = json.loads(tfile.read_text())
         if rec.get("source_sha256") == source_hash() and rec.get("workload") == a.config:
             traffic = rec.get("bytes_per_launch")
-    # The binding roof is the one whose ideal time is longest: elementwise ALU
-    # work at the fp32 vector peak versus algorithmic bytes at the HBM peak.
-    t_alu = alu_ops / (ALU_PEAK_TOPS * 1e12)
-    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
-    if t_alu >= t_hbm:
-        roofline = {"bound": "alu", "achieved": round(alu_tops, 3), "peak": round(ALU_PEAK_TOPS, 2),
-                    "unit": "Top/s", "frac": round(alu_tops / ALU_PEAK_TOPS, 4)}
-    else:
-        roofline = {"bound": "hbm", "achieved": round(hbm_gbps_main, 2), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(hbm_gbps_main / HBM_PEAK_GBS, 4)}
+    # The binding roof is the one whose ideal time is longest: elementwise ALU work at
+    # the fp32 vector peak, algorithmic bytes at the HBM peak, or the contractions at
+    # the matrix peak of the dtype they run in.
+    roofs = {
+        "alu": (alu_ops / (ALU_PEAK_TOPS * 1e12), alu_tops, round(ALU_PEAK_TOPS, 2), "Top/s"),
+        "hbm": (alg_bytes / (HBM_PEAK_GBS * 1e9), hbm_gbps_main, HBM_PEAK_GBS, "GB/s"),
+        "mfma": (alg_flops / (mfma_peak * 1e12), mfma_tflops, mfma_peak, "TFLOP/s"),
+    }
+    bound = max(roofs, key=lambda k: roofs[k][0])
+    _, achieved, peak, unit = roofs[bound]
+    roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4)}
     roofline.update({
-        "traffic": traffic, "kernel": "k_main", "kernel_ms": round(main_ms, 5),
+        "traffic": traffic, "kernel": main_name, "kernel_ms": round(main_ms, 5),
         "algorithmic_alu_ops_per_launch": alu_ops, "algorithmic_bytes_per_launch": alg_bytes,
+        "algorithmic_flops_per_launch": alg_flops, "mfma_dtype": mfma_unit_dtype,
         "hbm_frac": round(hbm_gbps_main / HBM_PEAK_GBS, 4),
+        "alu_frac": round(alu_tops / ALU_PEAK_TOPS, 4),
         "alu_frac_nonpacked": round(alu_tops / ALU_NONPACKED_TOPS, 4),
-        "mfma_frac": round(alg_flops / (main_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)})
+        "mfma_frac": round(mfma_tflops / mfma_peak, 5)})
 
     cpu = None
     if not a.no_cpu:
-        from oracle import o1
+        from oracle import o1, siso
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
         log(f"oracle CPU baseline on the whole workload ({threads} OpenMP threads)")
         t = time.perf_counter()
-        (o1.run_fwd_inputs if fwd else o1.run_inputs)(inp)
+        if siso_op:
+            siso.run(*[inp[n] for n in SISO_ORDER], chunk_size=case.C)
+        elif op == "fwd":
+            o1.run_fwd_inputs(inp)
+        else:
+            o1.run_inputs(inp, fp32=op == "bwd_fwd_fp32")
         cpu_ms = (time.perf_counter() - t) * 1e3
-        cpu = {"value": round(cpu_ms, 3), "unit": "ms/call", "cores": min(threads, B * H), "kind": "oracle",
-               "sample": f"the whole {a.config} workload once (OpenMP over the {B * H} (batch, head) pairs)"}
+        cpu = {"value": round(cpu_ms, 3), "unit": "ms/call", "cores": min(threads, case.B * case.H),
+               "kind": "oracle",
+               "sample": f"the whole {a.config} workload once (OpenMP over the {case.B * case.H} (batch, head) pairs)"}
         log(f"oracle: {cpu_ms:.1f} ms")
 
     gbps = alg_bytes / (ms * 1e-3) / 1e9
+    metric = {"bwd_fwd": METRIC, "fwd": FWD_METRIC, "bwd_fwd_fp32": FP32_METRIC, "siso": SISO_METRIC}[op]
+    if siso_op:
+        config = {"workload": a.config, "op": op, "B": case.B, "S": case.S, "Hq": case.Hq, "H": case.H,
+                  "K": case.K, "V": case.V, "A": case.width, "chunk_size": case.C, "dtype": case.dtype,
+                  "has_z": case.has_z, "has_d": case.has_d, "buffer_sets": nsets,
+                  "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops}
+        dtype = case.dtype + " in/out, f32 compute"
+    else:
+        config = {"workload": a.config, "op": op, "B": B, "S": S, "H": H, "G": G, "N": N, "P": P, "R": R,
+                  "chunk_size": C, "rotary_dim_divisor": case.rd, "reduce_o": case.reduce_o,
+                  "has_z": case.has_z, "has_d": case.has_d, "buffer_sets": nsets,
+                  "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops}
+        dtype = "f32" if op == "bwd_fwd_fp32" else "bf16"
     line = {
-        "metric": FWD_METRIC if fwd else METRIC,
+        "metric": metric,
         "value": round(ms, 5),
         "unit": "ms/call",
         "n_gpus": 1,
@@ -334,16 +434,13 @@ def main():
         "ms_per_step": round(ms, 5),
         "higher_is_better": False,
         "scaling": "weak",
-        "vs_baseline": round(ms / PAGES_MS, 6) if a.config == "perf_s8192" and not fwd else None,
-        "dtype": "bf16",
+        "vs_baseline": round(ms / PAGES_MS, 6) if a.config == "perf_s8192" and op == "bwd_fwd" else None,
+        "dtype": dtype,
         "data": "synthetic",
         "hbm_gbps": round(gbps, 2),
         "hbm_frac": round(gbps / HBM_PEAK_GBS, 4),
         "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
-        "config": {"workload": a.config, "op": a.op, "B": B, "S": S, "H": H, "G": G, "N": N, "P": P, "R": R,
-                   "chunk_size": C, "rotary_dim_divisor": case.rd, "reduce_o": case.reduce_o,
-                   "has_z": case.has_z, "has_d": case.has_d, "buffer_sets": nsets,
-                   "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops},
+        "config": config,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -323,6 +323,21 @@ struct Plan32 {
 
 int tidx3(int x) { return x == 32 ? 0 : (x == 64 ? 1 : 2); }
 
+const f32::F32Set* f32_set() {
+    static const f32::F32Set set = [] {
+        f32::F32Set s{};
+        const f32::F32Part* parts[3] = {f32::f32_part_mt32(), f32::f32_part_mt64(), f32::f32_part_mt128()};
+        for (int m = 0; m < 3; ++m)
+            for (int d = 0; d < 2; ++d)
+                for (int i = 0; i < 9; ++i) {
+                    s.agg[d][9 * m + i] = parts[m]->agg[d][i];
+                    s.main[d][9 * m + i] = parts[m]->main[d][i];
+                }
+        return s;
+    }();
+    return &set;
+}
+
 mimo_status make_plan32(const Prob32& q, Plan32* pl) {
     if (q.B < 1 || q.S < 1 || q.R < 1 || q.G < 1 || q.H < 1 || q.N < 1 || q.P < 1)
         return fail(MIMO_ERR_VALUE, "B, S, H, G, R, N and P must be positive");
@@ -385,7 +400,7 @@ mimo_status run32(const Prob32& q, Params& p, void* workspace, size_t workspace_
         for (int i = 0; i < MIMO_TIMED_EVENTS; ++i)
             if (events[i] == nullptr) return fail(MIMO_ERR_VALUE, "timing event %d is NULL", i);
     if ((s = check_device()) != MIMO_OK) return s;
-    const f32::F32Set* set = f32::f32_set();
+    const f32::F32Set* set = f32_set();
     const kfn kmain = set->main[q.f16][pl.ti], kagg = set->agg[q.f16][pl.ti];
     if (kmain == nullptr || kagg == nullptr) return fail(MIMO_ERR_UNSUPPORTED, "no fp32 kernel for this tile shape");
     p.B = (int)q.B; p.S = (int)q.S; p.H = (int)q.H; p.G = (int)q.G; p.R = (int)q.R; p.N = (int)q.N; p.P = (int)q.P;

@@ -97,6 +97,11 @@ __device__ __forceinline__ unsigned short st16(float x) {
 
 __device__ __forceinline__ float sig32(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// x[v] for a run-time v in [0, 4) by selects (no indexed register access)
+__device__ __forceinline__ float pick4(const float* x, int v) {
+    return v == 0 ? x[0] : (v == 1 ? x[1] : (v == 2 ? x[2] : x[3]));
+}
+
 __device__ __forceinline__ f32x4 mfma32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -104,8 +109,14 @@ __device__ __forceinline__ f32x4 mfma32(float a, float b, f32x4 c) {
 // MAIN = false: segment aggregate (state increment of a sub-segment from zero and
 // its decay product). MAIN = true: the chunk pass (states, qk_dot, y and the
 // backward's gating outputs, or the layer output when p.fwd).
+// Two workgroups per compute unit where the LDS layout allows it.
+template <int MT, int NT, int PT, bool MAIN>
+constexpr int wg_per_cu32() {
+    return lds32(MT, NT, PT, MAIN).total <= 80 * 1024 ? 2 : 1;
+}
+
 template <int MT, int NT, int PT, bool MAIN, bool F16>
-__global__ __launch_bounds__(256, 1) void k_chunk32(Params p) {
+__global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN>())) void k_chunk32(Params p) {
     using T = Tile32<MT, NT, PT>;
     constexpr int NW = T::NW, NTHR = T::NTHR, LQ = T::LQ, LA = T::LA, LP = T::LP, CX = T::CX;
     constexpr int MTT = T::MTT, NTT = T::NTT, PTT = T::PTT, PW = T::PW;
@@ -250,9 +261,22 @@ __global__ __launch_bounds__(256, 1) void k_chunk32(Params p) {
             }
         }
 
-        // ---- q0, k0 (biased, unrotated) and Psi into LDS; zero outside the problem
+        // ---- q0, k0 (biased, unrotated) and Psi into LDS; zero outside the problem. The
+        // loops are unrolled so that each thread's loads are all in flight together; the
+        // angles of the rotation below are fetched here too.
         constexpr int N4 = NT / 4, P4 = PT / 4;
-        for (int e = tid; e < MT * N4; e += NTHR) {
+        constexpr int QK_IT = MT * N4 / NTHR, PS_IT = MT * P4 / NTHR;   // exact: MT * NT >= 32 * 32
+        constexpr int ROT_IT = MT * (NT / 2) / NTHR;                     // rotation items (t < MT, n < NT/2)
+        float ang[ROT_IT];
+#pragma unroll
+        for (int k2 = 0; k2 < ROT_IT; ++k2) {
+            const int e = tid + k2 * NTHR;
+            const int t = e / (NT / 2), n = e % (NT / 2);
+            ang[k2] = (t < cl && n < W) ? p.angles[((long)(b * p.S + c0 + t) * p.H + h) * W + n] : 0.f;
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < QK_IT; ++k2) {
+            const int e = tid + k2 * NTHR;
             const int i = e / N4, n = 4 * (e % N4);
             const int r = i / Cp, t = i % Cp;
             float qv[4] = {0.f, 0.f, 0.f, 0.f}, kv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -272,7 +296,9 @@ __global__ __launch_bounds__(256, 1) void k_chunk32(Params p) {
             *reinterpret_cast<f32x4*>(sK + i * LQ + n) = f32x4{kv[0], kv[1], kv[2], kv[3]};
             if (MAIN) *reinterpret_cast<f32x4*>(sQ + i * LQ + n) = f32x4{qv[0], qv[1], qv[2], qv[3]};
         }
-        for (int e = tid; e < MT * P4; e += NTHR) {
+#pragma unroll
+        for (int k2 = 0; k2 < PS_IT; ++k2) {
+            const int e = tid + k2 * NTHR;
             const int i = e / P4, pc = 4 * (e % P4);
             const int r = i / Cp, t = i % Cp;
             float x[4] = {0.f, 0.f, 0.f, 0.f};
@@ -322,12 +348,14 @@ __global__ __launch_bounds__(256, 1) void k_chunk32(Params p) {
         __syncthreads();
 
         // ---- rotation of q and k (pairs n, N/2 + n for n < W) and K~ = k * factor
-        for (int e = tid; e < Cp * (NT / 2); e += NTHR) {
+#pragma unroll
+        for (int k2 = 0; k2 < ROT_IT; ++k2) {
+            const int e = tid + k2 * NTHR;
             const int t = e / (NT / 2), n = e % (NT / 2);
             if (t >= cl || n >= M) continue;
             const float f = sFac[t];
             float cn = 1.f, sn = 0.f;
-            if (n < W) sin_cos(p.angles[((long)(b * p.S + c0 + t) * p.H + h) * W + n], sn, cn);
+            if (n < W) sin_cos(ang[k2], sn, cn);
             for (int r = 0; r < R; ++r) {
                 float* kr = sK + (r * Cp + t) * LQ;
                 const float ka = kr[n], ke = kr[M + n];
@@ -466,7 +494,8 @@ __global__ __launch_bounds__(256, 1) void k_chunk32(Params p) {
             }
             // ---- y = inter + intra + gamma * sum_r2 qk[r][r2] Psi[r2] + d * Psi, then the
             // gating outputs (backward) or the layer output (forward). A lane reads back
-            // only what it wrote itself.
+            // only what it wrote itself. The gate inputs (z, reduced dout) of a token tile's
+            // four tokens are loaded together, in one round trip.
             const int RR = R * R;
 #pragma unroll
             for (int j = 0; j < PW; ++j) {
@@ -474,14 +503,20 @@ __global__ __launch_bounds__(256, 1) void k_chunk32(Params p) {
                 const int pc = 16 * pt + l16;
                 if (pt >= PTT || pc >= P) continue;
                 for (int tt = 0; tt < CT; ++tt) {
+                    float zpre[4], dpre[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int t = 16 * tt + 4 * q4 + v;
+                        const long ivp = ((long)(b * p.S + c0 + t) * p.H + h) * P + pc;
+                        zpre[v] = (t < cl && p.has_z) ? ld16<F16>(p.z, ivp) : 0.f;
+                        dpre[v] = (t < cl && !p.fwd && p.reduce_o) ? ld16<F16>(p.dout, ivp) : 0.f;
+                    }
                     for (int v = 0; v < 4; ++v) {
                         const int t = 16 * tt + 4 * q4 + v;
                         if (t >= cl) continue;
                         const long ivp = ((long)(b * p.S + c0 + t) * p.H + h) * P + pc;
                         const float gam = sGam[t];
-                        float zr = 0.f, dv = 0.f;
-                        if (p.has_z) zr = ld16<F16>(p.z, ivp);
-                        if (!p.fwd && p.reduce_o) dv = ld16<F16>(p.dout, ivp);
+                        const float zr = pick4(zpre, v), dv = pick4(dpre, v);
                         float dzs = 0.f, osum = 0.f;
 #pragma unroll
                         for (int r = 0; r < 8; ++r) {
@@ -567,11 +602,36 @@ __global__ __launch_bounds__(256, 1) void k_chunk32(Params p) {
 }
 
 // Kernel table: [bf16 = 0 / fp16 = 1][9 * idx(MT) + 3 * idx(NT) + idx(PT)] with
-// idx(32, 64, 128) = 0, 1, 2; nullptr where the tile's LDS does not fit.
+// idx(32, 64, 128) = 0, 1, 2; nullptr where the tile's LDS does not fit. Each MT's
+// instances are compiled in a translation unit of their own (tiles_f32_mt*.hip).
 struct F32Set {
     kfn agg[2][27], main[2][27];
 };
-const F32Set* f32_set();
+struct F32Part {
+    kfn agg[2][9], main[2][9];
+};
+const F32Part* f32_part_mt32();
+const F32Part* f32_part_mt64();
+const F32Part* f32_part_mt128();
+
+template <int MT, int NT, int PT, bool MAIN, bool F16>
+constexpr kfn pick32() {
+    if constexpr (lds32(MT, NT, PT, MAIN).total <= 160 * 1024)
+        return k_chunk32<MT, NT, PT, MAIN, F16>;
+    else
+        return nullptr;
+}
+
+#define MIMO_F32_NP(MT, MAIN, F16)                                                                  \
+    {pick32<MT, 32, 32, MAIN, F16>(), pick32<MT, 32, 64, MAIN, F16>(), pick32<MT, 32, 128, MAIN, F16>(), \
+     pick32<MT, 64, 32, MAIN, F16>(), pick32<MT, 64, 64, MAIN, F16>(), pick32<MT, 64, 128, MAIN, F16>(), \
+     pick32<MT, 128, 32, MAIN, F16>(), pick32<MT, 128, 64, MAIN, F16>(), pick32<MT, 128, 128, MAIN, F16>()}
+#define MIMO_F32_PART(MT)                                                                           \
+    const F32Part* f32_part_mt##MT() {                                                              \
+        static const F32Part part = {{MIMO_F32_NP(MT, false, false), MIMO_F32_NP(MT, false, true)}, \
+                                     {MIMO_F32_NP(MT, true, false), MIMO_F32_NP(MT, true, true)}};  \
+        return &part;                                                                               \
+    }
 
 }  // namespace f32
 }  // namespace mimo

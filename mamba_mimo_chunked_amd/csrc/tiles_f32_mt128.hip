@@ -1,0 +1,9 @@
+// Instances of the fp32-intermediate chunk kernels with MT = 128 chunk-tile rows: every
+// (NT, PT) tile whose LDS layout fits a compute unit, for bf16 and fp16 inputs.
+#include "mimo_f32.hpp"
+
+namespace mimo {
+namespace f32 {
+MIMO_F32_PART(128)
+}  // namespace f32
+}  // namespace mimo

@@ -35,11 +35,14 @@ def test_library_exports_every_declared_symbol():
         assert re.search(rf"\bT {name}$", out, re.M), name
 
 
-def test_struct_layout_matches_c(tmp_path):
-    fields = [f[0] for f in _lib.MimoBwdFwdArgs._fields_]
+@pytest.mark.parametrize("cls,cname", [(_lib.MimoBwdFwdArgs, "mimo_bwd_fwd_args"),
+                                        (_lib.MimoFwdArgs, "mimo_fwd_args"),
+                                        (_lib.MimoSisoFwdArgs, "mimo_siso_fwd_args")])
+def test_struct_layout_matches_c(tmp_path, cls, cname):
+    fields = [f[0] for f in cls._fields_]
     prog = ["#include <stddef.h>", "#include <stdio.h>", '#include "mimo_bwd_fwd.h"', "int main(void){",
-            'printf("%zu\\n", sizeof(mimo_bwd_fwd_args));']
-    prog += [f'printf("%zu\\n", offsetof(mimo_bwd_fwd_args, {f}));' for f in fields]
+            f'printf("%zu\\n", sizeof({cname}));']
+    prog += [f'printf("%zu\\n", offsetof({cname}, {f}));' for f in fields]
     prog += ["return 0;}"]
     src = tmp_path / "layout.c"
     src.write_text("\n".join(prog))
@@ -47,9 +50,9 @@ def test_struct_layout_matches_c(tmp_path):
     subprocess.run(["gcc", f"-I{ROOT / 'include'}", str(src), "-o", str(exe)], check=True)
     vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
                                            check=True).stdout.split()]
-    assert vals[0] == ctypes.sizeof(_lib.MimoBwdFwdArgs)
+    assert vals[0] == ctypes.sizeof(cls)
     for f, off in zip(fields, vals[1:]):
-        assert getattr(_lib.MimoBwdFwdArgs, f).offset == off, f
+        assert getattr(cls, f).offset == off, f
 
 
 def test_workspace_size_query():
@@ -78,6 +81,51 @@ def test_c_call_rejects_bad_arguments_without_a_device():
     assert L.mimo_bwd_fwd(ctypes.byref(a), None) == _lib.MIMO_ERR_VALUE   # NULL inputs
     assert "NULL" in _lib.last_error()
     assert L.mimo_bwd_fwd(None, None) == _lib.MIMO_ERR_VALUE
+
+
+def test_fp32_and_siso_argument_checks_without_a_device():
+    """The fp32-intermediate and SISO entry points reject bad sizes before any device work."""
+    L = _lib.lib()
+    a = _lib.MimoBwdFwdArgs()
+    a.B, a.S, a.H, a.G, a.R, a.N, a.P = 1, 300, 2, 1, 8, 128, 128
+    a.chunk_size, a.rotary_dim_divisor = 16, 4
+    n = ctypes.c_size_t(0)
+    assert L.mimo_bwd_fwd_f32_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _lib.MIMO_ERR_UNSUPPORTED
+    assert "LDS" in _lib.last_error()
+    a.R, a.N, a.P = 4, 64, 64
+    assert L.mimo_bwd_fwd_f32_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _lib.MIMO_OK
+    assert L.mimo_bwd_fwd_f32(ctypes.byref(a), None) == _lib.MIMO_ERR_VALUE   # NULL inputs
+    s = _lib.MimoSisoFwdArgs()
+    s.B, s.S, s.Hq, s.H, s.K, s.V, s.A = 1, 128, 2, 4, 64, 96, 32
+    for c, err in ((48, _lib.MIMO_ERR_VALUE), (32, _lib.MIMO_OK), (64, _lib.MIMO_OK)):
+        s.chunk_size = c
+        assert L.mimo_siso_fwd_workspace_size(ctypes.byref(s), ctypes.byref(n)) == err, c
+    s.A = 33
+    assert L.mimo_siso_fwd_workspace_size(ctypes.byref(s), ctypes.byref(n)) == _lib.MIMO_ERR_VALUE
+    s.A, s.Hq = 32, 3
+    assert L.mimo_siso_fwd_workspace_size(ctypes.byref(s), ctypes.byref(n)) == _lib.MIMO_ERR_VALUE
+    s.Hq, s.dtype = 2, 7
+    assert L.mimo_siso_fwd_workspace_size(ctypes.byref(s), ctypes.byref(n)) == _lib.MIMO_ERR_TYPE
+    s.dtype = _lib.DTYPE_FP16
+    assert L.mimo_siso_fwd(ctypes.byref(s), None) == _lib.MIMO_ERR_VALUE      # NULL inputs
+
+
+@pytest.mark.parametrize("chunk", [48, 0, True, 64.0, "64"])
+def test_siso_invalid_chunk_size(chunk):
+    """chunk_size must be the int 32 or 64 (not a bool, a float or another int)."""
+    from mamba_mimo_chunked_amd import mamba3_siso_fwd
+    from synth.inputs import SISO_CONFIGS, SISO_ORDER, make_siso_inputs
+    inp = make_siso_inputs(SISO_CONFIGS["siso_example"])
+    with pytest.raises(ValueError, match="chunk_size"):
+        mamba3_siso_fwd(*[inp[n] for n in SISO_ORDER], chunk_size=chunk)
+
+
+def test_siso_cpu_tensors_are_rejected():
+    from mamba_mimo_chunked_amd import mamba3_siso_fwd
+    from synth.inputs import SISO_CONFIGS, SISO_ORDER, make_siso_inputs
+    inp = make_siso_inputs(SISO_CONFIGS["siso_example"])
+    with pytest.raises(ValueError, match="GPU"):
+        mamba3_siso_fwd(*[inp[n] for n in SISO_ORDER], chunk_size=64)
 
 
 # -------------------------------------------------------------- the pages' invalid-input tests
