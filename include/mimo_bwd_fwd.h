@@ -222,6 +222,55 @@ mimo_status mimo_siso_fwd(const mimo_siso_fwd_args *args, void *stream);
 /* mimo_siso_fwd with the MIMO_TIMED_EVENTS events of mimo_bwd_fwd_timed. */
 mimo_status mimo_siso_fwd_timed(const mimo_siso_fwd_args *args, void *stream, void *const *events);
 
+/*
+ * Stage-2 backward (mamba3_mimo_bwd_bwd; Triton-Ascend pull request page:
+ * "practice" document and migration note). Consumes the first stage's states
+ * and qk_dot and returns twelve gradients of L = sum dPhiO * y, with y the
+ * pre-gate per-rank output (Z gating belongs to the first stage) and dPhiO =
+ * dout * mimo_o (reduced) or the per-rank dout. Intermediates are fp32. Each
+ * output is the derivative with respect to one use of one quantity, the caches
+ * giving the values of the chunk entry states and same-token dots:
+ *   dq, dk      [B, S*R, H, N]  the biased q, k of each head (row t*R + r)
+ *   dv          [B,S,H,P]       dmimo_v [B,H,R,P] (per batch)   dd [B,H] (iff d)
+ *   dangles     [B,S,H,N/rotary_dim_divisor]
+ *   dfactor     [B,H,S]  the K scale factor_t = gamma_t + beta_t
+ *   dgamma      [B,H,S]  gamma_t in the same-token term
+ *   dda_cs      [B,H,S]  da_cs[t] in the inter-term scale exp(da_cs[t])
+ *   dda         [B,H,S]  da_cs at each chunk's last token in the state decay (0 elsewhere)
+ *   dda_cs_rev  [B,H,S]  da_cs_rev[t] in kappa = K~ * exp(da_cs_rev[t])
+ *   dssda       [B,H,nc,C,C]  segsum[c][t][s], s < t (0 elsewhere)
+ * dq, dk, dv are bf16, or fp32 when out_f32 != 0; the others fp32.
+ * Inputs as for mimo_bwd_fwd (dout reduced or not, bf16 q/k/v/dout/trap) plus
+ * states [B,H,nc,N,P] and qk_dot [B,H,S,R,R] (bf16). Limits: R * chunk_size,
+ * N and P at most 64, R at most 8 (MIMO_ERR_UNSUPPORTED otherwise). Ownership, asynchrony
+ * and errors as for mimo_bwd_fwd.
+ */
+typedef struct mimo_bwd_bwd_args {
+    int64_t B, S, H, G, R, N, P;
+    int32_t chunk_size;
+    int32_t rotary_dim_divisor;
+    int32_t out_f32;
+    const uint16_t *dout, *q, *k, *v;
+    const float *q_bias, *k_bias, *mimo_v;
+    const uint16_t *states, *qk_dot;
+    const float *da_cs, *da_cs_rev, *dt;
+    const uint16_t *trap;
+    const float *segsum, *angles;
+    const float *mimo_o;         /* optional: selects reduced dout                    */
+    const float *d;              /* optional                                          */
+    void *dq, *dk, *dv;
+    float *dmimo_v, *dangles, *dfactor, *dgamma, *dda, *dssda, *dda_cs_rev, *dda_cs;
+    float *dd;                   /* required iff d != NULL                            */
+    void *workspace;             /* at least mimo_bwd_bwd_workspace_size() bytes, 256-byte aligned */
+    size_t workspace_bytes;
+} mimo_bwd_bwd_args;
+
+mimo_status mimo_bwd_bwd_workspace_size(const mimo_bwd_bwd_args *args, size_t *bytes);
+mimo_status mimo_bwd_bwd(const mimo_bwd_bwd_args *args, void *stream);
+/* mimo_bwd_bwd with the MIMO_TIMED_EVENTS events of mimo_bwd_fwd_timed (segment
+ * aggregate, reverse scan, chunk pass, final sums). */
+mimo_status mimo_bwd_bwd_timed(const mimo_bwd_bwd_args *args, void *stream, void *const *events);
+
 /* Message describing the last error of the calling thread ("" if none). */
 const char *mimo_last_error(void);
 

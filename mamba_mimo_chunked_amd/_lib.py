@@ -87,13 +87,38 @@ class MimoSisoFwdArgs(ctypes.Structure):
     ]
 
 
+class MimoBwdBwdArgs(ctypes.Structure):
+    """Mirror of ``mimo_bwd_bwd_args`` (field order and types must match)."""
+
+    _fields_ = [
+        ("B", ctypes.c_int64), ("S", ctypes.c_int64), ("H", ctypes.c_int64), ("G", ctypes.c_int64),
+        ("R", ctypes.c_int64), ("N", ctypes.c_int64), ("P", ctypes.c_int64),
+        ("chunk_size", ctypes.c_int32), ("rotary_dim_divisor", ctypes.c_int32), ("out_f32", ctypes.c_int32),
+        ("dout", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("q_bias", ctypes.c_void_p), ("k_bias", ctypes.c_void_p), ("mimo_v", ctypes.c_void_p),
+        ("states", ctypes.c_void_p), ("qk_dot", ctypes.c_void_p),
+        ("da_cs", ctypes.c_void_p), ("da_cs_rev", ctypes.c_void_p), ("dt", ctypes.c_void_p),
+        ("trap", ctypes.c_void_p),
+        ("segsum", ctypes.c_void_p), ("angles", ctypes.c_void_p),
+        ("mimo_o", ctypes.c_void_p),
+        ("d", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dmimo_v", ctypes.c_void_p), ("dangles", ctypes.c_void_p), ("dfactor", ctypes.c_void_p),
+        ("dgamma", ctypes.c_void_p), ("dda", ctypes.c_void_p), ("dssda", ctypes.c_void_p),
+        ("dda_cs_rev", ctypes.c_void_p), ("dda_cs", ctypes.c_void_p),
+        ("dd", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 DTYPE_BF16, DTYPE_FP16 = 0, 1
 
 EXPORTED = ("mimo_bwd_fwd", "mimo_bwd_fwd_timed", "mimo_bwd_fwd_workspace_size", "mimo_fwd",
             "mimo_fwd_timed", "mimo_fwd_workspace_size", "mimo_bwd_fwd_f32", "mimo_bwd_fwd_f32_timed",
             "mimo_bwd_fwd_f32_workspace_size", "mimo_fwd_f32", "mimo_fwd_f32_workspace_size",
-            "mimo_siso_fwd", "mimo_siso_fwd_timed", "mimo_siso_fwd_workspace_size", "mimo_last_error",
-            "mimo_abi_version")
+            "mimo_siso_fwd", "mimo_siso_fwd_timed", "mimo_siso_fwd_workspace_size", "mimo_bwd_bwd",
+            "mimo_bwd_bwd_timed", "mimo_bwd_bwd_workspace_size", "mimo_last_error", "mimo_abi_version")
 TIMED_EVENTS = 5
 
 _lib = None
@@ -138,6 +163,13 @@ def lib():
         L.mimo_siso_fwd_timed.restype = ctypes.c_int
         L.mimo_siso_fwd_workspace_size.argtypes = [sargp, szp]
         L.mimo_siso_fwd_workspace_size.restype = ctypes.c_int
+        bargp = ctypes.POINTER(MimoBwdBwdArgs)
+        L.mimo_bwd_bwd.argtypes = [bargp, ctypes.c_void_p]
+        L.mimo_bwd_bwd.restype = ctypes.c_int
+        L.mimo_bwd_bwd_timed.argtypes = [bargp, ctypes.c_void_p, evp]
+        L.mimo_bwd_bwd_timed.restype = ctypes.c_int
+        L.mimo_bwd_bwd_workspace_size.argtypes = [bargp, szp]
+        L.mimo_bwd_bwd_workspace_size.restype = ctypes.c_int
         L.mimo_last_error.argtypes = []
         L.mimo_last_error.restype = ctypes.c_char_p
         L.mimo_abi_version.argtypes = []

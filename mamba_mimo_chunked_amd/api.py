@@ -1,5 +1,6 @@
 """Public Python entry points: ``mamba_mimo_bwd_fwd``, the layer output ``mamba_mimo_fwd``,
-their fp32-intermediate variants, and the SISO forward ``mamba3_siso_fwd``.
+their fp32-intermediate variants, the stage-2 backward ``mamba3_mimo_bwd_bwd`` and the SISO
+forward ``mamba3_siso_fwd``.
 
 Signature, defaults, output order, validation order and error types follow
 the Triton-Ascend mamba_mimo_bwd_fwd page (public API module: the
@@ -20,7 +21,8 @@ import torch
 from . import _lib
 
 __all__ = ["MambaMimoBwdFwdOutputs", "mamba_mimo_bwd_fwd", "mamba_mimo_fwd", "mamba_mimo_bwd_fwd_fp32",
-           "mamba_mimo_fwd_fp32", "mamba3_siso_fwd", "workspace_size", "fwd_workspace_size"]
+           "mamba_mimo_fwd_fp32", "mamba3_mimo_bwd_bwd", "mamba3_siso_fwd", "workspace_size",
+           "fwd_workspace_size"]
 
 Tensor = torch.Tensor
 
@@ -412,3 +414,89 @@ def mamba3_siso_fwd(q, k, v, adt, dt, trap, q_bias, k_bias, angles, d=None, z=No
     if st != _lib.MIMO_OK:
         _raise(st)
     return out
+
+
+# ---------------------------------------------------------------- stage-2 backward
+BWD2_KEYS = ("DQ", "DK", "DV", "DMIMO_V", "DANGLES", "DFACTOR", "DGAMMA", "DDA", "DSSDA", "DDA_CS_REV",
+             "DDA_CS", "DD")
+_BWD2_INPUTS = ("dout", "q", "k", "v", "q_bias", "k_bias", "mimo_v", "states", "qk_dot", "da_cs", "da_cs_rev",
+                "dt", "trap", "segsum", "angles", "mimo_o", "d")
+_BWD2_OUT_FIELDS = {"DQ": "dq", "DK": "dk", "DV": "dv", "DMIMO_V": "dmimo_v", "DANGLES": "dangles",
+                    "DFACTOR": "dfactor", "DGAMMA": "dgamma", "DDA": "dda", "DSSDA": "dssda",
+                    "DDA_CS_REV": "dda_cs_rev", "DDA_CS": "dda_cs", "DD": "dd"}
+
+
+def _make_bwd2_args(dims, C, rd, out_f32, t: dict, outs: dict, workspace=None, ws_bytes=0):
+    B, S, H, G, R, N, P = dims
+    a = _lib.MimoBwdBwdArgs()
+    a.B, a.S, a.H, a.G, a.R, a.N, a.P = B, S, H, G, R, N, P
+    a.chunk_size, a.rotary_dim_divisor, a.out_f32 = C, rd, int(out_f32)
+    for name in _BWD2_INPUTS:
+        x = t.get(name)
+        setattr(a, name, None if x is None else x.data_ptr())
+    for key, field in _BWD2_OUT_FIELDS.items():
+        x = outs.get(key)
+        setattr(a, field, None if x is None else x.data_ptr())
+    a.workspace = None if workspace is None else workspace.data_ptr()
+    a.workspace_bytes = ws_bytes
+    return a
+
+
+def mamba3_mimo_bwd_bwd(dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, da_cs, da_cs_rev, dt, trap,
+                        segsum, angles, mimo_o=None, d=None, chunk_size: int = 16, rotary_dim_divisor: int = 4,
+                        output_dtype=None, *, workspace: Optional[Tensor] = None) -> dict:
+    """Stage-2 backward of the MIMO scan: the twelve gradients (dict keys DQ, DK, DV,
+    DMIMO_V, DANGLES, DFACTOR, DGAMMA, DDA, DSSDA, DDA_CS_REV, DDA_CS, DD) of
+    sum(dPhiO * y) given the first stage's ``states`` and ``qk_dot``. DQ, DK
+    [B, S*R, H, N] and DV take q's dtype (bf16) unless ``output_dtype=torch.float32``;
+    the others are float32; DD is None without ``d``. Asynchronous on the current
+    HIP stream."""
+    _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, None, None, angles, da_cs, da_cs_rev,
+                     dt, trap, d, segsum, chunk_size, rotary_dim_divisor)
+    B, S, R, G, N = q.shape
+    H, P = v.shape[2:]
+    C = int(chunk_size)
+    nc = (S + C - 1) // C
+    dev = q.device
+    _check_tensor("states", states, (B, H, nc, N, P), torch.bfloat16, dev)
+    _check_tensor("qk_dot", qk_dot, (B, H, S, R, R), torch.bfloat16, dev)
+    if output_dtype not in (None, torch.bfloat16, torch.float32):
+        raise TypeError("output_dtype must be None, torch.bfloat16 or torch.float32")
+    out_f32 = output_dtype == torch.float32
+    odt = torch.float32 if out_f32 else torch.bfloat16
+    L = _lib.lib()
+    vals = (dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, da_cs, da_cs_rev, dt, trap, segsum, angles,
+            mimo_o, d)
+    t = {n: (None if x is None else x.contiguous()) for n, x in zip(_BWD2_INPUTS, vals)}
+    f32 = torch.float32
+    W = N // rotary_dim_divisor
+    outs = {
+        "DQ": torch.empty((B, S * R, H, N), dtype=odt, device=dev),
+        "DK": torch.empty((B, S * R, H, N), dtype=odt, device=dev),
+        "DV": torch.empty((B, S, H, P), dtype=odt, device=dev),
+        "DMIMO_V": torch.empty((B, H, R, P), dtype=f32, device=dev),
+        "DANGLES": torch.empty((B, S, H, W), dtype=f32, device=dev),
+        "DFACTOR": torch.empty((B, H, S), dtype=f32, device=dev),
+        "DGAMMA": torch.empty((B, H, S), dtype=f32, device=dev),
+        "DDA": torch.empty((B, H, S), dtype=f32, device=dev),
+        "DSSDA": torch.empty((B, H, nc, C, C), dtype=f32, device=dev),
+        "DDA_CS_REV": torch.empty((B, H, S), dtype=f32, device=dev),
+        "DDA_CS": torch.empty((B, H, S), dtype=f32, device=dev),
+        "DD": torch.empty((B, H), dtype=f32, device=dev) if d is not None else None,
+    }
+    args = _make_bwd2_args((B, S, H, G, R, N, P), C, int(rotary_dim_divisor), out_f32, t, outs)
+    need = ctypes.c_size_t(0)
+    st = L.mimo_bwd_bwd_workspace_size(ctypes.byref(args), ctypes.byref(need))
+    if st != _lib.MIMO_OK:
+        _raise(st)
+    if need.value > 0:
+        if workspace is None or workspace.numel() < need.value:
+            workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = L.mimo_bwd_bwd(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != _lib.MIMO_OK:
+        _raise(st)
+    return outs

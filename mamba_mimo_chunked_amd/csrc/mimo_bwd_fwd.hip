@@ -47,6 +47,7 @@
 #include <mutex>
 #include <string>
 
+#include "mimo_bwd2.hpp"
 #include "mimo_f32.hpp"
 
 namespace mimo {
@@ -539,6 +540,137 @@ mimo_status run_siso(const mimo_siso_fwd_args* a, void* stream, void* const* eve
     return run32(q, p, a->workspace, a->workspace_bytes, stream, events);
 }
 
+// ---------------------------------------------------------------- stage-2 backward
+struct PlanB2 {
+    int nc, L, nseg, F, nsub, W;
+    size_t off_agg, off_decay, off_mv, off_d, ws_bytes;
+};
+
+mimo_status make_plan_b2(const mimo_bwd_bwd_args* a, PlanB2* pl) {
+    if (a == nullptr) return fail(MIMO_ERR_VALUE, "args must not be NULL");
+    const int64_t B = a->B, S = a->S, H = a->H, G = a->G, R = a->R, N = a->N, P = a->P, C = a->chunk_size;
+    const int64_t rd = a->rotary_dim_divisor;
+    if (B < 1 || S < 1 || H < 1 || G < 1 || R < 1 || N < 1 || P < 1)
+        return fail(MIMO_ERR_VALUE, "B, S, H, G, R, N and P must be positive");
+    if (C < 1) return fail(MIMO_ERR_VALUE, "chunk_size must be positive");
+    if (H % G) return fail(MIMO_ERR_VALUE, "H must be divisible by G");
+    if (rd != 2 && rd != 4) return fail(MIMO_ERR_VALUE, "rotary_dim_divisor must be 2 or 4");
+    if (N % 2 || N % rd) return fail(MIMO_ERR_VALUE, "N must be even and divisible by rotary_dim_divisor");
+    if (C * R > 64 || N > 64 || P > 64 || R > 8)
+        return fail(MIMO_ERR_UNSUPPORTED, "the stage-2 backward supports R * chunk_size, N and P up to 64 and R up to 8");
+    if (S > (int64_t)1 << 30 || B * H * ((S + C - 1) / C + 8) > (int64_t)1 << 31)
+        return fail(MIMO_ERR_UNSUPPORTED, "problem too large");
+    pl->W = (int)(N / rd);
+    pl->nc = (int)((S + C - 1) / C);
+    // one workgroup per compute unit (the chunk pass keeps nine 64 x 64 fp32 tiles in LDS)
+    int64_t L = (pl->nc * B * H + 255) / 256;
+    if (L < 1) L = 1;
+    if (L > pl->nc) L = pl->nc;
+    pl->L = (int)L;
+    pl->nseg = (int)((pl->nc + L - 1) / L);
+    if (pl->nseg > 65535) return fail(MIMO_ERR_UNSUPPORTED, "too many segments");
+    pl->F = (L % 2 == 0 && L >= 4) ? 2 : 1;
+    pl->nsub = (pl->nseg - 1) * pl->F;
+    size_t off = 0;
+    pl->off_agg = off;
+    if (pl->nseg > 1) off = align256(off + (size_t)B * H * pl->nsub * N * P * 4);
+    pl->off_decay = off;
+    if (pl->nseg > 1) off = align256(off + (size_t)B * H * pl->nsub * 4);
+    pl->off_mv = off;
+    off = align256(off + (size_t)B * H * pl->nseg * R * P * 4);
+    pl->off_d = off;
+    off = align256(off + (size_t)B * H * pl->nseg * 4);
+    pl->ws_bytes = off;
+    return MIMO_OK;
+}
+
+mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events) {
+    g_err.clear();
+    PlanB2 pl;
+    mimo_status s = make_plan_b2(a, &pl);
+    if (s != MIMO_OK) return s;
+    if (!a->dout || !a->q || !a->k || !a->v || !a->q_bias || !a->k_bias || !a->mimo_v || !a->states ||
+        !a->qk_dot || !a->da_cs || !a->da_cs_rev || !a->dt || !a->trap || !a->segsum || !a->angles)
+        return fail(MIMO_ERR_VALUE, "a required input pointer is NULL");
+    if (!a->dq || !a->dk || !a->dv || !a->dmimo_v || !a->dangles || !a->dfactor || !a->dgamma || !a->dda ||
+        !a->dssda || !a->dda_cs_rev || !a->dda_cs)
+        return fail(MIMO_ERR_VALUE, "an output pointer is NULL");
+    if ((a->dd != nullptr) != (a->d != nullptr)) return fail(MIMO_ERR_VALUE, "dd must be given exactly when d is given");
+    if (a->workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && a->workspace == nullptr))
+        return fail(MIMO_ERR_VALUE, "workspace too small: need %zu bytes, got %zu", pl.ws_bytes, a->workspace_bytes);
+    if (pl.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(a->workspace) & 255))
+        return fail(MIMO_ERR_VALUE, "workspace must be 256-byte aligned");
+    if (events != nullptr)
+        for (int i = 0; i < MIMO_TIMED_EVENTS; ++i)
+            if (events[i] == nullptr) return fail(MIMO_ERR_VALUE, "timing event %d is NULL", i);
+    if ((s = check_device()) != MIMO_OK) return s;
+    b2::Params2 p = {};
+    p.B = (int)a->B; p.S = (int)a->S; p.H = (int)a->H; p.G = (int)a->G; p.R = (int)a->R; p.N = (int)a->N;
+    p.P = (int)a->P; p.C = a->chunk_size; p.W = pl.W; p.nc = pl.nc; p.L = pl.L; p.nseg = pl.nseg; p.F = pl.F;
+    p.nsub = pl.nsub; p.reduce_o = a->mimo_o != nullptr; p.has_d = a->d != nullptr; p.out_f32 = a->out_f32 != 0;
+    p.dout = a->dout; p.q = a->q; p.k = a->k; p.v = a->v; p.states = a->states; p.qk_dot = a->qk_dot;
+    p.trap = a->trap; p.q_bias = a->q_bias; p.k_bias = a->k_bias; p.mimo_v = a->mimo_v; p.mimo_o = a->mimo_o;
+    p.da_cs = a->da_cs; p.da_cs_rev = a->da_cs_rev; p.dt = a->dt; p.segsum = a->segsum; p.angles = a->angles;
+    p.d = a->d;
+    p.dq = a->dq; p.dk = a->dk; p.dv = a->dv; p.dmimo_v = a->dmimo_v; p.dangles = a->dangles;
+    p.dfactor = a->dfactor; p.dgamma = a->dgamma; p.dda = a->dda; p.dssda = a->dssda;
+    p.dda_cs_rev = a->dda_cs_rev; p.dda_cs = a->dda_cs; p.dd = a->dd;
+    unsigned char* ws = static_cast<unsigned char*>(a->workspace);
+    p.agg = pl.nseg > 1 ? reinterpret_cast<float*>(ws + pl.off_agg) : nullptr;
+    p.decay = pl.nseg > 1 ? reinterpret_cast<float*>(ws + pl.off_decay) : nullptr;
+    p.part_mv = reinterpret_cast<float*>(ws + pl.off_mv);
+    p.part_d = reinterpret_cast<float*>(ws + pl.off_d);
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) -> mimo_status {
+        if (events == nullptr) return MIMO_OK;
+        if (hipEventRecord(static_cast<hipEvent_t>(events[i]), st) != hipSuccess)
+            return fail(MIMO_ERR_HIP, "hipEventRecord failed");
+        return MIMO_OK;
+    };
+    auto launch2 = [&](const void* f, dim3 grid, int lds) -> mimo_status {
+        void* args[] = {&p};
+        const hipError_t e = hipLaunchKernel(f, grid, dim3(b2::NTHR), args, (size_t)lds, st);
+        if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return MIMO_OK;
+    };
+    auto set_lds2 = [&](const void* f, int bytes) -> mimo_status {
+        if (bytes <= 64 * 1024) return MIMO_OK;
+        if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+            return fail(MIMO_ERR_HIP, "hipFuncSetAttribute(MaxDynamicSharedMemorySize=%d) failed", bytes);
+        return MIMO_OK;
+    };
+    Params pp = {};
+    pp.B = p.B; pp.H = p.H; pp.G = p.G;
+    const void* kmain = p.out_f32 ? reinterpret_cast<const void*>(&b2::k_main2<true>)
+                                  : reinterpret_cast<const void*>(&b2::k_main2<false>);
+    const int lds_main = b2::L2::TOTAL * 4, lds_agg = b2::L2::AGG_TOTAL * 4;
+    if ((s = set_lds2(kmain, lds_main)) != MIMO_OK) return s;
+    if ((s = mark(0)) != MIMO_OK) return s;
+    if (pl.nseg > 1) {
+        const void* kagg = reinterpret_cast<const void*>(&b2::k_agg2);
+        if ((s = set_lds2(kagg, lds_agg)) != MIMO_OK) return s;
+        if ((s = launch2(kagg, dim3(grid_blocks(pp, pl.nsub)), lds_agg)) != MIMO_OK) return s;
+        if ((s = mark(1)) != MIMO_OK) return s;
+        const int NP = p.N * p.P;
+        if ((s = launch2(reinterpret_cast<const void*>(&b2::k_scan_rev), dim3((NP + 255) / 256, p.B * p.H), 0)) !=
+            MIMO_OK)
+            return s;
+    } else if ((s = mark(1)) != MIMO_OK) {
+        return s;
+    }
+    if ((s = mark(2)) != MIMO_OK) return s;
+    if ((s = launch2(kmain, dim3(grid_blocks(pp, pl.nseg)), lds_main)) != MIMO_OK) return s;
+    if ((s = mark(3)) != MIMO_OK) return s;
+    const long tot = (long)p.B * p.H * p.R * p.P;
+    if ((s = launch2(reinterpret_cast<const void*>(&b2::k_finish2), dim3((unsigned)((tot + 255) / 256)), 0)) != MIMO_OK)
+        return s;
+    if ((s = mark(4)) != MIMO_OK) return s;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return MIMO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -738,6 +870,22 @@ mimo_status mimo_siso_fwd(const mimo_siso_fwd_args* a, void* stream) { return ru
 mimo_status mimo_siso_fwd_timed(const mimo_siso_fwd_args* a, void* stream, void* const* events) {
     if (events == nullptr) return fail(MIMO_ERR_VALUE, "events must not be NULL");
     return run_siso(a, stream, events);
+}
+
+mimo_status mimo_bwd_bwd_workspace_size(const mimo_bwd_bwd_args* args, size_t* bytes) {
+    PlanB2 pl;
+    const mimo_status s = make_plan_b2(args, &pl);
+    if (s != MIMO_OK) return s;
+    if (bytes == nullptr) return fail(MIMO_ERR_VALUE, "bytes must not be NULL");
+    *bytes = pl.ws_bytes;
+    return MIMO_OK;
+}
+
+mimo_status mimo_bwd_bwd(const mimo_bwd_bwd_args* a, void* stream) { return run_b2(a, stream, nullptr); }
+
+mimo_status mimo_bwd_bwd_timed(const mimo_bwd_bwd_args* a, void* stream, void* const* events) {
+    if (events == nullptr) return fail(MIMO_ERR_VALUE, "events must not be NULL");
+    return run_b2(a, stream, events);
 }
 
 }  // extern "C"

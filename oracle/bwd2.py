@@ -128,19 +128,24 @@ def run(dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, da_cs, da_cs_rev,
             "bhtrn,bhtrp->bhnp", kap, Psi[:, :, sl])
     L.backward()
 
+    def grad(x):
+        # a quantity the loss does not reach (e.g. the state decay of a one-chunk
+        # sequence) has a zero derivative
+        return torch.zeros_like(x) if x.grad is None else x.grad
+
     out = {
-        "DQ": Q0.grad.permute(0, 2, 3, 1, 4).reshape(B, S * R, H, N),
-        "DK": K0.grad.permute(0, 2, 3, 1, 4).reshape(B, S * R, H, N),
-        "DV": V.grad,
-        "DMIMO_V": MV.grad,
-        "DANGLES": ANG.grad,
-        "DFACTOR": FAC.grad,
-        "DGAMMA": GAM.grad,
-        "DDA": CSS.grad,
-        "DSSDA": SEG.grad,
-        "DDA_CS_REV": REV.grad,
-        "DDA_CS": CSI.grad,
-        "DD": None if D is None else D.grad,
+        "DQ": grad(Q0).permute(0, 2, 3, 1, 4).reshape(B, S * R, H, N),
+        "DK": grad(K0).permute(0, 2, 3, 1, 4).reshape(B, S * R, H, N),
+        "DV": grad(V),
+        "DMIMO_V": grad(MV),
+        "DANGLES": grad(ANG),
+        "DFACTOR": grad(FAC),
+        "DGAMMA": grad(GAM),
+        "DDA": grad(CSS),
+        "DSSDA": grad(SEG),
+        "DDA_CS_REV": grad(REV),
+        "DDA_CS": grad(CSI),
+        "DD": None if D is None else grad(D),
     }
     return {kk: (None if vv is None else vv.detach().numpy()) for kk, vv in out.items()}
 

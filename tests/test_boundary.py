@@ -37,7 +37,8 @@ def test_library_exports_every_declared_symbol():
 
 @pytest.mark.parametrize("cls,cname", [(_lib.MimoBwdFwdArgs, "mimo_bwd_fwd_args"),
                                         (_lib.MimoFwdArgs, "mimo_fwd_args"),
-                                        (_lib.MimoSisoFwdArgs, "mimo_siso_fwd_args")])
+                                        (_lib.MimoSisoFwdArgs, "mimo_siso_fwd_args"),
+                                        (_lib.MimoBwdBwdArgs, "mimo_bwd_bwd_args")])
 def test_struct_layout_matches_c(tmp_path, cls, cname):
     fields = [f[0] for f in cls._fields_]
     prog = ["#include <stddef.h>", "#include <stdio.h>", '#include "mimo_bwd_fwd.h"', "int main(void){",

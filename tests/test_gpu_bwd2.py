@@ -1,0 +1,159 @@
+"""GPU parity of the stage-2 backward ``mamba3_mimo_bwd_bwd`` (through the C ABI)
+against the float64 oracle ``oracle.bwd2``.
+
+Both sides take the same seeded inputs and the same first-stage caches (states
+and qk_dot from the CPU contract oracle O1, so no oracle input comes from the
+HIP path). With fp32 outputs every one of the twelve gradients must satisfy
+RMS(gpu - oracle) / RMS(oracle) < 1e-4 (fp32 intermediates against float64;
+a tenth of the operator's 1e-3 bar); with the default bf16 outputs DQ, DK and
+DV must be within 1e-3 of the oracle rounded to bf16. Cases: several segments
+and ragged tails, GQA, R = 1..8, both dout layouts, with and without d,
+rotary divisor 2, the perf shape on sampled heads, every element written, and
+the shapes beyond the kernel's tiles (NotImplementedError).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bwd2, o1
+from synth.inputs import CONFIGS, Case, make_inputs
+
+from ._parity import log, rel_rms
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+ORDER = ("dout", "q", "k", "v", "q_bias", "k_bias", "mimo_v", "states", "qk_dot", "da_cs", "da_cs_rev", "dt",
+         "trap", "segsum", "angles")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from mamba_mimo_chunked_amd import _lib
+    _lib.lib()
+
+
+def _caches(inp):
+    """First-stage caches from the CPU contract oracle, as bf16 tensors."""
+    _, states, _, _, qk = o1.run_inputs(inp)
+    return torch.from_numpy(states).to(torch.bfloat16), torch.from_numpy(qk).to(torch.bfloat16)
+
+
+def _run_gpu(inp, states, qk, output_dtype=None):
+    from mamba_mimo_chunked_amd import mamba3_mimo_bwd_bwd
+    dev = dict(inp, states=states, qk_dot=qk)
+    args = [dev[n].to("cuda") for n in ORDER]
+    mo = None if inp["mimo_o"] is None else inp["mimo_o"].to("cuda")
+    d = None if inp["d"] is None else inp["d"].to("cuda")
+    out = mamba3_mimo_bwd_bwd(*args, mimo_o=mo, d=d, chunk_size=inp["chunk_size"],
+                              rotary_dim_divisor=inp["rotary_dim_divisor"], output_dtype=output_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle(inp, states, qk):
+    return bwd2.run_inputs(inp, states, qk)
+
+
+def _compare(got, ref, label, tol=TOL):
+    errs = {}
+    for key in bwd2.NAMES:
+        r = ref[key]
+        if r is None:
+            assert got[key] is None, f"{label}{key}: expected None"
+            continue
+        g = got[key].double().cpu().numpy()
+        assert g.shape == r.shape, f"{label}{key}: shape {g.shape} vs {r.shape}"
+        assert np.isfinite(g).all(), f"{label}{key}: non-finite"
+        e = rel_rms(g, r)
+        errs[key] = e
+        assert e < tol, f"{label}{key}: rel RMS {e:.3e} >= {tol}"
+    return errs
+
+
+CASES = [
+    CONFIGS["tiny"],
+    Case(1, 300, 3, 1, 64, 64, 4, 16, name="b2_segments_tail"),
+    Case(2, 777, 4, 2, 32, 64, 2, 16, name="b2_gqa_tail_r2"),
+    Case(1, 500, 2, 1, 64, 64, 1, 64, name="b2_r1_c64"),
+    Case(1, 260, 2, 1, 32, 32, 8, 8, name="b2_r8_c8"),
+    Case(1, 95, 1, 1, 32, 48, 3, 6, rd=2, name="b2_r3_c6_rd2_p48"),
+    Case(1, 333, 2, 2, 64, 32, 4, 16, reduce_o=False, has_z=False, has_d=True, name="b2_nonreduced"),
+    Case(2, 257, 4, 4, 64, 64, 4, 16, reduce_o=False, has_z=False, has_d=False, name="b2_nonreduced_nod"),
+    Case(1, 1, 1, 1, 16, 16, 2, 16, name="b2_one_token"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c.name)
+def test_bwd2_fp32_outputs(case):
+    log(f"[bwd2] {case.name} B={case.B} S={case.S} H={case.H} G={case.G} N={case.N} P={case.P} "
+        f"R={case.R} C={case.C}")
+    inp = make_inputs(case)
+    states, qk = _caches(inp)
+    got = _run_gpu(inp, states, qk, torch.float32)
+    ref = _oracle(inp, states, qk)
+    errs = _compare(got, ref, f"{case.name}: ")
+    log("    " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+
+
+@pytest.mark.parametrize("case", [Case(1, 300, 3, 1, 64, 64, 4, 16, name="b2_bf16_out")], ids=lambda c: c.name)
+def test_bwd2_bf16_outputs(case):
+    inp = make_inputs(case)
+    states, qk = _caches(inp)
+    got = _run_gpu(inp, states, qk)
+    ref = _oracle(inp, states, qk)
+    for key in ("DQ", "DK", "DV"):
+        assert got[key].dtype == torch.bfloat16
+        r = torch.from_numpy(ref[key]).to(torch.bfloat16).double().numpy()
+        e = rel_rms(got[key].double().cpu().numpy(), r)
+        log(f"    {key} vs bf16(oracle): {e:.2e}")
+        assert e < 1e-3
+    for key in ("DMIMO_V", "DANGLES", "DFACTOR", "DGAMMA", "DDA", "DSSDA", "DDA_CS_REV", "DDA_CS", "DD"):
+        assert got[key].dtype == torch.float32
+        assert rel_rms(got[key].double().cpu().numpy(), ref[key]) < TOL
+
+
+def test_bwd2_perf_shape_sampled_heads():
+    """The benchmark's shape (B=1, S=8192, H=16, N=P=64, R=4, C=16); the oracle runs on
+    sampled heads (heads are independent)."""
+    case = CONFIGS["perf_s8192"].with_(seed=17)
+    inp = make_inputs(case)
+    states, qk = _caches(inp)
+    got = _run_gpu(inp, states, qk, torch.float32)
+    for h in (0, 11):
+        sl = o1.slice_heads(inp, 0, h)
+        ref = _oracle(sl, states[:, h:h + 1], qk[:, h:h + 1])
+        sub = {}
+        for key in bwd2.NAMES:
+            x = got[key]
+            if x is None:
+                sub[key] = None
+            elif key in ("DQ", "DK", "DV", "DANGLES"):
+                sub[key] = x[:, :, h:h + 1]
+            else:
+                sub[key] = x[:, h:h + 1]
+        errs = _compare(sub, ref, f"perf h={h}: ")
+        log(f"    h={h} " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+
+
+def test_bwd2_every_element_written_and_deterministic():
+    case = Case(1, 300, 2, 1, 64, 64, 4, 16, name="det")
+    inp = make_inputs(case)
+    states, qk = _caches(inp)
+    a = _run_gpu(inp, states, qk, torch.float32)
+    b = _run_gpu(inp, states, qk, torch.float32)
+    for key in bwd2.NAMES:
+        assert torch.isfinite(a[key]).all(), key
+        assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("case", [Case(1, 64, 1, 1, 128, 64, 2, 16, name="n128"),
+                                  Case(1, 64, 1, 1, 64, 64, 8, 16, name="rc128")], ids=lambda c: c.name)
+def test_bwd2_beyond_tiles_rejected(case):
+    inp = make_inputs(case)
+    states, qk = _caches(inp)
+    with pytest.raises(NotImplementedError):
+        _run_gpu(inp, states, qk)
