@@ -15,7 +15,9 @@ Other operations (``--op``), each on its own workload line:
                 backward stage computes), same workload;
   bwd_fwd_fp32  the backward stage with fp32 intermediates, same workload;
   siso          the SISO forward mamba3_siso_fwd, B=1, S=8192, H=Hq=16, K=128,
-                V=64, chunk 64, bf16 (--config siso_s8192_k128_fp16 for fp16).
+                V=64, chunk 64, bf16 (--config siso_s8192_k128_fp16 for fp16);
+  bwd_bwd       the stage-2 backward mamba3_mimo_bwd_bwd on the same workload as
+                the first stage, fed that stage's states and qk_dot.
 
 Prints progress on stderr and ONE JSON line on stdout.
 """
@@ -39,6 +41,8 @@ METRIC = "mimo_bwd_fwd ms/call + HBM GB/s at B1 S8192 H16 G1 N=P=64 R4 C16"
 FWD_METRIC = "mimo_fwd (layer output) ms/call + HBM GB/s at B1 S8192 H16 G1 N=P=64 R4 C16"
 FP32_METRIC = "mimo_bwd_fwd_fp32 (fp32 intermediates) ms/call + HBM GB/s at B1 S8192 H16 G1 N=P=64 R4 C16"
 SISO_METRIC = "mamba3_siso_fwd ms/call + HBM GB/s at B1 S8192 H=Hq=16 K128 V64 C64"
+BWD2_METRIC = "mamba3_mimo_bwd_bwd (stage-2 backward) ms/call + HBM GB/s at B1 S8192 H16 G1 N=P=64 R4 C16"
+VALU_FP32_PEAK_TFLOPS = 157.3   # fp32 FMA counted as two flops
 MFMA_FP32_PEAK_TFLOPS = 157.3
 PAGES_MS = 53.849475          # the pages' Ascend910_9382 median at this exact workload (context)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
@@ -51,11 +55,12 @@ ALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
 ALU_NONPACKED_TOPS = ALU_PEAK_TOPS / 2
 
 KERNEL_SOURCES = [ROOT / "mamba_mimo_chunked_amd" / "csrc" / n for n in ("mimo_kernels.hpp", "mimo_bwd_fwd.hip")]
-KERNEL_SOURCES += [ROOT / "mamba_mimo_chunked_amd" / "csrc" / "mimo_f32.hpp"]
+KERNEL_SOURCES += [ROOT / "mamba_mimo_chunked_amd" / "csrc" / n for n in ("mimo_f32.hpp", "mimo_bwd2.hpp")]
 TRAFFIC_FILES = {"bwd_fwd": ROOT / "profiles" / "k_main_perf_s8192_traffic.json",
                  "fwd": ROOT / "profiles" / "k_main_fwd_perf_s8192_traffic.json",
                  "bwd_fwd_fp32": ROOT / "profiles" / "k_chunk32_perf_s8192_traffic.json",
-                 "siso": ROOT / "profiles" / "k_chunk32_siso_s8192_k128_traffic.json"}
+                 "siso": ROOT / "profiles" / "k_chunk32_siso_s8192_k128_traffic.json",
+                 "bwd_bwd": ROOT / "profiles" / "k_main2_perf_s8192_traffic.json"}
 
 
 def log(msg):
@@ -179,6 +184,34 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
+def bwd2_bytes(c) -> int:
+    """Algorithmic bytes of the stage-2 backward: its inputs (dout, q, k, v, the caches,
+    controls, segsum, angles, parameters) read once and its twelve outputs written once
+    (DQ, DK, DV in bf16)."""
+    B, S, H, G, R, N, P, C = c.B, c.S, c.H, c.G, c.R, c.N, c.P, c.C
+    nc = (S + C - 1) // C
+    W = N // c.rd
+    b = B * S * H * P * 2 * (1 if c.reduce_o else R)          # dout
+    b += 2 * B * S * R * G * N * 2 + B * S * H * P * 2          # q, k, v
+    b += B * H * nc * N * P * 2 + B * H * S * R * R * 2         # states, qk_dot
+    b += 3 * B * H * S * 4 + B * H * S * 2 + B * H * nc * C * C * 4 + B * S * H * W * 4
+    b += 2 * H * R * N * 4 + (1 + c.reduce_o) * H * R * P * 4 + (H * 4 if c.has_d else 0)
+    b += 2 * B * S * R * H * N * 2 + B * S * H * P * 2          # DQ, DK, DV
+    b += B * H * R * P * 4 + B * S * H * W * 4 + 5 * B * H * S * 4 + B * H * nc * C * C * 4
+    return b + (B * H * 4 if c.has_d else 0)
+
+
+def bwd2_flops(c) -> int:
+    """Multiply-adds (x2) of the stage-2 contractions: per chunk, over the strictly
+    causal (token, rank) pairs, the causal block, dPhiO Psi^T and the three products
+    with them (3N + 2P per pair), and the four products with a state ([C*R, N] x [N, P]:
+    dPhiO S^T, Psi dS^T, kappa dS, the dS increment)."""
+    B, S, H, R, N, P, C = c.B, c.S, c.H, c.R, c.N, c.P, c.C
+    full, tail = S // C, S - (S // C) * C
+    pairs = full * C * (C - 1) // 2 + tail * (tail - 1) // 2
+    return B * H * 2 * (pairs * R * R * (3 * N + 2 * P) + 4 * S * R * N * P)
+
+
 def siso_bytes(c) -> int:
     """Algorithmic bytes of the SISO forward: every input once, the output once."""
     B, S, Hq, H, K, V, A = c.B, c.S, c.Hq, c.H, c.K, c.V, c.width
@@ -219,7 +252,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--mode", choices=("op", "copy"), default="op",
                     help="copy: a plain device copy of known size, for counter calibration")
-    ap.add_argument("--op", choices=("bwd_fwd", "fwd", "bwd_fwd_fp32", "siso"), default="bwd_fwd",
+    ap.add_argument("--op", choices=("bwd_fwd", "fwd", "bwd_fwd_fp32", "siso", "bwd_bwd"), default="bwd_fwd",
                     help="operation to time (default: the backward first stage)")
     a = ap.parse_args()
     if a.gpus != 1:
@@ -231,7 +264,7 @@ def main():
 
     import torch
     from mamba_mimo_chunked_amd import _lib
-    from mamba_mimo_chunked_amd.api import _make_args, _make_fwd_args, _make_siso_args
+    from mamba_mimo_chunked_amd.api import _make_args, _make_bwd2_args, _make_fwd_args, _make_siso_args
     from synth.inputs import API_ORDER, CONFIGS, SISO_CONFIGS, SISO_ORDER, make_inputs, make_siso_inputs
 
     if not torch.cuda.is_available():
@@ -264,11 +297,15 @@ def main():
     inp = make_siso_inputs(case) if siso_op else make_inputs(case)
     log(f"inputs generated in {time.perf_counter() - t:.1f}s")
     L = _lib.lib()
+    bwd2_op = op == "bwd_bwd"
+    fwd = op == "fwd"
     if siso_op:
         alg_bytes, alg_flops, alu_ops = siso_bytes(case), siso_flops(case), siso_alu_ops(case)
         mfma_peak, mfma_unit_dtype = MFMA_FP32_PEAK_TFLOPS, "fp32"
+    elif bwd2_op:
+        alg_bytes, alg_flops, alu_ops = bwd2_bytes(case), bwd2_flops(case), 0
+        mfma_peak, mfma_unit_dtype = VALU_FP32_PEAK_TFLOPS, "fp32 (vector FMA)"
     else:
-        fwd = op == "fwd"
         alg_bytes, alg_flops = algorithmic_bytes(case, fwd), algorithmic_flops(case, fwd)
         alu_ops = algorithmic_alu_ops(case, fwd)
         fp32 = op == "bwd_fwd_fp32"
@@ -294,6 +331,39 @@ def main():
         ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
         cargs = [_make_siso_args(dims, odt, d, o, ws, ws_bytes) for d, o in sets]
         run_call, run_timed = L.mimo_siso_fwd, L.mimo_siso_fwd_timed
+    elif bwd2_op:
+        from mamba_mimo_chunked_amd import mamba_mimo_bwd_fwd
+        B, S, H, G, R, N, P, C = case.B, case.S, case.H, case.G, case.R, case.N, case.P, case.C
+        nc = case.nchunks
+        W = N // case.rd
+        d0 = {n: (None if inp[n] is None else inp[n].to(dev)) for n in API_ORDER}
+        st1 = mamba_mimo_bwd_fwd(*[d0[n] for n in API_ORDER], C, case.rd)   # the caches
+        torch.cuda.synchronize()
+        caches = (st1.states, st1.qk_dot)
+        f32 = torch.float32
+        for _ in range(nsets):
+            d = {n: (None if inp[n] is None else inp[n].to(dev)) for n in API_ORDER}
+            d["states"], d["qk_dot"] = caches[0].clone(), caches[1].clone()
+            outs = {"DQ": torch.empty((B, S * R, H, N), dtype=torch.bfloat16, device=dev),
+                    "DK": torch.empty((B, S * R, H, N), dtype=torch.bfloat16, device=dev),
+                    "DV": torch.empty((B, S, H, P), dtype=torch.bfloat16, device=dev),
+                    "DMIMO_V": torch.empty((B, H, R, P), dtype=f32, device=dev),
+                    "DANGLES": torch.empty((B, S, H, W), dtype=f32, device=dev),
+                    "DSSDA": torch.empty((B, H, nc, C, C), dtype=f32, device=dev),
+                    "DD": torch.empty((B, H), dtype=f32, device=dev) if case.has_d else None}
+            for key in ("DFACTOR", "DGAMMA", "DDA", "DDA_CS_REV", "DDA_CS"):
+                outs[key] = torch.empty((B, H, S), dtype=f32, device=dev)
+            sets.append((d, outs))
+        dims = (B, S, H, G, R, N, P)
+        probe = _make_bwd2_args(dims, C, case.rd, False, sets[0][0], sets[0][1])
+        nbytes = ctypes.c_size_t(0)
+        st = L.mimo_bwd_bwd_workspace_size(ctypes.byref(probe), ctypes.byref(nbytes))
+        if st != 0:
+            raise RuntimeError(_lib.last_error())
+        ws_bytes = int(nbytes.value)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        cargs = [_make_bwd2_args(dims, C, case.rd, False, d, o, ws, ws_bytes) for d, o in sets]
+        run_call, run_timed = L.mimo_bwd_bwd, L.mimo_bwd_bwd_timed
     else:
         B, S, H, G, R, N, P, C = case.B, case.S, case.H, case.G, case.R, case.N, case.P, case.C
         nc = case.nchunks
@@ -353,6 +423,8 @@ def main():
     names = ("k_agg", "k_scan", "k_main", "k_finish")
     if f32_names:
         names = ("k_chunk32_agg", "k_scan", "k_chunk32_main", "k_finish")
+    if bwd2_op:
+        names = ("k_agg2", "k_scan_rev", "k_main2", "k_finish2")
     per = {n: 0.0 for n in names}
     for e in evs:
         for j, n in enumerate(names):
@@ -379,6 +451,10 @@ def main():
         "hbm": (alg_bytes / (HBM_PEAK_GBS * 1e9), hbm_gbps_main, HBM_PEAK_GBS, "GB/s"),
         "mfma": (alg_flops / (mfma_peak * 1e12), mfma_tflops, mfma_peak, "TFLOP/s"),
     }
+    if bwd2_op:
+        # the contractions run as fp32 vector FMAs: the fp32 vector peak is the compute roof
+        roofs["alu"] = (alg_flops / (VALU_FP32_PEAK_TFLOPS * 1e12), mfma_tflops, VALU_FP32_PEAK_TFLOPS, "TFLOP/s")
+        del roofs["mfma"]
     bound = max(roofs, key=lambda k: roofs[k][0])
     _, achieved, peak, unit = roofs[bound]
     roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
@@ -390,7 +466,7 @@ def main():
         "hbm_frac": round(hbm_gbps_main / HBM_PEAK_GBS, 4),
         "alu_frac": round(alu_tops / ALU_PEAK_TOPS, 4),
         "alu_frac_nonpacked": round(alu_tops / ALU_NONPACKED_TOPS, 4),
-        "mfma_frac": round(mfma_tflops / mfma_peak, 5)})
+        "mfma_frac": round(mfma_tflops / mfma_peak, 5) if not bwd2_op else None})
 
     cpu = None
     if not a.no_cpu:
@@ -398,20 +474,31 @@ def main():
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
         log(f"oracle CPU baseline on the whole workload ({threads} OpenMP threads)")
         t = time.perf_counter()
+        sample = f"the whole {a.config} workload once (OpenMP over the {case.B * case.H} (batch, head) pairs)"
+        scale = 1.0
         if siso_op:
             siso.run(*[inp[n] for n in SISO_ORDER], chunk_size=case.C)
+        elif bwd2_op:
+            from oracle import bwd2
+            heads = (0, case.H // 2)
+            for h in heads:
+                sl = o1.slice_heads(inp, 0, h)
+                bwd2.run_inputs(sl, caches[0][:, h:h + 1].cpu(), caches[1][:, h:h + 1].cpu())
+            scale = case.B * case.H / len(heads)
+            sample = (f"{len(heads)} of the {case.B * case.H} (batch, head) pairs of {a.config} (float64 autograd, "
+                      f"one thread per op), scaled by {scale:g} to the whole workload")
         elif op == "fwd":
             o1.run_fwd_inputs(inp)
         else:
             o1.run_inputs(inp, fp32=op == "bwd_fwd_fp32")
-        cpu_ms = (time.perf_counter() - t) * 1e3
-        cpu = {"value": round(cpu_ms, 3), "unit": "ms/call", "cores": min(threads, case.B * case.H),
-               "kind": "oracle",
-               "sample": f"the whole {a.config} workload once (OpenMP over the {case.B * case.H} (batch, head) pairs)"}
+        cpu_ms = (time.perf_counter() - t) * 1e3 * scale
+        cores = torch.get_num_threads() if bwd2_op else min(threads, case.B * case.H)
+        cpu = {"value": round(cpu_ms, 3), "unit": "ms/call", "cores": cores, "kind": "oracle", "sample": sample}
         log(f"oracle: {cpu_ms:.1f} ms")
 
     gbps = alg_bytes / (ms * 1e-3) / 1e9
-    metric = {"bwd_fwd": METRIC, "fwd": FWD_METRIC, "bwd_fwd_fp32": FP32_METRIC, "siso": SISO_METRIC}[op]
+    metric = {"bwd_fwd": METRIC, "fwd": FWD_METRIC, "bwd_fwd_fp32": FP32_METRIC, "siso": SISO_METRIC,
+              "bwd_bwd": BWD2_METRIC}[op]
     if siso_op:
         config = {"workload": a.config, "op": op, "B": case.B, "S": case.S, "Hq": case.Hq, "H": case.H,
                   "K": case.K, "V": case.V, "A": case.width, "chunk_size": case.C, "dtype": case.dtype,
@@ -423,7 +510,7 @@ def main():
                   "chunk_size": C, "rotary_dim_divisor": case.rd, "reduce_o": case.reduce_o,
                   "has_z": case.has_z, "has_d": case.has_d, "buffer_sets": nsets,
                   "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops}
-        dtype = "f32" if op == "bwd_fwd_fp32" else "bf16"
+        dtype = "f32" if op in ("bwd_fwd_fp32", "bwd_bwd") else "bf16"
     line = {
         "metric": metric,
         "value": round(ms, 5),
