@@ -242,7 +242,8 @@ mimo_status mimo_siso_fwd_timed(const mimo_siso_fwd_args *args, void *stream, vo
  * dq, dk, dv are bf16, or fp32 when out_f32 != 0; the others fp32.
  * Inputs as for mimo_bwd_fwd (dout reduced or not, bf16 q/k/v/dout/trap) plus
  * states [B,H,nc,N,P] and qk_dot [B,H,S,R,R] (bf16). Limits: R * chunk_size,
- * N and P at most 64, R at most 8 (MIMO_ERR_UNSUPPORTED otherwise). Ownership, asynchrony
+ * N and P at most 64, R at most 8, P a multiple of 8 (MIMO_ERR_UNSUPPORTED
+ * otherwise). Ownership, asynchrony
  * and errors as for mimo_bwd_fwd.
  */
 typedef struct mimo_bwd_bwd_args {

@@ -28,7 +28,8 @@
 namespace mimo {
 namespace b2 {
 
-constexpr int NTHR = 256;
+constexpr int NTHR = 256;      // the aggregate (two workgroups per CU)
+constexpr int NTHR2 = 512;     // the chunk pass (one workgroup per CU: eight waves hide more latency)
 constexpr int LD = 65;              // row pitch (floats) of every tile
 constexpr int TILE = 64 * LD;       // floats per tile
 
@@ -47,54 +48,81 @@ struct Params2 {
 __device__ __forceinline__ float bf(unsigned short x) { return __uint_as_float(static_cast<unsigned>(x) << 16); }
 __device__ __forceinline__ unsigned short to_bf(float x) { return static_cast<unsigned short>(pk2(0.f, x) >> 16); }
 
-// C(i, j) = sum_k A(i, k) B(k, j) (* sk[k]) for i < Mi, j < Nj, k < K, with
-// A(i, k) = A[i * ai + k * ak] and B(k, j) = B[k * bk + j * bj]; thread (ti, tj) =
-// (tid / 16, tid % 16) owns rows ti + 16x and columns tj + 16y, and hands each
-// result to epi(i, j, value).
-template <typename F>
-__device__ __forceinline__ void gemm64(int Mi, int Nj, int K, const float* A, int ai, int ak, const float* B, int bk,
-                                       int bj, const float* sk, F&& epi) {
+// C(i, j) = sum_k A(i, k) B(k, j) (* sk[k]) for i < Mi, j < Nj, k < K (all <= 64) on
+// [64][LD] LDS tiles. AK1: A(i, k) = A[i*LD + k], else A[k*LD + i]; BK1: B(k, j) =
+// B[j*LD + k], else B[k*LD + j]. Of NT threads, thread (ti, tj) = (tid / 16, tid % 16)
+// owns rows ti + (NT/16) x and columns tj + 16 y and hands each result to
+// epi(i, j, value). Rows and columns past Mi / Nj are computed too (their reads stay
+// inside the tiles) and dropped, so the inner loop has no bounds tests; with the
+// layouts known at compile time every operand read is one base address plus a
+// constant offset.
+template <int NT, bool AK1, bool BK1, bool SK, typename F>
+__device__ __forceinline__ void gemm64(int Mi, int Nj, int K, const float* A, const float* B, const float* sk,
+                                       F&& epi) {
+    constexpr int RX = 64 * 16 / NT, RS = NT / 16;   // rows per thread, row stride
+    constexpr int AX = AK1 ? RS * LD : RS, AKS = AK1 ? 1 : LD;
+    constexpr int BY = BK1 ? 16 * LD : 16, BKS = BK1 ? 1 : LD;
     const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
-    float acc[4][4];
+    const float* pa = A + (AK1 ? ti * LD : ti);
+    const float* pb = B + (BK1 ? tj * LD : tj);
+    float acc[RX][4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < RX; ++x)
 #pragma unroll
         for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
+#pragma unroll 4
     for (int kk = 0; kk < K; ++kk) {
-        float a[4], bv[4];
-        const float s = sk ? sk[kk] : 1.f;
+        float a[RX], bv[4];
+        const float s = SK ? sk[kk] : 1.f;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int i = ti + 16 * x;
-            a[x] = i < Mi ? A[i * ai + kk * ak] : 0.f;
-        }
+        for (int x = 0; x < RX; ++x) a[x] = SK ? pa[x * AX + kk * AKS] * s : pa[x * AX + kk * AKS];
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const int j = tj + 16 * y;
-            bv[y] = j < Nj ? B[kk * bk + j * bj] * s : 0.f;
-        }
+        for (int y = 0; y < 4; ++y) bv[y] = pb[y * BY + kk * BKS];
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int x = 0; x < RX; ++x)
 #pragma unroll
             for (int y = 0; y < 4; ++y) acc[x][y] = __fmaf_rn(a[x], bv[y], acc[x][y]);
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < RX; ++x)
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
-            const int i = ti + 16 * x, j = tj + 16 * y;
+            const int i = ti + RS * x, j = tj + 16 * y;
             if (i < Mi && j < Nj) epi(i, j, acc[x][y]);
         }
 }
 
-// Block-wide sum (every thread passes its value; the result is valid in every thread).
+// Block-wide sum over NT threads (every thread passes its value; the result is
+// valid in every thread).
+template <int NT>
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    return red[0] + red[1] + red[2] + red[3];
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) s += red[w];
+    return s;
+}
+
+// Per-token sums over (rank, column): token t's sum of f(row, n) over rows
+// r*C + t (r < R) and n < N, by a group of 16 lanes (columns strided by 16, then
+// a butterfly over the group); out(t, value) is called by the group's first lane.
+template <int NT, typename F, typename O>
+__device__ __forceinline__ void token_sum(int cl, int R, int C, int N, F&& f, O&& out) {
+    const int grp = threadIdx.x >> 4, l = threadIdx.x & 15;
+    for (int t0 = 0; t0 < cl; t0 += NT / 16) {
+        const int t = t0 + grp;
+        float s = 0.f;
+        if (t < cl)
+            for (int r = 0; r < R; ++r)
+                for (int n = l; n < N; n += 16) s += f(r * C + t, n);
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+        if (l == 0 && t < cl) out(t, s);
+    }
 }
 
 // LDS layout (floats) of the chunk pass: q^, k^, Psi, dPhiO, S_c, dS, the causal
@@ -114,7 +142,7 @@ struct L2 {
 // Load chunk c's rotated q^ (and k^, Psi, the cached state and qk_dot, and the
 // per-row scalars when MAIN), dPhiO and exp(da_cs) into LDS. Rows past the chunk
 // (t >= cl) are zero.
-template <bool MAIN>
+template <bool MAIN, int NT>
 __device__ __forceinline__ void load_chunk(const Params2& p, float* sm, int b, int h, int g, int bh, int c, int cl) {
     const int R = p.R, N = p.N, P = p.P, C = p.C, W = p.W, M = N / 2;
     const int tid = threadIdx.x;
@@ -125,7 +153,7 @@ __device__ __forceinline__ void load_chunk(const Params2& p, float* sm, int b, i
     float* PS = sm + L2::PS;
     float* DPO = sm + (MAIN ? L2::DPO : L2::A_DPO);
     float* ECS = sm + (MAIN ? L2::ECS : L2::A_ECS);
-    for (int e = tid; e < rows * M; e += NTHR) {
+    for (int e = tid; e < rows * M; e += NT) {
         const int i = e / M, n = e % M;
         const int r = i / C, t = i % C;
         float qa = 0.f, qe = 0.f, ka = 0.f, ke = 0.f;
@@ -159,7 +187,7 @@ __device__ __forceinline__ void load_chunk(const Params2& p, float* sm, int b, i
             KH[i * LD + M + n] = ke;
         }
     }
-    for (int e = tid; e < rows * P; e += NTHR) {
+    for (int e = tid; e < rows * P; e += NT) {
         const int i = e / P, pc = e % P;
         const int r = i / C, t = i % C;
         float dpo = 0.f, psi = 0.f;
@@ -198,10 +226,27 @@ __device__ __forceinline__ void load_chunk(const Params2& p, float* sm, int b, i
     }
     if (MAIN) {
         const unsigned short* st = p.states + ((long)bh * p.nc + c) * N * P;
-        for (int e = tid; e < N * P; e += NTHR) sm[L2::SC + (e / P) * LD + e % P] = bf(st[e]);
+        // 8 consecutive bf16 a thread (N * P is a multiple of 8: P is a multiple of 8)
+        for (int e8 = tid; e8 < N * P / 8; e8 += NT) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(st + 8 * e8);
+            const int n = (8 * e8) / P, pc = (8 * e8) % P;
+            float* dst = sm + L2::SC + n * LD + pc;
+#pragma unroll
+            for (int d2 = 0; d2 < 4; ++d2) {
+                dst[2 * d2] = __uint_as_float(w[d2] << 16);
+                dst[2 * d2 + 1] = __uint_as_float(w[d2] & 0xffff0000u);
+            }
+        }
         const int RR = R * R;
-        for (int e = tid; e < cl * RR; e += NTHR)
+        for (int e = tid; e < cl * RR; e += NT)
             sm[L2::QKC + e] = bf(p.qk_dot[((long)bh * p.S + c0) * RR + e]);
+        // exp(segsum) of the chunk's strictly causal token pairs, in the output tile
+        // (free until the dQ^ products)
+        for (int e = tid; e < C * C; e += NT) {
+            const int t = e / C, s2 = e % C;
+            sm[L2::OUT + t * LD + s2] =
+                (s2 < t && t < cl) ? expf(p.segsum[(((long)bh * p.nc + c) * C + t) * C + s2]) : 0.f;
+        }
     }
 }
 
@@ -233,13 +278,14 @@ __global__ __launch_bounds__(NTHR, 2) void k_agg2(Params2 p) {
     for (int c = c_end - 1; c >= c_begin; --c) {
         const int cl = min(C, p.S - c * C);
         __syncthreads();
-        load_chunk<false>(p, sm, b, h, g, bh, c, cl);
+        load_chunk<false, NTHR>(p, sm, b, h, g, bh, c, cl);
         __syncthreads();
         const float dA = expf(p.da_cs[(long)bh * p.S + c * C + cl - 1]);
         // U[n][p] = sum_i Q^[i][n] exp(da_cs[t_i]) dPhiO[i][p] + dA U[n][p]; the thread that
         // owns (n, p) in the product is the only one reading and writing U[n][p]
-        gemm64(N, P, rows, QH, 1, LD, DPO, LD, 1, ECS,
-               [&](int n, int pc, float v) { U[n * LD + pc] = v + dA * U[n * LD + pc]; });
+        // A(n, i) = Q^[i][n], B(i, p) = dPhiO[i][p] scaled per i by exp(da_cs[t_i])
+        gemm64<NTHR, false, false, true>(N, P, rows, QH, DPO, ECS,
+                                         [&](int n, int pc, float v) { U[n * LD + pc] = v + dA * U[n * LD + pc]; });
         dprod *= dA;
     }
     __syncthreads();
@@ -291,7 +337,7 @@ __device__ __forceinline__ void store_out(void* base, long i, float v) {
 
 // The chunk pass of one segment, chunks from the last down.
 template <bool F32OUT>
-__global__ __launch_bounds__(NTHR, 1) void k_main2(Params2 p) {
+__global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
     extern __shared__ __align__(16) float sm[];
     int seg, bh;
     Params pp = {};
@@ -328,9 +374,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_main2(Params2 p) {
     // dS entering the segment from the right
     {
         const float* E = (seg + 1 < p.nseg) ? p.agg + ((long)bh * p.nsub + seg * p.F) * N * P : nullptr;
-        for (int e = tid; e < N * P; e += NTHR) DS[(e / P) * LD + e % P] = E ? E[e] : 0.f;
+        for (int e = tid; e < N * P; e += NTHR2) DS[(e / P) * LD + e % P] = E ? E[e] : 0.f;
     }
-    float mvacc[2] = {0.f, 0.f};   // DMIMO_V items (r, p) = tid, tid + 256
+    float mvacc = 0.f;   // DMIMO_V item (r, p) = tid (R * P <= 512)
     float ddacc = 0.f;
     const long tokS = (long)bh * p.S;
 
@@ -338,11 +384,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_main2(Params2 p) {
         const int c0 = c * C;
         const int cl = min(C, p.S - c0);
         __syncthreads();
-        load_chunk<true>(p, sm, b, h, g, bh, c, cl);
+        load_chunk<true, NTHR2>(p, sm, b, h, g, bh, c, cl);
         __syncthreads();
 
         // ---- same-token dots dPhiO[t,r] . Psi[t,r2]; DGAMMA; the D-skip sum
-        for (int e = tid; e < cl * RR; e += NTHR) {
+        for (int e = tid; e < cl * RR; e += NTHR2) {
             const int t = e / RR, r = (e % RR) / R, r2 = e % R;
             const float* x = DPO + (r * C + t) * LD;
             const float* y = PS + (r2 * C + t) * LD;
@@ -351,14 +397,14 @@ __global__ __launch_bounds__(NTHR, 1) void k_main2(Params2 p) {
             DQK[e] = s;
         }
         // ---- causal block A = E (Q^ K~^T) and dP = dPhiO Psi^T
-        gemm64(rows, rows, N, QH, LD, 1, KH, 1, LD, nullptr, [&](int i, int j, float v) {
+        gemm64<NTHR2, true, true, false>(rows, rows, N, QH, KH, nullptr, [&](int i, int j, float v) {
             const int ti = i % C, tj = j % C;
             float a = 0.f;
-            if (tj < ti && ti < cl)
-                a = v * FAC[j] * expf(p.segsum[(((long)bh * p.nc + c) * C + ti) * C + tj]);
+            if (tj < ti && ti < cl) a = v * FAC[j] * OUT[ti * LD + tj];
             AM[i * LD + j] = a;
         });
-        gemm64(rows, rows, P, DPO, LD, 1, PS, 1, LD, nullptr, [&](int i, int j, float v) { WM[i * LD + j] = v; });
+        gemm64<NTHR2, true, true, false>(rows, rows, P, DPO, PS, nullptr,
+                                         [&](int i, int j, float v) { WM[i * LD + j] = v; });
         __syncthreads();
         if (tid < cl) {
             const int t = tid;
@@ -368,11 +414,11 @@ __global__ __launch_bounds__(NTHR, 1) void k_main2(Params2 p) {
             for (int r = 0; r < R; ++r) ddacc += DQK[t * RR + r * R + r];
         }
         // ---- DSSDA (per token pair: sum over rank pairs of A * dP), then W = E dP in place
-        for (int e = tid; e < C * C; e += NTHR) {
+        for (int e = tid; e < C * C; e += NTHR2) {
             const int t = e / C, s = e % C;
             float acc = 0.f;
             const bool live = s < t && t < cl;
-            const float ex = live ? expf(p.segsum[(((long)bh * p.nc + c) * C + t) * C + s]) : 0.f;
+            const float ex = OUT[t * LD + s];   // zero unless live
             for (int r = 0; r < R; ++r)
                 for (int r2 = 0; r2 < R; ++r2) {
                     const int i = r * C + t, j = r2 * C + s;
@@ -384,26 +430,24 @@ __global__ __launch_bounds__(NTHR, 1) void k_main2(Params2 p) {
         }
         __syncthreads();
         // same-token factors of the diagonal: gamma_t times the dots
-        for (int e = tid; e < cl * RR; e += NTHR) DQK[e] *= GAM[e / RR];
+        for (int e = tid; e < cl * RR; e += NTHR2) DQK[e] *= GAM[e / RR];
 
         // ---- dQ^ = exp(da_cs) dPhiO S_c^T (then DDA_CS) + W K~
-        gemm64(rows, N, P, DPO, LD, 1, SC, 1, LD, nullptr,
-               [&](int i, int n, float v) { OUT[i * LD + n] = v * ECS[i]; });
+        gemm64<NTHR2, true, true, false>(rows, N, P, DPO, SC, nullptr,
+                                         [&](int i, int n, float v) { OUT[i * LD + n] = v * ECS[i]; });
         __syncthreads();
-        if (tid < cl) {
-            float s = 0.f;
-            for (int r = 0; r < R; ++r)
-                for (int n = 0; n < N; ++n) s = __fmaf_rn(QH[(r * C + tid) * LD + n], OUT[(r * C + tid) * LD + n], s);
-            p.dda_cs[tokS + c0 + tid] = s;
-        }
+        token_sum<NTHR2>(cl, R, C, N, [&](int i, int n) { return QH[i * LD + n] * OUT[i * LD + n]; },
+                         [&](int t, float v) { p.dda_cs[tokS + c0 + t] = v; });
         __syncthreads();
-        gemm64(rows, N, rows, WM, LD, 1, KH, LD, 1, FAC, [&](int i, int n, float v) { OUT[i * LD + n] += v; });
+        // W K~: B(j, n) = k^[j][n] scaled per j by the factor (folded into A)
+        gemm64<NTHR2, true, false, true>(rows, N, rows, WM, KH, FAC,
+                                         [&](int i, int n, float v) { OUT[i * LD + n] += v; });
         __syncthreads();
         // angle gradient, q part: d(a')/dθ = -e', d(e')/dθ = a' for the rotated pair (a', e')
-        float dth[8];
+        float dth[4];   // items (t, n): t < 64, n < 32 (W <= 32)
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            const int e = tid + NTHR * x;
+        for (int x = 0; x < 4; ++x) {
+            const int e = tid + NTHR2 * x;
             const int t = e / 32, n = e % 32;
             float s = 0.f;
             if (t < cl && n < W)
@@ -415,7 +459,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_main2(Params2 p) {
         }
         __syncthreads();
         // same-token part, in the rotated frame: dq^[t,r] += sum_r2 dqk[t][r][r2] k^[t,r2]
-        for (int e = tid; e < rows * N; e += NTHR) {
+        for (int e = tid; e < rows * N; e += NTHR2) {
             const int i = e / N, n = e % N, r = i / C, t = i % C;
             if (t >= cl) continue;
             float s = 0.f;
@@ -424,7 +468,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_main2(Params2 p) {
         }
         __syncthreads();
         // back to the input frame; DQ [B, S*R, H, N]
-        for (int e = tid; e < rows * M; e += NTHR) {
+        for (int e = tid; e < rows * M; e += NTHR2) {
             const int i = e / M, n = e % M, r = i / C, t = i % C;
             if (t >= cl) continue;
             float a = OUT[i * LD + n], ee = OUT[i * LD + M + n];
@@ -442,27 +486,20 @@ __global__ __launch_bounds__(NTHR, 1) void k_main2(Params2 p) {
         __syncthreads();
 
         // ---- dK~ = exp(da_cs_rev) Psi dS^T (then DDA_CS_REV) + W^T Q^
-        gemm64(rows, N, P, PS, LD, 1, DS, 1, LD, nullptr,
-               [&](int j, int n, float v) { OUT[j * LD + n] = v * EREV[j]; });
+        gemm64<NTHR2, true, true, false>(rows, N, P, PS, DS, nullptr,
+                                         [&](int j, int n, float v) { OUT[j * LD + n] = v * EREV[j]; });
         __syncthreads();
-        if (tid < cl) {
-            float s = 0.f;
-            for (int r = 0; r < R; ++r)
-                for (int n = 0; n < N; ++n) s = __fmaf_rn(KH[(r * C + tid) * LD + n], OUT[(r * C + tid) * LD + n], s);
-            p.dda_cs_rev[tokS + c0 + tid] = s * FAC[tid];
-        }
+        token_sum<NTHR2>(cl, R, C, N, [&](int i, int n) { return KH[i * LD + n] * OUT[i * LD + n]; },
+                         [&](int t, float v) { p.dda_cs_rev[tokS + c0 + t] = v * FAC[t]; });
         __syncthreads();
-        gemm64(rows, N, rows, WM, 1, LD, QH, LD, 1, nullptr, [&](int j, int n, float v) { OUT[j * LD + n] += v; });
+        gemm64<NTHR2, false, false, false>(rows, N, rows, WM, QH, nullptr,
+                                           [&](int j, int n, float v) { OUT[j * LD + n] += v; });
         __syncthreads();
-        if (tid < cl) {
-            float s = 0.f;
-            for (int r = 0; r < R; ++r)
-                for (int n = 0; n < N; ++n) s = __fmaf_rn(KH[(r * C + tid) * LD + n], OUT[(r * C + tid) * LD + n], s);
-            p.dfactor[tokS + c0 + tid] = s;
-        }
+        token_sum<NTHR2>(cl, R, C, N, [&](int i, int n) { return KH[i * LD + n] * OUT[i * LD + n]; },
+                         [&](int t, float v) { p.dfactor[tokS + c0 + t] = v; });
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            const int e = tid + NTHR * x;
+        for (int x = 0; x < 4; ++x) {
+            const int e = tid + NTHR2 * x;
             const int t = e / 32, n = e % 32;
             if (t < cl && n < W) {
                 float s = 0.f;
@@ -476,7 +513,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_main2(Params2 p) {
         }
         __syncthreads();
         // dk^ = factor dK~ plus the same-token part sum_r dqk[t][r][r2] q^[t,r]
-        for (int e = tid; e < rows * N; e += NTHR) {
+        for (int e = tid; e < rows * N; e += NTHR2) {
             const int j = e / N, n = e % N, r2 = j / C, t = j % C;
             if (t >= cl) continue;
             float s = OUT[j * LD + n] * FAC[j];
@@ -484,7 +521,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_main2(Params2 p) {
             OUT[j * LD + n] = s;
         }
         __syncthreads();
-        for (int e = tid; e < rows * M; e += NTHR) {
+        for (int e = tid; e < rows * M; e += NTHR2) {
             const int i = e / M, n = e % M, r = i / C, t = i % C;
             if (t >= cl) continue;
             float a = OUT[i * LD + n], ee = OUT[i * LD + M + n];
@@ -502,56 +539,53 @@ __global__ __launch_bounds__(NTHR, 1) void k_main2(Params2 p) {
         __syncthreads();
 
         // ---- dPsi = kappa dS + A^T dPhiO + gamma (qk^T dPhiO)_same-token + d dPhiO
-        gemm64(rows, P, N, KH, LD, 1, DS, LD, 1, nullptr,
-               [&](int j, int pc, float v) { OUT[j * LD + pc] = v * FAC[j] * EREV[j]; });
-        gemm64(rows, P, rows, AM, 1, LD, DPO, LD, 1, nullptr, [&](int j, int pc, float v) { OUT[j * LD + pc] += v; });
+        gemm64<NTHR2, true, false, false>(rows, P, N, KH, DS, nullptr,
+                                          [&](int j, int pc, float v) { OUT[j * LD + pc] = v * FAC[j] * EREV[j]; });
+        gemm64<NTHR2, false, false, false>(rows, P, rows, AM, DPO, nullptr,
+                                           [&](int j, int pc, float v) { OUT[j * LD + pc] += v; });
         __syncthreads();
-        for (int e = tid; e < rows * P; e += NTHR) {
+        for (int e = tid; e < rows * P; e += NTHR2) {
             const int j = e / P, pc = e % P, r2 = j / C, t = j % C;
             if (t >= cl) continue;
             float s = 0.f;
             for (int r = 0; r < R; ++r) s = __fmaf_rn(QKC[t * RR + r * R + r2], DPO[(r * C + t) * LD + pc], s);
             OUT[j * LD + pc] += GAM[j] * s + dval * DPO[j * LD + pc];
         }
+        // v of the chunk into the W tile (free after the dK~ products), for DMIMO_V
+        for (int e = tid; e < cl * P; e += NTHR2) {
+            const int t = e / P, pc = e % P;
+            WM[t * LD + pc] = bf(p.v[((long)(b * p.S + c0 + t) * p.H + h) * P + pc]);
+        }
         __syncthreads();
-        for (int e = tid; e < cl * P; e += NTHR) {
+        for (int e = tid; e < cl * P; e += NTHR2) {
             const int t = e / P, pc = e % P;
             float s = 0.f;
             for (int r = 0; r < R; ++r) s = __fmaf_rn(OUT[(r * C + t) * LD + pc], p.mimo_v[((long)h * R + r) * P + pc], s);
             store_out<F32OUT>(p.dv, ((long)(b * p.S + c0 + t) * p.H + h) * P + pc, s);
         }
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int e = tid + NTHR * x;
-            if (e < R * P) {
-                const int r = e / P, pc = e % P;
-                float s = 0.f;
-                for (int t = 0; t < cl; ++t)
-                    s = __fmaf_rn(OUT[(r * C + t) * LD + pc], bf(p.v[((long)(b * p.S + c0 + t) * p.H + h) * P + pc]), s);
-                mvacc[x] += s;
-            }
+        if (tid < R * P) {
+            const int r = tid / P, pc = tid % P;
+            float s = 0.f;
+            for (int t = 0; t < cl; ++t) s = __fmaf_rn(OUT[(r * C + t) * LD + pc], WM[t * LD + pc], s);
+            mvacc += s;
         }
 
         // ---- DDA: the state decay exp(da_cs[last]) multiplies S_c in S_{c+1}
         const float dA = expf(p.da_cs[tokS + c0 + cl - 1]);
         float part = 0.f;
-        for (int e = tid; e < N * P; e += NTHR) part = __fmaf_rn(DS[(e / P) * LD + e % P], SC[(e / P) * LD + e % P], part);
-        const float tot = block_sum(part, RED);
+        for (int e = tid; e < N * P; e += NTHR2) part = __fmaf_rn(DS[(e / P) * LD + e % P], SC[(e / P) * LD + e % P], part);
+        const float tot = block_sum<NTHR2>(part, RED);
         if (tid < cl) p.dda[tokS + c0 + tid] = (tid == cl - 1) ? dA * tot : 0.f;
 
         // ---- dS_c = Q^^T (exp(da_cs) dPhiO) + exp(da_cs[last]) dS_{c+1}
-        gemm64(N, P, rows, QH, 1, LD, DPO, LD, 1, ECS,
-               [&](int n, int pc, float v) { DS[n * LD + pc] = v + dA * DS[n * LD + pc]; });
+        gemm64<NTHR2, false, false, true>(N, P, rows, QH, DPO, ECS,
+                                          [&](int n, int pc, float v) { DS[n * LD + pc] = v + dA * DS[n * LD + pc]; });
     }
 
     // ---- per-segment partial sums of DMIMO_V and DD
     __syncthreads();
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        const int e = tid + NTHR * x;
-        if (e < R * P) p.part_mv[((long)bh * p.nseg + seg) * R * P + e] = mvacc[x];
-    }
-    const float dd = block_sum(ddacc, RED);
+    if (tid < R * P) p.part_mv[((long)bh * p.nseg + seg) * R * P + tid] = mvacc;
+    const float dd = block_sum<NTHR2>(ddacc, RED);
     if (tid == 0) p.part_d[(long)bh * p.nseg + seg] = dd;
 }
 

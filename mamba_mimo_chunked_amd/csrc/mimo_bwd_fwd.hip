@@ -556,8 +556,9 @@ mimo_status make_plan_b2(const mimo_bwd_bwd_args* a, PlanB2* pl) {
     if (H % G) return fail(MIMO_ERR_VALUE, "H must be divisible by G");
     if (rd != 2 && rd != 4) return fail(MIMO_ERR_VALUE, "rotary_dim_divisor must be 2 or 4");
     if (N % 2 || N % rd) return fail(MIMO_ERR_VALUE, "N must be even and divisible by rotary_dim_divisor");
-    if (C * R > 64 || N > 64 || P > 64 || R > 8)
-        return fail(MIMO_ERR_UNSUPPORTED, "the stage-2 backward supports R * chunk_size, N and P up to 64 and R up to 8");
+    if (C * R > 64 || N > 64 || P > 64 || R > 8 || P % 8)
+        return fail(MIMO_ERR_UNSUPPORTED,
+                    "the stage-2 backward supports R * chunk_size, N and P up to 64, R up to 8 and P a multiple of 8");
     if (S > (int64_t)1 << 30 || B * H * ((S + C - 1) / C + 8) > (int64_t)1 << 31)
         return fail(MIMO_ERR_UNSUPPORTED, "problem too large");
     pl->W = (int)(N / rd);
@@ -628,9 +629,9 @@ mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events
             return fail(MIMO_ERR_HIP, "hipEventRecord failed");
         return MIMO_OK;
     };
-    auto launch2 = [&](const void* f, dim3 grid, int lds) -> mimo_status {
+    auto launch2 = [&](const void* f, dim3 grid, int lds, int threads = b2::NTHR) -> mimo_status {
         void* args[] = {&p};
-        const hipError_t e = hipLaunchKernel(f, grid, dim3(b2::NTHR), args, (size_t)lds, st);
+        const hipError_t e = hipLaunchKernel(f, grid, dim3(threads), args, (size_t)lds, st);
         if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
         return MIMO_OK;
     };
@@ -660,7 +661,7 @@ mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events
         return s;
     }
     if ((s = mark(2)) != MIMO_OK) return s;
-    if ((s = launch2(kmain, dim3(grid_blocks(pp, pl.nseg)), lds_main)) != MIMO_OK) return s;
+    if ((s = launch2(kmain, dim3(grid_blocks(pp, pl.nseg)), lds_main, b2::NTHR2)) != MIMO_OK) return s;
     if ((s = mark(3)) != MIMO_OK) return s;
     const long tot = (long)p.B * p.H * p.R * p.P;
     if ((s = launch2(reinterpret_cast<const void*>(&b2::k_finish2), dim3((unsigned)((tot + 255) / 256)), 0)) != MIMO_OK)
