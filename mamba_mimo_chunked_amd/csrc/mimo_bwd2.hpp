@@ -14,8 +14,7 @@
 //               the rotated frame (the rotation is the same for q and k of a token)
 // and the per-token partials DDA_CS, DDA_CS_REV, DFACTOR, DGAMMA, DDA, DSSDA and
 // DANGLES from the same products. Everything is fp32 on small LDS-resident
-// tiles (R*C, N, P <= 64): every contraction is a register-blocked product in
-// which a thread owns a 4 x 4 block of the output.
+// tiles (R*C, N, P <= 64); every contraction runs on fp32 MFMA.
 //
 // Work split: k_agg2 forms each sub-segment's dS increment from a zero start,
 // k_scan_rev chains them from the end of the sequence, k_main2 walks each
@@ -30,7 +29,7 @@ namespace b2 {
 
 constexpr int NTHR = 256;      // the aggregate (two workgroups per CU)
 constexpr int NTHR2 = 512;     // the chunk pass (one workgroup per CU: eight waves hide more latency)
-constexpr int LD = 65;              // row pitch (floats) of every tile
+constexpr int LD = 68;              // row pitch (floats) of every tile (16-byte rows, 4 mod 64)
 constexpr int TILE = 64 * LD;       // floats per tile
 
 struct Params2 {
@@ -48,48 +47,75 @@ struct Params2 {
 __device__ __forceinline__ float bf(unsigned short x) { return __uint_as_float(static_cast<unsigned>(x) << 16); }
 __device__ __forceinline__ unsigned short to_bf(float x) { return static_cast<unsigned short>(pk2(0.f, x) >> 16); }
 
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // C(i, j) = sum_k A(i, k) B(k, j) (* sk[k]) for i < Mi, j < Nj, k < K (all <= 64) on
-// [64][LD] LDS tiles. AK1: A(i, k) = A[i*LD + k], else A[k*LD + i]; BK1: B(k, j) =
-// B[j*LD + k], else B[k*LD + j]. Of NT threads, thread (ti, tj) = (tid / 16, tid % 16)
-// owns rows ti + (NT/16) x and columns tj + 16 y and hands each result to
-// epi(i, j, value). Rows and columns past Mi / Nj are computed too (their reads stay
-// inside the tiles) and dropped, so the inner loop has no bounds tests; with the
-// layouts known at compile time every operand read is one base address plus a
-// constant offset.
+// [64][LD] LDS tiles, on fp32 MFMA (16 x 16 x 4). AK1: A(i, k) = A[i*LD + k], else
+// A[k*LD + i]; BK1: B(k, j) = B[j*LD + k], else B[k*LD + j]. The output is 4 x 4
+// blocks of 16 x 16: of the NT/64 waves, wave w owns row block w / (4/CW) and the CW =
+// 16 / (NT/64) column blocks from CW * (w % (4/CW)), and hands each result to epi(i,
+// j, value). The contraction index is split k = 16 kt + 4 q + v (q = lane / 16, v the
+// accumulation step), so a lane reads four consecutive floats of a
+// contraction-contiguous row in one 16-byte load, or one float of each of four rows;
+// with LD = 4 (mod 64) neither pattern has bank conflicts. Values past K are zeroed
+// (the tiles hold stale data there); rows and columns past Mi / Nj are dropped.
 template <int NT, bool AK1, bool BK1, bool SK, typename F>
 __device__ __forceinline__ void gemm64(int Mi, int Nj, int K, const float* A, const float* B, const float* sk,
                                        F&& epi) {
-    constexpr int RX = 64 * 16 / NT, RS = NT / 16;   // rows per thread, row stride
-    constexpr int AX = AK1 ? RS * LD : RS, AKS = AK1 ? 1 : LD;
-    constexpr int BY = BK1 ? 16 * LD : 16, BKS = BK1 ? 1 : LD;
-    const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
-    const float* pa = A + (AK1 ? ti * LD : ti);
-    const float* pb = B + (BK1 ? tj * LD : tj);
-    float acc[RX][4];
+    constexpr int NW = NT / 64, CW = 16 / NW, WR = 4 / CW;   // waves, column blocks a wave, waves a row block
+    const int w = threadIdx.x >> 6, x = threadIdx.x & 15, q = (threadIdx.x >> 4) & 3;
+    const int i0 = 16 * (w / WR), j0 = 16 * CW * (w % WR);
+    if (i0 >= Mi) return;   // wave-uniform
+    f32x4 acc[CW];
 #pragma unroll
-    for (int x = 0; x < RX; ++x)
+    for (int cb = 0; cb < CW; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nk = (K + 15) >> 4;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int kb = 16 * kt + 4 * q;
+        float a[4];
+        if constexpr (AK1) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(A + (i0 + x) * LD + kb);
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
-#pragma unroll 4
-    for (int kk = 0; kk < K; ++kk) {
-        float a[RX], bv[4];
-        const float s = SK ? sk[kk] : 1.f;
+            for (int v = 0; v < 4; ++v) a[v] = t[v];
+        } else {
 #pragma unroll
-        for (int x = 0; x < RX; ++x) a[x] = SK ? pa[x * AX + kk * AKS] * s : pa[x * AX + kk * AKS];
+            for (int v = 0; v < 4; ++v) a[v] = A[(kb + v) * LD + i0 + x];
+        }
+        if constexpr (SK) {
+            const f32x4 s = *reinterpret_cast<const f32x4*>(sk + kb);
 #pragma unroll
-        for (int y = 0; y < 4; ++y) bv[y] = pb[y * BY + kk * BKS];
+            for (int v = 0; v < 4; ++v) a[v] *= s[v];
+        }
 #pragma unroll
-        for (int x = 0; x < RX; ++x)
+        for (int v = 0; v < 4; ++v) a[v] = kb + v < K ? a[v] : 0.f;
 #pragma unroll
-            for (int y = 0; y < 4; ++y) acc[x][y] = __fmaf_rn(a[x], bv[y], acc[x][y]);
+        for (int cb = 0; cb < CW; ++cb) {
+            const int jb = j0 + 16 * cb;
+            if (jb >= Nj) break;   // wave-uniform
+            float bv[4];
+            if constexpr (BK1) {
+                const f32x4 t = *reinterpret_cast<const f32x4*>(B + (jb + x) * LD + kb);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) bv[v] = t[v];
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) bv[v] = B[(kb + v) * LD + jb + x];
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[cb] = mfma_f32(a[v], kb + v < K ? bv[v] : 0.f, acc[cb]);
+        }
     }
 #pragma unroll
-    for (int x = 0; x < RX; ++x)
+    for (int cb = 0; cb < CW; ++cb) {
+        const int j = j0 + 16 * cb + x;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const int i = ti + RS * x, j = tj + 16 * y;
-            if (i < Mi && j < Nj) epi(i, j, acc[x][y]);
+        for (int v = 0; v < 4; ++v) {
+            const int i = i0 + 4 * q + v;
+            if (i < Mi && j < Nj) epi(i, j, acc[cb][v]);
         }
+    }
 }
 
 // Block-wide sum over NT threads (every thread passes its value; the result is
