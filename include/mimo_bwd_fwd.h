@@ -242,8 +242,9 @@ mimo_status mimo_siso_fwd_timed(const mimo_siso_fwd_args *args, void *stream, vo
  * dq, dk, dv are bf16, or fp32 when out_f32 != 0; the others fp32.
  * Inputs as for mimo_bwd_fwd (dout reduced or not, bf16 q/k/v/dout/trap) plus
  * states [B,H,nc,N,P] and qk_dot [B,H,S,R,R] (bf16). Limits: R * chunk_size,
- * N and P at most 64, R at most 8, P a multiple of 8 (MIMO_ERR_UNSUPPORTED
- * otherwise). Ownership, asynchrony
+ * N and P at most 64, R at most 8, N and P multiples of 8 (MIMO_ERR_UNSUPPORTED
+ * otherwise). dout, q, k, v, states, q_bias, k_bias, mimo_v, mimo_o, dq and dk
+ * must be 16-byte aligned (MIMO_ERR_VALUE otherwise). Ownership, asynchrony
  * and errors as for mimo_bwd_fwd.
  */
 typedef struct mimo_bwd_bwd_args {

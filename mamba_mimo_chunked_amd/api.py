@@ -426,6 +426,12 @@ _BWD2_OUT_FIELDS = {"DQ": "dq", "DK": "dk", "DV": "dv", "DMIMO_V": "dmimo_v", "D
                     "DDA_CS_REV": "dda_cs_rev", "DDA_CS": "dda_cs", "DD": "dd"}
 
 
+def _aligned(x: Tensor) -> Tensor:
+    """Contiguous and 16-byte aligned (a copy when a view starts inside a row)."""
+    x = x.contiguous()
+    return x if x.data_ptr() % 16 == 0 else x.clone()
+
+
 def _make_bwd2_args(dims, C, rd, out_f32, t: dict, outs: dict, workspace=None, ws_bytes=0):
     B, S, H, G, R, N, P = dims
     a = _lib.MimoBwdBwdArgs()
@@ -467,7 +473,7 @@ def mamba3_mimo_bwd_bwd(dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, d
     L = _lib.lib()
     vals = (dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, da_cs, da_cs_rev, dt, trap, segsum, angles,
             mimo_o, d)
-    t = {n: (None if x is None else x.contiguous()) for n, x in zip(_BWD2_INPUTS, vals)}
+    t = {n: (None if x is None else _aligned(x)) for n, x in zip(_BWD2_INPUTS, vals)}
     f32 = torch.float32
     W = N // rotary_dim_divisor
     outs = {

@@ -47,6 +47,15 @@ struct Params2 {
 __device__ __forceinline__ float bf(unsigned short x) { return __uint_as_float(static_cast<unsigned>(x) << 16); }
 __device__ __forceinline__ unsigned short to_bf(float x) { return static_cast<unsigned short>(pk2(0.f, x) >> 16); }
 
+// The thread index as a value the compiler cannot move out of a loop: index and
+// address arithmetic is then redone per chunk instead of being held in registers
+// across the whole chunk loop (which spills). No instruction is emitted.
+__device__ __forceinline__ int tid_x() {
+    int x = threadIdx.x;
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -65,7 +74,7 @@ template <int NT, bool AK1, bool BK1, bool SK, typename F>
 __device__ __forceinline__ void gemm64(int Mi, int Nj, int K, const float* A, const float* B, const float* sk,
                                        F&& epi) {
     constexpr int NW = NT / 64, CW = 16 / NW, WR = 4 / CW;   // waves, column blocks a wave, waves a row block
-    const int w = threadIdx.x >> 6, x = threadIdx.x & 15, q = (threadIdx.x >> 4) & 3;
+    const int tid = tid_x(), w = tid >> 6, x = tid & 15, q = (tid >> 4) & 3;
     const int i0 = 16 * (w / WR), j0 = 16 * CW * (w % WR);
     if (i0 >= Mi) return;   // wave-uniform
     f32x4 acc[CW];
@@ -138,7 +147,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // a butterfly over the group); out(t, value) is called by the group's first lane.
 template <int NT, typename F, typename O>
 __device__ __forceinline__ void token_sum(int cl, int R, int C, int N, F&& f, O&& out) {
-    const int grp = threadIdx.x >> 4, l = threadIdx.x & 15;
+    const int tid = tid_x(), grp = tid >> 4, l = tid & 15;
     for (int t0 = 0; t0 < cl; t0 += NT / 16) {
         const int t = t0 + grp;
         float s = 0.f;
@@ -165,113 +174,236 @@ struct L2 {
                          AGG_TOTAL = 4 * TILE + 64;
 };
 
-// Load chunk c's rotated q^ (and k^, Psi, the cached state and qk_dot, and the
-// per-row scalars when MAIN), dPhiO and exp(da_cs) into LDS. Rows past the chunk
-// (t >= cl) are zero.
+// e / d and e % d for 0 <= e < 16384 and 1 <= d <= 64 from d's reciprocal: the exact
+// quotient of e + 1/2 is at least 1/(2d) >= 1/128 away from an integer and the
+// rounded product is off by less than 0.002.
+struct DivS {
+    int d;
+    float rd;
+    __device__ explicit DivS(int d_) : d(d_), rd(1.0f / static_cast<float>(d_)) {}
+    __device__ int q(int e) const { return static_cast<int>((static_cast<float>(e) + 0.5f) * rd); }
+    __device__ int r(int e) const { return e - q(e) * d; }
+};
+
+// Items of the chunk load, a thread's items being e = tid + NT x for x < IX (every
+// kind has at most 64 * 64 / 8 = 512 of them):
+//   rotation items (i, n4): four columns n4.. of each half (n4 < N/2) of row i of q^
+//     (and k^); the thread keeps cos and sin of its columns (1 and 0 where the
+//     column is past the rotated width or the row past the chunk) for the output pass;
+//   value items (i, p8): eight columns of dPhiO (and Psi) of row i; the thread keeps
+//     its raw v (the rank-0 items' v is the chunk's v);
+//   state items: eight consecutive values of the cached state.
+template <int NT>
+struct Items {
+    static constexpr int IX = 512 / NT;
+};
+template <int NT>
+struct Keep {
+    float cs[Items<NT>::IX][4], sn[Items<NT>::IX][4];
+    u32x4 v[Items<NT>::IX];
+};
+
+// Load chunk c's rotated q^ (and k^, Psi, the cached state, qk_dot, exp(segsum) and
+// the per-row scalars when MAIN), dPhiO and exp(da_cs) into LDS. Every global load
+// of a thread is issued before any of them is used. Rows past the chunk (t >= cl)
+// are zero.
 template <bool MAIN, int NT>
-__device__ __forceinline__ void load_chunk(const Params2& p, float* sm, int b, int h, int g, int bh, int c, int cl) {
+__device__ __forceinline__ void load_chunk(const Params2& p, float* sm, int b, int h, int g, int bh, int c, int cl,
+                                           const DivS& dC, const DivS& dM4, const DivS& dP8, Keep<NT>& keep) {
+    constexpr int IX = Items<NT>::IX;
+    constexpr int SX = 64 * 64 / NT;   // segsum values a thread (C * C <= 4096)
     const int R = p.R, N = p.N, P = p.P, C = p.C, W = p.W, M = N / 2;
-    const int tid = threadIdx.x;
+    const int tid = tid_x();
     const int c0 = c * C;
-    const int rows = R * C;
+    const int rows = R * C, RR = R * R;
+    const int nrot = rows * (M / 4), nval = rows * (P / 8), nst = N * (P / 8);
+    const long tok0 = (long)b * p.S + c0;   // (b, c0) as a token index
+    const long tb0 = (long)bh * p.S + c0;   // (b, h, c0) for the per-token arrays
     float* QH = sm + (MAIN ? L2::QH : L2::A_QH);
     float* KH = sm + L2::KH;
     float* PS = sm + L2::PS;
     float* DPO = sm + (MAIN ? L2::DPO : L2::A_DPO);
     float* ECS = sm + (MAIN ? L2::ECS : L2::A_ECS);
-    for (int e = tid; e < rows * M; e += NT) {
-        const int i = e / M, n = e % M;
-        const int r = i / C, t = i % C;
-        float qa = 0.f, qe = 0.f, ka = 0.f, ke = 0.f;
-        if (t < cl) {
-            const long src = (((long)(b * p.S + c0 + t) * R + r) * p.G + g) * N;
-            const float* qb = p.q_bias + ((long)h * R + r) * N;
-            qa = bf(p.q[src + n]) + qb[n];
-            qe = bf(p.q[src + M + n]) + qb[M + n];
-            if (MAIN) {
-                const float* kb = p.k_bias + ((long)h * R + r) * N;
-                ka = bf(p.k[src + n]) + kb[n];
-                ke = bf(p.k[src + M + n]) + kb[M + n];
-            }
-            if (n < W) {
-                float sn, cs;
-                sin_cos(p.angles[((long)(b * p.S + c0 + t) * p.H + h) * W + n], sn, cs);
-                const float qa2 = cs * qa - sn * qe, qe2 = sn * qa + cs * qe;
-                qa = qa2;
-                qe = qe2;
-                if (MAIN) {
-                    const float ka2 = cs * ka - sn * ke, ke2 = sn * ka + cs * ke;
-                    ka = ka2;
-                    ke = ke2;
-                }
-            }
-        }
-        QH[i * LD + n] = qa;
-        QH[i * LD + M + n] = qe;
-        if (MAIN) {
-            KH[i * LD + n] = ka;
-            KH[i * LD + M + n] = ke;
-        }
-    }
-    for (int e = tid; e < rows * P; e += NT) {
-        const int i = e / P, pc = e % P;
-        const int r = i / C, t = i % C;
-        float dpo = 0.f, psi = 0.f;
-        if (t < cl) {
-            const long tk = (long)(b * p.S + c0 + t);
-            if (p.reduce_o)
-                dpo = bf(p.dout[(tk * p.H + h) * P + pc]) * p.mimo_o[((long)h * R + r) * P + pc];
-            else
-                dpo = bf(p.dout[((tk * R + r) * p.H + h) * P + pc]);
-            if (MAIN) psi = bf(p.v[(tk * p.H + h) * P + pc]) * p.mimo_v[((long)h * R + r) * P + pc];
-        }
-        DPO[i * LD + pc] = dpo;
-        if (MAIN) PS[i * LD + pc] = psi;
-    }
-    if (tid < rows) {
-        const int t = tid % C;
-        const long tb = (long)bh * p.S + c0 + t;
-        ECS[tid] = t < cl ? expf(p.da_cs[tb]) : 0.f;
-        if (MAIN) {
-            float gam = 0.f, fac = 0.f, er = 0.f;
+
+    // ---- issue the loads
+    u32x2 qw[IX][2], kw[IX][2];
+    f32x4 qb[IX][2], kb[IX][2];
+    float ang[IX][4];
+    u32x4 dw[IX], vw[IX], sw[IX];
+    f32x4 mo[IX][2], mv[IX][2];
+#pragma unroll
+    for (int x = 0; x < IX; ++x) {
+        const int e = tid + NT * x;
+        if (e < nrot) {
+            const int i = dM4.q(e), n4 = 4 * (e - i * (M / 4));
+            const int r = dC.q(i), t = i - r * C;
             if (t < cl) {
-                const float sg = 1.0f / (1.0f + expf(-bf(p.trap[tb])));
-                gam = p.dt[tb] * sg;
-                float beta = 0.f;
-                if (c0 + t + 1 < p.S) {
-                    const float sg1 = 1.0f / (1.0f + expf(-bf(p.trap[tb + 1])));
-                    beta = p.dt[tb + 1] * (1.0f - sg1);
+                const long src = (((tok0 + t) * R + r) * p.G + g) * N + n4;
+                const float* qbp = p.q_bias + ((long)h * R + r) * N + n4;
+                qw[x][0] = *reinterpret_cast<const u32x2*>(p.q + src);
+                qw[x][1] = *reinterpret_cast<const u32x2*>(p.q + src + M);
+                qb[x][0] = *reinterpret_cast<const f32x4*>(qbp);
+                qb[x][1] = *reinterpret_cast<const f32x4*>(qbp + M);
+                if (MAIN) {
+                    const float* kbp = p.k_bias + ((long)h * R + r) * N + n4;
+                    kw[x][0] = *reinterpret_cast<const u32x2*>(p.k + src);
+                    kw[x][1] = *reinterpret_cast<const u32x2*>(p.k + src + M);
+                    kb[x][0] = *reinterpret_cast<const f32x4*>(kbp);
+                    kb[x][1] = *reinterpret_cast<const f32x4*>(kbp + M);
                 }
-                fac = gam + beta;
-                er = expf(p.da_cs_rev[tb]);
+                const float* ap = p.angles + ((tok0 + t) * p.H + h) * W;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) ang[x][v] = n4 + v < W ? ap[n4 + v] : 0.f;
             }
-            sm[L2::GAM + tid] = gam;
-            sm[L2::FAC + tid] = fac;
-            sm[L2::EREV + tid] = er;
+        }
+        if (e < nval) {
+            const int i = dP8.q(e), p8 = 8 * (e - i * (P / 8));
+            const int r = dC.q(i), t = i - r * C;
+            if (t < cl) {
+                const long tk = tok0 + t;
+                if (p.reduce_o) {
+                    dw[x] = *reinterpret_cast<const u32x4*>(p.dout + (tk * p.H + h) * P + p8);
+                    const float* m = p.mimo_o + ((long)h * R + r) * P + p8;
+                    mo[x][0] = *reinterpret_cast<const f32x4*>(m);
+                    mo[x][1] = *reinterpret_cast<const f32x4*>(m + 4);
+                } else {
+                    dw[x] = *reinterpret_cast<const u32x4*>(p.dout + ((tk * R + r) * p.H + h) * P + p8);
+                }
+                if (MAIN) {
+                    vw[x] = *reinterpret_cast<const u32x4*>(p.v + (tk * p.H + h) * P + p8);
+                    const float* m = p.mimo_v + ((long)h * R + r) * P + p8;
+                    mv[x][0] = *reinterpret_cast<const f32x4*>(m);
+                    mv[x][1] = *reinterpret_cast<const f32x4*>(m + 4);
+                }
+            }
+        }
+        if (MAIN && e < nst) sw[x] = *reinterpret_cast<const u32x4*>(p.states + ((long)bh * p.nc + c) * N * P + 8 * e);
+    }
+    // per-token scalars (one thread a token) and the same-token and segsum tables
+    float s_cs = 0.f, s_rev = 0.f, s_dt = 0.f, s_tr = 0.f, s_dt1 = 0.f, s_tr1 = 0.f;
+    const bool tok_live = tid < cl;
+    if (tok_live) {
+        s_cs = p.da_cs[tb0 + tid];
+        if (MAIN) {
+            s_rev = p.da_cs_rev[tb0 + tid];
+            s_dt = p.dt[tb0 + tid];
+            s_tr = bf(p.trap[tb0 + tid]);
+            if (c0 + tid + 1 < p.S) {
+                s_dt1 = p.dt[tb0 + tid + 1];
+                s_tr1 = bf(p.trap[tb0 + tid + 1]);
+            }
+        }
+    }
+    float qk = 0.f, seg[SX];
+    if (MAIN) {
+        if (tid < cl * RR) qk = bf(p.qk_dot[tb0 * RR + tid]);
+#pragma unroll
+        for (int x = 0; x < SX; ++x) {
+            const int e = tid + NT * x;
+            const int t = dC.q(e), s2 = e - t * C;
+            seg[x] = (e < C * C && s2 < t && t < cl) ? p.segsum[((long)bh * p.nc + c) * C * C + e] : 0.f;
+        }
+    }
+
+    // ---- rotate and store
+#pragma unroll
+    for (int x = 0; x < IX; ++x) {
+        const int e = tid + NT * x;
+        if (e < nrot) {
+            const int i = dM4.q(e), n4 = 4 * (e - i * (M / 4));
+            const int t = dC.r(i);
+            float qa[4], qe[4], ka[4], ke[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float sn = 0.f, cs = 1.f;
+                qa[v] = qe[v] = ka[v] = ke[v] = 0.f;
+                if (t < cl) {
+                    const unsigned wa = qw[x][0][v >> 1], we = qw[x][1][v >> 1];
+                    qa[v] = ((v & 1) ? hi16(wa) : lo16(wa)) + qb[x][0][v];
+                    qe[v] = ((v & 1) ? hi16(we) : lo16(we)) + qb[x][1][v];
+                    if (MAIN) {
+                        const unsigned ua = kw[x][0][v >> 1], ue = kw[x][1][v >> 1];
+                        ka[v] = ((v & 1) ? hi16(ua) : lo16(ua)) + kb[x][0][v];
+                        ke[v] = ((v & 1) ? hi16(ue) : lo16(ue)) + kb[x][1][v];
+                    }
+                    if (n4 + v < W) sin_cos(ang[x][v], sn, cs);
+                }
+                keep.cs[x][v] = cs;
+                keep.sn[x][v] = sn;
+                const float qa2 = cs * qa[v] - sn * qe[v], qe2 = sn * qa[v] + cs * qe[v];
+                qa[v] = qa2;
+                qe[v] = qe2;
+                if (MAIN) {
+                    const float ka2 = cs * ka[v] - sn * ke[v], ke2 = sn * ka[v] + cs * ke[v];
+                    ka[v] = ka2;
+                    ke[v] = ke2;
+                }
+            }
+            *reinterpret_cast<f32x4*>(QH + i * LD + n4) = f32x4{qa[0], qa[1], qa[2], qa[3]};
+            *reinterpret_cast<f32x4*>(QH + i * LD + M + n4) = f32x4{qe[0], qe[1], qe[2], qe[3]};
+            if (MAIN) {
+                *reinterpret_cast<f32x4*>(KH + i * LD + n4) = f32x4{ka[0], ka[1], ka[2], ka[3]};
+                *reinterpret_cast<f32x4*>(KH + i * LD + M + n4) = f32x4{ke[0], ke[1], ke[2], ke[3]};
+            }
+        }
+        if (e < nval) {
+            const int i = dP8.q(e), p8 = 8 * (e - i * (P / 8));
+            const bool live = dC.r(i) < cl;
+            float d8[8], s8[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const unsigned wd = dw[x][v >> 1];
+                const float dv = (v & 1) ? hi16(wd) : lo16(wd);
+                d8[v] = live ? (p.reduce_o ? dv * mo[x][v >> 2][v & 3] : dv) : 0.f;
+                if (MAIN) {
+                    const unsigned wv = vw[x][v >> 1];
+                    s8[v] = live ? ((v & 1) ? hi16(wv) : lo16(wv)) * mv[x][v >> 2][v & 3] : 0.f;
+                }
+            }
+            *reinterpret_cast<f32x4*>(DPO + i * LD + p8) = f32x4{d8[0], d8[1], d8[2], d8[3]};
+            *reinterpret_cast<f32x4*>(DPO + i * LD + p8 + 4) = f32x4{d8[4], d8[5], d8[6], d8[7]};
+            if (MAIN) {
+                *reinterpret_cast<f32x4*>(PS + i * LD + p8) = f32x4{s8[0], s8[1], s8[2], s8[3]};
+                *reinterpret_cast<f32x4*>(PS + i * LD + p8 + 4) = f32x4{s8[4], s8[5], s8[6], s8[7]};
+                keep.v[x] = live ? vw[x] : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        if (MAIN && e < nst) {
+            const int n = dP8.q(e), pc = 8 * (e - n * (P / 8));
+            float* dst = sm + L2::SC + n * LD + pc;
+            *reinterpret_cast<f32x4*>(dst) = f32x4{lo16(sw[x][0]), hi16(sw[x][0]), lo16(sw[x][1]), hi16(sw[x][1])};
+            *reinterpret_cast<f32x4*>(dst + 4) =
+                f32x4{lo16(sw[x][2]), hi16(sw[x][2]), lo16(sw[x][3]), hi16(sw[x][3])};
+        }
+    }
+    if (tid < C) {
+        const float ecs = tok_live ? expf(s_cs) : 0.f;
+        float gam = 0.f, fac = 0.f, er = 0.f;
+        if (MAIN && tok_live) {
+            gam = s_dt * (1.0f / (1.0f + expf(-s_tr)));
+            const float beta = c0 + tid + 1 < p.S ? s_dt1 * (1.0f - 1.0f / (1.0f + expf(-s_tr1))) : 0.f;
+            fac = gam + beta;
+            er = expf(s_rev);
+        }
+        for (int r = 0; r < R; ++r) {
+            const int i = r * C + tid;
+            ECS[i] = ecs;
+            if (MAIN) {
+                sm[L2::GAM + i] = gam;
+                sm[L2::FAC + i] = fac;
+                sm[L2::EREV + i] = er;
+            }
         }
     }
     if (MAIN) {
-        const unsigned short* st = p.states + ((long)bh * p.nc + c) * N * P;
-        // 8 consecutive bf16 a thread (N * P is a multiple of 8: P is a multiple of 8)
-        for (int e8 = tid; e8 < N * P / 8; e8 += NT) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(st + 8 * e8);
-            const int n = (8 * e8) / P, pc = (8 * e8) % P;
-            float* dst = sm + L2::SC + n * LD + pc;
-#pragma unroll
-            for (int d2 = 0; d2 < 4; ++d2) {
-                dst[2 * d2] = __uint_as_float(w[d2] << 16);
-                dst[2 * d2 + 1] = __uint_as_float(w[d2] & 0xffff0000u);
-            }
-        }
-        const int RR = R * R;
-        for (int e = tid; e < cl * RR; e += NT)
-            sm[L2::QKC + e] = bf(p.qk_dot[((long)bh * p.S + c0) * RR + e]);
+        if (tid < cl * RR) sm[L2::QKC + tid] = qk;
         // exp(segsum) of the chunk's strictly causal token pairs, in the output tile
         // (free until the dQ^ products)
-        for (int e = tid; e < C * C; e += NT) {
-            const int t = e / C, s2 = e % C;
-            sm[L2::OUT + t * LD + s2] =
-                (s2 < t && t < cl) ? expf(p.segsum[(((long)bh * p.nc + c) * C + t) * C + s2]) : 0.f;
+#pragma unroll
+        for (int x = 0; x < SX; ++x) {
+            const int e = tid + NT * x;
+            const int t = dC.q(e), s2 = e - t * C;
+            if (e < C * C) sm[L2::OUT + t * LD + s2] = (s2 < t && t < cl) ? expf(seg[x]) : 0.f;
         }
     }
 }
@@ -301,10 +433,12 @@ __global__ __launch_bounds__(NTHR, 2) void k_agg2(Params2 p) {
     float* ECS = sm + L2::A_ECS;
     for (int e = threadIdx.x; e < N * P; e += NTHR) U[(e / P) * LD + e % P] = 0.f;
     float dprod = 1.f;
+    const DivS dC(C), dM4(N / 8), dP8(P / 8);
+    Keep<NTHR> keep;
     for (int c = c_end - 1; c >= c_begin; --c) {
         const int cl = min(C, p.S - c * C);
         __syncthreads();
-        load_chunk<false, NTHR>(p, sm, b, h, g, bh, c, cl);
+        load_chunk<false, NTHR>(p, sm, b, h, g, bh, c, cl, dC, dM4, dP8, keep);
         __syncthreads();
         const float dA = expf(p.da_cs[(long)bh * p.S + c * C + cl - 1]);
         // U[n][p] = sum_i Q^[i][n] exp(da_cs[t_i]) dPhiO[i][p] + dA U[n][p]; the thread that
@@ -361,6 +495,41 @@ __device__ __forceinline__ void store_out(void* base, long i, float v) {
         static_cast<unsigned short*>(base)[i] = to_bf(v);
 }
 
+// A [rows][N] gradient tile of the rotated frame back to the input frame (the
+// inverse rotation of the thread's rotation items, whose cos and sin it kept from
+// the load) and out to DQ or DK [B, S*R, H, N], four columns of each half a store.
+template <bool F32OUT, int NT>
+__device__ __forceinline__ void store_rot(const Params2& p, void* dst, const float* OUT, const Keep<NT>& keep, int b,
+                                          int h, int c0, int cl, const DivS& dC, const DivS& dM4) {
+    const int R = p.R, N = p.N, C = p.C, M = N / 2;
+#pragma unroll
+    for (int x = 0; x < Items<NT>::IX; ++x) {
+        const int e = tid_x() + NT * x;
+        if (e >= R * C * (M / 4)) continue;
+        const int i = dM4.q(e), n4 = 4 * (e - i * (M / 4));
+        const int r = dC.q(i), t = i - r * C;
+        if (t >= cl) continue;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(OUT + i * LD + n4);
+        const f32x4 ee = *reinterpret_cast<const f32x4*>(OUT + i * LD + M + n4);
+        float a2[4], e2[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float cs = keep.cs[x][v], sn = keep.sn[x][v];
+            a2[v] = cs * a[v] + sn * ee[v];
+            e2[v] = -sn * a[v] + cs * ee[v];
+        }
+        const long o = (((long)b * p.S * R + (long)(c0 + t) * R + r) * p.H + h) * N + n4;
+        if constexpr (F32OUT) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + o) = f32x4{a2[0], a2[1], a2[2], a2[3]};
+            *reinterpret_cast<f32x4*>(static_cast<float*>(dst) + o + M) = f32x4{e2[0], e2[1], e2[2], e2[3]};
+        } else {
+            *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(dst) + o) = u32x2{pk2(a2[0], a2[1]), pk2(a2[2], a2[3])};
+            *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(dst) + o + M) =
+                u32x2{pk2(e2[0], e2[1]), pk2(e2[2], e2[3])};
+        }
+    }
+}
+
 // The chunk pass of one segment, chunks from the last down.
 template <bool F32OUT>
 __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
@@ -402,6 +571,8 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         const float* E = (seg + 1 < p.nseg) ? p.agg + ((long)bh * p.nsub + seg * p.F) * N * P : nullptr;
         for (int e = tid; e < N * P; e += NTHR2) DS[(e / P) * LD + e % P] = E ? E[e] : 0.f;
     }
+    const DivS dC(C), dR(R), dRR(RR), dN(N), dP(P), dM4(N / 8), dP8(P / 8);
+    Keep<NTHR2> keep;
     float mvacc = 0.f;   // DMIMO_V item (r, p) = tid (R * P <= 512)
     float ddacc = 0.f;
     const long tokS = (long)bh * p.S;
@@ -409,28 +580,24 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
     for (int c = c_end - 1; c >= c_begin; --c) {
         const int c0 = c * C;
         const int cl = min(C, p.S - c0);
+        const int tid = tid_x();
         __syncthreads();
-        load_chunk<true, NTHR2>(p, sm, b, h, g, bh, c, cl);
+        load_chunk<true, NTHR2>(p, sm, b, h, g, bh, c, cl, dC, dM4, dP8, keep);
         __syncthreads();
 
-        // ---- same-token dots dPhiO[t,r] . Psi[t,r2]; DGAMMA; the D-skip sum
-        for (int e = tid; e < cl * RR; e += NTHR2) {
-            const int t = e / RR, r = (e % RR) / R, r2 = e % R;
-            const float* x = DPO + (r * C + t) * LD;
-            const float* y = PS + (r2 * C + t) * LD;
-            float s = 0.f;
-            for (int pc = 0; pc < P; ++pc) s = __fmaf_rn(x[pc], y[pc], s);
-            DQK[e] = s;
-        }
-        // ---- causal block A = E (Q^ K~^T) and dP = dPhiO Psi^T
+        // ---- causal block A = E (Q^ K~^T) and dP = dPhiO Psi^T; dP's same-token entries
+        // are the dots dPhiO[t,r] . Psi[t,r2] (DGAMMA, the D-skip sum, the same-token parts)
         gemm64<NTHR2, true, true, false>(rows, rows, N, QH, KH, nullptr, [&](int i, int j, float v) {
-            const int ti = i % C, tj = j % C;
+            const int ti = dC.r(i), tj = dC.r(j);
             float a = 0.f;
             if (tj < ti && ti < cl) a = v * FAC[j] * OUT[ti * LD + tj];
             AM[i * LD + j] = a;
         });
-        gemm64<NTHR2, true, true, false>(rows, rows, P, DPO, PS, nullptr,
-                                         [&](int i, int j, float v) { WM[i * LD + j] = v; });
+        gemm64<NTHR2, true, true, false>(rows, rows, P, DPO, PS, nullptr, [&](int i, int j, float v) {
+            WM[i * LD + j] = v;
+            const int ri = dC.q(i), ti = i - ri * C, rj = dC.q(j), tj = j - rj * C;
+            if (ti == tj && ti < cl) DQK[ti * RR + ri * R + rj] = v;
+        });
         __syncthreads();
         if (tid < cl) {
             const int t = tid;
@@ -441,7 +608,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         }
         // ---- DSSDA (per token pair: sum over rank pairs of A * dP), then W = E dP in place
         for (int e = tid; e < C * C; e += NTHR2) {
-            const int t = e / C, s = e % C;
+            const int t = dC.q(e), s = e - t * C;
             float acc = 0.f;
             const bool live = s < t && t < cl;
             const float ex = OUT[t * LD + s];   // zero unless live
@@ -456,7 +623,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         }
         __syncthreads();
         // same-token factors of the diagonal: gamma_t times the dots
-        for (int e = tid; e < cl * RR; e += NTHR2) DQK[e] *= GAM[e / RR];
+        for (int e = tid; e < cl * RR; e += NTHR2) DQK[e] *= GAM[dRR.q(e)];
 
         // ---- dQ^ = exp(da_cs) dPhiO S_c^T (then DDA_CS) + W K~
         gemm64<NTHR2, true, true, false>(rows, N, P, DPO, SC, nullptr,
@@ -486,7 +653,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         __syncthreads();
         // same-token part, in the rotated frame: dq^[t,r] += sum_r2 dqk[t][r][r2] k^[t,r2]
         for (int e = tid; e < rows * N; e += NTHR2) {
-            const int i = e / N, n = e % N, r = i / C, t = i % C;
+            const int i = dN.q(e), n = e - i * N, r = dC.q(i), t = i - r * C;
             if (t >= cl) continue;
             float s = 0.f;
             for (int r2 = 0; r2 < R; ++r2) s = __fmaf_rn(DQK[t * RR + r * R + r2], KH[(r2 * C + t) * LD + n], s);
@@ -494,21 +661,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         }
         __syncthreads();
         // back to the input frame; DQ [B, S*R, H, N]
-        for (int e = tid; e < rows * M; e += NTHR2) {
-            const int i = e / M, n = e % M, r = i / C, t = i % C;
-            if (t >= cl) continue;
-            float a = OUT[i * LD + n], ee = OUT[i * LD + M + n];
-            if (n < W) {
-                float sn, cs;
-                sin_cos(p.angles[((long)(b * p.S + c0 + t) * p.H + h) * W + n], sn, cs);
-                const float a2 = cs * a + sn * ee, e2 = -sn * a + cs * ee;
-                a = a2;
-                ee = e2;
-            }
-            const long o = (((long)b * p.S * R + (long)(c0 + t) * R + r) * p.H + h) * N;
-            store_out<F32OUT>(p.dq, o + n, a);
-            store_out<F32OUT>(p.dq, o + M + n, ee);
-        }
+        store_rot<F32OUT, NTHR2>(p, p.dq, OUT, keep, b, h, c0, cl, dC, dM4);
         __syncthreads();
 
         // ---- dK~ = exp(da_cs_rev) Psi dS^T (then DDA_CS_REV) + W^T Q^
@@ -540,28 +693,14 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         __syncthreads();
         // dk^ = factor dK~ plus the same-token part sum_r dqk[t][r][r2] q^[t,r]
         for (int e = tid; e < rows * N; e += NTHR2) {
-            const int j = e / N, n = e % N, r2 = j / C, t = j % C;
+            const int j = dN.q(e), n = e - j * N, r2 = dC.q(j), t = j - r2 * C;
             if (t >= cl) continue;
             float s = OUT[j * LD + n] * FAC[j];
             for (int r = 0; r < R; ++r) s = __fmaf_rn(DQK[t * RR + r * R + r2], QH[(r * C + t) * LD + n], s);
             OUT[j * LD + n] = s;
         }
         __syncthreads();
-        for (int e = tid; e < rows * M; e += NTHR2) {
-            const int i = e / M, n = e % M, r = i / C, t = i % C;
-            if (t >= cl) continue;
-            float a = OUT[i * LD + n], ee = OUT[i * LD + M + n];
-            if (n < W) {
-                float sn, cs;
-                sin_cos(p.angles[((long)(b * p.S + c0 + t) * p.H + h) * W + n], sn, cs);
-                const float a2 = cs * a + sn * ee, e2 = -sn * a + cs * ee;
-                a = a2;
-                ee = e2;
-            }
-            const long o = (((long)b * p.S * R + (long)(c0 + t) * R + r) * p.H + h) * N;
-            store_out<F32OUT>(p.dk, o + n, a);
-            store_out<F32OUT>(p.dk, o + M + n, ee);
-        }
+        store_rot<F32OUT, NTHR2>(p, p.dk, OUT, keep, b, h, c0, cl, dC, dM4);
         __syncthreads();
 
         // ---- dPsi = kappa dS + A^T dPhiO + gamma (qk^T dPhiO)_same-token + d dPhiO
@@ -571,26 +710,29 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                                            [&](int j, int pc, float v) { OUT[j * LD + pc] += v; });
         __syncthreads();
         for (int e = tid; e < rows * P; e += NTHR2) {
-            const int j = e / P, pc = e % P, r2 = j / C, t = j % C;
+            const int j = dP.q(e), pc = e - j * P, r2 = dC.q(j), t = j - r2 * C;
             if (t >= cl) continue;
             float s = 0.f;
             for (int r = 0; r < R; ++r) s = __fmaf_rn(QKC[t * RR + r * R + r2], DPO[(r * C + t) * LD + pc], s);
             OUT[j * LD + pc] += GAM[j] * s + dval * DPO[j * LD + pc];
         }
         // v of the chunk into the W tile (free after the dK~ products), for DMIMO_V
-        for (int e = tid; e < cl * P; e += NTHR2) {
-            const int t = e / P, pc = e % P;
-            WM[t * LD + pc] = bf(p.v[((long)(b * p.S + c0 + t) * p.H + h) * P + pc]);
+        // (the rank-0 value items hold the chunk's v, zero past the chunk)
+        if (tid < C * (P / 8)) {
+            const int t = dP8.q(tid), p8 = 8 * (tid - t * (P / 8));
+            const u32x4 w = keep.v[0];
+            *reinterpret_cast<f32x4*>(WM + t * LD + p8) = f32x4{lo16(w[0]), hi16(w[0]), lo16(w[1]), hi16(w[1])};
+            *reinterpret_cast<f32x4*>(WM + t * LD + p8 + 4) = f32x4{lo16(w[2]), hi16(w[2]), lo16(w[3]), hi16(w[3])};
         }
         __syncthreads();
         for (int e = tid; e < cl * P; e += NTHR2) {
-            const int t = e / P, pc = e % P;
+            const int t = dP.q(e), pc = e - t * P;
             float s = 0.f;
             for (int r = 0; r < R; ++r) s = __fmaf_rn(OUT[(r * C + t) * LD + pc], p.mimo_v[((long)h * R + r) * P + pc], s);
             store_out<F32OUT>(p.dv, ((long)(b * p.S + c0 + t) * p.H + h) * P + pc, s);
         }
         if (tid < R * P) {
-            const int r = tid / P, pc = tid % P;
+            const int r = dP.q(tid), pc = tid - r * P;
             float s = 0.f;
             for (int t = 0; t < cl; ++t) s = __fmaf_rn(OUT[(r * C + t) * LD + pc], WM[t * LD + pc], s);
             mvacc += s;
@@ -599,7 +741,10 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         // ---- DDA: the state decay exp(da_cs[last]) multiplies S_c in S_{c+1}
         const float dA = expf(p.da_cs[tokS + c0 + cl - 1]);
         float part = 0.f;
-        for (int e = tid; e < N * P; e += NTHR2) part = __fmaf_rn(DS[(e / P) * LD + e % P], SC[(e / P) * LD + e % P], part);
+        for (int e = tid; e < N * P; e += NTHR2) {
+            const int n = dP.q(e), pc = e - n * P;
+            part = __fmaf_rn(DS[n * LD + pc], SC[n * LD + pc], part);
+        }
         const float tot = block_sum<NTHR2>(part, RED);
         if (tid < cl) p.dda[tokS + c0 + tid] = (tid == cl - 1) ? dA * tot : 0.f;
 

@@ -556,9 +556,10 @@ mimo_status make_plan_b2(const mimo_bwd_bwd_args* a, PlanB2* pl) {
     if (H % G) return fail(MIMO_ERR_VALUE, "H must be divisible by G");
     if (rd != 2 && rd != 4) return fail(MIMO_ERR_VALUE, "rotary_dim_divisor must be 2 or 4");
     if (N % 2 || N % rd) return fail(MIMO_ERR_VALUE, "N must be even and divisible by rotary_dim_divisor");
-    if (C * R > 64 || N > 64 || P > 64 || R > 8 || P % 8)
+    if (C * R > 64 || N > 64 || P > 64 || R > 8 || P % 8 || N % 8)
         return fail(MIMO_ERR_UNSUPPORTED,
-                    "the stage-2 backward supports R * chunk_size, N and P up to 64, R up to 8 and P a multiple of 8");
+                    "the stage-2 backward supports R * chunk_size, N and P up to 64, R up to 8 and N and P multiples "
+                    "of 8");
     if (S > (int64_t)1 << 30 || B * H * ((S + C - 1) / C + 8) > (int64_t)1 << 31)
         return fail(MIMO_ERR_UNSUPPORTED, "problem too large");
     pl->W = (int)(N / rd);
@@ -597,6 +598,13 @@ mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events
         !a->dssda || !a->dda_cs_rev || !a->dda_cs)
         return fail(MIMO_ERR_VALUE, "an output pointer is NULL");
     if ((a->dd != nullptr) != (a->d != nullptr)) return fail(MIMO_ERR_VALUE, "dd must be given exactly when d is given");
+    // rows of eight 16-bit or four fp32 values are moved as one 16-byte access
+    for (const void* x : {(const void*)a->dout, (const void*)a->q, (const void*)a->k, (const void*)a->v,
+                          (const void*)a->states, (const void*)a->q_bias, (const void*)a->k_bias,
+                          (const void*)a->mimo_v, (const void*)a->mimo_o, (const void*)a->dq, (const void*)a->dk})
+        if (reinterpret_cast<uintptr_t>(x) % 16)
+            return fail(MIMO_ERR_VALUE, "dout, q, k, v, states, q_bias, k_bias, mimo_v, mimo_o, dq and dk must be "
+                                        "16-byte aligned");
     if (a->workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && a->workspace == nullptr))
         return fail(MIMO_ERR_VALUE, "workspace too small: need %zu bytes, got %zu", pl.ws_bytes, a->workspace_bytes);
     if (pl.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(a->workspace) & 255))

@@ -111,6 +111,34 @@ def test_fp32_and_siso_argument_checks_without_a_device():
     assert L.mimo_siso_fwd(ctypes.byref(s), None) == _lib.MIMO_ERR_VALUE      # NULL inputs
 
 
+def test_bwd_bwd_argument_checks_without_a_device():
+    """The stage-2 entry point rejects shapes beyond its tiles and misaligned rows
+    before any device work."""
+    L = _lib.lib()
+    a = _lib.MimoBwdBwdArgs()
+    a.B, a.S, a.H, a.G, a.R, a.N, a.P = 1, 8192, 16, 1, 4, 64, 64
+    a.chunk_size, a.rotary_dim_divisor = 16, 4
+    n = ctypes.c_size_t(0)
+    assert L.mimo_bwd_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _lib.MIMO_OK
+    for field, val in (("N", 60), ("P", 60), ("N", 128), ("R", 16)):
+        old = getattr(a, field)
+        setattr(a, field, val)
+        if field == "R":
+            a.chunk_size = 4
+        assert L.mimo_bwd_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _lib.MIMO_ERR_UNSUPPORTED, field
+        assert "multiples of 8" in _lib.last_error()
+        setattr(a, field, old)
+        a.chunk_size = 16
+    # every pointer present, one input row start 8 bytes off
+    for f, typ in _lib.MimoBwdBwdArgs._fields_:
+        if typ is ctypes.c_void_p and f not in ("d", "dd", "workspace"):
+            setattr(a, f, 1 << 20)
+    a.S = 16                    # one chunk: no workspace
+    a.q = (1 << 20) + 8
+    assert L.mimo_bwd_bwd(ctypes.byref(a), None) == _lib.MIMO_ERR_VALUE
+    assert "16-byte aligned" in _lib.last_error()
+
+
 @pytest.mark.parametrize("chunk", [48, 0, True, 64.0, "64"])
 def test_siso_invalid_chunk_size(chunk):
     """chunk_size must be the int 32 or 64 (not a bool, a float or another int)."""

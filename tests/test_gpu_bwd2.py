@@ -157,3 +157,31 @@ def test_bwd2_beyond_tiles_rejected(case):
     states, qk = _caches(inp)
     with pytest.raises(NotImplementedError):
         _run_gpu(inp, states, qk)
+
+
+def test_bwd2_unaligned_views_match():
+    """Device inputs that are views starting inside a 16-byte row (the binding copies
+    them to aligned storage) give bit-identical results."""
+    from mamba_mimo_chunked_amd import mamba3_mimo_bwd_bwd
+    case = Case(1, 200, 2, 1, 32, 32, 4, 16, name="unaligned")
+    inp = make_inputs(case)
+    states, qk = _caches(inp)
+    a = _run_gpu(inp, states, qk, torch.float32)
+
+    def shifted(x):
+        buf = torch.empty(x.numel() + 3, dtype=x.dtype, device="cuda")
+        view = buf[3:].view(x.shape)
+        view.copy_(x)
+        assert view.data_ptr() % 16 != 0
+        return view
+
+    dev = {n: x.to("cuda") for n, x in dict(inp, states=states, qk_dot=qk).items() if n in ORDER}
+    for n in ("dout", "q", "k", "v", "states"):
+        dev[n] = shifted(dev[n])
+    b = mamba3_mimo_bwd_bwd(*[dev[n] for n in ORDER], mimo_o=inp["mimo_o"].to("cuda"), d=inp["d"].to("cuda"),
+                            chunk_size=inp["chunk_size"], rotary_dim_divisor=inp["rotary_dim_divisor"],
+                            output_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for key in bwd2.NAMES:
+        if a[key] is not None:
+            assert torch.equal(a[key], b[key]), key
