@@ -77,43 +77,55 @@ __device__ __forceinline__ void gemm64(int Mi, int Nj, int K, const float* A, co
     const int tid = tid_x(), w = tid >> 6, x = tid & 15, q = (tid >> 4) & 3;
     const int i0 = 16 * (w / WR), j0 = 16 * CW * (w % WR);
     if (i0 >= Mi) return;   // wave-uniform
-    f32x4 acc[CW];
-#pragma unroll
-    for (int cb = 0; cb < CW; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // every operand of the product is read before the first MFMA (K <= 64: four steps)
     const int nk = (K + 15) >> 4;
-    for (int kt = 0; kt < nk; ++kt) {
+    float a[4][4], bv[4][CW][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+        if (kt >= nk) break;   // wave-uniform
         const int kb = 16 * kt + 4 * q;
-        float a[4];
         if constexpr (AK1) {
             const f32x4 t = *reinterpret_cast<const f32x4*>(A + (i0 + x) * LD + kb);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) a[v] = t[v];
+            for (int v = 0; v < 4; ++v) a[kt][v] = t[v];
         } else {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) a[v] = A[(kb + v) * LD + i0 + x];
+            for (int v = 0; v < 4; ++v) a[kt][v] = A[(kb + v) * LD + i0 + x];
         }
         if constexpr (SK) {
-            const f32x4 s = *reinterpret_cast<const f32x4*>(sk + kb);
+            const f32x4 sc = *reinterpret_cast<const f32x4*>(sk + kb);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) a[v] *= s[v];
+            for (int v = 0; v < 4; ++v) a[kt][v] *= sc[v];
         }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) a[v] = kb + v < K ? a[v] : 0.f;
 #pragma unroll
         for (int cb = 0; cb < CW; ++cb) {
             const int jb = j0 + 16 * cb;
             if (jb >= Nj) break;   // wave-uniform
-            float bv[4];
             if constexpr (BK1) {
                 const f32x4 t = *reinterpret_cast<const f32x4*>(B + (jb + x) * LD + kb);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) bv[v] = t[v];
+                for (int v = 0; v < 4; ++v) bv[kt][cb][v] = t[v];
             } else {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) bv[v] = B[(kb + v) * LD + jb + x];
+                for (int v = 0; v < 4; ++v) bv[kt][cb][v] = B[(kb + v) * LD + jb + x];
             }
+        }
+    }
+    f32x4 acc[CW];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[cb] = mfma_f32(a[v], kb + v < K ? bv[v] : 0.f, acc[cb]);
+    for (int cb = 0; cb < CW; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+        if (kt >= nk) break;
+        const int kb = 16 * kt + 4 * q;
+#pragma unroll
+        for (int cb = 0; cb < CW; ++cb) {
+            if (j0 + 16 * cb >= Nj) break;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const bool in = kb + v < K;
+                acc[cb] = mfma_f32(in ? a[kt][v] : 0.f, in ? bv[kt][cb][v] : 0.f, acc[cb]);
+            }
         }
     }
 #pragma unroll
@@ -440,7 +452,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_agg2(Params2 p) {
         __syncthreads();
         load_chunk<false, NTHR>(p, sm, b, h, g, bh, c, cl, dC, dM4, dP8, keep);
         __syncthreads();
-        const float dA = expf(p.da_cs[(long)bh * p.S + c * C + cl - 1]);
+        const float dA = ECS[cl - 1];   // exp(da_cs) at the chunk's last token
         // U[n][p] = sum_i Q^[i][n] exp(da_cs[t_i]) dPhiO[i][p] + dA U[n][p]; the thread that
         // owns (n, p) in the product is the only one reading and writing U[n][p]
         // A(n, i) = Q^[i][n], B(i, p) = dPhiO[i][p] scaled per i by exp(da_cs[t_i])
@@ -571,26 +583,45 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         const float* E = (seg + 1 < p.nseg) ? p.agg + ((long)bh * p.nsub + seg * p.F) * N * P : nullptr;
         for (int e = tid; e < N * P; e += NTHR2) DS[(e / P) * LD + e % P] = E ? E[e] : 0.f;
     }
-    const DivS dC(C), dR(R), dRR(RR), dN(N), dP(P), dM4(N / 8), dP8(P / 8);
+    const long tokS = (long)bh * p.S;
+    const DivS dC(C), dRR(RR), dP(P), dN4(N / 4), dP4(P / 4), dM4(N / 8), dP8(P / 8);
     Keep<NTHR2> keep;
+    // DDA of the previous chunk: its last token takes exp(da_cs[last]) times the sum of
+    // the per-wave partials in RED (written after the chunk's dS product)
+    int pend_c0 = 0, pend_cl = 0;
+    float pend_dA = 0.f;
+    auto flush_dda = [&]() {
+        const int t = tid_x();
+        if (t < pend_cl) {
+            float tot = 0.f;
+#pragma unroll
+            for (int w = 0; w < NTHR2 / 64; ++w) tot += RED[w];
+            p.dda[tokS + pend_c0 + t] = (t == pend_cl - 1) ? pend_dA * tot : 0.f;
+        }
+        pend_cl = 0;
+    };
     float mvacc = 0.f;   // DMIMO_V item (r, p) = tid (R * P <= 512)
     float ddacc = 0.f;
-    const long tokS = (long)bh * p.S;
 
     for (int c = c_end - 1; c >= c_begin; --c) {
         const int c0 = c * C;
         const int cl = min(C, p.S - c0);
         const int tid = tid_x();
         __syncthreads();
+        flush_dda();
         load_chunk<true, NTHR2>(p, sm, b, h, g, bh, c, cl, dC, dM4, dP8, keep);
         __syncthreads();
 
         // ---- causal block A = E (Q^ K~^T) and dP = dPhiO Psi^T; dP's same-token entries
-        // are the dots dPhiO[t,r] . Psi[t,r2] (DGAMMA, the D-skip sum, the same-token parts)
+        // are the dots dPhiO[t,r] . Psi[t,r2] (DGAMMA, the D-skip sum, the same-token parts).
+        // The same-token entries of A take the coefficients with which Psi[t,r2] enters
+        // y[t,r] directly, gamma_t qk_dot[t][r][r2] (+ d where r = r2), so A^T dPhiO carries
+        // those terms of dPsi.
         gemm64<NTHR2, true, true, false>(rows, rows, N, QH, KH, nullptr, [&](int i, int j, float v) {
-            const int ti = dC.r(i), tj = dC.r(j);
+            const int ri = dC.q(i), ti = i - ri * C, rj = dC.q(j), tj = j - rj * C;
             float a = 0.f;
             if (tj < ti && ti < cl) a = v * FAC[j] * OUT[ti * LD + tj];
+            if (tj == ti && ti < cl) a = GAM[j] * QKC[ti * RR + ri * R + rj] + (i == j ? dval : 0.f);
             AM[i * LD + j] = a;
         });
         gemm64<NTHR2, true, true, false>(rows, rows, P, DPO, PS, nullptr, [&](int i, int j, float v) {
@@ -652,12 +683,19 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         }
         __syncthreads();
         // same-token part, in the rotated frame: dq^[t,r] += sum_r2 dqk[t][r][r2] k^[t,r2]
-        for (int e = tid; e < rows * N; e += NTHR2) {
-            const int i = dN.q(e), n = e - i * N, r = dC.q(i), t = i - r * C;
+        for (int e = tid; e < rows * (N / 4); e += NTHR2) {
+            const int i = dN4.q(e), n4 = 4 * (e - i * (N / 4)), r = dC.q(i), t = i - r * C;
             if (t >= cl) continue;
-            float s = 0.f;
-            for (int r2 = 0; r2 < R; ++r2) s = __fmaf_rn(DQK[t * RR + r * R + r2], KH[(r2 * C + t) * LD + n], s);
-            OUT[i * LD + n] += s;
+            float s[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int r2 = 0; r2 < R; ++r2) {
+                const float dq = DQK[t * RR + r * R + r2];
+                const f32x4 k4 = *reinterpret_cast<const f32x4*>(KH + (r2 * C + t) * LD + n4);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) s[v] = __fmaf_rn(dq, k4[v], s[v]);
+            }
+            f32x4* o = reinterpret_cast<f32x4*>(OUT + i * LD + n4);
+            const f32x4 ov = *o;
+            *o = f32x4{ov[0] + s[0], ov[1] + s[1], ov[2] + s[2], ov[3] + s[3]};
         }
         __syncthreads();
         // back to the input frame; DQ [B, S*R, H, N]
@@ -692,30 +730,30 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         }
         __syncthreads();
         // dk^ = factor dK~ plus the same-token part sum_r dqk[t][r][r2] q^[t,r]
-        for (int e = tid; e < rows * N; e += NTHR2) {
-            const int j = dN.q(e), n = e - j * N, r2 = dC.q(j), t = j - r2 * C;
+        for (int e = tid; e < rows * (N / 4); e += NTHR2) {
+            const int j = dN4.q(e), n4 = 4 * (e - j * (N / 4)), r2 = dC.q(j), t = j - r2 * C;
             if (t >= cl) continue;
-            float s = OUT[j * LD + n] * FAC[j];
-            for (int r = 0; r < R; ++r) s = __fmaf_rn(DQK[t * RR + r * R + r2], QH[(r * C + t) * LD + n], s);
-            OUT[j * LD + n] = s;
+            f32x4* o = reinterpret_cast<f32x4*>(OUT + j * LD + n4);
+            const f32x4 ov = *o;
+            const float fj = FAC[j];
+            float s[4] = {ov[0] * fj, ov[1] * fj, ov[2] * fj, ov[3] * fj};
+            for (int r = 0; r < R; ++r) {
+                const float dq = DQK[t * RR + r * R + r2];
+                const f32x4 q4 = *reinterpret_cast<const f32x4*>(QH + (r * C + t) * LD + n4);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) s[v] = __fmaf_rn(dq, q4[v], s[v]);
+            }
+            *o = f32x4{s[0], s[1], s[2], s[3]};
         }
         __syncthreads();
         store_rot<F32OUT, NTHR2>(p, p.dk, OUT, keep, b, h, c0, cl, dC, dM4);
         __syncthreads();
 
-        // ---- dPsi = kappa dS + A^T dPhiO + gamma (qk^T dPhiO)_same-token + d dPhiO
+        // ---- dPsi = kappa dS + A^T dPhiO (the latter with the same-token and d terms)
         gemm64<NTHR2, true, false, false>(rows, P, N, KH, DS, nullptr,
                                           [&](int j, int pc, float v) { OUT[j * LD + pc] = v * FAC[j] * EREV[j]; });
         gemm64<NTHR2, false, false, false>(rows, P, rows, AM, DPO, nullptr,
                                            [&](int j, int pc, float v) { OUT[j * LD + pc] += v; });
-        __syncthreads();
-        for (int e = tid; e < rows * P; e += NTHR2) {
-            const int j = dP.q(e), pc = e - j * P, r2 = dC.q(j), t = j - r2 * C;
-            if (t >= cl) continue;
-            float s = 0.f;
-            for (int r = 0; r < R; ++r) s = __fmaf_rn(QKC[t * RR + r * R + r2], DPO[(r * C + t) * LD + pc], s);
-            OUT[j * LD + pc] += GAM[j] * s + dval * DPO[j * LD + pc];
-        }
         // v of the chunk into the W tile (free after the dK~ products), for DMIMO_V
         // (the rank-0 value items hold the chunk's v, zero past the chunk)
         if (tid < C * (P / 8)) {
@@ -725,11 +763,20 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
             *reinterpret_cast<f32x4*>(WM + t * LD + p8 + 4) = f32x4{lo16(w[2]), hi16(w[2]), lo16(w[3]), hi16(w[3])};
         }
         __syncthreads();
-        for (int e = tid; e < cl * P; e += NTHR2) {
-            const int t = dP.q(e), pc = e - t * P;
-            float s = 0.f;
-            for (int r = 0; r < R; ++r) s = __fmaf_rn(OUT[(r * C + t) * LD + pc], p.mimo_v[((long)h * R + r) * P + pc], s);
-            store_out<F32OUT>(p.dv, ((long)(b * p.S + c0 + t) * p.H + h) * P + pc, s);
+        for (int e = tid; e < cl * (P / 4); e += NTHR2) {
+            const int t = dP4.q(e), p4 = 4 * (e - t * (P / 4));
+            float s[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < R; ++r) {
+                const f32x4 o = *reinterpret_cast<const f32x4*>(OUT + (r * C + t) * LD + p4);
+                const f32x4 m = *reinterpret_cast<const f32x4*>(p.mimo_v + ((long)h * R + r) * P + p4);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) s[v] = __fmaf_rn(o[v], m[v], s[v]);
+            }
+            const long o = ((long)(b * p.S + c0 + t) * p.H + h) * P + p4;
+            if constexpr (F32OUT)
+                *reinterpret_cast<f32x4*>(static_cast<float*>(p.dv) + o) = f32x4{s[0], s[1], s[2], s[3]};
+            else
+                *reinterpret_cast<u32x2*>(static_cast<unsigned short*>(p.dv) + o) = u32x2{pk2(s[0], s[1]), pk2(s[2], s[3])};
         }
         if (tid < R * P) {
             const int r = dP.q(tid), pc = tid - r * P;
@@ -738,20 +785,26 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
             mvacc += s;
         }
 
-        // ---- DDA: the state decay exp(da_cs[last]) multiplies S_c in S_{c+1}
-        const float dA = expf(p.da_cs[tokS + c0 + cl - 1]);
+        // ---- dS_c = Q^^T (exp(da_cs) dPhiO) + exp(da_cs[last]) dS_{c+1}, and DDA: the state
+        // decay exp(da_cs[last]) multiplies S_c in S_{c+1}, so DDA[last] = exp(da_cs[last])
+        // sum(dS_{c+1} * S_c), summed from the elements each lane updates (a wave's partial
+        // into RED, the total after the next barrier)
+        const float dA = ECS[cl - 1];
         float part = 0.f;
-        for (int e = tid; e < N * P; e += NTHR2) {
-            const int n = dP.q(e), pc = e - n * P;
-            part = __fmaf_rn(DS[n * LD + pc], SC[n * LD + pc], part);
-        }
-        const float tot = block_sum<NTHR2>(part, RED);
-        if (tid < cl) p.dda[tokS + c0 + tid] = (tid == cl - 1) ? dA * tot : 0.f;
-
-        // ---- dS_c = Q^^T (exp(da_cs) dPhiO) + exp(da_cs[last]) dS_{c+1}
-        gemm64<NTHR2, false, false, true>(N, P, rows, QH, DPO, ECS,
-                                          [&](int n, int pc, float v) { DS[n * LD + pc] = v + dA * DS[n * LD + pc]; });
+        gemm64<NTHR2, false, false, true>(N, P, rows, QH, DPO, ECS, [&](int n, int pc, float v) {
+            const float old = DS[n * LD + pc];
+            part = __fmaf_rn(old, SC[n * LD + pc], part);
+            DS[n * LD + pc] = v + dA * old;
+        });
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+        if ((tid & 63) == 0) RED[tid >> 6] = part;
+        pend_c0 = c0;
+        pend_cl = cl;
+        pend_dA = dA;
     }
+    __syncthreads();
+    flush_dda();
 
     // ---- per-segment partial sums of DMIMO_V and DD
     __syncthreads();
