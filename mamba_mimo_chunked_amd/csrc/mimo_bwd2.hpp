@@ -45,7 +45,6 @@ struct Params2 {
 };
 
 __device__ __forceinline__ float bf(unsigned short x) { return __uint_as_float(static_cast<unsigned>(x) << 16); }
-__device__ __forceinline__ unsigned short to_bf(float x) { return static_cast<unsigned short>(pk2(0.f, x) >> 16); }
 
 // The thread index as a value the compiler cannot move out of a loop: index and
 // address arithmetic is then redone per chunk instead of being held in registers
@@ -68,16 +67,19 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 // j, value). The contraction index is split k = 16 kt + 4 q + v (q = lane / 16, v the
 // accumulation step), so a lane reads four consecutive floats of a
 // contraction-contiguous row in one 16-byte load, or one float of each of four rows;
-// with LD = 4 (mod 64) neither pattern has bank conflicts. Values past K are zeroed
-// (the tiles hold stale data there); rows and columns past Mi / Nj are dropped.
-template <int NT, bool AK1, bool BK1, bool SK, typename F>
+// with LD = 4 (mod 64) neither pattern has bank conflicts. Every operand is read
+// before the first MFMA. Values past K are zeroed (the tiles hold stale data there);
+// rows and columns past Mi / Nj are dropped.
+// RS: epi returns a term of a row sum; the sums over the wave's columns go to
+// rs[(w % (4/CW)) * 64 + i] (one partial per column group, added in a fixed order
+// by the reader after a barrier).
+template <int NT, bool AK1, bool BK1, bool SK, bool RS = false, typename F>
 __device__ __forceinline__ void gemm64(int Mi, int Nj, int K, const float* A, const float* B, const float* sk,
-                                       F&& epi) {
+                                       F&& epi, float* rs = nullptr) {
     constexpr int NW = NT / 64, CW = 16 / NW, WR = 4 / CW;   // waves, column blocks a wave, waves a row block
     const int tid = tid_x(), w = tid >> 6, x = tid & 15, q = (tid >> 4) & 3;
     const int i0 = 16 * (w / WR), j0 = 16 * CW * (w % WR);
     if (i0 >= Mi) return;   // wave-uniform
-    // every operand of the product is read before the first MFMA (K <= 64: four steps)
     const int nk = (K + 15) >> 4;
     float a[4][4], bv[4][CW][4];
 #pragma unroll
@@ -114,27 +116,58 @@ __device__ __forceinline__ void gemm64(int Mi, int Nj, int K, const float* A, co
     f32x4 acc[CW];
 #pragma unroll
     for (int cb = 0; cb < CW; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if ((K & 15) == 0) {   // whole steps: no masking
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-        if (kt >= nk) break;
-        const int kb = 16 * kt + 4 * q;
+        for (int kt = 0; kt < 4; ++kt) {
+            if (kt >= nk) break;
 #pragma unroll
-        for (int cb = 0; cb < CW; ++cb) {
-            if (j0 + 16 * cb >= Nj) break;
+            for (int cb = 0; cb < CW; ++cb) {
+                if (j0 + 16 * cb >= Nj) break;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const bool in = kb + v < K;
-                acc[cb] = mfma_f32(in ? a[kt][v] : 0.f, in ? bv[kt][cb][v] : 0.f, acc[cb]);
+                for (int v = 0; v < 4; ++v) acc[cb] = mfma_f32(a[kt][v], bv[kt][cb][v], acc[cb]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            if (kt >= nk) break;
+            const int kb = 16 * kt + 4 * q;
+#pragma unroll
+            for (int cb = 0; cb < CW; ++cb) {
+                if (j0 + 16 * cb >= Nj) break;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const bool in = kb + v < K;
+                    acc[cb] = mfma_f32(in ? a[kt][v] : 0.f, in ? bv[kt][cb][v] : 0.f, acc[cb]);
+                }
             }
         }
     }
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+    const bool full = i0 + 16 <= Mi && j0 + 16 * CW <= Nj;   // wave-uniform
 #pragma unroll
     for (int cb = 0; cb < CW; ++cb) {
         const int j = j0 + 16 * cb + x;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int i = i0 + 4 * q + v;
-            if (i < Mi && j < Nj) epi(i, j, acc[cb][v]);
+            if (full || (i < Mi && j < Nj)) {
+                if constexpr (RS)
+                    rsum[v] += epi(i, j, acc[cb][v]);
+                else
+                    epi(i, j, acc[cb][v]);
+            }
+        }
+    }
+    if constexpr (RS) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) rsum[v] += __shfl_xor(rsum[v], o);
+        }
+        if (x == 0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) rs[(w % WR) * 64 + i0 + 4 * q + v] = rsum[v];
         }
     }
 }
@@ -154,34 +187,30 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     return s;
 }
 
-// Per-token sums over (rank, column): token t's sum of f(row, n) over rows
-// r*C + t (r < R) and n < N, by a group of 16 lanes (columns strided by 16, then
-// a butterfly over the group); out(t, value) is called by the group's first lane.
-template <int NT, typename F, typename O>
-__device__ __forceinline__ void token_sum(int cl, int R, int C, int N, F&& f, O&& out) {
-    const int tid = tid_x(), grp = tid >> 4, l = tid & 15;
-    for (int t0 = 0; t0 < cl; t0 += NT / 16) {
-        const int t = t0 + grp;
+// Per-token totals of row sums left by a product (rs[h * 64 + i], h < 2 column
+// groups): token t's total over its rows r*C + t (r < R), in a fixed order, handed to
+// out(t, total) by thread t.
+template <typename O>
+__device__ __forceinline__ void token_out(int cl, int R, int C, const float* rs, O&& out) {
+    const int t = tid_x();
+    if (t < cl) {
         float s = 0.f;
-        if (t < cl)
-            for (int r = 0; r < R; ++r)
-                for (int n = l; n < N; n += 16) s += f(r * C + t, n);
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-        if (l == 0 && t < cl) out(t, s);
+        for (int r = 0; r < R; ++r) s += rs[r * C + t] + rs[64 + r * C + t];
+        out(t, s);
     }
 }
 
 // LDS layout (floats) of the chunk pass: q^, k^, Psi, dPhiO, S_c, dS, the causal
 // block, W and an output tile, each [64][LD]; then per-row token scalars (row i =
-// r*C + t: gamma, factor, exp(da_cs), exp(da_cs_rev)), a reduction scratch and the
-// same-token tables [C][R][R] (dots, cached qk_dot). The aggregate uses q^, dPhiO,
+// r*C + t: gamma, factor, exp(da_cs), exp(da_cs_rev)), a reduction scratch, the
+// same-token tables [C][R][R] (dots, cached qk_dot) and two sets of row-sum partials
+// [2][64]. The aggregate uses q^, dPhiO,
 // dS, an output tile and exp(da_cs).
 struct L2 {
     static constexpr int QH = 0, KH = TILE, PS = 2 * TILE, DPO = 3 * TILE, SC = 4 * TILE, DS = 5 * TILE,
                          AM = 6 * TILE, WM = 7 * TILE, OUT = 8 * TILE;
     static constexpr int GAM = 9 * TILE, FAC = GAM + 64, ECS = FAC + 64, EREV = ECS + 64, RED = EREV + 64,
-                         DQK = RED + 8, QKC = DQK + 512, TOTAL = QKC + 512;
+                         DQK = RED + 8, QKC = DQK + 512, RS0 = QKC + 512, RS1 = RS0 + 128, TOTAL = RS1 + 128;
     static constexpr int A_QH = 0, A_DPO = TILE, A_U = 2 * TILE, A_G = 3 * TILE, A_ECS = 4 * TILE,
                          AGG_TOTAL = 4 * TILE + 64;
 };
@@ -499,21 +528,17 @@ __global__ __launch_bounds__(256) void k_scan_rev(Params2 p) {
     }
 }
 
-template <bool F32OUT>
-__device__ __forceinline__ void store_out(void* base, long i, float v) {
-    if constexpr (F32OUT)
-        static_cast<float*>(base)[i] = v;
-    else
-        static_cast<unsigned short*>(base)[i] = to_bf(v);
-}
-
-// A [rows][N] gradient tile of the rotated frame back to the input frame (the
-// inverse rotation of the thread's rotation items, whose cos and sin it kept from
-// the load) and out to DQ or DK [B, S*R, H, N], four columns of each half a store.
-template <bool F32OUT, int NT>
-__device__ __forceinline__ void store_rot(const Params2& p, void* dst, const float* OUT, const Keep<NT>& keep, int b,
-                                          int h, int c0, int cl, const DivS& dC, const DivS& dM4) {
-    const int R = p.R, N = p.N, C = p.C, M = N / 2;
+// The rotated-frame gradient of q^ (KSIDE false: dQ^ in OUT plus the same-token part
+// sum_r2 dqk'[t][r][r2] k^[t,r2]) or of k^ (KSIDE: factor_t dK~ with dK~ in OUT, plus
+// sum_r2 dqk'[t][r2][r] q^[t,r2]), X being k^ or q^ and dqk' the gamma-scaled
+// same-token dots, taken back to the input frame by the inverse rotation of the
+// thread's rotation items (cos and sin kept from the load) and written to DQ or DK
+// [B, S*R, H, N], four columns of each half a store. OUT is only read.
+template <bool F32OUT, int NT, bool KSIDE>
+__device__ __forceinline__ void finish_rot(const Params2& p, void* dst, const float* OUT, const float* X,
+                                           const float* DQK, const float* FAC, const Keep<NT>& keep, int b, int h,
+                                           int c0, int cl, const DivS& dC, const DivS& dM4) {
+    const int R = p.R, N = p.N, C = p.C, M = N / 2, RR = R * R;
 #pragma unroll
     for (int x = 0; x < Items<NT>::IX; ++x) {
         const int e = tid_x() + NT * x;
@@ -523,12 +548,30 @@ __device__ __forceinline__ void store_rot(const Params2& p, void* dst, const flo
         if (t >= cl) continue;
         const f32x4 a = *reinterpret_cast<const f32x4*>(OUT + i * LD + n4);
         const f32x4 ee = *reinterpret_cast<const f32x4*>(OUT + i * LD + M + n4);
+        const float f = KSIDE ? FAC[i] : 1.f;
+        float sa[4], se[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            sa[v] = a[v] * f;
+            se[v] = ee[v] * f;
+        }
+        for (int r2 = 0; r2 < R; ++r2) {
+            const float d = KSIDE ? DQK[t * RR + r2 * R + r] : DQK[t * RR + r * R + r2];
+            const float* xr = X + (r2 * C + t) * LD;
+            const f32x4 xa = *reinterpret_cast<const f32x4*>(xr + n4);
+            const f32x4 xe = *reinterpret_cast<const f32x4*>(xr + M + n4);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                sa[v] = __fmaf_rn(d, xa[v], sa[v]);
+                se[v] = __fmaf_rn(d, xe[v], se[v]);
+            }
+        }
         float a2[4], e2[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const float cs = keep.cs[x][v], sn = keep.sn[x][v];
-            a2[v] = cs * a[v] + sn * ee[v];
-            e2[v] = -sn * a[v] + cs * ee[v];
+            a2[v] = cs * sa[v] + sn * se[v];
+            e2[v] = -sn * sa[v] + cs * se[v];
         }
         const long o = (((long)b * p.S * R + (long)(c0 + t) * R + r) * p.H + h) * N + n4;
         if constexpr (F32OUT) {
@@ -576,6 +619,8 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
     float* RED = sm + L2::RED;
     float* DQK = sm + L2::DQK;
     float* QKC = sm + L2::QKC;
+    float* RS0 = sm + L2::RS0;
+    float* RS1 = sm + L2::RS1;
     const float dval = p.has_d ? p.d[h] : 0.f;
 
     // dS entering the segment from the right
@@ -584,7 +629,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         for (int e = tid; e < N * P; e += NTHR2) DS[(e / P) * LD + e % P] = E ? E[e] : 0.f;
     }
     const long tokS = (long)bh * p.S;
-    const DivS dC(C), dRR(RR), dP(P), dN4(N / 4), dP4(P / 4), dM4(N / 8), dP8(P / 8);
+    const DivS dC(C), dRR(RR), dP(P), dP4(P / 4), dM4(N / 8), dP8(P / 8);
     Keep<NTHR2> keep;
     // DDA of the previous chunk: its last token takes exp(da_cs[last]) times the sum of
     // the per-wave partials in RED (written after the chunk's dS product)
@@ -656,13 +701,18 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         // same-token factors of the diagonal: gamma_t times the dots
         for (int e = tid; e < cl * RR; e += NTHR2) DQK[e] *= GAM[dRR.q(e)];
 
-        // ---- dQ^ = exp(da_cs) dPhiO S_c^T (then DDA_CS) + W K~
-        gemm64<NTHR2, true, true, false>(rows, N, P, DPO, SC, nullptr,
-                                         [&](int i, int n, float v) { OUT[i * LD + n] = v * ECS[i]; });
+        // ---- dQ^ = exp(da_cs) dPhiO S_c^T + W K~; DDA_CS[t] = sum over the token's rows of
+        // q^ . (exp(da_cs) dPhiO S_c^T), as row sums of the first product
+        gemm64<NTHR2, true, true, false, true>(
+            rows, N, P, DPO, SC, nullptr,
+            [&](int i, int n, float v) {
+                const float o = v * ECS[i];
+                OUT[i * LD + n] = o;
+                return QH[i * LD + n] * o;
+            },
+            RS0);
         __syncthreads();
-        token_sum<NTHR2>(cl, R, C, N, [&](int i, int n) { return QH[i * LD + n] * OUT[i * LD + n]; },
-                         [&](int t, float v) { p.dda_cs[tokS + c0 + t] = v; });
-        __syncthreads();
+        token_out(cl, R, C, RS0, [&](int t, float v) { p.dda_cs[tokS + c0 + t] = v; });
         // W K~: B(j, n) = k^[j][n] scaled per j by the factor (folded into A)
         gemm64<NTHR2, true, false, true>(rows, N, rows, WM, KH, FAC,
                                          [&](int i, int n, float v) { OUT[i * LD + n] += v; });
@@ -681,39 +731,32 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                 }
             dth[x] = s;
         }
-        __syncthreads();
-        // same-token part, in the rotated frame: dq^[t,r] += sum_r2 dqk[t][r][r2] k^[t,r2]
-        for (int e = tid; e < rows * (N / 4); e += NTHR2) {
-            const int i = dN4.q(e), n4 = 4 * (e - i * (N / 4)), r = dC.q(i), t = i - r * C;
-            if (t >= cl) continue;
-            float s[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int r2 = 0; r2 < R; ++r2) {
-                const float dq = DQK[t * RR + r * R + r2];
-                const f32x4 k4 = *reinterpret_cast<const f32x4*>(KH + (r2 * C + t) * LD + n4);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) s[v] = __fmaf_rn(dq, k4[v], s[v]);
-            }
-            f32x4* o = reinterpret_cast<f32x4*>(OUT + i * LD + n4);
-            const f32x4 ov = *o;
-            *o = f32x4{ov[0] + s[0], ov[1] + s[1], ov[2] + s[2], ov[3] + s[3]};
-        }
-        __syncthreads();
-        // back to the input frame; DQ [B, S*R, H, N]
-        store_rot<F32OUT, NTHR2>(p, p.dq, OUT, keep, b, h, c0, cl, dC, dM4);
+        // the same-token part, then back to the input frame: DQ (OUT is only read)
+        finish_rot<F32OUT, NTHR2, false>(p, p.dq, OUT, KH, DQK, FAC, keep, b, h, c0, cl, dC, dM4);
         __syncthreads();
 
-        // ---- dK~ = exp(da_cs_rev) Psi dS^T (then DDA_CS_REV) + W^T Q^
-        gemm64<NTHR2, true, true, false>(rows, N, P, PS, DS, nullptr,
-                                         [&](int j, int n, float v) { OUT[j * LD + n] = v * EREV[j]; });
+        // ---- dK~ = exp(da_cs_rev) Psi dS^T + W^T Q^; DDA_CS_REV from the first product's row
+        // sums (k^ . its rows), DFACTOR from those of the whole dK~
+        gemm64<NTHR2, true, true, false, true>(
+            rows, N, P, PS, DS, nullptr,
+            [&](int j, int n, float v) {
+                const float o = v * EREV[j];
+                OUT[j * LD + n] = o;
+                return KH[j * LD + n] * o;
+            },
+            RS1);
         __syncthreads();
-        token_sum<NTHR2>(cl, R, C, N, [&](int i, int n) { return KH[i * LD + n] * OUT[i * LD + n]; },
-                         [&](int t, float v) { p.dda_cs_rev[tokS + c0 + t] = v * FAC[t]; });
+        token_out(cl, R, C, RS1, [&](int t, float v) { p.dda_cs_rev[tokS + c0 + t] = v * FAC[t]; });
+        gemm64<NTHR2, false, false, false, true>(
+            rows, N, rows, WM, QH, nullptr,
+            [&](int j, int n, float v) {
+                const float o = OUT[j * LD + n] + v;
+                OUT[j * LD + n] = o;
+                return KH[j * LD + n] * o;
+            },
+            RS0);
         __syncthreads();
-        gemm64<NTHR2, false, false, false>(rows, N, rows, WM, QH, nullptr,
-                                           [&](int j, int n, float v) { OUT[j * LD + n] += v; });
-        __syncthreads();
-        token_sum<NTHR2>(cl, R, C, N, [&](int i, int n) { return KH[i * LD + n] * OUT[i * LD + n]; },
-                         [&](int t, float v) { p.dfactor[tokS + c0 + t] = v; });
+        token_out(cl, R, C, RS0, [&](int t, float v) { p.dfactor[tokS + c0 + t] = v; });
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int e = tid + NTHR2 * x;
@@ -728,32 +771,8 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                 p.dangles[((long)(b * p.S + c0 + t) * p.H + h) * W + n] = dth[x];
             }
         }
-        __syncthreads();
-        // dk^ = factor dK~ plus the same-token part sum_r dqk[t][r][r2] q^[t,r]
-        for (int e = tid; e < rows * (N / 4); e += NTHR2) {
-            const int j = dN4.q(e), n4 = 4 * (e - j * (N / 4)), r2 = dC.q(j), t = j - r2 * C;
-            if (t >= cl) continue;
-            f32x4* o = reinterpret_cast<f32x4*>(OUT + j * LD + n4);
-            const f32x4 ov = *o;
-            const float fj = FAC[j];
-            float s[4] = {ov[0] * fj, ov[1] * fj, ov[2] * fj, ov[3] * fj};
-            for (int r = 0; r < R; ++r) {
-                const float dq = DQK[t * RR + r * R + r2];
-                const f32x4 q4 = *reinterpret_cast<const f32x4*>(QH + (r * C + t) * LD + n4);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) s[v] = __fmaf_rn(dq, q4[v], s[v]);
-            }
-            *o = f32x4{s[0], s[1], s[2], s[3]};
-        }
-        __syncthreads();
-        store_rot<F32OUT, NTHR2>(p, p.dk, OUT, keep, b, h, c0, cl, dC, dM4);
-        __syncthreads();
-
-        // ---- dPsi = kappa dS + A^T dPhiO (the latter with the same-token and d terms)
-        gemm64<NTHR2, true, false, false>(rows, P, N, KH, DS, nullptr,
-                                          [&](int j, int pc, float v) { OUT[j * LD + pc] = v * FAC[j] * EREV[j]; });
-        gemm64<NTHR2, false, false, false>(rows, P, rows, AM, DPO, nullptr,
-                                           [&](int j, int pc, float v) { OUT[j * LD + pc] += v; });
+        // dk^ = factor dK~ plus the same-token part, then back to the input frame: DK
+        finish_rot<F32OUT, NTHR2, true>(p, p.dk, OUT, QH, DQK, FAC, keep, b, h, c0, cl, dC, dM4);
         // v of the chunk into the W tile (free after the dK~ products), for DMIMO_V
         // (the rank-0 value items hold the chunk's v, zero past the chunk)
         if (tid < C * (P / 8)) {
@@ -762,6 +781,13 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
             *reinterpret_cast<f32x4*>(WM + t * LD + p8) = f32x4{lo16(w[0]), hi16(w[0]), lo16(w[1]), hi16(w[1])};
             *reinterpret_cast<f32x4*>(WM + t * LD + p8 + 4) = f32x4{lo16(w[2]), hi16(w[2]), lo16(w[3]), hi16(w[3])};
         }
+        __syncthreads();
+
+        // ---- dPsi = kappa dS + A^T dPhiO (the latter with the same-token and d terms)
+        gemm64<NTHR2, true, false, false>(rows, P, N, KH, DS, nullptr,
+                                          [&](int j, int pc, float v) { OUT[j * LD + pc] = v * FAC[j] * EREV[j]; });
+        gemm64<NTHR2, false, false, false>(rows, P, rows, AM, DPO, nullptr,
+                                           [&](int j, int pc, float v) { OUT[j * LD + pc] += v; });
         __syncthreads();
         for (int e = tid; e < cl * (P / 4); e += NTHR2) {
             const int t = dP4.q(e), p4 = 4 * (e - t * (P / 4));
