@@ -234,140 +234,171 @@ struct DivS {
 //   value items (i, p8): eight columns of dPhiO (and Psi) of row i; the thread keeps
 //     its raw v (the rank-0 items' v is the chunk's v);
 //   state items: eight consecutive values of the cached state.
+// A thread's items are the same in every chunk, so the biases and projections they
+// use are read once (Res). The loads of a chunk (Fetch) are issued a chunk ahead and
+// staged into LDS (rotated, scaled, converted to fp32) at the start of the chunk.
 template <int NT>
 struct Items {
     static constexpr int IX = 512 / NT;
+    static constexpr int SX = 64 * 64 / NT;   // segsum values a thread (C * C <= 4096)
 };
 template <int NT>
 struct Keep {
     float cs[Items<NT>::IX][4], sn[Items<NT>::IX][4];
     u32x4 v[Items<NT>::IX];
 };
+template <int NT>
+struct Res {
+    f32x4 qb[Items<NT>::IX][2], kb[Items<NT>::IX][2], mo[Items<NT>::IX][2], mv[Items<NT>::IX][2];
+};
+template <int NT>
+struct Fetch {
+    u32x2 qw[Items<NT>::IX][2], kw[Items<NT>::IX][2];
+    float ang[Items<NT>::IX][4];
+    u32x4 dw[Items<NT>::IX], vw[Items<NT>::IX], sw[Items<NT>::IX];
+    float s_cs, s_rev, s_dt, s_tr, s_dt1, s_tr1, qk;
+    float seg[Items<NT>::SX];
+};
 
-// Load chunk c's rotated q^ (and k^, Psi, the cached state, qk_dot, exp(segsum) and
-// the per-row scalars when MAIN), dPhiO and exp(da_cs) into LDS. Every global load
-// of a thread is issued before any of them is used. Rows past the chunk (t >= cl)
-// are zero.
+// The index decompositions of the chunk-load items.
+struct ItemDiv {
+    DivS dC, dM4, dP8;
+    __device__ ItemDiv(int C, int N, int P) : dC(C), dM4(N / 8), dP8(P / 8) {}
+};
+
 template <bool MAIN, int NT>
-__device__ __forceinline__ void load_chunk(const Params2& p, float* sm, int b, int h, int g, int bh, int c, int cl,
-                                           const DivS& dC, const DivS& dM4, const DivS& dP8, Keep<NT>& keep) {
-    constexpr int IX = Items<NT>::IX;
-    constexpr int SX = 64 * 64 / NT;   // segsum values a thread (C * C <= 4096)
+__device__ __forceinline__ void load_resident(const Params2& p, int h, const ItemDiv& dv, Res<NT>& res) {
+    const int R = p.R, N = p.N, P = p.P, C = p.C, M = N / 2;
+    const int tid = tid_x(), rows = R * C;
+#pragma unroll
+    for (int x = 0; x < Items<NT>::IX; ++x) {
+        const int e = tid + NT * x;
+        if (e < rows * (M / 4)) {
+            const int i = dv.dM4.q(e), n4 = 4 * (e - i * (M / 4)), r = dv.dC.q(i);
+            const float* qbp = p.q_bias + ((long)h * R + r) * N + n4;
+            res.qb[x][0] = *reinterpret_cast<const f32x4*>(qbp);
+            res.qb[x][1] = *reinterpret_cast<const f32x4*>(qbp + M);
+            if (MAIN) {
+                const float* kbp = p.k_bias + ((long)h * R + r) * N + n4;
+                res.kb[x][0] = *reinterpret_cast<const f32x4*>(kbp);
+                res.kb[x][1] = *reinterpret_cast<const f32x4*>(kbp + M);
+            }
+        }
+        if (e < rows * (P / 8)) {
+            const int i = dv.dP8.q(e), p8 = 8 * (e - i * (P / 8)), r = dv.dC.q(i);
+            if (p.reduce_o) {
+                const float* m = p.mimo_o + ((long)h * R + r) * P + p8;
+                res.mo[x][0] = *reinterpret_cast<const f32x4*>(m);
+                res.mo[x][1] = *reinterpret_cast<const f32x4*>(m + 4);
+            }
+            if (MAIN) {
+                const float* m = p.mimo_v + ((long)h * R + r) * P + p8;
+                res.mv[x][0] = *reinterpret_cast<const f32x4*>(m);
+                res.mv[x][1] = *reinterpret_cast<const f32x4*>(m + 4);
+            }
+        }
+    }
+}
+
+// Issue chunk c's global loads (rows past the chunk are not read).
+template <bool MAIN, int NT>
+__device__ __forceinline__ void fetch_chunk(const Params2& p, int b, int h, int g, int bh, int c, const ItemDiv& dv,
+                                            Fetch<NT>& f) {
     const int R = p.R, N = p.N, P = p.P, C = p.C, W = p.W, M = N / 2;
-    const int tid = tid_x();
-    const int c0 = c * C;
-    const int rows = R * C, RR = R * R;
-    const int nrot = rows * (M / 4), nval = rows * (P / 8), nst = N * (P / 8);
+    const int tid = tid_x(), rows = R * C, RR = R * R;
+    const int c0 = c * C, cl = min(C, p.S - c0);
     const long tok0 = (long)b * p.S + c0;   // (b, c0) as a token index
     const long tb0 = (long)bh * p.S + c0;   // (b, h, c0) for the per-token arrays
+#pragma unroll
+    for (int x = 0; x < Items<NT>::IX; ++x) {
+        const int e = tid + NT * x;
+        if (e < rows * (M / 4)) {
+            const int i = dv.dM4.q(e), n4 = 4 * (e - i * (M / 4));
+            const int r = dv.dC.q(i), t = i - r * C;
+            if (t < cl) {
+                const long src = (((tok0 + t) * R + r) * p.G + g) * N + n4;
+                f.qw[x][0] = *reinterpret_cast<const u32x2*>(p.q + src);
+                f.qw[x][1] = *reinterpret_cast<const u32x2*>(p.q + src + M);
+                if (MAIN) {
+                    f.kw[x][0] = *reinterpret_cast<const u32x2*>(p.k + src);
+                    f.kw[x][1] = *reinterpret_cast<const u32x2*>(p.k + src + M);
+                }
+                const float* ap = p.angles + ((tok0 + t) * p.H + h) * W;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) f.ang[x][v] = n4 + v < W ? ap[n4 + v] : 0.f;
+            }
+        }
+        if (e < rows * (P / 8)) {
+            const int i = dv.dP8.q(e), p8 = 8 * (e - i * (P / 8));
+            const int r = dv.dC.q(i), t = i - r * C;
+            if (t < cl) {
+                const long tk = tok0 + t;
+                f.dw[x] = *reinterpret_cast<const u32x4*>(
+                    p.dout + (p.reduce_o ? (tk * p.H + h) * P : ((tk * R + r) * p.H + h) * P) + p8);
+                if (MAIN) f.vw[x] = *reinterpret_cast<const u32x4*>(p.v + (tk * p.H + h) * P + p8);
+            }
+        }
+        if (MAIN && e < N * (P / 8))
+            f.sw[x] = *reinterpret_cast<const u32x4*>(p.states + ((long)bh * p.nc + c) * N * P + 8 * e);
+    }
+    if (tid < cl) {
+        f.s_cs = p.da_cs[tb0 + tid];
+        if (MAIN) {
+            f.s_rev = p.da_cs_rev[tb0 + tid];
+            f.s_dt = p.dt[tb0 + tid];
+            f.s_tr = bf(p.trap[tb0 + tid]);
+            if (c0 + tid + 1 < p.S) {
+                f.s_dt1 = p.dt[tb0 + tid + 1];
+                f.s_tr1 = bf(p.trap[tb0 + tid + 1]);
+            }
+        }
+    }
+    if (MAIN) {
+        if (tid < cl * RR) f.qk = bf(p.qk_dot[tb0 * RR + tid]);
+#pragma unroll
+        for (int x = 0; x < Items<NT>::SX; ++x) {
+            const int e = tid + NT * x;
+            const int t = dv.dC.q(e), s2 = e - t * C;
+            if (e < C * C && s2 < t && t < cl) f.seg[x] = p.segsum[((long)bh * p.nc + c) * C * C + e];
+        }
+    }
+}
+
+// Stage chunk c from its fetched loads into LDS: rotated q^ (and k^, Psi, the cached
+// state, qk_dot, exp(segsum) and the per-row scalars when MAIN), dPhiO and exp(da_cs).
+// Rows past the chunk (t >= cl) are zero.
+template <bool MAIN, int NT>
+__device__ __forceinline__ void stage_chunk(const Params2& p, float* sm, int c, const ItemDiv& dv, const Fetch<NT>& f,
+                                            const Res<NT>& res, Keep<NT>& keep) {
+    const int R = p.R, N = p.N, P = p.P, C = p.C, W = p.W, M = N / 2;
+    const int tid = tid_x(), rows = R * C, RR = R * R;
+    const int c0 = c * C, cl = min(C, p.S - c0);
     float* QH = sm + (MAIN ? L2::QH : L2::A_QH);
     float* KH = sm + L2::KH;
     float* PS = sm + L2::PS;
     float* DPO = sm + (MAIN ? L2::DPO : L2::A_DPO);
     float* ECS = sm + (MAIN ? L2::ECS : L2::A_ECS);
-
-    // ---- issue the loads
-    u32x2 qw[IX][2], kw[IX][2];
-    f32x4 qb[IX][2], kb[IX][2];
-    float ang[IX][4];
-    u32x4 dw[IX], vw[IX], sw[IX];
-    f32x4 mo[IX][2], mv[IX][2];
 #pragma unroll
-    for (int x = 0; x < IX; ++x) {
+    for (int x = 0; x < Items<NT>::IX; ++x) {
         const int e = tid + NT * x;
-        if (e < nrot) {
-            const int i = dM4.q(e), n4 = 4 * (e - i * (M / 4));
-            const int r = dC.q(i), t = i - r * C;
-            if (t < cl) {
-                const long src = (((tok0 + t) * R + r) * p.G + g) * N + n4;
-                const float* qbp = p.q_bias + ((long)h * R + r) * N + n4;
-                qw[x][0] = *reinterpret_cast<const u32x2*>(p.q + src);
-                qw[x][1] = *reinterpret_cast<const u32x2*>(p.q + src + M);
-                qb[x][0] = *reinterpret_cast<const f32x4*>(qbp);
-                qb[x][1] = *reinterpret_cast<const f32x4*>(qbp + M);
-                if (MAIN) {
-                    const float* kbp = p.k_bias + ((long)h * R + r) * N + n4;
-                    kw[x][0] = *reinterpret_cast<const u32x2*>(p.k + src);
-                    kw[x][1] = *reinterpret_cast<const u32x2*>(p.k + src + M);
-                    kb[x][0] = *reinterpret_cast<const f32x4*>(kbp);
-                    kb[x][1] = *reinterpret_cast<const f32x4*>(kbp + M);
-                }
-                const float* ap = p.angles + ((tok0 + t) * p.H + h) * W;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) ang[x][v] = n4 + v < W ? ap[n4 + v] : 0.f;
-            }
-        }
-        if (e < nval) {
-            const int i = dP8.q(e), p8 = 8 * (e - i * (P / 8));
-            const int r = dC.q(i), t = i - r * C;
-            if (t < cl) {
-                const long tk = tok0 + t;
-                if (p.reduce_o) {
-                    dw[x] = *reinterpret_cast<const u32x4*>(p.dout + (tk * p.H + h) * P + p8);
-                    const float* m = p.mimo_o + ((long)h * R + r) * P + p8;
-                    mo[x][0] = *reinterpret_cast<const f32x4*>(m);
-                    mo[x][1] = *reinterpret_cast<const f32x4*>(m + 4);
-                } else {
-                    dw[x] = *reinterpret_cast<const u32x4*>(p.dout + ((tk * R + r) * p.H + h) * P + p8);
-                }
-                if (MAIN) {
-                    vw[x] = *reinterpret_cast<const u32x4*>(p.v + (tk * p.H + h) * P + p8);
-                    const float* m = p.mimo_v + ((long)h * R + r) * P + p8;
-                    mv[x][0] = *reinterpret_cast<const f32x4*>(m);
-                    mv[x][1] = *reinterpret_cast<const f32x4*>(m + 4);
-                }
-            }
-        }
-        if (MAIN && e < nst) sw[x] = *reinterpret_cast<const u32x4*>(p.states + ((long)bh * p.nc + c) * N * P + 8 * e);
-    }
-    // per-token scalars (one thread a token) and the same-token and segsum tables
-    float s_cs = 0.f, s_rev = 0.f, s_dt = 0.f, s_tr = 0.f, s_dt1 = 0.f, s_tr1 = 0.f;
-    const bool tok_live = tid < cl;
-    if (tok_live) {
-        s_cs = p.da_cs[tb0 + tid];
-        if (MAIN) {
-            s_rev = p.da_cs_rev[tb0 + tid];
-            s_dt = p.dt[tb0 + tid];
-            s_tr = bf(p.trap[tb0 + tid]);
-            if (c0 + tid + 1 < p.S) {
-                s_dt1 = p.dt[tb0 + tid + 1];
-                s_tr1 = bf(p.trap[tb0 + tid + 1]);
-            }
-        }
-    }
-    float qk = 0.f, seg[SX];
-    if (MAIN) {
-        if (tid < cl * RR) qk = bf(p.qk_dot[tb0 * RR + tid]);
-#pragma unroll
-        for (int x = 0; x < SX; ++x) {
-            const int e = tid + NT * x;
-            const int t = dC.q(e), s2 = e - t * C;
-            seg[x] = (e < C * C && s2 < t && t < cl) ? p.segsum[((long)bh * p.nc + c) * C * C + e] : 0.f;
-        }
-    }
-
-    // ---- rotate and store
-#pragma unroll
-    for (int x = 0; x < IX; ++x) {
-        const int e = tid + NT * x;
-        if (e < nrot) {
-            const int i = dM4.q(e), n4 = 4 * (e - i * (M / 4));
-            const int t = dC.r(i);
+        if (e < rows * (M / 4)) {
+            const int i = dv.dM4.q(e), n4 = 4 * (e - i * (M / 4));
+            const bool live = i - dv.dC.q(i) * C < cl;
             float qa[4], qe[4], ka[4], ke[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 float sn = 0.f, cs = 1.f;
                 qa[v] = qe[v] = ka[v] = ke[v] = 0.f;
-                if (t < cl) {
-                    const unsigned wa = qw[x][0][v >> 1], we = qw[x][1][v >> 1];
-                    qa[v] = ((v & 1) ? hi16(wa) : lo16(wa)) + qb[x][0][v];
-                    qe[v] = ((v & 1) ? hi16(we) : lo16(we)) + qb[x][1][v];
+                if (live) {
+                    const unsigned wa = f.qw[x][0][v >> 1], we = f.qw[x][1][v >> 1];
+                    qa[v] = ((v & 1) ? hi16(wa) : lo16(wa)) + res.qb[x][0][v];
+                    qe[v] = ((v & 1) ? hi16(we) : lo16(we)) + res.qb[x][1][v];
                     if (MAIN) {
-                        const unsigned ua = kw[x][0][v >> 1], ue = kw[x][1][v >> 1];
-                        ka[v] = ((v & 1) ? hi16(ua) : lo16(ua)) + kb[x][0][v];
-                        ke[v] = ((v & 1) ? hi16(ue) : lo16(ue)) + kb[x][1][v];
+                        const unsigned ua = f.kw[x][0][v >> 1], ue = f.kw[x][1][v >> 1];
+                        ka[v] = ((v & 1) ? hi16(ua) : lo16(ua)) + res.kb[x][0][v];
+                        ke[v] = ((v & 1) ? hi16(ue) : lo16(ue)) + res.kb[x][1][v];
                     }
-                    if (n4 + v < W) sin_cos(ang[x][v], sn, cs);
+                    if (n4 + v < W) sin_cos(f.ang[x][v], sn, cs);
                 }
                 keep.cs[x][v] = cs;
                 keep.sn[x][v] = sn;
@@ -387,18 +418,18 @@ __device__ __forceinline__ void load_chunk(const Params2& p, float* sm, int b, i
                 *reinterpret_cast<f32x4*>(KH + i * LD + M + n4) = f32x4{ke[0], ke[1], ke[2], ke[3]};
             }
         }
-        if (e < nval) {
-            const int i = dP8.q(e), p8 = 8 * (e - i * (P / 8));
-            const bool live = dC.r(i) < cl;
+        if (e < rows * (P / 8)) {
+            const int i = dv.dP8.q(e), p8 = 8 * (e - i * (P / 8));
+            const bool live = i - dv.dC.q(i) * C < cl;
             float d8[8], s8[8];
 #pragma unroll
             for (int v = 0; v < 8; ++v) {
-                const unsigned wd = dw[x][v >> 1];
-                const float dv = (v & 1) ? hi16(wd) : lo16(wd);
-                d8[v] = live ? (p.reduce_o ? dv * mo[x][v >> 2][v & 3] : dv) : 0.f;
+                const unsigned wd = f.dw[x][v >> 1];
+                const float dv8 = (v & 1) ? hi16(wd) : lo16(wd);
+                d8[v] = live ? (p.reduce_o ? dv8 * res.mo[x][v >> 2][v & 3] : dv8) : 0.f;
                 if (MAIN) {
-                    const unsigned wv = vw[x][v >> 1];
-                    s8[v] = live ? ((v & 1) ? hi16(wv) : lo16(wv)) * mv[x][v >> 2][v & 3] : 0.f;
+                    const unsigned wv = f.vw[x][v >> 1];
+                    s8[v] = live ? ((v & 1) ? hi16(wv) : lo16(wv)) * res.mv[x][v >> 2][v & 3] : 0.f;
                 }
             }
             *reinterpret_cast<f32x4*>(DPO + i * LD + p8) = f32x4{d8[0], d8[1], d8[2], d8[3]};
@@ -406,25 +437,26 @@ __device__ __forceinline__ void load_chunk(const Params2& p, float* sm, int b, i
             if (MAIN) {
                 *reinterpret_cast<f32x4*>(PS + i * LD + p8) = f32x4{s8[0], s8[1], s8[2], s8[3]};
                 *reinterpret_cast<f32x4*>(PS + i * LD + p8 + 4) = f32x4{s8[4], s8[5], s8[6], s8[7]};
-                keep.v[x] = live ? vw[x] : u32x4{0u, 0u, 0u, 0u};
+                keep.v[x] = live ? f.vw[x] : u32x4{0u, 0u, 0u, 0u};
             }
         }
-        if (MAIN && e < nst) {
-            const int n = dP8.q(e), pc = 8 * (e - n * (P / 8));
+        if (MAIN && e < N * (P / 8)) {
+            const int n = dv.dP8.q(e), pc = 8 * (e - n * (P / 8));
             float* dst = sm + L2::SC + n * LD + pc;
-            *reinterpret_cast<f32x4*>(dst) = f32x4{lo16(sw[x][0]), hi16(sw[x][0]), lo16(sw[x][1]), hi16(sw[x][1])};
-            *reinterpret_cast<f32x4*>(dst + 4) =
-                f32x4{lo16(sw[x][2]), hi16(sw[x][2]), lo16(sw[x][3]), hi16(sw[x][3])};
+            const u32x4 w = f.sw[x];
+            *reinterpret_cast<f32x4*>(dst) = f32x4{lo16(w[0]), hi16(w[0]), lo16(w[1]), hi16(w[1])};
+            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{lo16(w[2]), hi16(w[2]), lo16(w[3]), hi16(w[3])};
         }
     }
     if (tid < C) {
-        const float ecs = tok_live ? expf(s_cs) : 0.f;
+        const bool tok_live = tid < cl;
+        const float ecs = tok_live ? expf(f.s_cs) : 0.f;
         float gam = 0.f, fac = 0.f, er = 0.f;
         if (MAIN && tok_live) {
-            gam = s_dt * (1.0f / (1.0f + expf(-s_tr)));
-            const float beta = c0 + tid + 1 < p.S ? s_dt1 * (1.0f - 1.0f / (1.0f + expf(-s_tr1))) : 0.f;
+            gam = f.s_dt * (1.0f / (1.0f + expf(-f.s_tr)));
+            const float beta = c0 + tid + 1 < p.S ? f.s_dt1 * (1.0f - 1.0f / (1.0f + expf(-f.s_tr1))) : 0.f;
             fac = gam + beta;
-            er = expf(s_rev);
+            er = expf(f.s_rev);
         }
         for (int r = 0; r < R; ++r) {
             const int i = r * C + tid;
@@ -437,14 +469,14 @@ __device__ __forceinline__ void load_chunk(const Params2& p, float* sm, int b, i
         }
     }
     if (MAIN) {
-        if (tid < cl * RR) sm[L2::QKC + tid] = qk;
+        if (tid < cl * RR) sm[L2::QKC + tid] = f.qk;
         // exp(segsum) of the chunk's strictly causal token pairs, in the output tile
         // (free until the dQ^ products)
 #pragma unroll
-        for (int x = 0; x < SX; ++x) {
+        for (int x = 0; x < Items<NT>::SX; ++x) {
             const int e = tid + NT * x;
-            const int t = dC.q(e), s2 = e - t * C;
-            if (e < C * C) sm[L2::OUT + t * LD + s2] = (s2 < t && t < cl) ? expf(seg[x]) : 0.f;
+            const int t = dv.dC.q(e), s2 = e - t * C;
+            if (e < C * C) sm[L2::OUT + t * LD + s2] = (s2 < t && t < cl) ? expf(f.seg[x]) : 0.f;
         }
     }
 }
@@ -474,13 +506,18 @@ __global__ __launch_bounds__(NTHR, 2) void k_agg2(Params2 p) {
     float* ECS = sm + L2::A_ECS;
     for (int e = threadIdx.x; e < N * P; e += NTHR) U[(e / P) * LD + e % P] = 0.f;
     float dprod = 1.f;
-    const DivS dC(C), dM4(N / 8), dP8(P / 8);
+    const ItemDiv dv(C, N, P);
     Keep<NTHR> keep;
+    Res<NTHR> res;
+    Fetch<NTHR> f;
+    load_resident<false, NTHR>(p, h, dv, res);
+    if (c_end > c_begin) fetch_chunk<false, NTHR>(p, b, h, g, bh, c_end - 1, dv, f);
     for (int c = c_end - 1; c >= c_begin; --c) {
         const int cl = min(C, p.S - c * C);
-        __syncthreads();
-        load_chunk<false, NTHR>(p, sm, b, h, g, bh, c, cl, dC, dM4, dP8, keep);
-        __syncthreads();
+        bar();
+        stage_chunk<false, NTHR>(p, sm, c, dv, f, res, keep);
+        if (c > c_begin) fetch_chunk<false, NTHR>(p, b, h, g, bh, c - 1, dv, f);   // in flight during this chunk
+        bar();
         const float dA = ECS[cl - 1];   // exp(da_cs) at the chunk's last token
         // U[n][p] = sum_i Q^[i][n] exp(da_cs[t_i]) dPhiO[i][p] + dA U[n][p]; the thread that
         // owns (n, p) in the product is the only one reading and writing U[n][p]
@@ -489,7 +526,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_agg2(Params2 p) {
                                          [&](int n, int pc, float v) { U[n * LD + pc] = v + dA * U[n * LD + pc]; });
         dprod *= dA;
     }
-    __syncthreads();
+    bar();
     float* out = p.agg + ((long)bh * p.nsub + seg) * N * P;
     for (int e = threadIdx.x; e < N * P; e += NTHR) out[e] = U[(e / P) * LD + e % P];
     if (threadIdx.x == 0) p.decay[(long)bh * p.nsub + seg] = dprod;
@@ -629,8 +666,14 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         for (int e = tid; e < N * P; e += NTHR2) DS[(e / P) * LD + e % P] = E ? E[e] : 0.f;
     }
     const long tokS = (long)bh * p.S;
-    const DivS dC(C), dRR(RR), dP(P), dP4(P / 4), dM4(N / 8), dP8(P / 8);
+    const ItemDiv dv(C, N, P);
+    const DivS &dC = dv.dC, &dM4 = dv.dM4, &dP8 = dv.dP8;
+    const DivS dRR(RR), dP(P), dP4(P / 4);
     Keep<NTHR2> keep;
+    Res<NTHR2> res;
+    Fetch<NTHR2> f;
+    load_resident<true, NTHR2>(p, h, dv, res);
+    if (c_end > c_begin) fetch_chunk<true, NTHR2>(p, b, h, g, bh, c_end - 1, dv, f);
     // DDA of the previous chunk: its last token takes exp(da_cs[last]) times the sum of
     // the per-wave partials in RED (written after the chunk's dS product)
     int pend_c0 = 0, pend_cl = 0;
@@ -652,10 +695,11 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         const int c0 = c * C;
         const int cl = min(C, p.S - c0);
         const int tid = tid_x();
-        __syncthreads();
+        bar();
         flush_dda();
-        load_chunk<true, NTHR2>(p, sm, b, h, g, bh, c, cl, dC, dM4, dP8, keep);
-        __syncthreads();
+        stage_chunk<true, NTHR2>(p, sm, c, dv, f, res, keep);
+        if (c > c_begin) fetch_chunk<true, NTHR2>(p, b, h, g, bh, c - 1, dv, f);   // in flight during this chunk
+        bar();
 
         // ---- causal block A = E (Q^ K~^T) and dP = dPhiO Psi^T; dP's same-token entries
         // are the dots dPhiO[t,r] . Psi[t,r2] (DGAMMA, the D-skip sum, the same-token parts).
@@ -674,7 +718,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
             const int ri = dC.q(i), ti = i - ri * C, rj = dC.q(j), tj = j - rj * C;
             if (ti == tj && ti < cl) DQK[ti * RR + ri * R + rj] = v;
         });
-        __syncthreads();
+        bar();
         if (tid < cl) {
             const int t = tid;
             float dg = 0.f;
@@ -697,7 +741,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                 }
             p.dssda[(((long)bh * p.nc + c) * C + t) * C + s] = live ? acc : 0.f;
         }
-        __syncthreads();
+        bar();
         // same-token factors of the diagonal: gamma_t times the dots
         for (int e = tid; e < cl * RR; e += NTHR2) DQK[e] *= GAM[dRR.q(e)];
 
@@ -711,12 +755,12 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                 return QH[i * LD + n] * o;
             },
             RS0);
-        __syncthreads();
+        bar();
         token_out(cl, R, C, RS0, [&](int t, float v) { p.dda_cs[tokS + c0 + t] = v; });
         // W K~: B(j, n) = k^[j][n] scaled per j by the factor (folded into A)
         gemm64<NTHR2, true, false, true>(rows, N, rows, WM, KH, FAC,
                                          [&](int i, int n, float v) { OUT[i * LD + n] += v; });
-        __syncthreads();
+        bar();
         // angle gradient, q part: d(a')/dθ = -e', d(e')/dθ = a' for the rotated pair (a', e')
         float dth[4];   // items (t, n): t < 64, n < 32 (W <= 32)
 #pragma unroll
@@ -733,7 +777,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         }
         // the same-token part, then back to the input frame: DQ (OUT is only read)
         finish_rot<F32OUT, NTHR2, false>(p, p.dq, OUT, KH, DQK, FAC, keep, b, h, c0, cl, dC, dM4);
-        __syncthreads();
+        bar();
 
         // ---- dK~ = exp(da_cs_rev) Psi dS^T + W^T Q^; DDA_CS_REV from the first product's row
         // sums (k^ . its rows), DFACTOR from those of the whole dK~
@@ -745,7 +789,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                 return KH[j * LD + n] * o;
             },
             RS1);
-        __syncthreads();
+        bar();
         token_out(cl, R, C, RS1, [&](int t, float v) { p.dda_cs_rev[tokS + c0 + t] = v * FAC[t]; });
         gemm64<NTHR2, false, false, false, true>(
             rows, N, rows, WM, QH, nullptr,
@@ -755,7 +799,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                 return KH[j * LD + n] * o;
             },
             RS0);
-        __syncthreads();
+        bar();
         token_out(cl, R, C, RS0, [&](int t, float v) { p.dfactor[tokS + c0 + t] = v; });
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -781,14 +825,14 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
             *reinterpret_cast<f32x4*>(WM + t * LD + p8) = f32x4{lo16(w[0]), hi16(w[0]), lo16(w[1]), hi16(w[1])};
             *reinterpret_cast<f32x4*>(WM + t * LD + p8 + 4) = f32x4{lo16(w[2]), hi16(w[2]), lo16(w[3]), hi16(w[3])};
         }
-        __syncthreads();
+        bar();
 
         // ---- dPsi = kappa dS + A^T dPhiO (the latter with the same-token and d terms)
         gemm64<NTHR2, true, false, false>(rows, P, N, KH, DS, nullptr,
                                           [&](int j, int pc, float v) { OUT[j * LD + pc] = v * FAC[j] * EREV[j]; });
         gemm64<NTHR2, false, false, false>(rows, P, rows, AM, DPO, nullptr,
                                            [&](int j, int pc, float v) { OUT[j * LD + pc] += v; });
-        __syncthreads();
+        bar();
         for (int e = tid; e < cl * (P / 4); e += NTHR2) {
             const int t = dP4.q(e), p4 = 4 * (e - t * (P / 4));
             float s[4] = {0.f, 0.f, 0.f, 0.f};
@@ -829,7 +873,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         pend_cl = cl;
         pend_dA = dA;
     }
-    __syncthreads();
+    bar();
     flush_dda();
 
     // ---- per-segment partial sums of DMIMO_V and DD
