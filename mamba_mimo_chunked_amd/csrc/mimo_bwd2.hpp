@@ -46,15 +46,6 @@ struct Params2 {
 
 __device__ __forceinline__ float bf(unsigned short x) { return __uint_as_float(static_cast<unsigned>(x) << 16); }
 
-// The thread index as a value the compiler cannot move out of a loop: index and
-// address arithmetic is then redone per chunk instead of being held in registers
-// across the whole chunk loop (which spills). No instruction is emitted.
-__device__ __forceinline__ int tid_x() {
-    int x = threadIdx.x;
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

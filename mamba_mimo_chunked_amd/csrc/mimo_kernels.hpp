@@ -104,6 +104,15 @@ __device__ __forceinline__ void sin_cos(float x, float& s, float& c) {
 // moving memory accesses across it.
 __device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// The thread index as a value the compiler cannot move out of a loop: index and
+// address arithmetic is then redone per chunk instead of being held in registers
+// across the whole chunk loop (which spills). No instruction is emitted.
+__device__ __forceinline__ int tid_x() {
+    int x = threadIdx.x;
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_ld(const void* p) { return *reinterpret_cast<const T*>(p); }
 template <typename T>
