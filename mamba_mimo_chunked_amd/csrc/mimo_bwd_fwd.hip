@@ -315,6 +315,7 @@ struct Prob32 {
     int64_t B, S, H, G, R, N, P;
     int C, W;
     bool reduce_o, has_z, has_d, fwd, f16;
+    bool uv;   // unit projections and controls from adt (the SISO forward): the *_uv kernels
 };
 
 struct Plan32 {
@@ -333,6 +334,8 @@ const f32::F32Set* f32_set() {
                 for (int i = 0; i < 9; ++i) {
                     s.agg[d][9 * m + i] = parts[m]->agg[d][i];
                     s.main[d][9 * m + i] = parts[m]->main[d][i];
+                    s.agg_uv[d][9 * m + i] = parts[m]->agg_uv[d][i];
+                    s.main_uv[d][9 * m + i] = parts[m]->main_uv[d][i];
                 }
         return s;
     }();
@@ -358,8 +361,8 @@ mimo_status make_plan32(const Prob32& q, Plan32* pl) {
     pl->NT = tile_size((int)q.N);
     pl->PT = tile_size((int)q.P);
     pl->ti = 9 * tidx3(pl->MT) + 3 * tidx3(pl->NT) + tidx3(pl->PT);
-    pl->lds_main = f32::lds32(pl->MT, pl->NT, pl->PT, true).total;
-    pl->lds_agg = f32::lds32(pl->MT, pl->NT, pl->PT, false).total;
+    pl->lds_main = f32::lds32(pl->MT, pl->NT, pl->PT, true, q.uv).total;
+    pl->lds_agg = f32::lds32(pl->MT, pl->NT, pl->PT, false, q.uv).total;
     if (pl->lds_main > 160 * 1024)
         return fail(MIMO_ERR_UNSUPPORTED,
                     "the fp32-intermediate kernels need %d bytes of LDS for R*C=%d, N=%lld, P=%lld (limit 163840)",
@@ -402,7 +405,8 @@ mimo_status run32(const Prob32& q, Params& p, void* workspace, size_t workspace_
             if (events[i] == nullptr) return fail(MIMO_ERR_VALUE, "timing event %d is NULL", i);
     if ((s = check_device()) != MIMO_OK) return s;
     const f32::F32Set* set = f32_set();
-    const kfn kmain = set->main[q.f16][pl.ti], kagg = set->agg[q.f16][pl.ti];
+    const kfn kmain = (q.uv ? set->main_uv : set->main)[q.f16][pl.ti];
+    const kfn kagg = (q.uv ? set->agg_uv : set->agg)[q.f16][pl.ti];
     if (kmain == nullptr || kagg == nullptr) return fail(MIMO_ERR_UNSUPPORTED, "no fp32 kernel for this tile shape");
     p.B = (int)q.B; p.S = (int)q.S; p.H = (int)q.H; p.G = (int)q.G; p.R = (int)q.R; p.N = (int)q.N; p.P = (int)q.P;
     p.C = q.C; p.W = q.W; p.nc = pl.nc; p.L = pl.L; p.nseg = pl.nseg; p.F = pl.F; p.nsub = pl.nsub;
@@ -460,7 +464,7 @@ mimo_status prob_from_mimo(const mimo_bwd_fwd_args* a, bool fwd, Prob32* q) {
     if ((a->z == nullptr) != (a->mimo_z == nullptr))
         return fail(MIMO_ERR_VALUE, "z and mimo_z must either both be present or both be NULL");
     *q = Prob32{a->B, a->S, a->H, a->G, a->R, a->N, a->P, a->chunk_size, (int)(a->N / rd),
-                a->mimo_o != nullptr, a->z != nullptr, a->d != nullptr, fwd, false};
+                a->mimo_o != nullptr, a->z != nullptr, a->d != nullptr, fwd, false, false};
     return MIMO_OK;
 }
 
@@ -519,7 +523,7 @@ mimo_status prob_from_siso(const mimo_siso_fwd_args* a, Prob32* q) {
     if (a->dtype != MIMO_DTYPE_BF16 && a->dtype != MIMO_DTYPE_FP16)
         return fail(MIMO_ERR_TYPE, "q, k, v and z must be bf16 or fp16");
     *q = Prob32{a->B, a->S, a->H, a->Hq, 1, a->K, a->V, a->chunk_size, (int)a->A,
-                false, a->z != nullptr, a->d != nullptr, true, a->dtype == MIMO_DTYPE_FP16};
+                false, a->z != nullptr, a->d != nullptr, true, a->dtype == MIMO_DTYPE_FP16, true};
     return MIMO_OK;
 }
 

@@ -38,7 +38,8 @@ struct Tile32 {
     static constexpr int CX = MT < 64 ? MT : 64;          // chunk length bound (C <= MT, C <= 64)
     static constexpr int LQ = NT + 4;                     // row pitch (floats) of sQ, sK
     static constexpr int LA = MT + 4;                     // row pitch of the causal block
-    static constexpr int LP = PT + 4;                     // row pitch of sPsi
+    static constexpr int LP = PT + 4;                     // row pitch of sPsi (fp32) and of y's partial sums
+    static constexpr int LP16 = PT + 8;                   // row pitch of a 16-bit sPsi (unit projections)
     static constexpr int AT = (MTT * MTT + NW - 1) / NW;  // causal-block tiles per wave
 };
 
@@ -46,7 +47,10 @@ struct Tile32 {
 struct Lds32 {
     int q, k, psi, se, qk, sc, total;
 };
-__host__ __device__ constexpr Lds32 lds32(int MT, int NT, int PT, bool main) {
+// uv: unit value projections and controls derived from adt (the SISO forward): Psi is
+// v itself, kept in its 16-bit input type, and exp(segsum) comes from the cumulative
+// log decays instead of a table.
+__host__ __device__ constexpr Lds32 lds32(int MT, int NT, int PT, bool main, bool uv = false) {
     const int CX = MT < 64 ? MT : 64;
     // q^, then the causal block, then y's partial sums: the widest of the three rows
     const int wq = NT > MT ? (NT > PT ? NT : PT) : (MT > PT ? MT : PT);
@@ -58,9 +62,9 @@ __host__ __device__ constexpr Lds32 lds32(int MT, int NT, int PT, bool main) {
     l.k = off;
     off += 4 * MT * (NT + 4);
     l.psi = off;
-    off += 4 * MT * (PT + 4);
+    off += uv ? 2 * MT * (PT + 8) : 4 * MT * (PT + 4);
     l.se = off;
-    if (main) off += 4 * CX * (CX + 1);
+    if (main && !uv) off += 4 * CX * (CX + 1);
     l.qk = off;
     if (main) off += 4 * MT * 8;
     l.sc = off;
@@ -110,23 +114,37 @@ __device__ __forceinline__ f32x4 mfma32(float a, float b, f32x4 c) {
 // its decay product). MAIN = true: the chunk pass (states, qk_dot, y and the
 // backward's gating outputs, or the layer output when p.fwd).
 // Two workgroups per compute unit where the LDS layout allows it.
-template <int MT, int NT, int PT, bool MAIN>
+template <int MT, int NT, int PT, bool MAIN, bool UV>
 constexpr int wg_per_cu32() {
-    return lds32(MT, NT, PT, MAIN).total <= 80 * 1024 ? 2 : 1;
+    return lds32(MT, NT, PT, MAIN, UV).total <= 80 * 1024 ? 2 : 1;
 }
 
-template <int MT, int NT, int PT, bool MAIN, bool F16>
-__global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN>())) void k_chunk32(Params p) {
+// A 16-bit value (bf16, or fp16 when F16) as fp32.
+template <bool F16>
+__device__ __forceinline__ float cvt16(unsigned short x) {
+    if constexpr (F16) return static_cast<float>(__builtin_bit_cast(_Float16, x));
+    return __uint_as_float(static_cast<unsigned>(x) << 16);
+}
+
+template <int MT, int NT, int PT, bool MAIN, bool F16, bool UV = false>
+__global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_chunk32(Params p) {
     using T = Tile32<MT, NT, PT>;
     constexpr int NW = T::NW, NTHR = T::NTHR, LQ = T::LQ, LA = T::LA, LP = T::LP, CX = T::CX;
     constexpr int MTT = T::MTT, NTT = T::NTT, PTT = T::PTT, PW = T::PW;
     extern __shared__ __align__(16) unsigned char smem[];
-    constexpr Lds32 L = lds32(MT, NT, PT, MAIN);
+    constexpr Lds32 L = lds32(MT, NT, PT, MAIN, UV);
     float* sQ = reinterpret_cast<float*>(smem + L.q);   // q^ [MT][LQ], then the causal block [MT][LA],
     float* sA = sQ;                                       // then y's partial sums [MT][LP]
     float* sY = sQ;
     float* sK = reinterpret_cast<float*>(smem + L.k);     // k0, then K~ [MT][LQ]
-    float* sPsi = reinterpret_cast<float*>(smem + L.psi); // Psi [MT][LP]
+    float* sPsi = reinterpret_cast<float*>(smem + L.psi); // Psi [MT][LP], or 16-bit [MT][LP16] when UV
+    unsigned short* sPsi16 = reinterpret_cast<unsigned short*>(smem + L.psi);
+    auto psi_at = [&](int row, int col) -> float {
+        if constexpr (UV)
+            return cvt16<F16>(sPsi16[row * T::LP16 + col]);
+        else
+            return sPsi[row * LP + col];
+    };
     float* sE = reinterpret_cast<float*>(smem + L.se);    // exp(segsum) [CX][CX+1]
     float* sQK = reinterpret_cast<float*>(smem + L.qk);   // same-token dots [C][R][R]
     float* sc = reinterpret_cast<float*>(smem + L.sc);    // gamma, factor, ecs, erev, cs [CX] each; dl
@@ -199,6 +217,11 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN>())) void k_chun
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C;
         const int cl = min(C, p.S - c0);
+        // The unit-projection chunk pass runs two workgroups per CU (at most 256 VGPRs):
+        // there the thread index is made opaque per chunk so that index arithmetic is
+        // redone per chunk instead of being held in registers across the loop.
+        const int tid = (UV && MAIN) ? tid_x() : static_cast<int>(threadIdx.x), lane = tid & 63, l16 = lane & 15,
+                  q4 = lane >> 4;
 
         // ---- states[c] = S entering chunk c, in the output type
         if constexpr (MAIN) {
@@ -301,6 +324,13 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN>())) void k_chun
             const int e = tid + k2 * NTHR;
             const int i = e / P4, pc = 4 * (e % P4);
             const int r = i / Cp, t = i % Cp;
+            if constexpr (UV) {
+                u32x2 w = {0u, 0u};
+                if (r < R && t < cl && pc < P)
+                    w = *reinterpret_cast<const u32x2*>(p.v + ((long)(b * p.S + c0 + t) * p.H + h) * P + pc);
+                *reinterpret_cast<u32x2*>(sPsi16 + i * T::LP16 + pc) = w;
+                continue;
+            }
             float x[4] = {0.f, 0.f, 0.f, 0.f};
             if (r < R && t < cl && pc < P) {
                 ld16x4<F16>(p.v, ((long)(b * p.S + c0 + t) * p.H + h) * P + pc, x);
@@ -333,7 +363,7 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN>())) void k_chun
                 sQK[e] = s;
                 if (!p.fwd) p.qk_dot[((long)bh * p.S + c0 + t) * RR + r * R + r2] = st16<F16>(s);
             }
-            for (int e = tid; e < cl * cl; e += NTHR) {
+            for (int e = tid; e < (UV ? 0 : cl * cl); e += NTHR) {
                 const int t = e / cl, s2 = e % cl;
                 if (s2 < t) {
                     float sg;
@@ -414,7 +444,10 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN>())) void k_chun
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int ti = 16 * (it % CT) + 4 * q4 + v;
-                        a4[v] = (ti < cl && tj < ti) ? a4[v] * sE[ti * (CX + 1) + tj] : 0.f;
+                        if constexpr (UV)
+                            a4[v] = (ti < cl && tj < ti) ? a4[v] * expf(sCs[ti] - sCs[tj]) : 0.f;
+                        else
+                            a4[v] = (ti < cl && tj < ti) ? a4[v] * sE[ti * (CX + 1) + tj] : 0.f;
                     }
                 }
                 at[w] = a4;
@@ -444,7 +477,7 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN>())) void k_chun
                         const f32x4 aa = *reinterpret_cast<const f32x4*>(sA + (16 * it + l16) * LA + 16 * jt + 4 * q4);
 #pragma unroll
                         for (int v = 0; v < 4; ++v)
-                            a4 = mfma32(aa[v], sPsi[(16 * jt + 4 * q4 + v) * LP + 16 * pt + l16], a4);
+                            a4 = mfma32(aa[v], psi_at(16 * jt + 4 * q4 + v, 16 * pt + l16), a4);
                     }
                     acc[j][it] = a4;
                 }
@@ -468,7 +501,7 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN>())) void k_chun
                         for (int v = 0; v < 4; ++v) {
                             const int row = 16 * it + 4 * q4 + v;
                             const float er = (tb + v < CX) ? sRev[tb + v] : 0.f;
-                            a4 = mfma32(sK[row * LQ + 16 * nt + l16] * er, sPsi[row * LP + 16 * pt + l16], a4);
+                            a4 = mfma32(sK[row * LQ + 16 * nt + l16] * er, psi_at(row, 16 * pt + l16), a4);
                         }
                     }
                     S[j][nt] = a4;
@@ -523,9 +556,9 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN>())) void k_chun
                             if (r >= R) break;
                             float dg = 0.f;
                             for (int r2 = 0; r2 < R; ++r2)
-                                dg = __fmaf_rn(sQK[t * RR + r * R + r2], sPsi[(r2 * Cp + t) * LP + pc], dg);
+                                dg = __fmaf_rn(sQK[t * RR + r * R + r2], psi_at(r2 * Cp + t, pc), dg);
                             const int row = r * Cp + t;
-                            const float y = sY[row * LP + pc] + gam * dg + dval * sPsi[row * LP + pc];
+                            const float y = sY[row * LP + pc] + gam * dg + dval * psi_at(row, pc);
                             float pz = 0.f, sg = 0.f, silu = 1.f;
                             if (p.has_z) {
                                 pz = zr * cz[j][r];
@@ -603,34 +636,42 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN>())) void k_chun
 
 // Kernel table: [bf16 = 0 / fp16 = 1][9 * idx(MT) + 3 * idx(NT) + idx(PT)] with
 // idx(32, 64, 128) = 0, 1, 2; nullptr where the tile's LDS does not fit. Each MT's
-// instances are compiled in a translation unit of their own (tiles_f32_mt*.hip).
+// instances are compiled in a translation unit of their own (tiles_f32_mt*.hip). The
+// *_uv tables hold the unit-projection instances (the SISO forward: MT of 32 and 64).
 struct F32Set {
-    kfn agg[2][27], main[2][27];
+    kfn agg[2][27], main[2][27], agg_uv[2][27], main_uv[2][27];
 };
 struct F32Part {
-    kfn agg[2][9], main[2][9];
+    kfn agg[2][9], main[2][9], agg_uv[2][9], main_uv[2][9];
 };
 const F32Part* f32_part_mt32();
 const F32Part* f32_part_mt64();
 const F32Part* f32_part_mt128();
 
-template <int MT, int NT, int PT, bool MAIN, bool F16>
+template <int MT, int NT, int PT, bool MAIN, bool F16, bool UV>
 constexpr kfn pick32() {
-    if constexpr (lds32(MT, NT, PT, MAIN).total <= 160 * 1024)
-        return k_chunk32<MT, NT, PT, MAIN, F16>;
+    if constexpr (lds32(MT, NT, PT, MAIN, UV).total <= 160 * 1024)
+        return k_chunk32<MT, NT, PT, MAIN, F16, UV>;
     else
         return nullptr;
 }
 
-#define MIMO_F32_NP(MT, MAIN, F16)                                                                  \
-    {pick32<MT, 32, 32, MAIN, F16>(), pick32<MT, 32, 64, MAIN, F16>(), pick32<MT, 32, 128, MAIN, F16>(), \
-     pick32<MT, 64, 32, MAIN, F16>(), pick32<MT, 64, 64, MAIN, F16>(), pick32<MT, 64, 128, MAIN, F16>(), \
-     pick32<MT, 128, 32, MAIN, F16>(), pick32<MT, 128, 64, MAIN, F16>(), pick32<MT, 128, 128, MAIN, F16>()}
-#define MIMO_F32_PART(MT)                                                                           \
-    const F32Part* f32_part_mt##MT() {                                                              \
-        static const F32Part part = {{MIMO_F32_NP(MT, false, false), MIMO_F32_NP(MT, false, true)}, \
-                                     {MIMO_F32_NP(MT, true, false), MIMO_F32_NP(MT, true, true)}};  \
-        return &part;                                                                               \
+#define MIMO_F32_NP(MT, MAIN, F16, UV)                                                                           \
+    {pick32<MT, 32, 32, MAIN, F16, UV>(),  pick32<MT, 32, 64, MAIN, F16, UV>(),  pick32<MT, 32, 128, MAIN, F16, UV>(),  \
+     pick32<MT, 64, 32, MAIN, F16, UV>(),  pick32<MT, 64, 64, MAIN, F16, UV>(),  pick32<MT, 64, 128, MAIN, F16, UV>(),  \
+     pick32<MT, 128, 32, MAIN, F16, UV>(), pick32<MT, 128, 64, MAIN, F16, UV>(), pick32<MT, 128, 128, MAIN, F16, UV>()}
+#define MIMO_F32_TABLES(MT, UV)                                                                         \
+    {MIMO_F32_NP(MT, false, false, UV), MIMO_F32_NP(MT, false, true, UV)},                             \
+        {MIMO_F32_NP(MT, true, false, UV), MIMO_F32_NP(MT, true, true, UV)}
+#define MIMO_F32_PART(MT)                                                                               \
+    const F32Part* f32_part_mt##MT() {                                                                  \
+        static const F32Part part = {MIMO_F32_TABLES(MT, false), {}, {}};                                \
+        return &part;                                                                                   \
+    }
+#define MIMO_F32_PART_UV(MT)                                                                            \
+    const F32Part* f32_part_mt##MT() {                                                                  \
+        static const F32Part part = {MIMO_F32_TABLES(MT, false), MIMO_F32_TABLES(MT, true)};             \
+        return &part;                                                                                   \
     }
 
 }  // namespace f32

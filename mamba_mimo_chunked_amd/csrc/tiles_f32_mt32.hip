@@ -1,9 +1,10 @@
 // Instances of the fp32-intermediate chunk kernels with MT = 32 chunk-tile rows: every
-// (NT, PT) tile whose LDS layout fits a compute unit, for bf16 and fp16 inputs.
+// (NT, PT) tile whose LDS layout fits a compute unit, for bf16 and fp16 inputs, and the
+// unit-projection (SISO) instances.
 #include "mimo_f32.hpp"
 
 namespace mimo {
 namespace f32 {
-MIMO_F32_PART(32)
+MIMO_F32_PART_UV(32)
 }  // namespace f32
 }  // namespace mimo
