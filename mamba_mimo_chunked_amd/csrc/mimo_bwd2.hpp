@@ -27,8 +27,9 @@
 namespace mimo {
 namespace b2 {
 
-constexpr int NTHR = 256;      // the aggregate (two workgroups per CU)
+constexpr int NTHR = 512;      // the aggregate (two workgroups of eight waves per CU)
 constexpr int NTHR2 = 512;     // the chunk pass (one workgroup per CU: eight waves hide more latency)
+constexpr int NTHR1 = 256;     // the reverse scan and the final sums
 constexpr int LD = 68;              // row pitch (floats) of every tile (16-byte rows, 4 mod 64)
 constexpr int TILE = 64 * LD;       // floats per tile
 
@@ -526,10 +527,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_agg2(Params2 p) {
 // dS at the start of every sub-segment, from the end of the sequence: E_j = U_j +
 // D_j E_{j+1}; written in place where a segment begins (j % F == 0), which is the
 // dS entering segment j / F from the right.
-__global__ __launch_bounds__(256) void k_scan_rev(Params2 p) {
+__global__ __launch_bounds__(NTHR1) void k_scan_rev(Params2 p) {
     const int bh = blockIdx.y;
     const int NP = p.N * p.P;
-    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int e = blockIdx.x * NTHR1 + threadIdx.x;
     if (e >= NP) return;
     float* base = p.agg + (long)bh * p.nsub * NP + e;
     const float* dec = p.decay + (long)bh * p.nsub;
@@ -875,9 +876,9 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
 }
 
 // DMIMO_V [B,H,R,P] and DD [B,H]: the per-segment partials summed in segment order.
-__global__ __launch_bounds__(256) void k_finish2(Params2 p) {
+__global__ __launch_bounds__(NTHR1) void k_finish2(Params2 p) {
     const long RP = (long)p.R * p.P;
-    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    const long e = (long)blockIdx.x * NTHR1 + threadIdx.x;
     const long tot = (long)p.B * p.H * RP;
     if (e < tot) {
         const long bh = e / RP, rp = e - bh * RP;

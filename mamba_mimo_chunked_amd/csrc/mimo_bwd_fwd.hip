@@ -641,7 +641,7 @@ mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events
             return fail(MIMO_ERR_HIP, "hipEventRecord failed");
         return MIMO_OK;
     };
-    auto launch2 = [&](const void* f, dim3 grid, int lds, int threads = b2::NTHR) -> mimo_status {
+    auto launch2 = [&](const void* f, dim3 grid, int lds, int threads) -> mimo_status {
         void* args[] = {&p};
         const hipError_t e = hipLaunchKernel(f, grid, dim3(threads), args, (size_t)lds, st);
         if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -663,11 +663,11 @@ mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events
     if (pl.nseg > 1) {
         const void* kagg = reinterpret_cast<const void*>(&b2::k_agg2);
         if ((s = set_lds2(kagg, lds_agg)) != MIMO_OK) return s;
-        if ((s = launch2(kagg, dim3(grid_blocks(pp, pl.nsub)), lds_agg)) != MIMO_OK) return s;
+        if ((s = launch2(kagg, dim3(grid_blocks(pp, pl.nsub)), lds_agg, b2::NTHR)) != MIMO_OK) return s;
         if ((s = mark(1)) != MIMO_OK) return s;
         const int NP = p.N * p.P;
-        if ((s = launch2(reinterpret_cast<const void*>(&b2::k_scan_rev), dim3((NP + 255) / 256, p.B * p.H), 0)) !=
-            MIMO_OK)
+        if ((s = launch2(reinterpret_cast<const void*>(&b2::k_scan_rev),
+                         dim3((NP + b2::NTHR1 - 1) / b2::NTHR1, p.B * p.H), 0, b2::NTHR1)) != MIMO_OK)
             return s;
     } else if ((s = mark(1)) != MIMO_OK) {
         return s;
@@ -676,7 +676,8 @@ mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events
     if ((s = launch2(kmain, dim3(grid_blocks(pp, pl.nseg)), lds_main, b2::NTHR2)) != MIMO_OK) return s;
     if ((s = mark(3)) != MIMO_OK) return s;
     const long tot = (long)p.B * p.H * p.R * p.P;
-    if ((s = launch2(reinterpret_cast<const void*>(&b2::k_finish2), dim3((unsigned)((tot + 255) / 256)), 0)) != MIMO_OK)
+    if ((s = launch2(reinterpret_cast<const void*>(&b2::k_finish2), dim3((unsigned)((tot + b2::NTHR1 - 1) / b2::NTHR1)),
+                     0, b2::NTHR1)) != MIMO_OK)
         return s;
     if ((s = mark(4)) != MIMO_OK) return s;
     const hipError_t e = hipGetLastError();
