@@ -562,7 +562,7 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
                             float pz = 0.f, sg = 0.f, silu = 1.f;
                             if (p.has_z) {
                                 pz = zr * cz[j][r];
-                                sg = sig32(pz);
+                                sg = sigmoid_fast(pz);   // hardware exp2 and reciprocal (about 1 ulp each)
                                 silu = pz * sg;
                             }
                             if (p.fwd) {
