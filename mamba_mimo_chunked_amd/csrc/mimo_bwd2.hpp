@@ -105,34 +105,31 @@ __device__ __forceinline__ void gemm64(int Mi, int Nj, int K, const float* A, co
             }
         }
     }
+    if (K & 15) {   // wave-uniform: zero the last step's values past K (the tiles hold stale data there)
+        const int kt = nk - 1, kb = 16 * kt + 4 * q;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+            if (t4 != kt) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const bool in = kb + v < K;
+                a[t4][v] = in ? a[t4][v] : 0.f;
+#pragma unroll
+                for (int cb = 0; cb < CW; ++cb) bv[t4][cb][v] = in ? bv[t4][cb][v] : 0.f;
+            }
+        }
+    }
     f32x4 acc[CW];
 #pragma unroll
     for (int cb = 0; cb < CW; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if ((K & 15) == 0) {   // whole steps: no masking
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            if (kt >= nk) break;
+    for (int kt = 0; kt < 4; ++kt) {
+        if (kt >= nk) break;
 #pragma unroll
-            for (int cb = 0; cb < CW; ++cb) {
-                if (j0 + 16 * cb >= Nj) break;
+        for (int cb = 0; cb < CW; ++cb) {
+            if (j0 + 16 * cb >= Nj) break;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[cb] = mfma_f32(a[kt][v], bv[kt][cb][v], acc[cb]);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            if (kt >= nk) break;
-            const int kb = 16 * kt + 4 * q;
-#pragma unroll
-            for (int cb = 0; cb < CW; ++cb) {
-                if (j0 + 16 * cb >= Nj) break;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const bool in = kb + v < K;
-                    acc[cb] = mfma_f32(in ? a[kt][v] : 0.f, in ? bv[kt][cb][v] : 0.f, acc[cb]);
-                }
-            }
+            for (int v = 0; v < 4; ++v) acc[cb] = mfma_f32(a[kt][v], bv[kt][cb][v], acc[cb]);
         }
     }
     float rsum[4] = {0.f, 0.f, 0.f, 0.f};
@@ -217,6 +214,18 @@ struct DivS {
     __device__ int q(int e) const { return static_cast<int>((static_cast<float>(e) + 0.5f) * rd); }
     __device__ int r(int e) const { return e - q(e) * d; }
 };
+
+// sin and cos as the shared helper computes them, with its large-argument path
+// (|x| > 8192, the library's sincosf) out of line: the load stages four angles a
+// thread, and four inlined copies of that path would make the chunk pass's code
+// larger than the instruction cache.
+__device__ __attribute__((noinline)) void sin_cos_far(float x, float& s, float& c) { sincosf(x, &s, &c); }
+__device__ __forceinline__ void sin_cos2(float x, float& s, float& c) {
+    if (__builtin_fabsf(x) <= 8192.f)
+        sin_cos(x, s, c);
+    else
+        sin_cos_far(x, s, c);
+}
 
 // Items of the chunk load, a thread's items being e = tid + NT x for x < IX (every
 // kind has at most 64 * 64 / 8 = 512 of them):
@@ -390,7 +399,7 @@ __device__ __forceinline__ void stage_chunk(const Params2& p, float* sm, int c, 
                         ka[v] = ((v & 1) ? hi16(ua) : lo16(ua)) + res.kb[x][0][v];
                         ke[v] = ((v & 1) ? hi16(ue) : lo16(ue)) + res.kb[x][1][v];
                     }
-                    if (n4 + v < W) sin_cos(f.ang[x][v], sn, cs);
+                    if (n4 + v < W) sin_cos2(f.ang[x][v], sn, cs);
                 }
                 keep.cs[x][v] = cs;
                 keep.sn[x][v] = sn;

@@ -185,3 +185,16 @@ def test_bwd2_unaligned_views_match():
     for key in bwd2.NAMES:
         if a[key] is not None:
             assert torch.equal(a[key], b[key]), key
+
+
+def test_bwd2_large_angles():
+    """Rotation angles far beyond 2*pi (offset by 20000, past the reduced hardware
+    sine range) take the library sine/cosine path; parity as for ordinary angles."""
+    case = Case(1, 300, 2, 1, 64, 64, 4, 16, name="b2_large_angles")
+    inp = make_inputs(case)
+    inp["angles"] = (inp["angles"].double() + 20000.0).float()
+    states, qk = _caches(inp)
+    got = _run_gpu(inp, states, qk, torch.float32)
+    ref = _oracle(inp, states, qk)
+    errs = _compare(got, ref, "large angles: ")
+    log("    " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
