@@ -215,18 +215,6 @@ struct DivS {
     __device__ int r(int e) const { return e - q(e) * d; }
 };
 
-// sin and cos as the shared helper computes them, with its large-argument path
-// (|x| > 8192, the library's sincosf) out of line: the load stages four angles a
-// thread, and four inlined copies of that path would make the chunk pass's code
-// larger than the instruction cache.
-__device__ __attribute__((noinline)) void sin_cos_far(float x, float& s, float& c) { sincosf(x, &s, &c); }
-__device__ __forceinline__ void sin_cos2(float x, float& s, float& c) {
-    if (__builtin_fabsf(x) <= 8192.f)
-        sin_cos(x, s, c);
-    else
-        sin_cos_far(x, s, c);
-}
-
 // Items of the chunk load, a thread's items being e = tid + NT x for x < IX (every
 // kind has at most 64 * 64 / 8 = 512 of them):
 //   rotation items (i, n4): four columns n4.. of each half (n4 < N/2) of row i of q^
@@ -399,7 +387,7 @@ __device__ __forceinline__ void stage_chunk(const Params2& p, float* sm, int c, 
                         ka[v] = ((v & 1) ? hi16(ua) : lo16(ua)) + res.kb[x][0][v];
                         ke[v] = ((v & 1) ? hi16(ue) : lo16(ue)) + res.kb[x][1][v];
                     }
-                    if (n4 + v < W) sin_cos2(f.ang[x][v], sn, cs);
+                    if (n4 + v < W) sin_cos_ool(f.ang[x][v], sn, cs);
                 }
                 keep.cs[x][v] = cs;
                 keep.sn[x][v] = sn;

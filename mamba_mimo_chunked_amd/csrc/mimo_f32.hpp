@@ -217,10 +217,10 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C;
         const int cl = min(C, p.S - c0);
-        // The unit-projection chunk pass runs two workgroups per CU (at most 256 VGPRs):
-        // there the thread index is made opaque per chunk so that index arithmetic is
-        // redone per chunk instead of being held in registers across the loop.
-        const int tid = (UV && MAIN) ? tid_x() : static_cast<int>(threadIdx.x), lane = tid & 63, l16 = lane & 15,
+        // The chunk pass runs two workgroups per CU (at most 256 VGPRs): its thread index
+        // is made opaque per chunk so that index arithmetic is redone per chunk instead
+        // of being held in registers across the loop (which spills).
+        const int tid = MAIN ? tid_x() : static_cast<int>(threadIdx.x), lane = tid & 63, l16 = lane & 15,
                   q4 = lane >> 4;
 
         // ---- states[c] = S entering chunk c, in the output type
@@ -385,7 +385,14 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
             if (t >= cl || n >= M) continue;
             const float f = sFac[t];
             float cn = 1.f, sn = 0.f;
-            if (n < W) sin_cos(ang[k2], sn, cn);
+            if (n < W) {
+                // the chunk pass's code would outgrow the instruction cache with the library
+                // path inlined at every unrolled item; the aggregate's does not
+                if constexpr (MAIN)
+                    sin_cos_ool(ang[k2], sn, cn);
+                else
+                    sin_cos(ang[k2], sn, cn);
+            }
             for (int r = 0; r < R; ++r) {
                 float* kr = sK + (r * Cp + t) * LQ;
                 const float ka = kr[n], ke = kr[M + n];

@@ -97,6 +97,17 @@ __device__ __forceinline__ void sin_cos(float x, float& s, float& c) {
     }
 }
 
+// sin_cos with its large-argument path out of line, for kernels that take many
+// angles a thread: inlined copies of the library path would outgrow the
+// instruction cache (64 KB, shared by two compute units).
+__device__ inline __attribute__((noinline)) void sin_cos_far(float x, float& s, float& c) { sincosf(x, &s, &c); }
+__device__ __forceinline__ void sin_cos_ool(float x, float& s, float& c) {
+    if (__builtin_fabsf(x) <= 8192.f)
+        sin_cos(x, s, c);
+    else
+        sin_cos_far(x, s, c);
+}
+
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS accesses, not
 // for its global memory traffic. __syncthreads() also waits for outstanding global
 // loads into LDS (the staging prefetch below), which would serialise the prefetch
