@@ -374,7 +374,9 @@ mimo_status make_plan32(const Prob32& q, Plan32* pl) {
     pl->L = (int)L;
     pl->nseg = (int)((pl->nc + L - 1) / L);
     if (pl->nseg > 65535) return fail(MIMO_ERR_UNSUPPORTED, "too many segments");
-    pl->F = (L % 2 == 0 && L >= 4) ? 2 : 1;
+    // two sub-segments a segment only when segments are long (8 chunks or more): for
+    // short ones the halved chain does not pay for twice the aggregate traffic
+    pl->F = (L % 2 == 0 && L >= 8) ? 2 : 1;
     pl->nsub = (pl->nseg - 1) * pl->F;
     const bool part = !q.fwd && pl->nseg > 1;
     size_t off = 0;
