@@ -8,8 +8,10 @@ RMS(gpu - oracle) / RMS(oracle) < 1e-4 (fp32 intermediates against float64;
 a tenth of the operator's 1e-3 bar); with the default bf16 outputs DQ, DK and
 DV must be within 1e-3 of the oracle rounded to bf16. Cases: several segments
 and ragged tails, GQA, R = 1..8, both dout layouts, with and without d,
-rotary divisor 2, the perf shape on sampled heads, every element written, and
-the shapes beyond the kernel's tiles (NotImplementedError).
+rotary divisor 2, the perf shape on sampled heads, every element written,
+angles far beyond 2*pi, inputs that are unaligned device views (bit-identical
+to aligned ones), and the shapes beyond the kernel's tiles
+(NotImplementedError).
 """
 
 import numpy as np
