@@ -80,8 +80,7 @@ __device__ __forceinline__ float ld16(const unsigned short* p, long i) {
     return __uint_as_float(static_cast<unsigned>(x) << 16);
 }
 template <bool F16>
-__device__ __forceinline__ void ld16x4(const unsigned short* p, long i, float* out) {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(p + i);
+__device__ __forceinline__ void cvt16x4(u32x2 w, float* out) {
     const unsigned short h[4] = {static_cast<unsigned short>(w[0]), static_cast<unsigned short>(w[0] >> 16),
                                  static_cast<unsigned short>(w[1]), static_cast<unsigned short>(w[1] >> 16)};
 #pragma unroll
@@ -91,6 +90,10 @@ __device__ __forceinline__ void ld16x4(const unsigned short* p, long i, float* o
         else
             out[d] = __uint_as_float(static_cast<unsigned>(h[d]) << 16);
     }
+}
+template <bool F16>
+__device__ __forceinline__ void ld16x4(const unsigned short* p, long i, float* out) {
+    cvt16x4<F16>(*reinterpret_cast<const u32x2*>(p + i), out);
 }
 // fp32 -> 16-bit output, round to nearest even
 template <bool F16>
@@ -214,6 +217,76 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
     const float dval = (MAIN && p.has_d) ? p.d[h] : 0.f;
     float dprod = 1.f;
 
+    // ---- the unit-projection (SISO) instances take a chunk's inputs into registers
+    // first: raw 16-bit q, k, v of the thread's load items, the angles of its rotation
+    // items, and (wave 0, lane t = token) the token's controls. With AHEAD (their
+    // aggregate, whose chunks are short and load-bound) these are fetched one chunk
+    // ahead, issued after the current chunk's rotation and consumed at the start of
+    // the next, and the chunk loop's barriers wait for LDS only so that the loads stay
+    // in flight through the state update. The other instances load at the point of
+    // use (measured: the register fetch costs them occupancy).
+    constexpr bool AHEAD = UV && !MAIN;
+    auto sync = [] {
+        if constexpr (AHEAD)
+            bar();
+        else
+            __syncthreads();
+    };
+    constexpr int N4 = NT / 4, P4 = PT / 4;
+    constexpr int QK_IT = MT * N4 / NTHR, PS_IT = MT * P4 / NTHR;   // exact: MT * NT >= 32 * 32
+    constexpr int ROT_IT = MT * (NT / 2) / NTHR;                     // rotation items (t < MT, n < NT/2)
+    u32x2 fq[QK_IT], fk[QK_IT], fv[PS_IT];
+    float fang[ROT_IT];
+    float fx0 = 0.f, fx1 = 0.f, fdt0 = 0.f, ftr0 = 0.f, fdt1 = 0.f, ftr1 = 0.f;
+    auto fetch = [&](int cc) {
+        if constexpr (!UV) return;
+        const int tf = MAIN ? tid_x() : static_cast<int>(threadIdx.x);
+        const int c0f = cc * C, clf = min(C, p.S - c0f);
+#pragma unroll
+        for (int k2 = 0; k2 < ROT_IT; ++k2) {
+            const int e = tf + k2 * NTHR;
+            const int t = e / (NT / 2), n = e % (NT / 2);
+            fang[k2] = (t < clf && n < W) ? p.angles[((long)(b * p.S + c0f + t) * p.H + h) * W + n] : 0.f;
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < QK_IT; ++k2) {
+            const int e = tf + k2 * NTHR;
+            const int i = e / N4, n = 4 * (e % N4);
+            const int r = i / Cp, t = i % Cp;
+            fk[k2] = fq[k2] = u32x2{0u, 0u};
+            if (r < R && t < clf && n < N) {
+                const long src = (((long)(b * p.S + c0f + t) * R + r) * p.G + g) * N + n;
+                fk[k2] = *reinterpret_cast<const u32x2*>(p.k + src);
+                if (MAIN) fq[k2] = *reinterpret_cast<const u32x2*>(p.q + src);
+            }
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < PS_IT; ++k2) {
+            const int e = tf + k2 * NTHR;
+            const int i = e / P4, pc = 4 * (e % P4);
+            const int r = i / Cp, t = i % Cp;
+            fv[k2] = u32x2{0u, 0u};
+            if (r < R && t < clf && pc < P)
+                fv[k2] = *reinterpret_cast<const u32x2*>(p.v + ((long)(b * p.S + c0f + t) * p.H + h) * P + pc);
+        }
+        if ((tf >> 6) == 0) {
+            const int t = tf & 63;
+            fx0 = fx1 = fdt0 = ftr0 = fdt1 = ftr1 = 0.f;
+            if (t < clf) {
+                const long T0 = tokb + c0f + t;
+                fx0 = p.adt != nullptr ? p.adt[T0] : p.da_cs[T0];
+                if (p.adt == nullptr) fx1 = p.da_cs_rev[T0];
+                fdt0 = p.dt[T0];
+                ftr0 = p.trapf ? p.trapf[T0] : bf2f(p.trap[T0]);
+                if (c0f + t + 1 < p.S) {
+                    fdt1 = p.dt[T0 + 1];
+                    ftr1 = p.trapf ? p.trapf[T0 + 1] : bf2f(p.trap[T0 + 1]);
+                }
+            }
+        }
+    };
+    if (AHEAD && c_begin < c_end) fetch(c_begin);
+
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C;
         const int cl = min(C, p.S - c0);
@@ -222,6 +295,7 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
         // of being held in registers across the loop (which spills).
         const int tid = MAIN ? tid_x() : static_cast<int>(threadIdx.x), lane = tid & 63, l16 = lane & 15,
                   q4 = lane >> 4;
+        if constexpr (UV && !AHEAD) fetch(c);
 
         // ---- states[c] = S entering chunk c, in the output type
         if constexpr (MAIN) {
@@ -249,7 +323,7 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
             float cs = 0.f, rev = 0.f;
             if (p.adt != nullptr) {
                 // chunk-local inclusive cumulative sum of the log decay
-                float a = (t < cl) ? p.adt[tokb + c0 + t] : 0.f;
+                float a = UV ? fx0 : ((t < cl) ? p.adt[tokb + c0 + t] : 0.f);   // zero past the chunk
 #pragma unroll
                 for (int o = 1; o < 64; o *= 2) {
                     const float u = __shfl_up(a, o);
@@ -259,19 +333,21 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
                 cs = a;
                 rev = last - a;
             } else if (t < cl) {
-                cs = p.da_cs[tokb + c0 + t];
-                rev = p.da_cs_rev[tokb + c0 + t];
+                cs = UV ? fx0 : p.da_cs[tokb + c0 + t];
+                rev = UV ? fx1 : p.da_cs_rev[tokb + c0 + t];
             }
             if (t < CX) {
                 float gam = 0.f, fac = 0.f;
                 if (t < cl) {
                     const long T0 = tokb + c0 + t;
-                    const float tr0 = p.trapf ? p.trapf[T0] : bf2f(p.trap[T0]);
-                    gam = p.dt[T0] * sig32(tr0);
+                    const float dt0 = UV ? fdt0 : p.dt[T0];
+                    const float tr0 = UV ? ftr0 : (p.trapf ? p.trapf[T0] : bf2f(p.trap[T0]));
+                    gam = dt0 * sig32(tr0);
                     float beta = 0.f;
                     if (c0 + t + 1 < p.S) {
-                        const float tr1 = p.trapf ? p.trapf[T0 + 1] : bf2f(p.trap[T0 + 1]);
-                        beta = p.dt[T0 + 1] * (1.0f - sig32(tr1));
+                        const float dt1 = UV ? fdt1 : p.dt[T0 + 1];
+                        const float tr1 = UV ? ftr1 : (p.trapf ? p.trapf[T0 + 1] : bf2f(p.trap[T0 + 1]));
+                        beta = dt1 * (1.0f - sig32(tr1));
                     }
                     fac = gam + beta;
                 }
@@ -284,18 +360,17 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
             }
         }
 
-        // ---- q0, k0 (biased, unrotated) and Psi into LDS; zero outside the problem. The
-        // loops are unrolled so that each thread's loads are all in flight together; the
-        // angles of the rotation below are fetched here too.
-        constexpr int N4 = NT / 4, P4 = PT / 4;
-        constexpr int QK_IT = MT * N4 / NTHR, PS_IT = MT * P4 / NTHR;   // exact: MT * NT >= 32 * 32
-        constexpr int ROT_IT = MT * (NT / 2) / NTHR;                     // rotation items (t < MT, n < NT/2)
+        // ---- q0, k0 (biased, unrotated) and Psi into LDS (from the fetched values, or
+        // loaded here: every load of a thread in flight together); zero outside the
+        // problem. The angles of the rotation below are loaded here too.
         float ang[ROT_IT];
+        if constexpr (!UV) {
 #pragma unroll
-        for (int k2 = 0; k2 < ROT_IT; ++k2) {
-            const int e = tid + k2 * NTHR;
-            const int t = e / (NT / 2), n = e % (NT / 2);
-            ang[k2] = (t < cl && n < W) ? p.angles[((long)(b * p.S + c0 + t) * p.H + h) * W + n] : 0.f;
+            for (int k2 = 0; k2 < ROT_IT; ++k2) {
+                const int e = tid + k2 * NTHR;
+                const int t = e / (NT / 2), n = e % (NT / 2);
+                ang[k2] = (t < cl && n < W) ? p.angles[((long)(b * p.S + c0 + t) * p.H + h) * W + n] : 0.f;
+            }
         }
 #pragma unroll
         for (int k2 = 0; k2 < QK_IT; ++k2) {
@@ -305,12 +380,18 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
             float qv[4] = {0.f, 0.f, 0.f, 0.f}, kv[4] = {0.f, 0.f, 0.f, 0.f};
             if (r < R && t < cl && n < N) {
                 const long src = (((long)(b * p.S + c0 + t) * R + r) * p.G + g) * N + n;
-                ld16x4<F16>(p.k, src, kv);
+                if constexpr (UV)
+                    cvt16x4<F16>(fk[k2], kv);
+                else
+                    ld16x4<F16>(p.k, src, kv);
                 const float* kb = p.k_bias + ((long)h * R + r) * N + n;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) kv[d] += kb[d];
                 if (MAIN) {
-                    ld16x4<F16>(p.q, src, qv);
+                    if constexpr (UV)
+                        cvt16x4<F16>(fq[k2], qv);
+                    else
+                        ld16x4<F16>(p.q, src, qv);
                     const float* qb = p.q_bias + ((long)h * R + r) * N + n;
 #pragma unroll
                     for (int d = 0; d < 4; ++d) qv[d] += qb[d];
@@ -323,26 +404,22 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
         for (int k2 = 0; k2 < PS_IT; ++k2) {
             const int e = tid + k2 * NTHR;
             const int i = e / P4, pc = 4 * (e % P4);
-            const int r = i / Cp, t = i % Cp;
+            const int r = i / Cp;
             if constexpr (UV) {
-                u32x2 w = {0u, 0u};
-                if (r < R && t < cl && pc < P)
-                    w = *reinterpret_cast<const u32x2*>(p.v + ((long)(b * p.S + c0 + t) * p.H + h) * P + pc);
-                *reinterpret_cast<u32x2*>(sPsi16 + i * T::LP16 + pc) = w;
+                *reinterpret_cast<u32x2*>(sPsi16 + i * T::LP16 + pc) = fv[k2];   // zero outside the problem
                 continue;
             }
             float x[4] = {0.f, 0.f, 0.f, 0.f};
-            if (r < R && t < cl && pc < P) {
-                ld16x4<F16>(p.v, ((long)(b * p.S + c0 + t) * p.H + h) * P + pc, x);
-                if (p.mimo_v) {
-                    const float* mv = p.mimo_v + ((long)h * R + r) * P + pc;
+            const int t = i % Cp;
+            if (r < R && t < cl && pc < P) ld16x4<F16>(p.v, ((long)(b * p.S + c0 + t) * p.H + h) * P + pc, x);
+            if (p.mimo_v && r < R && pc < P) {
+                const float* mv = p.mimo_v + ((long)h * R + r) * P + pc;
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) x[d] *= mv[d];
-                }
+                for (int d = 0; d < 4; ++d) x[d] *= mv[d];
             }
             *reinterpret_cast<f32x4*>(sPsi + i * LP + pc) = f32x4{x[0], x[1], x[2], x[3]};
         }
-        __syncthreads();
+        sync();
 
         // ---- same-token dots of the unrotated q, k (qk_dot) and exp(segsum)
         if constexpr (MAIN) {
@@ -375,7 +452,7 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
                 }
             }
         }
-        __syncthreads();
+        sync();
 
         // ---- rotation of q and k (pairs n, N/2 + n for n < W) and K~ = k * factor
 #pragma unroll
@@ -389,9 +466,9 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
                 // the chunk pass's code would outgrow the instruction cache with the library
                 // path inlined at every unrolled item; the aggregate's does not
                 if constexpr (MAIN)
-                    sin_cos_ool(ang[k2], sn, cn);
+                    sin_cos_ool(UV ? fang[k2] : ang[k2], sn, cn);
                 else
-                    sin_cos(ang[k2], sn, cn);
+                    sin_cos(UV ? fang[k2] : ang[k2], sn, cn);
             }
             for (int r = 0; r < R; ++r) {
                 float* kr = sK + (r * Cp + t) * LQ;
@@ -406,7 +483,9 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
                 }
             }
         }
-        __syncthreads();
+        // (with AHEAD: the next chunk's inputs, in flight through the state update)
+        if (AHEAD && c + 1 < c_end) fetch(c + 1);
+        sync();
 
         f32x4 acc[PW][MTT];
         if constexpr (MAIN) {
@@ -459,7 +538,7 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
                 }
                 at[w] = a4;
             }
-            __syncthreads();   // every wave is done reading sQ
+            sync();   // every wave is done reading sQ
 #pragma unroll
             for (int w = 0; w < T::AT; ++w) {
                 const int u = wave + NW * w;
@@ -469,7 +548,7 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
                     for (int v = 0; v < 4; ++v) sA[(16 * it + 4 * q4 + v) * LA + 16 * jt + l16] = at[w][v];
                 }
             }
-            __syncthreads();
+            sync();
             // ---- intra = A Psi onto the scaled inter term
 #pragma unroll
             for (int j = 0; j < PW; ++j) {
@@ -520,7 +599,7 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
         if constexpr (MAIN) {
             // ---- y's partial sums (inter + intra) through LDS, so that the epilogue
             // can address them by run-time rank and token
-            __syncthreads();   // every wave is done reading the causal block
+            sync();   // every wave is done reading the causal block
 #pragma unroll
             for (int j = 0; j < PW; ++j) {
                 const int pt = wave + NW * j;
@@ -601,7 +680,7 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
                 }
             }
         }
-        __syncthreads();   // the next chunk overwrites the tiles and tables
+        sync();   // the next chunk overwrites the tiles and tables
     }
 
     if constexpr (!MAIN) {
