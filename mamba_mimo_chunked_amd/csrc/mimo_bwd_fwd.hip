@@ -59,7 +59,49 @@ namespace mimo {
 // chain is latency-bound, so more waves keep more loads in flight); loads run
 // up to 64 sub-segments ahead of the serial chain, so that the usual segment
 // counts need a single round trip to memory.
-__global__ __launch_bounds__(256) void k_scan(Params p) {
+// Short scans (up to SCAN_SPANS * SCAN_SPAN sub-segments): wave w of a block walks
+// sub-segments [16w, 16w + 16) of 64 consecutive state elements. Each wave first
+// folds its span from zero (its increment L and decay product D), the spans'
+// carries are chained through LDS, and each wave then walks its span again from
+// its carry, writing E at segment ends. All loads of a span are in flight at once.
+constexpr int SCAN_SPAN = 16, SCAN_SPANS = 16;
+__global__ __launch_bounds__(64 * SCAN_SPANS) void k_scan(Params p) {
+    __shared__ float sL[SCAN_SPANS][64], sD[SCAN_SPANS][64];
+    const int bh = blockIdx.y;
+    const int NP = p.N * p.P;
+    const int lane = threadIdx.x & 63, sp = threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + lane;
+    const bool ok = e < NP;
+    const int ns = p.nsub, j0 = sp * SCAN_SPAN, n = min(SCAN_SPAN, ns - j0);
+    float* base = p.agg + (long)bh * ns * NP + (ok ? e : 0);
+    const float* dec = p.decay + (long)bh * ns + j0;
+    float U[SCAN_SPAN], D[SCAN_SPAN];
+#pragma unroll
+    for (int j = 0; j < SCAN_SPAN; ++j) {
+        U[j] = (j < n && ok) ? base[(long)(j0 + j) * NP] : 0.f;
+        D[j] = (j < n) ? dec[j] : 1.f;
+    }
+    float L = 0.f, Dp = 1.f;
+#pragma unroll
+    for (int j = 0; j < SCAN_SPAN; ++j) {
+        L = __fmaf_rn(L, D[j], U[j]);
+        Dp *= D[j];
+    }
+    sL[sp][lane] = L;
+    sD[sp][lane] = Dp;
+    __syncthreads();
+    float E = 0.f;
+    for (int s = 0; s < sp; ++s) E = __fmaf_rn(E, sD[s][lane], sL[s][lane]);
+#pragma unroll
+    for (int j = 0; j < SCAN_SPAN; ++j) {
+        E = __fmaf_rn(E, D[j], U[j]);
+        if (ok && j < n && (j0 + j + 1) % p.F == 0) base[(long)(j0 + j) * NP] = E;
+    }
+}
+
+// Longer scans: one thread per state element, E_{j+1} = E_j * D_j + U_j in
+// order, loads running 64 sub-segments ahead.
+__global__ __launch_bounds__(256) void k_scan_long(Params p) {
     const int bh = blockIdx.y;
     const int NP = p.N * p.P;
     const int e = blockIdx.x * 256 + threadIdx.x;
@@ -88,29 +130,31 @@ __global__ __launch_bounds__(256) void k_scan(Params p) {
     }
 }
 
-// dmimo = sum over segments of the partials, in segment order. Loads run up to
-// 32 segments ahead of the additions.
-__device__ __forceinline__ float sum_segments(const float* part, long stride, int nseg) {
+// dmimo = sum over segments of the partials, in segment order. Threads
+// [0, tot) sum dmimo_o and threads [tot, 2 tot) dmimo_z when both are present,
+// so that neither sum waits for the other's loads.
+__global__ __launch_bounds__(256) void k_finish(Params p) {
+    const long RP = (long)p.R * p.P, tot = (long)p.B * p.H * RP;
+    long e = (long)blockIdx.x * 256 + threadIdx.x;
+    bool z = !p.reduce_o;
+    if (p.reduce_o && p.has_z && e >= tot) {
+        e -= tot;
+        z = true;
+    }
+    if (e >= tot) return;
+    const long bh = e / RP, rp = e - bh * RP;
+    const float* part = (z ? p.part_z : p.part_o) + bh * p.nseg * RP + rp;
     constexpr int AHEAD = 32;
     float s = 0.f;
-    for (int s0 = 0; s0 < nseg; s0 += AHEAD) {
+    for (int s0 = 0; s0 < p.nseg; s0 += AHEAD) {
         float v[AHEAD];
 #pragma unroll
-        for (int j = 0; j < AHEAD; ++j) v[j] = (s0 + j < nseg) ? part[(long)(s0 + j) * stride] : 0.f;
+        for (int j = 0; j < AHEAD; ++j) v[j] = (s0 + j < p.nseg) ? part[(long)(s0 + j) * RP] : 0.f;
 #pragma unroll
         for (int j = 0; j < AHEAD; ++j)
-            if (s0 + j < nseg) s += v[j];
+            if (s0 + j < p.nseg) s += v[j];
     }
-    return s;
-}
-
-__global__ __launch_bounds__(256) void k_finish(Params p) {
-    const long RP = (long)p.R * p.P;
-    const long e = (long)blockIdx.x * 256 + threadIdx.x;
-    if (e >= (long)p.B * p.H * RP) return;
-    const long bh = e / RP, rp = e - bh * RP;
-    if (p.reduce_o) p.dmimo_o[e] = sum_segments(p.part_o + bh * p.nseg * RP + rp, RP, p.nseg);
-    if (p.has_z) p.dmimo_z[e] = sum_segments(p.part_z + bh * p.nseg * RP + rp, RP, p.nseg);
+    (z ? p.dmimo_z : p.dmimo_o)[e] = s;
 }
 
 }  // namespace mimo
@@ -291,6 +335,24 @@ mimo_status launch(kfn f, dim3 grid, dim3 block, int lds, hipStream_t st, Params
     return MIMO_OK;
 }
 
+// The state scan over sub-segments: the span kernel up to 256 of them, else the
+// sequential one.
+mimo_status launch_scan(Params& p, int bh, hipStream_t st) {
+    const int NP = p.N * p.P;
+    if (p.nsub <= SCAN_SPAN * SCAN_SPANS) {
+        const int spans = (p.nsub + SCAN_SPAN - 1) / SCAN_SPAN;
+        return launch(k_scan, dim3((NP + 63) / 64, bh), dim3(64 * spans), 0, st, p);
+    }
+    return launch(k_scan_long, dim3((NP + 255) / 256, bh), dim3(256), 0, st, p);
+}
+
+// The dmimo_o / dmimo_z sums: one thread per output element of each present gradient.
+mimo_status launch_finish(Params& p, hipStream_t st) {
+    const long tot = (long)p.B * p.H * p.R * p.P * ((p.reduce_o ? 1 : 0) + (p.has_z ? 1 : 0));
+    if (tot == 0) return MIMO_OK;
+    return launch(k_finish, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, p);
+}
+
 // The forward's arguments as those of the backward first stage (no dout, no
 // backward outputs): both run the same plan and kernels.
 mimo_bwd_fwd_args as_bwd_args(const mimo_fwd_args* f) {
@@ -438,18 +500,15 @@ mimo_status run32(const Prob32& q, Params& p, void* workspace, size_t workspace_
         if ((s = set_lds(kagg, pl.lds_agg)) != MIMO_OK) return s;
         if ((s = launch(kagg, dim3(grid_blocks(p, pl.nsub)), dim3(256), pl.lds_agg, st, p)) != MIMO_OK) return s;
         if ((s = mark(1)) != MIMO_OK) return s;
-        const int NP = p.N * p.P;
-        if ((s = launch(k_scan, dim3((NP + 255) / 256, p.B * p.H), dim3(256), 0, st, p)) != MIMO_OK) return s;
+        if ((s = launch_scan(p, p.B * p.H, st)) != MIMO_OK) return s;
     } else if ((s = mark(1)) != MIMO_OK) {
         return s;
     }
     if ((s = mark(2)) != MIMO_OK) return s;
     if ((s = launch(kmain, dim3(grid_blocks(p, pl.nseg)), dim3(256), pl.lds_main, st, p)) != MIMO_OK) return s;
     if ((s = mark(3)) != MIMO_OK) return s;
-    if (pl.nseg > 1 && !q.fwd && (q.reduce_o || q.has_z)) {
-        const long tot = (long)p.B * p.H * p.R * p.P;
-        if ((s = launch(k_finish, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, p)) != MIMO_OK) return s;
-    }
+    if (pl.nseg > 1 && !q.fwd && (q.reduce_o || q.has_z))
+        if ((s = launch_finish(p, st)) != MIMO_OK) return s;
     if ((s = mark(4)) != MIMO_OK) return s;
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -786,18 +845,15 @@ static mimo_status run(const mimo_bwd_fwd_args* a, uint16_t* out, void* stream, 
         if ((s = set_lds(kagg, pl.lds_agg)) != MIMO_OK) return s;
         if ((s = launch(kagg, dim3(grid_blocks(p, pl.nsub)), dim3(pl.NW * 64), pl.lds_agg, st, p)) != MIMO_OK) return s;
         if ((s = mark(1)) != MIMO_OK) return s;
-        const int NP = p.N * p.P;
-        if ((s = launch(k_scan, dim3((NP + 255) / 256, BH), dim3(256), 0, st, p)) != MIMO_OK) return s;
+        if ((s = launch_scan(p, BH, st)) != MIMO_OK) return s;
     } else if ((s = mark(1)) != MIMO_OK) {
         return s;
     }
     if ((s = mark(2)) != MIMO_OK) return s;
     if ((s = launch(kmain, dim3(grid_blocks(p, pl.nseg)), dim3(pl.NW * 64), pl.lds_main, st, p)) != MIMO_OK) return s;
     if ((s = mark(3)) != MIMO_OK) return s;
-    if (pl.nseg > 1 && p.need_y && !fwd) {
-        const long tot = (long)BH * p.R * p.P;
-        if ((s = launch(k_finish, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, p)) != MIMO_OK) return s;
-    }
+    if (pl.nseg > 1 && p.need_y && !fwd)
+        if ((s = launch_finish(p, st)) != MIMO_OK) return s;
     if ((s = mark(4)) != MIMO_OK) return s;
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -34,6 +34,10 @@ EXTRA = [
     Case(1, 130, 2, 1, 16, 16, 8, 8, name="r8_c8_small"),
     Case(1, 95, 1, 1, 32, 48, 3, 6, rd=2, name="r3_c6_rd2_p48"),
     Case(1, 64, 1, 1, 64, 64, 1, 64, name="r1_c64"),
+    # 255 sub-segments: the span scan with all 16 spans, the last one short
+    Case(1, 8192, 2, 1, 16, 16, 2, 16, name="scan_16_spans"),
+    # 511 sub-segments: the sequential scan
+    Case(1, 16384, 1, 1, 16, 16, 2, 16, name="scan_sequential"),
 ]
 
 
