@@ -1027,6 +1027,19 @@ __device__ __forceinline__ void flush_dz(const Params& p, unsigned short* out, c
     }
 }
 
+// Rows of the per-rank layer output [B,S,R,H,P] of one chunk, staged in LDS by the
+// epilogue as [r*Cp + t][PT + 8] bf16, written out 16 bytes a thread.
+template <int NTHR, int PT>
+__device__ __forceinline__ void flush_ranks(const Params& p, const unsigned short* sO, int Cp, int b, int h, int c0,
+                                            int cl) {
+    const int P8 = p.P / 8, per = cl * P8;
+    for (int e = threadIdx.x; e < p.R * per; e += NTHR) {
+        const int r = e / per, rem = e - r * per, t = rem / P8, pc = (rem - t * P8) * 8;
+        unsigned short* dst = p.o + ((long)(b * p.S + c0 + t) * p.R + r) * p.H * p.P + (long)h * p.P + pc;
+        *reinterpret_cast<u32x4*>(dst) = lds_ld<u32x4>(sO + (r * Cp + t) * (PT + 8) + pc);
+    }
+}
+
 template <int RP, int CT, int NT, int PT, bool EX, int MODE>
 __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params pin) {
     const Params p = specialise<RP, CT, NT, PT, EX, MODE>(pin);
@@ -1068,6 +1081,10 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
     const bool need_y = p.need_y;
     // the epilogue stages one [C,P] bf16 output per chunk in LDS: dz, or the reduced layer output
     const bool stage_out = p.fwd ? p.reduce_o : p.has_z;
+    // the per-rank layer output is staged too when its RP*Cp rows fit the k tile
+    // (dead from the kappa^T pass to the next chunk's phase A)
+    constexpr bool RANKS_FIT = RP * Cp * (PT + 8) <= MT * LDQ;
+    const bool stage_ranks = RANKS_FIT && p.fwd && !p.reduce_o;
     unsigned short* const out16 = p.fwd ? p.o : p.dz;
     // which threads fill Psi^T (LITE families): the second half under the rotation split, else all
     const int psi_t0 = PSPLIT ? NTHR / 2 : 0, psi_n = PSPLIT ? NTHR / 2 : NTHR;
@@ -1208,6 +1225,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         }
         // ---- dz of the previous chunk (always a full one), staged in LDS by its epilogue
         if (stage_out && c > c_begin) flush_dz<NTHR, PT>(p, out16, sDz, b, h, c0 - p.C, p.C);
+        if (stage_ranks && c > c_begin) flush_ranks<NTHR, PT>(p, sDz, Cp, b, h, c0 - p.C, p.C);
 
         // ---- phase 0: token scalars, cos/sin, exp(segsum)
         phase0<RP, CT, NT, PT, true, EX>(p, it, c0, cl, smb, sr, smem, L);
@@ -1534,6 +1552,8 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                             }
                             if (p.reduce_o) {
                                 dzc[v] = fadd(dzc[v], val);
+                            } else if (stage_ranks) {
+                                sDz[(r * Cp + tb + v) * (PT + 8) + pc] = bits16(rnd(val));
                             } else if (tb + v < cl && pc < p.P && r < R) {
                                 const long oi = ((long)(b * p.S + c0 + tb + v) * R + r) * p.H * p.P + (long)h * p.P + pc;
                                 p.o[oi] = bits16(rnd(val));
@@ -1579,11 +1599,12 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
 #pragma unroll
             for (int v = 0; v < 4; ++v) asm volatile("" ::"v"(zraw[ps][v]), "v"(draw[ps][v]));
     }
-    if (stage_out) {
+    if (stage_out || stage_ranks) {
         // dz (or the layer output) of the segment's last chunk
         bar();
         const int cl_last = min(p.C, p.S - (c_end - 1) * p.C);
-        flush_dz<NTHR, PT>(p, out16, sDz, b, h, (c_end - 1) * p.C, cl_last);
+        if (stage_out) flush_dz<NTHR, PT>(p, out16, sDz, b, h, (c_end - 1) * p.C, cl_last);
+        else flush_ranks<NTHR, PT>(p, sDz, Cp, b, h, (c_end - 1) * p.C, cl_last);
     }
 
     // ---- per-segment partial sums of dmimo_o / dmimo_z: reduce over the 4 lane groups
