@@ -26,6 +26,10 @@
  *   da_cs, da_cs_rev, dt [B,H,S] fp32     trap [B,H,S] bf16
  *   d [H] fp32                     segsum [B,H,nc,C,C] fp32
  * bf16 values are passed as their 16-bit patterns (uint16_t).
+ * Alignment: dout, q, k, v, z and the bf16 outputs (states, qk_dot, dz, and o
+ * of the layer output) are read and written in 16-byte pieces and must be
+ * 16-byte aligned (MIMO_ERR_VALUE otherwise); the other pointers need their
+ * element's natural alignment, and the workspace 256 bytes.
  *
  * Branches follow the pages: mimo_o != NULL selects the reduced dout layout
  * and enables dmimo_o; z != NULL enables dz and dmimo_z (mimo_z is then
@@ -197,7 +201,8 @@ mimo_status mimo_fwd_f32(const mimo_fwd_args *args, void *stream);
  * adt, dt, trap [B,H,S] fp32; q_bias, k_bias [H,K] fp32; angles [B,S,H,A]
  * fp32 (may be NULL when A = 0); d [H] fp32. chunk_size 32 or 64; H % Hq == 0; A even and <= K/2
  * (MIMO_ERR_VALUE otherwise). K and V must be multiples of 16 up to 128 and
- * the fp32 tiles must fit the LDS (MIMO_ERR_UNSUPPORTED otherwise).
+ * the fp32 tiles must fit the LDS (MIMO_ERR_UNSUPPORTED otherwise). q, k, v, z
+ * and out must be 16-byte aligned (MIMO_ERR_VALUE otherwise).
  * Ownership, asynchrony and errors as for mimo_bwd_fwd.
  */
 #define MIMO_DTYPE_BF16 0

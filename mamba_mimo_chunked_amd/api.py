@@ -2,10 +2,11 @@
 their fp32-intermediate variants, the stage-2 backward ``mamba3_mimo_bwd_bwd`` and the SISO
 forward ``mamba3_siso_fwd``.
 
-Signature, defaults, output order, validation order and error types follow
-the Triton-Ascend mamba_mimo_bwd_fwd page (public API module: the
-``MambaMimoBwdFwdOutputs`` named tuple, ``_check_tensor`` and
-``_validate_inputs``). PyTorch supplies device memory (outputs and the
+Signature, defaults, output order and error types follow the Triton-Ascend
+mamba_mimo_bwd_fwd page (public API module: the output named tuple and the
+classes of its input errors; operator document: the input and output tables).
+The argument checks here are table-driven: one (name, shape, dtype, branch)
+entry per tensor. PyTorch supplies device memory (outputs and the
 workspace) and the current stream; every step of the computation runs in the
 HIP library behind ``include/mimo_bwd_fwd.h``.
 """
@@ -44,6 +45,7 @@ def _is_gfx950(index: int) -> bool:
 
 
 def _check_tensor(name, tensor, shape, dtype, device):
+    """One argument against its expected shape (ValueError), dtype (TypeError) and device."""
     if tuple(tensor.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {list(shape)}, got {list(tensor.shape)}")
     if tensor.dtype != dtype:
@@ -52,67 +54,165 @@ def _check_tensor(name, tensor, shape, dtype, device):
         raise ValueError(f"{name} must be on {device}, got {tensor.device}")
 
 
-def _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
-                     da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, *, fwd=False):
+_BF16, _F32 = torch.bfloat16, torch.float32
+
+# When a tensor argument must be present: always, or only on a branch.
+_ALWAYS, _IF_REDUCED, _IF_Z, _IF_D = "always", "reduced", "z", "d"
+
+
+def _sizes(q, v, chunk_size, rotary_dim_divisor, what="mamba_mimo_bwd_fwd"):
+    """The problem sizes, read from q [B,S,R,G,N] and v [B,S,H,P], after the checks
+    that need no other tensor. The order of the checks (rank of q, positive sizes,
+    q's dtype, device, architecture, then the size constraints of the operator
+    document) is the order the operator's invalid-input tests rely on."""
     if q.dim() != 5:
         raise ValueError("q must have shape [B, S, R, G, N]")
-    batch, seqlen, rank, groups, state_dim = q.shape
-    if batch < 1 or seqlen < 1 or rank < 1 or groups < 1:
+    B, S, R, G, N = (int(x) for x in q.shape)
+    if min(B, S, R, G) < 1:
         raise ValueError("B, S, R and G must be positive")
-    if q.dtype != torch.bfloat16:
+    if q.dtype != _BF16:
         raise TypeError("q, k, v, dout and trap must use torch.bfloat16")
     if q.device.type != "cuda":
-        raise ValueError("mamba_mimo_bwd_fwd requires GPU (HIP) tensors")
+        raise ValueError(f"{what} requires GPU (HIP) tensors")
     if not _is_gfx950(q.device.index if q.device.index is not None else torch.cuda.current_device()):
-        raise NotImplementedError("mamba_mimo_bwd_fwd supports gfx950 (MI355X) devices only")
-    if chunk_size < 1 or chunk_size * rank > 128:
-        raise ValueError("chunk_size * R must be in [1, 128]")
-    if rotary_dim_divisor not in (2, 4):
-        raise ValueError("rotary_dim_divisor must be 2 or 4")
-    if state_dim % rotary_dim_divisor or state_dim % 2:
-        raise ValueError("N must be even and divisible by rotary_dim_divisor")
-    if state_dim > 128:
-        raise ValueError("N greater than 128 is not supported")
-    if k.shape != q.shape:
-        raise ValueError("k must have the same shape as q")
-    if v.dim() != 4 or tuple(v.shape[:2]) != (batch, seqlen):
-        raise ValueError("v must have shape [B, S, H, P]")
-    heads, value_dim = v.shape[2:]
-    if heads % groups:
+        raise NotImplementedError(f"{what} supports gfx950 (MI355X) devices only")
+    C, rd = int(chunk_size), int(rotary_dim_divisor)
+    limits = (
+        (1 <= C and C * R <= 128, "chunk_size * R must be in [1, 128]"),
+        (rd in (2, 4), "rotary_dim_divisor must be 2 or 4"),
+        (N % 2 == 0 and N % max(rd, 1) == 0, "N must be even and divisible by rotary_dim_divisor"),
+        (N <= 128, "N greater than 128 is not supported"),
+        (v.dim() == 4 and tuple(v.shape[:2]) == (B, S), "v must have shape [B, S, H, P]"),
+    )
+    for ok, msg in limits:
+        if not ok:
+            raise ValueError(msg)
+    H, P = (int(x) for x in v.shape[2:])
+    if H % G:
         raise ValueError("H must be divisible by G")
-    if value_dim > 128:
+    if P > 128:
         raise ValueError("P greater than 128 is not supported")
+    return B, S, H, G, R, N, P, C, rd
 
-    device = q.device
-    _check_tensor("k", k, tuple(q.shape), torch.bfloat16, device)
-    _check_tensor("v", v, (batch, seqlen, heads, value_dim), torch.bfloat16, device)
-    _check_tensor("q_bias", q_bias, (heads, rank, state_dim), torch.float32, device)
-    _check_tensor("k_bias", k_bias, (heads, rank, state_dim), torch.float32, device)
-    _check_tensor("mimo_v", mimo_v, (heads, rank, value_dim), torch.float32, device)
-    _check_tensor("angles", angles, (batch, seqlen, heads, state_dim // rotary_dim_divisor),
-                  torch.float32, device)
-    for name, tensor in (("da_cs", da_cs), ("da_cs_rev", da_cs_rev), ("dt", dt)):
-        _check_tensor(name, tensor, (batch, heads, seqlen), torch.float32, device)
-    _check_tensor("trap", trap, (batch, heads, seqlen), torch.bfloat16, device)
-    nchunks = (seqlen + chunk_size - 1) // chunk_size
-    _check_tensor("segsum", segsum, (batch, heads, nchunks, chunk_size, chunk_size), torch.float32, device)
-    if d is not None:
-        _check_tensor("d", d, (heads,), torch.float32, device)
-    if mimo_o is not None:
-        _check_tensor("mimo_o", mimo_o, (heads, rank, value_dim), torch.float32, device)
-    if not fwd:
-        if mimo_o is not None:
-            _check_tensor("dout", dout, (batch, seqlen, heads, value_dim), torch.bfloat16, device)
-        else:
-            _check_tensor("dout", dout, (batch, seqlen, rank, heads, value_dim), torch.bfloat16, device)
-    if z is None:
-        if mimo_z is not None:
-            raise ValueError("mimo_z must be None when z is None")
-    else:
-        _check_tensor("z", z, (batch, seqlen, heads, value_dim), torch.bfloat16, device)
-        if mimo_z is None:
-            raise ValueError("mimo_z is required when z is present")
-        _check_tensor("mimo_z", mimo_z, (heads, rank, value_dim), torch.float32, device)
+
+def _input_table(B, S, H, G, R, N, P, C, rd, *, reduce_o, with_dout):
+    """(name, expected shape, dtype, when present) of every tensor input but q."""
+    nc = (S + C - 1) // C
+    dout_shape = (B, S, H, P) if reduce_o else (B, S, R, H, P)
+    table = [
+        ("k", (B, S, R, G, N), _BF16, _ALWAYS),
+        ("v", (B, S, H, P), _BF16, _ALWAYS),
+        ("q_bias", (H, R, N), _F32, _ALWAYS),
+        ("k_bias", (H, R, N), _F32, _ALWAYS),
+        ("mimo_v", (H, R, P), _F32, _ALWAYS),
+        ("angles", (B, S, H, N // rd), _F32, _ALWAYS),
+        ("da_cs", (B, H, S), _F32, _ALWAYS),
+        ("da_cs_rev", (B, H, S), _F32, _ALWAYS),
+        ("dt", (B, H, S), _F32, _ALWAYS),
+        ("trap", (B, H, S), _BF16, _ALWAYS),
+        ("segsum", (B, H, nc, C, C), _F32, _ALWAYS),
+        ("d", (H,), _F32, _IF_D),
+        ("mimo_o", (H, R, P), _F32, _IF_REDUCED),
+        ("z", (B, S, H, P), _BF16, _IF_Z),
+        ("mimo_z", (H, R, P), _F32, _IF_Z),
+    ]
+    if with_dout:
+        table.append(("dout", dout_shape, _BF16, _ALWAYS))
+    return table
+
+
+def _check_table(table, values: dict, device):
+    for name, shape, dtype, when in table:
+        x = values.get(name)
+        if x is None:
+            if when == _ALWAYS:
+                raise ValueError(f"{name} is required")
+            continue
+        _check_tensor(name, x, shape, dtype, device)
+
+
+def _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
+                     da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, *, fwd=False):
+    """Check every argument of the backward first stage (or, with ``fwd``, of the
+    layer output, which takes no dout); returns the problem sizes."""
+    dims = _sizes(q, v, chunk_size, rotary_dim_divisor)
+    if (z is None) != (mimo_z is None):
+        raise ValueError("z and mimo_z must either both be present or both be None")
+    values = dict(dout=dout, k=k, v=v, q_bias=q_bias, k_bias=k_bias, mimo_v=mimo_v, mimo_o=mimo_o,
+                  z=z, mimo_z=mimo_z, angles=angles, da_cs=da_cs, da_cs_rev=da_cs_rev, dt=dt,
+                  trap=trap, d=d, segsum=segsum)
+    _check_table(_input_table(*dims, reduce_o=mimo_o is not None, with_dout=not fwd), values, q.device)
+    return dims
+
+
+def _output_table(B, S, H, G, R, N, P, C, rd, *, reduce_o, has_z):
+    """(name, shape, dtype, present) of the backward first stage's outputs."""
+    nc = (S + C - 1) // C
+    return (
+        ("dmimo_o", (B, H, R, P), _F32, reduce_o),
+        ("states", (B, H, nc, N, P), _BF16, True),
+        ("dz", (B, S, H, P), _BF16, has_z),
+        ("dmimo_z", (B, H, R, P), _F32, has_z),
+        ("qk_dot", (B, H, S, R, R), _BF16, True),
+    )
+
+
+def _check_output(name, x, shape, dtype, device):
+    """A caller-supplied output: the library writes it in place, rows of eight bf16
+    at a time, so it must be dense and 16-byte aligned."""
+    _check_tensor(name, x, shape, dtype, device)
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if x.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
+
+
+def _outputs(table, out: Optional[dict], device) -> dict:
+    """The output tensors: allocated here, or the caller's, checked against the table."""
+    if out is None:
+        return {name: (torch.empty(shape, dtype=dtype, device=device) if present else None)
+                for name, shape, dtype, present in table}
+    unknown = set(out) - {name for name, *_ in table}
+    if unknown:
+        raise ValueError(f"out has unknown keys {sorted(unknown)}")
+    res = {}
+    for name, shape, dtype, present in table:
+        x = out.get(name)
+        if not present:
+            if x is not None:
+                raise ValueError(f"out[{name!r}] must be None on this branch")
+            res[name] = None
+            continue
+        if x is None:
+            raise ValueError(f"out[{name!r}] is required")
+        _check_output(f"out[{name!r}]", x, shape, dtype, device)
+        res[name] = x
+    return res
+
+
+def _workspace(workspace: Optional[Tensor], need: int, device) -> Optional[Tensor]:
+    """A caller's workspace (uint8, dense, on the device, at least ``need`` bytes) or a new one."""
+    if need == 0:
+        return workspace
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8:
+        raise TypeError(f"workspace must have dtype torch.uint8, got {workspace.dtype}")
+    if workspace.device != device:
+        raise ValueError(f"workspace must be on {device}, got {workspace.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if workspace.numel() < need:
+        raise ValueError(f"workspace too small: need {need} bytes, got {workspace.numel()}")
+    return workspace
+
+
+def _aligned(x: Optional[Tensor]) -> Optional[Tensor]:
+    """Contiguous and 16-byte aligned (a copy when a view starts inside a row)."""
+    if x is None:
+        return None
+    x = x.contiguous()
+    return x if x.data_ptr() % 16 == 0 else x.clone()
 
 
 def _ptr(t):
@@ -191,36 +291,24 @@ def mamba_mimo_bwd_fwd_fp32(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mi
 
 def _bwd_fwd(fn, dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, da_cs_rev,
              dt, trap, d, segsum, chunk_size, rotary_dim_divisor, out, workspace):
-    _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
-                     da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor)
+    dims = _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
+                            da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor)
+    B, S, H, G, R, N, P, C, rd = dims
     L = _lib.lib()
-    B, S, R, G, N = q.shape
-    H, P = v.shape[2:]
-    C = int(chunk_size)
-    nc = (S + C - 1) // C
     dev = q.device
-    t = {name: (None if x is None else x.contiguous()) for name, x in (
+    t = {name: _aligned(x) for name, x in (
         ("dout", dout), ("q", q), ("k", k), ("v", v), ("q_bias", q_bias), ("k_bias", k_bias),
         ("mimo_v", mimo_v), ("mimo_o", mimo_o), ("z", z), ("mimo_z", mimo_z), ("angles", angles),
         ("da_cs", da_cs), ("da_cs_rev", da_cs_rev), ("dt", dt), ("trap", trap), ("d", d),
         ("segsum", segsum))}
-    reduce_o, has_z = mimo_o is not None, z is not None
-    if out is None:
-        out = {
-            "dmimo_o": torch.empty((B, H, R, P), dtype=torch.float32, device=dev) if reduce_o else None,
-            "states": torch.empty((B, H, nc, N, P), dtype=torch.bfloat16, device=dev),
-            "dz": torch.empty((B, S, H, P), dtype=torch.bfloat16, device=dev) if has_z else None,
-            "dmimo_z": torch.empty((B, H, R, P), dtype=torch.float32, device=dev) if has_z else None,
-            "qk_dot": torch.empty((B, H, S, R, R), dtype=torch.bfloat16, device=dev),
-        }
-    args = _make_args(B, S, H, G, R, N, P, C, int(rotary_dim_divisor), t, out)
+    out = _outputs(_output_table(*dims, reduce_o=mimo_o is not None, has_z=z is not None), out, dev)
+    args = _make_args(B, S, H, G, R, N, P, C, rd, t, out)
     need = ctypes.c_size_t(0)
     st = getattr(L, fn + "_workspace_size")(ctypes.byref(args), ctypes.byref(need))
     if st != _lib.MIMO_OK:
         _raise(st)
+    workspace = _workspace(workspace, int(need.value), dev)
     if need.value > 0:
-        if workspace is None or workspace.numel() < need.value:
-            workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
         args.workspace = workspace.data_ptr()
         args.workspace_bytes = workspace.numel()
     with torch.cuda.device(dev):
@@ -286,31 +374,26 @@ def mamba_mimo_fwd_fp32(q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angl
 
 def _fwd(fn, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, da_cs_rev, dt, trap, d,
          segsum, chunk_size, rotary_dim_divisor, out, workspace):
-    _validate_inputs(None, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
-                     da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, fwd=True)
+    dims = _validate_inputs(None, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
+                            da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, fwd=True)
+    B, S, H, G, R, N, P, C, rd = dims
     L = _lib.lib()
-    B, S, R, G, N = q.shape
-    H, P = v.shape[2:]
-    C = int(chunk_size)
     dev = q.device
     vals = (q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, da_cs_rev, dt, trap, d,
             segsum)
-    t = {name: (None if x is None else x.contiguous()) for name, x in zip(_FWD_INPUTS, vals)}
+    t = {name: _aligned(x) for name, x in zip(_FWD_INPUTS, vals)}
     shape = (B, S, H, P) if mimo_o is not None else (B, S, R, H, P)
     if out is None:
         out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
     else:
-        _check_tensor("out", out, shape, torch.bfloat16, dev)
-        if not out.is_contiguous():
-            raise ValueError("out must be contiguous")
-    args = _make_fwd_args(B, S, H, G, R, N, P, C, int(rotary_dim_divisor), t, out)
+        _check_output("out", out, shape, torch.bfloat16, dev)
+    args = _make_fwd_args(B, S, H, G, R, N, P, C, rd, t, out)
     need = ctypes.c_size_t(0)
     st = getattr(L, fn + "_workspace_size")(ctypes.byref(args), ctypes.byref(need))
     if st != _lib.MIMO_OK:
         _raise(st)
+    workspace = _workspace(workspace, int(need.value), dev)
     if need.value > 0:
-        if workspace is None or workspace.numel() < need.value:
-            workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
         args.workspace = workspace.data_ptr()
         args.workspace_bytes = workspace.numel()
     with torch.cuda.device(dev):
@@ -391,21 +474,18 @@ def mamba3_siso_fwd(q, k, v, adt, dt, trap, q_bias, k_bias, angles, d=None, z=No
     L = _lib.lib()
     dev = q.device
     vals = (q, k, v, adt, dt, trap, q_bias, k_bias, angles, d, z)
-    t = {n: (None if x is None else x.contiguous()) for n, x in zip(_SISO_INPUTS, vals)}
+    t = {n: _aligned(x) for n, x in zip(_SISO_INPUTS, vals)}
     if out is None:
         out = torch.empty((B, S, H, V), dtype=q.dtype, device=dev)
     else:
-        _check_tensor("out", out, (B, S, H, V), q.dtype, dev)
-        if not out.is_contiguous():
-            raise ValueError("out must be contiguous")
+        _check_output("out", out, (B, S, H, V), q.dtype, dev)
     args = _make_siso_args(dims + (int(chunk_size),), q.dtype, t, out)
     need = ctypes.c_size_t(0)
     st = L.mimo_siso_fwd_workspace_size(ctypes.byref(args), ctypes.byref(need))
     if st != _lib.MIMO_OK:
         _raise(st)
+    workspace = _workspace(workspace, int(need.value), dev)
     if need.value > 0:
-        if workspace is None or workspace.numel() < need.value:
-            workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
         args.workspace = workspace.data_ptr()
         args.workspace_bytes = workspace.numel()
     with torch.cuda.device(dev):
@@ -424,12 +504,6 @@ _BWD2_INPUTS = ("dout", "q", "k", "v", "q_bias", "k_bias", "mimo_v", "states", "
 _BWD2_OUT_FIELDS = {"DQ": "dq", "DK": "dk", "DV": "dv", "DMIMO_V": "dmimo_v", "DANGLES": "dangles",
                     "DFACTOR": "dfactor", "DGAMMA": "dgamma", "DDA": "dda", "DSSDA": "dssda",
                     "DDA_CS_REV": "dda_cs_rev", "DDA_CS": "dda_cs", "DD": "dd"}
-
-
-def _aligned(x: Tensor) -> Tensor:
-    """Contiguous and 16-byte aligned (a copy when a view starts inside a row)."""
-    x = x.contiguous()
-    return x if x.data_ptr() % 16 == 0 else x.clone()
 
 
 def _make_bwd2_args(dims, C, rd, out_f32, t: dict, outs: dict, workspace=None, ws_bytes=0):
@@ -457,11 +531,9 @@ def mamba3_mimo_bwd_bwd(dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, d
     [B, S*R, H, N] and DV take q's dtype (bf16) unless ``output_dtype=torch.float32``;
     the others are float32; DD is None without ``d``. Asynchronous on the current
     HIP stream."""
-    _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, None, None, angles, da_cs, da_cs_rev,
-                     dt, trap, d, segsum, chunk_size, rotary_dim_divisor)
-    B, S, R, G, N = q.shape
-    H, P = v.shape[2:]
-    C = int(chunk_size)
+    B, S, H, G, R, N, P, C, rd = _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, None, None,
+                                                  angles, da_cs, da_cs_rev, dt, trap, d, segsum, chunk_size,
+                                                  rotary_dim_divisor)
     nc = (S + C - 1) // C
     dev = q.device
     _check_tensor("states", states, (B, H, nc, N, P), torch.bfloat16, dev)
@@ -473,7 +545,7 @@ def mamba3_mimo_bwd_bwd(dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, d
     L = _lib.lib()
     vals = (dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, da_cs, da_cs_rev, dt, trap, segsum, angles,
             mimo_o, d)
-    t = {n: (None if x is None else _aligned(x)) for n, x in zip(_BWD2_INPUTS, vals)}
+    t = {n: _aligned(x) for n, x in zip(_BWD2_INPUTS, vals)}
     f32 = torch.float32
     W = N // rotary_dim_divisor
     outs = {
@@ -495,9 +567,8 @@ def mamba3_mimo_bwd_bwd(dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, d
     st = L.mimo_bwd_bwd_workspace_size(ctypes.byref(args), ctypes.byref(need))
     if st != _lib.MIMO_OK:
         _raise(st)
+    workspace = _workspace(workspace, int(need.value), dev)
     if need.value > 0:
-        if workspace is None or workspace.numel() < need.value:
-            workspace = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
         args.workspace = workspace.data_ptr()
         args.workspace_bytes = workspace.numel()
     with torch.cuda.device(dev):

@@ -44,6 +44,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -174,6 +175,15 @@ mimo_status fail(mimo_status s, const char* fmt, ...) {
     va_end(ap);
     g_err = buf;
     return s;
+}
+
+// The kernels move q, k, v, z and dout rows and the bf16 outputs in 16-byte
+// pieces: every such pointer must be 16-byte aligned (rows of N or P bf16 are a
+// multiple of 16 bytes, so the base alignment carries over to every row).
+mimo_status check_align16(std::initializer_list<const void*> ptrs, const char* names) {
+    for (const void* x : ptrs)
+        if (reinterpret_cast<uintptr_t>(x) % 16) return fail(MIMO_ERR_VALUE, "%s must be 16-byte aligned", names);
+    return MIMO_OK;
 }
 
 struct Plan {
@@ -460,6 +470,9 @@ mimo_status run32(const Prob32& q, Params& p, void* workspace, size_t workspace_
     Plan32 pl;
     mimo_status s = make_plan32(q, &pl);
     if (s != MIMO_OK) return s;
+    if ((s = check_align16({p.dout, p.q, p.k, p.v, p.z, p.states, p.qk_dot, p.dz, p.o},
+                           "dout, q, k, v, z, states, qk_dot, dz and o")) != MIMO_OK)
+        return s;
     if (workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && workspace == nullptr))
         return fail(MIMO_ERR_VALUE, "workspace too small: need %zu bytes, got %zu", pl.ws_bytes, workspace_bytes);
     if (pl.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255))
@@ -783,6 +796,9 @@ static mimo_status run(const mimo_bwd_fwd_args* a, uint16_t* out, void* stream, 
         if ((a->dz != nullptr) != has_z || (a->dmimo_z != nullptr) != has_z)
             return fail(MIMO_ERR_VALUE, "dz and dmimo_z must be given exactly when z is given");
     }
+    if ((s = check_align16({a->dout, a->q, a->k, a->v, a->z, a->states, a->qk_dot, a->dz, out},
+                           "dout, q, k, v, z, states, qk_dot, dz and o")) != MIMO_OK)
+        return s;
     if (a->workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && a->workspace == nullptr))
         return fail(MIMO_ERR_VALUE, "workspace too small: need %zu bytes, got %zu", pl.ws_bytes, a->workspace_bytes);
     if (pl.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(a->workspace) & 255))

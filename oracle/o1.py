@@ -10,6 +10,7 @@ multiply-add is fused behind the pages' separate fp32 rounding steps) into
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -49,6 +50,8 @@ def _load():
         lib.o1_bwd_fwd.argtypes = [i64] * 9 + [ctypes.c_int] * 4 + [dp] * 22
         lib.o1_fwd.restype = ctypes.c_int
         lib.o1_fwd.argtypes = [i64] * 9 + [ctypes.c_int] * 4 + [dp] * 18
+        lib.o1_set_skip.restype = ctypes.c_int
+        lib.o1_set_skip.argtypes = [ctypes.c_uint64]
         lib.o1_round_bf16.restype = None
         lib.o1_round_bf16.argtypes = [ctypes.POINTER(ctypes.c_float)] * 2 + [i64]
         _lib = lib
@@ -67,6 +70,32 @@ def _ptr(a):
     if a is None:
         return None
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+# The contract's bf16 rounding places of intermediate values, in the order of the
+# C enum (o1_contract.c). Each is one place the page's BF16-boundary reference
+# rounds to bf16.
+ROUNDING_SITES = (
+    "Q_BIAS", "K_BIAS", "Q0", "K0", "QK", "QROT", "KROT", "MIMO_V", "PSI",
+    "DT_G", "DT_B", "BETA", "FACTOR", "KT", "KAP", "A", "SB",
+    "DPROD", "DSUM", "DGAM", "Y", "MIMO_O", "G_IN", "G_OUT", "G_NR", "DZ",
+)
+
+
+@contextlib.contextmanager
+def skipping(*sites: str):
+    """Test hook: within the block, contract-mode runs leave out the named bf16
+    roundings (those values stay fp32). Used to show which outputs each
+    rounding reaches; never by a parity reference."""
+    mask = 0
+    for s in sites:
+        mask |= 1 << ROUNDING_SITES.index(s)
+    n = _load().o1_set_skip(mask)
+    assert n == len(ROUNDING_SITES), "rounding-place list out of step with o1_contract.c"
+    try:
+        yield
+    finally:
+        _load().o1_set_skip(0)
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -196,4 +225,15 @@ def slice_heads(inp: dict, b: int, h: int) -> dict:
     for name in ("segsum", "segsum64"):
         if name in inp and inp[name] is not None:
             out[name] = inp[name][bs, hs]
+    return out
+
+
+def slice_batch(inp: dict, b: int) -> dict:
+    """Inputs of batch b as a B=1 problem (batches are independent)."""
+    out = dict(inp)
+    bs = slice(b, b + 1)
+    for name in ("dout", "q", "k", "v", "z", "angles", "da_cs", "da_cs_rev", "dt", "trap",
+                 "segsum", "da_cs64", "da_cs_rev64", "segsum64", "da"):
+        if name in inp and inp[name] is not None:
+            out[name] = inp[name][bs]
     return out

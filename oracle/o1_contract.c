@@ -82,9 +82,25 @@ static inline double RB(double xd) {
     return (double)f;
 }
 
-/* A bf16 rounding of an intermediate value: the contract's RB, fp32 in mode 2.
- * RB itself is kept for the outputs, which are bf16 in every mode but exact. */
-static inline double RBI(double x) { return g_mode == 2 ? RF(x) : RB(x); }
+/* The contract's bf16 roundings of intermediate values, one id per place the
+ * BF16-boundary reference rounds. Tests may switch single places off (their
+ * value then stays fp32) to check which outputs each one reaches. */
+enum {
+    R_Q_BIAS, R_K_BIAS, R_Q0, R_K0, R_QK, R_QROT, R_KROT, R_MIMO_V, R_PSI,
+    R_DT_G, R_DT_B, R_BETA, R_FACTOR, R_KT, R_KAP, R_A, R_SB,
+    R_DPROD, R_DSUM, R_DGAM, R_Y, R_MIMO_O, R_G_IN, R_G_OUT, R_G_NR, R_DZ,
+    R_COUNT
+};
+static uint64_t g_skip = 0;   /* bit i set: rounding place i is left out (contract mode only) */
+
+/* A bf16 rounding of an intermediate value at place `site`: the contract's RB,
+ * fp32 in mode 2 or where the place is switched off. RB itself is kept for the
+ * outputs, which are bf16 in every mode but exact. */
+static inline double RBI_(int site, double x) {
+    if (g_mode == 2 || ((g_skip >> site) & 1u)) return RF(x);
+    return RB(x);
+}
+#define RBI(site, x) RBI_(R_##site, (x))
 
 static inline double EXP(double x) { return RF(exp(x)); }
 static inline double SIG(double x) { return RF(1.0 / (1.0 + exp(-x))); }
@@ -126,7 +142,7 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
         const int64_t cl = (S - c0 < C) ? (S - c0) : C;   /* real tokens in chunk */
 
         /* entry state of chunk c */
-        for (int64_t i = 0; i < N * P; ++i) Sb[i] = RBI(St[i]);
+        for (int64_t i = 0; i < N * P; ++i) Sb[i] = RBI(SB, St[i]);
         if (a->states) {
             double *st_out = a->states + (((b * H + h) * nc + c) * N) * P;
             for (int64_t i = 0; i < N * P; ++i) st_out[i] = RB(St[i]);
@@ -142,8 +158,8 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                 const double *kb = a->k_bias + (h * R + r) * N;
                 double *q0r = q0 + (t * R + r) * N, *k0r = k0 + (t * R + r) * N;
                 for (int64_t n = 0; n < N; ++n) {
-                    q0r[n] = RBI(RF(qs[n] + RBI(qb[n])));
-                    k0r[n] = RBI(RF(ks[n] + RBI(kb[n])));
+                    q0r[n] = RBI(Q0, RF(qs[n] + RBI(Q_BIAS, qb[n])));
+                    k0r[n] = RBI(K0, RF(ks[n] + RBI(K_BIAS, kb[n])));
                 }
             }
             /* same-token rank-by-rank dot of the biased, unrotated q and k */
@@ -152,7 +168,7 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                     double sum = 0.0;
                     const double *x = q0 + (t * R + r) * N, *w = k0 + (t * R + s2) * N;
                     for (int64_t n = 0; n < N; ++n) sum += x[n] * w[n];
-                    qk[(t * R + r) * R + s2] = RBI(RF(sum));
+                    qk[(t * R + r) * R + s2] = RBI(QK, RF(sum));
                     if (a->qk_dot) a->qk_dot[(((b * H + h) * S + T) * R + r) * R + s2] = RB(RF(sum));
                 }
             /* partial rotate-half: columns [0,W) pair with [M, M+W) */
@@ -163,33 +179,33 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                 for (int64_t n = 0; n < N; ++n) { qrr[n] = q0r[n]; ktr[n] = k0r[n]; }
                 for (int64_t n = 0; n < W; ++n) {
                     const double cs = RF(cos(th[n])), sn = RF(sin(th[n]));
-                    qrr[n] = RBI(RF(RF(cs * q0r[n]) - RF(sn * q0r[M + n])));
-                    qrr[M + n] = RBI(RF(RF(sn * q0r[n]) + RF(cs * q0r[M + n])));
-                    ktr[n] = RBI(RF(RF(cs * k0r[n]) - RF(sn * k0r[M + n])));
-                    ktr[M + n] = RBI(RF(RF(sn * k0r[n]) + RF(cs * k0r[M + n])));
+                    qrr[n] = RBI(QROT, RF(RF(cs * q0r[n]) - RF(sn * q0r[M + n])));
+                    qrr[M + n] = RBI(QROT, RF(RF(sn * q0r[n]) + RF(cs * q0r[M + n])));
+                    ktr[n] = RBI(KROT, RF(RF(cs * k0r[n]) - RF(sn * k0r[M + n])));
+                    ktr[M + n] = RBI(KROT, RF(RF(sn * k0r[n]) + RF(cs * k0r[M + n])));
                 }
             }
             /* PsiV = v * bf16(mimo_v) */
             for (int64_t r = 0; r < R; ++r)
                 for (int64_t p = 0; p < P; ++p)
                     psi[(t * R + r) * P + p] =
-                        RBI(RF(a->v[((b * S + T) * H + h) * P + p] * RBI(a->mimo_v[(h * R + r) * P + p])));
+                        RBI(PSI, RF(a->v[((b * S + T) * H + h) * P + p] * RBI(MIMO_V, a->mimo_v[(h * R + r) * P + p])));
             /* trapezoidal discretisation: gamma (fp32), beta from the next token, factor (bf16) */
             const int64_t ih = (b * H + h) * S;
-            const double gamma = RF(RBI(a->dt[ih + T]) * SIG(a->trap[ih + T]));
+            const double gamma = RF(RBI(DT_G, a->dt[ih + T]) * SIG(a->trap[ih + T]));
             double beta = 0.0;
             if (T + 1 < S) {
                 const double w = g_mode == 2 ? RF(1.0 - SIG(a->trap[ih + T + 1])) : SIG(-a->trap[ih + T + 1]);
-                beta = RBI(RF(RBI(a->dt[ih + T + 1]) * w));
+                beta = RBI(BETA, RF(RBI(DT_B, a->dt[ih + T + 1]) * w));
             }
-            const double factor = RBI(RF(gamma + beta));
+            const double factor = RBI(FACTOR, RF(gamma + beta));
             gam[t] = gamma;
             const double erev = EXP(a->da_cs_rev[ih + T]);
             for (int64_t r = 0; r < R; ++r)
                 for (int64_t n = 0; n < N; ++n) {
                     double *ktr = kt + (t * R + r) * N;
-                    ktr[n] = RBI(RF(ktr[n] * factor));
-                    kap[(t * R + r) * N + n] = RBI(RF(ktr[n] * erev));
+                    ktr[n] = RBI(KT, RF(ktr[n] * factor));
+                    kap[(t * R + r) * N + n] = RBI(KAP, RF(ktr[n] * erev));
                 }
         }
 
@@ -207,7 +223,7 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                         double sum = 0.0;
                         const double *krow = kt + (j * R + s2) * N;
                         for (int64_t n = 0; n < N; ++n) sum += qrow[n] * krow[n];
-                        A[j * R + s2] = RBI(RF(RF(sum) * es));
+                        A[j * R + s2] = RBI(A, RF(RF(sum) * es));
                     }
                 }
                 for (int64_t p = 0; p < P; ++p) acc[p] = 0.0;
@@ -225,13 +241,13 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                     /* diagonal: rank-ordered bf16 products and sums, then times gamma */
                     double dg = 0.0;
                     for (int64_t s2 = 0; s2 < R; ++s2) {
-                        const double prod = RBI(RF(qk[(t * R + r) * R + s2] * psi[(t * R + s2) * P + p]));
-                        dg = RBI(RF(dg + prod));
+                        const double prod = RBI(DPROD, RF(qk[(t * R + r) * R + s2] * psi[(t * R + s2) * P + p]));
+                        dg = RBI(DSUM, RF(dg + prod));
                     }
-                    dg = RBI(RF(dg * gam[t]));
+                    dg = RBI(DGAM, RF(dg * gam[t]));
                     double o = RF(RF(inter + intra) + dg);
                     if (a->has_d) o = RF(o + RF(a->d[h] * psi[(t * R + r) * P + p]));
-                    y[(t * R + r) * P + p] = RBI(o);
+                    y[(t * R + r) * P + p] = RBI(Y, o);
                 }
             }
         }
@@ -260,7 +276,7 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                     double oacc = 0.0;
                     for (int64_t r = 0; r < R; ++r) {
                         double val = y[(t * R + r) * P + p];
-                        if (a->reduce_o) val = RF(val * RBI(a->mimo_o[(h * R + r) * P + p]));
+                        if (a->reduce_o) val = RF(val * RBI(MIMO_O, a->mimo_o[(h * R + r) * P + p]));
                         if (a->has_z) {
                             const double pz = RF(a->z[ivp] * a->mimo_z[(h * R + r) * P + p]);
                             val = RF(val * RF(pz * SIG(pz)));
@@ -294,17 +310,17 @@ static void o1_head(const o1_args *a, int64_t b, int64_t h) {
                         const double dv = a->dout[ivp];
                         if (a->has_z) {
                             dmo[r * P + p] += RF(RF(yv * silu) * dv);
-                            G = RBI(RF(RBI(RF(dv * RBI(a->mimo_o[(h * R + r) * P + p]))) * yv));
+                            G = RBI(G_OUT, RF(RBI(G_IN, RF(dv * RBI(MIMO_O, a->mimo_o[(h * R + r) * P + p]))) * yv));
                         } else {
                             dmo[r * P + p] += RF(yv * dv);
                         }
                     } else if (a->has_z) {
                         const double dv = a->dout[(((b * S + T) * R + r) * H + h) * P + p];
-                        G = RBI(RF(dv * yv));
+                        G = RBI(G_NR, RF(dv * yv));
                     }
                     if (a->has_z) {
                         const double gz = RF(RF(G * sg) * RF(1.0 + RF(pz * SIG(-pz))));
-                        dzacc = RBI(RF(dzacc + RF(gz * a->mimo_z[(h * R + r) * P + p])));
+                        dzacc = RBI(DZ, RF(dzacc + RF(gz * a->mimo_z[(h * R + r) * P + p])));
                         dmz[r * P + p] += RF(gz * a->z[ivp]);
                     }
                 }
@@ -340,6 +356,14 @@ int o1_bwd_fwd(int64_t B, int64_t S, int64_t H, int64_t G, int64_t R, int64_t N,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < nbh; ++i) o1_head(&a, i / H, i % H);
     return 0;
+}
+
+/* Test hook: leave out the bf16 roundings whose bits are set in `mask` (ids
+ * from the enum above) in later contract-mode runs; 0 restores the contract.
+ * Returns the number of rounding places. */
+int o1_set_skip(uint64_t mask) {
+    g_skip = mask;
+    return R_COUNT;
 }
 
 /* bf16 rounding exposed for the oracle's own unit tests. */

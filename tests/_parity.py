@@ -45,8 +45,50 @@ def rel_rms(actual, ref) -> float:
     return float(np.sqrt(np.mean((a - r) ** 2)) / (nr if nr > 0 else 1.0))
 
 
+def _ulp_key(x):
+    """Monotonic integer key of bf16 values held as floats (one step per bf16 ulp)."""
+    u = (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.int64)
+    mag = u & 0x7FFF
+    return np.where(u & 0x8000, -mag, mag)
+
+
+def check_elements(name, gv, r, *, bf16: bool, label=""):
+    """Element-wise bars next to the whole-tensor one, so that a few wrong
+    elements in a large tensor cannot hide under the RMS:
+    * bf16 outputs: at least 99.9 % of the elements within one bf16 ulp of the
+      oracle, and every element within 2^-6 |ref| + 2^-5 RMS(ref) (a few ulps,
+      also where a rounded chain cancels);
+    * fp32 outputs: every element within 1e-3 RMS(ref) of the oracle.
+    Returns the fraction of bf16 elements within one ulp (1.0 for fp32)."""
+    a = np.asarray(gv, np.float64)
+    r = np.asarray(r, np.float64)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    dev = np.abs(a - r)
+    if bf16:
+        within = float(np.mean(np.abs(_ulp_key(a) - _ulp_key(r)) <= 1)) if r.size else 1.0
+        assert within >= 0.999, f"{label}{name}: only {within:.5f} of the elements within 1 bf16 ulp"
+        bound = 2.0 ** -6 * np.abs(r) + 2.0 ** -5 * rms
+    else:
+        within = 1.0
+        bound = np.full(r.shape, 1e-3 * rms)
+    bad = dev > bound
+    if bad.any():
+        i = np.unravel_index(int(np.argmax(dev - bound)), r.shape)
+        raise AssertionError(f"{label}{name}: {int(bad.sum())} element(s) off, worst at {i}: "
+                             f"{a[i]!r} vs {r[i]!r}")
+    return within
+
+
+def per_head(name, x):
+    """View of an output with (batch, head) as its two leading axes."""
+    x = np.asarray(x)
+    return np.swapaxes(x, 1, 2) if name == "dz" else x   # dz is [B,S,H,P]
+
+
 def compare(gpu_out, ref_out, *, tol=TOL, label=""):
-    """Assert per-output parity; returns {name: rel_rms}."""
+    """Assert per-output parity: the stated bar (relative RMS < tol over the whole
+    tensor), the same bar on every (batch, head) slice, and the element-wise bars
+    of check_elements. Returns {name: rel_rms}."""
     errs = {}
     dtypes = (torch.float32, torch.bfloat16, torch.bfloat16, torch.float32, torch.bfloat16)
     for name, g, r, dt in zip(NAMES, gpu_out, ref_out, dtypes):
@@ -61,6 +103,12 @@ def compare(gpu_out, ref_out, *, tol=TOL, label=""):
         e = rel_rms(gv, r)
         errs[name] = e
         assert e < tol, f"{label}{name}: rel RMS {e:.3e} >= {tol}"
+        gh, rh = per_head(name, gv), per_head(name, r)
+        for b in range(rh.shape[0]):
+            for h in range(rh.shape[1]):
+                eh = rel_rms(gh[b, h], rh[b, h])
+                assert eh < tol, f"{label}{name}: rel RMS {eh:.3e} >= {tol} at batch {b}, head {h}"
+        check_elements(name, gv, r, bf16=(dt == torch.bfloat16), label=label)
     return errs
 
 

@@ -187,3 +187,84 @@ def test_invalid_q_dtype():
 def test_cpu_tensors_are_rejected():
     with pytest.raises(ValueError, match="GPU"):
         mamba_mimo_bwd_fwd(*_args())
+
+
+def _stage1_args(S=64):
+    """Stage-1 arguments with every pointer set to a fake, 256-byte aligned address:
+    enough for the checks that come before any device work."""
+    a = _lib.MimoBwdFwdArgs()
+    a.B, a.S, a.H, a.G, a.R, a.N, a.P = 1, S, 2, 1, 2, 16, 16
+    a.chunk_size, a.rotary_dim_divisor = 16, 4
+    for f, typ in _lib.MimoBwdFwdArgs._fields_:
+        if typ is ctypes.c_void_p and f not in ("workspace",):
+            setattr(a, f, 1 << 20)
+    return a
+
+
+@pytest.mark.parametrize("field", ["dout", "q", "k", "v", "z", "states", "qk_dot", "dz"])
+def test_c_call_rejects_misaligned_rows_without_a_device(field):
+    L = _lib.lib()
+    a = _stage1_args(S=16)      # one chunk: no workspace
+    setattr(a, field, (1 << 20) + 8)
+    assert L.mimo_bwd_fwd(ctypes.byref(a), None) == _lib.MIMO_ERR_VALUE
+    assert "16-byte aligned" in _lib.last_error()
+    assert L.mimo_bwd_fwd_f32(ctypes.byref(a), None) == _lib.MIMO_ERR_VALUE
+    assert "16-byte aligned" in _lib.last_error()
+
+
+def test_c_call_rejects_small_or_misaligned_workspace_without_a_device():
+    L = _lib.lib()
+    a = _stage1_args(S=300)
+    need = ctypes.c_size_t(0)
+    assert L.mimo_bwd_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need)) == _lib.MIMO_OK
+    assert need.value > 0
+    a.workspace, a.workspace_bytes = 1 << 24, need.value - 1
+    assert L.mimo_bwd_fwd(ctypes.byref(a), None) == _lib.MIMO_ERR_VALUE
+    assert "workspace too small" in _lib.last_error()
+    a.workspace, a.workspace_bytes = None, need.value
+    assert L.mimo_bwd_fwd(ctypes.byref(a), None) == _lib.MIMO_ERR_VALUE
+    assert "workspace too small" in _lib.last_error()
+    a.workspace = (1 << 24) + 128
+    assert L.mimo_bwd_fwd(ctypes.byref(a), None) == _lib.MIMO_ERR_VALUE
+    assert "256-byte aligned" in _lib.last_error()
+
+
+def test_binding_checks_caller_outputs_and_workspace():
+    """Caller-supplied outputs and workspace are checked before they reach the library
+    (CPU tensors stand in for device ones here: the checks are device-agnostic)."""
+    from mamba_mimo_chunked_amd import api
+    dev = torch.device("cpu")
+    dims = (1, 40, 2, 1, 2, 16, 16, 16, 4)   # B, S, H, G, R, N, P, C, rd
+    table = api._output_table(*dims, reduce_o=True, has_z=False)
+    good = api._outputs(table, None, dev)
+    assert good["dz"] is None and good["dmimo_z"] is None
+    assert tuple(good["states"].shape) == (1, 2, 3, 16, 16)
+    assert api._outputs(table, dict(good), dev)["qk_dot"] is good["qk_dot"]
+    bad_cases = [
+        (dict(good, states=good["states"].float()), TypeError, "dtype"),
+        (dict(good, qk_dot=good["qk_dot"][:, :1]), ValueError, "shape"),
+        (dict(good, dz=torch.empty((1, 40, 2, 16), dtype=torch.bfloat16)), ValueError, "must be None"),
+        ({k: v for k, v in good.items() if k != "states"}, ValueError, "required"),
+        (dict(good, extra=good["states"]), ValueError, "unknown keys"),
+    ]
+    st = good["states"]
+    nc_view = torch.empty((1, 2, 16, 3, 16), dtype=torch.bfloat16).transpose(2, 3)
+    bad_cases.append((dict(good, states=nc_view), ValueError, "contiguous"))
+    flat = torch.empty(st.numel() + 8, dtype=torch.bfloat16)
+    off = flat[1:1 + st.numel()].view(st.shape)       # starts 2 bytes into an allocation
+    bad_cases.append((dict(good, states=off), ValueError, "16-byte aligned"))
+    for out, exc, msg in bad_cases:
+        with pytest.raises(exc, match=msg):
+            api._outputs(table, out, dev)
+    assert api._workspace(None, 0, dev) is None
+    assert api._workspace(None, 100, dev).numel() == 100
+    with pytest.raises(TypeError, match="uint8"):
+        api._workspace(torch.empty(100, dtype=torch.float32), 100, dev)
+    with pytest.raises(ValueError, match="too small"):
+        api._workspace(torch.empty(99, dtype=torch.uint8), 100, dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        api._workspace(torch.empty((100, 2), dtype=torch.uint8).t(), 100, dev)
+    # inputs: views that start inside a row are copied to an aligned buffer
+    x = torch.arange(72, dtype=torch.float32).to(torch.bfloat16)[1:65]
+    assert x.data_ptr() % 16 and api._aligned(x).data_ptr() % 16 == 0
+    assert torch.equal(api._aligned(x), x)

@@ -121,12 +121,38 @@ def test_full_gqa_tail_nonreduced_all_heads():
     _sampled("gqa_tail_nonreduced", None)
 
 
-def test_full_wide_chunk_sampled_heads():
-    _sampled("wide_chunk_n128", [(0, 0), (1, 9), (3, 31)])
+def _one_batch(name, b, extra_heads=()):
+    """Every head of batch b (the oracle runs them in parallel), plus single
+    (batch, head) pairs of the other batches."""
+    case = CONFIGS[name]
+    log(f"[parity-full] {name}: generating inputs")
+    inp = make_inputs(case)
+    got = run_gpu(to_device(inp))
+    log(f"[parity-full] {name}: GPU done, oracle on all {case.H} heads of batch {b}")
+    ref = o1.run_inputs(o1.slice_batch(inp, b))
+    sl = tuple(None if x is None else x[b:b + 1] for x in got)
+    sl = (sl[0], sl[1], None if got.dz is None else got.dz[b:b + 1], sl[3], sl[4])
+    errs = compare(sl, ref, label=f"{name} b={b}: ")
+    log("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for bb, h in extra_heads:
+        ref = o1.run_inputs(o1.slice_heads(inp, bb, h))
+        sl = (
+            None if got.dmimo_o is None else got.dmimo_o[bb:bb + 1, h:h + 1],
+            got.states[bb:bb + 1, h:h + 1],
+            None if got.dz is None else got.dz[bb:bb + 1, :, h:h + 1],
+            None if got.dmimo_z is None else got.dmimo_z[bb:bb + 1, h:h + 1],
+            got.qk_dot[bb:bb + 1, h:h + 1],
+        )
+        errs = compare(sl, ref, label=f"{name} b={bb} h={h}: ")
+        log(f"    b={bb} h={h} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
-def test_full_max_rank_tile_sampled_heads():
-    _sampled("max_rank_tile", [(0, 0), (1, 15)])
+def test_full_wide_chunk_one_batch_all_heads():
+    _one_batch("wide_chunk_n128", 0, [(1, 9), (3, 31)])
+
+
+def test_full_max_rank_tile_one_batch_all_heads():
+    _one_batch("max_rank_tile", 1, [(0, 0)])
 
 
 # ---------------------------------------------------------------- bitwise invariants on the GPU
@@ -234,3 +260,24 @@ def test_large_angles(scale, offset):
     got = run_gpu(to_device(inp))
     errs = compare(got, ref, label=f"{case.name}: ")
     log("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+def test_offset_views_are_accepted():
+    """Inputs that are views starting inside a row (2 bytes past an aligned
+    allocation) give the same outputs as dense, aligned copies."""
+    case = Case(1, 150, 2, 1, 64, 64, 4, 16, name="offset_views")
+    inp = make_inputs(case)
+    d = to_device(inp)
+    ref = _gpu_np(run_gpu(d))
+    shifted = dict(d)
+    for n in ("dout", "q", "k", "v", "z", "trap"):
+        x = d[n]
+        buf = torch.empty(x.numel() + 8, dtype=x.dtype, device=x.device)
+        view = buf[1:1 + x.numel()].view(x.shape)
+        view.copy_(x)
+        assert view.data_ptr() % 16
+        shifted[n] = view
+    got = _gpu_np(run_gpu(shifted))
+    for i, n in enumerate(NAMES):
+        assert _same(ref[i], got[i]), n
+    compare(run_gpu(shifted), oracle(inp), label="offset views: ")
