@@ -19,6 +19,15 @@ Other operations (``--op``), each on its own workload line:
   bwd_bwd       the stage-2 backward mamba3_mimo_bwd_bwd on the same workload as
                 the first stage, fed that stage's states and qk_dot.
 
+Timing (the pages' protocol, NPU performance record of the operator document):
+``--procs`` processes (default 3) each run ``--warmup`` calls and then
+``--steps`` timed calls; an event recorded on the stream between consecutive
+calls gives each call's device time. ``value`` is this process's ms per step
+over its timed calls (bracketed by synchronisation); ``timing`` holds the
+median, per-process medians, standard deviation and range over all processes,
+and the synchronous wall time of the Python entry point with output and
+workspace allocation included.
+
 Prints progress on stderr and ONE JSON line on stdout.
 """
 
@@ -30,6 +39,8 @@ import hashlib
 import json
 import math
 import os
+import statistics
+import subprocess
 import sys
 import time
 from pathlib import Path
@@ -168,6 +179,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         evs = []
@@ -187,6 +199,44 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.hip.hipEventDestroy(e)
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def sync_api_samples(op, case, inp, dev, n, torch) -> list:
+    """Synchronous wall time of n calls of the Python entry point, each allocating its
+    outputs and workspace (the pages' timing boundary includes that allocation)."""
+    from mamba_mimo_chunked_amd import mamba_mimo_bwd_fwd, mamba_mimo_bwd_fwd_fp32, mamba_mimo_fwd
+    from synth.inputs import API_ORDER
+    d = {k: (None if inp[k] is None else inp[k].to(dev)) for k in API_ORDER}
+    if op == "fwd":
+        fn, args = mamba_mimo_fwd, [d[k] for k in API_ORDER if k != "dout"]
+    else:
+        fn = mamba_mimo_bwd_fwd_fp32 if op == "bwd_fwd_fp32" else mamba_mimo_bwd_fwd
+        args = [d[k] for k in API_ORDER]
+    for _ in range(3):
+        fn(*args, case.C, case.rd)
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(n):
+        t0 = time.perf_counter()
+        r = fn(*args, case.C, case.rd)
+        torch.cuda.synchronize()
+        out.append((time.perf_counter() - t0) * 1e3)
+        del r
+    return out
 
 
 def bwd2_bytes(c) -> int:
@@ -259,6 +309,9 @@ def main():
                     help="copy: a plain device copy of known size, for counter calibration")
     ap.add_argument("--op", choices=("bwd_fwd", "fwd", "bwd_fwd_fp32", "siso", "bwd_bwd"), default="bwd_fwd",
                     help="operation to time (default: the backward first stage)")
+    ap.add_argument("--procs", type=int, default=3,
+                    help="processes of the timing protocol (each: warm-up, then the timed calls)")
+    ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this build has no "
@@ -266,6 +319,21 @@ def main():
         sys.exit(2)
     if a.config is None:
         a.config = "siso_s8192_k128" if a.op == "siso" else "perf_s8192"
+
+    # The other processes of the timing protocol run first, one after the other, as
+    # children started before this process touches the GPU; each prints its samples.
+    child_samples = []
+    if not a.child and a.mode == "op":
+        for k in range(1, max(1, a.procs)):
+            log(f"timing process {k + 1} of {a.procs}")
+            cmd = [sys.executable, str(ROOT / "bench.py"), "--child", "--op", a.op, "--config", a.config,
+                   "--steps", str(a.steps), "--warmup", str(a.warmup), "--sets", str(a.sets)]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            sys.stderr.write(res.stderr)
+            if res.returncode != 0:
+                log(f"timing process {k + 1} failed with status {res.returncode}")
+                sys.exit(res.returncode)
+            child_samples.append(json.loads(res.stdout.strip().splitlines()[-1]))
 
     import torch
     from mamba_mimo_chunked_amd import _lib
@@ -405,18 +473,29 @@ def main():
             raise RuntimeError(_lib.last_error())
 
     log(f"{nsets} buffer sets, workspace {ws_bytes} B; warmup {a.warmup}")
+    hip = HipEvents()
+    marks = hip.create(a.steps + 1)
     for i in range(a.warmup):
         call(i)
     torch.cuda.synchronize()
+    # K timed calls bracketed by synchronisation; an event on the stream between
+    # consecutive calls gives each call's device time
     t0 = time.perf_counter()
+    hip.record(marks[0], stream)
     for i in range(a.steps):
-        call(i)
+        call(a.warmup + i)
+        hip.record(marks[i + 1], stream)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / a.steps
-    log(f"timed {a.steps} steps: {ms:.4f} ms/call")
+    samples = [hip.elapsed_ms(marks[i], marks[i + 1]) for i in range(a.steps)]
+    hip.destroy(marks)
+    log(f"timed {a.steps} steps: {ms:.4f} ms/call (median call {statistics.median(samples):.4f} ms)")
+    api_samples = sync_api_samples(op, case, inp, dev, a.steps, torch) if not (siso_op or bwd2_op) else []
+    if a.child:
+        print(json.dumps({"samples_ms": samples, "api_samples_ms": api_samples, "ms_per_step": ms}), flush=True)
+        return
 
     # per-kernel durations, HIP events recorded by the library on its stream
-    hip = HipEvents()
     evs = [hip.create(_lib.TIMED_EVENTS) for _ in range(a.steps)]
     for i in range(a.steps):
         arr = (ctypes.c_void_p * _lib.TIMED_EVENTS)(*[e.value for e in evs[i]])
@@ -439,39 +518,65 @@ def main():
 
     main_name = names[2]
     main_ms = per[main_name]
+    all_samples = [samples] + [c["samples_ms"] for c in child_samples]
+    flat = [x for ss in all_samples for x in ss]
+    call_ms = statistics.median(flat)
     hbm_gbps_main = alg_bytes / (main_ms * 1e-3) / 1e9
     alu_tops = alu_ops / (main_ms * 1e-3) / 1e12
     mfma_tflops = alg_flops / (main_ms * 1e-3) / 1e12
-    traffic = None
+    traffic, traffic_call, per_kernel_traffic = None, None, None
     tfile = TRAFFIC_FILES[op]
     if tfile.exists():
         rec = json.loads(tfile.read_text())
         if rec.get("source_sha256") == source_hash(op) and rec.get("workload") == a.config:
             traffic = rec.get("bytes_per_launch")
-    # The binding roof is the one whose ideal time is longest: elementwise ALU work at
-    # the fp32 vector peak, algorithmic bytes at the HBM peak, or the contractions at
-    # the matrix peak of the dtype they run in.
+            per_kernel_traffic = rec.get("per_kernel_bytes")
+            if per_kernel_traffic:
+                traffic_call = sum(per_kernel_traffic.values())
+    # The binding roof: HBM (algorithmic bytes at 8 TB/s) or the matrix units at the
+    # dtype the contractions run in, whichever has the longer ideal time. The
+    # elementwise ALU work of the bf16 contract is reported beside it against the
+    # issue ceiling of non-packed fp32 (packed fp32 is not used).
     roofs = {
-        "alu": (alu_ops / (ALU_PEAK_TOPS * 1e12), alu_tops, round(ALU_PEAK_TOPS, 2), "Top/s"),
         "hbm": (alg_bytes / (HBM_PEAK_GBS * 1e9), hbm_gbps_main, HBM_PEAK_GBS, "GB/s"),
         "mfma": (alg_flops / (mfma_peak * 1e12), mfma_tflops, mfma_peak, "TFLOP/s"),
     }
-    if bwd2_op:
-        # the contractions run on fp32 MFMA and its elementwise work is not counted: the
-        # compute roof is the fp32 matrix peak
-        del roofs["alu"]
     bound = max(roofs, key=lambda k: roofs[k][0])
     _, achieved, peak, unit = roofs[bound]
     roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4)}
+                "frac": round(achieved / peak, 4), "traffic": traffic}
     roofline.update({
-        "traffic": traffic, "kernel": main_name, "kernel_ms": round(main_ms, 5),
-        "algorithmic_alu_ops_per_launch": alu_ops, "algorithmic_bytes_per_launch": alg_bytes,
-        "algorithmic_flops_per_launch": alg_flops, "mfma_dtype": mfma_unit_dtype,
+        "kernel": main_name, "kernel_ms": round(main_ms, 5),
+        "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": alg_flops,
+        "mfma_dtype": mfma_unit_dtype,
         "hbm_frac": round(hbm_gbps_main / HBM_PEAK_GBS, 4),
-        "alu_frac": round(alu_tops / ALU_PEAK_TOPS, 4),
-        "alu_frac_nonpacked": round(alu_tops / ALU_NONPACKED_TOPS, 4),
-        "mfma_frac": round(mfma_tflops / mfma_peak, 5)})
+        "mfma_frac": round(mfma_tflops / mfma_peak, 5),
+        "call_ms": round(call_ms, 5),
+        "call_hbm_frac": round(alg_bytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "traffic_call": traffic_call,
+        "traffic_call_ratio": None if traffic_call is None else round(traffic_call / alg_bytes, 3),
+        "traffic_per_kernel": per_kernel_traffic})
+    if alu_ops:
+        roofline["alu"] = {"ops_per_launch": alu_ops, "achieved_tops": round(alu_tops, 3),
+                           "peak_tops_nonpacked": round(ALU_NONPACKED_TOPS, 2),
+                           "frac_nonpacked": round(alu_tops / ALU_NONPACKED_TOPS, 4)}
+
+    procs = len(all_samples)
+    timing = {
+        "protocol": (f"{procs} processes x ({a.warmup} warm-up + {a.steps} timed calls); each call's device "
+                     f"time from HIP events on its stream; inputs resident, outputs preallocated"),
+        "median_ms": round(call_ms, 5),
+        "process_medians_ms": [round(statistics.median(ss), 5) for ss in all_samples],
+        "stdev_ms": round(statistics.stdev(flat), 5) if len(flat) > 1 else 0.0,
+        "min_ms": round(min(flat), 5), "max_ms": round(max(flat), 5), "samples": len(flat),
+    }
+    api_all = [api_samples] + [c["api_samples_ms"] for c in child_samples]
+    api_flat = [x for ss in api_all for x in ss]
+    if api_flat:
+        timing["sync_api_median_ms"] = round(statistics.median(api_flat), 5)
+        timing["sync_api_process_medians_ms"] = [round(statistics.median(ss), 5) for ss in api_all if ss]
+        timing["sync_api_note"] = ("synchronous wall time of the Python entry point per call: output and "
+                                   "workspace allocation, argument checks, launch, completion")
 
     cpu = None
     if not a.no_cpu:
@@ -498,8 +603,21 @@ def main():
             o1.run_inputs(inp, fp32=op == "bwd_fwd_fp32")
         cpu_ms = (time.perf_counter() - t) * 1e3 * scale
         cores = torch.get_num_threads() if bwd2_op else min(threads, case.B * case.H)
-        cpu = {"value": round(cpu_ms, 3), "unit": "ms/call", "cores": cores, "kind": "oracle", "sample": sample}
+        cpu = {"value": round(cpu_ms, 3), "unit": "ms/call", "cores": cores, "kind": "oracle", "sample": sample,
+               "cpu_model": cpu_model(), "host_threads": os.cpu_count()}
         log(f"oracle: {cpu_ms:.1f} ms")
+        if op in ("bwd_fwd", "fwd", "bwd_fwd_fp32"):
+            # one (batch, head) pair runs on one thread; scaled to the workload
+            sl = o1.slice_heads(inp, 0, 0)
+            t = time.perf_counter()
+            if op == "fwd":
+                o1.run_fwd_inputs(sl)
+            else:
+                o1.run_inputs(sl, fp32=op == "bwd_fwd_fp32")
+            one = (time.perf_counter() - t) * 1e3
+            cpu["single_thread"] = {"value": round(one * case.B * case.H, 3), "unit": "ms/call",
+                                    "sample": f"(batch 0, head 0) on one thread, scaled by {case.B * case.H}"}
+            log(f"oracle, one thread: {one:.1f} ms per head")
 
     gbps = alg_bytes / (ms * 1e-3) / 1e9
     metric = {"bwd_fwd": METRIC, "fwd": FWD_METRIC, "bwd_fwd_fp32": FP32_METRIC, "siso": SISO_METRIC,
@@ -532,6 +650,7 @@ def main():
         "hbm_gbps": round(gbps, 2),
         "hbm_frac": round(gbps / HBM_PEAK_GBS, 4),
         "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
+        "timing": timing,
         "config": config,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -147,10 +147,12 @@ def _one_batch(name, b, extra_heads=()):
         log(f"    b={bb} h={h} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
+@pytest.mark.timeout(600)
 def test_full_wide_chunk_one_batch_all_heads():
     _one_batch("wide_chunk_n128", 0, [(1, 9), (3, 31)])
 
 
+@pytest.mark.timeout(600)
 def test_full_max_rank_tile_one_batch_all_heads():
     _one_batch("max_rank_tile", 1, [(0, 0)])
 
