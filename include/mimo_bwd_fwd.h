@@ -120,6 +120,21 @@ mimo_status mimo_bwd_fwd(const mimo_bwd_fwd_args *args, void *stream);
 #define MIMO_TIMED_EVENTS 5
 mimo_status mimo_bwd_fwd_timed(const mimo_bwd_fwd_args *args, void *stream, void *const *events);
 
+/* mimo_bwd_fwd without any allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same operation, arguments, layouts, ownership and errors as
+ * mimo_bwd_fwd, except that args->workspace and args->workspace_bytes are
+ * ignored: the scratch lives in a fixed device array of
+ * MIMO_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends. A call whose workspace (mimo_bwd_fwd_workspace_size)
+ * would exceed it returns MIMO_ERR_UNSUPPORTED and queues nothing. The array
+ * is shared by every call on a device and keeps the last call's contents (no
+ * call relies on them): calls that overlap on one device, from other streams
+ * or threads, race on it and must be serialised by the caller. The call itself
+ * allocates nothing and never calls hipMalloc or hipFree. */
+#define MIMO_NOALLOC_SCRATCH_BYTES (64u << 20)
+mimo_status mimo_bwd_fwd_noalloc(const mimo_bwd_fwd_args *args, void *stream);
+
 /*
  * Layer output of the same chunked MIMO scan: the forward whose gradients the
  * backward's gating branches compute (Triton-Ascend mamba_mimo_bwd_fwd pull

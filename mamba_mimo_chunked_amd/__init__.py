@@ -11,9 +11,10 @@ package only marshals arguments.
 """
 
 from .api import (MambaMimoBwdFwdOutputs, fwd_workspace_size, mamba3_mimo_bwd_bwd, mamba3_siso_fwd,
-                  mamba_mimo_bwd_fwd, mamba_mimo_bwd_fwd_fp32, mamba_mimo_fwd, mamba_mimo_fwd_fp32,
-                  workspace_size)
+                  mamba_mimo_bwd_fwd, mamba_mimo_bwd_fwd_fp32, mamba_mimo_bwd_fwd_noalloc, mamba_mimo_fwd,
+                  mamba_mimo_fwd_fp32, workspace_size)
 
-__all__ = ["MambaMimoBwdFwdOutputs", "mamba_mimo_bwd_fwd", "mamba_mimo_fwd", "mamba_mimo_bwd_fwd_fp32",
+__all__ = ["MambaMimoBwdFwdOutputs", "mamba_mimo_bwd_fwd", "mamba_mimo_bwd_fwd_noalloc", "mamba_mimo_fwd",
+           "mamba_mimo_bwd_fwd_fp32",
            "mamba_mimo_fwd_fp32", "mamba3_mimo_bwd_bwd", "mamba3_siso_fwd", "workspace_size",
            "fwd_workspace_size"]

@@ -118,7 +118,9 @@ EXPORTED = ("mimo_bwd_fwd", "mimo_bwd_fwd_timed", "mimo_bwd_fwd_workspace_size",
             "mimo_fwd_timed", "mimo_fwd_workspace_size", "mimo_bwd_fwd_f32", "mimo_bwd_fwd_f32_timed",
             "mimo_bwd_fwd_f32_workspace_size", "mimo_fwd_f32", "mimo_fwd_f32_workspace_size",
             "mimo_siso_fwd", "mimo_siso_fwd_timed", "mimo_siso_fwd_workspace_size", "mimo_bwd_bwd",
-            "mimo_bwd_bwd_timed", "mimo_bwd_bwd_workspace_size", "mimo_last_error", "mimo_abi_version")
+            "mimo_bwd_bwd_timed", "mimo_bwd_bwd_workspace_size", "mimo_last_error", "mimo_abi_version",
+            "mimo_bwd_fwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 TIMED_EVENTS = 5
 
 _lib = None
@@ -140,6 +142,8 @@ def lib():
         L.mimo_bwd_fwd_timed.restype = ctypes.c_int
         L.mimo_bwd_fwd_workspace_size.argtypes = [argp, ctypes.POINTER(ctypes.c_size_t)]
         L.mimo_bwd_fwd_workspace_size.restype = ctypes.c_int
+        L.mimo_bwd_fwd_noalloc.argtypes = [argp, ctypes.c_void_p]
+        L.mimo_bwd_fwd_noalloc.restype = ctypes.c_int
         fargp = ctypes.POINTER(MimoFwdArgs)
         L.mimo_fwd.argtypes = [fargp, ctypes.c_void_p]
         L.mimo_fwd.restype = ctypes.c_int

@@ -21,7 +21,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["MambaMimoBwdFwdOutputs", "mamba_mimo_bwd_fwd", "mamba_mimo_fwd", "mamba_mimo_bwd_fwd_fp32",
+__all__ = ["MambaMimoBwdFwdOutputs", "mamba_mimo_bwd_fwd", "mamba_mimo_bwd_fwd_noalloc", "mamba_mimo_fwd", "mamba_mimo_bwd_fwd_fp32",
            "mamba_mimo_fwd_fp32", "mamba3_mimo_bwd_bwd", "mamba3_siso_fwd", "workspace_size",
            "fwd_workspace_size"]
 
@@ -289,6 +289,17 @@ def mamba_mimo_bwd_fwd_fp32(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mi
                     workspace)
 
 
+def mamba_mimo_bwd_fwd_noalloc(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
+                               da_cs_rev, dt, trap, d, segsum, chunk_size: int = 16,
+                               rotary_dim_divisor: int = 4, *, out: Optional[dict] = None) -> MambaMimoBwdFwdOutputs:
+    """``mamba_mimo_bwd_fwd`` through the library's entry point that allocates nothing
+    (``mimo_bwd_fwd_noalloc``): its scratch is a fixed device array inside the library,
+    shared by every call on the device, so calls on one device must not overlap.
+    Pass ``out`` to allocate nothing on this side either."""
+    return _bwd_fwd("mimo_bwd_fwd_noalloc", dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles,
+                    da_cs, da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, out, None)
+
+
 def _bwd_fwd(fn, dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs, da_cs_rev,
              dt, trap, d, segsum, chunk_size, rotary_dim_divisor, out, workspace):
     dims = _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
@@ -303,14 +314,15 @@ def _bwd_fwd(fn, dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angle
         ("segsum", segsum))}
     out = _outputs(_output_table(*dims, reduce_o=mimo_o is not None, has_z=z is not None), out, dev)
     args = _make_args(B, S, H, G, R, N, P, C, rd, t, out)
-    need = ctypes.c_size_t(0)
-    st = getattr(L, fn + "_workspace_size")(ctypes.byref(args), ctypes.byref(need))
-    if st != _lib.MIMO_OK:
-        _raise(st)
-    workspace = _workspace(workspace, int(need.value), dev)
-    if need.value > 0:
-        args.workspace = workspace.data_ptr()
-        args.workspace_bytes = workspace.numel()
+    if not fn.endswith("_noalloc"):
+        need = ctypes.c_size_t(0)
+        st = getattr(L, fn + "_workspace_size")(ctypes.byref(args), ctypes.byref(need))
+        if st != _lib.MIMO_OK:
+            _raise(st)
+        workspace = _workspace(workspace, int(need.value), dev)
+        if need.value > 0:
+            args.workspace = workspace.data_ptr()
+            args.workspace_bytes = workspace.numel()
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = getattr(L, fn)(ctypes.byref(args), ctypes.c_void_p(stream))

@@ -759,6 +759,33 @@ mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events
     return MIMO_OK;
 }
 
+// ---------------------------------------------------------------- fixed scratch
+// The entry point that allocates nothing keeps the workspace (segment increments,
+// decays, dmimo partials) in this array. Every device the library runs on holds its
+// own copy until the process ends. In host code the array's name is only a
+// stand-in: the device address comes from hipGetSymbolAddress, per device, with
+// that device current, and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[MIMO_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];   // device address of `scratch` on device i (nullptr: not looked up yet)
+
+mimo_status scratch_on_current_device(void** ptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MIMO_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= 64) return fail(MIMO_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(MIMO_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MIMO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -881,6 +908,26 @@ mimo_status mimo_bwd_fwd(const mimo_bwd_fwd_args* a, void* stream) { return run(
 mimo_status mimo_bwd_fwd_timed(const mimo_bwd_fwd_args* a, void* stream, void* const* events) {
     if (events == nullptr) return fail(MIMO_ERR_VALUE, "events must not be NULL");
     return run(a, nullptr, stream, events);
+}
+
+mimo_status mimo_bwd_fwd_noalloc(const mimo_bwd_fwd_args* a, void* stream) {
+    g_err.clear();
+    Plan pl;
+    mimo_status s = make_plan(a, &pl);
+    if (s != MIMO_OK) return s;
+    if (pl.ws_bytes > MIMO_NOALLOC_SCRATCH_BYTES)
+        return fail(MIMO_ERR_UNSUPPORTED,
+                    "this call needs %zu bytes of scratch; the fixed scratch of mimo_bwd_fwd_noalloc holds %zu "
+                    "(use mimo_bwd_fwd with a workspace)",
+                    pl.ws_bytes, (size_t)MIMO_NOALLOC_SCRATCH_BYTES);
+    mimo_bwd_fwd_args b = *a;
+    b.workspace = nullptr;
+    b.workspace_bytes = 0;
+    if (pl.ws_bytes > 0) {
+        if ((s = scratch_on_current_device(&b.workspace)) != MIMO_OK) return s;
+        b.workspace_bytes = MIMO_NOALLOC_SCRATCH_BYTES;
+    }
+    return run(&b, nullptr, stream, nullptr);
 }
 
 mimo_status mimo_fwd_workspace_size(const mimo_fwd_args* args, size_t* bytes) {

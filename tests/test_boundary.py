@@ -268,3 +268,18 @@ def test_binding_checks_caller_outputs_and_workspace():
     x = torch.arange(72, dtype=torch.float32).to(torch.bfloat16)[1:65]
     assert x.data_ptr() % 16 and api._aligned(x).data_ptr() % 16 == 0
     assert torch.equal(api._aligned(x), x)
+
+
+def test_noalloc_refuses_calls_beyond_its_scratch_without_a_device():
+    """The no-allocation entry point checks the call's workspace against its fixed
+    scratch before any device work."""
+    L = _lib.lib()
+    a = _stage1_args(S=30000)      # the planner's 512 workgroups leave 71 MB of segment state here
+    a.B, a.H, a.G, a.R, a.N, a.P = 1, 6, 1, 8, 128, 128
+    need = ctypes.c_size_t(0)
+    assert L.mimo_bwd_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need)) == _lib.MIMO_OK
+    assert need.value > _lib.NOALLOC_SCRATCH_BYTES
+    assert L.mimo_bwd_fwd_noalloc(ctypes.byref(a), None) == _lib.MIMO_ERR_UNSUPPORTED
+    assert "fixed scratch" in _lib.last_error()
+    a.chunk_size = 0
+    assert L.mimo_bwd_fwd_noalloc(ctypes.byref(a), None) == _lib.MIMO_ERR_VALUE
