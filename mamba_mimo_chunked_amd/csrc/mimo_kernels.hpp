@@ -1528,17 +1528,29 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                 float dzc[4] = {0.f, 0.f, 0.f, 0.f};   // dz chain, or the layer output's rank sum
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
-                    // diagonal: rank-ordered chain of bf16 products and bf16 sums, times gamma
-                    float y[4];
+                    // diagonal: rank-ordered chain of bf16 products and bf16 sums, times gamma.
+                    // The four tokens' chains advance together, one rank at a time, so that
+                    // consecutive instructions are independent (a lone wave then issues at
+                    // full rate); the operations of each chain are unchanged.
+                    float qkv[4][RP], dg[4], y[4];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float* qk = sQK + (tb + v) * QKS + r * RP;
-                        float dg = rnd(qk[0] * psi[0][v]);
+                    for (int v = 0; v < 4; ++v)
 #pragma unroll
-                        for (int r2 = 1; r2 < RP; ++r2) dg = rnd(dg + rnd(qk[r2] * psi[r2][v]));
-                        dg = rnd(dg * gam4[v]);
-                        y[v] = rnd(__fmaf_rn(dval, psi[r][v], fadd(acc[ps][r][v], dg)));
+                        for (int r2 = 0; r2 < RP; ++r2) qkv[v][r2] = sQK[(tb + v) * QKS + r * RP + r2];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) dg[v] = rnd(qkv[v][0] * psi[0][v]);
+#pragma unroll
+                    for (int r2 = 1; r2 < RP; ++r2) {
+                        float pr[4];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) pr[v] = rnd(qkv[v][r2] * psi[r2][v]);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) dg[v] = rnd(dg[v] + pr[v]);
                     }
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) dg[v] = rnd(dg[v] * gam4[v]);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) y[v] = rnd(__fmaf_rn(dval, psi[r][v], fadd(acc[ps][r][v], dg[v])));
                     if (p.fwd) {
                         // layer output: (y * bf16(mimo_o)) * silu(pz), summed over ranks in
                         // rank order (reduced) or stored per rank
@@ -1560,25 +1572,35 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                             }
                         }
                     } else if (p.has_z) {
+                        // gating, again the four tokens side by side; the dmimo sums keep
+                        // their token order
+                        float pz[4], sg[4], G[4], gz[4];
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const float pz = zr[v] * cz[ps][r];
-                            const float sg = sigmoid_fast(pz);
-                            float G;
-                            if (p.reduce_o) {
-                                dmo[ps][r] = __fmaf_rn(fmul(y[v], fmul(pz, sg)), dr[v], dmo[ps][r]);
-                                G = rnd(rnd(dr[v] * co[ps][r]) * y[v]);
-                            } else {
+                        for (int v = 0; v < 4; ++v) pz[v] = zr[v] * cz[ps][r];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) sg[v] = sigmoid_fast(pz[v]);
+                        if (p.reduce_o) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) G[v] = rnd(rnd(dr[v] * co[ps][r]) * y[v]);
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                dmo[ps][r] = __fmaf_rn(fmul(y[v], fmul(pz[v], sg[v])), dr[v], dmo[ps][r]);
+                        } else {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
                                 // per-rank dout [B,S,R,H,P]; lanes without a token read element 0
                                 const bool okr = tb + v < cl && pc < p.P && r < R;
                                 const long nb = ((long)(b * p.S + c0) * R + r) * p.H * p.P + (long)h * p.P;
                                 const unsigned short raw = p.dout[okr ? nb + (long)(tb + v) * R * p.H * p.P + pc : 0];
-                                G = rnd((okr ? bf2f(raw) : 0.f) * y[v]);
+                                G[v] = rnd((okr ? bf2f(raw) : 0.f) * y[v]);
                             }
-                            const float gz = fmul(fmul(G, sg), __fmaf_rn(pz, 1.0f - sg, 1.0f));
-                            dzc[v] = rnd(dzc[v] + fmul(gz, cz[ps][r]));
-                            dmz[ps][r] = __fmaf_rn(gz, zr[v], dmz[ps][r]);
                         }
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) gz[v] = fmul(fmul(G[v], sg[v]), __fmaf_rn(pz[v], 1.0f - sg[v], 1.0f));
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) dzc[v] = rnd(dzc[v] + fmul(gz[v], cz[ps][r]));
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) dmz[ps][r] = __fmaf_rn(gz[v], zr[v], dmz[ps][r]);
                     } else if (p.reduce_o) {
 #pragma unroll
                         for (int v = 0; v < 4; ++v) dmo[ps][r] = __fmaf_rn(y[v], dr[v], dmo[ps][r]);
