@@ -275,11 +275,20 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl, bool fwd = false) {
     pl->L = (int)L;
     pl->nseg = (int)((pl->nc + L - 1) / L);
     if (pl->nseg > 65535) return fail(MIMO_ERR_UNSUPPORTED, "too many segments");
-    // the aggregate kernel splits each full segment into F = 2 sub-segments: it
-    // fits more workgroups per compute unit than the chunk kernel (no y path), so
-    // twice the workgroups run at once; a larger F costs more than it saves in
-    // the scan, which reads every sub-segment's [N,P] increment
-    pl->F = (L % 2 == 0 && L >= 4) ? 2 : 1;
+    // The aggregate kernel splits each segment but the last into F sub-segments of
+    // ceil(L / F) chunks (the last piece shorter): its chain per workgroup shortens
+    // with F while the workgroups still fit the GPU at once (about four per compute
+    // unit for four-wave tiles, two for eight-wave ones); beyond that more pieces
+    // only add scan traffic (the scan reads every sub-segment's [N,P] increment).
+    {
+        const int64_t slots = pl->NW == 8 ? 512 : 1024;
+        const int64_t units = (int64_t)(pl->nseg - 1) * B * H;
+        int64_t F = units > 0 ? slots / units : 1;
+        if (F > (L + 3) / 4) F = (L + 3) / 4;   // pieces of at least four chunks
+        if (F < 1) F = 1;
+        while (F > 1 && (F - 1) * ((L + F - 1) / F) >= L) --F;   // every piece non-empty
+        pl->F = (int)F;
+    }
     pl->nsub = (pl->nseg - 1) * pl->F;
     const bool reduce_o = a->mimo_o != nullptr, has_z = a->z != nullptr;
     size_t off = 0;

@@ -891,9 +891,12 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
     bh = uni(bh);
     const int b = uni(bh / p.H), h = uni(bh - b * p.H);
     const int g = uni(h / (p.H / p.G));
-    const int La = p.L / p.F;   // chunks per sub-segment (all full)
-    const int c_begin = seg * La;
-    const int c_end = c_begin + La;
+    // sub-segment seg is piece k of segment s; pieces hold ceil(L / F) chunks, the last
+    // one of a segment fewer (the host keeps every piece non-empty); all chunks are full
+    const int La = (p.L + p.F - 1) / p.F;
+    const int s_ = uni(seg / p.F), k_ = seg - s_ * p.F;
+    const int c_begin = s_ * p.L + k_ * La;
+    const int c_end = min(c_begin + La, s_ * p.L + p.L);
     const int R = p.R;
     // With one 8-column group per thread and rotary divisor 4, the threads of the
     // first half hold exactly the rotated groups; the second half fills Psi.
