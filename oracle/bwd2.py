@@ -106,26 +106,33 @@ def run(dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, da_cs, da_cs_rev,
     qk_exact = torch.einsum("bhtrn,bhtsn->bhtrs", Q0, K0)
     qk = qk_exact + (QKC - qk_exact).detach()
 
+    # the per-token tensors cut into chunks once: an indexed slice per chunk would make
+    # autograd build a whole-sequence gradient for every chunk (quadratic in S); the
+    # values and the derivatives are the same either way
+    def chunks(x):
+        return x.split(C, dim=2)
+
+    Qh_c, Kt_c, Psi_c, qk_c, dpo_c = chunks(Qh), chunks(Kt), chunks(Psi), chunks(qk), chunks(dphio)
+    CSI_c, CSS_c, REV_c, GAM_c = chunks(CSI), chunks(CSS), chunks(REV), chunks(GAM)
+    SEG_c = SEG.unbind(2)
     L = torch.zeros((), dtype=torch.float64)
     Srec = torch.zeros((B, H, N, P), dtype=torch.float64)
     for c in range(nc):
-        c0 = c * C
-        cl = min(C, S - c0)
-        sl = slice(c0, c0 + cl)
+        cl = Qh_c[c].shape[2]
         Sused = Srec + (SC[:, :, c] - Srec).detach()
-        inter = torch.einsum("bhtrn,bhnp->bhtrp", Qh[:, :, sl], Sused) * torch.exp(CSI[:, :, sl])[..., None, None]
-        scores = torch.einsum("bhtrn,bhsqn->bhtrsq", Qh[:, :, sl], Kt[:, :, sl])
+        inter = torch.einsum("bhtrn,bhnp->bhtrp", Qh_c[c], Sused) * torch.exp(CSI_c[c])[..., None, None]
+        scores = torch.einsum("bhtrn,bhsqn->bhtrsq", Qh_c[c], Kt_c[c])
         mask = torch.tril(torch.ones(cl, cl, dtype=torch.bool), diagonal=-1)
-        decay = torch.where(mask, torch.exp(torch.where(mask, SEG[:, :, c, :cl, :cl], 0.0)), 0.0)
-        intra = torch.einsum("bhtrsq,bhts,bhsqp->bhtrp", scores, decay, Psi[:, :, sl])
-        diag = GAM[:, :, sl][..., None, None] * torch.einsum("bhtrs,bhtsp->bhtrp", qk[:, :, sl], Psi[:, :, sl])
+        decay = torch.where(mask, torch.exp(torch.where(mask, SEG_c[c][:, :, :cl, :cl], 0.0)), 0.0)
+        intra = torch.einsum("bhtrsq,bhts,bhsqp->bhtrp", scores, decay, Psi_c[c])
+        diag = GAM_c[c][..., None, None] * torch.einsum("bhtrs,bhtsp->bhtrp", qk_c[c], Psi_c[c])
         y = inter + intra + diag
         if D is not None:
-            y = y + D[:, :, None, None, None] * Psi[:, :, sl]
-        L = L + (dphio[:, :, sl] * y).sum()
-        kap = Kt[:, :, sl] * torch.exp(REV[:, :, sl])[..., None, None]
-        Srec = torch.exp(CSS[:, :, c0 + cl - 1])[..., None, None] * Sused + torch.einsum(
-            "bhtrn,bhtrp->bhnp", kap, Psi[:, :, sl])
+            y = y + D[:, :, None, None, None] * Psi_c[c]
+        L = L + (dpo_c[c] * y).sum()
+        kap = Kt_c[c] * torch.exp(REV_c[c])[..., None, None]
+        Srec = torch.exp(CSS_c[c][:, :, cl - 1])[..., None, None] * Sused + torch.einsum(
+            "bhtrn,bhtrp->bhnp", kap, Psi_c[c])
     L.backward()
 
     def grad(x):
