@@ -428,14 +428,15 @@ def main():
                 outs[key] = torch.empty((B, H, S), dtype=f32, device=dev)
             sets.append((d, outs))
         dims = (B, S, H, G, R, N, P)
-        probe = _make_bwd2_args(dims, C, case.rd, False, sets[0][0], sets[0][1])
+        probe = _make_bwd2_args(dims, C, case.rd, _lib.DTYPE_BF16, _lib.DTYPE_BF16, sets[0][0], sets[0][1])
         nbytes = ctypes.c_size_t(0)
         st = L.mimo_bwd_bwd_workspace_size(ctypes.byref(probe), ctypes.byref(nbytes))
         if st != 0:
             raise RuntimeError(_lib.last_error())
         ws_bytes = int(nbytes.value)
         ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-        cargs = [_make_bwd2_args(dims, C, case.rd, False, d, o, ws, ws_bytes) for d, o in sets]
+        cargs = [_make_bwd2_args(dims, C, case.rd, _lib.DTYPE_BF16, _lib.DTYPE_BF16, d, o, ws, ws_bytes)
+                 for d, o in sets]
         run_call, run_timed = L.mimo_bwd_bwd, L.mimo_bwd_bwd_timed
     else:
         B, S, H, G, R, N, P, C = case.B, case.S, case.H, case.G, case.R, case.N, case.P, case.C

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MIMO_ABI_VERSION 1
+#define MIMO_ABI_VERSION 2
 
 typedef enum {
     MIMO_OK = 0,
@@ -222,6 +222,7 @@ mimo_status mimo_fwd_f32(const mimo_fwd_args *args, void *stream);
  */
 #define MIMO_DTYPE_BF16 0
 #define MIMO_DTYPE_FP16 1
+#define MIMO_DTYPE_FP32 2   /* stage-2 backward only */
 typedef struct mimo_siso_fwd_args {
     int64_t B, S, Hq, H, K, V;
     int32_t chunk_size;          /* 32 or 64                                           */
@@ -259,24 +260,30 @@ mimo_status mimo_siso_fwd_timed(const mimo_siso_fwd_args *args, void *stream, vo
  *   dda         [B,H,S]  da_cs at each chunk's last token in the state decay (0 elsewhere)
  *   dda_cs_rev  [B,H,S]  da_cs_rev[t] in kappa = K~ * exp(da_cs_rev[t])
  *   dssda       [B,H,nc,C,C]  segsum[c][t][s], s < t (0 elsewhere)
- * dq, dk, dv are bf16, or fp32 when out_f32 != 0; the others fp32.
- * Inputs as for mimo_bwd_fwd (dout reduced or not, bf16 q/k/v/dout/trap) plus
- * states [B,H,nc,N,P] and qk_dot [B,H,S,R,R] (bf16). Limits: R * chunk_size,
- * N and P at most 64, R at most 8, N and P multiples of 8 (MIMO_ERR_UNSUPPORTED
- * otherwise). dout, q, k, v, states, q_bias, k_bias, mimo_v, mimo_o, dq and dk
- * must be 16-byte aligned (MIMO_ERR_VALUE otherwise). Ownership, asynchrony
- * and errors as for mimo_bwd_fwd.
+ * Inputs as for mimo_bwd_fwd (dout reduced or not) plus states [B,H,nc,N,P] and
+ * qk_dot [B,H,S,R,R]. The data tensors dout, q, k, v, states, qk_dot and trap
+ * share one dtype, in_dtype: MIMO_DTYPE_BF16, MIMO_DTYPE_FP16 or MIMO_DTYPE_FP32
+ * (the migration note's supported dtypes); the other inputs are fp32. dq, dk and
+ * dv are stored in out_dtype (same choices; the page's default is the input
+ * dtype, which the binding applies); the other outputs are fp32. Limits (the
+ * migration note's range): R * chunk_size, N and P at most 128, R at most 8, N
+ * and P multiples of 8 (MIMO_ERR_UNSUPPORTED otherwise). Beyond 64 in any of
+ * them the chunk tiles are kept in the workspace (one slot per workgroup, about
+ * 608 KB each). dout, q, k, v, states, q_bias, k_bias, mimo_v, mimo_o, dq, dk
+ * and dv must be 16-byte aligned (MIMO_ERR_VALUE otherwise). Ownership,
+ * asynchrony and errors as for mimo_bwd_fwd.
  */
 typedef struct mimo_bwd_bwd_args {
     int64_t B, S, H, G, R, N, P;
     int32_t chunk_size;
     int32_t rotary_dim_divisor;
-    int32_t out_f32;
-    const uint16_t *dout, *q, *k, *v;
+    int32_t in_dtype;            /* MIMO_DTYPE_* of dout, q, k, v, states, qk_dot, trap */
+    int32_t out_dtype;           /* MIMO_DTYPE_* of dq, dk, dv                          */
+    const void *dout, *q, *k, *v;
     const float *q_bias, *k_bias, *mimo_v;
-    const uint16_t *states, *qk_dot;
+    const void *states, *qk_dot;
     const float *da_cs, *da_cs_rev, *dt;
-    const uint16_t *trap;
+    const void *trap;
     const float *segsum, *angles;
     const float *mimo_o;         /* optional: selects reduced dout                    */
     const float *d;              /* optional                                          */

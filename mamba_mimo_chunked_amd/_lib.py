@@ -13,7 +13,7 @@ from pathlib import Path
 LIB_PATH = Path(__file__).resolve().parent / "_build" / "libmimo_bwd_fwd.so"
 
 MIMO_OK, MIMO_ERR_VALUE, MIMO_ERR_TYPE, MIMO_ERR_UNSUPPORTED, MIMO_ERR_HIP = range(5)
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _f32p = ctypes.POINTER(ctypes.c_float)
@@ -93,7 +93,8 @@ class MimoBwdBwdArgs(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int64), ("S", ctypes.c_int64), ("H", ctypes.c_int64), ("G", ctypes.c_int64),
         ("R", ctypes.c_int64), ("N", ctypes.c_int64), ("P", ctypes.c_int64),
-        ("chunk_size", ctypes.c_int32), ("rotary_dim_divisor", ctypes.c_int32), ("out_f32", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32), ("rotary_dim_divisor", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
         ("dout", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("q_bias", ctypes.c_void_p), ("k_bias", ctypes.c_void_p), ("mimo_v", ctypes.c_void_p),
         ("states", ctypes.c_void_p), ("qk_dot", ctypes.c_void_p),
@@ -112,7 +113,7 @@ class MimoBwdBwdArgs(ctypes.Structure):
     ]
 
 
-DTYPE_BF16, DTYPE_FP16 = 0, 1
+DTYPE_BF16, DTYPE_FP16, DTYPE_FP32 = 0, 1, 2
 
 EXPORTED = ("mimo_bwd_fwd", "mimo_bwd_fwd_timed", "mimo_bwd_fwd_workspace_size", "mimo_fwd",
             "mimo_fwd_timed", "mimo_fwd_workspace_size", "mimo_bwd_fwd_f32", "mimo_bwd_fwd_f32_timed",

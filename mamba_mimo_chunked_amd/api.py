@@ -60,7 +60,7 @@ _BF16, _F32 = torch.bfloat16, torch.float32
 _ALWAYS, _IF_REDUCED, _IF_Z, _IF_D = "always", "reduced", "z", "d"
 
 
-def _sizes(q, v, chunk_size, rotary_dim_divisor, what="mamba_mimo_bwd_fwd"):
+def _sizes(q, v, chunk_size, rotary_dim_divisor, what="mamba_mimo_bwd_fwd", data_dtypes=(_BF16,)):
     """The problem sizes, read from q [B,S,R,G,N] and v [B,S,H,P], after the checks
     that need no other tensor. The order of the checks (rank of q, positive sizes,
     q's dtype, device, architecture, then the size constraints of the operator
@@ -70,8 +70,9 @@ def _sizes(q, v, chunk_size, rotary_dim_divisor, what="mamba_mimo_bwd_fwd"):
     B, S, R, G, N = (int(x) for x in q.shape)
     if min(B, S, R, G) < 1:
         raise ValueError("B, S, R and G must be positive")
-    if q.dtype != _BF16:
-        raise TypeError("q, k, v, dout and trap must use torch.bfloat16")
+    if q.dtype not in data_dtypes:
+        names = " or ".join(str(d) for d in data_dtypes)
+        raise TypeError(f"q, k, v, dout and trap must use {names}")
     if q.device.type != "cuda":
         raise ValueError(f"{what} requires GPU (HIP) tensors")
     if not _is_gfx950(q.device.index if q.device.index is not None else torch.cuda.current_device()):
@@ -95,13 +96,14 @@ def _sizes(q, v, chunk_size, rotary_dim_divisor, what="mamba_mimo_bwd_fwd"):
     return B, S, H, G, R, N, P, C, rd
 
 
-def _input_table(B, S, H, G, R, N, P, C, rd, *, reduce_o, with_dout):
-    """(name, expected shape, dtype, when present) of every tensor input but q."""
+def _input_table(B, S, H, G, R, N, P, C, rd, *, reduce_o, with_dout, data=_BF16):
+    """(name, expected shape, dtype, when present) of every tensor input but q;
+    ``data`` is the dtype of the data tensors (k, v, trap, z, dout)."""
     nc = (S + C - 1) // C
     dout_shape = (B, S, H, P) if reduce_o else (B, S, R, H, P)
     table = [
-        ("k", (B, S, R, G, N), _BF16, _ALWAYS),
-        ("v", (B, S, H, P), _BF16, _ALWAYS),
+        ("k", (B, S, R, G, N), data, _ALWAYS),
+        ("v", (B, S, H, P), data, _ALWAYS),
         ("q_bias", (H, R, N), _F32, _ALWAYS),
         ("k_bias", (H, R, N), _F32, _ALWAYS),
         ("mimo_v", (H, R, P), _F32, _ALWAYS),
@@ -109,15 +111,15 @@ def _input_table(B, S, H, G, R, N, P, C, rd, *, reduce_o, with_dout):
         ("da_cs", (B, H, S), _F32, _ALWAYS),
         ("da_cs_rev", (B, H, S), _F32, _ALWAYS),
         ("dt", (B, H, S), _F32, _ALWAYS),
-        ("trap", (B, H, S), _BF16, _ALWAYS),
+        ("trap", (B, H, S), data, _ALWAYS),
         ("segsum", (B, H, nc, C, C), _F32, _ALWAYS),
         ("d", (H,), _F32, _IF_D),
         ("mimo_o", (H, R, P), _F32, _IF_REDUCED),
-        ("z", (B, S, H, P), _BF16, _IF_Z),
+        ("z", (B, S, H, P), data, _IF_Z),
         ("mimo_z", (H, R, P), _F32, _IF_Z),
     ]
     if with_dout:
-        table.append(("dout", dout_shape, _BF16, _ALWAYS))
+        table.append(("dout", dout_shape, data, _ALWAYS))
     return table
 
 
@@ -132,16 +134,19 @@ def _check_table(table, values: dict, device):
 
 
 def _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, z, mimo_z, angles, da_cs,
-                     da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, *, fwd=False):
+                     da_cs_rev, dt, trap, d, segsum, chunk_size, rotary_dim_divisor, *, fwd=False,
+                     what="mamba_mimo_bwd_fwd", data_dtypes=(_BF16,)):
     """Check every argument of the backward first stage (or, with ``fwd``, of the
-    layer output, which takes no dout); returns the problem sizes."""
-    dims = _sizes(q, v, chunk_size, rotary_dim_divisor)
+    layer output, which takes no dout); returns the problem sizes. The data tensors
+    take q's dtype, one of ``data_dtypes``."""
+    dims = _sizes(q, v, chunk_size, rotary_dim_divisor, what, data_dtypes)
     if (z is None) != (mimo_z is None):
         raise ValueError("z and mimo_z must either both be present or both be None")
     values = dict(dout=dout, k=k, v=v, q_bias=q_bias, k_bias=k_bias, mimo_v=mimo_v, mimo_o=mimo_o,
                   z=z, mimo_z=mimo_z, angles=angles, da_cs=da_cs, da_cs_rev=da_cs_rev, dt=dt,
                   trap=trap, d=d, segsum=segsum)
-    _check_table(_input_table(*dims, reduce_o=mimo_o is not None, with_dout=not fwd), values, q.device)
+    _check_table(_input_table(*dims, reduce_o=mimo_o is not None, with_dout=not fwd, data=q.dtype), values,
+                 q.device)
     return dims
 
 
@@ -518,11 +523,13 @@ _BWD2_OUT_FIELDS = {"DQ": "dq", "DK": "dk", "DV": "dv", "DMIMO_V": "dmimo_v", "D
                     "DDA_CS_REV": "dda_cs_rev", "DDA_CS": "dda_cs", "DD": "dd"}
 
 
-def _make_bwd2_args(dims, C, rd, out_f32, t: dict, outs: dict, workspace=None, ws_bytes=0):
+def _make_bwd2_args(dims, C, rd, in_dtype: int, out_dtype: int, t: dict, outs: dict, workspace=None, ws_bytes=0):
+    """The C argument struct; ``in_dtype`` / ``out_dtype`` are _lib.DTYPE_* codes."""
     B, S, H, G, R, N, P = dims
     a = _lib.MimoBwdBwdArgs()
     a.B, a.S, a.H, a.G, a.R, a.N, a.P = B, S, H, G, R, N, P
-    a.chunk_size, a.rotary_dim_divisor, a.out_f32 = C, rd, int(out_f32)
+    a.chunk_size, a.rotary_dim_divisor = C, rd
+    a.in_dtype, a.out_dtype = int(in_dtype), int(out_dtype)
     for name in _BWD2_INPUTS:
         x = t.get(name)
         setattr(a, name, None if x is None else x.data_ptr())
@@ -534,26 +541,31 @@ def _make_bwd2_args(dims, C, rd, out_f32, t: dict, outs: dict, workspace=None, w
     return a
 
 
+_BWD2_DTYPES = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}   # _lib.DTYPE_* codes
+
+
 def mamba3_mimo_bwd_bwd(dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, da_cs, da_cs_rev, dt, trap,
                         segsum, angles, mimo_o=None, d=None, chunk_size: int = 16, rotary_dim_divisor: int = 4,
                         output_dtype=None, *, workspace: Optional[Tensor] = None) -> dict:
     """Stage-2 backward of the MIMO scan: the twelve gradients (dict keys DQ, DK, DV,
     DMIMO_V, DANGLES, DFACTOR, DGAMMA, DDA, DSSDA, DDA_CS_REV, DDA_CS, DD) of
-    sum(dPhiO * y) given the first stage's ``states`` and ``qk_dot``. DQ, DK
-    [B, S*R, H, N] and DV take q's dtype (bf16) unless ``output_dtype=torch.float32``;
-    the others are float32; DD is None without ``d``. Asynchronous on the current
-    HIP stream."""
+    sum(dPhiO * y) given the first stage's ``states`` and ``qk_dot`` (the
+    Triton-Ascend mamba3_mimo_bwd_bwd pull request page, migration note). The data
+    tensors dout, q, k, v, states, qk_dot and trap share one dtype: bfloat16,
+    float16 or float32. DQ, DK [B, S*R, H, N] and DV take that dtype unless
+    ``output_dtype`` names another of the three; the others are float32; DD is None
+    without ``d``. Asynchronous on the current HIP stream."""
     B, S, H, G, R, N, P, C, rd = _validate_inputs(dout, q, k, v, q_bias, k_bias, mimo_v, mimo_o, None, None,
                                                   angles, da_cs, da_cs_rev, dt, trap, d, segsum, chunk_size,
-                                                  rotary_dim_divisor)
+                                                  rotary_dim_divisor, what="mamba3_mimo_bwd_bwd",
+                                                  data_dtypes=tuple(_BWD2_DTYPES))
     nc = (S + C - 1) // C
     dev = q.device
-    _check_tensor("states", states, (B, H, nc, N, P), torch.bfloat16, dev)
-    _check_tensor("qk_dot", qk_dot, (B, H, S, R, R), torch.bfloat16, dev)
-    if output_dtype not in (None, torch.bfloat16, torch.float32):
-        raise TypeError("output_dtype must be None, torch.bfloat16 or torch.float32")
-    out_f32 = output_dtype == torch.float32
-    odt = torch.float32 if out_f32 else torch.bfloat16
+    _check_tensor("states", states, (B, H, nc, N, P), q.dtype, dev)
+    _check_tensor("qk_dot", qk_dot, (B, H, S, R, R), q.dtype, dev)
+    if output_dtype is not None and output_dtype not in _BWD2_DTYPES:
+        raise TypeError("output_dtype must be None, torch.bfloat16, torch.float16 or torch.float32")
+    odt = q.dtype if output_dtype is None else output_dtype
     L = _lib.lib()
     vals = (dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, da_cs, da_cs_rev, dt, trap, segsum, angles,
             mimo_o, d)
@@ -574,7 +586,8 @@ def mamba3_mimo_bwd_bwd(dout, q, k, v, q_bias, k_bias, mimo_v, states, qk_dot, d
         "DDA_CS": torch.empty((B, H, S), dtype=f32, device=dev),
         "DD": torch.empty((B, H), dtype=f32, device=dev) if d is not None else None,
     }
-    args = _make_bwd2_args((B, S, H, G, R, N, P), C, int(rotary_dim_divisor), out_f32, t, outs)
+    args = _make_bwd2_args((B, S, H, G, R, N, P), C, int(rotary_dim_divisor), _BWD2_DTYPES[q.dtype],
+                           _BWD2_DTYPES[odt], t, outs)
     need = ctypes.c_size_t(0)
     st = L.mimo_bwd_bwd_workspace_size(ctypes.byref(args), ctypes.byref(need))
     if st != _lib.MIMO_OK:

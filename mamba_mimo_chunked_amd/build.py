@@ -15,7 +15,8 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
-SOURCES = (["mimo_bwd_fwd.hip"] + [f"tiles_f32_mt{m}.hip" for m in (32, 64, 128)]
+SOURCES = (["mimo_bwd_fwd.hip"] + [f"b2_{t}.hip" for t in ("bf16", "f16", "f32")]
+           + [f"tiles_f32_mt{m}.hip" for m in (32, 64, 128)]
            + [f"tiles_rp{r}_ct{c}.hip" for r, c in
               ((1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4), (4, 1), (4, 2), (8, 1))])
 INCLUDE = ROOT / "include"

@@ -1,0 +1,9 @@
+// Instances of the stage-2 backward kernels (aggregate and chunk pass, both tile
+// geometries) for fp16 data tensors.
+#include "mimo_bwd2.hpp"
+
+namespace mimo {
+namespace b2 {
+Kern kernels_f16(int md) { return kernel_pair<DT_F16>(md); }
+}  // namespace b2
+}  // namespace mimo

@@ -48,6 +48,7 @@
 #include <mutex>
 #include <string>
 
+#define MIMO_B2_COMMON_KERNELS
 #include "mimo_bwd2.hpp"
 #include "mimo_f32.hpp"
 
@@ -629,8 +630,8 @@ mimo_status run_siso(const mimo_siso_fwd_args* a, void* stream, void* const* eve
 
 // ---------------------------------------------------------------- stage-2 backward
 struct PlanB2 {
-    int nc, L, nseg, F, nsub, W;
-    size_t off_agg, off_decay, off_mv, off_d, ws_bytes;
+    int nc, L, nseg, F, nsub, W, md;
+    size_t off_agg, off_decay, off_mv, off_d, off_slots, ws_bytes;
 };
 
 mimo_status make_plan_b2(const mimo_bwd_bwd_args* a, PlanB2* pl) {
@@ -643,15 +644,20 @@ mimo_status make_plan_b2(const mimo_bwd_bwd_args* a, PlanB2* pl) {
     if (H % G) return fail(MIMO_ERR_VALUE, "H must be divisible by G");
     if (rd != 2 && rd != 4) return fail(MIMO_ERR_VALUE, "rotary_dim_divisor must be 2 or 4");
     if (N % 2 || N % rd) return fail(MIMO_ERR_VALUE, "N must be even and divisible by rotary_dim_divisor");
-    if (C * R > 64 || N > 64 || P > 64 || R > 8 || P % 8 || N % 8)
+    for (int32_t dt : {a->in_dtype, a->out_dtype})
+        if (dt != MIMO_DTYPE_BF16 && dt != MIMO_DTYPE_FP16 && dt != MIMO_DTYPE_FP32)
+            return fail(MIMO_ERR_VALUE, "in_dtype and out_dtype must be MIMO_DTYPE_BF16, _FP16 or _FP32");
+    if (C * R > 128 || N > 128 || P > 128 || R > 8 || P % 8 || N % 8)
         return fail(MIMO_ERR_UNSUPPORTED,
-                    "the stage-2 backward supports R * chunk_size, N and P up to 64, R up to 8 and N and P multiples "
-                    "of 8");
+                    "the stage-2 backward supports R * chunk_size, N and P up to 128, R up to 8 and N and P "
+                    "multiples of 8");
     if (S > (int64_t)1 << 30 || B * H * ((S + C - 1) / C + 8) > (int64_t)1 << 31)
         return fail(MIMO_ERR_UNSUPPORTED, "problem too large");
+    pl->md = (C * R <= 64 && N <= 64 && P <= 64) ? 64 : 128;
     pl->W = (int)(N / rd);
     pl->nc = (int)((S + C - 1) / C);
-    // one workgroup per compute unit (the chunk pass keeps nine 64 x 64 fp32 tiles in LDS)
+    // one workgroup per compute unit (the chunk pass keeps nine fp32 tiles in LDS, or
+    // is bound by its registers with the tiles in scratch)
     int64_t L = (pl->nc * B * H + 255) / 256;
     if (L < 1) L = 1;
     if (L > pl->nc) L = pl->nc;
@@ -669,6 +675,17 @@ mimo_status make_plan_b2(const mimo_bwd_bwd_args* a, PlanB2* pl) {
     off = align256(off + (size_t)B * H * pl->nseg * R * P * 4);
     pl->off_d = off;
     off = align256(off + (size_t)B * H * pl->nseg * 4);
+    pl->off_slots = off;
+    if (pl->md == 128) {
+        // one tile slot per block of the chunk pass and of the aggregate (they run one
+        // after the other and share the slots)
+        Params pp = {};
+        pp.B = (int)B; pp.H = (int)H; pp.G = (int)G;
+        using G128 = b2::Geo<128>;
+        const size_t main_f = (size_t)grid_blocks(pp, pl->nseg) * G128::MAIN_TILES;
+        const size_t agg_f = pl->nseg > 1 ? (size_t)grid_blocks(pp, pl->nsub) * G128::AGG_TILES : 0;
+        off = align256(off + 4 * (main_f > agg_f ? main_f : agg_f));
+    }
     pl->ws_bytes = off;
     return MIMO_OK;
 }
@@ -688,10 +705,11 @@ mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events
     // rows of eight 16-bit or four fp32 values are moved as one 16-byte access
     for (const void* x : {(const void*)a->dout, (const void*)a->q, (const void*)a->k, (const void*)a->v,
                           (const void*)a->states, (const void*)a->q_bias, (const void*)a->k_bias,
-                          (const void*)a->mimo_v, (const void*)a->mimo_o, (const void*)a->dq, (const void*)a->dk})
+                          (const void*)a->mimo_v, (const void*)a->mimo_o, (const void*)a->dq, (const void*)a->dk,
+                          (const void*)a->dv})
         if (reinterpret_cast<uintptr_t>(x) % 16)
-            return fail(MIMO_ERR_VALUE, "dout, q, k, v, states, q_bias, k_bias, mimo_v, mimo_o, dq and dk must be "
-                                        "16-byte aligned");
+            return fail(MIMO_ERR_VALUE, "dout, q, k, v, states, q_bias, k_bias, mimo_v, mimo_o, dq, dk and dv "
+                                        "must be 16-byte aligned");
     if (a->workspace_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && a->workspace == nullptr))
         return fail(MIMO_ERR_VALUE, "workspace too small: need %zu bytes, got %zu", pl.ws_bytes, a->workspace_bytes);
     if (pl.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(a->workspace) & 255))
@@ -703,7 +721,7 @@ mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events
     b2::Params2 p = {};
     p.B = (int)a->B; p.S = (int)a->S; p.H = (int)a->H; p.G = (int)a->G; p.R = (int)a->R; p.N = (int)a->N;
     p.P = (int)a->P; p.C = a->chunk_size; p.W = pl.W; p.nc = pl.nc; p.L = pl.L; p.nseg = pl.nseg; p.F = pl.F;
-    p.nsub = pl.nsub; p.reduce_o = a->mimo_o != nullptr; p.has_d = a->d != nullptr; p.out_f32 = a->out_f32 != 0;
+    p.nsub = pl.nsub; p.reduce_o = a->mimo_o != nullptr; p.has_d = a->d != nullptr; p.out_dt = a->out_dtype;
     p.dout = a->dout; p.q = a->q; p.k = a->k; p.v = a->v; p.states = a->states; p.qk_dot = a->qk_dot;
     p.trap = a->trap; p.q_bias = a->q_bias; p.k_bias = a->k_bias; p.mimo_v = a->mimo_v; p.mimo_o = a->mimo_o;
     p.da_cs = a->da_cs; p.da_cs_rev = a->da_cs_rev; p.dt = a->dt; p.segsum = a->segsum; p.angles = a->angles;
@@ -716,6 +734,7 @@ mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events
     p.decay = pl.nseg > 1 ? reinterpret_cast<float*>(ws + pl.off_decay) : nullptr;
     p.part_mv = reinterpret_cast<float*>(ws + pl.off_mv);
     p.part_d = reinterpret_cast<float*>(ws + pl.off_d);
+    p.slots = pl.md == 128 ? reinterpret_cast<float*>(ws + pl.off_slots) : nullptr;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     auto mark = [&](int i) -> mimo_status {
@@ -738,13 +757,16 @@ mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events
     };
     Params pp = {};
     pp.B = p.B; pp.H = p.H; pp.G = p.G;
-    const void* kmain = p.out_f32 ? reinterpret_cast<const void*>(&b2::k_main2<true>)
-                                  : reinterpret_cast<const void*>(&b2::k_main2<false>);
-    const int lds_main = b2::L2::TOTAL * 4, lds_agg = b2::L2::AGG_TOTAL * 4;
+    const b2::Kern kern = a->in_dtype == MIMO_DTYPE_FP32   ? b2::kernels_f32(pl.md)
+                          : a->in_dtype == MIMO_DTYPE_FP16 ? b2::kernels_f16(pl.md)
+                                                           : b2::kernels_bf16(pl.md);
+    const void* kmain = kern.main;
+    const int lds_main = (pl.md == 64 ? b2::Geo<64>::LDS_MAIN : b2::Geo<128>::LDS_MAIN) * 4;
+    const int lds_agg = (pl.md == 64 ? b2::Geo<64>::LDS_AGG : b2::Geo<128>::LDS_AGG) * 4;
     if ((s = set_lds2(kmain, lds_main)) != MIMO_OK) return s;
     if ((s = mark(0)) != MIMO_OK) return s;
     if (pl.nseg > 1) {
-        const void* kagg = reinterpret_cast<const void*>(&b2::k_agg2);
+        const void* kagg = kern.agg;
         if ((s = set_lds2(kagg, lds_agg)) != MIMO_OK) return s;
         if ((s = launch2(kagg, dim3(grid_blocks(pp, pl.nsub)), lds_agg, b2::NTHR)) != MIMO_OK) return s;
         if ((s = mark(1)) != MIMO_OK) return s;

@@ -120,7 +120,7 @@ def test_bwd_bwd_argument_checks_without_a_device():
     a.chunk_size, a.rotary_dim_divisor = 16, 4
     n = ctypes.c_size_t(0)
     assert L.mimo_bwd_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _lib.MIMO_OK
-    for field, val in (("N", 60), ("P", 60), ("N", 128), ("R", 16)):
+    for field, val in (("N", 60), ("P", 60), ("N", 136), ("P", 136), ("R", 16)):
         old = getattr(a, field)
         setattr(a, field, val)
         if field == "R":

@@ -8,10 +8,12 @@ RMS(gpu - oracle) / RMS(oracle) < 1e-4 (fp32 intermediates against float64;
 a tenth of the operator's 1e-3 bar); with the default bf16 outputs DQ, DK and
 DV must be within 1e-3 of the oracle rounded to bf16. Cases: several segments
 and ragged tails, GQA, R = 1..8, both dout layouts, with and without d,
-rotary divisor 2, the perf shape on sampled heads, every element written,
-angles far beyond 2*pi, inputs that are unaligned device views (bit-identical
-to aligned ones), and the shapes beyond the kernel's tiles
-(NotImplementedError).
+rotary divisor 2, both tile geometries (R*C, N and P up to 64 in LDS; any of
+them up to 128 with the tiles in scratch, chunk size up to 128), fp16 and fp32
+data tensors (the output dtypes following them or overridden), the perf shape
+and the two 128-wide workloads on sampled heads, every element written, angles
+far beyond 2*pi, inputs that are unaligned device views (bit-identical to
+aligned ones), and shapes beyond the page's range (rejected).
 """
 
 import numpy as np
@@ -42,6 +44,27 @@ def _caches(inp):
     """First-stage caches from the CPU contract oracle, as bf16 tensors."""
     _, states, _, _, qk = o1.run_inputs(inp)
     return torch.from_numpy(states).to(torch.bfloat16), torch.from_numpy(qk).to(torch.bfloat16)
+
+
+DATA = ("dout", "q", "k", "v", "trap")
+
+
+def _as_dtype(inp, states, qk, dtype, seed=5):
+    """The data tensors (and caches) in ``dtype``. For fp16 and fp32 the values are
+    first moved off the bf16 grid by a relative 2^-9 (seeded), so the wider mantissa
+    is exercised; both sides take the converted tensors."""
+    if dtype is torch.bfloat16:
+        return inp, states, qk
+    g = torch.Generator().manual_seed(seed)
+
+    def conv(x):
+        u = torch.rand(x.shape, generator=g, dtype=torch.float32) * 2 - 1
+        return (x.float() * (1 + u * 2.0 ** -9)).to(dtype)
+
+    out = dict(inp)
+    for n in DATA:
+        out[n] = conv(inp[n])
+    return out, conv(states), conv(qk)
 
 
 def _run_gpu(inp, states, qk, output_dtype=None):
@@ -86,6 +109,15 @@ CASES = [
     Case(1, 333, 2, 2, 64, 32, 4, 16, reduce_o=False, has_z=False, has_d=True, name="b2_nonreduced"),
     Case(2, 257, 4, 4, 64, 64, 4, 16, reduce_o=False, has_z=False, has_d=False, name="b2_nonreduced_nod"),
     Case(1, 1, 1, 1, 16, 16, 2, 16, name="b2_one_token"),
+    # the 128-wide geometry (tiles in scratch)
+    Case(1, 300, 2, 1, 128, 64, 2, 64, name="b2w_n128_c64_r2"),
+    Case(1, 130, 2, 2, 128, 128, 8, 16, name="b2w_r8_n128_p128_tail"),
+    Case(1, 200, 2, 1, 64, 64, 4, 32, name="b2w_rc128"),
+    Case(1, 150, 2, 1, 96, 120, 3, 40, rd=2, name="b2w_r3_c40_rd2_n96_p120"),
+    Case(2, 100, 4, 2, 128, 32, 2, 16, reduce_o=False, has_z=False, has_d=False, name="b2w_nonreduced_n128"),
+    Case(1, 257, 1, 1, 16, 16, 1, 128, name="b2w_c128_r1_tail"),
+    Case(1, 1, 1, 1, 128, 128, 1, 128, name="b2w_one_token"),
+    Case(1, 4096, 4, 1, 128, 64, 2, 16, name="b2w_split_segments"),
 ]
 
 
@@ -152,13 +184,81 @@ def test_bwd2_every_element_written_and_deterministic():
         assert torch.equal(a[key], b[key]), key
 
 
-@pytest.mark.parametrize("case", [Case(1, 64, 1, 1, 128, 64, 2, 16, name="n128"),
-                                  Case(1, 64, 1, 1, 64, 64, 8, 16, name="rc128")], ids=lambda c: c.name)
-def test_bwd2_beyond_tiles_rejected(case):
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32], ids=["fp16", "fp32"])
+@pytest.mark.parametrize("case", [Case(1, 300, 3, 1, 64, 64, 4, 16, name="dt_narrow"),
+                                  Case(1, 130, 2, 2, 128, 128, 8, 16, name="dt_wide")], ids=lambda c: c.name)
+def test_bwd2_input_dtypes(case, dtype):
+    """fp16 and fp32 data tensors: parity with fp32 outputs; DQ, DK, DV follow the
+    input dtype by default and equal the fp32 outputs rounded to it (the same fp32
+    values, stored with another conversion); output_dtype overrides it."""
     inp = make_inputs(case)
     states, qk = _caches(inp)
-    with pytest.raises(NotImplementedError):
-        _run_gpu(inp, states, qk)
+    inp, states, qk = _as_dtype(inp, states, qk, dtype)
+    got = _run_gpu(inp, states, qk, torch.float32)
+    errs = _compare(got, _oracle(inp, states, qk), f"{case.name} {dtype}: ")
+    log("    " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    own = _run_gpu(inp, states, qk)
+    other = torch.bfloat16 if dtype is torch.float32 else torch.float32
+    over = _run_gpu(inp, states, qk, other)
+    for key in bwd2.NAMES:
+        if got[key] is None:
+            continue
+        if key in ("DQ", "DK", "DV"):
+            assert own[key].dtype == dtype and over[key].dtype == other, key
+            assert torch.equal(own[key], got[key].to(dtype)), key
+            assert torch.equal(over[key], got[key].to(other)), key
+        else:
+            assert torch.equal(own[key], got[key]) and torch.equal(over[key], got[key]), key
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,heads", [("wide_chunk_n128", ((0, 0), (3, 31))), ("max_rank_tile", ((1, 7),))])
+def test_bwd2_wide_workload_sampled_heads(name, heads):
+    """The two 128-wide workloads at full size, compared on sampled (batch, head)
+    pairs (heads are independent). The caches of the sampled heads are the contract
+    oracle's; the other heads get zero states and dots (never compared)."""
+    case = CONFIGS[name]
+    log(f"[bwd2] {name} B={case.B} S={case.S} H={case.H} N={case.N} P={case.P} R={case.R} C={case.C}")
+    inp = make_inputs(case)
+    B, H, S, R, N, P = case.B, case.H, case.S, case.R, case.N, case.P
+    states = torch.zeros((B, H, case.nchunks, N, P), dtype=torch.bfloat16)
+    qk = torch.zeros((B, H, S, R, R), dtype=torch.bfloat16)
+    slices = {}
+    for b, h in heads:
+        sl = o1.slice_heads(inp, b, h)
+        st_h, qk_h = _caches(sl)
+        states[b, h], qk[b, h] = st_h[0, 0], qk_h[0, 0]
+        slices[(b, h)] = (sl, st_h, qk_h)
+    got = _run_gpu(inp, states, qk, torch.float32)
+    for (b, h), (sl, st_h, qk_h) in slices.items():
+        ref = _oracle(sl, st_h, qk_h)
+        sub = {}
+        for key in bwd2.NAMES:
+            x = got[key]
+            if x is None:
+                sub[key] = None
+            elif key in ("DQ", "DK", "DV", "DANGLES"):
+                sub[key] = x[b:b + 1, :, h:h + 1]
+            else:
+                sub[key] = x[b:b + 1, h:h + 1]
+        errs = _compare(sub, ref, f"{name} b={b} h={h}: ")
+        log(f"    b={b} h={h} " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+
+
+@pytest.mark.parametrize("case", [Case(1, 64, 1, 1, 136, 64, 2, 16, name="n136"),
+                                  Case(1, 64, 1, 1, 64, 64, 8, 32, name="rc256")], ids=lambda c: c.name)
+def test_bwd2_beyond_range_rejected(case):
+    """Beyond the page's range (N, P, R*C up to 128) the call is rejected before any
+    device work."""
+    from mamba_mimo_chunked_amd import mamba3_mimo_bwd_bwd
+    inp = make_inputs(case)
+    nc = case.nchunks
+    states = torch.zeros((1, 1, nc, case.N, case.P), dtype=torch.bfloat16)
+    qk = torch.zeros((1, 1, case.S, case.R, case.R), dtype=torch.bfloat16)
+    dev = {n: x.to("cuda") for n, x in dict(inp, states=states, qk_dot=qk).items() if n in ORDER}
+    with pytest.raises(ValueError):
+        mamba3_mimo_bwd_bwd(*[dev[n] for n in ORDER], mimo_o=inp["mimo_o"].to("cuda"), chunk_size=case.C,
+                            rotary_dim_divisor=case.rd)
 
 
 def test_bwd2_unaligned_views_match():
