@@ -189,8 +189,9 @@ mimo_status mimo_fwd_timed(const mimo_fwd_args *args, void *stream, void *const 
  * round-to-nearest-even; dmimo fp32). Arguments, layouts, ownership and errors
  * as for mimo_bwd_fwd, with these limits instead of its tile limits: N and P
  * multiples of 16 up to 128, chunk_size <= 64, R <= 8, R * (chunk_size rounded
- * up to 16) <= 128, and the fp32 tiles must fit one compute unit's LDS (not the
- * case for R * chunk_size > 64 with N or P = 128): MIMO_ERR_UNSUPPORTED otherwise.
+ * up to 16) <= 128 (MIMO_ERR_UNSUPPORTED otherwise). Where R * chunk_size > 64
+ * with N or P = 128 the fp32 tiles exceed one compute unit's LDS and the K~ tile
+ * of each workgroup is kept in the workspace (MT x (N + 4) floats a block).
  */
 mimo_status mimo_bwd_fwd_f32_workspace_size(const mimo_bwd_fwd_args *args, size_t *bytes);
 mimo_status mimo_bwd_fwd_f32(const mimo_bwd_fwd_args *args, void *stream);

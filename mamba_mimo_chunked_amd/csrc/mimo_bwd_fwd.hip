@@ -402,7 +402,8 @@ struct Prob32 {
 
 struct Plan32 {
     int MT, NT, PT, nc, L, nseg, F, nsub, ti, lds_main, lds_agg;
-    size_t off_agg, off_decay, off_po, off_pz, ws_bytes;
+    bool kg_main, kg_agg;   // K~ tile in scratch (the kernel table picks those instances by the same rule)
+    size_t off_agg, off_decay, off_po, off_pz, off_kslots, ws_bytes;
 };
 
 int tidx3(int x) { return x == 32 ? 0 : (x == 64 ? 1 : 2); }
@@ -443,9 +444,11 @@ mimo_status make_plan32(const Prob32& q, Plan32* pl) {
     pl->NT = tile_size((int)q.N);
     pl->PT = tile_size((int)q.P);
     pl->ti = 9 * tidx3(pl->MT) + 3 * tidx3(pl->NT) + tidx3(pl->PT);
-    pl->lds_main = f32::lds32(pl->MT, pl->NT, pl->PT, true, q.uv).total;
-    pl->lds_agg = f32::lds32(pl->MT, pl->NT, pl->PT, false, q.uv).total;
-    if (pl->lds_main > 160 * 1024)
+    pl->kg_main = f32::lds32(pl->MT, pl->NT, pl->PT, true, q.uv).total > 160 * 1024 && !q.uv;
+    pl->kg_agg = f32::lds32(pl->MT, pl->NT, pl->PT, false, q.uv).total > 160 * 1024 && !q.uv;
+    pl->lds_main = f32::lds32(pl->MT, pl->NT, pl->PT, true, q.uv, pl->kg_main).total;
+    pl->lds_agg = f32::lds32(pl->MT, pl->NT, pl->PT, false, q.uv, pl->kg_agg).total;
+    if (pl->lds_main > 160 * 1024 || pl->lds_agg > 160 * 1024)
         return fail(MIMO_ERR_UNSUPPORTED,
                     "the fp32-intermediate kernels need %d bytes of LDS for R*C=%d, N=%lld, P=%lld (limit 163840)",
                     pl->lds_main, rows, (long long)q.N, (long long)q.P);
@@ -470,6 +473,16 @@ mimo_status make_plan32(const Prob32& q, Plan32* pl) {
     if (part && q.reduce_o) off = align256(off + (size_t)q.B * q.H * pl->nseg * q.R * q.P * 4);
     pl->off_pz = off;
     if (part && q.has_z) off = align256(off + (size_t)q.B * q.H * pl->nseg * q.R * q.P * 4);
+    pl->off_kslots = off;
+    if (pl->kg_main || pl->kg_agg) {
+        // one K~ tile per block of whichever launch keeps it in scratch (they run one after
+        // the other and share the slots)
+        Params pp = {};
+        pp.B = (int)q.B; pp.H = (int)q.H; pp.G = (int)q.G;
+        size_t blocks = pl->kg_main ? grid_blocks(pp, pl->nseg) : 0;
+        if (pl->kg_agg && pl->nseg > 1 && grid_blocks(pp, pl->nsub) > blocks) blocks = grid_blocks(pp, pl->nsub);
+        off = align256(off + blocks * pl->MT * (pl->NT + 4) * 4);
+    }
     pl->ws_bytes = off;
     return MIMO_OK;
 }
@@ -510,6 +523,7 @@ mimo_status run32(const Prob32& q, Params& p, void* workspace, size_t workspace_
         p.part_o = p.dmimo_o;
         p.part_z = p.dmimo_z;
     }
+    p.kslots = (pl.kg_main || pl.kg_agg) ? reinterpret_cast<float*>(ws + pl.off_kslots) : nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
     auto mark = [&](int i) -> mimo_status {
         if (events == nullptr) return MIMO_OK;

@@ -23,6 +23,10 @@
 // Wave w owns the value tiles pt = w, w+4 (all state rows and all chunk rows of
 // them), so the state a wave reads for the inter term is in its own registers
 // and every rank of a (token, column) meets in one lane for the gating sums.
+// With 128 chunk rows and N or P of 128 the q^, K~ and Psi tiles need 188 to 225 KB,
+// more than a compute unit's LDS: those instances (KG) keep the K~ tile in a
+// per-workgroup slot of global scratch (its other uses are unchanged; the chunk
+// loop's barriers already order global memory) and the rest in LDS.
 #pragma once
 
 #include "mimo_kernels.hpp"
@@ -50,7 +54,7 @@ struct Lds32 {
 // uv: unit value projections and controls derived from adt (the SISO forward): Psi is
 // v itself, kept in its 16-bit input type, and exp(segsum) comes from the cumulative
 // log decays instead of a table.
-__host__ __device__ constexpr Lds32 lds32(int MT, int NT, int PT, bool main, bool uv = false) {
+__host__ __device__ constexpr Lds32 lds32(int MT, int NT, int PT, bool main, bool uv = false, bool kg = false) {
     const int CX = MT < 64 ? MT : 64;
     // q^, then the causal block, then y's partial sums: the widest of the three rows
     const int wq = NT > MT ? (NT > PT ? NT : PT) : (MT > PT ? MT : PT);
@@ -60,7 +64,7 @@ __host__ __device__ constexpr Lds32 lds32(int MT, int NT, int PT, bool main, boo
     l.q = off;
     off += qa;
     l.k = off;
-    off += 4 * MT * (NT + 4);
+    if (!kg) off += 4 * MT * (NT + 4);
     l.psi = off;
     off += uv ? 2 * MT * (PT + 8) : 4 * MT * (PT + 4);
     l.se = off;
@@ -117,9 +121,9 @@ __device__ __forceinline__ f32x4 mfma32(float a, float b, f32x4 c) {
 // its decay product). MAIN = true: the chunk pass (states, qk_dot, y and the
 // backward's gating outputs, or the layer output when p.fwd).
 // Two workgroups per compute unit where the LDS layout allows it.
-template <int MT, int NT, int PT, bool MAIN, bool UV>
+template <int MT, int NT, int PT, bool MAIN, bool UV, bool KG = false>
 constexpr int wg_per_cu32() {
-    return lds32(MT, NT, PT, MAIN, UV).total <= 80 * 1024 ? 2 : 1;
+    return lds32(MT, NT, PT, MAIN, UV, KG).total <= 80 * 1024 ? 2 : 1;
 }
 
 // A 16-bit value (bf16, or fp16 when F16) as fp32.
@@ -129,17 +133,18 @@ __device__ __forceinline__ float cvt16(unsigned short x) {
     return __uint_as_float(static_cast<unsigned>(x) << 16);
 }
 
-template <int MT, int NT, int PT, bool MAIN, bool F16, bool UV = false>
-__global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_chunk32(Params p) {
+template <int MT, int NT, int PT, bool MAIN, bool F16, bool UV = false, bool KG = false>
+__global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV, KG>())) void k_chunk32(Params p) {
     using T = Tile32<MT, NT, PT>;
     constexpr int NW = T::NW, NTHR = T::NTHR, LQ = T::LQ, LA = T::LA, LP = T::LP, CX = T::CX;
     constexpr int MTT = T::MTT, NTT = T::NTT, PTT = T::PTT, PW = T::PW;
     extern __shared__ __align__(16) unsigned char smem[];
-    constexpr Lds32 L = lds32(MT, NT, PT, MAIN, UV);
+    constexpr Lds32 L = lds32(MT, NT, PT, MAIN, UV, KG);
     float* sQ = reinterpret_cast<float*>(smem + L.q);   // q^ [MT][LQ], then the causal block [MT][LA],
     float* sA = sQ;                                       // then y's partial sums [MT][LP]
     float* sY = sQ;
-    float* sK = reinterpret_cast<float*>(smem + L.k);     // k0, then K~ [MT][LQ]
+    // k0, then K~ [MT][LQ] (with KG in this workgroup's scratch slot)
+    float* sK = KG ? p.kslots + (long)blockIdx.x * MT * LQ : reinterpret_cast<float*>(smem + L.k);
     float* sPsi = reinterpret_cast<float*>(smem + L.psi); // Psi [MT][LP], or 16-bit [MT][LP16] when UV
     unsigned short* sPsi16 = reinterpret_cast<unsigned short*>(smem + L.psi);
     auto psi_at = [&](int row, int col) -> float {
@@ -721,7 +726,8 @@ __global__ __launch_bounds__(256, (wg_per_cu32<MT, NT, PT, MAIN, UV>())) void k_
 }
 
 // Kernel table: [bf16 = 0 / fp16 = 1][9 * idx(MT) + 3 * idx(NT) + idx(PT)] with
-// idx(32, 64, 128) = 0, 1, 2; nullptr where the tile's LDS does not fit. Each MT's
+// idx(32, 64, 128) = 0, 1, 2; nullptr where the tile's LDS does not fit even with K~
+// in scratch. Each MT's
 // instances are compiled in a translation unit of their own (tiles_f32_mt*.hip). The
 // *_uv tables hold the unit-projection instances (the SISO forward: MT of 32 and 64).
 struct F32Set {
@@ -734,10 +740,18 @@ const F32Part* f32_part_mt32();
 const F32Part* f32_part_mt64();
 const F32Part* f32_part_mt128();
 
+// The instance of a tile: all tiles in LDS where they fit, else (not for the unit
+// projections) K~ in scratch.
+template <int MT, int NT, int PT, bool MAIN, bool UV>
+constexpr bool kg32() {
+    return lds32(MT, NT, PT, MAIN, UV).total > 160 * 1024;
+}
 template <int MT, int NT, int PT, bool MAIN, bool F16, bool UV>
 constexpr kfn pick32() {
-    if constexpr (lds32(MT, NT, PT, MAIN, UV).total <= 160 * 1024)
+    if constexpr (!kg32<MT, NT, PT, MAIN, UV>())
         return k_chunk32<MT, NT, PT, MAIN, F16, UV>;
+    else if constexpr (!UV && lds32(MT, NT, PT, MAIN, UV, true).total <= 160 * 1024)
+        return k_chunk32<MT, NT, PT, MAIN, F16, UV, true>;
     else
         return nullptr;
 }

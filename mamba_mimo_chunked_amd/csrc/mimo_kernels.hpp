@@ -148,6 +148,7 @@ struct Params {
     float* decay;   // [B*H][nsub]: product of the chunk decays of each sub-segment
     float* part_o;  // [B*H][nseg][R*P] partial dmimo_o (== dmimo_o when nseg == 1)
     float* part_z;  // [B*H][nseg][R*P] partial dmimo_z
+    float* kslots;  // fp32 path, 128-row tiles: per-workgroup K~ tiles [MT][NT+4] (one per block)
 };
 
 // ---------------------------------------------------------------- tile family

@@ -9,8 +9,9 @@
   SISO page's thresholds (2^-8 for bf16, 2^-11 for fp16 outputs) and below 1e-3
   against the oracle rounded to the output dtype.
 Cases span several tiles, segments and ragged tails, GQA, both dtypes, both
-chunk sizes, the branch combinations, the perf shapes, and the shapes the fp32
-tiles cannot hold (NotImplementedError).
+chunk sizes, the branch combinations, the perf shapes, and the 128-row tiles
+whose K~ tile lives in scratch (R * C > 64 with N or P = 128: small shapes on
+every head, the two 128-wide workloads at full size on sampled heads).
 """
 
 import numpy as np
@@ -116,12 +117,41 @@ def test_fp32_is_closer_to_exact_than_bf16_contract():
         assert ef * 20 < eb
 
 
-@pytest.mark.parametrize("case", [Case(1, 300, 2, 1, 128, 128, 8, 16, name="mt128_n128_p128"),
-                                  Case(1, 300, 2, 1, 128, 64, 2, 64, name="mt128_n128")],
-                         ids=lambda c: c.name)
-def test_fp32_tiles_beyond_lds_are_rejected(case):
-    with pytest.raises(NotImplementedError):
-        run_bwd32(to_device(make_inputs(case)))
+KG_CASES = [
+    Case(1, 300, 2, 1, 128, 128, 8, 16, name="kg_n128_p128_r8"),
+    Case(1, 300, 2, 1, 128, 64, 2, 64, name="kg_n128_c64"),
+    Case(2, 150, 4, 2, 64, 128, 4, 32, reduce_o=False, has_z=True, has_d=True, name="kg_p128_nonreduced_z"),
+    Case(1, 77, 2, 1, 128, 32, 3, 24, reduce_o=True, has_z=False, has_d=False, name="kg_n128_p32_r3_c24"),
+]
+
+
+@pytest.mark.parametrize("case", KG_CASES, ids=lambda c: c.name)
+def test_bwd_fwd_fp32_k_tile_in_scratch(case):
+    """128-row tiles beyond the LDS with all tiles in it: K~ in scratch."""
+    log(f"[fp32] {case.name} B={case.B} S={case.S} H={case.H} G={case.G} N={case.N} P={case.P} "
+        f"R={case.R} C={case.C}")
+    inp = make_inputs(case)
+    got = run_bwd32(to_device(inp))
+    errs = compare(got, o1.run_inputs(inp, fp32=True), tol=TOL32, label=f"{case.name}: ")
+    log("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,heads", [("wide_chunk_n128", ((0, 0), (3, 31))), ("max_rank_tile", ((1, 9),))])
+def test_bwd_fwd_fp32_wide_workloads_sampled(name, heads):
+    """The two 128-wide workloads at full size; the oracle runs on sampled (batch,
+    head) pairs, the per-head outputs compared on those heads and dmimo_o / dmimo_z
+    on their (batch, head) entries."""
+    case = CONFIGS[name].with_(seed=13)
+    log(f"[fp32] {name} (sampled heads)")
+    inp = make_inputs(case)
+    got = run_bwd32(to_device(inp))
+    for b, h in heads:
+        ref = o1.run_inputs(o1.slice_heads(inp, b, h), fp32=True)
+        pick = lambda x, dz=False: None if x is None else (x[b:b + 1, :, h:h + 1] if dz else x[b:b + 1, h:h + 1])
+        sl = (pick(got[0]), pick(got[1]), pick(got[2], dz=True), pick(got[3]), pick(got[4]))
+        errs = compare(sl, ref, tol=TOL32, label=f"{name} b={b} h={h}: ")
+        log(f"    b={b} h={h} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
 @pytest.mark.parametrize("case", [Case(1, 300, 3, 1, 64, 64, 4, 16, name="fwd32_reduced"),
