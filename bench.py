@@ -627,6 +627,10 @@ def main():
     gbps = alg_bytes / (ms * 1e-3) / 1e9
     metric = {"bwd_fwd": METRIC, "fwd": FWD_METRIC, "bwd_fwd_fp32": FP32_METRIC, "siso": SISO_METRIC,
               "bwd_bwd": BWD2_METRIC}[op]
+    if not siso_op and (case.B, case.S, case.H, case.G, case.N, case.P, case.R, case.C) != (1, 8192, 16, 1, 64, 64, 4, 16):
+        # another workload: the same metric, named with that workload's shape
+        metric = metric.split(" at ")[0] + (f" at B{case.B} S{case.S} H{case.H} G{case.G} N{case.N} P{case.P} "
+                                            f"R{case.R} C{case.C}")
     if siso_op:
         config = {"workload": a.config, "op": op, "B": case.B, "S": case.S, "Hq": case.Hq, "H": case.H,
                   "K": case.K, "V": case.V, "A": case.width, "chunk_size": case.C, "dtype": case.dtype,

@@ -66,8 +66,10 @@ struct Geo {
     static constexpr int GAM = 0, FAC = GAM + MD, ECS = FAC + MD, EREV = ECS + MD, RED = EREV + MD,
                          DQK = RED + 8, QKC = DQK + 8 * MD, RS0 = QKC + 8 * MD, RS1 = RS0 + 2 * MD,
                          SMALL = RS1 + 2 * MD;
-    static constexpr int LDS_MAIN = (WIDE ? 0 : MAIN_TILES) + SMALL;   // floats
-    static constexpr int LDS_AGG = (WIDE ? 0 : AGG_TILES) + SMALL;
+    // MD = 128: after the small tables, one tile that stages each product's B operand
+    static constexpr int BSTG = SMALL;
+    static constexpr int LDS_MAIN = (WIDE ? TILE : MAIN_TILES) + SMALL;   // floats
+    static constexpr int LDS_AGG = (WIDE ? TILE : AGG_TILES) + SMALL;
 };
 
 struct Params2 {
@@ -300,16 +302,31 @@ __device__ __forceinline__ void gemm64(int Mi, int Nj, int K, const float* A, co
 
 // MD = 128 (all <= 128, tiles in global scratch): eight waves, wave w owns row block w
 // and every column block; the contraction runs in 16-wide steps, each step's operands
-// loaded just before its MFMAs.
+// loaded just before its MFMAs. Every wave reads all of B, so B is first copied into
+// the LDS tile bs (one global read instead of eight); the barriers around the copy
+// also order the product after the stores of whatever came before it. Called by
+// every thread of the workgroup.
 template <int NT, bool AK1, bool BK1, bool SK, bool RS, typename F>
-__device__ __forceinline__ void gemm128(int Mi, int Nj, int K, const float* A, const float* B, const float* sk,
-                                        F&& epi, float* rs) {
+__device__ __forceinline__ void gemm128(int Mi, int Nj, int K, const float* A, const float* Bg, const float* sk,
+                                        F&& epi, float* rs, float* bs) {
     static_assert(NT == 512, "one 16-row block a wave");
     constexpr int LD = Geo<128>::LD;
     const int tid = tid_x(), w = tid >> 6, x = tid & 15, q = (tid >> 4) & 3;
+    const int ncb = (Nj + 15) >> 4, nk = (K + 15) >> 4;
+    {
+        // the B region the product reads: rows j < 16 ncb of k < 16 nk (BK1), else rows
+        // k < 16 nk of j < 16 ncb; four floats a copy
+        const int rows = BK1 ? 16 * ncb : 16 * nk, c4 = BK1 ? 4 * nk : 4 * ncb;
+        __syncthreads();
+        for (int e = tid; e < rows * c4; e += NT) {
+            const int r = e / c4, c = 4 * (e - r * c4);
+            *reinterpret_cast<f32x4*>(bs + r * LD + c) = *reinterpret_cast<const f32x4*>(Bg + r * LD + c);
+        }
+        __syncthreads();
+    }
+    const float* B = bs;
     const int i0 = 16 * w;
     if (i0 >= Mi) return;   // wave-uniform
-    const int ncb = (Nj + 15) >> 4, nk = (K + 15) >> 4;
     f32x4 acc[8];
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -389,11 +406,12 @@ __device__ __forceinline__ void gemm128(int Mi, int Nj, int K, const float* A, c
     }
 }
 
+// bs: MD = 128's LDS staging tile for B (unused with MD = 64)
 template <int MD, int NT, bool AK1, bool BK1, bool SK, bool RS = false, typename F>
 __device__ __forceinline__ void gemm(int Mi, int Nj, int K, const float* A, const float* B, const float* sk,
-                                     F&& epi, float* rs = nullptr) {
+                                     F&& epi, float* rs, float* bs) {
     if constexpr (Geo<MD>::WIDE)
-        gemm128<NT, AK1, BK1, SK, RS>(Mi, Nj, K, A, B, sk, epi, rs);
+        gemm128<NT, AK1, BK1, SK, RS>(Mi, Nj, K, A, B, sk, epi, rs, bs);
     else
         gemm64<NT, AK1, BK1, SK, RS>(Mi, Nj, K, A, B, sk, epi, rs);
 }
@@ -844,6 +862,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_agg2(Params2 p) {
     const int c_begin = (1 + seg / p.F) * p.L + (seg % p.F) * La;
     const int c_end = min(c_begin + La, p.nc);
     float* tiles = GE::WIDE ? p.slots + (long)blockIdx.x * GE::AGG_TILES : sm + GE::SMALL;
+    float* BS = sm + GE::BSTG;   // MD = 128 only
     Tiles T = {};
     T.QH = tiles + GE::A_QH;
     T.DPO = tiles + GE::A_DPO;
@@ -878,8 +897,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_agg2(Params2 p) {
         // U[n][p] = sum_i Q^[i][n] exp(da_cs[t_i]) dPhiO[i][p] + dA U[n][p]; the thread that
         // owns (n, p) in the product is the only one reading and writing U[n][p]
         // A(n, i) = Q^[i][n], B(i, p) = dPhiO[i][p] scaled per i by exp(da_cs[t_i])
-        gemm<MD, NTHR, false, false, true>(N, P, rows, T.QH, T.DPO, ECS,
-                                           [&](int n, int pc, float v) { U[n * LD + pc] = v + dA * U[n * LD + pc]; });
+        gemm<MD, NTHR, false, false, true>(
+            N, P, rows, T.QH, T.DPO, ECS, [&](int n, int pc, float v) { U[n * LD + pc] = v + dA * U[n * LD + pc]; },
+            nullptr, BS);
         dprod *= dA;
     }
     sync<MD>();
@@ -980,6 +1000,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
     float* QKC = sm + GE::QKC;
     float* RS0 = sm + GE::RS0;
     float* RS1 = sm + GE::RS1;
+    float* BS = sm + GE::BSTG;   // MD = 128 only
     const float dval = p.has_d ? p.d[h] : 0.f;
 
     // dS entering the segment from the right
@@ -1047,12 +1068,12 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
             if (tj < ti && ti < cl) av = v * FAC[j] * OUT[ti * LD + tj];
             if (tj == ti && ti < cl) av = GAM[j] * QKC[ti * RR + ri * R + rj] + (i == j ? dval : 0.f);
             AM[i * LD + j] = av;
-        });
+        }, nullptr, BS);
         gemm<MD, NTHR2, true, true, false>(rows, rows, P, DPO, PS, nullptr, [&](int i, int j, float v) {
             WM[i * LD + j] = v;
             const int ri = dC.q(i), ti = i - ri * C, rj = dC.q(j), tj = j - rj * C;
             if (ti == tj && ti < cl) DQK[ti * RR + ri * R + rj] = v;
-        });
+        }, nullptr, BS);
         sync<MD>();
         if (tid < cl) {
             const int t = tid;
@@ -1089,12 +1110,12 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                 OUT[i * LD + n] = o;
                 return QH[i * LD + n] * o;
             },
-            RS0);
+            RS0, BS);
         sync<MD>();
         token_out<MD>(cl, R, C, RS0, [&](int t, float v) { p.dda_cs[tokS + c0 + t] = v; });
         // W K~: B(j, n) = k^[j][n] scaled per j by the factor (folded into A)
-        gemm<MD, NTHR2, true, false, true>(rows, N, rows, WM, KH, FAC,
-                                           [&](int i, int n, float v) { OUT[i * LD + n] += v; });
+        gemm<MD, NTHR2, true, false, true>(
+            rows, N, rows, WM, KH, FAC, [&](int i, int n, float v) { OUT[i * LD + n] += v; }, nullptr, BS);
         sync<MD>();
         // angle gradient, q part: d(a')/dθ = -e', d(e')/dθ = a' for the rotated pair (a', e')
         float dth[IS::DX];   // items (t, n): t < C, n < W <= MD / 2
@@ -1123,7 +1144,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                 OUT[j * LD + n] = o;
                 return KH[j * LD + n] * o;
             },
-            RS1);
+            RS1, BS);
         sync<MD>();
         token_out<MD>(cl, R, C, RS1, [&](int t, float v) { p.dda_cs_rev[tokS + c0 + t] = v * FAC[t]; });
         gemm<MD, NTHR2, false, false, false, true>(
@@ -1133,7 +1154,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                 OUT[j * LD + n] = o;
                 return KH[j * LD + n] * o;
             },
-            RS0);
+            RS0, BS);
         sync<MD>();
         token_out<MD>(cl, R, C, RS0, [&](int t, float v) { p.dfactor[tokS + c0 + t] = v; });
 #pragma unroll
@@ -1170,10 +1191,11 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
         sync<MD>();
 
         // ---- dPsi = kappa dS + A^T dPhiO (the latter with the same-token and d terms)
-        gemm<MD, NTHR2, true, false, false>(rows, P, N, KH, DS, nullptr,
-                                            [&](int j, int pc, float v) { OUT[j * LD + pc] = v * FAC[j] * EREV[j]; });
-        gemm<MD, NTHR2, false, false, false>(rows, P, rows, AM, DPO, nullptr,
-                                             [&](int j, int pc, float v) { OUT[j * LD + pc] += v; });
+        gemm<MD, NTHR2, true, false, false>(
+            rows, P, N, KH, DS, nullptr, [&](int j, int pc, float v) { OUT[j * LD + pc] = v * FAC[j] * EREV[j]; },
+            nullptr, BS);
+        gemm<MD, NTHR2, false, false, false>(
+            rows, P, rows, AM, DPO, nullptr, [&](int j, int pc, float v) { OUT[j * LD + pc] += v; }, nullptr, BS);
         sync<MD>();
         for (int e = tid; e < cl * (P / 4); e += NTHR2) {
             const int t = dP4.q(e), p4 = 4 * (e - t * (P / 4));
@@ -1207,7 +1229,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
             const float old = DS[n * LD + pc];
             part = __fmaf_rn(old, SC[n * LD + pc], part);
             DS[n * LD + pc] = v + dA * old;
-        });
+        }, nullptr, BS);
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
         if ((tid & 63) == 0) RED[tid >> 6] = part;
