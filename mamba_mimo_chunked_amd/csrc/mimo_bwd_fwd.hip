@@ -191,7 +191,7 @@ struct Plan {
     int RP, CT, MT, NW, NT, PT, Cp, W, nc, L, nseg, F, nsub;
     bool ex;   // the shape-exact kernel instances apply
     size_t off_agg, off_decay, off_po, off_pz, ws_bytes;
-    int lds_agg, lds_main;
+    int lds_agg, lds_main, lds_states;   // lds_states: the no-y chunk pass (k_agg in ST mode)
 };
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -267,9 +267,13 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl, bool fwd = false) {
     pl->NW = (pl->MT == 128 && pl->PT >= 64) ? 8 : 4;
     pl->nc = (int)((S + C - 1) / C);
     // segments: about two workgroups per compute unit, so that every
-    // workgroup of the chunk kernel is resident at once
+    // workgroup of the chunk kernel is resident at once. A call that needs no y
+    // (states and qk_dot only) runs the aggregate's state walk as its chunk pass,
+    // whose time is the chain of chunk steps of one workgroup: it takes twice as many
+    // shorter segments (about four workgroups per compute unit for four-wave tiles).
     pl->ex = !force_generic() && R == RP && N == pl->NT && P == pl->PT && C == pl->Cp && rd == 4;
-    const int64_t target = 512;
+    const bool states_only = !fwd && a->mimo_o == nullptr && a->z == nullptr;
+    const int64_t target = states_only && pl->NW == 4 ? 1024 : 512;
     int64_t L = (pl->nc * B * H + target - 1) / target;
     if (L < 1) L = 1;
     if (L > pl->nc) L = pl->nc;
@@ -306,6 +310,7 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl, bool fwd = false) {
     Lds la = lds_layout(RP, CT, pl->NT, pl->PT, (int)C, pl->W, false);
     pl->lds_main = lm.total;
     pl->lds_agg = la.total;
+    pl->lds_states = la.total + pl->NT * (pl->PT + 8) * 2;
     // the token-tile reduction of the dmimo partials reuses LDS from offset 0
     if (CT > 1) {
         const int red = 2 * CT * RP * pl->PT * 4;
@@ -339,6 +344,120 @@ mimo_status set_lds(kfn f, int bytes) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(f), hipFuncAttributeMaxDynamicSharedMemorySize, bytes) !=
         hipSuccess)
         return fail(MIMO_ERR_HIP, "hipFuncSetAttribute(MaxDynamicSharedMemorySize=%d) failed", bytes);
+    return MIMO_OK;
+}
+
+// qk_dot of the calls that need no y (their chunk pass is k_agg's state walk):
+// qk_dot[b,h,t,r,r2] = bf16(q0[t,r] . k0[t,r2]), q0 = bf16(q + bf16(q_bias)) and k0
+// likewise (biased, unrotated). One workgroup per (batch, q/k group, 16 tokens): the
+// group's raw q and k rows of the 16 tokens are staged in LDS once ([2][16][R][NT]
+// bf16, zero past N and the sequence), and wave w serves heads w, w + 4, ... of the
+// group. A head's dots are the diagonals of 16 x 16 MFMA tiles (rows the tokens' q0 of
+// rank r, columns their k0 of rank r2), built from the same fragments and steps as the
+// chunk pass's qk_dot, so both give the same bits. Lane (l16, q4) with q4 == l16 / 4
+// ends up holding every dot of token l16 and writes them out.
+template <int NT>
+__global__ __launch_bounds__(256) void k_qk(Params p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned short* sx = reinterpret_cast<unsigned short*>(smem);   // [2][16][R][NT]: q, then k
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
+    const int ntt = (p.S + 15) / 16;
+    const int unit = blockIdx.x;   // (b * G + g) * ntt + tile
+    const int bg = unit / ntt, tile = unit - bg * ntt;
+    const int b = bg / p.G, g = bg - b * p.G, hpg = p.H / p.G;
+    const int R = p.R, N = p.N, t0 = 16 * tile;
+    constexpr int KS = NT / 32, NT8 = NT / 8;
+    // this wave's bf16 biases of its current head: [2][R][NT] (q, then k), zero past N
+    unsigned short* sb = sx + 2 * 16 * R * NT + wave * 2 * R * NT;
+    // stage: items (which, token, rank, 8 columns)
+    const int items = 2 * 16 * R * NT8;
+    for (int e = tid; e < items; e += 256) {
+        const int c8 = e % NT8, rest = e / NT8;
+        const int r = rest % R, tk = (rest / R) % 16, which = rest / (16 * R);
+        const int t = t0 + tk, col = 8 * c8;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (t < p.S && col < N) {
+            const unsigned short* x = which ? p.k : p.q;
+            w = *reinterpret_cast<const u32x4*>(x + ((((long)b * p.S + t) * R + r) * p.G + g) * N + col);
+        }
+        *reinterpret_cast<u32x4*>(sx + ((which * 16 + tk) * R + r) * NT + col) = w;
+    }
+    __syncthreads();
+    const int t = t0 + l16;
+    const bool diag = q4 == (l16 >> 2) && t < p.S;
+    const int v = l16 & 3;
+    // fragment of token l16, rank r: columns 32 ks + 8 q4 .. + 7, biased and rounded
+    // (zero past N, where raw and bias are zero, and past the sequence)
+    auto frag = [&](int which, int r, int ks) -> u32x4 {
+        const int col = 32 * ks + 8 * q4;
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + ((which * 16 + l16) * R + r) * NT + col);
+        const u32x4 bb = *reinterpret_cast<const u32x4*>(sb + (which * R + r) * NT + col);
+        float x[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            x[2 * d] = rnd(lo16(raw[d]) + lo16(bb[d]));
+            x[2 * d + 1] = rnd(hi16(raw[d]) + hi16(bb[d]));
+        }
+        return t < p.S ? pack8(x) : u32x4{0u, 0u, 0u, 0u};
+    };
+    for (int hh = wave; hh < hpg; hh += 4) {
+        const int h = g * hpg + hh;
+        // the head's biases, rounded to bf16, into this wave's slice (a wave's own LDS
+        // writes are visible to its later reads once they have completed)
+        for (int e = lane; e < 2 * R * NT8; e += 64) {
+            const int c8 = e % NT8, rest = e / NT8, r = rest % R, which = rest / R, col = 8 * c8;
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (col < N) {
+                const float* bp = (which ? p.k_bias : p.q_bias) + ((long)h * R + r) * N + col;
+                const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
+                w = u32x4{pk2(b0[0], b0[1]), pk2(b0[2], b0[3]), pk2(b1[0], b1[1]), pk2(b1[2], b1[3])};
+            }
+            *reinterpret_cast<u32x4*>(sb + (which * R + r) * NT + col) = w;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+        u32x4 kf[8][KS], qf[8][KS];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                kf[r][ks] = r < R ? frag(1, r, ks) : u32x4{0u, 0u, 0u, 0u};
+                qf[r][ks] = r < R ? frag(0, r, ks) : u32x4{0u, 0u, 0u, 0u};
+            }
+        unsigned short* out = p.qk_dot + ((long)(b * p.H + h) * p.S + t) * R * R;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if (r >= R) break;
+#pragma unroll
+            for (int r2 = 0; r2 < 8; ++r2) {
+                if (r2 >= R) break;
+                f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) a4 = mfma(qf[r][ks], kf[r2][ks], a4);
+                const float x01 = (v & 1) ? a4[1] : a4[0], x23 = (v & 1) ? a4[3] : a4[2];
+                if (diag) out[r * R + r2] = bits16(rnd((v & 2) ? x23 : x01));
+            }
+        }
+        // every lane is done reading the slice before the next head overwrites it
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+mimo_status launch_qk(const Params& p, int NT, hipStream_t st) {
+    const unsigned grid = (unsigned)((long)p.B * p.G * ((p.S + 15) / 16));
+    // the staged rows and four waves' bias slices: at most 64 + 16 KB (R <= 8, NT <= 128)
+    const int lds = (2 * 16 * p.R * NT + 4 * 2 * p.R * NT) * 2;
+    Params pc = p;
+    void* args[] = {&pc};
+    const void* f = NT == 32 ? reinterpret_cast<const void*>(&k_qk<32>)
+                  : NT == 64 ? reinterpret_cast<const void*>(&k_qk<64>)
+                             : reinterpret_cast<const void*>(&k_qk<128>);
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+        return fail(MIMO_ERR_HIP, "hipFuncSetAttribute(MaxDynamicSharedMemorySize=%d) failed", lds);
+    const hipError_t e = hipLaunchKernel(f, dim3(grid), dim3(256), args, (size_t)lds, st);
+    if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return MIMO_OK;
 }
 
@@ -909,11 +1028,18 @@ static mimo_status run(const mimo_bwd_fwd_args* a, uint16_t* out, void* stream, 
     const int ti = tidx(pl.NT) * 3 + tidx(pl.PT);
     const bool ex = pl.ex;
     kfn kmain = fam->main[ti];
+    int lds_main = pl.lds_main;
+    // without y (no reduced dout, no z) the outputs are the states and qk_dot: the chunk
+    // pass is the aggregate's state walk over whole segments (k_agg in ST mode) and
+    // qk_dot a token-parallel kernel
+    const bool states_only = !fwd && !p.need_y;
     if (fwd) {
         if (ex && p.reduce_o && p.has_z) kmain = fam->main_ex_fwd[ti];
-    } else {
-        if (ex && !p.need_y) kmain = fam->main_ex_noy[ti];
-        if (ex && p.reduce_o && p.has_z) kmain = fam->main_ex_rz[ti];
+    } else if (states_only) {
+        kmain = ex ? fam->states_ex[ti] : fam->states[ti];
+        lds_main = pl.lds_states;
+    } else if (ex && p.reduce_o && p.has_z) {
+        kmain = fam->main_ex_rz[ti];
     }
     const kfn kagg = ex ? fam->agg_ex[ti] : fam->agg[ti];
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -927,7 +1053,7 @@ static mimo_status run(const mimo_bwd_fwd_args* a, uint16_t* out, void* stream, 
     if (events != nullptr)
         for (int i = 0; i < MIMO_TIMED_EVENTS; ++i)
             if (events[i] == nullptr) return fail(MIMO_ERR_VALUE, "timing event %d is NULL", i);
-    if ((s = set_lds(kmain, pl.lds_main)) != MIMO_OK) return s;
+    if ((s = set_lds(kmain, lds_main)) != MIMO_OK) return s;
     if ((s = mark(0)) != MIMO_OK) return s;
     if (pl.nseg > 1) {
         if ((s = set_lds(kagg, pl.lds_agg)) != MIMO_OK) return s;
@@ -938,7 +1064,8 @@ static mimo_status run(const mimo_bwd_fwd_args* a, uint16_t* out, void* stream, 
         return s;
     }
     if ((s = mark(2)) != MIMO_OK) return s;
-    if ((s = launch(kmain, dim3(grid_blocks(p, pl.nseg)), dim3(pl.NW * 64), pl.lds_main, st, p)) != MIMO_OK) return s;
+    if ((s = launch(kmain, dim3(grid_blocks(p, pl.nseg)), dim3(pl.NW * 64), lds_main, st, p)) != MIMO_OK) return s;
+    if (states_only && (s = launch_qk(p, pl.NT, st)) != MIMO_OK) return s;
     if ((s = mark(3)) != MIMO_OK) return s;
     if (pl.nseg > 1 && p.need_y && !fwd)
         if ((s = launch_finish(p, st)) != MIMO_OK) return s;

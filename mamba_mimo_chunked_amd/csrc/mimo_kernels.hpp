@@ -867,7 +867,12 @@ __device__ __forceinline__ Params specialise(const Params& pin) {
 // ---------------------------------------------------------------- segment aggregate
 // U_s = state added by segment s from a zero start: U <- U*exp(da_cs[last]) + kappa^T Psi
 // per chunk; also the product of the chunk decays.
-template <int RP, int CT, int NT, int PT, bool EX>
+// ST: the chunk pass of a call that needs no y (neither reduced dout nor z: the outputs
+// are the states and qk_dot only). The same walk over whole segments, from the state
+// entering the segment; at the top of chunk c the state is written out as states[c] =
+// bf16(S) through an LDS tile [NT][PT + 8] after the kernel's other LDS, so the global
+// stores are 16-byte pieces of consecutive rows. qk_dot comes from k_qk.
+template <int RP, int CT, int NT, int PT, bool EX, bool ST = false>
 __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params pin) {
     const Params p = specialise<RP, CT, NT, PT, EX, -1>(pin);
     using T = Tile<RP, CT, NT, PT>;
@@ -884,7 +889,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
     int seg, bh;
-    if (!map_block(p, p.nsub, seg, bh)) return;
+    if (!map_block(p, ST ? p.nseg : p.nsub, seg, bh)) return;
     // block-uniform indices, pinned to scalar registers (the divisions by run-time
     // sizes leave them in vector registers, and every address derived from them
     // would follow)
@@ -892,13 +897,22 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
     bh = uni(bh);
     const int b = uni(bh / p.H), h = uni(bh - b * p.H);
     const int g = uni(h / (p.H / p.G));
-    // sub-segment seg is piece k of segment s; pieces hold ceil(L / F) chunks, the last
-    // one of a segment fewer (the host keeps every piece non-empty); all chunks are full
-    const int La = (p.L + p.F - 1) / p.F;
-    const int s_ = uni(seg / p.F), k_ = seg - s_ * p.F;
-    const int c_begin = s_ * p.L + k_ * La;
-    const int c_end = min(c_begin + La, s_ * p.L + p.L);
+    int c_begin, c_end;
+    if constexpr (ST) {
+        c_begin = seg * p.L;
+        c_end = min(c_begin + p.L, p.nc);
+    } else {
+        // sub-segment seg is piece k of segment s; pieces hold ceil(L / F) chunks, the
+        // last one of a segment fewer (the host keeps every piece non-empty); all chunks
+        // are full
+        const int La = (p.L + p.F - 1) / p.F;
+        const int s_ = uni(seg / p.F), k_ = seg - s_ * p.F;
+        c_begin = s_ * p.L + k_ * La;
+        c_end = min(c_begin + La, s_ * p.L + p.L);
+    }
     const int R = p.R;
+    constexpr int SPP = PT + 8;   // row pitch (halves) of the ST state tile
+    unsigned short* sSt = reinterpret_cast<unsigned short*>(smem + L.total);
     // With one 8-column group per thread and rotary divisor 4, the threads of the
     // first half hold exactly the rotated groups; the second half fills Psi.
     constexpr bool SPLIT = SG::LITE && EX && T::QK_IT == 1 && T::MT * (NT / 32) == T::NTHR / 2;
@@ -919,6 +933,23 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
     f32x4 U[T::STW];
 #pragma unroll
     for (int w = 0; w < T::STW; ++w) U[w] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ST && seg > 0) {
+        // the state entering the segment (after the last piece of the segment before it)
+        const float* E = p.agg + ((long)bh * p.nsub + seg * p.F - 1) * p.N * p.P;
+#pragma unroll
+        for (int w = 0; w < T::STW; ++w) {
+            const int u = wave + w * T::NW;
+            if (T::ST_FULL || u < T::ST) {
+                const int nt = u / T::PTT, pt = u % T::PTT;
+                const int pc = 16 * pt + l16;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int n = 16 * nt + 4 * q4 + v;
+                    if (n < p.N && pc < p.P) U[w][v] = E[n * p.P + pc];
+                }
+            }
+        }
+    }
     float dprod = 1.f;
 
     for (int c = c_begin; c < c_end; ++c) {
@@ -940,7 +971,33 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
             load_small(p, it, b, h, bh, c, c0, cl, sr);
         }
         if constexpr (!SG::QKON) load_qk(p, it, b, c0, cl, in);
+        if constexpr (ST) {
+            // bf16(S entering chunk c) into the state tile, rows n, columns p
+#pragma unroll
+            for (int w = 0; w < T::STW; ++w) {
+                const int u = wave + w * T::NW;
+                if (T::ST_FULL || u < T::ST) {
+                    const int nt = u / T::PTT, pt = u % T::PTT;
+                    const int pc = 16 * pt + l16;
+                    const unsigned lo = pk2(U[w][0], U[w][1]), hi = pk2(U[w][2], U[w][3]);
+                    unsigned short* d = sSt + (16 * nt + 4 * q4) * SPP + pc;
+                    d[0] = static_cast<unsigned short>(lo);
+                    d[SPP] = static_cast<unsigned short>(lo >> 16);
+                    d[2 * SPP] = static_cast<unsigned short>(hi);
+                    d[3 * SPP] = static_cast<unsigned short>(hi >> 16);
+                }
+            }
+        }
         bar();   // chunk c's staging loads of every thread have landed; previous chunk done with LDS
+        if constexpr (ST) {
+            // states[c]: consecutive threads take consecutive 16-byte pieces of a row
+            unsigned short* dst = p.states + ((long)bh * p.nc + c) * p.N * p.P;
+            const int P8 = p.P / 8;
+            for (int e = static_cast<int>(threadIdx.x); e < p.N * P8; e += T::NTHR) {
+                const int n = e / P8, p8 = 8 * (e - n * P8);
+                *reinterpret_cast<u32x4*>(dst + n * p.P + p8) = lds_ld<u32x4>(sSt + n * SPP + p8);
+            }
+        }
         phase0<RP, CT, NT, PT, false, EX>(p, it, c0, cl, smb, sr, smem, L);
         bar();
         // kappa = bf16(bf16(rot(bf16(k + bf16(k_bias))) * factor) * exp(da_cs_rev)), row-major;
@@ -998,6 +1055,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
         }
         dprod *= dl;
     }
+    if constexpr (ST) return;
     float* out = p.agg + ((long)bh * p.nsub + seg) * p.N * p.P;
 #pragma unroll
     for (int w = 0; w < T::STW; ++w) {
@@ -1705,7 +1763,8 @@ typedef void (*kfn)(Params);
 // with idx(32, 64, 128) = 0, 1, 2: the generic instances and the shape-exact ones.
 struct Family {
     kfn agg[9], agg_ex[9];
-    kfn main[9], main_ex_noy[9], main_ex_rz[9], main_ex_fwd[9];
+    kfn main[9], main_ex_rz[9], main_ex_fwd[9];
+    kfn states[9], states_ex[9];   // the chunk pass of calls without y (k_agg in ST mode)
 };
 
 #define MIMO_NP_LIST(F, RP, CT)                                                                             \
@@ -1714,14 +1773,16 @@ struct Family {
 #define MIMO_AGG_FN(RP, CT, NT, PT) k_agg<RP, CT, NT, PT, false>
 #define MIMO_AGG_EX_FN(RP, CT, NT, PT) k_agg<RP, CT, NT, PT, true>
 #define MIMO_MAIN_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT, false, -1>
-#define MIMO_MAIN_EX0_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT, true, 0>
 #define MIMO_MAIN_EX1_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT, true, 1>
 #define MIMO_MAIN_EX2_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT, true, 2>
+#define MIMO_ST_FN(RP, CT, NT, PT) k_agg<RP, CT, NT, PT, false, true>
+#define MIMO_ST_EX_FN(RP, CT, NT, PT) k_agg<RP, CT, NT, PT, true, true>
 #define MIMO_FAMILY(RP, CT)                                                                               \
     const Family* family_rp##RP##_ct##CT() {                                                              \
         static const Family f = {{MIMO_NP_LIST(MIMO_AGG_FN, RP, CT)},     {MIMO_NP_LIST(MIMO_AGG_EX_FN, RP, CT)}, \
-                                 {MIMO_NP_LIST(MIMO_MAIN_FN, RP, CT)},    {MIMO_NP_LIST(MIMO_MAIN_EX0_FN, RP, CT)}, \
-                                 {MIMO_NP_LIST(MIMO_MAIN_EX1_FN, RP, CT)}, {MIMO_NP_LIST(MIMO_MAIN_EX2_FN, RP, CT)}}; \
+                                 {MIMO_NP_LIST(MIMO_MAIN_FN, RP, CT)},    {MIMO_NP_LIST(MIMO_MAIN_EX1_FN, RP, CT)}, \
+                                 {MIMO_NP_LIST(MIMO_MAIN_EX2_FN, RP, CT)}, \
+                                 {MIMO_NP_LIST(MIMO_ST_FN, RP, CT)},      {MIMO_NP_LIST(MIMO_ST_EX_FN, RP, CT)}}; \
         return &f;                                                                                        \
     }
 #define MIMO_DECL_FAMILY(RP, CT) const Family* family_rp##RP##_ct##CT();
