@@ -349,114 +349,121 @@ mimo_status set_lds(kfn f, int bytes) {
 
 // qk_dot of the calls that need no y (their chunk pass is k_agg's state walk):
 // qk_dot[b,h,t,r,r2] = bf16(q0[t,r] . k0[t,r2]), q0 = bf16(q + bf16(q_bias)) and k0
-// likewise (biased, unrotated). One workgroup per (batch, q/k group, 16 tokens): the
-// group's raw q and k rows of the 16 tokens are staged in LDS once ([2][16][R][NT]
-// bf16, zero past N and the sequence), and wave w serves heads w, w + 4, ... of the
-// group. A head's dots are the diagonals of 16 x 16 MFMA tiles (rows the tokens' q0 of
-// rank r, columns their k0 of rank r2), built from the same fragments and steps as the
-// chunk pass's qk_dot, so both give the same bits. Lane (l16, q4) with q4 == l16 / 4
-// ends up holding every dot of token l16 and writes them out.
+// likewise (biased, unrotated). One workgroup per (batch, head, 64 tokens), wave w
+// taking tokens 16 w .. 16 w + 15. Each lane issues the loads of all its q and k
+// fragments at once while the workgroup stages the head's rounded biases in LDS, so a
+// workgroup waits for one memory round trip. A head's dots are the diagonals of 16 x 16
+// MFMA tiles (rows the tokens' q0 of rank r, columns their k0 of rank r2), built from
+// the same fragments and steps as the chunk pass's qk_dot, so both give the same bits.
+// Lane (l16, q4) with q4 == l16 / 4 ends up holding every dot of token l16 and writes
+// them out.
 template <int NT>
 __global__ __launch_bounds__(256) void k_qk(Params p) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    unsigned short* sx = reinterpret_cast<unsigned short*>(smem);   // [2][16][R][NT]: q, then k
+    __shared__ __align__(16) unsigned short sb[2 * 8 * NT];   // [2][R][NT] bf16 biases: q, then k
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
-    const int ntt = (p.S + 15) / 16;
-    const int unit = blockIdx.x;   // (b * G + g) * ntt + tile
-    const int bg = unit / ntt, tile = unit - bg * ntt;
-    const int b = bg / p.G, g = bg - b * p.G, hpg = p.H / p.G;
-    const int R = p.R, N = p.N, t0 = 16 * tile;
+    const int n64 = (p.S + 63) / 64;
+    const int bh = blockIdx.x / n64, tile = blockIdx.x - bh * n64;
+    const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
+    const int R = p.R, N = p.N, t = 64 * tile + 16 * wave + l16;
+    const bool tok = t < p.S;
     constexpr int KS = NT / 32, NT8 = NT / 8;
-    // this wave's bf16 biases of its current head: [2][R][NT] (q, then k), zero past N
-    unsigned short* sb = sx + 2 * 16 * R * NT + wave * 2 * R * NT;
-    // stage: items (which, token, rank, 8 columns)
-    const int items = 2 * 16 * R * NT8;
-    for (int e = tid; e < items; e += 256) {
-        const int c8 = e % NT8, rest = e / NT8;
-        const int r = rest % R, tk = (rest / R) % 16, which = rest / (16 * R);
-        const int t = t0 + tk, col = 8 * c8;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (t < p.S && col < N) {
-            const unsigned short* x = which ? p.k : p.q;
-            w = *reinterpret_cast<const u32x4*>(x + ((((long)b * p.S + t) * R + r) * p.G + g) * N + col);
+    // this lane's raw fragments: rank r, columns 32 ks + 8 q4 .. + 7 (zero past N, R or S)
+    u32x4 qf[8][KS], kf[8][KS];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int col = 32 * ks + 8 * q4;
+            qf[r][ks] = kf[r][ks] = u32x4{0u, 0u, 0u, 0u};
+            if (r < R && tok && col < N) {
+                const long src = ((((long)b * p.S + t) * R + r) * p.G + g) * N + col;
+                qf[r][ks] = *reinterpret_cast<const u32x4*>(p.q + src);
+                kf[r][ks] = *reinterpret_cast<const u32x4*>(p.k + src);
+            }
         }
-        *reinterpret_cast<u32x4*>(sx + ((which * 16 + tk) * R + r) * NT + col) = w;
+    for (int e = tid; e < 2 * R * NT8; e += 256) {
+        const int c8 = e % NT8, rest = e / NT8, r = rest % R, which = rest / R, col = 8 * c8;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (col < N) {
+            const float* bp = (which ? p.k_bias : p.q_bias) + ((long)h * R + r) * N + col;
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
+            w = u32x4{pk2(b0[0], b0[1]), pk2(b0[2], b0[3]), pk2(b1[0], b1[1]), pk2(b1[2], b1[3])};
+        }
+        *reinterpret_cast<u32x4*>(sb + (which * R + r) * NT + col) = w;
     }
     __syncthreads();
-    const int t = t0 + l16;
-    const bool diag = q4 == (l16 >> 2) && t < p.S;
-    const int v = l16 & 3;
-    // fragment of token l16, rank r: columns 32 ks + 8 q4 .. + 7, biased and rounded
-    // (zero past N, where raw and bias are zero, and past the sequence)
-    auto frag = [&](int which, int r, int ks) -> u32x4 {
-        const int col = 32 * ks + 8 * q4;
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + ((which * 16 + l16) * R + r) * NT + col);
-        const u32x4 bb = *reinterpret_cast<const u32x4*>(sb + (which * R + r) * NT + col);
-        float x[8];
+    // biased and rounded, in place (past the sequence the fragment stays zero)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            x[2 * d] = rnd(lo16(raw[d]) + lo16(bb[d]));
-            x[2 * d + 1] = rnd(hi16(raw[d]) + hi16(bb[d]));
-        }
-        return t < p.S ? pack8(x) : u32x4{0u, 0u, 0u, 0u};
-    };
-    for (int hh = wave; hh < hpg; hh += 4) {
-        const int h = g * hpg + hh;
-        // the head's biases, rounded to bf16, into this wave's slice (a wave's own LDS
-        // writes are visible to its later reads once they have completed)
-        for (int e = lane; e < 2 * R * NT8; e += 64) {
-            const int c8 = e % NT8, rest = e / NT8, r = rest % R, which = rest / R, col = 8 * c8;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (col < N) {
-                const float* bp = (which ? p.k_bias : p.q_bias) + ((long)h * R + r) * N + col;
-                const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
-                w = u32x4{pk2(b0[0], b0[1]), pk2(b0[2], b0[3]), pk2(b1[0], b1[1]), pk2(b1[2], b1[3])};
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (r >= R || !tok) continue;
+            const int col = 32 * ks + 8 * q4;
+#pragma unroll
+            for (int which = 0; which < 2; ++which) {
+                const u32x4 raw = which ? kf[r][ks] : qf[r][ks];
+                const u32x4 bb = *reinterpret_cast<const u32x4*>(sb + (which * R + r) * NT + col);
+                float x[8];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    x[2 * d] = rnd(lo16(raw[d]) + lo16(bb[d]));
+                    x[2 * d + 1] = rnd(hi16(raw[d]) + hi16(bb[d]));
+                }
+                if (which)
+                    kf[r][ks] = pack8(x);
+                else
+                    qf[r][ks] = pack8(x);
             }
-            *reinterpret_cast<u32x4*>(sb + (which * R + r) * NT + col) = w;
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_wave_barrier();
-        u32x4 kf[8][KS], qf[8][KS];
+    const bool diag = q4 == (l16 >> 2) && tok;
+    const int v = l16 & 3;
+    float dv[8][8];   // the lane's dots (its token's, on the diagonal lanes)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+#pragma unroll
+        for (int r2 = 0; r2 < 8; ++r2) {
+            dv[r][r2] = 0.f;
+            if (r >= R || r2 >= R) continue;
+            f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) a4 = mfma(qf[r][ks], kf[r2][ks], a4);
+            const float x01 = (v & 1) ? a4[1] : a4[0], x23 = (v & 1) ? a4[3] : a4[2];
+            dv[r][r2] = (v & 2) ? x23 : x01;
+        }
+    }
+    if (!diag) return;
+    // the token's R*R dots are contiguous: 8- or 16-byte pieces where R*R allows
+    unsigned short* out = p.qk_dot + ((long)bh * p.S + t) * R * R;
+    if (R == 4) {
+#pragma unroll
+        for (int r = 0; r < 4; r += 2)
+            *reinterpret_cast<u32x4*>(out + 4 * r) =
+                u32x4{pk2(dv[r][0], dv[r][1]), pk2(dv[r][2], dv[r][3]), pk2(dv[r + 1][0], dv[r + 1][1]),
+                      pk2(dv[r + 1][2], dv[r + 1][3])};
+    } else if (R == 8) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            *reinterpret_cast<u32x4*>(out + 8 * r) =
+                u32x4{pk2(dv[r][0], dv[r][1]), pk2(dv[r][2], dv[r][3]), pk2(dv[r][4], dv[r][5]), pk2(dv[r][6], dv[r][7])};
+    } else if (R == 2) {
+        *reinterpret_cast<u32x2*>(out) = u32x2{pk2(dv[0][0], dv[0][1]), pk2(dv[1][0], dv[1][1])};
+    } else {
 #pragma unroll
         for (int r = 0; r < 8; ++r)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                kf[r][ks] = r < R ? frag(1, r, ks) : u32x4{0u, 0u, 0u, 0u};
-                qf[r][ks] = r < R ? frag(0, r, ks) : u32x4{0u, 0u, 0u, 0u};
-            }
-        unsigned short* out = p.qk_dot + ((long)(b * p.H + h) * p.S + t) * R * R;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            if (r >= R) break;
-#pragma unroll
-            for (int r2 = 0; r2 < 8; ++r2) {
-                if (r2 >= R) break;
-                f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) a4 = mfma(qf[r][ks], kf[r2][ks], a4);
-                const float x01 = (v & 1) ? a4[1] : a4[0], x23 = (v & 1) ? a4[3] : a4[2];
-                if (diag) out[r * R + r2] = bits16(rnd((v & 2) ? x23 : x01));
-            }
-        }
-        // every lane is done reading the slice before the next head overwrites it
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_wave_barrier();
+            for (int r2 = 0; r2 < 8; ++r2)
+                if (r < R && r2 < R) out[r * R + r2] = bits16(rnd(dv[r][r2]));
     }
 }
 
 mimo_status launch_qk(const Params& p, int NT, hipStream_t st) {
-    const unsigned grid = (unsigned)((long)p.B * p.G * ((p.S + 15) / 16));
-    // the staged rows and four waves' bias slices: at most 64 + 16 KB (R <= 8, NT <= 128)
-    const int lds = (2 * 16 * p.R * NT + 4 * 2 * p.R * NT) * 2;
+    const unsigned grid = (unsigned)((long)p.B * p.H * ((p.S + 63) / 64));
     Params pc = p;
     void* args[] = {&pc};
     const void* f = NT == 32 ? reinterpret_cast<const void*>(&k_qk<32>)
                   : NT == 64 ? reinterpret_cast<const void*>(&k_qk<64>)
                              : reinterpret_cast<const void*>(&k_qk<128>);
-    if (lds > 64 * 1024 &&
-        hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-        return fail(MIMO_ERR_HIP, "hipFuncSetAttribute(MaxDynamicSharedMemorySize=%d) failed", lds);
-    const hipError_t e = hipLaunchKernel(f, dim3(grid), dim3(256), args, (size_t)lds, st);
+    const hipError_t e = hipLaunchKernel(f, dim3(grid), dim3(256), args, 0, st);
     if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return MIMO_OK;
 }
