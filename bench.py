@@ -72,11 +72,6 @@ _COMMON = [_CSRC / "mimo_kernels.hpp", _CSRC / "mimo_bwd_fwd.hip"]
 KERNEL_SOURCES = {"bwd_fwd": _COMMON, "fwd": _COMMON,
                   "bwd_fwd_fp32": _COMMON + [_CSRC / "mimo_f32.hpp"], "siso": _COMMON + [_CSRC / "mimo_f32.hpp"],
                   "bwd_bwd": _COMMON + [_CSRC / "mimo_bwd2.hpp"]}
-TRAFFIC_FILES = {"bwd_fwd": ROOT / "profiles" / "traffic_bwd_fwd_perf_s8192.json",
-                 "fwd": ROOT / "profiles" / "k_main_fwd_perf_s8192_traffic.json",
-                 "bwd_fwd_fp32": ROOT / "profiles" / "k_chunk32_perf_s8192_traffic.json",
-                 "siso": ROOT / "profiles" / "k_chunk32_siso_s8192_k128_traffic.json",
-                 "bwd_bwd": ROOT / "profiles" / "k_main2_perf_s8192_traffic.json"}
 
 
 def log(msg):
@@ -526,11 +521,7 @@ def main():
     alu_tops = alu_ops / (main_ms * 1e-3) / 1e12
     mfma_tflops = alg_flops / (main_ms * 1e-3) / 1e12
     traffic, traffic_call, per_kernel_traffic = None, None, None
-    tfile = TRAFFIC_FILES[op]
-    if op in ("bwd_fwd", "fwd"):
-        tfile = ROOT / "profiles" / f"traffic_{op}_{a.config}.json"
-        if not tfile.exists():
-            tfile = TRAFFIC_FILES[op]
+    tfile = ROOT / "profiles" / f"traffic_{op}_{a.config}.json"
     if tfile.exists():
         rec = json.loads(tfile.read_text())
         if rec.get("source_sha256") == source_hash(op) and rec.get("workload") == a.config:

@@ -44,6 +44,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <initializer_list>
 #include <mutex>
 #include <string>
@@ -349,121 +350,150 @@ mimo_status set_lds(kfn f, int bytes) {
 
 // qk_dot of the calls that need no y (their chunk pass is k_agg's state walk):
 // qk_dot[b,h,t,r,r2] = bf16(q0[t,r] . k0[t,r2]), q0 = bf16(q + bf16(q_bias)) and k0
-// likewise (biased, unrotated). One workgroup per (batch, head, 64 tokens), wave w
-// taking tokens 16 w .. 16 w + 15. Each lane issues the loads of all its q and k
-// fragments at once while the workgroup stages the head's rounded biases in LDS, so a
-// workgroup waits for one memory round trip. A head's dots are the diagonals of 16 x 16
-// MFMA tiles (rows the tokens' q0 of rank r, columns their k0 of rank r2), built from
-// the same fragments and steps as the chunk pass's qk_dot, so both give the same bits.
-// Lane (l16, q4) with q4 == l16 / 4 ends up holding every dot of token l16 and writes
-// them out.
-template <int NT>
+// likewise (biased, unrotated). One workgroup per (batch, q/k group, 16 tokens): in one
+// round of loads it stages the group's raw q and k rows of the 16 tokens ([2][16][R][NT]
+// bf16, read once for all the group's heads) and the rounded biases of up to eight of
+// the group's heads ([8][2][R][NT] bf16; zero past N and the sequence); wave w then
+// serves heads w, w + 4, ... of the batch, and further batches of heads restage the
+// biases. A head's dots are the diagonals of 16 x 16 MFMA tiles
+// (rows the tokens' q0 of rank r, columns their k0 of rank r2), built from the same
+// fragments and steps as the chunk pass's qk_dot, so both give the same bits. Lane
+// (l16, q4) with q4 == l16 / 4 ends up holding every dot of token l16 and stores them,
+// in 8- or 16-byte pieces where R allows.
+template <int NT, int RP>   // RP: the rank count rounded up to a power of two (register arrays)
 __global__ __launch_bounds__(256) void k_qk(Params p) {
-    __shared__ __align__(16) unsigned short sb[2 * 8 * NT];   // [2][R][NT] bf16 biases: q, then k
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned short* sx = reinterpret_cast<unsigned short*>(smem);   // [2][16][R][NT]: q, then k
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
-    const int n64 = (p.S + 63) / 64;
-    const int bh = blockIdx.x / n64, tile = blockIdx.x - bh * n64;
-    const int b = bh / p.H, h = bh - b * p.H, g = h / (p.H / p.G);
-    const int R = p.R, N = p.N, t = 64 * tile + 16 * wave + l16;
-    const bool tok = t < p.S;
+    const int ntt = (p.S + 15) / 16;
+    const int unit = blockIdx.x;   // (b * G + g) * ntt + tile
+    const int bg = unit / ntt, tile = unit - bg * ntt;
+    const int b = bg / p.G, g = bg - b * p.G, hpg = p.H / p.G;
+    const int R = p.R, N = p.N, t0 = 16 * tile;
     constexpr int KS = NT / 32, NT8 = NT / 8;
-    // this lane's raw fragments: rank r, columns 32 ks + 8 q4 .. + 7 (zero past N, R or S)
-    u32x4 qf[8][KS], kf[8][KS];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int col = 32 * ks + 8 * q4;
-            qf[r][ks] = kf[r][ks] = u32x4{0u, 0u, 0u, 0u};
-            if (r < R && tok && col < N) {
-                const long src = ((((long)b * p.S + t) * R + r) * p.G + g) * N + col;
-                qf[r][ks] = *reinterpret_cast<const u32x4*>(p.q + src);
-                kf[r][ks] = *reinterpret_cast<const u32x4*>(p.k + src);
-            }
-        }
-    for (int e = tid; e < 2 * R * NT8; e += 256) {
-        const int c8 = e % NT8, rest = e / NT8, r = rest % R, which = rest / R, col = 8 * c8;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (col < N) {
-            const float* bp = (which ? p.k_bias : p.q_bias) + ((long)h * R + r) * N + col;
-            const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
-            w = u32x4{pk2(b0[0], b0[1]), pk2(b0[2], b0[3]), pk2(b1[0], b1[1]), pk2(b1[2], b1[3])};
-        }
-        *reinterpret_cast<u32x4*>(sb + (which * R + r) * NT + col) = w;
-    }
-    __syncthreads();
-    // biased and rounded, in place (past the sequence the fragment stays zero)
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (r >= R || !tok) continue;
-            const int col = 32 * ks + 8 * q4;
-#pragma unroll
-            for (int which = 0; which < 2; ++which) {
-                const u32x4 raw = which ? kf[r][ks] : qf[r][ks];
-                const u32x4 bb = *reinterpret_cast<const u32x4*>(sb + (which * R + r) * NT + col);
-                float x[8];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    x[2 * d] = rnd(lo16(raw[d]) + lo16(bb[d]));
-                    x[2 * d + 1] = rnd(hi16(raw[d]) + hi16(bb[d]));
-                }
-                if (which)
-                    kf[r][ks] = pack8(x);
-                else
-                    qf[r][ks] = pack8(x);
-            }
-        }
+    unsigned short* sb = sx + 2 * 16 * R * NT;   // [8][2][R][NT] rounded biases of a batch of heads
+    const int t = t0 + l16;
+    const bool tok = t < p.S;
     const bool diag = q4 == (l16 >> 2) && tok;
     const int v = l16 & 3;
-    float dv[8][8];   // the lane's dots (its token's, on the diagonal lanes)
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-#pragma unroll
-        for (int r2 = 0; r2 < 8; ++r2) {
-            dv[r][r2] = 0.f;
-            if (r >= R || r2 >= R) continue;
-            f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) a4 = mfma(qf[r][ks], kf[r2][ks], a4);
-            const float x01 = (v & 1) ? a4[1] : a4[0], x23 = (v & 1) ? a4[3] : a4[2];
-            dv[r][r2] = (v & 2) ? x23 : x01;
+    for (int h0 = 0; h0 < hpg; h0 += 8) {
+        const int nh = min(8, hpg - h0);
+        const int rows = h0 == 0 ? 2 * 16 * R * NT8 : 0, bias = nh * 2 * R * NT8;
+        if (h0 > 0) __syncthreads();   // every wave is done with the previous batch's biases
+        for (int e = tid; e < rows + bias; e += 256) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (e < rows) {
+                const int c8 = e % NT8, rest = e / NT8;
+                const int r = rest % R, tk = (rest / R) % 16, which = rest / (16 * R);
+                const int t = t0 + tk, col = 8 * c8;
+                if (t < p.S && col < N) {
+                    const unsigned short* x = which ? p.k : p.q;
+                    w = *reinterpret_cast<const u32x4*>(x + ((((long)b * p.S + t) * R + r) * p.G + g) * N + col);
+                }
+                *reinterpret_cast<u32x4*>(sx + ((which * 16 + tk) * R + r) * NT + col) = w;
+            } else {
+                const int e2 = e - rows, c8 = e2 % NT8, rest = e2 / NT8;
+                const int r = rest % R, which = (rest / R) % 2, hh = rest / (2 * R), col = 8 * c8;
+                if (col < N) {
+                    const float* bp = (which ? p.k_bias : p.q_bias) + ((long)(g * hpg + h0 + hh) * R + r) * N + col;
+                    const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
+                    w = u32x4{pk2(b0[0], b0[1]), pk2(b0[2], b0[3]), pk2(b1[0], b1[1]), pk2(b1[2], b1[3])};
+                }
+                *reinterpret_cast<u32x4*>(sb + ((hh * 2 + which) * R + r) * NT + col) = w;
+            }
         }
-    }
-    if (!diag) return;
-    // the token's R*R dots are contiguous: 8- or 16-byte pieces where R*R allows
-    unsigned short* out = p.qk_dot + ((long)bh * p.S + t) * R * R;
-    if (R == 4) {
+        __syncthreads();
+        for (int hh = wave; hh < nh; hh += 4) {
+            const int h = g * hpg + h0 + hh;
+            // fragments of token l16: rank r, columns 32 ks + 8 q4 .. + 7, biased and rounded
+            // (zero past N, where raw and bias are zero, and past the sequence)
+            u32x4 qf[RP][KS], kf[RP][KS];
 #pragma unroll
-        for (int r = 0; r < 4; r += 2)
-            *reinterpret_cast<u32x4*>(out + 4 * r) =
-                u32x4{pk2(dv[r][0], dv[r][1]), pk2(dv[r][2], dv[r][3]), pk2(dv[r + 1][0], dv[r + 1][1]),
-                      pk2(dv[r + 1][2], dv[r + 1][3])};
-    } else if (R == 8) {
+            for (int r = 0; r < RP; ++r)
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            *reinterpret_cast<u32x4*>(out + 8 * r) =
-                u32x4{pk2(dv[r][0], dv[r][1]), pk2(dv[r][2], dv[r][3]), pk2(dv[r][4], dv[r][5]), pk2(dv[r][6], dv[r][7])};
-    } else if (R == 2) {
-        *reinterpret_cast<u32x2*>(out) = u32x2{pk2(dv[0][0], dv[0][1]), pk2(dv[1][0], dv[1][1])};
-    } else {
+                for (int ks = 0; ks < KS; ++ks) {
+                    qf[r][ks] = kf[r][ks] = u32x4{0u, 0u, 0u, 0u};
+                    if (r >= R || !tok) continue;
+                    const int col = 32 * ks + 8 * q4;
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
+                    for (int which = 0; which < 2; ++which) {
+                        const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + ((which * 16 + l16) * R + r) * NT + col);
+                        const u32x4 bb = *reinterpret_cast<const u32x4*>(sb + ((hh * 2 + which) * R + r) * NT + col);
+                        float x[8];
 #pragma unroll
-            for (int r2 = 0; r2 < 8; ++r2)
-                if (r < R && r2 < R) out[r * R + r2] = bits16(rnd(dv[r][r2]));
+                        for (int d = 0; d < 4; ++d) {
+                            x[2 * d] = rnd(lo16(raw[d]) + lo16(bb[d]));
+                            x[2 * d + 1] = rnd(hi16(raw[d]) + hi16(bb[d]));
+                        }
+                        if (which)
+                            kf[r][ks] = pack8(x);
+                        else
+                            qf[r][ks] = pack8(x);
+                    }
+                }
+            float dv[RP][RP];   // the lane's dots (its token's, on the diagonal lanes)
+#pragma unroll
+            for (int r = 0; r < RP; ++r) {
+#pragma unroll
+                for (int r2 = 0; r2 < RP; ++r2) {
+                    dv[r][r2] = 0.f;
+                    if (r >= R || r2 >= R) continue;
+                    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) a4 = mfma(qf[r][ks], kf[r2][ks], a4);
+                    const float x01 = (v & 1) ? a4[1] : a4[0], x23 = (v & 1) ? a4[3] : a4[2];
+                    dv[r][r2] = (v & 2) ? x23 : x01;
+                }
+            }
+            if (!diag) continue;
+            unsigned short* out = p.qk_dot + ((long)(b * p.H + h) * p.S + t) * R * R;
+            if (RP == 4 && R == 4) {
+#pragma unroll
+                for (int r = 0; r < RP; r += 2)
+                    *reinterpret_cast<u32x4*>(out + 4 * r) =
+                        u32x4{pk2(dv[r][0], dv[r][1]), pk2(dv[r][2], dv[r][3]), pk2(dv[r + 1][0], dv[r + 1][1]),
+                              pk2(dv[r + 1][2], dv[r + 1][3])};
+            } else if (RP == 8 && R == 8) {
+#pragma unroll
+                for (int r = 0; r < RP; ++r)
+                    *reinterpret_cast<u32x4*>(out + 8 * r) =
+                        u32x4{pk2(dv[r][0], dv[r][1]), pk2(dv[r][2], dv[r][3]), pk2(dv[r][4], dv[r][5]),
+                              pk2(dv[r][6], dv[r][7])};
+            } else if (RP == 2 && R == 2) {
+                *reinterpret_cast<u32x2*>(out) = u32x2{pk2(dv[0][0], dv[0][1]), pk2(dv[1][0], dv[1][1])};
+            } else {
+#pragma unroll
+                for (int r = 0; r < RP; ++r)
+#pragma unroll
+                    for (int r2 = 0; r2 < RP; ++r2)
+                        if (r < R && r2 < R) out[r * R + r2] = bits16(rnd(dv[r][r2]));
+            }
+        }
     }
 }
 
+// LDS of k_qk: the staged rows and one batch of biases (at most 96 KB).
+int qk_lds_bytes(const Params& p, int NT) { return (2 * 16 + 2 * std::min(8, p.H / p.G)) * p.R * NT * 2; }
+
 mimo_status launch_qk(const Params& p, int NT, hipStream_t st) {
-    const unsigned grid = (unsigned)((long)p.B * p.H * ((p.S + 63) / 64));
+    const unsigned grid = (unsigned)((long)p.B * p.G * ((p.S + 15) / 16));
+    const int lds = qk_lds_bytes(p, NT);
     Params pc = p;
     void* args[] = {&pc};
-    const void* f = NT == 32 ? reinterpret_cast<const void*>(&k_qk<32>)
-                  : NT == 64 ? reinterpret_cast<const void*>(&k_qk<64>)
-                             : reinterpret_cast<const void*>(&k_qk<128>);
-    const hipError_t e = hipLaunchKernel(f, dim3(grid), dim3(256), args, 0, st);
+    // instances [NT 32, 64, 128][RP 1, 2, 4, 8]
+    static const void* const table[3][4] = {
+        {reinterpret_cast<const void*>(&k_qk<32, 1>), reinterpret_cast<const void*>(&k_qk<32, 2>),
+         reinterpret_cast<const void*>(&k_qk<32, 4>), reinterpret_cast<const void*>(&k_qk<32, 8>)},
+        {reinterpret_cast<const void*>(&k_qk<64, 1>), reinterpret_cast<const void*>(&k_qk<64, 2>),
+         reinterpret_cast<const void*>(&k_qk<64, 4>), reinterpret_cast<const void*>(&k_qk<64, 8>)},
+        {reinterpret_cast<const void*>(&k_qk<128, 1>), reinterpret_cast<const void*>(&k_qk<128, 2>),
+         reinterpret_cast<const void*>(&k_qk<128, 4>), reinterpret_cast<const void*>(&k_qk<128, 8>)}};
+    const int ri = p.R <= 1 ? 0 : (p.R <= 2 ? 1 : (p.R <= 4 ? 2 : 3));
+    const void* f = table[NT == 32 ? 0 : (NT == 64 ? 1 : 2)][ri];
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+        return fail(MIMO_ERR_HIP, "hipFuncSetAttribute(MaxDynamicSharedMemorySize=%d) failed", lds);
+    const hipError_t e = hipLaunchKernel(f, dim3(grid), dim3(256), args, (size_t)lds, st);
     if (e != hipSuccess) return fail(MIMO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return MIMO_OK;
 }
