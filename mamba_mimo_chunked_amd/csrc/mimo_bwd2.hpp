@@ -66,9 +66,10 @@ struct Geo {
     static constexpr int GAM = 0, FAC = GAM + MD, ECS = FAC + MD, EREV = ECS + MD, RED = EREV + MD,
                          DQK = RED + 8, QKC = DQK + 8 * MD, RS0 = QKC + 8 * MD, RS1 = RS0 + 2 * MD,
                          SMALL = RS1 + 2 * MD;
-    // MD = 128: after the small tables, one tile that stages each product's B operand
-    static constexpr int BSTG = SMALL;
-    static constexpr int LDS_MAIN = (WIDE ? TILE : MAIN_TILES) + SMALL;   // floats
+    // MD = 128: after the small tables, LDS-resident tiles: W, then the output tile
+    // (the two most used of the chunk pass's nine); U in the aggregate
+    static constexpr int W_LDS = SMALL, OUT_LDS = SMALL + TILE, U_LDS = SMALL;
+    static constexpr int LDS_MAIN = (WIDE ? 2 * TILE : MAIN_TILES) + SMALL;   // floats
     static constexpr int LDS_AGG = (WIDE ? TILE : AGG_TILES) + SMALL;
 };
 
@@ -300,31 +301,16 @@ __device__ __forceinline__ void gemm64(int Mi, int Nj, int K, const float* A, co
     }
 }
 
-// MD = 128 (all <= 128, tiles in global scratch): eight waves, wave w owns row block w
-// and every column block; the contraction runs in 16-wide steps, each step's operands
-// loaded just before its MFMAs. Every wave reads all of B, so B is first copied into
-// the LDS tile bs (one global read instead of eight); the barriers around the copy
-// also order the product after the stores of whatever came before it. Called by
-// every thread of the workgroup.
+// MD = 128 (all <= 128; the operands in global scratch or in LDS): eight waves, wave w
+// owns row block w and every column block; the contraction runs in 16-wide steps, each
+// step's operands loaded just before its MFMAs.
 template <int NT, bool AK1, bool BK1, bool SK, bool RS, typename F>
-__device__ __forceinline__ void gemm128(int Mi, int Nj, int K, const float* A, const float* Bg, const float* sk,
-                                        F&& epi, float* rs, float* bs) {
+__device__ __forceinline__ void gemm128(int Mi, int Nj, int K, const float* A, const float* B, const float* sk,
+                                        F&& epi, float* rs) {
     static_assert(NT == 512, "one 16-row block a wave");
     constexpr int LD = Geo<128>::LD;
     const int tid = tid_x(), w = tid >> 6, x = tid & 15, q = (tid >> 4) & 3;
     const int ncb = (Nj + 15) >> 4, nk = (K + 15) >> 4;
-    {
-        // the B region the product reads: rows j < 16 ncb of k < 16 nk (BK1), else rows
-        // k < 16 nk of j < 16 ncb; four floats a copy
-        const int rows = BK1 ? 16 * ncb : 16 * nk, c4 = BK1 ? 4 * nk : 4 * ncb;
-        __syncthreads();
-        for (int e = tid; e < rows * c4; e += NT) {
-            const int r = e / c4, c = 4 * (e - r * c4);
-            *reinterpret_cast<f32x4*>(bs + r * LD + c) = *reinterpret_cast<const f32x4*>(Bg + r * LD + c);
-        }
-        __syncthreads();
-    }
-    const float* B = bs;
     const int i0 = 16 * w;
     if (i0 >= Mi) return;   // wave-uniform
     f32x4 acc[8];
@@ -406,12 +392,11 @@ __device__ __forceinline__ void gemm128(int Mi, int Nj, int K, const float* A, c
     }
 }
 
-// bs: MD = 128's LDS staging tile for B (unused with MD = 64)
 template <int MD, int NT, bool AK1, bool BK1, bool SK, bool RS = false, typename F>
 __device__ __forceinline__ void gemm(int Mi, int Nj, int K, const float* A, const float* B, const float* sk,
-                                     F&& epi, float* rs, float* bs) {
+                                     F&& epi, float* rs = nullptr) {
     if constexpr (Geo<MD>::WIDE)
-        gemm128<NT, AK1, BK1, SK, RS>(Mi, Nj, K, A, B, sk, epi, rs, bs);
+        gemm128<NT, AK1, BK1, SK, RS>(Mi, Nj, K, A, B, sk, epi, rs);
     else
         gemm64<NT, AK1, BK1, SK, RS>(Mi, Nj, K, A, B, sk, epi, rs);
 }
@@ -862,11 +847,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_agg2(Params2 p) {
     const int c_begin = (1 + seg / p.F) * p.L + (seg % p.F) * La;
     const int c_end = min(c_begin + La, p.nc);
     float* tiles = GE::WIDE ? p.slots + (long)blockIdx.x * GE::AGG_TILES : sm + GE::SMALL;
-    float* BS = sm + GE::BSTG;   // MD = 128 only
     Tiles T = {};
     T.QH = tiles + GE::A_QH;
     T.DPO = tiles + GE::A_DPO;
-    float* U = tiles + GE::A_U;
+    float* U = GE::WIDE ? sm + GE::U_LDS : tiles + GE::A_U;
     const float* ECS = sm + GE::ECS;
     for (int e = threadIdx.x; e < N * P; e += NTHR) U[(e / P) * LD + e % P] = 0.f;
     float dprod = 1.f;
@@ -898,8 +882,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_agg2(Params2 p) {
         // owns (n, p) in the product is the only one reading and writing U[n][p]
         // A(n, i) = Q^[i][n], B(i, p) = dPhiO[i][p] scaled per i by exp(da_cs[t_i])
         gemm<MD, NTHR, false, false, true>(
-            N, P, rows, T.QH, T.DPO, ECS, [&](int n, int pc, float v) { U[n * LD + pc] = v + dA * U[n * LD + pc]; },
-            nullptr, BS);
+            N, P, rows, T.QH, T.DPO, ECS, [&](int n, int pc, float v) { U[n * LD + pc] = v + dA * U[n * LD + pc]; });
         dprod *= dA;
     }
     sync<MD>();
@@ -981,7 +964,13 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
     const int tid = threadIdx.x;
     const int c_begin = seg * p.L;
     const int c_end = min(c_begin + p.L, p.nc);
-    const Tiles T = tiles_at<MD>(GE::WIDE ? p.slots + (long)blockIdx.x * GE::MAIN_TILES : sm + GE::SMALL);
+    Tiles T = tiles_at<MD>(GE::WIDE ? p.slots + (long)blockIdx.x * GE::MAIN_TILES : sm + GE::SMALL);
+    if constexpr (GE::WIDE) {
+        // the two most used tiles in LDS (their slot regions stay unused); the products
+        // read their other operands from the slot
+        T.OUT = sm + GE::OUT_LDS;
+        T.WM = sm + GE::W_LDS;
+    }
     float* QH = T.QH;
     float* KH = T.KH;
     float* PS = T.PS;
@@ -1000,7 +989,6 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
     float* QKC = sm + GE::QKC;
     float* RS0 = sm + GE::RS0;
     float* RS1 = sm + GE::RS1;
-    float* BS = sm + GE::BSTG;   // MD = 128 only
     const float dval = p.has_d ? p.d[h] : 0.f;
 
     // dS entering the segment from the right
@@ -1068,12 +1056,12 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
             if (tj < ti && ti < cl) av = v * FAC[j] * OUT[ti * LD + tj];
             if (tj == ti && ti < cl) av = GAM[j] * QKC[ti * RR + ri * R + rj] + (i == j ? dval : 0.f);
             AM[i * LD + j] = av;
-        }, nullptr, BS);
+        });
         gemm<MD, NTHR2, true, true, false>(rows, rows, P, DPO, PS, nullptr, [&](int i, int j, float v) {
             WM[i * LD + j] = v;
             const int ri = dC.q(i), ti = i - ri * C, rj = dC.q(j), tj = j - rj * C;
             if (ti == tj && ti < cl) DQK[ti * RR + ri * R + rj] = v;
-        }, nullptr, BS);
+        });
         sync<MD>();
         if (tid < cl) {
             const int t = tid;
@@ -1110,12 +1098,12 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                 OUT[i * LD + n] = o;
                 return QH[i * LD + n] * o;
             },
-            RS0, BS);
+            RS0);
         sync<MD>();
         token_out<MD>(cl, R, C, RS0, [&](int t, float v) { p.dda_cs[tokS + c0 + t] = v; });
         // W K~: B(j, n) = k^[j][n] scaled per j by the factor (folded into A)
         gemm<MD, NTHR2, true, false, true>(
-            rows, N, rows, WM, KH, FAC, [&](int i, int n, float v) { OUT[i * LD + n] += v; }, nullptr, BS);
+            rows, N, rows, WM, KH, FAC, [&](int i, int n, float v) { OUT[i * LD + n] += v; });
         sync<MD>();
         // angle gradient, q part: d(a')/dθ = -e', d(e')/dθ = a' for the rotated pair (a', e')
         float dth[IS::DX];   // items (t, n): t < C, n < W <= MD / 2
@@ -1144,7 +1132,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                 OUT[j * LD + n] = o;
                 return KH[j * LD + n] * o;
             },
-            RS1, BS);
+            RS1);
         sync<MD>();
         token_out<MD>(cl, R, C, RS1, [&](int t, float v) { p.dda_cs_rev[tokS + c0 + t] = v * FAC[t]; });
         gemm<MD, NTHR2, false, false, false, true>(
@@ -1154,7 +1142,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
                 OUT[j * LD + n] = o;
                 return KH[j * LD + n] * o;
             },
-            RS0, BS);
+            RS0);
         sync<MD>();
         token_out<MD>(cl, R, C, RS0, [&](int t, float v) { p.dfactor[tokS + c0 + t] = v; });
 #pragma unroll
@@ -1192,10 +1180,9 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
 
         // ---- dPsi = kappa dS + A^T dPhiO (the latter with the same-token and d terms)
         gemm<MD, NTHR2, true, false, false>(
-            rows, P, N, KH, DS, nullptr, [&](int j, int pc, float v) { OUT[j * LD + pc] = v * FAC[j] * EREV[j]; },
-            nullptr, BS);
+            rows, P, N, KH, DS, nullptr, [&](int j, int pc, float v) { OUT[j * LD + pc] = v * FAC[j] * EREV[j]; });
         gemm<MD, NTHR2, false, false, false>(
-            rows, P, rows, AM, DPO, nullptr, [&](int j, int pc, float v) { OUT[j * LD + pc] += v; }, nullptr, BS);
+            rows, P, rows, AM, DPO, nullptr, [&](int j, int pc, float v) { OUT[j * LD + pc] += v; });
         sync<MD>();
         for (int e = tid; e < cl * (P / 4); e += NTHR2) {
             const int t = dP4.q(e), p4 = 4 * (e - t * (P / 4));
@@ -1229,7 +1216,7 @@ __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
             const float old = DS[n * LD + pc];
             part = __fmaf_rn(old, SC[n * LD + pc], part);
             DS[n * LD + pc] = v + dA * old;
-        }, nullptr, BS);
+        });
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
         if ((tid & 63) == 0) RED[tid >> 6] = part;
