@@ -1078,6 +1078,7 @@ static mimo_status run(const mimo_bwd_fwd_args* a, uint16_t* out, void* stream, 
     } else if (ex && p.reduce_o && p.has_z) {
         kmain = fam->main_ex_rz[ti];
     }
+    if (!states_only) lds_main += kmain == fam->main[ti] ? fam->main_sa[ti] : fam->main_ex_sa[ti];
     const kfn kagg = ex ? fam->agg_ex[ti] : fam->agg[ti];
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int BH = p.B * p.H;

@@ -274,6 +274,12 @@ struct Stage {
     static constexpr bool QKON = LITE && DYN + 2 * SMB + QKB <= 80 * 1024;
     static constexpr int QK = 2 * SMB;
     static constexpr int BYTES = LITE ? 2 * SMB + (QKON ? QKB : 0) : 16;
+    // The chunk pass's causal block in a tile of its own, after the layout's regions,
+    // where that still leaves room for two workgroups per compute unit: its stores then
+    // wait for no read of q, and the kappa^T pass for no read of the block. Extra
+    // dynamic LDS of the chunk pass (0: the block reuses the q tile).
+    static constexpr int SA = align16(T::MT * T::LDA * 2);
+    static constexpr int SA_BYTES = (MAIN && LITE && DYN + BYTES + SA <= 80 * 1024) ? SA : 0;
     // scalar rows inside SCAL
     static constexpr int DT0 = 0, DT1 = 4 * T::Cp, TR0 = 8 * T::Cp, TR1 = 12 * T::Cp, CS = 16 * T::Cp,
                          REV = 20 * T::Cp, DLAST = 24 * T::Cp;
@@ -1113,8 +1119,9 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
     constexpr bool PSPLIT = RSPLIT && SG::LITE;   // the second half fills Psi^T
     extern __shared__ __align__(16) unsigned char smem[];
     const Lds L = lds_layout(RP, CT, NT, PT, p.C, p.W, true);
-    unsigned short* sQ = reinterpret_cast<unsigned short*>(smem + L.r1);   // also sA, sKapT
-    unsigned short* sA = sQ;
+    constexpr bool SEPA = SG::SA_BYTES > 0;   // causal block in its own tile
+    unsigned short* sQ = reinterpret_cast<unsigned short*>(smem + L.r1);   // also sKapT (and sA unless SEPA)
+    unsigned short* sA = SEPA ? reinterpret_cast<unsigned short*>(smem + L.total) : sQ;
     unsigned short* sKapT = sQ;
     unsigned short* sK = reinterpret_cast<unsigned short*>(smem + L.r2);
     unsigned short* sPsiT = reinterpret_cast<unsigned short*>(smem + L.r3);
@@ -1483,7 +1490,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                     at[w] = u32x2{pk2(m[0], m[1]), pk2(m[2], m[3])};
                 }
             }
-            bar();   // every wave is done reading sQ
+            if constexpr (!SEPA) bar();   // every wave is done reading sQ (sA overlays it)
 #pragma unroll
             for (int w = 0; w < T::ATW; ++w) {
                 const int u = wave + w * NW;
@@ -1516,7 +1523,8 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                     }
                 }
             }
-            bar();   // every wave is done reading sA
+            // the kappa^T pass writes the q tile, which no wave reads after the barrier above
+            if constexpr (!SEPA) bar();   // every wave is done reading sA (it overlays that tile)
         }
 
         // ---- kappa^T = bf16(K~ * exp(da_cs_rev)), transposed, into R1: items (row
@@ -1765,6 +1773,7 @@ struct Family {
     kfn agg[9], agg_ex[9];
     kfn main[9], main_ex_rz[9], main_ex_fwd[9];
     kfn states[9], states_ex[9];   // the chunk pass of calls without y (k_agg in ST mode)
+    int main_sa[9], main_ex_sa[9];  // extra dynamic LDS of the chunk pass (generic, shape-exact)
 };
 
 #define MIMO_NP_LIST(F, RP, CT)                                                                             \
@@ -1777,12 +1786,15 @@ struct Family {
 #define MIMO_MAIN_EX2_FN(RP, CT, NT, PT) k_main<RP, CT, NT, PT, true, 2>
 #define MIMO_ST_FN(RP, CT, NT, PT) k_agg<RP, CT, NT, PT, false, true>
 #define MIMO_ST_EX_FN(RP, CT, NT, PT) k_agg<RP, CT, NT, PT, true, true>
+#define MIMO_SA_FN(RP, CT, NT, PT) Stage<RP, CT, NT, PT, true, false>::SA_BYTES
+#define MIMO_SA_EX_FN(RP, CT, NT, PT) Stage<RP, CT, NT, PT, true, true>::SA_BYTES
 #define MIMO_FAMILY(RP, CT)                                                                               \
     const Family* family_rp##RP##_ct##CT() {                                                              \
         static const Family f = {{MIMO_NP_LIST(MIMO_AGG_FN, RP, CT)},     {MIMO_NP_LIST(MIMO_AGG_EX_FN, RP, CT)}, \
                                  {MIMO_NP_LIST(MIMO_MAIN_FN, RP, CT)},    {MIMO_NP_LIST(MIMO_MAIN_EX1_FN, RP, CT)}, \
                                  {MIMO_NP_LIST(MIMO_MAIN_EX2_FN, RP, CT)}, \
-                                 {MIMO_NP_LIST(MIMO_ST_FN, RP, CT)},      {MIMO_NP_LIST(MIMO_ST_EX_FN, RP, CT)}}; \
+                                 {MIMO_NP_LIST(MIMO_ST_FN, RP, CT)},      {MIMO_NP_LIST(MIMO_ST_EX_FN, RP, CT)}, \
+                                 {MIMO_NP_LIST(MIMO_SA_FN, RP, CT)},      {MIMO_NP_LIST(MIMO_SA_EX_FN, RP, CT)}}; \
         return &f;                                                                                        \
     }
 #define MIMO_DECL_FAMILY(RP, CT) const Family* family_rp##RP##_ct##CT();
