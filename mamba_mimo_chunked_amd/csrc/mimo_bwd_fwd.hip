@@ -353,7 +353,8 @@ mimo_status set_lds(kfn f, int bytes) {
 // likewise (biased, unrotated). One workgroup per (batch, q/k group, 16 tokens): in one
 // round of loads it stages the group's raw q and k rows of the 16 tokens ([2][16][R][NT]
 // bf16, read once for all the group's heads) and the rounded biases of up to eight of
-// the group's heads ([8][2][R][NT] bf16; zero past N and the sequence); wave w then
+// the group's heads ([8][2][R][NT], bf16 values held as fp32 so that the bias add needs
+// no unpacking; zero past N and the sequence); wave w then
 // serves heads w, w + 4, ... of the batch, and further batches of heads restage the
 // biases. A head's dots are the diagonals of 16 x 16 MFMA tiles
 // (rows the tokens' q0 of rank r, columns their k0 of rank r2), built from the same
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
     const int b = bg / p.G, g = bg - b * p.G, hpg = p.H / p.G;
     const int R = p.R, N = p.N, t0 = 16 * tile;
     constexpr int KS = NT / 32, NT8 = NT / 8;
-    unsigned short* sb = sx + 2 * 16 * R * NT;   // [8][2][R][NT] rounded biases of a batch of heads
+    float* sb = reinterpret_cast<float*>(sx + 2 * 16 * R * NT);   // [8][2][R][NT] rounded biases of a batch of heads
     const int t = t0 + l16;
     const bool tok = t < p.S;
     const bool diag = q4 == (l16 >> 2) && tok;
@@ -381,8 +382,8 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
         const int rows = h0 == 0 ? 2 * 16 * R * NT8 : 0, bias = nh * 2 * R * NT8;
         if (h0 > 0) __syncthreads();   // every wave is done with the previous batch's biases
         for (int e = tid; e < rows + bias; e += 256) {
-            u32x4 w = {0u, 0u, 0u, 0u};
             if (e < rows) {
+                u32x4 w = {0u, 0u, 0u, 0u};
                 const int c8 = e % NT8, rest = e / NT8;
                 const int r = rest % R, tk = (rest / R) % 16, which = rest / (16 * R);
                 const int t = t0 + tk, col = 8 * c8;
@@ -392,14 +393,21 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
                 }
                 *reinterpret_cast<u32x4*>(sx + ((which * 16 + tk) * R + r) * NT + col) = w;
             } else {
+                f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0;
                 const int e2 = e - rows, c8 = e2 % NT8, rest = e2 / NT8;
                 const int r = rest % R, which = (rest / R) % 2, hh = rest / (2 * R), col = 8 * c8;
                 if (col < N) {
                     const float* bp = (which ? p.k_bias : p.q_bias) + ((long)(g * hpg + h0 + hh) * R + r) * N + col;
                     const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
-                    w = u32x4{pk2(b0[0], b0[1]), pk2(b0[2], b0[3]), pk2(b1[0], b1[1]), pk2(b1[2], b1[3])};
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        w0[d] = rnd(b0[d]);
+                        w1[d] = rnd(b1[d]);
+                    }
                 }
-                *reinterpret_cast<u32x4*>(sb + ((hh * 2 + which) * R + r) * NT + col) = w;
+                float* dst = sb + ((hh * 2 + which) * R + r) * NT + col;
+                *reinterpret_cast<f32x4*>(dst) = w0;
+                *reinterpret_cast<f32x4*>(dst + 4) = w1;
             }
         }
         __syncthreads();
@@ -418,17 +426,17 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
 #pragma unroll
                     for (int which = 0; which < 2; ++which) {
                         const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + ((which * 16 + l16) * R + r) * NT + col);
-                        const u32x4 bb = *reinterpret_cast<const u32x4*>(sb + ((hh * 2 + which) * R + r) * NT + col);
-                        float x[8];
-#pragma unroll
-                        for (int d = 0; d < 4; ++d) {
-                            x[2 * d] = rnd(lo16(raw[d]) + lo16(bb[d]));
-                            x[2 * d + 1] = rnd(hi16(raw[d]) + hi16(bb[d]));
-                        }
+                        const float* bp = sb + ((hh * 2 + which) * R + r) * NT + col;
+                        const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
+                        // bf16(raw + bias): the packing conversion is the rounding
+                        const u32x4 o = {pk2(lo16(raw[0]) + b0[0], hi16(raw[0]) + b0[1]),
+                                         pk2(lo16(raw[1]) + b0[2], hi16(raw[1]) + b0[3]),
+                                         pk2(lo16(raw[2]) + b1[0], hi16(raw[2]) + b1[1]),
+                                         pk2(lo16(raw[3]) + b1[2], hi16(raw[3]) + b1[3])};
                         if (which)
-                            kf[r][ks] = pack8(x);
+                            kf[r][ks] = o;
                         else
-                            qf[r][ks] = pack8(x);
+                            qf[r][ks] = o;
                     }
                 }
             float dv[RP][RP];   // the lane's dots (its token's, on the diagonal lanes)
@@ -472,8 +480,8 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
     }
 }
 
-// LDS of k_qk: the staged rows and one batch of biases (at most 96 KB).
-int qk_lds_bytes(const Params& p, int NT) { return (2 * 16 + 2 * std::min(8, p.H / p.G)) * p.R * NT * 2; }
+// LDS of k_qk: the staged rows (bf16) and one batch of biases (fp32): at most 160 KB.
+int qk_lds_bytes(const Params& p, int NT) { return (2 * 16 * 2 + 2 * std::min(8, p.H / p.G) * 4) * p.R * NT; }
 
 mimo_status launch_qk(const Params& p, int NT, hipStream_t st) {
     const unsigned grid = (unsigned)((long)p.B * p.G * ((p.S + 15) / 16));
