@@ -311,7 +311,7 @@ mimo_status make_plan(const mimo_bwd_fwd_args* a, Plan* pl, bool fwd = false) {
     Lds la = lds_layout(RP, CT, pl->NT, pl->PT, (int)C, pl->W, false);
     pl->lds_main = lm.total;
     pl->lds_agg = la.total;
-    pl->lds_states = la.total + pl->NT * (pl->PT + 8) * 2;
+    pl->lds_states = la.total;
     // the token-tile reduction of the dmimo partials reuses LDS from offset 0
     if (CT > 1) {
         const int red = 2 * CT * RP * pl->PT * 4;

@@ -875,9 +875,10 @@ __device__ __forceinline__ Params specialise(const Params& pin) {
 // per chunk; also the product of the chunk decays.
 // ST: the chunk pass of a call that needs no y (neither reduced dout nor z: the outputs
 // are the states and qk_dot only). The same walk over whole segments, from the state
-// entering the segment; at the top of chunk c the state is written out as states[c] =
-// bf16(S) through an LDS tile [NT][PT + 8] after the kernel's other LDS, so the global
-// stores are 16-byte pieces of consecutive rows. qk_dot comes from k_qk.
+// entering the segment; at the top of chunk c each lane writes its accumulator values of
+// the state out as states[c] = bf16(S) (2-byte stores: 16 lanes cover 32 contiguous
+// bytes of a row). Writing them straight from registers keeps the walk's LDS at the
+// aggregate's, four workgroups per CU. qk_dot comes from k_qk.
 template <int RP, int CT, int NT, int PT, bool EX, bool ST = false>
 __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params pin) {
     const Params p = specialise<RP, CT, NT, PT, EX, -1>(pin);
@@ -917,8 +918,6 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
         c_end = min(c_begin + La, s_ * p.L + p.L);
     }
     const int R = p.R;
-    constexpr int SPP = PT + 8;   // row pitch (halves) of the ST state tile
-    unsigned short* sSt = reinterpret_cast<unsigned short*>(smem + L.total);
     // With one 8-column group per thread and rotary divisor 4, the threads of the
     // first half hold exactly the rotated groups; the second half fills Psi.
     constexpr bool SPLIT = SG::LITE && EX && T::QK_IT == 1 && T::MT * (NT / 32) == T::NTHR / 2;
@@ -978,32 +977,27 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
         }
         if constexpr (!SG::QKON) load_qk(p, it, b, c0, cl, in);
         if constexpr (ST) {
-            // bf16(S entering chunk c) into the state tile, rows n, columns p
+            // states[c] = bf16(S entering chunk c): lane (l16, q4) of tile (nt, pt) holds rows
+            // 16 nt + 4 q4 + v of column 16 pt + l16
+            unsigned short* dst = p.states + ((long)bh * p.nc + c) * p.N * p.P;
 #pragma unroll
             for (int w = 0; w < T::STW; ++w) {
                 const int u = wave + w * T::NW;
                 if (T::ST_FULL || u < T::ST) {
                     const int nt = u / T::PTT, pt = u % T::PTT;
-                    const int pc = 16 * pt + l16;
+                    const int pc = 16 * pt + l16, n0 = 16 * nt + 4 * q4;
                     const unsigned lo = pk2(U[w][0], U[w][1]), hi = pk2(U[w][2], U[w][3]);
-                    unsigned short* d = sSt + (16 * nt + 4 * q4) * SPP + pc;
-                    d[0] = static_cast<unsigned short>(lo);
-                    d[SPP] = static_cast<unsigned short>(lo >> 16);
-                    d[2 * SPP] = static_cast<unsigned short>(hi);
-                    d[3 * SPP] = static_cast<unsigned short>(hi >> 16);
+                    const unsigned short x[4] = {static_cast<unsigned short>(lo), static_cast<unsigned short>(lo >> 16),
+                                                 static_cast<unsigned short>(hi), static_cast<unsigned short>(hi >> 16)};
+                    if (pc < p.P) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (n0 + v < p.N) dst[(n0 + v) * p.P + pc] = x[v];
+                    }
                 }
             }
         }
         bar();   // chunk c's staging loads of every thread have landed; previous chunk done with LDS
-        if constexpr (ST) {
-            // states[c]: consecutive threads take consecutive 16-byte pieces of a row
-            unsigned short* dst = p.states + ((long)bh * p.nc + c) * p.N * p.P;
-            const int P8 = p.P / 8;
-            for (int e = static_cast<int>(threadIdx.x); e < p.N * P8; e += T::NTHR) {
-                const int n = e / P8, p8 = 8 * (e - n * P8);
-                *reinterpret_cast<u32x4*>(dst + n * p.P + p8) = lds_ld<u32x4>(sSt + n * SPP + p8);
-            }
-        }
         phase0<RP, CT, NT, PT, false, EX>(p, it, c0, cl, smb, sr, smem, L);
         bar();
         // kappa = bf16(bf16(rot(bf16(k + bf16(k_bias))) * factor) * exp(da_cs_rev)), row-major;
