@@ -351,8 +351,9 @@ mimo_status set_lds(kfn f, int bytes) {
 // qk_dot of the calls that need no y (their chunk pass is k_agg's state walk):
 // qk_dot[b,h,t,r,r2] = bf16(q0[t,r] . k0[t,r2]), q0 = bf16(q + bf16(q_bias)) and k0
 // likewise (biased, unrotated). One workgroup per (batch, q/k group, 16 tokens): in one
-// round of loads it stages the group's raw q and k rows of the 16 tokens ([2][16][R][NT]
-// bf16, read once for all the group's heads) and the rounded biases of up to eight of
+// round of loads it stages the group's raw q and k rows of the 16 tokens ([2][16] token
+// rows of R*NT bf16 plus 16 of padding, read once for all the group's heads; the padding
+// puts the 16 tokens of a fragment read on distinct LDS banks) and the rounded biases of up to eight of
 // the group's heads ([8][2][R][NT], bf16 values held as fp32 so that the bias add needs
 // no unpacking; zero past N and the sequence); wave w then
 // serves heads w, w + 4, ... of the batch, and further batches of heads restage the
@@ -364,7 +365,8 @@ mimo_status set_lds(kfn f, int bytes) {
 template <int NT, int RP>   // RP: the rank count rounded up to a power of two (register arrays)
 __global__ __launch_bounds__(256) void k_qk(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    unsigned short* sx = reinterpret_cast<unsigned short*>(smem);   // [2][16][R][NT]: q, then k
+    const int TS = p.R * NT + 16;   // token row pitch (bf16)
+    unsigned short* sx = reinterpret_cast<unsigned short*>(smem);   // [2][16][TS]: q, then k
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
     const int ntt = (p.S + 15) / 16;
     const int unit = blockIdx.x;   // (b * G + g) * ntt + tile
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
     const int b = bg / p.G, g = bg - b * p.G, hpg = p.H / p.G;
     const int R = p.R, N = p.N, t0 = 16 * tile;
     constexpr int KS = NT / 32, NT8 = NT / 8;
-    float* sb = reinterpret_cast<float*>(sx + 2 * 16 * R * NT);   // [8][2][R][NT] rounded biases of a batch of heads
+    float* sb = reinterpret_cast<float*>(sx + 2 * 16 * TS);   // [8][2][R][NT] rounded biases of a batch of heads
     const int t = t0 + l16;
     const bool tok = t < p.S;
     const bool diag = q4 == (l16 >> 2) && tok;
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
                     const unsigned short* x = which ? p.k : p.q;
                     w = *reinterpret_cast<const u32x4*>(x + ((((long)b * p.S + t) * R + r) * p.G + g) * N + col);
                 }
-                *reinterpret_cast<u32x4*>(sx + ((which * 16 + tk) * R + r) * NT + col) = w;
+                *reinterpret_cast<u32x4*>(sx + (which * 16 + tk) * TS + r * NT + col) = w;
             } else {
                 f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0;
                 const int e2 = e - rows, c8 = e2 % NT8, rest = e2 / NT8;
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
                     const int col = 32 * ks + 8 * q4;
 #pragma unroll
                     for (int which = 0; which < 2; ++which) {
-                        const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + ((which * 16 + l16) * R + r) * NT + col);
+                        const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + (which * 16 + l16) * TS + r * NT + col);
                         const float* bp = sb + ((hh * 2 + which) * R + r) * NT + col;
                         const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
                         // bf16(raw + bias): the packing conversion is the rounding
@@ -480,8 +482,10 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
     }
 }
 
-// LDS of k_qk: the staged rows (bf16) and one batch of biases (fp32): at most 160 KB.
-int qk_lds_bytes(const Params& p, int NT) { return (2 * 16 * 2 + 2 * std::min(8, p.H / p.G) * 4) * p.R * NT; }
+// LDS of k_qk: the staged rows (bf16, padded) and one batch of biases (fp32): at most 129 KB.
+int qk_lds_bytes(const Params& p, int NT) {
+    return 2 * 16 * (p.R * NT + 16) * 2 + 2 * std::min(8, p.H / p.G) * p.R * NT * 4;
+}
 
 mimo_status launch_qk(const Params& p, int NT, hipStream_t st) {
     const unsigned grid = (unsigned)((long)p.B * p.G * ((p.S + 15) / 16));
