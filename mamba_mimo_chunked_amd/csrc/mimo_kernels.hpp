@@ -151,6 +151,78 @@ struct Params {
     float* kslots;  // fp32 path, 128-row tiles: per-workgroup K~ tiles [MT][NT+4] (one per block)
 };
 
+// LDS carve-up (byte offsets), shared by host and device. Every region but the
+// last two depends only on the tile family (RP, CT, NT, PT), so inside a kernel
+// their offsets and pitches are compile-time constants and one per-lane address
+// register serves many accesses (the rest goes into the instructions' offset
+// field). cos/sin and exp(segsum) are sized by the runtime C and W and come last.
+struct Lds {
+    int r1;   // bf16 main: [MT][LDQ] q | [MT][LDA] causal block | [NT][LDA] kappa^T; aggregate: [MT][KPN] kappa
+    int r2;   // bf16 [MT][LDQ] k (main only)
+    int r3;   // bf16 main: [PT][LDA] Psi^T; aggregate: [MT][PT+16] Psi
+    int r4;   // bf16 [PT][LDQ] bf16(state)^T (main only)
+    int qk;   // fp32 [Cp][RP*RP+RP] qk_dot, zero for padded ranks, RP pad words per token (main only)
+    int dz;   // bf16 [Cp][PT+8] dz of the chunk, written out at the top of the next one (main only;
+              // inside r2 when it fits there: k is dead from the kappa^T pass to the next chunk's phase A)
+    int sc;   // fp32 [5][Cp] token scalars (exp(da_cs), gamma, exp(da_cs_rev), factor) + chunk decay
+    int tb;   // bf16 tables: q_bias [RP][NT] (main only), k_bias [RP][NT], mimo_v [RP][PT]
+    int cs;   // fp32 [2][C][W + 4] cos, sin (rows padded: 8 consecutive tokens hit distinct banks)
+    int se;   // fp32 [C][C + 4] exp(segsum) (main only; rows padded likewise)
+    int total;
+};
+
+__host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
+
+// kpad: row pad (bf16) of the aggregate's kappa tile
+__host__ __device__ constexpr Lds lds_layout_k(int RP, int CT, int NT, int PT, int C, int W, bool main, int kpad) {
+    const int Cp = 16 * CT, MT = RP * Cp < 32 ? 32 : RP * Cp;
+    const int ldq = NT + 8, lda = MT + 8;
+    int r1 = main ? NT * lda : MT * (NT + kpad);
+    if (main && MT * ldq > r1) r1 = MT * ldq;
+    if (main && MT * lda > r1) r1 = MT * lda;
+    Lds s{};
+    int off = 0;
+    s.r1 = off; off += align16(r1 * 2);
+    s.r2 = off; if (main) off += align16(MT * ldq * 2);
+    s.r3 = off; off += align16((main ? PT * lda : MT * (PT + 16)) * 2);
+    s.r4 = off; if (main) off += align16(PT * ldq * 2);
+    s.qk = off; if (main) off += align16(Cp * (RP * RP + RP) * 4);
+    s.dz = off;
+    if (main && Cp * (PT + 8) <= MT * ldq) s.dz = s.r2;
+    else if (main) off += align16(Cp * (PT + 8) * 2);
+    s.sc = off; off += align16((4 * Cp + 4) * 4);
+    s.tb = off; off += align16(((main ? 2 : 1) * RP * NT + RP * PT) * 2);
+    s.cs = off; off += align16(2 * C * (W + 4) * 4);
+    s.se = off; if (main) off += align16(C * (C + 4) * 4);
+    s.total = off;
+    return s;
+}
+
+// Row pad (bf16) of the aggregate's kappa tile: 16 puts the four rows of a transpose
+// read in four different 8-bank groups. Eight-wave families whose aggregate would
+// then just miss two workgroups per CU (for the rotary divisor 4 layout, with its
+// staging) take 8 when that brings them in: two rows of a read then share a bank
+// group, but a second workgroup per CU is worth more.
+__host__ __device__ constexpr int agg_kpad(int RP, int CT, int NT, int PT) {
+    const int Cp = 16 * CT, MT = RP * Cp < 32 ? 32 : RP * Cp;
+    const int NTHR = (MT == 128 && PT >= 64) ? 512 : 256;
+    if (NTHR != 512) return 16;
+    const int QK_IT = (MT * (NT / 16) + NTHR - 1) / NTHR;
+    const int SMB = align16(Cp * PT * 2 + Cp * (NT / 4) * 4 + (6 * Cp + 1) * 4);
+    const int QKB = QK_IT * 2 * NTHR * 16;
+    int tot[2] = {0, 0};
+    for (int k = 0; k < 2; ++k) {
+        const int dyn = lds_layout_k(RP, CT, NT, PT, Cp, NT / 4, false, k == 0 ? 16 : 8).total;
+        const bool lite = dyn + 256 + 2 * SMB <= 80 * 1024;
+        const bool qkon = lite && dyn + 256 + 2 * SMB + QKB <= 80 * 1024;
+        tot[k] = dyn + (lite ? 2 * SMB + (qkon ? QKB : 0) : 16);
+    }
+    return (tot[0] > 80 * 1024 && tot[1] <= 80 * 1024) ? 8 : 16;
+}
+__host__ __device__ constexpr Lds lds_layout(int RP, int CT, int NT, int PT, int C, int W, bool main) {
+    return lds_layout_k(RP, CT, NT, PT, C, W, main, main ? 16 : agg_kpad(RP, CT, NT, PT));
+}
+
 // ---------------------------------------------------------------- tile family
 // RP: rank count rounded up to a power of two (ranks >= R are zero rows);
 // CT: 16-token tiles per rank (Cp = 16*CT >= C); NT / PT: state and value
@@ -165,8 +237,8 @@ struct Tile {
     static constexpr int LDQ = NT + 8;                          // pitch of [*][NT] bf16 rows
     static constexpr int LDA = MT + 8;                          // pitch of [*][MT] bf16 rows
     // pitches of row-major tiles read through transpose reads (frag_tr): 16 extra
-    // bf16 put the 4 rows of one read in 4 different 8-bank groups
-    static constexpr int KPN = NT + 16;                         // [MT][KPN] kappa (aggregate kernel)
+    // bf16 put the 4 rows of one read in 4 different 8-bank groups (see agg_kpad)
+    static constexpr int KPN = NT + agg_kpad(RP, CT, NT, PT);   // [MT][KPN] kappa (aggregate kernel)
     static constexpr int PPN = PT + 16;                         // [MT][PPN] Psi (aggregate kernel)
     static constexpr int PTT = PT / 16;
     static constexpr int QK_IT = (MT * (NT / 16) + NTHR - 1) / NTHR;      // q/k items per thread
@@ -195,52 +267,6 @@ struct Tile {
     // idle; the second half fills Psi^T meanwhile.
     static constexpr bool RSPLIT_OK = NT >= 32 && (MT * NT / 32) % (NTHR / 2) == 0;
 };
-
-// LDS carve-up (byte offsets), shared by host and device. Every region but the
-// last two depends only on the tile family (RP, CT, NT, PT), so inside a kernel
-// their offsets and pitches are compile-time constants and one per-lane address
-// register serves many accesses (the rest goes into the instructions' offset
-// field). cos/sin and exp(segsum) are sized by the runtime C and W and come last.
-struct Lds {
-    int r1;   // bf16 main: [MT][LDQ] q | [MT][LDA] causal block | [NT][LDA] kappa^T; aggregate: [MT][NT+16] kappa
-    int r2;   // bf16 [MT][LDQ] k (main only)
-    int r3;   // bf16 main: [PT][LDA] Psi^T; aggregate: [MT][PT+16] Psi
-    int r4;   // bf16 [PT][LDQ] bf16(state)^T (main only)
-    int qk;   // fp32 [Cp][RP*RP+RP] qk_dot, zero for padded ranks, RP pad words per token (main only)
-    int dz;   // bf16 [Cp][PT+8] dz of the chunk, written out at the top of the next one (main only;
-              // inside r2 when it fits there: k is dead from the kappa^T pass to the next chunk's phase A)
-    int sc;   // fp32 [5][Cp] token scalars (exp(da_cs), gamma, exp(da_cs_rev), factor) + chunk decay
-    int tb;   // bf16 tables: q_bias [RP][NT], k_bias [RP][NT], mimo_v [RP][PT]
-    int cs;   // fp32 [2][C][W + 4] cos, sin (rows padded: 8 consecutive tokens hit distinct banks)
-    int se;   // fp32 [C][C + 4] exp(segsum) (main only; rows padded likewise)
-    int total;
-};
-
-__host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
-
-__host__ __device__ constexpr Lds lds_layout(int RP, int CT, int NT, int PT, int C, int W, bool main) {
-    const int Cp = 16 * CT, MT = RP * Cp < 32 ? 32 : RP * Cp;
-    const int ldq = NT + 8, lda = MT + 8;
-    int r1 = main ? NT * lda : MT * (NT + 16);
-    if (main && MT * ldq > r1) r1 = MT * ldq;
-    if (main && MT * lda > r1) r1 = MT * lda;
-    Lds s{};
-    int off = 0;
-    s.r1 = off; off += align16(r1 * 2);
-    s.r2 = off; if (main) off += align16(MT * ldq * 2);
-    s.r3 = off; off += align16((main ? PT * lda : MT * (PT + 16)) * 2);
-    s.r4 = off; if (main) off += align16(PT * ldq * 2);
-    s.qk = off; if (main) off += align16(Cp * (RP * RP + RP) * 4);
-    s.dz = off;
-    if (main && Cp * (PT + 8) <= MT * ldq) s.dz = s.r2;
-    else if (main) off += align16(Cp * (PT + 8) * 2);
-    s.sc = off; off += align16((4 * Cp + 4) * 4);
-    s.tb = off; off += align16((2 * RP * NT + RP * PT) * 2);
-    s.cs = off; off += align16(2 * C * (W + 4) * 4);
-    s.se = off; if (main) off += align16(C * (C + 4) * 4);
-    s.total = off;
-    return s;
-}
 
 // ---------------------------------------------------------------- staging of chunk inputs
 // LITE tile families (their LDS leaves room for two workgroups per compute unit
@@ -763,18 +789,20 @@ template <int RP, int CT, int NT, int PT, bool NAT = false>
 __device__ __forceinline__ void fill_tables(const Params& p, int h, unsigned char* smem, const Lds& L) {
     using T = Tile<RP, CT, NT, PT>;
     const int tid = threadIdx.x;
-    unsigned short* tb = reinterpret_cast<unsigned short*>(smem + L.tb);   // [RP][NT] x2, [RP][PT]
+    // [RP][NT] q_bias (chunk pass only), [RP][NT] k_bias, [RP][PT] mimo_v
+    unsigned short* tb = reinterpret_cast<unsigned short*>(smem + L.tb);
+    constexpr int KB = NAT ? 0 : RP * NT;   // offset of k_bias
     for (int e = tid; e < RP * NT; e += T::NTHR) {
         const int r = e / NT, n = e % NT;
         const bool ok = r < p.R && n < p.N;
         const long src = ((long)h * p.R + r) * p.N + n;
-        tb[e] = ok ? f2bf(p.q_bias[src]) : 0;
-        tb[RP * NT + e] = ok ? f2bf(p.k_bias[src]) : 0;
+        if constexpr (!NAT) tb[e] = ok ? f2bf(p.q_bias[src]) : 0;
+        tb[KB + e] = ok ? f2bf(p.k_bias[src]) : 0;
     }
     for (int e = tid; e < RP * PT; e += T::NTHR) {
         const int r = e / PT, pc = e % PT;
         const bool ok = r < p.R && pc < p.P;
-        tb[2 * RP * NT + e] = ok ? f2bf(p.mimo_v[((long)h * p.R + r) * p.P + pc]) : 0;
+        tb[KB + RP * NT + e] = ok ? f2bf(p.mimo_v[((long)h * p.R + r) * p.P + pc]) : 0;
     }
     unsigned short* sPsiT = reinterpret_cast<unsigned short*>(smem + L.r3);
     constexpr int used = RP * T::Cp, pad = T::MT - used;
@@ -890,8 +918,8 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_agg(Params 
     unsigned short* sPsi = reinterpret_cast<unsigned short*>(smem + L.r3);   // [MT][PPN] Psi
     const float* sc = reinterpret_cast<const float*>(smem + L.sc);
     const float* scs = reinterpret_cast<const float*>(smem + L.cs);
-    const unsigned short* tbk = reinterpret_cast<const unsigned short*>(smem + L.tb) + RP * NT;
-    const unsigned short* smv = reinterpret_cast<const unsigned short*>(smem + L.tb) + 2 * RP * NT;
+    const unsigned short* tbk = reinterpret_cast<const unsigned short*>(smem + L.tb);   // the aggregate has no q_bias
+    const unsigned short* smv = reinterpret_cast<const unsigned short*>(smem + L.tb) + RP * NT;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int l16 = lane & 15, q4 = lane >> 4;
