@@ -91,8 +91,14 @@ def test_fp32_and_siso_argument_checks_without_a_device():
     a.B, a.S, a.H, a.G, a.R, a.N, a.P = 1, 300, 2, 1, 8, 128, 128
     a.chunk_size, a.rotary_dim_divisor = 16, 4
     n = ctypes.c_size_t(0)
+    # the largest tiles of the range fit (K~ in scratch when the LDS cannot hold it)
+    assert L.mimo_bwd_fwd_f32_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _lib.MIMO_OK
+    a.chunk_size = 32   # R * chunk_size = 256: outside the API's range
+    assert L.mimo_bwd_fwd_f32_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _lib.MIMO_ERR_VALUE
+    assert "chunk_size * R" in _lib.last_error()
+    a.chunk_size, a.N = 16, 144
     assert L.mimo_bwd_fwd_f32_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _lib.MIMO_ERR_UNSUPPORTED
-    assert "LDS" in _lib.last_error()
+    assert "N must be" in _lib.last_error()
     a.R, a.N, a.P = 4, 64, 64
     assert L.mimo_bwd_fwd_f32_workspace_size(ctypes.byref(a), ctypes.byref(n)) == _lib.MIMO_OK
     assert L.mimo_bwd_fwd_f32(ctypes.byref(a), None) == _lib.MIMO_ERR_VALUE   # NULL inputs
