@@ -101,7 +101,11 @@ mimo_status mimo_bwd_fwd_workspace_size(const mimo_bwd_fwd_args *args, size_t *b
 
 /* Validate the arguments and queue the whole computation on `stream`
  * (a hipStream_t; NULL = the default stream of the current device).
- * Asynchronous: returns once the kernels are queued. Within the pages'
+ * Asynchronous: returns once the kernels are queued. A call without y (no
+ * mimo_o and no z: the outputs are states and qk_dot) runs its qk_dot kernel
+ * on a stream of the library's own (one per calling thread and device, made
+ * on first use and kept, default priority), ordered after the work already
+ * queued on `stream`; work queued on `stream` afterwards waits for it. Within the pages'
  * constraints (C*R <= 128, N, P <= 128, N even and divisible by the rotary
  * divisor, H % G == 0) this library further requires N and P to be
  * multiples of 16, C <= 64, R <= 8 and RP * CP <= 128, where RP is R rounded

@@ -1018,7 +1018,42 @@ mimo_status mimo_bwd_fwd_workspace_size(const mimo_bwd_fwd_args* args, size_t* b
 
 // The backward first stage (out == nullptr) or the layer output o (out != nullptr,
 // `a` built by as_bwd_args).
-static mimo_status run(const mimo_bwd_fwd_args* a, uint16_t* out, void* stream, void* const* events) {
+// A side stream and two events per (host thread, device), created on first use and kept
+// for the life of the thread. A call whose chunk pass has an independent kernel (qk_dot
+// of the calls without y) forks it onto the side stream after the caller's earlier work
+// and joins it back before the chunk pass ends, so it can fill the CUs the chain leaves
+// idle (the aggregate's tail, the scan, launch gaps). Default priority, like every stream
+// here.
+struct Side {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+thread_local Side g_side[64];
+
+mimo_status side_stream(Side** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(MIMO_ERR_HIP, "hipGetDevice failed");
+    Side& sd = g_side[dev];
+    if (sd.s == nullptr) {
+        hipStream_t st = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess)
+            return fail(MIMO_ERR_HIP, "hipStreamCreateWithFlags failed");
+        if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess)
+            return fail(MIMO_ERR_HIP, "hipEventCreateWithFlags failed");
+        sd.s = st;
+        sd.fork = f;
+        sd.join = j;
+    }
+    *out = &sd;
+    return MIMO_OK;
+}
+
+// fork: qk_dot of a no-y call on the side stream (false: in order on the call's stream,
+// for the entry point that may create nothing)
+static mimo_status run(const mimo_bwd_fwd_args* a, uint16_t* out, void* stream, void* const* events,
+                       bool fork = true) {
     g_err.clear();
     const bool fwd = out != nullptr;
     Plan pl;
@@ -1105,17 +1140,37 @@ static mimo_status run(const mimo_bwd_fwd_args* a, uint16_t* out, void* stream, 
             if (events[i] == nullptr) return fail(MIMO_ERR_VALUE, "timing event %d is NULL", i);
     if ((s = set_lds(kmain, lds_main)) != MIMO_OK) return s;
     if ((s = mark(0)) != MIMO_OK) return s;
+    // the fork point is recorded before the chain; the side kernel is queued after the
+    // chain's first kernel, which is on the critical path and so is dispatched first
+    Side* sd = nullptr;
+    if (states_only && fork) {
+        if ((s = side_stream(&sd)) != MIMO_OK) return s;
+        if (hipEventRecord(sd->fork, st) != hipSuccess) return fail(MIMO_ERR_HIP, "hipEventRecord failed");
+    }
+    auto side_qk = [&]() -> mimo_status {
+        if (sd == nullptr) return MIMO_OK;
+        if (hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
+            return fail(MIMO_ERR_HIP, "fork onto the side stream failed");
+        mimo_status r = launch_qk(p, pl.NT, sd->s);
+        if (r != MIMO_OK) return r;
+        if (hipEventRecord(sd->join, sd->s) != hipSuccess) return fail(MIMO_ERR_HIP, "hipEventRecord failed");
+        return MIMO_OK;
+    };
     if (pl.nseg > 1) {
         if ((s = set_lds(kagg, pl.lds_agg)) != MIMO_OK) return s;
         if ((s = launch(kagg, dim3(grid_blocks(p, pl.nsub)), dim3(pl.NW * 64), pl.lds_agg, st, p)) != MIMO_OK) return s;
+        if ((s = side_qk()) != MIMO_OK) return s;
         if ((s = mark(1)) != MIMO_OK) return s;
         if ((s = launch_scan(p, BH, st)) != MIMO_OK) return s;
-    } else if ((s = mark(1)) != MIMO_OK) {
-        return s;
+    } else {
+        if ((s = mark(1)) != MIMO_OK) return s;
     }
     if ((s = mark(2)) != MIMO_OK) return s;
     if ((s = launch(kmain, dim3(grid_blocks(p, pl.nseg)), dim3(pl.NW * 64), lds_main, st, p)) != MIMO_OK) return s;
-    if (states_only && (s = launch_qk(p, pl.NT, st)) != MIMO_OK) return s;
+    if (pl.nseg <= 1 && (s = side_qk()) != MIMO_OK) return s;
+    if (sd != nullptr && hipStreamWaitEvent(st, sd->join, 0) != hipSuccess)
+        return fail(MIMO_ERR_HIP, "join of the side stream failed");
+    if (states_only && sd == nullptr && (s = launch_qk(p, pl.NT, st)) != MIMO_OK) return s;
     if ((s = mark(3)) != MIMO_OK) return s;
     if (pl.nseg > 1 && p.need_y && !fwd)
         if ((s = launch_finish(p, st)) != MIMO_OK) return s;
@@ -1149,7 +1204,7 @@ mimo_status mimo_bwd_fwd_noalloc(const mimo_bwd_fwd_args* a, void* stream) {
         if ((s = scratch_on_current_device(&b.workspace)) != MIMO_OK) return s;
         b.workspace_bytes = MIMO_NOALLOC_SCRATCH_BYTES;
     }
-    return run(&b, nullptr, stream, nullptr);
+    return run(&b, nullptr, stream, nullptr, false);
 }
 
 mimo_status mimo_fwd_workspace_size(const mimo_fwd_args* args, size_t* bytes) {
