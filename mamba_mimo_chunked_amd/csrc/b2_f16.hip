@@ -4,6 +4,6 @@
 
 namespace mimo {
 namespace b2 {
-Kern kernels_f16(int md) { return kernel_pair<DT_F16>(md); }
+Kern kernels_f16(int md, bool ex) { return kernel_pair<DT_F16>(md, ex); }
 }  // namespace b2
 }  // namespace mimo

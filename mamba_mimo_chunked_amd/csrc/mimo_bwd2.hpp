@@ -439,7 +439,11 @@ struct DivS {
     int d;
     float rd;
     __device__ explicit DivS(int d_) : d(d_), rd(1.0f / static_cast<float>(d_)) {}
-    __device__ int q(int e) const { return static_cast<int>((static_cast<float>(e) + 0.5f) * rd); }
+    __device__ int q(int e) const {
+        // a divisor the compiler sees as a constant (the shape-exact instances): a shift
+        if (__builtin_constant_p(d) && d > 0) return static_cast<int>(static_cast<unsigned>(e) / static_cast<unsigned>(d));
+        return static_cast<int>((static_cast<float>(e) + 0.5f) * rd);
+    }
     __device__ int r(int e) const { return e - q(e) * d; }
 };
 
@@ -828,8 +832,22 @@ __device__ __forceinline__ Tiles tiles_at(float* base) {
 // chunks of the sub-segment from the last one down, and the product of the decays.
 // Sub-segment j covers part j % F of segment 1 + j / F (segment 0's aggregate is
 // never needed).
-template <int IT, int MD>
+// EX: the shape-exact instance (R = 4, C = 16, N = P = 64, rotated width 16): the sizes
+// become constants, so index arithmetic folds (divisions by C, N/8, P/8 become shifts).
+template <bool EX>
+__device__ __forceinline__ void exact_shape(Params2& p) {
+    if constexpr (EX) {
+        p.R = 4;
+        p.C = 16;
+        p.N = 64;
+        p.P = 64;
+        p.W = 16;
+    }
+}
+
+template <int IT, int MD, bool EX = false>
 __global__ __launch_bounds__(NTHR, 2) void k_agg2(Params2 p) {
+    exact_shape<EX>(p);
     using GE = Geo<MD>;
     constexpr int LD = GE::LD;
     extern __shared__ __align__(16) float sm[];
@@ -944,8 +962,9 @@ __device__ __forceinline__ void finish_rot(const Params2& p, void* dst, const fl
 }
 
 // The chunk pass of one segment, chunks from the last down.
-template <int IT, int MD>
+template <int IT, int MD, bool EX = false>
 __global__ __launch_bounds__(NTHR2, 1) void k_main2(Params2 p) {
+    exact_shape<EX>(p);
     using GE = Geo<MD>;
     using IS = Items<NTHR2, MD>;
     constexpr int LD = GE::LD, HM = MD / 2;
@@ -1244,13 +1263,16 @@ struct Kern {
     const void *agg, *main;
 };
 template <int IT>
-Kern kernel_pair(int md) {
+Kern kernel_pair(int md, bool ex) {
+    if (md == 64 && ex)
+        return Kern{reinterpret_cast<const void*>(&k_agg2<IT, 64, true>), reinterpret_cast<const void*>(&k_main2<IT, 64, true>)};
     if (md == 64) return Kern{reinterpret_cast<const void*>(&k_agg2<IT, 64>), reinterpret_cast<const void*>(&k_main2<IT, 64>)};
     return Kern{reinterpret_cast<const void*>(&k_agg2<IT, 128>), reinterpret_cast<const void*>(&k_main2<IT, 128>)};
 }
-Kern kernels_bf16(int md);
-Kern kernels_f16(int md);
-Kern kernels_f32(int md);
+// ex: the shape-exact instances (R = 4, C = 16, N = P = 64, rotated width 16; md 64 only)
+Kern kernels_bf16(int md, bool ex);
+Kern kernels_f16(int md, bool ex);
+Kern kernels_f32(int md, bool ex);
 
 #ifdef MIMO_B2_COMMON_KERNELS
 // dS at the start of every sub-segment, from the end of the sequence: E_j = U_j +

@@ -939,9 +939,12 @@ mimo_status run_b2(const mimo_bwd_bwd_args* a, void* stream, void* const* events
     };
     Params pp = {};
     pp.B = p.B; pp.H = p.H; pp.G = p.G;
-    const b2::Kern kern = a->in_dtype == MIMO_DTYPE_FP32   ? b2::kernels_f32(pl.md)
-                          : a->in_dtype == MIMO_DTYPE_FP16 ? b2::kernels_f16(pl.md)
-                                                           : b2::kernels_bf16(pl.md);
+    // shape-exact instances where the call's shape is theirs (see exact_shape); a switch
+    // for tests can force the generic ones
+    const bool ex2 = !force_generic() && pl.md == 64 && p.R == 4 && p.C == 16 && p.N == 64 && p.P == 64 && p.W == 16;
+    const b2::Kern kern = a->in_dtype == MIMO_DTYPE_FP32   ? b2::kernels_f32(pl.md, ex2)
+                          : a->in_dtype == MIMO_DTYPE_FP16 ? b2::kernels_f16(pl.md, ex2)
+                                                           : b2::kernels_bf16(pl.md, ex2);
     const void* kmain = kern.main;
     const int lds_main = (pl.md == 64 ? b2::Geo<64>::LDS_MAIN : b2::Geo<128>::LDS_MAIN) * 4;
     const int lds_agg = (pl.md == 64 ? b2::Geo<64>::LDS_AGG : b2::Geo<128>::LDS_AGG) * 4;

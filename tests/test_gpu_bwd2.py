@@ -173,6 +173,30 @@ def test_bwd2_perf_shape_sampled_heads():
         log(f"    h={h} " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
 
 
+@pytest.mark.parametrize("case", [Case(1, 300, 3, 1, 64, 64, 4, 16, name="b2_exact_reduced"),
+                                  Case(2, 257, 4, 4, 64, 64, 4, 16, reduce_o=False, has_z=False, has_d=False,
+                                       name="b2_exact_nonreduced_nod")], ids=lambda c: c.name)
+def test_bwd2_shape_exact_and_generic_agree(case, monkeypatch):
+    """R=4, C=16, N=P=64 with rotary divisor 4 runs the shape-exact stage-2 instances
+    (sizes as constants); the generic ones (forced through MIMO_FORCE_GENERIC) must
+    give the same bits, and both meet the oracle bar."""
+    log(f"[bwd2 exact-vs-generic] {case.name}")
+    inp = make_inputs(case)
+    states, qk = _caches(inp)
+    ex = _run_gpu(inp, states, qk, torch.float32)
+    monkeypatch.setenv("MIMO_FORCE_GENERIC", "1")
+    gen = _run_gpu(inp, states, qk, torch.float32)
+    monkeypatch.delenv("MIMO_FORCE_GENERIC")
+    ref = _oracle(inp, states, qk)
+    _compare(ex, ref, f"{case.name} exact: ")
+    _compare(gen, ref, f"{case.name} generic: ")
+    for key in bwd2.NAMES:
+        if ex[key] is None or gen[key] is None:
+            assert ex[key] is None and gen[key] is None, key
+            continue
+        assert torch.equal(ex[key], gen[key]), f"{key}: shape-exact and generic instances differ"
+
+
 def test_bwd2_every_element_written_and_deterministic():
     case = Case(1, 300, 2, 1, 64, 64, 4, 16, name="det")
     inp = make_inputs(case)
