@@ -80,6 +80,31 @@ def test_bwd_fwd_fp32(case):
     log("    " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
+@pytest.mark.parametrize("case", [Case(1, 300, 3, 1, 64, 64, 4, 16, name="f32_exact_reduced_z"),
+                                  Case(2, 257, 4, 4, 64, 64, 4, 16, reduce_o=False, has_z=False, has_d=False,
+                                       name="f32_exact_nonreduced")], ids=lambda c: c.name)
+def test_bwd_fwd_fp32_shape_exact_and_generic_agree(case, monkeypatch):
+    """R=4, C=16, N=P=64 with rotary divisor 4 runs the shape-exact fp32 instances
+    (sizes as constants); the generic ones (forced through MIMO_FORCE_GENERIC) must give
+    the same bits, and both meet the oracle bar. The layer output likewise."""
+    log(f"[fp32 exact-vs-generic] {case.name}")
+    inp = make_inputs(case)
+    d = to_device(inp)
+    ex, ex_o = run_bwd32(d), run_fwd32(d)
+    monkeypatch.setenv("MIMO_FORCE_GENERIC", "1")
+    gen, gen_o = run_bwd32(d), run_fwd32(d)
+    monkeypatch.delenv("MIMO_FORCE_GENERIC")
+    ref = o1.run_inputs(inp, fp32=True)
+    compare(ex, ref, tol=TOL32, label=f"{case.name} exact: ")
+    compare(gen, ref, tol=TOL32, label=f"{case.name} generic: ")
+    for a, b in zip(ex, gen):
+        if a is None or b is None:
+            assert a is None and b is None
+            continue
+        assert torch.equal(a, b), "shape-exact and generic fp32 instances differ"
+    assert torch.equal(ex_o, gen_o), "shape-exact and generic fp32 layer outputs differ"
+
+
 def test_bwd_fwd_fp32_perf_shape_all_heads():
     case = CONFIGS["perf_s8192"].with_(seed=5)
     log("[fp32] perf_s8192 (all heads)")
