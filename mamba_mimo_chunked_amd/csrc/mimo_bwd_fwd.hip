@@ -352,20 +352,24 @@ mimo_status set_lds(kfn f, int bytes) {
 // qk_dot[b,h,t,r,r2] = bf16(q0[t,r] . k0[t,r2]), q0 = bf16(q + bf16(q_bias)) and k0
 // likewise (biased, unrotated). One workgroup per (batch, q/k group, 16 tokens): in one
 // round of loads it stages the group's raw q and k rows of the 16 tokens ([2][16] token
-// rows of R*NT bf16 plus 16 of padding, read once for all the group's heads; the padding
-// puts the 16 tokens of a fragment read on distinct LDS banks) and the rounded biases of up to eight of
-// the group's heads ([8][2][R][NT], bf16 values held as fp32 so that the bias add needs
-// no unpacking; zero past N and the sequence); wave w then
-// serves heads w, w + 4, ... of the batch, and further batches of heads restage the
-// biases. A head's dots are the diagonals of 16 x 16 MFMA tiles
-// (rows the tokens' q0 of rank r, columns their k0 of rank r2), built from the same
-// fragments and steps as the chunk pass's qk_dot, so both give the same bits. Lane
-// (l16, q4) with q4 == l16 / 4 ends up holding every dot of token l16 and stores them,
-// in 8- or 16-byte pieces where R allows.
+// rows of RP*NT bf16 plus 16 of padding, RP being R rounded up to a power of two; read
+// once for all the group's heads; the padding puts the 16 tokens of a fragment read on
+// distinct LDS banks) and the rounded biases of up to eight of the group's heads
+// ([8][2][RP][NT], bf16 values held as fp32 so that the bias add needs no unpacking;
+// zero past R, N and the sequence); wave w then serves heads w, w + 4, ... of the
+// batch, and further batches of heads restage the biases. A head's dots are the
+// diagonals of 16 x 16 MFMA tiles (rows the tokens' q0 of rank r, columns their k0 of
+// rank r2), built from the same fragments and steps as the chunk pass's qk_dot, so both
+// give the same bits. Lane (l16, q4) with q4 == l16 / 4 ends up holding every dot of
+// token l16 and stores them, in 8- or 16-byte pieces where R allows.
 template <int NT, int RP>   // RP: the rank count rounded up to a power of two (register arrays)
 __global__ __launch_bounds__(256) void k_qk(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int TS = p.R * NT + 16;   // token row pitch (bf16)
+    // every row and bias table is laid out for RP ranks (padded ranks stay zero), so
+    // that the staging index arithmetic is shifts and masks only
+    constexpr int NT8 = NT / 8, TS = RP * NT + 16;   // token row pitch (bf16)
+    constexpr unsigned LN8 = NT8 == 4 ? 2 : (NT8 == 8 ? 3 : 4), LR = RP == 1 ? 0 : (RP == 2 ? 1 : (RP == 4 ? 2 : 3));
+    static_assert((1 << LN8) == NT8 && (1 << LR) == RP, "power-of-two tile sizes");
     unsigned short* sx = reinterpret_cast<unsigned short*>(smem);   // [2][16][TS]: q, then k
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
     const int ntt = (p.S + 15) / 16;
@@ -373,33 +377,36 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
     const int bg = unit / ntt, tile = unit - bg * ntt;
     const int b = bg / p.G, g = bg - b * p.G, hpg = p.H / p.G;
     const int R = p.R, N = p.N, t0 = 16 * tile;
-    constexpr int KS = NT / 32, NT8 = NT / 8;
-    float* sb = reinterpret_cast<float*>(sx + 2 * 16 * TS);   // [8][2][R][NT] rounded biases of a batch of heads
+    constexpr int KS = NT / 32;
+    float* sb = reinterpret_cast<float*>(sx + 2 * 16 * TS);   // [8][2][RP][NT] rounded biases of a batch of heads
     const int t = t0 + l16;
     const bool tok = t < p.S;
     const bool diag = q4 == (l16 >> 2) && tok;
     const int v = l16 & 3;
     for (int h0 = 0; h0 < hpg; h0 += 8) {
         const int nh = min(8, hpg - h0);
-        const int rows = h0 == 0 ? 2 * 16 * R * NT8 : 0, bias = nh * 2 * R * NT8;
+        const unsigned rows = h0 == 0 ? 2u * 16u * RP * NT8 : 0u, bias = (unsigned)nh * 2u * RP * NT8;
         if (h0 > 0) __syncthreads();   // every wave is done with the previous batch's biases
-        for (int e = tid; e < rows + bias; e += 256) {
+        for (unsigned e = tid; e < rows + bias; e += 256) {
             if (e < rows) {
+                // e = ((which * 16 + tk) * RP + r) * NT8 + c8
                 u32x4 w = {0u, 0u, 0u, 0u};
-                const int c8 = e % NT8, rest = e / NT8;
-                const int r = rest % R, tk = (rest / R) % 16, which = rest / (16 * R);
-                const int t = t0 + tk, col = 8 * c8;
-                if (t < p.S && col < N) {
-                    const unsigned short* x = which ? p.k : p.q;
+                const unsigned c8 = e & (NT8 - 1), rest = e >> LN8;
+                const unsigned r = rest & (RP - 1), row = rest >> LR;
+                const int t = t0 + (int)(row & 15u), col = 8 * (int)c8;
+                if ((int)r < R && t < p.S && col < N) {
+                    const unsigned short* x = (row >> 4) ? p.k : p.q;
                     w = *reinterpret_cast<const u32x4*>(x + ((((long)b * p.S + t) * R + r) * p.G + g) * N + col);
                 }
-                *reinterpret_cast<u32x4*>(sx + (which * 16 + tk) * TS + r * NT + col) = w;
+                *reinterpret_cast<u32x4*>(sx + row * TS + r * NT + col) = w;
             } else {
+                // e - rows = ((hh * 2 + which) * RP + r) * NT8 + c8
                 f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0;
-                const int e2 = e - rows, c8 = e2 % NT8, rest = e2 / NT8;
-                const int r = rest % R, which = (rest / R) % 2, hh = rest / (2 * R), col = 8 * c8;
-                if (col < N) {
-                    const float* bp = (which ? p.k_bias : p.q_bias) + ((long)(g * hpg + h0 + hh) * R + r) * N + col;
+                const unsigned e2 = e - rows, c8 = e2 & (NT8 - 1), rest = e2 >> LN8;
+                const unsigned r = rest & (RP - 1), hw = rest >> LR;   // hw = hh * 2 + which
+                const int col = 8 * (int)c8;
+                if ((int)r < R && col < N) {
+                    const float* bp = ((hw & 1u) ? p.k_bias : p.q_bias) + ((long)(g * hpg + h0 + (int)(hw >> 1)) * R + r) * N + col;
                     const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
@@ -407,7 +414,7 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
                         w1[d] = rnd(b1[d]);
                     }
                 }
-                float* dst = sb + ((hh * 2 + which) * R + r) * NT + col;
+                float* dst = sb + rest * NT + col;
                 *reinterpret_cast<f32x4*>(dst) = w0;
                 *reinterpret_cast<f32x4*>(dst + 4) = w1;
             }
@@ -415,6 +422,55 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
         __syncthreads();
         for (int hh = wave; hh < nh; hh += 4) {
             const int h = g * hpg + h0 + hh;
+            if constexpr (RP == 4) {
+                // Four tiles, one per 4 tokens: rows and columns are the 16 (token, rank)
+                // pairs of tokens 4 grp .. 4 grp + 3, row l16 = (token 4 grp + l16 / 4,
+                // rank l16 % 4). Lane (l16, q4) supplies that row of K0 (A operand) and of
+                // Q0 (B operand), columns 32 ks + 8 q4 .. + 7; it then holds
+                // dot(k0[token 4 grp + q4, rank i], q0[token 4 grp + l16 / 4, rank l16 % 4])
+                // for i = 0..3, so the lanes with q4 == l16 / 4 hold rank r = l16 % 4's row
+                // of their token's dots (each product is exact, so the operand order does
+                // not change the sums). A row past R or past the sequence only reaches
+                // dots that are not stored (staged rows and biases past R are zero).
+                // (the lane's offsets pass through an empty asm statement, so that the
+                // raw-row reads, which do not depend on the head, are redone per head
+                // instead of being held in registers across the head loop)
+                int rl = l16 & 3, tq = l16 >> 2;
+                asm volatile("" : "+v"(rl), "+v"(tq));
+#pragma unroll
+                for (int grp = 0; grp < 4; ++grp) {
+                    const int tl = 4 * grp + tq;
+                    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int col = 32 * ks + 8 * q4;
+                        u32x4 fr[2];
+#pragma unroll
+                        for (int which = 0; which < 2; ++which) {
+                            const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + (which * 16 + tl) * TS + rl * NT + col);
+                            const float* bp = sb + ((hh * 2 + which) * RP + rl) * NT + col;
+                            const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
+                            fr[which] = u32x4{pk2(lo16(raw[0]) + b0[0], hi16(raw[0]) + b0[1]),
+                                              pk2(lo16(raw[1]) + b0[2], hi16(raw[1]) + b0[3]),
+                                              pk2(lo16(raw[2]) + b1[0], hi16(raw[2]) + b1[1]),
+                                              pk2(lo16(raw[3]) + b1[2], hi16(raw[3]) + b1[3])};
+                        }
+                        a4 = mfma(fr[1], fr[0], a4);
+                    }
+                    const int tt = t0 + 4 * grp + q4;
+                    if (q4 == tq && rl < R && tt < p.S) {
+                        unsigned short* out = p.qk_dot + (((long)(b * p.H + h) * p.S + tt) * R + rl) * R;
+                        if (R == 4) {
+                            *reinterpret_cast<u32x2*>(out) = u32x2{pk2(a4[0], a4[1]), pk2(a4[2], a4[3])};
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (i < R) out[i] = bits16(rnd(a4[i]));
+                        }
+                    }
+                }
+                continue;
+            }
             // fragments of token l16: rank r, columns 32 ks + 8 q4 .. + 7, biased and rounded
             // (zero past N, where raw and bias are zero, and past the sequence)
             u32x4 qf[RP][KS], kf[RP][KS];
@@ -428,7 +484,7 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
 #pragma unroll
                     for (int which = 0; which < 2; ++which) {
                         const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + (which * 16 + l16) * TS + r * NT + col);
-                        const float* bp = sb + ((hh * 2 + which) * R + r) * NT + col;
+                        const float* bp = sb + ((hh * 2 + which) * RP + r) * NT + col;
                         const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
                         // bf16(raw + bias): the packing conversion is the rounding
                         const u32x4 o = {pk2(lo16(raw[0]) + b0[0], hi16(raw[0]) + b0[1]),
@@ -482,9 +538,11 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
     }
 }
 
-// LDS of k_qk: the staged rows (bf16, padded) and one batch of biases (fp32): at most 129 KB.
+// LDS of k_qk: the staged rows (bf16, padded) and one batch of biases (fp32), both
+// for the rank count rounded up to a power of two: at most 129 KB.
 int qk_lds_bytes(const Params& p, int NT) {
-    return 2 * 16 * (p.R * NT + 16) * 2 + 2 * std::min(8, p.H / p.G) * p.R * NT * 4;
+    const int RP = p.R <= 1 ? 1 : (p.R <= 2 ? 2 : (p.R <= 4 ? 4 : 8));
+    return 2 * 16 * (RP * NT + 16) * 2 + 2 * std::min(8, p.H / p.G) * RP * NT * 4;
 }
 
 mimo_status launch_qk(const Params& p, int NT, hipStream_t st) {

@@ -210,6 +210,22 @@ def test_reduced_equals_nonreduced_bitwise():
         assert _same(a[i], b[i]), NAMES[i]
 
 
+@pytest.mark.parametrize("R,N", [(4, 64), (3, 64), (2, 32), (8, 128)], ids=lambda x: str(x))
+def test_qk_dot_same_bits_with_and_without_y(R, N):
+    """qk_dot depends on q, k and their biases only. A call that needs y takes it
+    from the chunk pass, a call without y (non-reduced dout, no z) from its own
+    kernel; both round the same biased rows and sum the same products in the same
+    steps, so the two must agree bit for bit, tail tokens included."""
+    case = Case(1, 203, 4, 2, N, 64, R, 16, name=f"qk_bits_R{R}_N{N}")
+    log(f"[qk-bits] {case}")
+    inp = make_inputs(case)
+    a = _gpu_np(run_gpu(to_device(inp)))
+    dnr = inp["dout"][:, :, None].expand(-1, -1, R, -1, -1).contiguous()
+    b = _gpu_np(run_gpu(to_device(dict(inp, dout=dnr, mimo_o=None, z=None, mimo_z=None))))
+    assert b[0] is None and b[2] is None and b[3] is None
+    assert _same(a[4], b[4]), "qk_dot differs between the calls with and without y"
+
+
 def test_unused_segsum_entries_ignored():
     case = Case(1, 75, 2, 1, 64, 64, 4, 16)
     inp = make_inputs(case)
