@@ -1391,6 +1391,30 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         // tile; its diagonal holds the same-token dots. Lane (l16, q4) holds rows
         // 4*q4 .. 4*q4+3 of column l16, so the lanes with q4 == l16/4 hold one
         // diagonal element each (token 16*tt + l16). Padded rank pairs get zero.
+        if constexpr (RP == 4 && CT == 1 && NW == 4) {
+            // Four ranks, one token tile: one tile per wave instead, whose rows and
+            // columns are the (token, rank) pairs of tokens 4 wave .. 4 wave + 3 (row l16 =
+            // token 4 wave + l16 / 4, rank l16 % 4), K0 rows as the A operand and Q0 rows
+            // as B. Lane (l16, q4) then holds dot(k0[token 4 wave + q4, rank i],
+            // q0[token 4 wave + l16 / 4, rank l16 % 4]) for i = 0..3: on the lanes with
+            // q4 == l16 / 4 that is row l16 % 4 of their token's dots, stored as one
+            // 16-byte row (each product is exact, so the operand order does not change
+            // the sums). Padded rank pairs get zero.
+            const int rl = l16 & 3, tl = 4 * wave + (l16 >> 2);
+            f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NT / 32; ++ks) {
+                const u32x4 a = lds_ld<u32x4>(sK + (16 * rl + tl) * LDQ + 32 * ks + 8 * q4);
+                const u32x4 bb = lds_ld<u32x4>(sQ + (16 * rl + tl) * LDQ + 32 * ks + 8 * q4);
+                a4 = mfma(a, bb, a4);
+            }
+            if (q4 == (l16 >> 2)) {
+                f32x4 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = (rl < R && i < R) ? rnd(a4[i]) : 0.f;
+                lds_st<f32x4>(sQK + tl * QKS + rl * RP, o);
+            }
+        } else {
 #pragma unroll
         for (int w = 0; w < (T::QKT + NW - 1) / NW; ++w) {
             const int u = wave + w * NW;
@@ -1411,6 +1435,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                 }
                 if (q4 == (l16 >> 2)) sQK[(16 * tt + l16) * QKS + ri * RP + rj] = val;
             }
+        }
         }
         bar();
 
