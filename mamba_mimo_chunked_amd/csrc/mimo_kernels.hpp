@@ -1386,33 +1386,51 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
         }
         bar();
 
-        // ---- phase B: qk_dot of the same token (biased, unrotated) by MFMA: tile
-        // (ri, rj, tt) is Q0 rows of rank ri times K0 rows of rank rj over one token
-        // tile; its diagonal holds the same-token dots. Lane (l16, q4) holds rows
-        // 4*q4 .. 4*q4+3 of column l16, so the lanes with q4 == l16/4 hold one
-        // diagonal element each (token 16*tt + l16). Padded rank pairs get zero.
-        if constexpr (RP == 4 && CT == 1 && NW == 4) {
-            // Four ranks, one token tile: one tile per wave instead, whose rows and
-            // columns are the (token, rank) pairs of tokens 4 wave .. 4 wave + 3 (row l16 =
-            // token 4 wave + l16 / 4, rank l16 % 4), K0 rows as the A operand and Q0 rows
-            // as B. Lane (l16, q4) then holds dot(k0[token 4 wave + q4, rank i],
-            // q0[token 4 wave + l16 / 4, rank l16 % 4]) for i = 0..3: on the lanes with
-            // q4 == l16 / 4 that is row l16 % 4 of their token's dots, stored as one
-            // 16-byte row (each product is exact, so the operand order does not change
-            // the sums). Padded rank pairs get zero.
-            const int rl = l16 & 3, tl = 4 * wave + (l16 >> 2);
-            f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+        // ---- phase B: qk_dot of the same token (biased, unrotated) by MFMA, into sQK.
+        // One rank: tile tt is Q0 rows times K0 rows over one token tile; its diagonal
+        // holds the same-token dots. Lane (l16, q4) holds rows 4*q4 .. 4*q4+3 of
+        // column l16, so the lanes with q4 == l16/4 hold one diagonal element each
+        // (token 16*tt + l16).
+        if constexpr (RP >= 2) {
+            // Two or more ranks: tiles whose rows and columns are the 16 (token, rank) pairs of
+            // TPT = 16 / RP consecutive tokens (row l16 = token u TPT + l16 / RP, rank
+            // l16 % RP), K0 rows as the A operand and Q0 rows as B. Lane (l16, q4) then
+            // holds dot(k0[row 4 q4 + i], q0[row l16]) for i = 0..3; those whose two
+            // rows share a token are row r = l16 % RP of that token's dots, columns
+            // (4 q4 + i) % RP: four of them (RP >= 4) or two (RP = 2), stored as one LDS
+            // write. Each bf16 product is exact in fp32 and the K steps are the same, so
+            // the sums are those of the rank-pair tiles. Padded rank pairs get zero.
+            constexpr int TPT = 16 / RP, TL = Cp * RP / 16;
+            const int rl = l16 % RP;
 #pragma unroll
-            for (int ks = 0; ks < NT / 32; ++ks) {
-                const u32x4 a = lds_ld<u32x4>(sK + (16 * rl + tl) * LDQ + 32 * ks + 8 * q4);
-                const u32x4 bb = lds_ld<u32x4>(sQ + (16 * rl + tl) * LDQ + 32 * ks + 8 * q4);
-                a4 = mfma(a, bb, a4);
-            }
-            if (q4 == (l16 >> 2)) {
-                f32x4 o;
+            for (int w = 0; w < (TL + NW - 1) / NW; ++w) {
+                const int u = wave + w * NW;
+                if (TL % NW == 0 || u < TL) {
+                    const int tl = u * TPT + l16 / RP;
+                    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = (rl < R && i < R) ? rnd(a4[i]) : 0.f;
-                lds_st<f32x4>(sQK + tl * QKS + rl * RP, o);
+                    for (int ks = 0; ks < NT / 32; ++ks) {
+                        const u32x4 a = lds_ld<u32x4>(sK + (rl * Cp + tl) * LDQ + 32 * ks + 8 * q4);
+                        const u32x4 bb = lds_ld<u32x4>(sQ + (rl * Cp + tl) * LDQ + 32 * ks + 8 * q4);
+                        a4 = mfma(a, bb, a4);
+                    }
+                    if constexpr (RP >= 4) {
+                        if ((4 * q4) / RP == l16 / RP) {
+                            const int r20 = (4 * q4) % RP;
+                            f32x4 o;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) o[i] = (rl < R && r20 + i < R) ? rnd(a4[i]) : 0.f;
+                            lds_st<f32x4>(sQK + tl * QKS + rl * RP + r20, o);
+                        }
+                    } else {
+                        if (q4 == (l16 >> 2)) {
+                            const bool hi = (l16 >> 1) & 1;
+                            const float x0 = hi ? a4[2] : a4[0], x1 = hi ? a4[3] : a4[1];
+                            const f32x2 o = {rl < R ? rnd(x0) : 0.f, (rl < R && R > 1) ? rnd(x1) : 0.f};
+                            lds_st<f32x2>(sQK + tl * QKS + rl * RP, o);
+                        }
+                    }
+                }
             }
         } else {
 #pragma unroll
