@@ -357,12 +357,11 @@ mimo_status set_lds(kfn f, int bytes) {
 // distinct LDS banks) and the rounded biases of up to eight of the group's heads
 // ([8][2][RP][NT], bf16 values held as fp32 so that the bias add needs no unpacking;
 // zero past R, N and the sequence); wave w then serves heads w, w + 4, ... of the
-// batch, and further batches of heads restage the biases. A head's dots are the
-// diagonals of 16 x 16 MFMA tiles (rows the tokens' q0 of rank r, columns their k0 of
-// rank r2), built from the same fragments and steps as the chunk pass's qk_dot, so both
-// give the same bits. Lane (l16, q4) with q4 == l16 / 4 ends up holding every dot of
-// token l16 and stores them, in 8- or 16-byte pieces where R allows.
-template <int NT, int RP>   // RP: the rank count rounded up to a power of two (register arrays)
+// batch, and further batches of heads restage the biases. A head's dots come from
+// 16 x 16 MFMA tiles whose rows and columns are (token, rank) pairs, with the chunk
+// pass's fragments and K steps (each product is exact), so both give the same bits;
+// each lane on a tile's block diagonal stores its part of one row of its token's dots.
+template <int NT, int RP>   // RP: the rank count rounded up to a power of two (tile shape, LDS layout)
 __global__ __launch_bounds__(256) void k_qk(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     // every row and bias table is laid out for RP ranks (padded ranks stay zero), so
@@ -379,10 +378,6 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
     const int R = p.R, N = p.N, t0 = 16 * tile;
     constexpr int KS = NT / 32;
     float* sb = reinterpret_cast<float*>(sx + 2 * 16 * TS);   // [8][2][RP][NT] rounded biases of a batch of heads
-    const int t = t0 + l16;
-    const bool tok = t < p.S;
-    const bool diag = q4 == (l16 >> 2) && tok;
-    const int v = l16 & 3;
     for (int h0 = 0; h0 < hpg; h0 += 8) {
         const int nh = min(8, hpg - h0);
         const unsigned rows = h0 == 0 ? 2u * 16u * RP * NT8 : 0u, bias = (unsigned)nh * 2u * RP * NT8;
@@ -422,117 +417,67 @@ __global__ __launch_bounds__(256) void k_qk(Params p) {
         __syncthreads();
         for (int hh = wave; hh < nh; hh += 4) {
             const int h = g * hpg + h0 + hh;
-            if constexpr (RP == 4) {
-                // Four tiles, one per 4 tokens: rows and columns are the 16 (token, rank)
-                // pairs of tokens 4 grp .. 4 grp + 3, row l16 = (token 4 grp + l16 / 4,
-                // rank l16 % 4). Lane (l16, q4) supplies that row of K0 (A operand) and of
-                // Q0 (B operand), columns 32 ks + 8 q4 .. + 7; it then holds
-                // dot(k0[token 4 grp + q4, rank i], q0[token 4 grp + l16 / 4, rank l16 % 4])
-                // for i = 0..3, so the lanes with q4 == l16 / 4 hold rank r = l16 % 4's row
-                // of their token's dots (each product is exact, so the operand order does
-                // not change the sums). A row past R or past the sequence only reaches
-                // dots that are not stored (staged rows and biases past R are zero).
-                // (the lane's offsets pass through an empty asm statement, so that the
-                // raw-row reads, which do not depend on the head, are redone per head
-                // instead of being held in registers across the head loop)
-                int rl = l16 & 3, tq = l16 >> 2;
-                asm volatile("" : "+v"(rl), "+v"(tq));
+            // Tiles of TPT = 16 / RP tokens: rows and columns are the 16 (token, rank)
+            // pairs of tokens u TPT .. u TPT + TPT - 1, row l16 = (token u TPT + l16 / RP,
+            // rank l16 % RP). Lane (l16, q4) supplies that row of K0 (A operand) and of Q0
+            // (B operand), columns 32 ks + 8 q4 .. + 7; it then holds
+            // dot(k0[row 4 q4 + i], q0[row l16]) for i = 0..3, and those whose two rows
+            // share a token are row r = l16 % RP of that token's dots, columns
+            // (4 q4 + i) % RP (each product is exact, so the operand order does not
+            // change the sums). A row past R or past the sequence only reaches dots that
+            // are not stored (staged rows and biases past R are zero). The lane's offsets
+            // pass through an empty asm statement, so that the raw-row reads, which do
+            // not depend on the head, are redone per head instead of being held in
+            // registers across the head loop.
+            constexpr int TPT = 16 / RP;
+            int rl = l16 % RP, tq = l16 / RP;
+            asm volatile("" : "+v"(rl), "+v"(tq));
 #pragma unroll
-                for (int grp = 0; grp < 4; ++grp) {
-                    const int tl = 4 * grp + tq;
-                    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const int col = 32 * ks + 8 * q4;
-                        u32x4 fr[2];
-#pragma unroll
-                        for (int which = 0; which < 2; ++which) {
-                            const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + (which * 16 + tl) * TS + rl * NT + col);
-                            const float* bp = sb + ((hh * 2 + which) * RP + rl) * NT + col;
-                            const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
-                            fr[which] = u32x4{pk2(lo16(raw[0]) + b0[0], hi16(raw[0]) + b0[1]),
-                                              pk2(lo16(raw[1]) + b0[2], hi16(raw[1]) + b0[3]),
-                                              pk2(lo16(raw[2]) + b1[0], hi16(raw[2]) + b1[1]),
-                                              pk2(lo16(raw[3]) + b1[2], hi16(raw[3]) + b1[3])};
-                        }
-                        a4 = mfma(fr[1], fr[0], a4);
-                    }
-                    const int tt = t0 + 4 * grp + q4;
-                    if (q4 == tq && rl < R && tt < p.S) {
-                        unsigned short* out = p.qk_dot + (((long)(b * p.H + h) * p.S + tt) * R + rl) * R;
-                        if (R == 4) {
-                            *reinterpret_cast<u32x2*>(out) = u32x2{pk2(a4[0], a4[1]), pk2(a4[2], a4[3])};
-                        } else {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                if (i < R) out[i] = bits16(rnd(a4[i]));
-                        }
-                    }
-                }
-                continue;
-            }
-            // fragments of token l16: rank r, columns 32 ks + 8 q4 .. + 7, biased and rounded
-            // (zero past N, where raw and bias are zero, and past the sequence)
-            u32x4 qf[RP][KS], kf[RP][KS];
-#pragma unroll
-            for (int r = 0; r < RP; ++r)
+            for (int u = 0; u < RP; ++u) {
+                const int tl = u * TPT + tq;
+                f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    qf[r][ks] = kf[r][ks] = u32x4{0u, 0u, 0u, 0u};
-                    if (r >= R || !tok) continue;
                     const int col = 32 * ks + 8 * q4;
+                    u32x4 fr[2];
 #pragma unroll
                     for (int which = 0; which < 2; ++which) {
-                        const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + (which * 16 + l16) * TS + r * NT + col);
-                        const float* bp = sb + ((hh * 2 + which) * RP + r) * NT + col;
+                        const u32x4 raw = *reinterpret_cast<const u32x4*>(sx + (which * 16 + tl) * TS + rl * NT + col);
+                        const float* bp = sb + ((hh * 2 + which) * RP + rl) * NT + col;
                         const f32x4 b0 = *reinterpret_cast<const f32x4*>(bp), b1 = *reinterpret_cast<const f32x4*>(bp + 4);
-                        // bf16(raw + bias): the packing conversion is the rounding
-                        const u32x4 o = {pk2(lo16(raw[0]) + b0[0], hi16(raw[0]) + b0[1]),
-                                         pk2(lo16(raw[1]) + b0[2], hi16(raw[1]) + b0[3]),
-                                         pk2(lo16(raw[2]) + b1[0], hi16(raw[2]) + b1[1]),
-                                         pk2(lo16(raw[3]) + b1[2], hi16(raw[3]) + b1[3])};
-                        if (which)
-                            kf[r][ks] = o;
-                        else
-                            qf[r][ks] = o;
+                        fr[which] = u32x4{pk2(lo16(raw[0]) + b0[0], hi16(raw[0]) + b0[1]),
+                                          pk2(lo16(raw[1]) + b0[2], hi16(raw[1]) + b0[3]),
+                                          pk2(lo16(raw[2]) + b1[0], hi16(raw[2]) + b1[1]),
+                                          pk2(lo16(raw[3]) + b1[2], hi16(raw[3]) + b1[3])};
                     }
+                    a4 = mfma(fr[1], fr[0], a4);
                 }
-            float dv[RP][RP];   // the lane's dots (its token's, on the diagonal lanes)
+                const int tt = t0 + tl;
+                if (rl >= R || tt >= p.S) continue;
+                unsigned short* out = p.qk_dot + (((long)(b * p.H + h) * p.S + tt) * R + rl) * R;
+                if constexpr (RP >= 4) {
+                    // four values, columns r20 .. r20 + 3
+                    if ((4 * q4) / RP != tq) continue;
+                    const int r20 = (4 * q4) % RP;
+                    if (R == RP) {
+                        *reinterpret_cast<u32x2*>(out + r20) = u32x2{pk2(a4[0], a4[1]), pk2(a4[2], a4[3])};
+                    } else {
 #pragma unroll
-            for (int r = 0; r < RP; ++r) {
-#pragma unroll
-                for (int r2 = 0; r2 < RP; ++r2) {
-                    dv[r][r2] = 0.f;
-                    if (r >= R || r2 >= R) continue;
-                    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) a4 = mfma(qf[r][ks], kf[r2][ks], a4);
+                        for (int i = 0; i < 4; ++i)
+                            if (r20 + i < R) out[r20 + i] = bits16(rnd(a4[i]));
+                    }
+                } else if constexpr (RP == 2) {
+                    // two values, columns 0 and 1
+                    if (q4 != (l16 >> 2)) continue;
+                    const bool hi = (l16 >> 1) & 1;
+                    *reinterpret_cast<unsigned*>(out) = pk2(hi ? a4[2] : a4[0], hi ? a4[3] : a4[1]);
+                } else {
+                    // one value
+                    if (q4 != (l16 >> 2)) continue;
+                    const int v = l16 & 3;
                     const float x01 = (v & 1) ? a4[1] : a4[0], x23 = (v & 1) ? a4[3] : a4[2];
-                    dv[r][r2] = (v & 2) ? x23 : x01;
+                    out[0] = bits16(rnd((v & 2) ? x23 : x01));
                 }
-            }
-            if (!diag) continue;
-            unsigned short* out = p.qk_dot + ((long)(b * p.H + h) * p.S + t) * R * R;
-            if (RP == 4 && R == 4) {
-#pragma unroll
-                for (int r = 0; r < RP; r += 2)
-                    *reinterpret_cast<u32x4*>(out + 4 * r) =
-                        u32x4{pk2(dv[r][0], dv[r][1]), pk2(dv[r][2], dv[r][3]), pk2(dv[r + 1][0], dv[r + 1][1]),
-                              pk2(dv[r + 1][2], dv[r + 1][3])};
-            } else if (RP == 8 && R == 8) {
-#pragma unroll
-                for (int r = 0; r < RP; ++r)
-                    *reinterpret_cast<u32x4*>(out + 8 * r) =
-                        u32x4{pk2(dv[r][0], dv[r][1]), pk2(dv[r][2], dv[r][3]), pk2(dv[r][4], dv[r][5]),
-                              pk2(dv[r][6], dv[r][7])};
-            } else if (RP == 2 && R == 2) {
-                *reinterpret_cast<u32x2*>(out) = u32x2{pk2(dv[0][0], dv[0][1]), pk2(dv[1][0], dv[1][1])};
-            } else {
-#pragma unroll
-                for (int r = 0; r < RP; ++r)
-#pragma unroll
-                    for (int r2 = 0; r2 < RP; ++r2)
-                        if (r < R && r2 < R) out[r * R + r2] = bits16(rnd(dv[r][r2]));
             }
         }
     }
