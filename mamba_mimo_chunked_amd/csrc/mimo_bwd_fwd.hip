@@ -594,6 +594,8 @@ const f32::F32Set* f32_set() {
         for (int d = 0; d < 2; ++d) {
             s.agg_ex[d] = parts[1]->agg_ex[d];
             s.main_ex[d] = parts[1]->main_ex[d];
+            s.agg_sx[d] = parts[1]->agg_sx[d];
+            s.main_sx[d] = parts[1]->main_sx[d];
         }
         return s;
     }();
@@ -684,8 +686,14 @@ mimo_status run32(const Prob32& q, Params& p, void* workspace, size_t workspace_
     // force the generic ones)
     const bool ex = !force_generic() && !q.uv && pl.MT == 64 && pl.NT == 64 && pl.PT == 64 && q.R == 4 &&
                     q.C == 16 && q.N == 64 && q.P == 64 && q.W == 16 && !pl.kg_main && !pl.kg_agg;
-    const kfn kmain = ex ? set->main_ex[q.f16] : (q.uv ? set->main_uv : set->main)[q.f16][pl.ti];
-    const kfn kagg = ex ? set->agg_ex[q.f16] : (q.uv ? set->agg_uv : set->agg)[q.f16][pl.ti];
+    const bool sx = !force_generic() && q.uv && pl.MT == 64 && pl.NT == 128 && pl.PT == 64 && q.R == 1 &&
+                    q.C == 64 && q.N == 128 && q.P == 64 && q.W == 64 && !pl.kg_main && !pl.kg_agg;
+    const kfn kmain = ex   ? set->main_ex[q.f16]
+                      : sx ? set->main_sx[q.f16]
+                           : (q.uv ? set->main_uv : set->main)[q.f16][pl.ti];
+    const kfn kagg = ex   ? set->agg_ex[q.f16]
+                     : sx ? set->agg_sx[q.f16]
+                          : (q.uv ? set->agg_uv : set->agg)[q.f16][pl.ti];
     if (kmain == nullptr || kagg == nullptr) return fail(MIMO_ERR_UNSUPPORTED, "no fp32 kernel for this tile shape");
     p.B = (int)q.B; p.S = (int)q.S; p.H = (int)q.H; p.G = (int)q.G; p.R = (int)q.R; p.N = (int)q.N; p.P = (int)q.P;
     p.C = q.C; p.W = q.W; p.nc = pl.nc; p.L = pl.L; p.nseg = pl.nseg; p.F = pl.F; p.nsub = pl.nsub;

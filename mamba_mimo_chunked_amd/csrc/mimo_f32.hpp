@@ -133,21 +133,31 @@ __device__ __forceinline__ float cvt16(unsigned short x) {
     return __uint_as_float(static_cast<unsigned>(x) << 16);
 }
 
-// EX: the shape-exact instance (R = 4, C = 16, N = P = 64, rotated width 16, with
-// MT = NT = PT = 64): the sizes become constants, so index arithmetic folds.
-// (The exact aggregate is held to four waves per SIMD, 128 VGPRs: the grid of the
-// aggregate is sized for four workgroups per CU, which its LDS allows.)
-template <int MT, int NT, int PT, bool MAIN, bool F16, bool UV = false, bool KG = false, bool EX = false>
-__global__ __launch_bounds__(256, ((EX && !MAIN) ? 4 : wg_per_cu32<MT, NT, PT, MAIN, UV, KG>())) void k_chunk32(
+// EX: a shape-exact instance, whose sizes are constants, so that index arithmetic
+// folds. EX = 1: the MIMO shape R = 4, C = 16, N = P = 64, rotated width 16 (MT = NT =
+// PT = 64); its aggregate is held to four waves per SIMD, 128 VGPRs, since the
+// aggregate's grid is sized for four workgroups per CU, which its LDS allows.
+// EX = 2: the SISO shape R = 1, C = 64, N = 128 (all of it rotated: width 64),
+// P = 64, unit projections (MT = 64, NT = 128, PT = 64).
+template <int MT, int NT, int PT, bool MAIN, bool F16, bool UV = false, bool KG = false, int EX = 0>
+__global__ __launch_bounds__(256, ((EX == 1 && !MAIN) ? 4 : wg_per_cu32<MT, NT, PT, MAIN, UV, KG>())) void k_chunk32(
     Params pin) {
-    static_assert(!EX || (MT == 64 && NT == 64 && PT == 64 && !UV && !KG), "the exact shape's tile");
+    static_assert(EX == 0 || (EX == 1 && MT == 64 && NT == 64 && PT == 64 && !UV && !KG) ||
+                      (EX == 2 && MT == 64 && NT == 128 && PT == 64 && UV && !KG),
+                  "the exact shape's tile");
     Params p = pin;
-    if constexpr (EX) {
+    if constexpr (EX == 1) {
         p.R = 4;
         p.C = 16;
         p.N = 64;
         p.P = 64;
         p.W = 16;
+    } else if constexpr (EX == 2) {
+        p.R = 1;
+        p.C = 64;
+        p.N = 128;
+        p.P = 64;
+        p.W = 64;
     }
     using T = Tile32<MT, NT, PT>;
     constexpr int NW = T::NW, NTHR = T::NTHR, LQ = T::LQ, LA = T::LA, LP = T::LP, CX = T::CX;
@@ -746,11 +756,13 @@ __global__ __launch_bounds__(256, ((EX && !MAIN) ? 4 : wg_per_cu32<MT, NT, PT, M
 // *_uv tables hold the unit-projection instances (the SISO forward: MT of 32 and 64).
 struct F32Set {
     kfn agg[2][27], main[2][27], agg_uv[2][27], main_uv[2][27];
-    kfn agg_ex[2], main_ex[2];   // the shape-exact instances (by input dtype)
+    kfn agg_ex[2], main_ex[2];   // the shape-exact MIMO instances (by input dtype)
+    kfn agg_sx[2], main_sx[2];   // the shape-exact SISO instances (by input dtype)
 };
 struct F32Part {
     kfn agg[2][9], main[2][9], agg_uv[2][9], main_uv[2][9];
     kfn agg_ex[2], main_ex[2];   // MT = 64 only
+    kfn agg_sx[2], main_sx[2];   // MT = 64 only
 };
 const F32Part* f32_part_mt32();
 const F32Part* f32_part_mt64();
@@ -781,22 +793,26 @@ constexpr kfn pick32() {
         {MIMO_F32_NP(MT, true, false, UV), MIMO_F32_NP(MT, true, true, UV)}
 #define MIMO_F32_PART(MT)                                                                               \
     const F32Part* f32_part_mt##MT() {                                                                  \
-        static const F32Part part = {MIMO_F32_TABLES(MT, false), {}, {}};                                \
+        static const F32Part part = {MIMO_F32_TABLES(MT, false), {}, {}, {}, {}};                        \
         return &part;                                                                                   \
     }
 #define MIMO_F32_PART_UV(MT)                                                                            \
     const F32Part* f32_part_mt##MT() {                                                                  \
-        static const F32Part part = {MIMO_F32_TABLES(MT, false), MIMO_F32_TABLES(MT, true), {}, {}};     \
+        static const F32Part part = {MIMO_F32_TABLES(MT, false), MIMO_F32_TABLES(MT, true), {}, {}, {}, {}}; \
         return &part;                                                                                   \
     }
 // MT = 64 with the shape-exact instances
 #define MIMO_F32_PART_UV_EX(MT)                                                                         \
     const F32Part* f32_part_mt##MT() {                                                                  \
         static const F32Part part = {MIMO_F32_TABLES(MT, false), MIMO_F32_TABLES(MT, true),              \
-                                     {k_chunk32<64, 64, 64, false, false, false, false, true>,          \
-                                      k_chunk32<64, 64, 64, false, true, false, false, true>},          \
-                                     {k_chunk32<64, 64, 64, true, false, false, false, true>,           \
-                                      k_chunk32<64, 64, 64, true, true, false, false, true>}};          \
+                                     {k_chunk32<64, 64, 64, false, false, false, false, 1>,             \
+                                      k_chunk32<64, 64, 64, false, true, false, false, 1>},             \
+                                     {k_chunk32<64, 64, 64, true, false, false, false, 1>,              \
+                                      k_chunk32<64, 64, 64, true, true, false, false, 1>},              \
+                                     {k_chunk32<64, 128, 64, false, false, true, false, 2>,             \
+                                      k_chunk32<64, 128, 64, false, true, true, false, 2>},             \
+                                     {k_chunk32<64, 128, 64, true, false, true, false, 2>,              \
+                                      k_chunk32<64, 128, 64, true, true, true, false, 2>}};             \
         return &part;                                                                                   \
     }
 

@@ -249,6 +249,24 @@ def test_siso_perf_shapes_all_heads(name):
     _check_siso(SISO_CONFIGS[name])
 
 
+@pytest.mark.parametrize("case", [SisoCase(1, 300, 2, 4, 128, 64, 64, name="sx_bf16_tail"),
+                                  SisoCase(2, 257, 3, 3, 128, 64, 64, dtype="fp16", has_z=False,
+                                           name="sx_fp16_no_z")], ids=lambda c: c.name)
+def test_siso_shape_exact_and_generic_agree(case, monkeypatch):
+    """K=128, V=64, chunk 64 with every pair rotated runs the shape-exact SISO
+    instances (sizes as constants); the generic ones (forced through
+    MIMO_FORCE_GENERIC) must give the same bits, and both meet the oracle gates."""
+    log(f"[siso exact-vs-generic] {case.name}")
+    assert case.width == 64
+    d = _siso_dev(make_siso_inputs(case))
+    ex = run_siso(d)
+    monkeypatch.setenv("MIMO_FORCE_GENERIC", "1")
+    gen = run_siso(d)
+    monkeypatch.delenv("MIMO_FORCE_GENERIC")
+    assert torch.equal(ex.view(torch.int16), gen.view(torch.int16)), "shape-exact and generic SISO instances differ"
+    _check_siso(case)
+
+
 def test_siso_determinism_and_every_element_written():
     case = SisoCase(1, 300, 2, 2, 64, 64, 64, name="det")
     d = _siso_dev(make_siso_inputs(case))
