@@ -34,6 +34,13 @@ EXTRA = [
     Case(1, 130, 2, 1, 16, 16, 8, 8, name="r8_c8_small"),
     Case(1, 95, 1, 1, 32, 48, 3, 6, rd=2, name="r3_c6_rd2_p48"),
     Case(1, 64, 1, 1, 64, 64, 1, 64, name="r1_c64"),
+    # calls without y (states walk + qk_dot kernel) across rank counts and tile families
+    Case(1, 203, 2, 1, 64, 64, 1, 16, reduce_o=False, has_z=False, name="noy_r1"),
+    Case(2, 150, 4, 2, 32, 64, 2, 32, reduce_o=False, has_z=False, has_d=False, name="noy_r2_c32"),
+    Case(1, 333, 2, 1, 64, 32, 3, 16, reduce_o=False, has_z=False, name="noy_r3_p32"),
+    Case(1, 300, 3, 1, 128, 64, 2, 64, reduce_o=False, has_z=False, name="noy_r2_c64_n128"),
+    Case(1, 230, 2, 2, 128, 128, 8, 16, reduce_o=False, has_z=False, name="noy_r8_n128_p128"),
+    Case(1, 120, 2, 1, 32, 32, 6, 16, reduce_o=False, has_z=False, name="noy_r6_pad8"),
     # 255 sub-segments: the span scan with all 16 spans, the last one short
     Case(1, 8192, 2, 1, 16, 16, 2, 16, name="scan_16_spans"),
     # 511 sub-segments: the sequential scan
