@@ -697,7 +697,8 @@ mimo_status run32(const Prob32& q, Params& p, void* workspace, size_t workspace_
     if (kmain == nullptr || kagg == nullptr) return fail(MIMO_ERR_UNSUPPORTED, "no fp32 kernel for this tile shape");
     p.B = (int)q.B; p.S = (int)q.S; p.H = (int)q.H; p.G = (int)q.G; p.R = (int)q.R; p.N = (int)q.N; p.P = (int)q.P;
     p.C = q.C; p.W = q.W; p.nc = pl.nc; p.L = pl.L; p.nseg = pl.nseg; p.F = pl.F; p.nsub = pl.nsub;
-    p.reduce_o = q.reduce_o; p.has_z = q.has_z; p.has_d = q.has_d; p.fwd = q.fwd; p.need_y = 1;
+    p.reduce_o = q.reduce_o; p.has_z = q.has_z; p.has_d = q.has_d; p.fwd = q.fwd;
+    p.need_y = q.fwd || q.reduce_o || q.has_z;   // else the chunk pass emits states and qk_dot only
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     p.agg = pl.nseg > 1 ? reinterpret_cast<float*>(ws + pl.off_agg) : nullptr;
     p.decay = pl.nseg > 1 ? reinterpret_cast<float*>(ws + pl.off_decay) : nullptr;

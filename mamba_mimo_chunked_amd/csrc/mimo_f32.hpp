@@ -469,7 +469,7 @@ __global__ __launch_bounds__(256, ((EX == 1 && !MAIN) ? 4 : wg_per_cu32<MT, NT, 
                 sQK[e] = s;
                 if (!p.fwd) p.qk_dot[((long)bh * p.S + c0 + t) * RR + r * R + r2] = st16<F16>(s);
             }
-            for (int e = tid; e < (UV ? 0 : cl * cl); e += NTHR) {
+            for (int e = tid; e < (UV || !p.need_y ? 0 : cl * cl); e += NTHR) {
                 const int t = e / cl, s2 = e % cl;
                 if (s2 < t) {
                     float sg;
@@ -504,7 +504,7 @@ __global__ __launch_bounds__(256, ((EX == 1 && !MAIN) ? 4 : wg_per_cu32<MT, NT, 
                 const float ka = kr[n], ke = kr[M + n];
                 kr[n] = (cn * ka - sn * ke) * f;
                 kr[M + n] = (sn * ka + cn * ke) * f;
-                if (MAIN) {
+                if (MAIN && p.need_y) {   // rotated q serves y only (qk_dot took q0 above)
                     float* qr = sQ + (r * Cp + t) * LQ;
                     const float qa = qr[n], qe = qr[M + n];
                     qr[n] = cn * qa - sn * qe;
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(256, ((EX == 1 && !MAIN) ? 4 : wg_per_cu32<MT, NT, 
         sync();
 
         f32x4 acc[PW][MTT];
-        if constexpr (MAIN) {
+        if constexpr (MAIN) if (p.need_y) {   // y: inter, causal block, intra
             // ---- inter = Q^ S, rows scaled by exp(da_cs[t])
 #pragma unroll
             for (int j = 0; j < PW; ++j) {
@@ -625,7 +625,7 @@ __global__ __launch_bounds__(256, ((EX == 1 && !MAIN) ? 4 : wg_per_cu32<MT, NT, 
             dprod *= dl;
         }
 
-        if constexpr (MAIN) {
+        if constexpr (MAIN) if (p.need_y) {
             // ---- y's partial sums (inter + intra) through LDS, so that the epilogue
             // can address them by run-time rank and token
             sync();   // every wave is done reading the causal block

@@ -66,6 +66,9 @@ BWD32_CASES = [
     Case(1, 500, 2, 1, 128, 64, 4, 16, name="f32_n128_r4"),
     Case(1, 400, 2, 1, 64, 128, 2, 16, name="f32_p128_r2"),
     Case(1, 300, 1, 1, 64, 64, 8, 16, name="f32_r8_c16_mt128"),
+    # calls without y (states and qk_dot only) on other tiles
+    Case(1, 200, 2, 2, 32, 64, 2, 32, reduce_o=False, has_z=False, name="f32_noy_r2_c32"),
+    Case(1, 150, 2, 1, 64, 32, 3, 16, reduce_o=False, has_z=False, has_d=False, name="f32_noy_r3_p32"),
 ]
 
 
@@ -147,6 +150,7 @@ KG_CASES = [
     Case(1, 300, 2, 1, 128, 64, 2, 64, name="kg_n128_c64"),
     Case(2, 150, 4, 2, 64, 128, 4, 32, reduce_o=False, has_z=True, has_d=True, name="kg_p128_nonreduced_z"),
     Case(1, 77, 2, 1, 128, 32, 3, 24, reduce_o=True, has_z=False, has_d=False, name="kg_n128_p32_r3_c24"),
+    Case(1, 150, 2, 2, 128, 128, 8, 16, reduce_o=False, has_z=False, name="kg_noy_n128_p128_r8"),
 ]
 
 
