@@ -1434,26 +1434,26 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             }
         } else {
 #pragma unroll
-        for (int w = 0; w < (T::QKT + NW - 1) / NW; ++w) {
-            const int u = wave + w * NW;
-            if (T::QKT_FULL || u < T::QKT) {
-                const int rj = u % RP, ri = (u / RP) % RP, tt = u / (RP * RP);
-                float val = 0.f;
-                if (ri < R && rj < R) {
-                    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+            for (int w = 0; w < (T::QKT + NW - 1) / NW; ++w) {
+                const int u = wave + w * NW;
+                if (T::QKT_FULL || u < T::QKT) {
+                    const int rj = u % RP, ri = (u / RP) % RP, tt = u / (RP * RP);
+                    float val = 0.f;
+                    if (ri < R && rj < R) {
+                        f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < NT / 32; ++ks) {
-                        const u32x4 a = lds_ld<u32x4>(sQ + (16 * (ri * CT + tt) + l16) * LDQ + 32 * ks + 8 * q4);
-                        const u32x4 bb = lds_ld<u32x4>(sK + (16 * (rj * CT + tt) + l16) * LDQ + 32 * ks + 8 * q4);
-                        a4 = mfma(a, bb, a4);
+                        for (int ks = 0; ks < NT / 32; ++ks) {
+                            const u32x4 a = lds_ld<u32x4>(sQ + (16 * (ri * CT + tt) + l16) * LDQ + 32 * ks + 8 * q4);
+                            const u32x4 bb = lds_ld<u32x4>(sK + (16 * (rj * CT + tt) + l16) * LDQ + 32 * ks + 8 * q4);
+                            a4 = mfma(a, bb, a4);
+                        }
+                        const int v = l16 & 3;
+                        const float x01 = (v & 1) ? a4[1] : a4[0], x23 = (v & 1) ? a4[3] : a4[2];
+                        val = rnd((v & 2) ? x23 : x01);
                     }
-                    const int v = l16 & 3;
-                    const float x01 = (v & 1) ? a4[1] : a4[0], x23 = (v & 1) ? a4[3] : a4[2];
-                    val = rnd((v & 2) ? x23 : x01);
+                    if (q4 == (l16 >> 2)) sQK[(16 * tt + l16) * QKS + ri * RP + rj] = val;
                 }
-                if (q4 == (l16 >> 2)) sQK[(16 * tt + l16) * QKS + ri * RP + rj] = val;
             }
-        }
         }
         bar();
 
