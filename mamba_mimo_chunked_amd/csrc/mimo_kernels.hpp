@@ -1257,6 +1257,12 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
                                                        min(p.C, p.S - c_begin * p.C), qkst, stg + (c_begin & 1) * SG::SMB);
 
     for (int c = c_begin; c < c_end; ++c) {
+        // Wave priority (four-wave tiles, two workgroups per CU): the chunk's chain of
+        // barrier-separated phases issues at a raised priority, the epilogue
+        // (independent VALU work, no barrier until the next chunk) at the normal one,
+        // so that on a SIMD shared by the two workgroups the other workgroup's
+        // epilogue fills the chain's gaps instead of delaying it
+        if constexpr (NW == 4) __builtin_amdgcn_s_setprio(1);
         const int c0 = c * p.C;
         const int cl = min(p.C, p.S - c0);
         const unsigned char* smb = stg + (c & 1) * SG::SMB;
@@ -1632,6 +1638,7 @@ __global__ __launch_bounds__((Tile<RP, CT, NT, PT>::NTHR), 2) void k_main(Params
             emit_state();
         }
 
+        if constexpr (NW == 4) __builtin_amdgcn_s_setprio(0);
         // ---- y = bf16(inter + intra + diag + d*Psi) and the gating gradients. Ranks
         // r >= R, tokens past the chunk's end and columns p >= P run on zero data
         // (zero Psi, qk pairs, projections, gate inputs and scales) and come out
