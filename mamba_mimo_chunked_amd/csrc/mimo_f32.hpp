@@ -316,7 +316,13 @@ __global__ __launch_bounds__(256, ((EX == 1 && !MAIN) ? 4 : wg_per_cu32<MT, NT, 
     };
     if (AHEAD && c_begin < c_end) fetch(c_begin);
 
+    // Wave priority (chunk passes with two workgroups per CU): a chunk's chain of
+    // barrier-separated phases issues at a raised priority, the y epilogue (no barrier
+    // until the chunk's end) at the normal one, so that the other workgroup's epilogue
+    // fills the chain's gaps instead of delaying it
+    constexpr bool PRIO = MAIN && wg_per_cu32<MT, NT, PT, MAIN, UV, KG>() == 2;
     for (int c = c_begin; c < c_end; ++c) {
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
         const int c0 = c * C;
         const int cl = min(C, p.S - c0);
         // The chunk pass runs two workgroups per CU (at most 256 VGPRs): its thread index
@@ -629,6 +635,7 @@ __global__ __launch_bounds__(256, ((EX == 1 && !MAIN) ? 4 : wg_per_cu32<MT, NT, 
             // ---- y's partial sums (inter + intra) through LDS, so that the epilogue
             // can address them by run-time rank and token
             sync();   // every wave is done reading the causal block
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);   // the epilogue at normal priority
 #pragma unroll
             for (int j = 0; j < PW; ++j) {
                 const int pt = wave + NW * j;
