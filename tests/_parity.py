@@ -56,10 +56,15 @@ def check_elements(name, gv, r, *, bf16: bool, label=""):
     """Element-wise bars next to the whole-tensor one, so that a few wrong
     elements in a large tensor cannot hide under the RMS:
     * bf16 outputs: at least 99.9 % of the elements within one bf16 ulp of the
-      oracle, and every element within 2^-5 |ref| + 2^-3 RMS(ref): a rank-ordered
-      bf16 chain (dz over up to 8 ranks) can cancel from partial sums many times
-      its result, where one tie broken the other way is one ulp of the partial
-      sum; a wrong element is off by the order of RMS(ref);
+      oracle (at most 32 elements off by more in tensors too small for 0.1 % to
+      hold a cascade: the hardware sine and cosine differ from the oracle's
+      correctly rounded ones by up to ~3e-7, so now and then one rotated q or k
+      value rounds to the other bf16 neighbour, and that reaches every dz and
+      state element of its token and the chunks after it through the bf16
+      chains), and every element within 2^-5 |ref| + 2^-3 RMS(ref): a
+      rank-ordered bf16 chain (dz over up to 8 ranks) can cancel from partial
+      sums many times its result, where one tie broken the other way is one ulp
+      of the partial sum; a wrong element is off by the order of RMS(ref);
     * fp32 outputs (sums over tokens of products with bf16 y, where one y may sit
       one ulp apart because a rounding tie broke the other way; with few tokens one
       such term moves an element by up to ~1 %): every element within
@@ -70,8 +75,10 @@ def check_elements(name, gv, r, *, bf16: bool, label=""):
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     dev = np.abs(a - r)
     if bf16:
-        within = float(np.mean(np.abs(_ulp_key(a) - _ulp_key(r)) <= 1)) if r.size else 1.0
-        assert within >= 0.999, f"{label}{name}: only {within:.5f} of the elements within 1 bf16 ulp"
+        far = int(np.sum(np.abs(_ulp_key(a) - _ulp_key(r)) > 1)) if r.size else 0
+        within = 1.0 - far / r.size if r.size else 1.0
+        assert within >= 0.999 or far <= 32, \
+            f"{label}{name}: only {within:.5f} of the elements within 1 bf16 ulp ({far} beyond)"
         bound = 2.0 ** -5 * np.abs(r) + 2.0 ** -3 * rms
     else:
         within = 1.0

@@ -91,6 +91,42 @@ def test_extra_shapes(case):
     _check(case)
 
 
+def _random_case(k):
+    """A seeded random shape within the supported range: ranks 1-8, chunk 8-64 with
+    C*R <= 128 (rank count padded to a power of two, chunk to 16/32/64 tokens),
+    N and P multiples of 16 up to 128 with N divisible by the rotary divisor, GQA
+    groups, a ragged tail, and random branch flags."""
+    rng = np.random.default_rng(1000 + k)
+    while True:
+        R = int(rng.integers(1, 9))
+        C = int(rng.choice([8, 16, 24, 32, 48, 64]))
+        RP = 1 << (R - 1).bit_length()
+        CP = 16 if C <= 16 else (32 if C <= 32 else 64)
+        if C * R <= 128 and RP * CP <= 128:
+            break
+    N = int(rng.choice([16, 32, 48, 64, 96, 128]))
+    P = int(rng.choice([16, 32, 48, 64, 96, 128]))
+    rd = int(rng.choice([2, 4])) if N % 4 == 0 else 2
+    G = int(rng.choice([1, 2]))
+    H = G * int(rng.choice([1, 2, 3]))
+    S = int(rng.integers(1, 6 * C + 1))
+    return Case(1, S, H, G, N, P, R, C, rd=rd, reduce_o=bool(rng.integers(2)), has_z=bool(rng.integers(2)),
+                has_d=bool(rng.integers(2)), seed=k, name=f"random_{k}")
+
+
+@pytest.mark.parametrize("k", range(16))
+def test_random_shapes(k):
+    """Sixteen seeded random shapes and branch combinations against the oracle (the
+    outputs with y and without, every tile family the draw reaches). A shape whose
+    tile family's LDS layout exceeds a CU must be refused as such, not run."""
+    case = _random_case(k)
+    try:
+        _check(case)
+    except NotImplementedError as e:
+        assert "bytes of LDS" in str(e), e
+        pytest.skip(f"{case.name}: {e}")
+
+
 @pytest.mark.parametrize("seed", [0, 1, 42])
 def test_tiny_and_tail_seeds(seed):
     _check(CONFIGS["tiny"].with_(seed=seed, name=f"tiny_seed{seed}"))
