@@ -128,6 +128,22 @@ def test_bwd_fwd_fp32_gqa_tail_nonreduced_sampled():
         compare(sl, ref, tol=TOL32, label=f"gqa b={b} h={h}: ")
 
 
+@pytest.mark.parametrize("k", range(8))
+def test_bwd_fwd_fp32_random_shapes(k):
+    """Seeded random shapes (the same draw as the bf16 path's random parity cases) for
+    the fp32-intermediate variant against the oracle in fp32 mode; shapes beyond the
+    variant's LDS and scratch tiles must be refused as such."""
+    from .test_gpu_parity import _random_case
+    case = _random_case(k)
+    log(f"[fp32 random] {case}")
+    inp = make_inputs(case)
+    try:
+        got = run_bwd32(to_device(inp))
+    except NotImplementedError as e:
+        pytest.skip(f"{case.name}: {e}")
+    compare(got, o1.run_inputs(inp, fp32=True), tol=TOL32, label=f"{case.name} fp32: ")
+
+
 def test_fp32_is_closer_to_exact_than_bf16_contract():
     """The fp32 variant's dmimo outputs sit far closer to exact arithmetic than the
     bf16-contract operator's (both on the GPU, the same inputs)."""

@@ -83,6 +83,19 @@ def test_fwd_shapes(case):
     _check(case)
 
 
+@pytest.mark.parametrize("k", range(8))
+def test_fwd_random_shapes(k):
+    """Seeded random shapes (the same draw as the backward's random parity cases) for
+    the layer output against the oracle; an LDS refusal must say so."""
+    from .test_gpu_parity import _random_case
+    case = _random_case(k)
+    try:
+        _check(case)
+    except NotImplementedError as e:
+        assert "bytes of LDS" in str(e), e
+        pytest.skip(f"{case.name}: {e}")
+
+
 def test_fwd_tiny_config():
     _check(CONFIGS["tiny"].with_(name="fwd_tiny"))
 
