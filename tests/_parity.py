@@ -56,12 +56,15 @@ def check_elements(name, gv, r, *, bf16: bool, label=""):
     """Element-wise bars next to the whole-tensor one, so that a few wrong
     elements in a large tensor cannot hide under the RMS:
     * bf16 outputs: at least 99.9 % of the elements within one bf16 ulp of the
-      oracle (at most 32 elements off by more in tensors too small for 0.1 % to
-      hold a cascade: the hardware sine and cosine differ from the oracle's
-      correctly rounded ones by up to ~3e-7, so now and then one rotated q or k
-      value rounds to the other bf16 neighbour, and that reaches every dz and
-      state element of its token and the chunks after it through the bf16
-      chains), and every element within 2^-5 |ref| + 2^-3 RMS(ref): a
+      oracle, or, in tensors too small for 0.1 % to hold a cascade, at most 32
+      elements off by more or all of them inside at most 4 rows (a row: the
+      values along the last axis, e.g. one token's dz of one head). The hardware
+      sine and cosine differ from the oracle's correctly rounded ones by up to
+      ~3e-7, so now and then one rotated q or k value rounds to the other bf16
+      neighbour; that reaches the dz row of its token, the rows of the later
+      tokens of its chunk whose causal-block entry it changes, and the states
+      after the chunk, through the bf16 chains. A wrong index or term is off in
+      most rows instead. And every element within 2^-5 |ref| + 2^-3 RMS(ref): a
       rank-ordered bf16 chain (dz over up to 8 ranks) can cancel from partial
       sums many times its result, where one tie broken the other way is one ulp
       of the partial sum; a wrong element is off by the order of RMS(ref);
@@ -75,10 +78,12 @@ def check_elements(name, gv, r, *, bf16: bool, label=""):
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     dev = np.abs(a - r)
     if bf16:
-        far = int(np.sum(np.abs(_ulp_key(a) - _ulp_key(r)) > 1)) if r.size else 0
+        far_mask = np.abs(_ulp_key(a) - _ulp_key(r)) > 1
+        far = int(far_mask.sum()) if r.size else 0
+        rows = int(np.any(far_mask.reshape(-1, r.shape[-1]), axis=1).sum()) if r.size else 0
         within = 1.0 - far / r.size if r.size else 1.0
-        assert within >= 0.999 or far <= 32, \
-            f"{label}{name}: only {within:.5f} of the elements within 1 bf16 ulp ({far} beyond)"
+        assert within >= 0.999 or far <= 32 or rows <= 4, \
+            f"{label}{name}: only {within:.5f} of the elements within 1 bf16 ulp ({far} beyond, in {rows} rows)"
         bound = 2.0 ** -5 * np.abs(r) + 2.0 ** -3 * rms
     else:
         within = 1.0

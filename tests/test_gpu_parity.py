@@ -114,9 +114,9 @@ def _random_case(k):
                 has_d=bool(rng.integers(2)), seed=k, name=f"random_{k}")
 
 
-@pytest.mark.parametrize("k", range(16))
+@pytest.mark.parametrize("k", range(96))
 def test_random_shapes(k):
-    """Sixteen seeded random shapes and branch combinations against the oracle (the
+    """Ninety-six seeded random shapes and branch combinations against the oracle (the
     outputs with y and without, every tile family the draw reaches). A shape whose
     tile family's LDS layout exceeds a CU must be refused as such, not run."""
     case = _random_case(k)
