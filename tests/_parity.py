@@ -52,7 +52,7 @@ def _ulp_key(x):
     return np.where(u & 0x8000, -mag, mag)
 
 
-def check_elements(name, gv, r, *, bf16: bool, label=""):
+def check_elements(name, gv, r, *, bf16: bool, label="", ulp_frac=0.999):
     """Element-wise bars next to the whole-tensor one, so that a few wrong
     elements in a large tensor cannot hide under the RMS:
     * bf16 outputs: at least 99.9 % of the elements within one bf16 ulp of the
@@ -72,6 +72,8 @@ def check_elements(name, gv, r, *, bf16: bool, label=""):
       one ulp apart because a rounding tie broke the other way; with few tokens one
       such term moves an element by up to ~1 %): every element within
       2^-6 (|ref| + RMS(ref)); a wrong element is off by the order of itself.
+    ``ulp_frac`` replaces the 99.9 % (random shapes with drawn angles, whose long
+    chains let one such flip reach more than 0.1 % of a small tensor).
     Returns the fraction of bf16 elements within one ulp (1.0 for fp32)."""
     a = np.asarray(gv, np.float64)
     r = np.asarray(r, np.float64)
@@ -82,7 +84,7 @@ def check_elements(name, gv, r, *, bf16: bool, label=""):
         far = int(far_mask.sum()) if r.size else 0
         rows = int(np.any(far_mask.reshape(-1, r.shape[-1]), axis=1).sum()) if r.size else 0
         within = 1.0 - far / r.size if r.size else 1.0
-        assert within >= 0.999 or far <= 32 or rows <= 4, \
+        assert within >= ulp_frac or far <= 32 or rows <= 4, \
             f"{label}{name}: only {within:.5f} of the elements within 1 bf16 ulp ({far} beyond, in {rows} rows)"
         bound = 2.0 ** -5 * np.abs(r) + 2.0 ** -3 * rms
     else:
@@ -102,7 +104,7 @@ def per_head(name, x):
     return np.swapaxes(x, 1, 2) if name == "dz" else x   # dz is [B,S,H,P]
 
 
-def compare(gpu_out, ref_out, *, tol=TOL, label=""):
+def compare(gpu_out, ref_out, *, tol=TOL, label="", ulp_frac=0.999):
     """Assert per-output parity: the stated bar (relative RMS < tol over the whole
     tensor), a per-(batch, head) bar, and the element-wise bars of check_elements.
     Returns {name: rel_rms}."""
@@ -128,7 +130,7 @@ def compare(gpu_out, ref_out, *, tol=TOL, label=""):
             for h in range(rh.shape[1]):
                 eh = rel_rms(gh[b, h], rh[b, h])
                 assert eh < 4 * tol, f"{label}{name}: rel RMS {eh:.3e} >= {4 * tol} at batch {b}, head {h}"
-        check_elements(name, gv, r, bf16=(dt == torch.bfloat16), label=label)
+        check_elements(name, gv, r, bf16=(dt == torch.bfloat16), label=label, ulp_frac=ulp_frac)
     return errs
 
 

@@ -57,7 +57,7 @@ def run_fwd(dinp: dict, **kw):
     return o
 
 
-def _cmp(got, ref, label):
+def _cmp(got, ref, label, ulp_frac=0.999):
     assert got.dtype == torch.bfloat16, f"{label}: dtype {got.dtype}"
     g = got.float().cpu().numpy()
     assert g.shape == ref.shape, f"{label}: shape {g.shape} vs {ref.shape}"
@@ -65,17 +65,19 @@ def _cmp(got, ref, label):
     e = rel_rms(g, ref)
     log(f"    {label}: o={e:.2e}")
     assert e < TOL, f"{label}: rel RMS {e:.3e} >= {TOL}"
-    check_elements("o", g, ref, bf16=True, label=f"{label}: ")
+    check_elements("o", g, ref, bf16=True, label=f"{label}: ", ulp_frac=ulp_frac)
     return e
 
 
-def _check(case):
+def _check(case, *, zero_angles=False, ulp_frac=0.999):
     log(f"[fwd] {case.name} B={case.B} S={case.S} H={case.H} G={case.G} N={case.N} P={case.P} "
-        f"R={case.R} C={case.C} reduce_o={case.reduce_o} z={case.has_z}")
+        f"R={case.R} C={case.C} reduce_o={case.reduce_o} z={case.has_z}" + (" (zero angles)" if zero_angles else ""))
     inp = make_inputs(case)
+    if zero_angles:
+        inp["angles"] = torch.zeros_like(inp["angles"])
     ref = o1.run_fwd_inputs(inp)
     got = run_fwd(to_device(inp))
-    return _cmp(got, ref, case.name)
+    return _cmp(got, ref, case.name, ulp_frac)
 
 
 @pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: c.name)
@@ -83,14 +85,17 @@ def test_fwd_shapes(case):
     _check(case)
 
 
-@pytest.mark.parametrize("k", range(8))
+@pytest.mark.parametrize("k", range(96))
 def test_fwd_random_shapes(k):
     """Seeded random shapes (the same draw as the backward's random parity cases) for
-    the layer output against the oracle; an LDS refusal must say so."""
+    the layer output against the oracle, with zero angles at the full bars and with
+    the drawn angles at 99.5 % of elements within one ulp (as the backward's random
+    cases); an LDS refusal must say so."""
     from .test_gpu_parity import _random_case
     case = _random_case(k)
     try:
-        _check(case)
+        _check(case, zero_angles=True)
+        _check(case, ulp_frac=0.995)
     except NotImplementedError as e:
         assert "bytes of LDS" in str(e), e
         pytest.skip(f"{case.name}: {e}")
