@@ -133,6 +133,20 @@ def test_bwd2_fp32_outputs(case):
     log("    " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
 
 
+@pytest.mark.parametrize("k", range(96))
+def test_bwd2_random_shapes(k):
+    """Seeded random shapes (the same draw as the first stage's random parity cases:
+    ranks 1-8, chunks 8-64, N and P 16-128, GQA, ragged tails, random branch flags)
+    against the stage-2 oracle, fp32 outputs."""
+    from .test_gpu_parity import _random_case
+    case = _random_case(k)
+    log(f"[bwd2 random] {case}")
+    inp = make_inputs(case)
+    states, qk = _caches(inp)
+    got = _run_gpu(inp, states, qk, torch.float32)
+    _compare(got, _oracle(inp, states, qk), f"{case.name}: ")
+
+
 @pytest.mark.parametrize("case", [Case(1, 300, 3, 1, 64, 64, 4, 16, name="b2_bf16_out")], ids=lambda c: c.name)
 def test_bwd2_bf16_outputs(case):
     inp = make_inputs(case)
