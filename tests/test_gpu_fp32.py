@@ -259,6 +259,33 @@ SISO_CASES = [
 ]
 
 
+def _random_siso(k):
+    """A seeded random SISO shape: K and V multiples of 16 up to 128, chunks of 32 or
+    64 tokens, an even rotated width up to K/2 (zero included), query heads dividing
+    the value heads, bf16 or fp16, a ragged tail and random z/D flags."""
+    rng = np.random.default_rng(5000 + k)
+    K = int(rng.choice([16, 32, 48, 64, 96, 128]))
+    V = int(rng.choice([16, 32, 48, 64, 96, 128]))
+    C = int(rng.choice([32, 64]))
+    A = 2 * int(rng.integers(0, K // 4 + 1))
+    Hq = int(rng.choice([1, 2]))
+    H = Hq * int(rng.choice([1, 2, 3]))
+    S = int(rng.integers(1, 4 * C + 1))
+    return SisoCase(1, S, Hq, H, K, V, C, A=A, dtype=str(rng.choice(["bf16", "fp16"])),
+                    has_z=bool(rng.integers(2)), has_d=bool(rng.integers(2)), seed=k, name=f"siso_random_{k}")
+
+
+@pytest.mark.parametrize("k", range(48))
+def test_siso_random_shapes(k):
+    """Seeded random SISO shapes against the SISO oracle; a shape beyond the tiles
+    must be refused as such."""
+    case = _random_siso(k)
+    try:
+        _check_siso(case)
+    except NotImplementedError as e:
+        pytest.skip(f"{case.name}: {e}")
+
+
 @pytest.mark.parametrize("case", SISO_CASES, ids=lambda c: c.name)
 def test_siso(case):
     _check_siso(case)
