@@ -135,6 +135,21 @@ def test_random_shapes(k):
         pytest.skip(f"{case.name}: {e}")
 
 
+@pytest.mark.parametrize("k", range(8))
+def test_random_long_shapes(k):
+    """Random shapes as above at 1,500-9,000 tokens, where the plan splits the
+    sequence into segments of several chunks and the aggregate into sub-segments,
+    with the same two passes and bars."""
+    rng = np.random.default_rng(7000 + k)
+    case = _random_case(k).with_(S=int(rng.integers(1500, 9000)), name=f"long_{k}")
+    try:
+        _check(case, zero_angles=True)
+        _check(case, ulp_frac=0.995)
+    except NotImplementedError as e:
+        assert "bytes of LDS" in str(e), e
+        pytest.skip(f"{case.name}: {e}")
+
+
 @pytest.mark.parametrize("seed", [0, 1, 42])
 def test_tiny_and_tail_seeds(seed):
     _check(CONFIGS["tiny"].with_(seed=seed, name=f"tiny_seed{seed}"))
