@@ -60,3 +60,45 @@ def test_outputs_independent_of_stale_lds(case):
         except NotImplementedError as e:
             assert "bytes of LDS" in str(e), e
             pytest.skip(f"{case.name}: {e}")
+
+
+OTHER = [Case(1, 300, 2, 1, 64, 64, 4, 12, name="fill_other_r4_c12"),
+         Case(1, 200, 2, 1, 128, 128, 2, 40, rd=2, name="fill_other_r2_c40_n128"),
+         Case(1, 150, 2, 1, 96, 48, 3, 24, rd=2, name="fill_other_r3_c24")]
+
+
+@pytest.mark.parametrize("case", OTHER, ids=lambda c: c.name)
+def test_fp32_and_stage2_independent_of_stale_lds(case):
+    """The same for the fp32-intermediate variant and stage 2 (fp32 outputs)."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from oracle import o1
+    from synth.inputs import make_inputs
+    from ._parity import compare, to_device
+    from . import test_gpu_bwd2, test_gpu_fp32
+    inp = make_inputs(case)
+    inp["angles"] = torch.zeros_like(inp["angles"])
+    _fill()
+    try:
+        got = test_gpu_fp32.run_bwd32(to_device(inp))
+    except NotImplementedError as e:
+        got = None
+        assert "LDS" in str(e) or "tile" in str(e), e
+    if got is not None:
+        compare(got, o1.run_inputs(inp, fp32=True), tol=test_gpu_fp32.TOL32, label=f"{case.name} fp32: ")
+    states, qk = test_gpu_bwd2._caches(inp)
+    _fill()
+    got2 = test_gpu_bwd2._run_gpu(inp, states, qk, torch.float32)
+    test_gpu_bwd2._compare(got2, test_gpu_bwd2._oracle(inp, states, qk), f"{case.name} stage 2: ")
+
+
+@pytest.mark.parametrize("k", range(6))
+def test_siso_independent_of_stale_lds(k):
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from . import test_gpu_fp32
+    _fill()
+    try:
+        test_gpu_fp32._check_siso(test_gpu_fp32._random_siso(k))
+    except NotImplementedError as e:
+        pytest.skip(str(e))
