@@ -102,3 +102,44 @@ def test_siso_independent_of_stale_lds(k):
         test_gpu_fp32._check_siso(test_gpu_fp32._random_siso(k))
     except NotImplementedError as e:
         pytest.skip(str(e))
+
+
+WS_CASES = [Case(1, 2000, 2, 1, 64, 64, 4, 16, name="ws_segments"),
+            Case(2, 1500, 4, 2, 64, 64, 4, 16, reduce_o=False, has_z=False, name="ws_no_y"),
+            Case(1, 1200, 2, 1, 128, 128, 2, 32, name="ws_n128_c32")]
+
+
+@pytest.mark.parametrize("case", WS_CASES, ids=lambda c: c.name)
+def test_outputs_independent_of_workspace_contents(case):
+    """The caller's workspace may hold anything: outputs with a workspace of 0xFF
+    bytes (NaN as fp32) equal those with a zeroed one bit for bit."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from mamba_mimo_chunked_amd import _lib as mlib
+    from mamba_mimo_chunked_amd.api import _make_args
+    from synth.inputs import API_ORDER, make_inputs
+    from ._parity import NAMES
+    from .test_zz_no_alloc import _outputs
+    L = mlib.lib()
+    inp = make_inputs(case)
+    d = {n: (None if inp[n] is None else inp[n].to("cuda")) for n in API_ORDER}
+    res = []
+    for fill in (0x00, 0xFF):
+        out = _outputs(case, d["q"].device)
+        args = _make_args(case.B, case.S, case.H, case.G, case.R, case.N, case.P, case.C, case.rd, d, out)
+        need = ctypes.c_size_t(0)
+        assert L.mimo_bwd_fwd_workspace_size(ctypes.byref(args), ctypes.byref(need)) == mlib.MIMO_OK
+        assert need.value > 0, "these shapes split the sequence into segments"
+        ws = torch.full((int(need.value),), fill, dtype=torch.uint8, device="cuda")
+        args.workspace, args.workspace_bytes = ws.data_ptr(), int(need.value)
+        st = L.mimo_bwd_fwd(ctypes.byref(args), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == mlib.MIMO_OK, mlib.last_error()
+        torch.cuda.synchronize()
+        res.append({n: out[n] for n in NAMES})
+    for n in NAMES:
+        a, b = res[0][n], res[1][n]
+        assert (a is None) == (b is None), n
+        if a is not None:
+            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.uint8) if b.dtype == torch.bfloat16 else b.view(torch.int32)), \
+                f"{case.name}: {n} depends on the workspace contents"
